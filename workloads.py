@@ -1,0 +1,151 @@
+"""Seeded synthetic workloads for speculative-decoding verification.
+
+This module only draws random numbers and casts them: it holds none of the
+verification arithmetic (no softmax, no ratio, no sampling). It is the single
+piece shared by the oracle-side tests and the GPU side. Draft tokens, which the
+draft model would sample from its own distribution, are made by a sampler the
+caller passes in (the oracle's in tests, the library's K = 0 call in the bench),
+from the uniform stream ``u_draft`` drawn here.
+
+Shapes follow the workloads the pages discuss: LLM-sized vocabularies, K of 2 to
+16 drafts per round (lecture-16 notes, "动态调整 K": 8/16 for a good drafter,
+2/4 for a poor one), draft rows close to the target rows so that most drafts are
+accepted, and a bonus row per sequence.
+
+Recipe (numpy PCG64, fixed draw order; all arithmetic in float32):
+  1. ragged workloads first draw K_b for every sequence from ``k_choices``;
+  2. per sequence, base rows G ~ N(0, sd^2) of shape [K_b + 1, V];
+  3. per row, ``peaks`` distinct ids (rng.choice without replacement) get +boost;
+  4. noise E ~ N(0, 1) of the same shape; target = G + sd_t * E; draft = G[:K_b]
+     (row K_b of G is a phantom draft row that only shapes the bonus target row);
+  5. both are cast to the storage dtype with round-to-nearest-even (torch CPU);
+  6. u_draft ~ U[0,1) float32 from stream [seed, 1], one per draft row;
+     uniforms ~ U[0,1) float32 from stream [seed, 2], one per target row.
+Steps 2-4 use stream [seed, 0]; the target-noise scale is applied after the draw,
+so a sweep over sd_t at one seed shares its base rows and noise.
+"""
+
+import numpy as np
+import torch
+
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+# The five workloads, named by what they are.
+WORKLOADS = {
+    "tiny_f32_B4_K4_V1024": dict(
+        dtype="f32", B=4, K=4, V=1024, temperature=1.0, sd=2.0, peaks=0,
+        boost=0.0, sd_t=0.5, top_k=0, top_p=1.0, seed=1000),
+    "bf16_B32_K4_V32000": dict(
+        dtype="bf16", B=32, K=4, V=32000, temperature=1.0, sd=3.0, peaks=20,
+        boost=8.0, sd_t=1.0, top_k=0, top_p=1.0, seed=1001),
+    "bf16_B64_K8_V128256": dict(
+        dtype="bf16", B=64, K=8, V=128256, temperature=0.7, sd=3.0, peaks=20,
+        boost=8.0, sd_t=1.0, top_k=0, top_p=1.0, seed=1002,
+        sd_t_sweep=(0.25, 1.0, 4.0)),
+    "f16_B256_K4_V151936_topk50_topp0.9": dict(
+        dtype="f16", B=256, K=4, V=151936, temperature=0.8, sd=3.0, peaks=50,
+        boost=6.0, sd_t=1.5, top_k=50, top_p=0.9, seed=1003),
+    "bf16_B512_Kragged_V128256_halfgreedy": dict(
+        dtype="bf16", B=512, K=None, k_choices=(2, 4, 8, 16), V=128256,
+        temperature=1.0, sd=3.0, peaks=20, boost=8.0, sd_t=1.0, top_k=0,
+        top_p=1.0, seed=1004, greedy="odd"),
+}
+HEADLINE = "bf16_B64_K8_V128256"
+TINY = "tiny_f32_B4_K4_V1024"
+
+
+def _cast(a32, dtype):
+    return torch.from_numpy(a32).to(DTYPES[dtype])
+
+
+def make(name=None, *, cfg=None, seed=None, sd_t=None, B=None, V=None, K=None,
+         k_choices=None):
+    """Build a workload without draft tokens.
+
+    Returns a dict with torch CPU tensors ``draft`` [sum K_b, V] and ``target``
+    [sum (K_b + 1), V] in the storage dtype, int32 ``cu_draft`` [B + 1], bool
+    ``greedy`` [B], float32 ``u_draft`` [sum K_b] and ``uniforms``
+    [sum (K_b + 1)], plus the scalar settings. Overrides shrink a workload for
+    quick tests while keeping its value distribution.
+    """
+    c = dict(WORKLOADS[name] if cfg is None else cfg)
+    if seed is not None:
+        c["seed"] = seed
+    if sd_t is not None:
+        c["sd_t"] = sd_t
+    if B is not None:
+        c["B"] = B
+    if V is not None:
+        c["V"] = V
+    if K is not None:
+        c["K"] = K
+    if k_choices is not None:
+        c["k_choices"] = tuple(k_choices)
+        c["K"] = None
+    Bn, Vn = int(c["B"]), int(c["V"])
+    rng = np.random.default_rng([c["seed"], 0])
+    if c.get("K") is None:
+        Ks = rng.choice(np.asarray(c["k_choices"], dtype=np.int64), Bn)
+    else:
+        Ks = np.full(Bn, int(c["K"]), dtype=np.int64)
+    cu = np.zeros(Bn + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(Ks)
+    n_draft, n_target = int(cu[-1]), int(cu[-1]) + Bn
+    draft = torch.empty((n_draft, Vn), dtype=DTYPES[c["dtype"]])
+    target = torch.empty((n_target, Vn), dtype=DTYPES[c["dtype"]])
+    sd, sd_t = np.float32(c["sd"]), np.float32(c["sd_t"])
+    boost = np.float32(c["boost"])
+    for b in range(Bn):
+        kb = int(Ks[b])
+        g = rng.standard_normal((kb + 1, Vn), dtype=np.float32) * sd
+        for r in range(kb + 1):
+            if c["peaks"] > 0:
+                ids = rng.choice(Vn, int(c["peaks"]), replace=False)
+                g[r, ids] += boost
+        e = rng.standard_normal((kb + 1, Vn), dtype=np.float32)
+        t = g + sd_t * e
+        d0 = int(cu[b])
+        draft[d0:d0 + kb] = _cast(np.ascontiguousarray(g[:kb]), c["dtype"])
+        target[d0 + b:d0 + b + kb + 1] = _cast(t, c["dtype"])
+    greedy = np.zeros(Bn, dtype=bool)
+    if c.get("greedy") == "odd":
+        greedy[1::2] = True
+    u_draft = np.random.default_rng([c["seed"], 1]).random(n_draft, dtype=np.float32)
+    uniforms = np.random.default_rng([c["seed"], 2]).random(n_target, dtype=np.float32)
+    return dict(
+        name=name, dtype=c["dtype"], B=Bn, V=Vn,
+        K=None if c.get("K") is None else int(c["K"]),
+        ragged=c.get("K") is None,
+        temperature=float(c["temperature"]), top_k=int(c["top_k"]),
+        top_p=float(c["top_p"]), sd_t=float(c["sd_t"]), seed=int(c["seed"]),
+        draft=draft, target=target, cu_draft=cu.astype(np.int32), Ks=Ks,
+        greedy=greedy, u_draft=u_draft, uniforms=uniforms)
+
+
+def draft_row_greedy_mask(w):
+    """Per draft row: True where the owning sequence is greedy."""
+    return np.repeat(w["greedy"], w["Ks"])
+
+
+def raw_numpy(t):
+    """Storage bits of a CPU tensor as numpy (bf16 -> uint16 bit patterns)."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def compulsory_bytes(w):
+    """Bytes a verification call must move at least once.
+
+    Every logit of a sampling sequence's K_b draft rows and K_b + 1 target rows,
+    only the target rows of a greedy sequence, plus draft ids, uniforms and the
+    outputs."""
+    esize = torch.tensor([], dtype=DTYPES[w["dtype"]]).element_size()
+    Ks = np.asarray(w["Ks"])
+    if w["temperature"] == 0.0:
+        rows = int((Ks + 1).sum())
+    else:
+        g = np.asarray(w["greedy"], dtype=bool)
+        rows = int(((Ks + 1) + np.where(g, 0, Ks)).sum())
+    small = 4 * int(Ks.sum()) + 4 * int((Ks + 1).sum()) * 2 + 4 * w["B"]
+    return rows * w["V"] * esize + small
