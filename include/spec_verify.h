@@ -1,0 +1,168 @@
+/*
+ * spec_verify.h -- C ABI of the batched speculative-decoding verification step
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (pages cited by title and section):
+ *  - aivaro.ru answer 289, "Как работает speculative decoding на уровне
+ *    логитов, а не токенов?": section 5 step 3 and section 6 (accept a draft
+ *    token with probability min(1, p_target/p_draft); after a rejection drop
+ *    the later drafts and draw from max(0, p_target - p_draft)/Z), section 9
+ *    (softmax of both rows, a uniform compared with "<", multinomial draw).
+ *  - Hung-yi Lee lecture 16 notes, part "4、推测解码验证流程图": item 1
+ *    (one target pass scores all positions), items 2-3 (position-by-position
+ *    check, truncation at the first failure), item 4 (bonus token from the
+ *    (K+1)-th target distribution when every draft passes).
+ *  - aihero.vn "Speculative decoding": section "Chấp nhận bằng tỉ lệ, không chỉ
+ *    bằng argmax" (q = draft, p = target at the same prefix; ratio test;
+ *    residual), section "Cùng phân bố không có nghĩa cùng chuỗi mỗi lần"
+ *    (temperature / top-k / top-p applied consistently; greedy decoding has
+ *    its own check).
+ *
+ * For each sequence b with K_b draft tokens x_0..x_{K_b-1}:
+ *   q_i = softmax(filter(draft_row_i / T)),  p_i = softmax(filter(target_row_i / T))
+ *   accept x_i iff u_i < p_i(x_i) / q_i(x_i)   (strict; q_i(x)=0<p_i(x): accept)
+ *   n = index of the first rejection, or K_b
+ *   n < K_b: token n = inverse CDF of max(0, p_n - q_n) with u_{K_b}
+ *   n = K_b: token n = inverse CDF of p_{K_b} with u_{K_b}      (bonus)
+ * The inverse CDF takes the smallest id j (ascending ids) whose cumulative
+ * weight exceeds u * Z. filter = top-k (values >= the k-th largest, ties kept)
+ * then top-p (keep ids whose strictly-larger-logit mass is < top_p).
+ * Greedy sequences (temperature 0, or the per-sequence mask) accept x_i iff it
+ * equals argmax(target_row_i) (lowest id on ties) and emit argmax(target_row_n)
+ * at position n; they never read draft rows or uniforms.
+ *
+ * Layout (all device pointers, row-major, rows contiguous with stride V):
+ *   draft_logits  [sum_b K_b, V]        sequence b owns rows cu[b] .. cu[b+1]-1
+ *   target_logits [sum_b (K_b+1), V]    rows cu[b]+b .. cu[b+1]+b
+ *   draft_tokens  int32 [sum_b K_b]
+ *   uniforms      float [sum_b (K_b+1)] slots 0..K_b-1 accept tests, slot K_b
+ *                                       the resample-or-bonus draw
+ *   out_tokens    int32 [sum_b (K_b+1)] tokens 0..n valid, the rest -1
+ *   num_accepted  int32 [B]             n, or a negative per-sequence code
+ * The dense entry point is the case cu[b] = b*K ([B,K,V], [B,K+1,V], ...).
+ *
+ * Ownership: the caller owns every buffer (inputs, outputs and the workspace);
+ * the library allocates nothing, keeps no state between calls and enqueues all
+ * work on `stream` without synchronising it. Calls that share a workspace must
+ * be ordered (same stream, or synchronised).
+ *
+ * Errors: argument errors return a negative SV_E* code before any device work.
+ * Data errors found on the device are reported per sequence in num_accepted
+ * (SV_SEQ_*), with that sequence's out_tokens all -1.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage type of the logit rows. */
+typedef enum sv_dtype { SV_F32 = 0, SV_F16 = 1, SV_BF16 = 2 } sv_dtype;
+
+/* Return codes of the entry points. */
+#define SV_OK 0
+#define SV_EINVAL (-1)       /* null pointer, negative size, K out of [0,64],
+                                temperature < 0 / NaN / inf, top_p outside (0,1] */
+#define SV_EDTYPE (-2)       /* dtype not one of sv_dtype */
+#define SV_EWORKSPACE (-3)   /* workspace null, not 256-byte aligned, or smaller
+                                than spec_verify_workspace_bytes() */
+#define SV_EHIP (-4)         /* a HIP launch or event record failed */
+#define SV_EUNSUPPORTED (-5) /* valid request outside this build's limits
+                                (top_k above SV_MAX_TOP_K) */
+
+/* Per-sequence codes written to num_accepted[b] instead of a count. */
+#define SV_SEQ_BAD_TOKEN (-1)   /* a draft id outside [0, V) */
+#define SV_SEQ_BAD_ROW (-2)     /* a used row holds NaN or +inf, or no finite
+                                   value (greedy: target rows only) */
+#define SV_SEQ_BAD_OFFSETS (-3) /* ragged offsets: cu[b] > cu[b+1], outside
+                                   [0, total_draft_rows], or K_b > 64 */
+
+#define SV_MAX_K 64
+#define SV_MAX_TOP_K 1024
+
+/* Human-readable text for a return code or per-sequence code. Never NULL. */
+const char* spec_verify_strerror(int code);
+
+/* Bytes of device workspace a call with these sizes needs (the same value for
+ * spec_verify with total_draft_rows = B*K). Returns 0 for invalid sizes. */
+size_t spec_verify_workspace_bytes(int B, int total_draft_rows, int V, int top_k,
+                                   float top_p);
+
+/* Zero-fill a workspace on `stream` (kernel fill, no memset node). Needed once
+ * before a workspace is first used; every call leaves it valid for the next. */
+int spec_verify_workspace_init(void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* Dense batch: B sequences with K drafts each.
+ *   draft_logits  [B, K, V]   (may be NULL when K == 0 or temperature == 0)
+ *   target_logits [B, K+1, V]
+ *   draft_tokens  int32 [B, K] (may be NULL when K == 0)
+ *   uniforms      float [B, K+1] in [0, 1) (may be NULL when temperature == 0)
+ *   temperature   > 0 sampling, == 0 greedy for every sequence
+ *   top_k         <= 0 or >= V: off;  top_p in (0, 1], 1: off
+ *   out_tokens    int32 [B, K+1];  num_accepted int32 [B]
+ * B == 0 returns SV_OK and launches nothing. */
+int spec_verify(const void* draft_logits, const void* target_logits,
+                const int32_t* draft_tokens, const float* uniforms, int B, int K,
+                int V, float temperature, int top_k, float top_p, sv_dtype dtype,
+                int32_t* out_tokens, int32_t* num_accepted, void* workspace,
+                size_t workspace_bytes, hipStream_t stream);
+
+/* Ragged batch (per-sequence K_b, the dynamic-K setting of the lecture-16 notes,
+ * "工程里的关键优化点" item 3): packed rows as described above.
+ *   cu_draft   int32 [B+1] device offsets, cu[0] = 0, non-decreasing,
+ *              cu[B] = total_draft_rows, K_b = cu[b+1]-cu[b] <= 64
+ *   greedy     uint8 [B] device mask (nonzero: greedy), or NULL for none;
+ *              temperature == 0 makes every sequence greedy. */
+int spec_verify_ragged(const void* draft_logits, const void* target_logits,
+                       const int32_t* draft_tokens, const float* uniforms,
+                       const int32_t* cu_draft, const uint8_t* greedy, int B,
+                       int total_draft_rows, int V, float temperature, int top_k,
+                       float top_p, sv_dtype dtype, int32_t* out_tokens,
+                       int32_t* num_accepted, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/* Optional side outputs of spec_verify_diag (every pointer may be NULL).
+ *   row_max_*    raw logit maximum of each row's kept set
+ *   row_logsum_* ln sum_{kept} exp((l - max)/T) of each row; the row's
+ *                normaliser is exp(max/T) * exp(row_logsum)
+ *   ratio        p_i(x_i)/q_i(x_i) per draft row (sampling sequences)
+ *   resid_Z      per sequence: the mass the final inverse CDF normalised by
+ *                (residual mass at n, or the bonus row's mass)
+ *   stage_events n_stage_events events recorded on `stream` before the first
+ *                kernel and after each kernel of the call (for timing). */
+typedef struct sv_diag {
+  float* row_max_draft;
+  float* row_logsum_draft;
+  float* row_max_target;
+  float* row_logsum_target;
+  float* ratio;
+  float* resid_Z;
+  hipEvent_t* stage_events;
+  int n_stage_events;
+} sv_diag;
+
+/* Number of kernels a call launches for these settings (stage events = this+1). */
+int spec_verify_num_stages(int top_k, float top_p);
+
+/* spec_verify_ragged with side outputs (diag may be NULL). */
+int spec_verify_diag(const void* draft_logits, const void* target_logits,
+                     const int32_t* draft_tokens, const float* uniforms,
+                     const int32_t* cu_draft, const uint8_t* greedy, int B,
+                     int total_draft_rows, int V, float temperature, int top_k,
+                     float top_p, sv_dtype dtype, int32_t* out_tokens,
+                     int32_t* num_accepted, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream,
+                     const sv_diag* diag);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

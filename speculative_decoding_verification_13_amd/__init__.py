@@ -1,0 +1,24 @@
+"""MI355X-native batched speculative-decoding verification.
+
+The work runs in hand-written HIP kernels for gfx950 behind the C ABI of
+``include/spec_verify.h`` (``libspecverify.so``, built in-tree by
+``python -m speculative_decoding_verification_13_amd.build``). This package is
+the thin Python binding: it marshals torch device tensors and the current
+stream into those calls.
+"""
+
+from ._lib import (  # noqa: F401
+    SV_MAX_K,
+    SV_SEQ_BAD_OFFSETS,
+    SV_SEQ_BAD_ROW,
+    SV_SEQ_BAD_TOKEN,
+    SpecVerifyError,
+    lib,
+    make_stage_events,
+    make_workspace,
+    num_stages,
+    spec_verify,
+    spec_verify_ragged,
+    strerror,
+    workspace_bytes,
+)

@@ -1,0 +1,54 @@
+"""Compile the HIP library ``libspecverify.so`` in-tree for gfx950.
+
+Run as ``python -m speculative_decoding_verification_13_amd.build``. The shared
+library lands next to this file, so it travels with the source tree.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libspecverify.so"
+LIB_PATH = os.path.join(HERE, LIB_NAME)
+SOURCES = ["sv_api.hip", "sv_kernels.hip"]
+ARCH = "gfx950"
+
+
+def hipcc():
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found: the HIP library cannot be built")
+    return path
+
+
+def compile_flags():
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+        # keep the compiler from forming packed fp32 instructions
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", INCLUDE, "-I", CSRC,
+    ]
+
+
+def build(verbose=False):
+    """Compile every source and link the shared library (always rebuilds)."""
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc(), *compile_flags(), "-shared", "-o", tmp,
+           *[os.path.join(CSRC, s) for s in SOURCES]]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

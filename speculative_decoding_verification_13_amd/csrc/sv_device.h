@@ -1,0 +1,239 @@
+// Device-side helpers of the verification kernels (gfx950, wave64).
+//
+// Numerics: every softmax statistic is kept in base-2 exponent units. For a row
+// with raw logits l, temperature T and c = log2(e)/T, the reference of a
+// (partial) row is R = fp32(m * c) where m is the raw maximum seen, and the
+// partial sum is S = sum 2^(l*c - R) with each exponent formed by one fused
+// multiply-add. Every later use of the row (ratio, residual, bonus) forms its
+// exponents with the same R and the same fused multiply-add, so the rounding
+// of R cancels exactly between numerator and normaliser.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "spec_verify.h"
+
+namespace sv {
+
+constexpr int kBlock = 256;       // threads of the streaming kernels (4 waves)
+constexpr int kWave = 64;
+constexpr int kTileElems = 2048;  // residual/bonus tile: one wave, 32 elements/lane
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kPosInf = __builtin_huge_valf();
+
+template <int DT> struct Dt;
+template <> struct Dt<SV_F32> { static constexpr int N = 4; static constexpr int kBytes = 4; };
+template <> struct Dt<SV_F16> { static constexpr int N = 8; static constexpr int kBytes = 2; };
+template <> struct Dt<SV_BF16> { static constexpr int N = 8; static constexpr int kBytes = 2; };
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void unpack2(uint32_t w, float& lo, float& hi,
+                                        std::integral_constant<int, SV_BF16>) {
+  lo = __uint_as_float(w << 16);
+  hi = __uint_as_float(w & 0xffff0000u);
+}
+__device__ __forceinline__ void unpack2(uint32_t w, float& lo, float& hi,
+                                        std::integral_constant<int, SV_F16>) {
+  half2_t h = __builtin_bit_cast(half2_t, w);
+  lo = (float)h.x;
+  hi = (float)h.y;
+}
+
+// Unpack one 16-byte vector into N floats (exact widening).
+template <int DT>
+__device__ __forceinline__ void unpack(const uint4 v, float* f) {
+  if constexpr (DT == SV_F32) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  } else {
+    std::integral_constant<int, DT> tag;
+    unpack2(v.x, f[0], f[1], tag);
+    unpack2(v.y, f[2], f[3], tag);
+    unpack2(v.z, f[4], f[5], tag);
+    unpack2(v.w, f[6], f[7], tag);
+  }
+}
+
+// One logit, exact widening. `idx` is an element index from the array base.
+template <int DT>
+__device__ __forceinline__ float load_elem(const void* base, size_t idx) {
+  if constexpr (DT == SV_F32) {
+    return reinterpret_cast<const float*>(base)[idx];
+  } else {
+    uint32_t w = reinterpret_cast<const uint16_t*>(base)[idx];
+    if constexpr (DT == SV_BF16) {
+      return __uint_as_float(w << 16);
+    } else {
+      return (float)__builtin_bit_cast(_Float16, (uint16_t)w);
+    }
+  }
+}
+
+// Row reader: VEC = 16-byte vectors (rows 16-byte aligned, V % N == 0), else one
+// element per "vector".
+template <int DT, bool VEC> struct Reader {
+  static constexpr int N = VEC ? Dt<DT>::N : 1;
+  // v indexes vectors of the row that starts at element row_elem.
+  __device__ __forceinline__ static void load(const void* base, size_t row_elem, int v,
+                                              float* f) {
+    if constexpr (VEC) {
+      const uint4* p = reinterpret_cast<const uint4*>(
+          reinterpret_cast<const char*>(base) + row_elem * Dt<DT>::kBytes);
+      unpack<DT>(p[v], f);
+    } else {
+      f[0] = load_elem<DT>(base, row_elem + (size_t)v);
+    }
+  }
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 2^(a - b) for two references, 1 when equal (covers -inf == -inf).
+__device__ __forceinline__ float rescale(float r_old, float r_new) {
+  return (r_old == r_new) ? 1.0f : fast_exp2(r_old - r_new);
+}
+
+// Reference R = fp32(m * c) of a raw maximum m; 0 for an empty (all -inf) row.
+__device__ __forceinline__ float ref_of(float m, float c) {
+  return (m == kNegInf) ? 0.0f : m * c;
+}
+
+// Merge partial (m, s) statistics: both s are relative to ref_of(their m).
+__device__ __forceinline__ void merge_ms(float& m, float& s, float om, float os, float c) {
+  const float nm = fmaxf(m, om);
+  const float nr = ref_of(nm, c);
+  const float a = (s == 0.0f) ? 0.0f : s * rescale(ref_of(m, c), nr);
+  const float b = (os == 0.0f) ? 0.0f : os * rescale(ref_of(om, c), nr);
+  m = nm;
+  s = a + b;
+}
+
+// Online update of (m, s) with M values held in registers.
+template <int M>
+__device__ __forceinline__ void online_update(float& m, float& s, const float* x, float c) {
+  float bm = x[0];
+#pragma unroll
+  for (int k = 1; k < M; ++k) bm = fmaxf(bm, x[k]);
+  const float nm = fmaxf(m, bm);
+  const float nr = ref_of(nm, c);
+  float e[M];
+#pragma unroll
+  for (int k = 0; k < M; ++k) e[k] = fast_exp2(fmaf(x[k], c, -nr));
+#pragma unroll
+  for (int w = 1; w < M; w *= 2) {
+#pragma unroll
+    for (int k = 0; k + w < M; k += 2 * w) e[k] += e[k + w];
+  }
+  const float old = (s == 0.0f) ? 0.0f : s * rescale(ref_of(m, c), nr);
+  s = old + e[0];
+  m = nm;
+}
+
+// Argmax with lowest index on ties; indices visited in increasing order per
+// thread so the strict compare keeps the first maximum.
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi) {
+  if (ov > v || (ov == v && oi < i)) {
+    v = ov;
+    i = oi;
+  }
+}
+
+__device__ __forceinline__ bool is_nan_or_posinf(float x) {
+  return __builtin_isfpclass(x, 0x0003 | 0x0200);  // sNaN | qNaN | +inf
+}
+
+// ---- wave / block reductions (wave64) ----
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ int wave_min_i(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = min(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ int wave_max_i(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ void wave_merge_ms(float& m, float& s, float c) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float om = __shfl_xor(m, o);
+    const float os = __shfl_xor(s, o);
+    merge_ms(m, s, om, os, c);
+  }
+}
+__device__ __forceinline__ void wave_argmax(float& v, int& i, int& bad) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float ov = __shfl_xor(v, o);
+    const int oi = __shfl_xor(i, o);
+    bad |= __shfl_xor(bad, o);
+    argmax_merge(v, i, ov, oi);
+  }
+}
+
+// Inclusive prefix sum over the wave (lane order).
+__device__ __forceinline__ float wave_incl_scan(float x) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const float y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Block-wide inclusive scan for kBlock threads; `total` receives the block sum.
+__device__ __forceinline__ float block_incl_scan(float x, float& total) {
+  __shared__ float s_w[kBlock / kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  float incl = wave_incl_scan(x);
+  __syncthreads();
+  if (lane == kWave - 1) s_w[w] = incl;
+  __syncthreads();
+  float base = 0.0f;
+  total = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kBlock / kWave; ++k) {
+    const float t = s_w[k];
+    if (k < w) base += t;
+    total += t;
+  }
+  return base + incl;
+}
+
+__device__ __forceinline__ int block_min_i(int x) {
+  __shared__ int s_w[kBlock / kWave];
+  x = wave_min_i(x);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) s_w[threadIdx.x / kWave] = x;
+  __syncthreads();
+  int r = s_w[0];
+#pragma unroll
+  for (int k = 1; k < kBlock / kWave; ++k) r = min(r, s_w[k]);
+  return r;
+}
+__device__ __forceinline__ int block_max_i(int x) {
+  __shared__ int s_w[kBlock / kWave];
+  x = wave_max_i(x);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) s_w[threadIdx.x / kWave] = x;
+  __syncthreads();
+  int r = s_w[0];
+#pragma unroll
+  for (int k = 1; k < kBlock / kWave; ++k) r = max(r, s_w[k]);
+  return r;
+}
+
+}  // namespace sv

@@ -59,7 +59,7 @@ def _cast(a32, dtype):
 
 
 def make(name=None, *, cfg=None, seed=None, sd_t=None, B=None, V=None, K=None,
-         k_choices=None):
+         k_choices=None, ks=None, dtype=None, temperature=None):
     """Build a workload without draft tokens.
 
     Returns a dict with torch CPU tensors ``draft`` [sum K_b, V] and ``target``
@@ -82,9 +82,18 @@ def make(name=None, *, cfg=None, seed=None, sd_t=None, B=None, V=None, K=None,
     if k_choices is not None:
         c["k_choices"] = tuple(k_choices)
         c["K"] = None
+    if dtype is not None:
+        c["dtype"] = dtype
+    if temperature is not None:
+        c["temperature"] = temperature
+    if ks is not None:
+        c["K"] = None
+        c["B"] = len(ks)
     Bn, Vn = int(c["B"]), int(c["V"])
     rng = np.random.default_rng([c["seed"], 0])
-    if c.get("K") is None:
+    if ks is not None:
+        Ks = np.asarray(ks, dtype=np.int64)
+    elif c.get("K") is None:
         Ks = rng.choice(np.asarray(c["k_choices"], dtype=np.int64), Bn)
     else:
         Ks = np.full(Bn, int(c["K"]), dtype=np.int64)
