@@ -1,0 +1,282 @@
+"""Throughput of the batched speculative-decoding verification step on one MI355X.
+
+One step = one spec_verify call (every kernel of the path) over one batch of
+synthetic logits resident in HBM. Default workload: B=64 sequences, K=8 drafts,
+V=128256, bf16 logits, temperature 0.7, target perturbation sd 1.0. Four copies
+of the inputs rotate so that the 256 MB Infinity Cache cannot serve one step's
+rows from the previous step.
+
+Prints one JSON line: verified (sequence, position) rows per second, effective
+HBM bandwidth of the compulsory bytes, a roofline entry for the kernel (its
+algorithmic bytes over its HIP-event duration on the launch stream) and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "verified rows/sec + effective HBM GB/s (% of ~8 TB/s), B=64 K=8 V=128256 bf16"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_verify_bf16_B64_K8_V128256_traffic.json")
+DOMINANT = "k_verify"
+
+
+class HipEvents:
+    """Timing events made directly with the HIP runtime, flagged to skip the
+    system-scope fence a default event performs (that fence writes back and
+    invalidates caches, which would sit between the kernels being timed)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.handles = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(h), self.DISABLE_SYSTEM_FENCE)
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+            self.handles.append(h.value)
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(ms), self.handles[a], self.handles[b])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value
+
+    def close(self):
+        for h in self.handles:
+            self.hip.hipEventDestroy(h)
+        self.handles = []
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "speculative_decoding_verification_13_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=W.HEADLINE, choices=sorted(W.WORKLOADS))
+    ap.add_argument("--sd-t", type=float, default=None, help="target perturbation sd")
+    ap.add_argument("--sets", type=int, default=4, help="rotating input copies")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the CPU oracle sample (0 disables)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of known size (counter calibration)")
+    return ap.parse_args()
+
+
+def calibrate_copy():
+    """A plain 1 GiB device-to-device copy, for scaling the HBM byte counters."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "launches": 3}),
+          flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(sequences shard across GPUs with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    import speculative_decoding_verification_13_amd as sv
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    w = W.make(args.workload, sd_t=args.sd_t)
+    B, V = w["B"], w["V"]
+    cu = w["cu_draft"]
+    n_draft = int(cu[-1])
+    n_target = n_draft + B
+    T, top_k, top_p = w["temperature"], w["top_k"], w["top_p"]
+
+    # --- device-resident inputs (rotating copies) --------------------------------
+    draft0 = w["draft"].to(dev)
+    target0 = w["target"].to(dev)
+    cu_d = torch.from_numpy(cu.astype(np.int32)).to(dev)
+    greedy_d = torch.from_numpy(w["greedy"].astype(np.uint8)).to(dev) if w["greedy"].any() else None
+    uni_d = torch.from_numpy(w["uniforms"]).to(dev)
+
+    # Draft tokens: the draft model's own draw from its rows, made by the library
+    # (each draft row as a K = 0 "sequence": plain sampling with its uniform).
+    zeros_cu = torch.zeros(n_draft + 1, dtype=torch.int32, device=dev)
+    u_draft = torch.from_numpy(w["u_draft"]).to(dev)
+    g_rows = (torch.from_numpy(W.draft_row_greedy_mask(w).astype(np.uint8)).to(dev)
+              if w["greedy"].any() else None)
+    tok_out, _ = sv.spec_verify_ragged(None, draft0, None, u_draft, zeros_cu, g_rows, n_draft,
+                                       V, T, top_k, top_p, total_draft_rows=0)
+    tokens_d = tok_out.clone()
+    del zeros_cu
+
+    sets = []
+    for s in range(max(1, args.sets)):
+        if s == 0:
+            sets.append((draft0, target0))
+        else:
+            sets.append((draft0.clone(), target0.clone()))
+    ws = sv.make_workspace(B, n_draft, V, top_k, top_p, dev)
+    out = torch.empty(n_target, dtype=torch.int32, device=dev)
+    num = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def step(k, events=None):
+        d, t = sets[k % len(sets)]
+        diag = None if events is None else {"stage_events": events}
+        sv.spec_verify_ragged(d, t, tokens_d, uni_d, cu_d, greedy_d, B, V, T, top_k, top_p,
+                              total_draft_rows=n_draft, out_tokens=out, num_accepted=num,
+                              workspace=ws, diag=diag)
+
+    # stage events on the launch stream: before and after the kernel, one pair per
+    # timed step (HIP events without the system-scope fence)
+    hev = HipEvents(2 * args.steps)
+    ev_pairs = [hev.handles[2 * k:2 * k + 2] for k in range(args.steps)]
+    for k in range(args.warmup):
+        step(k, ev_pairs[k % len(ev_pairs)])
+    torch.cuda.synchronize()
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for k in range(args.steps):
+        step(k, ev_pairs[k])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    k1_ms = float(np.mean([hev.elapsed_ms(2 * k, 2 * k + 1) for k in range(args.steps)]))
+    hev.close()
+
+    rows = int((w["Ks"] + 1).sum())
+    comp = W.compulsory_bytes(w)
+    esize = target0.element_size()
+    greedy = w["greedy"].astype(bool)
+    algo_rows = int(((w["Ks"] + 1) + np.where(greedy, 0, w["Ks"])).sum()) if T > 0 else rows
+    algo_bytes_k1 = algo_rows * V * esize
+    achieved = algo_bytes_k1 / (k1_ms * 1e-3) / 1e9
+    eff = comp / (ms_step * 1e-3) / 1e9
+
+    n_acc = num.cpu().numpy()
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("source_sha256") == kernel_source_digest() and tr.get("workload") == args.workload \
+                and args.sd_t in (None, tr.get("sd_t")):
+            traffic = tr.get("hbm_bytes_per_launch")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    res = {
+        "metric": METRIC,
+        "value": rows / (ms_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload, "B": B, "K": w["K"], "V": V, "input_dtype": w["dtype"],
+            "temperature": T, "top_k": top_k, "top_p": top_p, "sd_t": w["sd_t"],
+            "rows_per_step": rows, "rotating_sets": len(sets),
+        },
+        "effective_GBps": eff,
+        "effective_frac_of_peak": eff / PEAK_HBM_GBPS,
+        "compulsory_bytes_per_step": comp,
+        "roofline": {
+            "kernel": DOMINANT, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+            "algorithmic_bytes_per_launch": algo_bytes_k1, "avg_launch_ms": k1_ms,
+        },
+        "acceptance": {
+            "mean_accepted": float(n_acc.mean()),
+            "all_accepted_frac": float((n_acc == w["Ks"]).mean()),
+            "errors": int((n_acc < 0).sum()),
+        },
+        "wall_s": wall,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(w, budget_s):
+    """The float64 oracle, as it stands, on the first sequences of the same workload
+    (cycled until the budget is spent), one process on the host."""
+    import oracle
+    B, V = w["B"], w["V"]
+    cu = w["cu_draft"]
+    draft = W.raw_numpy(w["draft"])
+    target = W.raw_numpy(w["target"])
+    n_seq = min(B, 16)
+    d1 = int(cu[n_seq])
+    toks, _ = oracle.sample_rows(draft[:d1], w["u_draft"][:d1], V=V, dtype=w["dtype"],
+                                 temperature=w["temperature"], top_k=w["top_k"],
+                                 top_p=w["top_p"], greedy=W.draft_row_greedy_mask(w)[:d1])
+    t0 = time.perf_counter()
+    rows = 0
+    calls = 0
+    while True:
+        oracle.verify(draft[:d1], target[: d1 + n_seq], toks, w["uniforms"][: d1 + n_seq],
+                      B=n_seq, V=V, dtype=w["dtype"], cu_draft=cu[: n_seq + 1],
+                      temperature=w["temperature"], top_k=w["top_k"], top_p=w["top_p"],
+                      greedy=w["greedy"][:n_seq])
+        rows += int((w["Ks"][:n_seq] + 1).sum())
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {
+        "value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
+        "sample": f"first {n_seq} of {B} sequences of the same workload, {calls} passes, "
+                  f"{el:.1f} s, numpy float64, one process",
+        "host_cpus": os.cpu_count(),
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -74,7 +74,8 @@ typedef enum sv_dtype { SV_F32 = 0, SV_F16 = 1, SV_BF16 = 2 } sv_dtype;
                                 than spec_verify_workspace_bytes() */
 #define SV_EHIP (-4)         /* a HIP launch or event record failed */
 #define SV_EUNSUPPORTED (-5) /* valid request outside this build's limits
-                                (top_k above SV_MAX_TOP_K) */
+                                (top_k above SV_MAX_TOP_K, or V above
+                                2,097,152 elements) */
 
 /* Per-sequence codes written to num_accepted[b] instead of a count. */
 #define SV_SEQ_BAD_TOKEN (-1)   /* a draft id outside [0, V) */
@@ -82,6 +83,9 @@ typedef enum sv_dtype { SV_F32 = 0, SV_F16 = 1, SV_BF16 = 2 } sv_dtype;
                                    value (greedy: target rows only) */
 #define SV_SEQ_BAD_OFFSETS (-3) /* ragged offsets: cu[b] > cu[b+1], outside
                                    [0, total_draft_rows], or K_b > 64 */
+#define SV_SEQ_SYNC_TIMEOUT (-4) /* a bounded wait between the blocks that share
+                                    a row ran out (the row's blocks did not all
+                                    run); the sequence's outputs are not valid */
 
 #define SV_MAX_K 64
 #define SV_MAX_TOP_K 1024
@@ -94,8 +98,13 @@ const char* spec_verify_strerror(int code);
 size_t spec_verify_workspace_bytes(int B, int total_draft_rows, int V, int top_k,
                                    float top_p);
 
-/* Zero-fill a workspace on `stream` (kernel fill, no memset node). Needed once
- * before a workspace is first used; every call leaves it valid for the next. */
+/* Zero-fill a workspace on `stream` (kernel fill, no memset node). A workspace
+ * must be zero-filled once before its first use: the blocks of a call exchange
+ * partial results through it, and a zero entry means "not yet published".
+ * Every call returns the whole workspace to zero before it ends, so calls that
+ * share one workspace may differ in B, K, V and dtype, as long as it is large
+ * enough for each of them. After a call that reports SV_SEQ_SYNC_TIMEOUT or
+ * SV_SEQ_BAD_OFFSETS for any sequence, zero-fill the workspace again. */
 int spec_verify_workspace_init(void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
@@ -117,7 +126,10 @@ int spec_verify(const void* draft_logits, const void* target_logits,
 /* Ragged batch (per-sequence K_b, the dynamic-K setting of the lecture-16 notes,
  * "工程里的关键优化点" item 3): packed rows as described above.
  *   cu_draft   int32 [B+1] device offsets, cu[0] = 0, non-decreasing,
- *              cu[B] = total_draft_rows, K_b = cu[b+1]-cu[b] <= 64
+ *              cu[B] = total_draft_rows, K_b = cu[b+1]-cu[b] <= 64; a sequence
+ *              whose own pair (cu[b], cu[b+1]) breaks this reports
+ *              SV_SEQ_BAD_OFFSETS; if the array as a whole is not
+ *              non-decreasing the other sequences' results are unspecified
  *   greedy     uint8 [B] device mask (nonzero: greedy), or NULL for none;
  *              temperature == 0 makes every sequence greedy. */
 int spec_verify_ragged(const void* draft_logits, const void* target_logits,
@@ -136,7 +148,9 @@ int spec_verify_ragged(const void* draft_logits, const void* target_logits,
  *   resid_Z      per sequence: the mass the final inverse CDF normalised by
  *                (residual mass at n, or the bonus row's mass)
  *   stage_events n_stage_events events recorded on `stream` before the first
- *                kernel and after each kernel of the call (for timing). */
+ *                kernel and after each kernel of the call (for timing).
+ *   spin_limit   bound of the wait between blocks of one row (0: default);
+ *                a small value forces SV_SEQ_SYNC_TIMEOUT paths in tests. */
 typedef struct sv_diag {
   float* row_max_draft;
   float* row_logsum_draft;
@@ -146,6 +160,7 @@ typedef struct sv_diag {
   float* resid_Z;
   hipEvent_t* stage_events;
   int n_stage_events;
+  int spin_limit;
 } sv_diag;
 
 /* Number of kernels a call launches for these settings (stage events = this+1). */

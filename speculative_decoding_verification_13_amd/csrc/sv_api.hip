@@ -1,9 +1,11 @@
 // C ABI of the verification library: argument checks, workspace layout and the
-// launch of the kernels in sv_kernels.hip. Nothing here touches the device
+// launch of the kernel in sv_verify.hip. Nothing here touches the device
 // before every argument has been checked.
 #include <limits.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <cstdint>
 
 #include "spec_verify.h"
 #include "sv_launch.h"
@@ -11,47 +13,65 @@
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kStatsTargetBlocks = 2048;   // aim: several blocks per CU
-constexpr int kMinChunkElems = 8192;       // smallest V-chunk worth a block
-constexpr int kMaxChunks = 16;
-constexpr int kTileElems = 2048;           // must match sv::kTileElems
-constexpr int kTilesPerBlock = 4;          // one tile per wave of k_resid_tiles
+constexpr int kMaxChunks = 512;         // decide() stages 2*chunks slots per position
+constexpr int kDefaultSpinLimit = 1 << 22;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int esize_of(int dtype) { return dtype == SV_F32 ? 4 : 2; }
 
-bool make_plan(int B, int total_draft, int V, sv::Plan& L) {
+// Chunks per row for a given vector count per row.
+long long chunks_for(long long nvec) { return (nvec + sv::kChunkVecs - 1) / sv::kChunkVecs; }
+
+// Workspace layout (per call):
+//   draw_done[B], seq_flags[B], job_ready[B], jobs[B]   per sequence
+//   slots[rows * 2 * cmax]          64-bit chunk partials (0 = unpublished)
+//   tiles[B * dmax * tiles/draw]    draw-weight tile sums
+// Every call returns every entry it wrote to zero before it ends, so the
+// layout may differ from call to call. The regions are sized for the scalar
+// path (one element per vector), the largest chunk counts of any dtype.
+bool data_bytes(int B, int total_draft, int V, size_t& bytes, long long& rows, long long& cmax,
+                long long& dmax) {
   if (B < 0 || total_draft < 0 || V < 1) return false;
-  const long long rows_t = (long long)total_draft + B;
-  if (rows_t > INT_MAX) return false;
-  long long chunks = 1;
-  if (rows_t > 0) {
-    const long long want = (kStatsTargetBlocks + rows_t - 1) / rows_t;
-    long long cap = V / kMinChunkElems;
-    if (cap < 1) cap = 1;
-    if (cap > kMaxChunks) cap = kMaxChunks;
-    chunks = want < cap ? want : cap;
-    if (chunks < 1) chunks = 1;
-  }
-  L.chunks = (int)chunks;
-  L.ntiles = (int)(((long long)V + kTileElems - 1) / kTileElems);
-  L.tiles_per_chunk = kTilesPerBlock;
-  L.tile_chunks = (L.ntiles + kTilesPerBlock - 1) / kTilesPerBlock;
-  L.stats_blocks = rows_t * chunks;
-  L.tile_blocks = (long long)B * L.tile_chunks;
-  // grid x * block must stay below 2^32 threads
-  if (L.stats_blocks * 256 > (long long)UINT32_MAX || L.tile_blocks * 256 > (long long)UINT32_MAX)
-    return false;
-  size_t off = 0;
-  L.off_jobs = off;
-  off = align_up(off + (size_t)B * sizeof(sv::Job));
-  L.off_partials = off;
-  off = align_up(off + (size_t)rows_t * (size_t)chunks * 16);
-  L.off_tiles = off;
-  off = align_up(off + (size_t)B * (size_t)L.ntiles * 4);
-  L.total_bytes = off;
+  rows = (long long)total_draft + B;
+  if (rows > INT_MAX) return false;
+  cmax = chunks_for(V);
+  if (cmax > kMaxChunks) return false;
+  dmax = ((long long)V + sv::kDrawVecs - 1) / sv::kDrawVecs;
+  bytes = 3 * align_up((size_t)B * 4) + align_up((size_t)rows * 2 * (size_t)cmax * 8) +
+          align_up((size_t)B * (size_t)dmax * sv::kTilesPerDraw * 4) +
+          align_up((size_t)B * sizeof(sv::Job));
   return true;
+}
+
+bool make_plan(int B, int total_draft, int V, size_t ws_bytes, sv::Plan& L) {
+  size_t dbytes;
+  long long rows, cmax, dmax;
+  if (!data_bytes(B, total_draft, V, dbytes, rows, cmax, dmax)) return false;
+  L.chunks = (int)cmax;
+  L.dchunks = (int)dmax;
+  L.blocks = rows * 2 * cmax + (long long)B * dmax;
+  size_t off = 0;
+  L.off_draw_done = off;
+  off += align_up((size_t)B * 4);
+  L.off_seq_flags = off;
+  off += align_up((size_t)B * 4);
+  L.off_job_ready = off;
+  off += align_up((size_t)B * 4);
+  L.off_jobs = off;
+  off += align_up((size_t)B * sizeof(sv::Job));
+  L.off_slots = off;
+  off += align_up((size_t)rows * 2 * (size_t)cmax * 8);
+  L.off_tiles = off;
+  off += align_up((size_t)B * (size_t)dmax * sv::kTilesPerDraw * 4);
+  L.total_bytes = off;
+  return off <= ws_bytes;
+}
+
+size_t required_bytes(int B, int total_draft, int V) {
+  sv::Plan L;
+  if (!make_plan(B, total_draft, V, SIZE_MAX, L)) return 0;
+  return L.total_bytes > 0 ? L.total_bytes : kAlign;
 }
 
 bool filters_active(int V, int top_k, float top_p) {
@@ -80,10 +100,12 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
     if (top_k > SV_MAX_TOP_K) return SV_EUNSUPPORTED;
     return SV_EUNSUPPORTED;  // top-k / top-p path not in this build yet
   }
+  size_t dbytes;
+  long long rows_ll, cmax_ll, dmax_ll;
+  if (!data_bytes(B, total_draft, V, dbytes, rows_ll, cmax_ll, dmax_ll)) return SV_EUNSUPPORTED;
   sv::Plan L;
-  if (!make_plan(B, total_draft, V, L)) return SV_EINVAL;
   if (workspace == nullptr || ((uintptr_t)workspace % kAlign) != 0 ||
-      workspace_bytes < L.total_bytes)
+      !make_plan(B, total_draft, V, workspace_bytes, L))
     return SV_EWORKSPACE;
 
   const int es = esize_of(dtype);
@@ -101,20 +123,31 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
   P.K = (cu == nullptr) ? K : 0;
   P.V = V;
   P.total_draft = total_draft;
+  P.rows = total_draft + B;
   P.all_greedy = all_greedy ? 1 : 0;
   P.c = all_greedy ? 0.0f : (float)(1.4426950408889634074 / (double)temperature);
   P.nvec = vec ? V / n_per_vec : V;
-  P.chunks = L.chunks;
-  P.chunk_vecs = (P.nvec + L.chunks - 1) / L.chunks;
-  P.ntiles = L.ntiles;
-  P.tile_chunks = L.tile_chunks;
-  P.tiles_per_chunk = L.tiles_per_chunk;
+  P.chunks = (int)chunks_for(P.nvec);
+  P.dchunks = (P.nvec + sv::kDrawVecs - 1) / sv::kDrawVecs;
+  P.ntiles = P.dchunks * sv::kTilesPerDraw;
+  P.lag0 = sv::kDecideLag;
+  P.lag1 = sv::kDrawLag;
+  P.spin_limit = (diag != nullptr && diag->spin_limit > 0) ? diag->spin_limit : kDefaultSpinLimit;
   P.out_tokens = out_tokens;
   P.num_accepted = num_accepted;
   char* ws = static_cast<char*>(workspace);
+  P.slots = reinterpret_cast<unsigned long long*>(ws + L.off_slots);
+  P.tiles = reinterpret_cast<float*>(ws + L.off_tiles);
   P.jobs = reinterpret_cast<sv::Job*>(ws + L.off_jobs);
-  P.partials = reinterpret_cast<float4*>(ws + L.off_partials);
-  P.tile_sums = reinterpret_cast<float*>(ws + L.off_tiles);
+  P.job_ready = reinterpret_cast<int*>(ws + L.off_job_ready);
+  P.draw_done = reinterpret_cast<int*>(ws + L.off_draw_done);
+  P.seq_flags = reinterpret_cast<int*>(ws + L.off_seq_flags);
+  // the grid uses the chunk counts of the actual vector width
+  sv::Plan G = L;
+  G.chunks = P.chunks;
+  G.dchunks = P.dchunks;
+  G.blocks = (long long)P.rows * 2 * P.chunks + (long long)B * P.dchunks;
+  if (G.blocks > (long long)UINT32_MAX / sv::kThreads) return SV_EUNSUPPORTED;
   hipEvent_t* ev = nullptr;
   int nev = 0;
   if (diag != nullptr) {
@@ -127,8 +160,7 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
     ev = diag->stage_events;
     nev = diag->n_stage_events;
   }
-  L.any_sampling = !all_greedy;
-  const hipError_t err = sv::launch(dtype, vec, P, L, stream, ev, nev);
+  const hipError_t err = sv::launch(dtype, vec, P, G, stream, ev, nev);
   return err == hipSuccess ? SV_OK : SV_EHIP;
 }
 
@@ -151,9 +183,7 @@ const char* spec_verify_strerror(int code) {
 size_t spec_verify_workspace_bytes(int B, int total_draft_rows, int V, int top_k, float top_p) {
   (void)top_k;
   (void)top_p;
-  sv::Plan L;
-  if (!make_plan(B, total_draft_rows, V, L)) return 0;
-  return L.total_bytes;
+  return required_bytes(B, total_draft_rows, V);
 }
 
 int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
@@ -165,7 +195,7 @@ int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, hipStrea
 int spec_verify_num_stages(int top_k, float top_p) {
   (void)top_k;
   (void)top_p;
-  return 4;
+  return 1;
 }
 
 int spec_verify(const void* draft_logits, const void* target_logits, const int32_t* draft_tokens,

@@ -164,6 +164,62 @@ def test_large_magnitude_logits():
     _check(w, api="ragged", diag=True, tag="x300")
 
 
+def test_forced_sync_timeout_is_reported():
+    """A spin limit of one iteration, set from the host, makes blocks give up
+    waiting for their sibling chunks; each sequence then either matches the
+    oracle or reports SV_SEQ_SYNC_TIMEOUT. A following call with the default
+    limit on the same workspace is exact again (counters were cleared)."""
+    import speculative_decoding_verification_13_amd as sv
+    w = W.make(W.HEADLINE, B=16)
+    toks = draft_tokens_from_oracle(w)
+    ora = run_oracle(w, toks)
+    d = to_device(w, toks)
+    n_draft = int(w["cu_draft"][-1])
+    ws = sv.make_workspace(w["B"], n_draft, w["V"])
+    _say("[gpu] forced timeout spin_limit=1")
+    out, num = sv.spec_verify_ragged(d["draft"], d["target"], d["tokens"], d["uniforms"], d["cu"],
+                                     None, w["B"], w["V"], w["temperature"],
+                                     total_draft_rows=n_draft, workspace=ws,
+                                     diag={"spin_limit": 1})
+    num = num.cpu().numpy()
+    out = out.cpu().numpy()
+    cu = w["cu_draft"]
+    for b in range(w["B"]):
+        if num[b] == sv.SV_SEQ_SYNC_TIMEOUT:
+            continue
+        t0, t1 = cu[b] + b, cu[b + 1] + b + 1
+        if ora["margin"][b] > 1e-5:
+            assert num[b] == ora["num_accepted"][b]
+            assert np.array_equal(out[t0:t1], ora["out_tokens"][t0:t1])
+    _say(f"      timeouts={(num == sv.SV_SEQ_SYNC_TIMEOUT).sum()} of {w['B']}")
+    gpu = run_gpu(w, toks, api="ragged", dev=d)
+    rep = compare(w, toks, gpu, ora)
+    assert not rep["mismatches"]
+
+
+def test_workspace_reuse_across_calls_and_shapes():
+    """One workspace, sized for the largest call, serves calls of other shapes
+    and dtypes in a row (its counters return to zero after each call)."""
+    import speculative_decoding_verification_13_amd as sv
+    big = W.make(W.HEADLINE, B=8)
+    calls = (big, W.make(W.TINY), W.make("bf16_B32_K4_V32000", B=6, dtype="f16"),
+             W.make("bf16_B512_Kragged_V128256_halfgreedy", B=6), big)
+    n = max(sv.workspace_bytes(w["B"], int(w["cu_draft"][-1]), w["V"]) for w in calls)
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    for w in calls:
+        toks = draft_tokens_from_oracle(w)
+        ora = run_oracle(w, toks)
+        d = to_device(w, toks)
+        n_draft = int(w["cu_draft"][-1])
+        out, num = sv.spec_verify_ragged(d["draft"], d["target"], d["tokens"], d["uniforms"],
+                                         d["cu"], d["greedy"] if w["greedy"].any() else None,
+                                         w["B"], w["V"], w["temperature"],
+                                         total_draft_rows=n_draft, workspace=ws[: ws.numel()])
+        gpu = dict(out_tokens=out.cpu().numpy(), num_accepted=num.cpu().numpy())
+        rep = compare(w, toks, gpu, ora)
+        assert not rep["mismatches"], (w["name"], rep["mismatches"])
+
+
 def test_determinism_bitwise():
     w = W.make(W.HEADLINE, B=8)
     toks = draft_tokens_from_oracle(w)
