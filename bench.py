@@ -7,9 +7,10 @@ of the inputs rotate so that the 256 MB Infinity Cache cannot serve one step's
 rows from the previous step.
 
 Prints one JSON line: verified (sequence, position) rows per second, effective
-HBM bandwidth of the compulsory bytes, a roofline entry for the kernel (its
-algorithmic bytes over its HIP-event duration on the launch stream) and the CPU
-oracle timed on a bounded sample of the same workload.
+HBM bandwidth of the compulsory bytes, a roofline entry for the dominant kernel
+(the row-statistics pass: its algorithmic bytes over its HIP-event duration on
+the launch stream) and the CPU oracle timed on a bounded sample of the same
+workload.
 """
 
 import argparse
@@ -30,8 +31,8 @@ import workloads as W  # noqa: E402
 
 PEAK_HBM_GBPS = 8000.0
 METRIC = "verified rows/sec + effective HBM GB/s (% of ~8 TB/s), B=64 K=8 V=128256 bf16"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_verify_bf16_B64_K8_V128256_traffic.json")
-DOMINANT = "k_verify"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_stats_bf16_B64_K8_V128256_traffic.json")
+DOMINANT = "k_stats"
 
 
 class HipEvents:
@@ -163,12 +164,14 @@ def main():
                               total_draft_rows=n_draft, out_tokens=out, num_accepted=num,
                               workspace=ws, diag=diag)
 
-    # stage events on the launch stream: before and after the kernel, one pair per
-    # timed step (HIP events without the system-scope fence)
-    hev = HipEvents(2 * args.steps)
-    ev_pairs = [hev.handles[2 * k:2 * k + 2] for k in range(args.steps)]
+    # stage events on the launch stream: before the first kernel, between the
+    # two kernels and after the second, one triple per timed step (HIP events
+    # without the system-scope fence)
+    nst = sv.num_stages(top_k, top_p) + 1
+    hev = HipEvents(nst * args.steps)
+    ev_sets = [hev.handles[nst * k:nst * (k + 1)] for k in range(args.steps)]
     for k in range(args.warmup):
-        step(k, ev_pairs[k % len(ev_pairs)])
+        step(k, ev_sets[k % len(ev_sets)])
     torch.cuda.synchronize()
 
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -176,14 +179,27 @@ def main():
     t_wall = time.perf_counter()
     start.record()
     for k in range(args.steps):
-        step(k, ev_pairs[k])
+        step(k, ev_sets[k])
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
-    k1_ms = float(np.mean([hev.elapsed_ms(2 * k, 2 * k + 1) for k in range(args.steps)]))
+    stage_ms = [float(np.mean([hev.elapsed_ms(nst * k + i, nst * k + i + 1)
+                               for k in range(args.steps)])) for i in range(nst - 1)]
+    call_ms = float(np.mean([hev.elapsed_ms(nst * k, nst * k + nst - 1)
+                             for k in range(args.steps)]))
     hev.close()
+    k1_ms = stage_ms[0]
+
+    # the same steps without stage events (for the cost of the events themselves)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(args.steps):
+        step(k)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step_plain = start.elapsed_time(stop) / args.steps
 
     rows = int((w["Ks"] + 1).sum())
     comp = W.compulsory_bytes(w)
@@ -233,6 +249,9 @@ def main():
             "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
             "algorithmic_bytes_per_launch": algo_bytes_k1, "avg_launch_ms": k1_ms,
         },
+        "stage_ms": {"k_stats": stage_ms[0], "k_draw": stage_ms[1] if len(stage_ms) > 1 else None,
+                     "call": call_ms},
+        "ms_per_step_without_stage_events": ms_step_plain,
         "acceptance": {
             "mean_accepted": float(n_acc.mean()),
             "all_accepted_frac": float((n_acc == w["Ks"]).mean()),

@@ -48,7 +48,8 @@
  *
  * Errors: argument errors return a negative SV_E* code before any device work.
  * Data errors found on the device are reported per sequence in num_accepted
- * (SV_SEQ_*), with that sequence's out_tokens all -1.
+ * (SV_SEQ_*), with that sequence's out_tokens all -1 (for SV_SEQ_BAD_OFFSETS,
+ * whose rows cannot be located, out_tokens is left unwritten).
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H
@@ -74,8 +75,8 @@ typedef enum sv_dtype { SV_F32 = 0, SV_F16 = 1, SV_BF16 = 2 } sv_dtype;
                                 than spec_verify_workspace_bytes() */
 #define SV_EHIP (-4)         /* a HIP launch or event record failed */
 #define SV_EUNSUPPORTED (-5) /* valid request outside this build's limits
-                                (top_k above SV_MAX_TOP_K, or V above
-                                2,097,152 elements) */
+                                (top_k above SV_MAX_TOP_K, or a grid of more
+                                than 2^24 blocks) */
 
 /* Per-sequence codes written to num_accepted[b] instead of a count. */
 #define SV_SEQ_BAD_TOKEN (-1)   /* a draft id outside [0, V) */
@@ -83,9 +84,6 @@ typedef enum sv_dtype { SV_F32 = 0, SV_F16 = 1, SV_BF16 = 2 } sv_dtype;
                                    value (greedy: target rows only) */
 #define SV_SEQ_BAD_OFFSETS (-3) /* ragged offsets: cu[b] > cu[b+1], outside
                                    [0, total_draft_rows], or K_b > 64 */
-#define SV_SEQ_SYNC_TIMEOUT (-4) /* a bounded wait between the blocks that share
-                                    a row ran out (the row's blocks did not all
-                                    run); the sequence's outputs are not valid */
 
 #define SV_MAX_K 64
 #define SV_MAX_TOP_K 1024
@@ -99,12 +97,12 @@ size_t spec_verify_workspace_bytes(int B, int total_draft_rows, int V, int top_k
                                    float top_p);
 
 /* Zero-fill a workspace on `stream` (kernel fill, no memset node). A workspace
- * must be zero-filled once before its first use: the blocks of a call exchange
- * partial results through it, and a zero entry means "not yet published".
- * Every call returns the whole workspace to zero before it ends, so calls that
+ * must be zero-filled once before its first use: it holds per-sequence
+ * counters that must read zero when a call starts. Every call returns them to
+ * zero before it ends (also for sequences that report an error), so calls that
  * share one workspace may differ in B, K, V and dtype, as long as it is large
- * enough for each of them. After a call that reports SV_SEQ_SYNC_TIMEOUT or
- * SV_SEQ_BAD_OFFSETS for any sequence, zero-fill the workspace again. */
+ * enough for each of them. The rest of the workspace holds per-row partial
+ * results that each call writes before it reads them. */
 int spec_verify_workspace_init(void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
@@ -148,9 +146,9 @@ int spec_verify_ragged(const void* draft_logits, const void* target_logits,
  *   resid_Z      per sequence: the mass the final inverse CDF normalised by
  *                (residual mass at n, or the bonus row's mass)
  *   stage_events n_stage_events events recorded on `stream` before the first
- *                kernel and after each kernel of the call (for timing).
- *   spin_limit   bound of the wait between blocks of one row (0: default);
- *                a small value forces SV_SEQ_SYNC_TIMEOUT paths in tests. */
+ *                kernel and after each kernel of the call (for timing); with
+ *                two kernels, event 1 separates the row statistics pass from
+ *                the decision-and-draw pass. */
 typedef struct sv_diag {
   float* row_max_draft;
   float* row_logsum_draft;
@@ -160,7 +158,6 @@ typedef struct sv_diag {
   float* resid_Z;
   hipEvent_t* stage_events;
   int n_stage_events;
-  int spin_limit;
 } sv_diag;
 
 /* Number of kernels a call launches for these settings (stage events = this+1). */

@@ -1,5 +1,5 @@
 // C ABI of the verification library: argument checks, workspace layout and the
-// launch of the kernel in sv_verify.hip. Nothing here touches the device
+// launch of the kernels in sv_verify.hip. Nothing here touches the device
 // before every argument has been checked.
 #include <limits.h>
 #include <math.h>
@@ -13,34 +13,39 @@
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kMaxChunks = 512;         // decide() stages 2*chunks slots per position
-constexpr int kDefaultSpinLimit = 1 << 22;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int esize_of(int dtype) { return dtype == SV_F32 ? 4 : 2; }
 
-// Chunks per row for a given vector count per row.
-long long chunks_for(long long nvec) { return (nvec + sv::kChunkVecs - 1) / sv::kChunkVecs; }
+// Vectors per stats block for rows of nvec vectors: kChunkSteps batches, grown
+// so that no row has more than kMaxChunks chunks.
+long long chunk_vecs_for(long long nvec) {
+  const long long per = (long long)sv::kStepVecs * sv::kMaxChunks;
+  long long steps = (nvec + per - 1) / per;
+  if (steps < sv::kChunkSteps) steps = sv::kChunkSteps;
+  return steps * sv::kStepVecs;
+}
 
 // Workspace layout (per call):
-//   draw_done[B], seq_flags[B], job_ready[B], jobs[B]   per sequence
-//   slots[rows * 2 * cmax]          64-bit chunk partials (0 = unpublished)
-//   tiles[B * dmax * tiles/draw]    draw-weight tile sums
-// Every call returns every entry it wrote to zero before it ends, so the
-// layout may differ from call to call. The regions are sized for the scalar
-// path (one element per vector), the largest chunk counts of any dtype.
+//   draw_done[B]                           per-sequence counters, zero between calls
+//   slots[(total_draft + rows) * cmax]     64-bit chunk partials of every row
+//   tiles[B * dmax * tiles per draw block] draw-weight tile sums
+// Only the counters must be zero when a call starts, and every call leaves
+// them zero, so the layout may differ from call to call. The regions are sized
+// for the scalar path (one element per vector), which has the most chunks:
+// a row of nvec <= V vectors never has more than cmax chunks.
 bool data_bytes(int B, int total_draft, int V, size_t& bytes, long long& rows, long long& cmax,
                 long long& dmax) {
   if (B < 0 || total_draft < 0 || V < 1) return false;
   rows = (long long)total_draft + B;
   if (rows > INT_MAX) return false;
-  cmax = chunks_for(V);
-  if (cmax > kMaxChunks) return false;
+  const long long base = (long long)sv::kStepVecs * sv::kChunkSteps;
+  cmax = ((long long)V + base - 1) / base;
+  if (cmax > sv::kMaxChunks) cmax = sv::kMaxChunks;
   dmax = ((long long)V + sv::kDrawVecs - 1) / sv::kDrawVecs;
-  bytes = 3 * align_up((size_t)B * 4) + align_up((size_t)rows * 2 * (size_t)cmax * 8) +
-          align_up((size_t)B * (size_t)dmax * sv::kTilesPerDraw * 4) +
-          align_up((size_t)B * sizeof(sv::Job));
+  bytes = align_up((size_t)B * 4) + align_up((size_t)(total_draft + rows) * (size_t)cmax * 8) +
+          align_up((size_t)B * (size_t)dmax * sv::kTilesPerDraw * 4);
   return true;
 }
 
@@ -48,20 +53,11 @@ bool make_plan(int B, int total_draft, int V, size_t ws_bytes, sv::Plan& L) {
   size_t dbytes;
   long long rows, cmax, dmax;
   if (!data_bytes(B, total_draft, V, dbytes, rows, cmax, dmax)) return false;
-  L.chunks = (int)cmax;
-  L.dchunks = (int)dmax;
-  L.blocks = rows * 2 * cmax + (long long)B * dmax;
   size_t off = 0;
   L.off_draw_done = off;
   off += align_up((size_t)B * 4);
-  L.off_seq_flags = off;
-  off += align_up((size_t)B * 4);
-  L.off_job_ready = off;
-  off += align_up((size_t)B * 4);
-  L.off_jobs = off;
-  off += align_up((size_t)B * sizeof(sv::Job));
   L.off_slots = off;
-  off += align_up((size_t)rows * 2 * (size_t)cmax * 8);
+  off += align_up((size_t)(total_draft + rows) * (size_t)cmax * 8);
   L.off_tiles = off;
   off += align_up((size_t)B * (size_t)dmax * sv::kTilesPerDraw * 4);
   L.total_bytes = off;
@@ -127,27 +123,26 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
   P.all_greedy = all_greedy ? 1 : 0;
   P.c = all_greedy ? 0.0f : (float)(1.4426950408889634074 / (double)temperature);
   P.nvec = vec ? V / n_per_vec : V;
-  P.chunks = (int)chunks_for(P.nvec);
+  P.chunk_vecs = (int)chunk_vecs_for(P.nvec);
+  P.chunks = (P.nvec + P.chunk_vecs - 1) / P.chunk_vecs;
   P.dchunks = (P.nvec + sv::kDrawVecs - 1) / sv::kDrawVecs;
   P.ntiles = P.dchunks * sv::kTilesPerDraw;
-  P.lag0 = sv::kDecideLag;
-  P.lag1 = sv::kDrawLag;
-  P.spin_limit = (diag != nullptr && diag->spin_limit > 0) ? diag->spin_limit : kDefaultSpinLimit;
+  // greedy-only calls skip the draft rows
+  P.stats_block0 = all_greedy ? (long long)total_draft * P.chunks : 0;
   P.out_tokens = out_tokens;
   P.num_accepted = num_accepted;
   char* ws = static_cast<char*>(workspace);
   P.slots = reinterpret_cast<unsigned long long*>(ws + L.off_slots);
   P.tiles = reinterpret_cast<float*>(ws + L.off_tiles);
-  P.jobs = reinterpret_cast<sv::Job*>(ws + L.off_jobs);
-  P.job_ready = reinterpret_cast<int*>(ws + L.off_job_ready);
   P.draw_done = reinterpret_cast<int*>(ws + L.off_draw_done);
-  P.seq_flags = reinterpret_cast<int*>(ws + L.off_seq_flags);
-  // the grid uses the chunk counts of the actual vector width
-  sv::Plan G = L;
-  G.chunks = P.chunks;
-  G.dchunks = P.dchunks;
-  G.blocks = (long long)P.rows * 2 * P.chunks + (long long)B * P.dchunks;
-  if (G.blocks > (long long)UINT32_MAX / sv::kThreads) return SV_EUNSUPPORTED;
+  L.chunks = P.chunks;
+  L.chunk_vecs = P.chunk_vecs;
+  L.dchunks = P.dchunks;
+  L.stats_blocks = ((long long)total_draft + P.rows) * P.chunks - P.stats_block0;
+  L.draw_blocks = (long long)B * P.dchunks;
+  if (L.stats_blocks > (long long)UINT32_MAX / sv::kThreads ||
+      L.draw_blocks > (long long)UINT32_MAX / sv::kThreads)
+    return SV_EUNSUPPORTED;
   hipEvent_t* ev = nullptr;
   int nev = 0;
   if (diag != nullptr) {
@@ -160,7 +155,7 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
     ev = diag->stage_events;
     nev = diag->n_stage_events;
   }
-  const hipError_t err = sv::launch(dtype, vec, P, G, stream, ev, nev);
+  const hipError_t err = sv::launch(dtype, vec, P, L, stream, ev, nev);
   return err == hipSuccess ? SV_OK : SV_EHIP;
 }
 
@@ -195,7 +190,7 @@ int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, hipStrea
 int spec_verify_num_stages(int top_k, float top_p) {
   (void)top_k;
   (void)top_p;
-  return 1;
+  return 2;
 }
 
 int spec_verify(const void* draft_logits, const void* target_logits, const int32_t* draft_tokens,

@@ -1,4 +1,4 @@
-// Internal interface between the C ABI (sv_api.hip) and the kernel (sv_verify.hip).
+// Internal interface between the C ABI (sv_api.hip) and the kernels (sv_verify.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -12,21 +12,20 @@ namespace sv {
 constexpr int kThreads = 256;             // threads per block (4 waves)
 constexpr int kBatch = 4;                 // 16-byte vectors per thread in flight per batch
 constexpr int kTileVecs = kThreads;       // draw tile = one vector per thread
-constexpr int kChunkVecs = 16 * kTileVecs;  // vectors of one row per stats block (64 KB)
-constexpr int kDrawVecs = kBatch * kTileVecs;  // vectors of each row per draw block
+constexpr int kStepVecs = kBatch * kThreads;  // vectors of a row one batch covers
+constexpr int kDrawVecs = kStepVecs;      // vectors of each row per draw block
 constexpr int kTilesPerDraw = kDrawVecs / kTileVecs;
-constexpr int kDecideLag = 16;            // draw chunk 0 of sequence b (which decides)
-                                          // follows the stats of sequence b + kDecideLag
-constexpr int kDrawLag = 20;              // its other draw chunks follow the stats of
-                                          // sequence b + kDrawLag
-
-// Per-sequence status bits raised by any block (cleared when the sequence ends).
-enum { kSeqFlagTimeout = 1 };
+#ifndef SV_CHUNK_STEPS
+#define SV_CHUNK_STEPS 4
+#endif
+constexpr int kChunkSteps = SV_CHUNK_STEPS;  // batches per stats block (64 KB of bf16)
+constexpr int kMaxChunks = 64;            // stats chunks per row (larger rows take
+                                          // larger chunks)
 
 enum { kJobNone = 0, kJobResidual = 1, kJobBonus = 2 };
 
-// Final draw of one sequence, published by its deciding block.
-struct alignas(16) Job {
+// Final draw of one sequence (every draw block of the sequence derives it).
+struct Job {
   int mode;      // kJobNone / kJobResidual / kJobBonus
   int n;         // accepted drafts = position of the draw
   int prow;      // target row of position n
@@ -34,7 +33,6 @@ struct alignas(16) Job {
   float Rq, invSq, Rp, invSp;  // references R = fp32(max*c) and 1/S of both rows
   float u;       // the resample-or-bonus uniform
   int out_idx;   // output slot of the drawn token
-  int pad[6];
 };
 
 // Device pointers of the optional side outputs.
@@ -58,31 +56,26 @@ struct Params {
   int all_greedy;
   float c;                 // log2(e) / temperature (0 if all greedy)
   int chunks;              // stats blocks per row
+  int chunk_vecs;          // vectors per stats block (a multiple of kStepVecs)
   int dchunks;             // draw blocks per sequence
   int nvec;                // vectors (or elements, scalar path) per row
   int ntiles;              // draw tiles per row = dchunks * kTilesPerDraw
-  int lag0, lag1;          // draw chunk 0 / other chunks of sequence b follow the
-                           // stats blocks of sequence b + lag0 / b + lag1
-  int spin_limit;          // bound of every wait (iterations)
+  long long stats_block0;  // first stats block (skips draft rows when all greedy)
   int32_t* out_tokens;
   int32_t* num_accepted;
-  // Chunk partial of (target row, draft|target, chunk), 64-bit, 0 = not yet
-  // published: sampling (max, sum) floats; greedy (max, tagged argmax).
-  unsigned long long* slots;  // [rows * 2 * chunks]
+  // Chunk partials, 64-bit: sampling (max, sum) floats; greedy (max value,
+  // argmax and bad flag). Draft rows first, then target rows, chunks innermost.
+  unsigned long long* slots;  // [(total_draft + rows) * chunks]
   float* tiles;            // [B * ntiles] draw-weight tile sums
-  Job* jobs;               // [B]
-  int* job_ready;          // [B]
-  int* draw_done;          // [B] draw blocks finished per sequence
-  int* seq_flags;          // [B]
+  int* draw_done;          // [B] draw blocks finished per sequence (zero between calls)
   DiagPtrs diag;
 };
 
 // Grid size and workspace offsets of one call.
 struct Plan {
-  int chunks, dchunks;
-  long long blocks;
-  size_t off_slots, off_tiles, off_jobs, off_job_ready, off_draw_done, off_seq_flags,
-      total_bytes;
+  int chunks, chunk_vecs, dchunks;
+  long long stats_blocks, draw_blocks;
+  size_t off_slots, off_tiles, off_draw_done, total_bytes;
 };
 
 hipError_t launch(int dtype, bool vec, const Params& P, const Plan& L, hipStream_t s,

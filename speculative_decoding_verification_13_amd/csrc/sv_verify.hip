@@ -1,26 +1,20 @@
-// The verification step as one HIP kernel for gfx950.
+// The verification step as two HIP kernels for gfx950.
 //
-// Grid: step s holds the stats blocks of sequence s (one per (row, V-chunk)),
-// then draw chunk 0 of sequence s - lag0, then the other draw chunks of
-// sequence s - lag1 (lag0 < lag1); the draws of the last sequences close the
-// grid. Blocks are dispatched in index order, so when a sequence's draw chunk
-// 0 starts, its stats blocks have long finished; when its other chunks start,
-// chunk 0 has published the decision; and the rows being re-read were read
-// recently enough to be served again from the last-level cache.
+// k_stats streams every logit row once. Each block takes one chunk of one row
+// and writes one 64-bit partial: for a sampling row the chunk maximum m and the
+// sum of 2^(l*c - R) with R = fp32(m*c); for a greedy row the chunk argmax
+// (lowest id on ties) and whether the chunk holds NaN or +inf. Blocks never
+// wait on each other; the kernel boundary publishes the partials.
 //
-// Stats block (never waits): max m and sum 2^(l*c - R) of its chunk of one row
-// (R = fp32(m*c)), or the chunk argmax for greedy sequences, published with one
-// 64-bit agent-scope store into a slot that is zero while unpublished. It keeps
-// no counter and needs no drain, so it retires as soon as its store is issued.
-//
-// Draw chunk 0 of sequence b decides: it reads (bounded wait) the slots of
-// every row of b, merges them in chunk order, clears them, forms
-// r_i = p_i(x_i)/q_i(x_i), tests u_i < r_i, finds the first rejection n, writes
-// the accepted prefix and publishes the job of the final draw (residual at n,
-// or the bonus row). Every draw chunk then sums the draw weights
-// (max(0, p_n - q_n), or p_K) of the tiles of its part of row pair n and
-// publishes them; the last one scans the sums for u*Z, re-reads that one tile,
-// scans it, writes the drawn token and returns the workspace to zero.
+// k_draw runs one group of blocks per sequence, each group covering the vocabulary
+// of one row pair in slices. Every block of the group merges the row partials
+// of its sequence in chunk order, forms r_i = p_i(x_i)/q_i(x_i), tests
+// u_i < r_i and finds the first rejection n itself (the same arithmetic in
+// every block gives the same decision, so no block waits for another). Each
+// block then sums the draw weights (max(0, p_n - q_n), or p_K for the bonus)
+// over the tiles of its slice and publishes the sums; the last block of the
+// group to finish scans the tile sums for u*Z, re-reads the one tile that
+// holds the crossing, scans it and writes the drawn token.
 //
 // Pages (by title, section): aivaro.ru answer 289 "Как работает speculative
 // decoding на уровне логитов, а не токенов?" s.5 step 3, s.6, s.9 (ratio test,
@@ -39,7 +33,7 @@ namespace sv {
 
 namespace {
 
-constexpr int kPollSlots = 2048;  // LDS staging of polled slots per group of positions
+constexpr int kCuLds = 2048;  // offsets staged in LDS for the row -> sequence search
 
 __device__ __forceinline__ bool seq_bounds(const Params& P, int b, int& d0, int& kb) {
   if (P.cu == nullptr) {
@@ -55,31 +49,11 @@ __device__ __forceinline__ bool seq_bounds(const Params& P, int b, int& d0, int&
   return true;
 }
 
-// Sequence owning target row g: the largest b with cu[b] + b <= g.
-__device__ __forceinline__ int seq_of_target_row(const Params& P, int g) {
-  if (P.cu == nullptr) return g / (P.K + 1);
-  int lo = 0, hi = P.B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if ((long long)P.cu[mid] + mid <= (long long)g) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
-}
-
 __device__ __forceinline__ bool seq_greedy(const Params& P, int b) {
   return P.all_greedy || (P.greedy != nullptr && P.greedy[b] != 0);
 }
 
-// ---- 64-bit slots: zero means "not published" ----
-__device__ __forceinline__ void pub_u64(unsigned long long* p, unsigned long long v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ unsigned long long obs_u64(unsigned long long* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// (max, sum) of a sampling chunk: never all-zero bits (a +0 maximum brings a
-// term 2^0 = 1 into the sum; NaN is stored canonical).
+// (max, sum) of a sampling chunk; NaN is stored canonical.
 __device__ __forceinline__ unsigned long long pack_ms(float m, float s) {
   if (m != m) m = __builtin_nanf("");
   return ((unsigned long long)__float_as_uint(s) << 32) | __float_as_uint(m);
@@ -88,16 +62,16 @@ __device__ __forceinline__ void unpack_ms(unsigned long long v, float& m, float&
   m = __uint_as_float((unsigned)v);
   s = __uint_as_float((unsigned)(v >> 32));
 }
-// (max value, argmax, bad flag) of a greedy chunk: the high word has bit 31 set.
+// (max value, argmax, bad flag) of a greedy chunk.
 __device__ __forceinline__ unsigned long long pack_am(float v, int idx, int bad) {
-  const unsigned hi = 0x80000000u | (bad ? 0x40000000u : 0u) | ((unsigned)idx & 0x3fffffffu);
+  const unsigned hi = (bad ? 0x80000000u : 0u) | ((unsigned)idx & 0x7fffffffu);
   return ((unsigned long long)hi << 32) | __float_as_uint(v);
 }
 __device__ __forceinline__ void unpack_am(unsigned long long p, float& v, int& idx, int& bad) {
   v = __uint_as_float((unsigned)p);
   const unsigned hi = (unsigned)(p >> 32);
-  idx = (int)(hi & 0x3fffffffu);
-  bad = (hi & 0x40000000u) ? 1 : 0;
+  idx = (int)(hi & 0x7fffffffu);
+  bad = (hi & 0x80000000u) ? 1 : 0;
 }
 
 // One 16-byte vector (or one element on the scalar path) of a row.
@@ -187,29 +161,6 @@ __device__ __forceinline__ int find_tile(const float* ts, int ntiles, float u, f
   return tile;
 }
 
-// ------------------------------------------------------------- grid mapping
-// Stats blocks of sequences [0, s), s <= B: two rows (draft, target) per target
-// row, `chunks` blocks per row (draft rows that do not exist stay idle).
-// The grid was sized from total_draft on the host, so offsets are clamped into
-// [0, total_draft] here and cu[B] is never read: the mapping always covers
-// exactly the launched blocks (malformed offsets only idle some blocks).
-__device__ __forceinline__ long long stats_before(const Params& P, int s) {
-  long long t;
-  if (P.cu == nullptr) {
-    t = (long long)s * (P.K + 1);
-  } else {
-    const long long c = (s >= P.B) ? P.total_draft : min(max(P.cu[s], 0), P.total_draft);
-    t = c + s;
-  }
-  return 2LL * P.chunks * t;
-}
-// First block of grid step s in [0, B + lag1]: stats of sequences < min(s, B),
-// draw chunk 0 of sequences < s - lag0, other draw chunks of sequences < s - lag1.
-__device__ __forceinline__ long long step_start(const Params& P, int s) {
-  return stats_before(P, min(s, P.B)) + min(max(0, s - P.lag0), P.B) +
-         (long long)(P.dchunks - 1) * min(max(0, s - P.lag1), P.B);
-}
-
 // This thread's vector of tile t (= vector t*kTileVecs + thread) of both rows.
 template <int DT, bool VEC>
 __device__ __forceinline__ bool tile_vector(const Params& P, const Job& j, int t, float* fp,
@@ -282,126 +233,126 @@ __device__ int pick(const Params& P, int b, Job j, float& Zout) {
   return tok;
 }
 
-// Per-sequence decision state, kept in LDS by the deciding block.
-struct SeqState {
-  float m[2][SV_MAX_K + 1];  // merged row maxima (draft, target)
+// Decision state of one sequence, in LDS.
+struct Dec {
+  float m[2][SV_MAX_K + 1];  // merged row maxima (draft, target) per position
   float s[2][SV_MAX_K + 1];  // merged sums 2^(l*c - R)
-  int am[SV_MAX_K + 1];      // greedy argmax of target rows
-  int bad[SV_MAX_K + 1];     // row not usable
-  unsigned long long poll[kPollSlots];
-  int flags;                 // 1 bad token, 2 bad row, 4 wait timed out
+  int flags;                 // 1 bad token, 2 bad row
   unsigned long long rej;    // ballot of rejected draft positions
-  Job job;
 };
 
-// Decision of sequence b (whole block): reads and clears the slots of its rows,
-// writes the accepted prefix and the side outputs, and returns the job of the
-// final draw in S.job (published for the other draw chunks when sampling).
+// Merge the chunk partials of one position's rows in chunk order (loads issued
+// eight chunks at a time so their round trips overlap).
+__device__ __forceinline__ void merge_sampling(const unsigned long long* dsl,
+                                               const unsigned long long* tsl, bool with_draft,
+                                               int C, float c, float& mq, float& sq, float& mp,
+                                               float& sp) {
+  constexpr int G = 8;
+  for (int k0 = 0; k0 < C; k0 += G) {
+    unsigned long long dv[G], tv[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const bool in = k0 + g < C;
+      tv[g] = in ? tsl[k0 + g] : 0ull;
+      dv[g] = (in && with_draft) ? dsl[k0 + g] : 0ull;
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (k0 + g < C) {
+        float m, s;
+        if (with_draft) {
+          unpack_ms(dv[g], m, s);
+          merge_ms(mq, sq, m, s, c);
+        }
+        unpack_ms(tv[g], m, s);
+        merge_ms(mp, sp, m, s, c);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void merge_greedy(const unsigned long long* tsl, int C, float& v,
+                                             int& idx, int& bad) {
+  constexpr int G = 8;
+  for (int k0 = 0; k0 < C; k0 += G) {
+    unsigned long long tv[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) tv[g] = (k0 + g < C) ? tsl[k0 + g] : 0ull;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (k0 + g < C) {
+        float cv;
+        int ci, cb;
+        unpack_am(tv[g], cv, ci, cb);
+        argmax_merge(v, idx, cv, ci);
+        bad |= cb;
+      }
+    }
+  }
+}
+
+// Decision of sequence b (whole block; thread i owns position i). Every block
+// of the sequence computes it with the same arithmetic and so reaches the same
+// result; only the writer block stores the outputs it fixes: the accepted
+// prefix and -1 after it, the side outputs, and num_accepted when nothing is
+// drawn. Returns the job of the final draw (kJobNone when there is none).
 template <int DT>
-__device__ void decide(const Params& P, int b, int d0, int kb, bool greedy, SeqState& S) {
+__device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool writer, Dec& S) {
   const int tid = threadIdx.x;
   const int t0 = d0 + b;
   const bool active = tid <= kb;
   const bool is_draft = tid < kb;
   const float c = P.c;
   const int C = P.chunks;
-  if (tid == 0) {
-    S.flags = 0;
-    S.rej = 0ull;
-  }
-  // inputs of the ratio test: the token and its uniform now, its logits once
-  // the token is known (issued before the slot wait so the trips overlap)
+  if (tid == 0) S.flags = 0;
   int x = -1;
   float u = 1.f;
   if (is_draft) {
     x = P.tokens[d0 + tid];
     if (!greedy) u = P.uniforms[t0 + tid];
   }
-  // Read, merge (chunk order) and clear the slots, a group of positions at a time.
-  const int per_pos = 2 * C;
-  const int group = max(1, kPollSlots / per_pos);
-  int timed_out = 0;
-  for (int g0 = 0; g0 <= kb; g0 += group) {
-    const int g1 = min(kb + 1, g0 + group);
-    const int nslot = (g1 - g0) * per_pos;
-    __syncthreads();
-    for (int k = tid; k < nslot; k += kThreads) {
-      const int pos = g0 + k / per_pos;
-      const int which = (k % per_pos) / C;  // 0 draft row, 1 target row
-      unsigned long long v = 0ull;
-      if (which == 1 || (!greedy && pos < kb)) {
-        unsigned long long* sl = P.slots + (size_t)(t0 + pos) * per_pos + (k % per_pos);
-        int spins = 0;
-        while ((v = obs_u64(sl)) == 0ull) {
-          if (++spins > P.spin_limit) {
-            timed_out = 1;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(2);
-        }
-        pub_u64(sl, 0ull);
-      }
-      S.poll[k] = v;
-    }
-    __syncthreads();
-    if (tid >= g0 && tid < g1) {
-      const unsigned long long* mine = S.poll + (tid - g0) * per_pos;
-      if (greedy) {
-        float gv = kNegInf;
-        int gi = INT_MAX, gbad = 0;
-        for (int k = 0; k < C; ++k) {
-          float v;
-          int idx, bad;
-          unpack_am(mine[C + k], v, idx, bad);
-          argmax_merge(gv, gi, v, idx);
-          gbad |= bad;
-        }
-        S.m[1][tid] = gv;
-        S.s[1][tid] = 0.f;
-        S.am[tid] = gi;
-        S.bad[tid] = gbad || gv == kNegInf;
-      } else {
-        float mq = kNegInf, sq = 0.f, mp = kNegInf, sp = 0.f;
-        for (int k = 0; k < C; ++k) {
-          float m, s;
-          if (is_draft) {
-            unpack_ms(mine[k], m, s);
-            merge_ms(mq, sq, m, s, c);
-          }
-          unpack_ms(mine[C + k], m, s);
-          merge_ms(mp, sp, m, s, c);
-        }
-        S.m[0][tid] = mq;
-        S.s[0][tid] = sq;
-        S.m[1][tid] = mp;
-        S.s[1][tid] = sp;
-        bool ok = __builtin_isfinite(mp) && sp > 0.f && __builtin_isfinite(sp);
-        if (is_draft) ok = ok && __builtin_isfinite(mq) && sq > 0.f && __builtin_isfinite(sq);
-        S.bad[tid] = !ok;
-      }
-    }
-  }
-  if (timed_out) atomicOr(&S.flags, 4);
-  __syncthreads();
+  const float u_draw = greedy ? 0.f : P.uniforms[t0 + kb];
   const bool tok_ok = !is_draft || (x >= 0 && x < P.V);
+  // logits at the draft token (issued before the partials are merged)
+  float lq = 0.f, lp = 0.f;
+  if (is_draft && !greedy) {
+    const int xs = tok_ok ? x : 0;
+    lq = load_elem<DT>(P.draft, (size_t)(d0 + tid) * P.V + xs);
+    lp = load_elem<DT>(P.target, (size_t)(t0 + tid) * P.V + xs);
+  }
+  float mq = kNegInf, sq = 0.f, mp = kNegInf, sp = 0.f;
+  int am = INT_MAX;
+  bool bad = false;
+  if (active) {
+    const unsigned long long* tsl = P.slots + (size_t)(P.total_draft + t0 + tid) * C;
+    if (greedy) {
+      int gbad = 0;
+      merge_greedy(tsl, C, mp, am, gbad);
+      bad = gbad || mp == kNegInf;
+    } else {
+      merge_sampling(P.slots + (size_t)(d0 + tid) * C, tsl, is_draft, C, c, mq, sq, mp, sp);
+      bool ok = __builtin_isfinite(mp) && sp > 0.f && __builtin_isfinite(sp);
+      if (is_draft) ok = ok && __builtin_isfinite(mq) && sq > 0.f && __builtin_isfinite(sq);
+      bad = !ok;
+    }
+    S.m[0][tid] = mq;
+    S.s[0][tid] = sq;
+    S.m[1][tid] = mp;
+    S.s[1][tid] = sp;
+    if (bad) atomicOr(&S.flags, 2);
+    if (!tok_ok) atomicOr(&S.flags, 1);
+  }
   bool acc = false;
   float ratio = __builtin_nanf("");
-  if (active) {
-    const bool row_ok = !S.bad[tid];
-    if (!row_ok) atomicOr(&S.flags, 2);
-    if (!tok_ok) atomicOr(&S.flags, 1);
-    if (is_draft && tok_ok && row_ok) {
-      if (greedy) {
-        acc = S.am[tid] == x;
-      } else {
-        // r = p(x)/q(x) = 2^((lp*c - Rp) - (lq*c - Rq)) * Sq / Sp
-        const float lq = load_elem<DT>(P.draft, (size_t)(d0 + tid) * P.V + x);
-        const float lp = load_elem<DT>(P.target, (size_t)(t0 + tid) * P.V + x);
-        const float ep = fmaf(lp, c, -ref_of(S.m[1][tid], c));
-        const float eq = fmaf(lq, c, -ref_of(S.m[0][tid], c));
-        ratio = fast_exp2(ep - eq) * (S.s[0][tid] / S.s[1][tid]);
-        acc = u < ratio;  // strict: u == r rejects
-      }
+  if (is_draft && tok_ok && !bad) {
+    if (greedy) {
+      acc = am == x;
+    } else {
+      // r = p(x)/q(x) = 2^((lp*c - Rp) - (lq*c - Rq)) * Sq / Sp
+      const float ep = fmaf(lp, c, -ref_of(mp, c));
+      const float eq = fmaf(lq, c, -ref_of(mq, c));
+      ratio = fast_exp2(ep - eq) * (sq / sp);
+      acc = u < ratio;  // strict: u == r rejects
     }
   }
   if (tid < kWave) {
@@ -410,102 +361,101 @@ __device__ void decide(const Params& P, int b, int d0, int kb, bool greedy, SeqS
   }
   __syncthreads();
   const int sf = S.flags;
-  const int code = (sf & 1) ? SV_SEQ_BAD_TOKEN
-                            : ((sf & 2) ? SV_SEQ_BAD_ROW : ((sf & 4) ? SV_SEQ_SYNC_TIMEOUT : 0));
+  const int code = (sf & 1) ? SV_SEQ_BAD_TOKEN : ((sf & 2) ? SV_SEQ_BAD_ROW : 0);
   const int n = S.rej ? (__ffsll(S.rej) - 1) : kb;
   const bool draws = code == 0 && !greedy;
 
-  // outputs: slot n of a drawing sequence belongs to the draw chunks
-  if (active && !(draws && tid == n)) {
-    int tok = -1;
-    if (code == 0) {
-      if (tid < n) tok = x;
-      else if (tid == n) tok = S.am[n];
+  if (writer) {
+    // slot n of a drawing sequence is written by the block that draws
+    if (active && !(draws && tid == n)) {
+      int tok = -1;
+      if (code == 0) {
+        if (tid < n) tok = x;
+        else if (tid == n) tok = am;
+      }
+      P.out_tokens[t0 + tid] = tok;
     }
-    P.out_tokens[t0 + tid] = tok;
-  }
-  const float kLn2 = 0.69314718055994531f;
-  const float nan = __builtin_nanf("");
-  if (active) {
-    const float mp = S.m[1][tid], sp = S.s[1][tid];
-    if (P.diag.row_max_target) P.diag.row_max_target[t0 + tid] = mp;
-    if (P.diag.row_logsum_target)
-      P.diag.row_logsum_target[t0 + tid] =
-          greedy ? nan : (__log2f(sp) + fmaf(-mp, c, ref_of(mp, c))) * kLn2;
-    if (is_draft) {
-      const float mq = S.m[0][tid], sq = S.s[0][tid];
-      if (P.diag.row_max_draft) P.diag.row_max_draft[d0 + tid] = greedy ? nan : mq;
-      if (P.diag.row_logsum_draft)
-        P.diag.row_logsum_draft[d0 + tid] =
-            greedy ? nan : (__log2f(sq) + fmaf(-mq, c, ref_of(mq, c))) * kLn2;
-      if (P.diag.ratio) P.diag.ratio[d0 + tid] = ratio;
+    const float kLn2 = 0.69314718055994531f;
+    const float nan = __builtin_nanf("");
+    if (active) {
+      if (P.diag.row_max_target) P.diag.row_max_target[t0 + tid] = mp;
+      if (P.diag.row_logsum_target)
+        P.diag.row_logsum_target[t0 + tid] =
+            greedy ? nan : (__log2f(sp) + fmaf(-mp, c, ref_of(mp, c))) * kLn2;
+      if (is_draft) {
+        if (P.diag.row_max_draft) P.diag.row_max_draft[d0 + tid] = greedy ? nan : mq;
+        if (P.diag.row_logsum_draft)
+          P.diag.row_logsum_draft[d0 + tid] =
+              greedy ? nan : (__log2f(sq) + fmaf(-mq, c, ref_of(mq, c))) * kLn2;
+        if (P.diag.ratio) P.diag.ratio[d0 + tid] = ratio;
+      }
     }
-  }
-  if (tid == 0) {
-    if (!draws) {
+    if (tid == 0 && !draws) {
       P.num_accepted[b] = code ? code : n;
       if (P.diag.resid_Z) P.diag.resid_Z[b] = nan;
     }
-    Job j;
-    j.mode = draws ? (n < kb ? kJobResidual : kJobBonus) : kJobNone;
-    j.n = n;
-    j.prow = t0 + n;
-    j.qrow = d0 + n;
-    j.Rq = ref_of(S.m[0][n], c);
-    j.invSq = 1.0f / S.s[0][n];
-    j.Rp = ref_of(S.m[1][n], c);
-    j.invSp = 1.0f / S.s[1][n];
-    j.u = draws ? P.uniforms[t0 + kb] : 0.f;
-    j.out_idx = t0 + n;
-    S.job = j;
-    if (!greedy) {
-      int* q = reinterpret_cast<int*>(P.jobs + b);
-      pub_i(q, j.mode);
-      pub_i(q + 1, j.n);
-      pub_i(q + 2, j.prow);
-      pub_i(q + 3, j.qrow);
-      pub_f(reinterpret_cast<float*>(q + 4), j.Rq);
-      pub_f(reinterpret_cast<float*>(q + 5), j.invSq);
-      pub_f(reinterpret_cast<float*>(q + 6), j.Rp);
-      pub_f(reinterpret_cast<float*>(q + 7), j.invSp);
-      pub_f(reinterpret_cast<float*>(q + 8), j.u);
-      pub_i(q + 9, j.out_idx);
-      drain_stores();
-      pub_i(P.job_ready + b, 1);
-    }
   }
-  __syncthreads();
+  Job j;
+  j.mode = draws ? (n < kb ? kJobResidual : kJobBonus) : kJobNone;
+  j.n = n;
+  j.prow = t0 + n;
+  j.qrow = d0 + n;
+  j.Rq = ref_of(S.m[0][n], c);
+  j.invSq = 1.0f / S.s[0][n];
+  j.Rp = ref_of(S.m[1][n], c);
+  j.invSp = 1.0f / S.s[1][n];
+  j.u = u_draw;
+  j.out_idx = t0 + n;
+  return j;
 }
 
-// Bounded wait (one thread) until *flag != 0. Returns false on timeout.
-__device__ __forceinline__ bool wait_flag(const Params& P, const int* flag) {
-  int spins = 0;
-  while (obs_i(flag) == 0) {
-    if (++spins > P.spin_limit) return false;
-    __builtin_amdgcn_s_sleep(8);
+// Sequence of a draft row (is_target false) or target row: the largest b with
+// cu[b] <= row, or cu[b] + b <= row. Whole block (stages cu in LDS).
+__device__ int row_seq(const Params& P, int row, bool is_target, int* s_cu) {
+  if (P.cu == nullptr) return is_target ? row / (P.K + 1) : row / P.K;
+  const bool staged = P.B <= kCuLds;
+  if (staged) {
+    for (int k = threadIdx.x; k < P.B; k += kThreads) s_cu[k] = P.cu[k];
+    __syncthreads();
   }
-  compiler_fence();
-  return true;
+  const int* cu = staged ? s_cu : P.cu;
+  int lo = 0, hi = P.B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    const long long key = (long long)cu[mid] + (is_target ? mid : 0);
+    if (key <= (long long)row) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
 }
 
-// ----------------------------------------------------------------- stats block
+}  // namespace
+
+// ------------------------------------------------------------------ k_stats
+// Block g (after the offset stats_block0) covers chunk g % chunks of unit
+// g / chunks: draft row u for u < total_draft, else target row u - total_draft.
+// Its partial goes to slots[g].
 template <int DT, bool VEC>
-__device__ void stats_block(const Params& P, int b, int d0, int kb, int local, int ch) {
+__global__ __launch_bounds__(kThreads) void k_stats(const Params P) {
   using Vc = Vec<DT, VEC>;
   constexpr int N = Vc::N;
   __shared__ float4 s_part[kThreads / kWave];
+  __shared__ int s_cu[kCuLds];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int i = local >> 1;
-  const int which = local & 1;  // 0: draft row of position i, 1: target row
-  const int rp = d0 + b + i;
-  const bool greedy = seq_greedy(P, b);
-  if (which == 0 && (greedy || i == kb)) return;  // no draft row to read
-  const void* base = which ? P.target : P.draft;
-  const size_t row = (size_t)(which ? rp : d0 + i) * (size_t)P.V;
-  const int vb = ch * kChunkVecs;
-  const int ve = min(P.nvec, vb + kChunkVecs);
+  const long long g = (long long)blockIdx.x + P.stats_block0;
+  const int unit = (int)(g / P.chunks);
+  const int ch = (int)(g - (long long)unit * P.chunks);
+  const bool is_target = unit >= P.total_draft;
+  const int row = is_target ? unit - P.total_draft : unit;
+  bool greedy = P.all_greedy != 0;
+  if (!greedy && P.greedy != nullptr) greedy = P.greedy[row_seq(P, row, is_target, s_cu)] != 0;
+  if (greedy && !is_target) return;  // greedy sequences never read draft rows
+  const void* base = is_target ? P.target : P.draft;
+  const size_t roff = (size_t)row * (size_t)P.V;
+  const int vb = ch * P.chunk_vecs;
+  const int ve = min(P.nvec, vb + P.chunk_vecs);
   int v = vb + tid;
   unsigned long long packed;
   if (greedy) {
@@ -514,7 +464,7 @@ __device__ void stats_block(const Params& P, int b, int d0, int kb, int local, i
     for (; v + (kBatch - 1) * kThreads < ve; v += kBatch * kThreads) {
       typename Vc::Raw r[kBatch];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) r[u] = Vc::load(base, row, v + u * kThreads);
+      for (int u = 0; u < kBatch; ++u) r[u] = Vc::load(base, roff, v + u * kThreads);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
@@ -532,7 +482,7 @@ __device__ void stats_block(const Params& P, int b, int d0, int kb, int local, i
     }
     for (; v < ve; v += kThreads) {
       float f[N];
-      Vc::get(Vc::load(base, row, v), f);
+      Vc::get(Vc::load(base, roff, v), f);
 #pragma unroll
       for (int k = 0; k < N; ++k) {
         bad |= is_nan_or_posinf(f[k]);
@@ -558,7 +508,7 @@ __device__ void stats_block(const Params& P, int b, int d0, int kb, int local, i
     for (; v + (kBatch - 1) * kThreads < ve; v += kBatch * kThreads) {
       typename Vc::Raw r[kBatch];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) r[u] = Vc::load(base, row, v + u * kThreads);
+      for (int u = 0; u < kBatch; ++u) r[u] = Vc::load(base, roff, v + u * kThreads);
       __builtin_amdgcn_sched_barrier(0);
       float f[kBatch * N];
 #pragma unroll
@@ -567,7 +517,7 @@ __device__ void stats_block(const Params& P, int b, int d0, int kb, int local, i
     }
     for (; v < ve; v += kThreads) {
       float f[N];
-      Vc::get(Vc::load(base, row, v), f);
+      Vc::get(Vc::load(base, roff, v), f);
       online_update<N>(m, s, f, c);
     }
     wave_merge_ms(m, s, c);
@@ -578,92 +528,68 @@ __device__ void stats_block(const Params& P, int b, int d0, int kb, int local, i
     for (int w = 1; w < kThreads / kWave; ++w) merge_ms(m, s, s_part[w].x, s_part[w].y, c);
     packed = pack_ms(m, s);
   }
-  pub_u64(P.slots + ((size_t)rp * 2 + which) * P.chunks + ch, packed);
+  P.slots[g] = packed;
 }
 
-// ------------------------------------------------------------------ draw block
+// ------------------------------------------------------------------- k_draw
+// Block (b, ch), ch < dchunks: decision of sequence b, then the tile sums of
+// slice ch of row pair n; the last block of b to finish draws the token.
 template <int DT, bool VEC>
-__device__ void draw_block(const Params& P, int b, int ch) {
+__global__ __launch_bounds__(kThreads) void k_draw(const Params P) {
   using Vc = Vec<DT, VEC>;
   constexpr int N = Vc::N;
-  __shared__ SeqState S;
-  __shared__ int s_last, s_to;
+  __shared__ Dec S;
+  __shared__ int s_last;
   const int tid = threadIdx.x;
+  const int b = blockIdx.x / P.dchunks;
+  const int ch = blockIdx.x - b * P.dchunks;
   int d0, kb;
-  if (!seq_bounds(P, b, d0, kb)) return;  // reported by the offsets check
-  const bool greedy = seq_greedy(P, b);
-  if (greedy) {
-    // chunk 0 decides a greedy sequence; there is nothing to draw
-    if (ch == 0) decide<DT>(P, b, d0, kb, true, S);
+  if (!seq_bounds(P, b, d0, kb)) {
+    if (ch == 0 && tid == 0) P.num_accepted[b] = SV_SEQ_BAD_OFFSETS;
     return;
   }
-  if (ch == 0) {
-    decide<DT>(P, b, d0, kb, false, S);
-  } else {
-    if (tid == 0) {
-      const bool ok = wait_flag(P, P.job_ready + b);
-      Job j;
-      const int* q = reinterpret_cast<const int*>(P.jobs + b);
-      j.mode = ok ? obs_i(q) : kJobNone;
-      j.n = obs_i(q + 1);
-      j.prow = obs_i(q + 2);
-      j.qrow = obs_i(q + 3);
-      j.Rq = obs_f(reinterpret_cast<const float*>(q + 4));
-      j.invSq = obs_f(reinterpret_cast<const float*>(q + 5));
-      j.Rp = obs_f(reinterpret_cast<const float*>(q + 6));
-      j.invSp = obs_f(reinterpret_cast<const float*>(q + 7));
-      j.u = obs_f(reinterpret_cast<const float*>(q + 8));
-      j.out_idx = obs_i(q + 9);
-      if (!ok) {
-        raise_flag(P.seq_flags + b, kSeqFlagTimeout);
-        drain_stores();
-      }
-      S.job = j;
-    }
-    __syncthreads();
-  }
-  const Job j = S.job;
-  if (j.mode != kJobNone) {
-    // tile sums of this draw chunk of row pair n: the thread's vector
-    // k*kThreads + tid of the chunk belongs to tile ch*kTilesPerDraw + k
-    const size_t prow = (size_t)j.prow * P.V;
-    const size_t qrow = (size_t)j.qrow * P.V;
-    const int vb = ch * kDrawVecs + tid;
-    typename Vc::Raw rp[kBatch], rq[kBatch];
+  const bool greedy = seq_greedy(P, b);
+  if (greedy && ch != 0) return;  // one block decides a greedy sequence
+  const Job j = decide<DT>(P, b, d0, kb, greedy, ch == 0, S);
+  if (j.mode == kJobNone) return;
+  // tile sums of slice ch of row pair n: the thread's vector k*kThreads + tid of
+  // the slice belongs to tile ch*kTilesPerDraw + k
+  const size_t prow = (size_t)j.prow * P.V;
+  const size_t qrow = (size_t)j.qrow * P.V;
+  const int vb = ch * kDrawVecs + tid;
+  typename Vc::Raw rp[kBatch], rq[kBatch];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int v = vb + u * kThreads;
-      if (v < P.nvec) {
-        rp[u] = Vc::load(P.target, prow, v);
-        if (j.mode == kJobResidual) rq[u] = Vc::load(P.draft, qrow, v);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    float ts[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int v = vb + u * kThreads;
-      if (v < P.nvec) {
-        float fp[N], fq[N];
-        Vc::get(rp[u], fp);
-        if (j.mode == kJobResidual) Vc::get(rq[u], fq);
-        float s = 0.f;
-#pragma unroll
-        for (int k = 0; k < N; ++k) s += draw_weight(fp[k], fq[k], j, P.c);
-        ts[u] = s;
-      }
-    }
-    float tot[8];
-    block_sum8(ts, tot);
-    if (tid < kTilesPerDraw) {
-      float val = tot[0];
-#pragma unroll
-      for (int k = 1; k < kTilesPerDraw; ++k) val = (tid == k) ? tot[k] : val;
-      pub_f(P.tiles + (size_t)b * P.ntiles + ch * kTilesPerDraw + tid, val);
-      drain_stores();
+  for (int u = 0; u < kBatch; ++u) {
+    const int v = vb + u * kThreads;
+    if (v < P.nvec) {
+      rp[u] = Vc::load(P.target, prow, v);
+      if (j.mode == kJobResidual) rq[u] = Vc::load(P.draft, qrow, v);
     }
   }
-  // every draw chunk of the sequence counts itself, timed out or not
+  __builtin_amdgcn_sched_barrier(0);
+  float ts[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    const int v = vb + u * kThreads;
+    if (v < P.nvec) {
+      float fp[N], fq[N];
+      Vc::get(rp[u], fp);
+      if (j.mode == kJobResidual) Vc::get(rq[u], fq);
+      float s = 0.f;
+#pragma unroll
+      for (int k = 0; k < N; ++k) s += draw_weight(fp[k], fq[k], j, P.c);
+      ts[u] = s;
+    }
+  }
+  float tot[8];
+  block_sum8(ts, tot);
+  if (tid < kTilesPerDraw) {
+    float val = tot[0];
+#pragma unroll
+    for (int k = 1; k < kTilesPerDraw; ++k) val = (tid == k) ? tot[k] : val;
+    pub_f(P.tiles + (size_t)b * P.ntiles + ch * kTilesPerDraw + tid, val);
+    drain_stores();
+  }
   __syncthreads();
   if (tid == 0) {
     s_last = (bump(P.draw_done + b) == P.dchunks - 1) ? 1 : 0;
@@ -671,73 +597,15 @@ __device__ void draw_block(const Params& P, int b, int ch) {
   }
   __syncthreads();
   if (!s_last) return;
-  // Last draw chunk: draw, write the token, return the workspace to zero.
-  if (tid == 0) s_to = obs_i(P.seq_flags + b) & kSeqFlagTimeout;
-  __syncthreads();
-  if (s_to) {
-    for (int k = tid; k <= kb; k += kThreads) P.out_tokens[d0 + b + k] = -1;
-    if (tid == 0) P.num_accepted[b] = SV_SEQ_SYNC_TIMEOUT;
-  } else if (j.mode != kJobNone) {
-    float Z;
-    const int tok = pick<DT, VEC>(P, b, j, Z);
-    if (tid == 0) {
-      P.out_tokens[j.out_idx] = tok;
-      P.num_accepted[b] = j.n;
-      if (P.diag.resid_Z) P.diag.resid_Z[b] = Z;
-    }
-  }
-  __syncthreads();
-  if (j.mode != kJobNone)
-    for (int t = tid; t < P.ntiles; t += kThreads) pub_f(P.tiles + (size_t)b * P.ntiles + t, 0.f);
-  if (tid < (int)(sizeof(Job) / sizeof(int))) pub_i(reinterpret_cast<int*>(P.jobs + b) + tid, 0);
+  // Last block of the sequence: every tile sum is published.
+  float Z;
+  const int tok = pick<DT, VEC>(P, b, j, Z);
   if (tid == 0) {
-    pub_i(P.job_ready + b, 0);
-    pub_i(P.draw_done + b, 0);
-    pub_i(P.seq_flags + b, 0);
+    P.out_tokens[j.out_idx] = tok;
+    P.num_accepted[b] = j.n;
+    if (P.diag.resid_Z) P.diag.resid_Z[b] = Z;
+    pub_i(P.draw_done + b, 0);  // the workspace counter returns to zero
   }
-}
-
-}  // namespace
-
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_verify(const Params P) {
-  // Sequences whose own offsets are invalid are reported by block b.
-  if (P.cu != nullptr && blockIdx.x < (unsigned)P.B && threadIdx.x == 0) {
-    int d0_, kb_;
-    if (!seq_bounds(P, blockIdx.x, d0_, kb_)) P.num_accepted[blockIdx.x] = SV_SEQ_BAD_OFFSETS;
-  }
-  // step s of the grid: stats blocks of sequence s, draw chunk 0 of s - lag0,
-  // the other draw chunks of s - lag1
-  const long long idx = blockIdx.x;
-  int lo = 0, hi = P.B + P.lag1 - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (step_start(P, mid) <= idx) lo = mid;
-    else hi = mid - 1;
-  }
-  const int step = lo;
-  long long off = idx - step_start(P, step);
-  int d0, kb;
-  long long nstats = 0;
-  if (step < P.B && seq_bounds(P, step, d0, kb)) nstats = 2LL * P.chunks * (kb + 1);
-  const long long nstats_slots =
-      (step < P.B) ? stats_before(P, step + 1) - stats_before(P, step) : 0;
-  if (off < nstats) {
-    stats_block<DT, VEC>(P, step, d0, kb, (int)(off / P.chunks), (int)(off % P.chunks));
-    return;
-  }
-  off -= nstats_slots;
-  if (off < 0) return;  // idle block of a sequence with invalid offsets
-  const int b0 = step - P.lag0;
-  if (b0 >= 0 && b0 < P.B) {
-    if (off == 0) {
-      draw_block<DT, VEC>(P, b0, 0);
-      return;
-    }
-    off -= 1;
-  }
-  const int b1 = step - P.lag1;
-  if (b1 >= 0 && b1 < P.B && off < P.dchunks - 1) draw_block<DT, VEC>(P, b1, (int)off + 1);
 }
 
 __global__ void k_fill_zero(uint4* p, size_t n16) {
@@ -749,10 +617,14 @@ __global__ void k_fill_zero(uint4* p, size_t n16) {
 template <int DT, bool VEC>
 static hipError_t launch_t(const Params& P, const Plan& L, hipStream_t s, hipEvent_t* ev, int nev) {
   hipError_t err;
-  if (ev != nullptr && nev > 0 && (err = hipEventRecord(ev[0], s)) != hipSuccess) return err;
-  hipLaunchKernelGGL((k_verify<DT, VEC>), dim3((unsigned)L.blocks), dim3(kThreads), 0, s, P);
+  if (nev > 0 && (err = hipEventRecord(ev[0], s)) != hipSuccess) return err;
+  if (L.stats_blocks > 0)
+    hipLaunchKernelGGL((k_stats<DT, VEC>), dim3((unsigned)L.stats_blocks), dim3(kThreads), 0, s, P);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (ev != nullptr && nev > 1 && (err = hipEventRecord(ev[1], s)) != hipSuccess) return err;
+  if (nev > 1 && (err = hipEventRecord(ev[1], s)) != hipSuccess) return err;
+  hipLaunchKernelGGL((k_draw<DT, VEC>), dim3((unsigned)L.draw_blocks), dim3(kThreads), 0, s, P);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (nev > 2 && (err = hipEventRecord(ev[2], s)) != hipSuccess) return err;
   return hipSuccess;
 }
 

@@ -48,7 +48,7 @@ def to_device(w, toks, device="cuda"):
     return d
 
 
-def run_gpu(w, toks, api="auto", diag=False, dev=None):
+def run_gpu(w, toks, api="auto", diag=False, dev=None, workspace=None):
     """Run through the C ABI. api: 'dense', 'ragged' or 'auto' (dense when the
     workload is dense without a greedy mask). Returns numpy outputs."""
     import speculative_decoding_verification_13_amd as sv
@@ -62,7 +62,8 @@ def run_gpu(w, toks, api="auto", diag=False, dev=None):
         K = w["K"]
         out, num = sv.spec_verify(d["draft"].view(B, K, V), d["target"].view(B, K + 1, V),
                                   d["tokens"].view(B, K), d["uniforms"].view(B, K + 1), B, K,
-                                  V, w["temperature"], w["top_k"], w["top_p"])
+                                  V, w["temperature"], w["top_k"], w["top_p"],
+                                  workspace=workspace)
         out = out.view(-1)
     else:
         diag_t = None
@@ -74,7 +75,8 @@ def run_gpu(w, toks, api="auto", diag=False, dev=None):
         g = d["greedy"] if w["greedy"].any() else None
         out, num = sv.spec_verify_ragged(d["draft"], d["target"], d["tokens"], d["uniforms"],
                                          d["cu"], g, B, V, w["temperature"], w["top_k"],
-                                         w["top_p"], total_draft_rows=n_draft, diag=diag_t)
+                                         w["top_p"], total_draft_rows=n_draft, diag=diag_t,
+                                         workspace=workspace)
         if diag:
             for k, t in diag_t.items():
                 res[k] = t.cpu().numpy()
