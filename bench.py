@@ -120,9 +120,12 @@ def main():
         return
     import speculative_decoding_verification_13_amd as sv
 
+    w = W.make(args.workload, sd_t=args.sd_t)
+    # the CPU oracle first: its worker processes fork before this process uses the GPU
+    cpu = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
+
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    w = W.make(args.workload, sd_t=args.sd_t)
     B, V = w["B"], w["V"]
     cu = w["cu_draft"]
     n_draft = int(cu[-1])
@@ -157,49 +160,61 @@ def main():
     out = torch.empty(n_target, dtype=torch.int32, device=dev)
     num = torch.empty(B, dtype=torch.int32, device=dev)
 
+    # Dense workloads without a greedy mask go through the dense entry point (the
+    # launch the full-size parity test checks); stage events need the diag one.
+    dense = not w["ragged"] and greedy_d is None
+    K = w["K"]
+    dense_sets = [(d.view(B, K, V), t.view(B, K + 1, V)) for d, t in sets] if dense else None
+
     def step(k, events=None):
+        if events is None and dense:
+            d, t = dense_sets[k % len(sets)]
+            sv.spec_verify(d, t, tokens_d.view(B, K), uni_d.view(B, K + 1), B, K, V, T, top_k,
+                           top_p, out_tokens=out.view(B, K + 1), num_accepted=num, workspace=ws)
+            return
         d, t = sets[k % len(sets)]
         diag = None if events is None else {"stage_events": events}
         sv.spec_verify_ragged(d, t, tokens_d, uni_d, cu_d, greedy_d, B, V, T, top_k, top_p,
                               total_draft_rows=n_draft, out_tokens=out, num_accepted=num,
                               workspace=ws, diag=diag)
 
-    # stage events on the launch stream: before the first kernel, between the
-    # two kernels and after the second, one triple per timed step (HIP events
-    # without the system-scope fence)
-    nst = sv.num_stages(top_k, top_p) + 1
-    hev = HipEvents(nst * args.steps)
-    ev_sets = [hev.handles[nst * k:nst * (k + 1)] for k in range(args.steps)]
     for k in range(args.warmup):
-        step(k, ev_sets[k % len(ev_sets)])
+        step(k)
     torch.cuda.synchronize()
 
+    # the timed steps: K calls back to back on the stream, nothing else enqueued
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record()
     for k in range(args.steps):
-        step(k, ev_sets[k])
+        step(k)
     stop.record()
+    host_enqueue = time.perf_counter() - t_wall
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    ms_total = start.elapsed_time(stop)
-    ms_step = ms_total / args.steps
-    stage_ms = [float(np.mean([hev.elapsed_ms(nst * k + i, nst * k + i + 1)
-                               for k in range(args.steps)])) for i in range(nst - 1)]
-    call_ms = float(np.mean([hev.elapsed_ms(nst * k, nst * k + nst - 1)
-                             for k in range(args.steps)]))
-    hev.close()
-    k1_ms = stage_ms[0]
+    ms_step = start.elapsed_time(stop) / args.steps
 
-    # the same steps without stage events (for the cost of the events themselves)
+    # The same K steps again with stage events on the launch stream: before the
+    # first kernel, between the kernels and after the last (HIP events without
+    # the system-scope fence). They give each kernel's duration; recording them
+    # lengthens a step, so the step time above is taken without them.
+    nst = sv.num_stages(top_k, top_p) + 1
+    hev = HipEvents(nst * args.steps)
+    ev_sets = [hev.handles[nst * k:nst * (k + 1)] for k in range(args.steps)]
     torch.cuda.synchronize()
     start.record()
     for k in range(args.steps):
-        step(k)
+        step(k, ev_sets[k])
     stop.record()
     torch.cuda.synchronize()
-    ms_step_plain = start.elapsed_time(stop) / args.steps
+    ms_step_events = start.elapsed_time(stop) / args.steps
+    per_stage = np.array([[hev.elapsed_ms(nst * k + i, nst * k + i + 1) for i in range(nst - 1)]
+                          for k in range(args.steps)])
+    per_call = np.array([hev.elapsed_ms(nst * k, nst * k + nst - 1) for k in range(args.steps)])
+    hev.close()
+    stage_ms = per_stage.mean(axis=0).tolist()
+    k1_ms = stage_ms[0]
 
     rows = int((w["Ks"] + 1).sum())
     comp = W.compulsory_bytes(w)
@@ -219,10 +234,6 @@ def main():
                 and args.sd_t in (None, tr.get("sd_t")):
             traffic = tr.get("hbm_bytes_per_launch")
 
-    cpu = None
-    if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, args.cpu_seconds)
-
     res = {
         "metric": METRIC,
         "value": rows / (ms_step * 1e-3),
@@ -240,6 +251,7 @@ def main():
             "workload": args.workload, "B": B, "K": w["K"], "V": V, "input_dtype": w["dtype"],
             "temperature": T, "top_k": top_k, "top_p": top_p, "sd_t": w["sd_t"],
             "rows_per_step": rows, "rotating_sets": len(sets),
+            "entry_point": "spec_verify" if dense else "spec_verify_ragged",
         },
         "effective_GBps": eff,
         "effective_frac_of_peak": eff / PEAK_HBM_GBPS,
@@ -250,49 +262,83 @@ def main():
             "algorithmic_bytes_per_launch": algo_bytes_k1, "avg_launch_ms": k1_ms,
         },
         "stage_ms": {"k_stats": stage_ms[0], "k_draw": stage_ms[1] if len(stage_ms) > 1 else None,
-                     "call": call_ms},
-        "ms_per_step_without_stage_events": ms_step_plain,
+                     "call_mean": float(per_call.mean()), "call_median": float(np.median(per_call)),
+                     "ms_per_step_with_stage_events": ms_step_events},
         "acceptance": {
             "mean_accepted": float(n_acc.mean()),
             "all_accepted_frac": float((n_acc == w["Ks"]).mean()),
             "errors": int((n_acc < 0).sum()),
         },
         "wall_s": wall,
+        "host_enqueue_us_per_step": host_enqueue / args.steps * 1e6,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
 
 
+_CPU = {}
+
+
+def _cpu_one(b):
+    """Oracle verification of sequence b of the prepared sample (one task)."""
+    import oracle
+    c = _CPU
+    cu = c["cu"]
+    d0, d1 = int(cu[b]), int(cu[b + 1])
+    t0, t1 = d0 + b, d1 + b + 1
+    oracle.verify(c["draft"][d0:d1], c["target"][t0:t1], c["toks"][d0:d1], c["uniforms"][t0:t1],
+                  B=1, V=c["V"], dtype=c["dtype"], cu_draft=np.array([0, d1 - d0]),
+                  temperature=c["T"], top_k=c["top_k"], top_p=c["top_p"],
+                  greedy=c["greedy"][b:b + 1])
+    return t1 - t0
+
+
 def cpu_baseline(w, budget_s):
-    """The float64 oracle, as it stands, on the first sequences of the same workload
-    (cycled until the budget is spent), one process on the host."""
+    """The float64 oracle, as it stands, on the same workload: a third of the
+    budget in this process over the first 16 sequences, the rest with every
+    sequence mapped over a pool of worker processes (forked before this process
+    touches the GPU). Returns the pool rate as the baseline."""
+    import multiprocessing as mp
+
     import oracle
     B, V = w["B"], w["V"]
     cu = w["cu_draft"]
     draft = W.raw_numpy(w["draft"])
     target = W.raw_numpy(w["target"])
-    n_seq = min(B, 16)
-    d1 = int(cu[n_seq])
-    toks, _ = oracle.sample_rows(draft[:d1], w["u_draft"][:d1], V=V, dtype=w["dtype"],
+    toks, _ = oracle.sample_rows(draft, w["u_draft"], V=V, dtype=w["dtype"],
                                  temperature=w["temperature"], top_k=w["top_k"],
-                                 top_p=w["top_p"], greedy=W.draft_row_greedy_mask(w)[:d1])
+                                 top_p=w["top_p"], greedy=W.draft_row_greedy_mask(w))
+    _CPU.update(draft=draft, target=target, toks=toks, uniforms=w["uniforms"], cu=cu, V=V,
+                dtype=w["dtype"], T=w["temperature"], top_k=w["top_k"], top_p=w["top_p"],
+                greedy=w["greedy"])
+    n_one = min(B, 16)
     t0 = time.perf_counter()
-    rows = 0
-    calls = 0
+    rows_one = 0
     while True:
-        oracle.verify(draft[:d1], target[: d1 + n_seq], toks, w["uniforms"][: d1 + n_seq],
-                      B=n_seq, V=V, dtype=w["dtype"], cu_draft=cu[: n_seq + 1],
-                      temperature=w["temperature"], top_k=w["top_k"], top_p=w["top_p"],
-                      greedy=w["greedy"][:n_seq])
-        rows += int((w["Ks"][:n_seq] + 1).sum())
-        calls += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
+        for b in range(n_one):
+            rows_one += _cpu_one(b)
+        el_one = time.perf_counter() - t0
+        if el_one >= budget_s / 3:
             break
+    workers = max(1, min(16, os.cpu_count() or 1))
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers) as pool:
+        pool.map(_cpu_one, range(min(B, workers)))
+        t0 = time.perf_counter()
+        rows_pool = 0
+        passes = 0
+        while True:
+            rows_pool += sum(pool.map(_cpu_one, range(B), chunksize=1))
+            passes += 1
+            el_pool = time.perf_counter() - t0
+            if el_pool >= budget_s * 2 / 3:
+                break
     return {
-        "value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
-        "sample": f"first {n_seq} of {B} sequences of the same workload, {calls} passes, "
-                  f"{el:.1f} s, numpy float64, one process",
+        "value": rows_pool / el_pool, "unit": "rows/s", "cores": workers, "kind": "oracle",
+        "sample": f"all {B} sequences of the same workload, {passes} passes in {el_pool:.1f} s, "
+                  f"numpy float64, sequences mapped over {workers} worker processes",
+        "single_process": {"value": rows_one / el_one, "unit": "rows/s", "cores": 1,
+                           "sample": f"first {n_one} sequences cycled for {el_one:.1f} s"},
         "host_cpus": os.cpu_count(),
     }
 
