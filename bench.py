@@ -261,9 +261,11 @@ def main():
             "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
             "algorithmic_bytes_per_launch": algo_bytes_k1, "avg_launch_ms": k1_ms,
         },
-        "stage_ms": {"k_stats": stage_ms[0], "k_draw": stage_ms[1] if len(stage_ms) > 1 else None,
-                     "call_mean": float(per_call.mean()), "call_median": float(np.median(per_call)),
-                     "ms_per_step_with_stage_events": ms_step_events},
+        "stage_ms": dict(
+            zip(["k_stats", "k_filter", "k_draw"] if len(stage_ms) == 3 else ["k_stats", "k_draw"],
+                stage_ms),
+            call_mean=float(per_call.mean()), call_median=float(np.median(per_call)),
+            ms_per_step_with_stage_events=ms_step_events),
         "acceptance": {
             "mean_accepted": float(n_acc.mean()),
             "all_accepted_frac": float((n_acc == w["Ks"]).mean()),

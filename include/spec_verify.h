@@ -74,9 +74,10 @@ typedef enum sv_dtype { SV_F32 = 0, SV_F16 = 1, SV_BF16 = 2 } sv_dtype;
 #define SV_EWORKSPACE (-3)   /* workspace null, not 256-byte aligned, or smaller
                                 than spec_verify_workspace_bytes() */
 #define SV_EHIP (-4)         /* a HIP launch or event record failed */
-#define SV_EUNSUPPORTED (-5) /* valid request outside this build's limits
-                                (top_k above SV_MAX_TOP_K, or a grid of more
-                                than 2^24 blocks) */
+#define SV_EUNSUPPORTED (-5) /* valid request outside this build's limits:
+                                top_k above SV_MAX_TOP_K, top_p < 1 without
+                                an active top_k (0 < top_k < V), or a grid of
+                                more than 2^24 blocks */
 
 /* Per-sequence codes written to num_accepted[b] instead of a count. */
 #define SV_SEQ_BAD_TOKEN (-1)   /* a draft id outside [0, V) */
@@ -92,7 +93,9 @@ typedef enum sv_dtype { SV_F32 = 0, SV_F16 = 1, SV_BF16 = 2 } sv_dtype;
 const char* spec_verify_strerror(int code);
 
 /* Bytes of device workspace a call with these sizes needs (the same value for
- * spec_verify with total_draft_rows = B*K). Returns 0 for invalid sizes. */
+ * spec_verify with total_draft_rows = B*K). An active top_k (0 < top_k < V,
+ * top_k <= SV_MAX_TOP_K) adds per-chunk candidate records; a workspace sized
+ * with it also serves calls without filters. Returns 0 for invalid sizes. */
 size_t spec_verify_workspace_bytes(int B, int total_draft_rows, int V, int top_k,
                                    float top_p);
 
@@ -146,9 +149,11 @@ int spec_verify_ragged(const void* draft_logits, const void* target_logits,
  *   resid_Z      per sequence: the mass the final inverse CDF normalised by
  *                (residual mass at n, or the bonus row's mass)
  *   stage_events n_stage_events events recorded on `stream` before the first
- *                kernel and after each kernel of the call (for timing); with
- *                two kernels, event 1 separates the row statistics pass from
- *                the decision-and-draw pass. */
+ *                kernel and after each kernel of the call (for timing); events
+ *                beyond the kernel count are recorded after the last kernel.
+ *                Without filters the kernels are the row statistics pass and
+ *                the decision-and-draw pass; with top-k a per-row filter pass
+ *                (threshold and kept-set normaliser) runs between them. */
 typedef struct sv_diag {
   float* row_max_draft;
   float* row_logsum_draft;

@@ -27,52 +27,66 @@ long long chunk_vecs_for(long long nvec) {
   return steps * sv::kStepVecs;
 }
 
+bool topk_active(int V, int top_k) { return top_k > 0 && top_k < V; }
+
+bool filters_active(int V, int top_k, float top_p) {
+  return topk_active(V, top_k) || top_p < 1.0f;
+}
+
+// (value, id) pairs per chunk record of a filtered row: k plus room for ties.
+int kcap_for(int top_k) { return (top_k + 256 + 63) / 64 * 64; }
+
 // Workspace layout (per call):
 //   draw_done[B]                           per-sequence counters, zero between calls
-//   slots[(total_draft + rows) * cmax]     64-bit chunk partials of every row
+//   slots[(total_draft + rows) * cmax]     64-bit chunk partials (greedy rows, and
+//                                          every row when no filter is active)
 //   tiles[B * dmax * tiles per draw block] draw-weight tile sums
+// and with top-k active:
+//   rec[(total_draft + rows) * cmax * rec_words]  chunk records of sampling rows
+//   rowres[total_draft + rows]                    kept-set statistics per row
 // Only the counters must be zero when a call starts, and every call leaves
 // them zero, so the layout may differ from call to call. The regions are sized
 // for the scalar path (one element per vector), which has the most chunks:
 // a row of nvec <= V vectors never has more than cmax chunks.
-bool data_bytes(int B, int total_draft, int V, size_t& bytes, long long& rows, long long& cmax,
-                long long& dmax) {
+bool make_plan(int B, int total_draft, int V, int top_k, size_t ws_bytes, sv::Plan& L) {
   if (B < 0 || total_draft < 0 || V < 1) return false;
-  rows = (long long)total_draft + B;
+  const long long rows = (long long)total_draft + B;
   if (rows > INT_MAX) return false;
-  const long long base = (long long)sv::kStepVecs * sv::kChunkSteps;
-  cmax = ((long long)V + base - 1) / base;
-  if (cmax > sv::kMaxChunks) cmax = sv::kMaxChunks;
-  dmax = ((long long)V + sv::kDrawVecs - 1) / sv::kDrawVecs;
-  bytes = align_up((size_t)B * 4) + align_up((size_t)(total_draft + rows) * (size_t)cmax * 8) +
-          align_up((size_t)B * (size_t)dmax * sv::kTilesPerDraw * 4);
-  return true;
-}
-
-bool make_plan(int B, int total_draft, int V, size_t ws_bytes, sv::Plan& L) {
-  size_t dbytes;
-  long long rows, cmax, dmax;
-  if (!data_bytes(B, total_draft, V, dbytes, rows, cmax, dmax)) return false;
+  const size_t units = (size_t)(total_draft + rows);
+  const bool filt = topk_active(V, top_k) && top_k <= SV_MAX_TOP_K;
+  long long cmax;
+  if (filt) {
+    cmax = ((long long)V + sv::kFiltChunkVecs - 1) / sv::kFiltChunkVecs;
+  } else {
+    const long long base = (long long)sv::kStepVecs * sv::kChunkSteps;
+    cmax = ((long long)V + base - 1) / base;
+    if (cmax > sv::kMaxChunks) cmax = sv::kMaxChunks;
+  }
+  const long long dmax = ((long long)V + sv::kDrawVecs - 1) / sv::kDrawVecs;
   size_t off = 0;
   L.off_draw_done = off;
   off += align_up((size_t)B * 4);
   L.off_slots = off;
-  off += align_up((size_t)(total_draft + rows) * (size_t)cmax * 8);
+  off += align_up(units * (size_t)cmax * 8);
   L.off_tiles = off;
   off += align_up((size_t)B * (size_t)dmax * sv::kTilesPerDraw * 4);
+  L.off_rec = L.off_rowres = off;
+  if (filt) {
+    const size_t rec_words = sv::kRecHeader + 2 * (size_t)kcap_for(top_k);
+    off += align_up(units * (size_t)cmax * rec_words * 4);
+    L.off_rowres = off;
+    off += align_up(units * sizeof(sv::RowRes));
+  }
   L.total_bytes = off;
   return off <= ws_bytes;
 }
 
-size_t required_bytes(int B, int total_draft, int V) {
+size_t required_bytes(int B, int total_draft, int V, int top_k) {
   sv::Plan L;
-  if (!make_plan(B, total_draft, V, SIZE_MAX, L)) return 0;
+  if (!make_plan(B, total_draft, V, top_k, SIZE_MAX, L)) return 0;
   return L.total_bytes > 0 ? L.total_bytes : kAlign;
 }
 
-bool filters_active(int V, int top_k, float top_p) {
-  return (top_k > 0 && top_k < V) || top_p < 1.0f;
-}
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -92,16 +106,14 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
   if (total_draft > 0 && tokens == nullptr) return SV_EINVAL;
   if (total_draft > 0 && !all_greedy && draft == nullptr) return SV_EINVAL;
   if (!all_greedy && uniforms == nullptr) return SV_EINVAL;
-  if (!all_greedy && filters_active(V, top_k, top_p)) {
-    if (top_k > SV_MAX_TOP_K) return SV_EUNSUPPORTED;
-    return SV_EUNSUPPORTED;  // top-k / top-p path not in this build yet
-  }
-  size_t dbytes;
-  long long rows_ll, cmax_ll, dmax_ll;
-  if (!data_bytes(B, total_draft, V, dbytes, rows_ll, cmax_ll, dmax_ll)) return SV_EUNSUPPORTED;
+  // Filters act on sampling rows through top-k; top-p alone (no top-k) is not
+  // in this build.
+  const bool filt = !all_greedy && filters_active(V, top_k, top_p);
+  if (filt && (!topk_active(V, top_k) || top_k > SV_MAX_TOP_K)) return SV_EUNSUPPORTED;
   sv::Plan L;
+  if (!make_plan(B, total_draft, V, filt ? top_k : 0, SIZE_MAX, L)) return SV_EUNSUPPORTED;
   if (workspace == nullptr || ((uintptr_t)workspace % kAlign) != 0 ||
-      !make_plan(B, total_draft, V, workspace_bytes, L))
+      !make_plan(B, total_draft, V, filt ? top_k : 0, workspace_bytes, L))
     return SV_EWORKSPACE;
 
   const int es = esize_of(dtype);
@@ -123,15 +135,22 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
   P.all_greedy = all_greedy ? 1 : 0;
   P.c = all_greedy ? 0.0f : (float)(1.4426950408889634074 / (double)temperature);
   P.nvec = vec ? V / n_per_vec : V;
-  P.chunk_vecs = (int)chunk_vecs_for(P.nvec);
+  P.chunk_vecs = filt ? sv::kFiltChunkVecs : (int)chunk_vecs_for(P.nvec);
   P.chunks = (P.nvec + P.chunk_vecs - 1) / P.chunk_vecs;
   P.dchunks = (P.nvec + sv::kDrawVecs - 1) / sv::kDrawVecs;
   P.ntiles = P.dchunks * sv::kTilesPerDraw;
   // greedy-only calls skip the draft rows
   P.stats_block0 = all_greedy ? (long long)total_draft * P.chunks : 0;
+  P.filt = filt ? 1 : 0;
+  P.top_k = top_k;
+  P.top_p = top_p;
+  P.kcap = filt ? kcap_for(top_k) : 0;
+  P.rec_words = sv::kRecHeader + 2 * P.kcap;
   P.out_tokens = out_tokens;
   P.num_accepted = num_accepted;
   char* ws = static_cast<char*>(workspace);
+  P.rec = filt ? reinterpret_cast<unsigned*>(ws + L.off_rec) : nullptr;
+  P.rowres = filt ? reinterpret_cast<sv::RowRes*>(ws + L.off_rowres) : nullptr;
   P.slots = reinterpret_cast<unsigned long long*>(ws + L.off_slots);
   P.tiles = reinterpret_cast<float*>(ws + L.off_tiles);
   P.draw_done = reinterpret_cast<int*>(ws + L.off_draw_done);
@@ -139,6 +158,7 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
   L.chunk_vecs = P.chunk_vecs;
   L.dchunks = P.dchunks;
   L.stats_blocks = ((long long)total_draft + P.rows) * P.chunks - P.stats_block0;
+  L.filter_blocks = filt ? (long long)total_draft + P.rows : 0;
   L.draw_blocks = (long long)B * P.dchunks;
   if (L.stats_blocks > (long long)UINT32_MAX / sv::kThreads ||
       L.draw_blocks > (long long)UINT32_MAX / sv::kThreads)
@@ -176,9 +196,8 @@ const char* spec_verify_strerror(int code) {
 }
 
 size_t spec_verify_workspace_bytes(int B, int total_draft_rows, int V, int top_k, float top_p) {
-  (void)top_k;
   (void)top_p;
-  return required_bytes(B, total_draft_rows, V);
+  return required_bytes(B, total_draft_rows, V, top_k);
 }
 
 int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
@@ -188,9 +207,7 @@ int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, hipStrea
 }
 
 int spec_verify_num_stages(int top_k, float top_p) {
-  (void)top_k;
-  (void)top_p;
-  return 2;
+  return (top_k > 0 || top_p < 1.0f) ? 3 : 2;
 }
 
 int spec_verify(const void* draft_logits, const void* target_logits, const int32_t* draft_tokens,

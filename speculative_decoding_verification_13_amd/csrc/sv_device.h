@@ -236,6 +236,66 @@ __device__ __forceinline__ int block_max_i(int x) {
   return r;
 }
 
+// Block-wide exclusive scan of ints for kBlock threads; `total` receives the sum.
+__device__ __forceinline__ int block_excl_scan_i(int x, int& total) {
+  __shared__ int s_w[kBlock / kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  int incl = x;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) s_w[w] = incl;
+  __syncthreads();
+  int base = 0;
+  total = 0;
+#pragma unroll
+  for (int k = 0; k < kBlock / kWave; ++k) {
+    const int t = s_w[k];
+    if (k < w) base += t;
+    total += t;
+  }
+  return base + incl - x;
+}
+
+__device__ __forceinline__ float block_max_f(float x) {
+  __shared__ float s_w[kBlock / kWave];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) s_w[threadIdx.x / kWave] = x;
+  __syncthreads();
+  float r = s_w[0];
+#pragma unroll
+  for (int k = 1; k < kBlock / kWave; ++k) r = fmaxf(r, s_w[k]);
+  return r;
+}
+
+__device__ __forceinline__ int block_sum_i(int x) {
+  __shared__ int s_w[kBlock / kWave];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) s_w[threadIdx.x / kWave] = x;
+  __syncthreads();
+  int r = 0;
+#pragma unroll
+  for (int k = 0; k < kBlock / kWave; ++k) r += s_w[k];
+  return r;
+}
+
+// Order-preserving 32-bit key of a non-NaN float (-0 and +0 share one key).
+__device__ __forceinline__ unsigned key_of(float f) {
+  const unsigned u = __float_as_uint(f == 0.0f ? 0.0f : f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float float_of_key(unsigned k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 // ---- cross-block publication (agent scope, no L2 writeback/invalidate) ----
 // Shared records are written with agent-scope atomic stores, which write
 // through to the device coherence point, and read with agent-scope atomic

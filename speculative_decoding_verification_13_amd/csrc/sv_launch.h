@@ -21,6 +21,24 @@ constexpr int kTilesPerDraw = kDrawVecs / kTileVecs;
 constexpr int kChunkSteps = SV_CHUNK_STEPS;  // batches per stats block (64 KB of bf16)
 constexpr int kMaxChunks = 64;            // stats chunks per row (larger rows take
                                           // larger chunks)
+// Filtered rows (top-k): a stats block keeps its whole chunk in registers.
+constexpr int kFiltVpt = 8;               // vectors per thread of a filtered chunk
+constexpr int kFiltChunkVecs = kFiltVpt * kThreads;
+constexpr int kRecHeader = 8;             // header words of a chunk record
+constexpr int kBoundMaxK = kThreads;      // largest k bounded by the per-thread maxima
+constexpr int kFilterMaxLevels = 2048;    // LDS entries of the per-row level sort
+
+// Chunk record of a filtered row: header then `kcap` (value bits, id) pairs.
+//   [0] entries written   [1] value of an implicit tie class   [2] its count
+//   [3] flags: 1 NaN or +inf seen, 2 the tie class is implicit (count only)
+enum { kRecFlagBad = 1, kRecFlagImplicitTies = 2 };
+
+// Per-row result of the filter pass: kept-set maximum, kept-set sum of
+// 2^(l*c - R) (R = fp32(max*c)), threshold theta (kept iff l >= theta), flags.
+struct RowRes {
+  float m, s, theta;
+  int flags;
+};
 
 enum { kJobNone = 0, kJobResidual = 1, kJobBonus = 2 };
 
@@ -31,6 +49,7 @@ struct Job {
   int prow;      // target row of position n
   int qrow;      // draft row of position n (residual only)
   float Rq, invSq, Rp, invSp;  // references R = fp32(max*c) and 1/S of both rows
+  float thr_q, thr_p;  // kept-set thresholds of both rows (-inf: no filter)
   float u;       // the resample-or-bonus uniform
   int out_idx;   // output slot of the drawn token
 };
@@ -61,6 +80,13 @@ struct Params {
   int nvec;                // vectors (or elements, scalar path) per row
   int ntiles;              // draw tiles per row = dchunks * kTilesPerDraw
   long long stats_block0;  // first stats block (skips draft rows when all greedy)
+  int filt;                // 1: top-k (and top-p) filters active
+  int top_k;
+  float top_p;
+  int kcap;                // (value, id) pairs per chunk record
+  int rec_words;           // words per chunk record = kRecHeader + 2 * kcap
+  unsigned* rec;           // [(total_draft + rows) * chunks * rec_words] (filtered)
+  RowRes* rowres;          // [total_draft + rows] (filtered)
   int32_t* out_tokens;
   int32_t* num_accepted;
   // Chunk partials, 64-bit: sampling (max, sum) floats; greedy (max value,
@@ -74,8 +100,8 @@ struct Params {
 // Grid size and workspace offsets of one call.
 struct Plan {
   int chunks, chunk_vecs, dchunks;
-  long long stats_blocks, draw_blocks;
-  size_t off_slots, off_tiles, off_draw_done, total_bytes;
+  long long stats_blocks, filter_blocks, draw_blocks;
+  size_t off_slots, off_tiles, off_draw_done, off_rec, off_rowres, total_bytes;
 };
 
 hipError_t launch(int dtype, bool vec, const Params& P, const Plan& L, hipStream_t s,

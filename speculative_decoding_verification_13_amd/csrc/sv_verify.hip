@@ -93,11 +93,19 @@ struct Vec {
   }
 };
 
-// Weight of one id in the final draw: residual max(0, p - q) or bonus p.
+// Makes a register value opaque to the compiler, so values derived from it in
+// one pass are recomputed in the next instead of being kept alive.
+__device__ __forceinline__ void opaque(uint4& x) {
+  asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w));
+}
+__device__ __forceinline__ void opaque(float& x) { asm volatile("" : "+v"(x)); }
+
+// Weight of one id in the final draw: residual max(0, p - q) or bonus p, where
+// an id outside a row's kept set (l < threshold) has probability 0 in that row.
 __device__ __forceinline__ float draw_weight(float lp, float lq, const Job& j, float c) {
-  const float ep = fast_exp2(fmaf(lp, c, -j.Rp));
+  const float ep = (lp >= j.thr_p) ? fast_exp2(fmaf(lp, c, -j.Rp)) : 0.0f;
   if (j.mode == kJobBonus) return ep * j.invSp;
-  const float q = fast_exp2(fmaf(lq, c, -j.Rq)) * j.invSq;
+  const float q = (lq >= j.thr_q) ? fast_exp2(fmaf(lq, c, -j.Rq)) * j.invSq : 0.0f;
   return fmaxf(fmaf(ep, j.invSp, -q), 0.0f);
 }
 
@@ -236,7 +244,8 @@ __device__ int pick(const Params& P, int b, Job j, float& Zout) {
 // Decision state of one sequence, in LDS.
 struct Dec {
   float m[2][SV_MAX_K + 1];  // merged row maxima (draft, target) per position
-  float s[2][SV_MAX_K + 1];  // merged sums 2^(l*c - R)
+  float s[2][SV_MAX_K + 1];  // merged sums 2^(l*c - R) (over the kept set)
+  float th[2][SV_MAX_K + 1]; // kept-set thresholds (-inf: no filter)
   int flags;                 // 1 bad token, 2 bad row
   unsigned long long rej;    // ballot of rejected draft positions
 };
@@ -321,6 +330,7 @@ __device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool 
     lp = load_elem<DT>(P.target, (size_t)(t0 + tid) * P.V + xs);
   }
   float mq = kNegInf, sq = 0.f, mp = kNegInf, sp = 0.f;
+  float thq = kNegInf, thp = kNegInf;
   int am = INT_MAX;
   bool bad = false;
   if (active) {
@@ -330,8 +340,25 @@ __device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool 
       merge_greedy(tsl, C, mp, am, gbad);
       bad = gbad || mp == kNegInf;
     } else {
-      merge_sampling(P.slots + (size_t)(d0 + tid) * C, tsl, is_draft, C, c, mq, sq, mp, sp);
-      bool ok = __builtin_isfinite(mp) && sp > 0.f && __builtin_isfinite(sp);
+      int rbad = 0;
+      if (P.filt) {
+        // kept-set statistics of the filter pass
+        const RowRes rt = P.rowres[P.total_draft + t0 + tid];
+        mp = rt.m;
+        sp = rt.s;
+        thp = rt.theta;
+        rbad = rt.flags;
+        if (is_draft) {
+          const RowRes rd = P.rowres[d0 + tid];
+          mq = rd.m;
+          sq = rd.s;
+          thq = rd.theta;
+          rbad |= rd.flags;
+        }
+      } else {
+        merge_sampling(P.slots + (size_t)(d0 + tid) * C, tsl, is_draft, C, c, mq, sq, mp, sp);
+      }
+      bool ok = !rbad && __builtin_isfinite(mp) && sp > 0.f && __builtin_isfinite(sp);
       if (is_draft) ok = ok && __builtin_isfinite(mq) && sq > 0.f && __builtin_isfinite(sq);
       bad = !ok;
     }
@@ -339,6 +366,8 @@ __device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool 
     S.s[0][tid] = sq;
     S.m[1][tid] = mp;
     S.s[1][tid] = sp;
+    S.th[0][tid] = thq;
+    S.th[1][tid] = thp;
     if (bad) atomicOr(&S.flags, 2);
     if (!tok_ok) atomicOr(&S.flags, 1);
   }
@@ -348,10 +377,17 @@ __device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool 
     if (greedy) {
       acc = am == x;
     } else {
-      // r = p(x)/q(x) = 2^((lp*c - Rp) - (lq*c - Rq)) * Sq / Sp
-      const float ep = fmaf(lp, c, -ref_of(mp, c));
-      const float eq = fmaf(lq, c, -ref_of(mq, c));
-      ratio = fast_exp2(ep - eq) * (sq / sp);
+      // r = p(x)/q(x) = 2^((lp*c - Rp) - (lq*c - Rq)) * Sq / Sp; an id outside
+      // a row's kept set has probability 0 there: q(x) = 0 < p(x) accepts,
+      // p(x) = 0 rejects
+      const bool pk = lp >= thp, qk = lq >= thq;
+      if (pk && qk) {
+        const float ep = fmaf(lp, c, -ref_of(mp, c));
+        const float eq = fmaf(lq, c, -ref_of(mq, c));
+        ratio = fast_exp2(ep - eq) * (sq / sp);
+      } else {
+        ratio = pk ? kPosInf : 0.f;
+      }
       acc = u < ratio;  // strict: u == r rejects
     }
   }
@@ -404,6 +440,8 @@ __device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool 
   j.invSq = 1.0f / S.s[0][n];
   j.Rp = ref_of(S.m[1][n], c);
   j.invSp = 1.0f / S.s[1][n];
+  j.thr_q = S.th[0][n];
+  j.thr_p = S.th[1][n];
   j.u = u_draw;
   j.out_idx = t0 + n;
   return j;
@@ -429,13 +467,154 @@ __device__ int row_seq(const Params& P, int row, bool is_target, int* s_cu) {
   return lo;
 }
 
+// Candidates of one chunk of a filtered sampling row (whole block; the chunk
+// stays in registers). The candidates are the finite logits at or above a
+// lower bound of the chunk's k-th largest finite logit, so they include every
+// logit the row's top-k set can take from this chunk. They are written to the
+// chunk record as (value bits, id) pairs. A chunk with more candidates than the
+// record holds (heavy ties, or k beyond what the bound covers) is cut to its
+// exact top k by a radix select on order-preserving keys; a tie class at the
+// cut that still does not fit is recorded as (value, count).
+template <int DT, bool VEC>
+__device__ void topk_block(const Params& P, long long g, const void* base, size_t roff, int ch) {
+  using Vc = Vec<DT, VEC>;
+  constexpr int N = Vc::N;
+  __shared__ __align__(16) float s_max[kThreads];
+  __shared__ int s_hist[256];
+  __shared__ int s_sel[2];
+  const int tid = threadIdx.x;
+  const int vb = ch * P.chunk_vecs;
+  typename Vc::Raw r[kFiltVpt]{};
+#pragma unroll
+  for (int u = 0; u < kFiltVpt; ++u) {
+    const int v = vb + u * kThreads + tid;
+    if (v < P.nvec) r[u] = Vc::load(base, roff, v);
+  }
+  // this thread's logits in registers, in ascending id order: fn(value, id)
+  auto each = [&](auto&& fn) {
+#pragma unroll
+    for (int u = 0; u < kFiltVpt; ++u) opaque(r[u]);
+#pragma unroll
+    for (int u = 0; u < kFiltVpt; ++u) {
+      const int v = vb + u * kThreads + tid;
+      if (v < P.nvec) {
+        float f[N];
+        Vc::get(r[u], f);
+#pragma unroll
+        for (int k = 0; k < N; ++k) fn(f[k], v * N + k);
+      }
+    }
+  };
+  float tmax = kNegInf;
+  int bad = 0;
+  each([&](float f, int) {
+    bad |= is_nan_or_posinf(f);
+    if (__builtin_isfinite(f)) tmax = fmaxf(tmax, f);
+  });
+  // Bound: the largest thread maximum that at least k thread maxima reach; k
+  // threads then hold a finite logit >= it, so it is <= the k-th largest.
+  const int k = P.top_k;
+  float lb = kNegInf;
+  if (k <= kBoundMaxK) {
+    s_max[tid] = tmax;
+    __syncthreads();
+    int ge = 0;
+    for (int j = 0; j < kThreads; j += 4) {
+      const float4 t = *reinterpret_cast<const float4*>(&s_max[j]);
+      ge += (t.x >= tmax) + (t.y >= tmax) + (t.z >= tmax) + (t.w >= tmax);
+    }
+    lb = block_max_f((ge >= k && tmax != kNegInf) ? tmax : kNegInf);
+  }
+  const int flags = block_sum_i(bad) ? kRecFlagBad : 0;
+  unsigned* rec = P.rec + (size_t)g * P.rec_words;
+  unsigned* ent = rec + kRecHeader;
+  int cnt = 0;
+  each([&](float f, int) { cnt += (__builtin_isfinite(f) && f >= lb) ? 1 : 0; });
+  int total;
+  int off = block_excl_scan_i(cnt, total);
+  if (total <= P.kcap) {
+    each([&](float f, int id) {
+      if (__builtin_isfinite(f) && f >= lb) {
+        ent[2 * off] = __float_as_uint(f);
+        ent[2 * off + 1] = (unsigned)id;
+        ++off;
+      }
+    });
+    if (tid == 0) {
+      rec[0] = (unsigned)total;
+      rec[1] = 0u;
+      rec[2] = 0u;
+      rec[3] = (unsigned)flags;
+    }
+    return;
+  }
+  // Exact k-th largest finite logit of the chunk, one key byte at a time from
+  // the top (more than kcap > k candidates exist here).
+  unsigned prefix = 0u, mask = 0u;
+  int rem = k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    s_hist[tid] = 0;
+    __syncthreads();
+    each([&](float f, int) {
+      if (__builtin_isfinite(f) && f >= lb) {
+        const unsigned key = key_of(f);
+        if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1);
+      }
+    });
+    __syncthreads();
+    if (tid == 0) {
+      int acc = 0, b = 255;
+      for (; b > 0; --b) {
+        if (acc + s_hist[b] >= rem) break;
+        acc += s_hist[b];
+      }
+      s_sel[0] = b;
+      s_sel[1] = rem - acc;
+    }
+    __syncthreads();
+    prefix |= (unsigned)s_sel[0] << shift;
+    mask |= 255u << shift;
+    rem = s_sel[1];
+    __syncthreads();
+  }
+  const float tau = float_of_key(prefix);
+  int gt = 0, eq = 0;
+  each([&](float f, int) {
+    if (__builtin_isfinite(f)) {
+      gt += f > tau;
+      eq += f == tau;
+    }
+  });
+  const int gt_tot = block_sum_i(gt);
+  const int eq_tot = block_sum_i(eq);
+  const bool ties_fit = gt_tot + eq_tot <= P.kcap;  // gt_tot < k <= kcap always
+  cnt = 0;
+  each([&](float f, int) {
+    cnt += (__builtin_isfinite(f) && (f > tau || (ties_fit && f == tau))) ? 1 : 0;
+  });
+  off = block_excl_scan_i(cnt, total);
+  each([&](float f, int id) {
+    if (__builtin_isfinite(f) && (f > tau || (ties_fit && f == tau))) {
+      ent[2 * off] = __float_as_uint(f);
+      ent[2 * off + 1] = (unsigned)id;
+      ++off;
+    }
+  });
+  if (tid == 0) {
+    rec[0] = (unsigned)total;
+    rec[1] = __float_as_uint(tau);
+    rec[2] = ties_fit ? 0u : (unsigned)eq_tot;
+    rec[3] = (unsigned)(flags | (ties_fit ? 0 : kRecFlagImplicitTies));
+  }
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ k_stats
 // Block g (after the offset stats_block0) covers chunk g % chunks of unit
 // g / chunks: draft row u for u < total_draft, else target row u - total_draft.
 // Its partial goes to slots[g].
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool FILT>
 __global__ __launch_bounds__(kThreads) void k_stats(const Params P) {
   using Vc = Vec<DT, VEC>;
   constexpr int N = Vc::N;
@@ -454,6 +633,12 @@ __global__ __launch_bounds__(kThreads) void k_stats(const Params P) {
   if (greedy && !is_target) return;  // greedy sequences never read draft rows
   const void* base = is_target ? P.target : P.draft;
   const size_t roff = (size_t)row * (size_t)P.V;
+  if constexpr (FILT) {
+    if (!greedy) {
+      topk_block<DT, VEC>(P, g, base, roff, ch);
+      return;
+    }
+  }
   const int vb = ch * P.chunk_vecs;
   const int ve = min(P.nvec, vb + P.chunk_vecs);
   int v = vb + tid;
@@ -529,6 +714,184 @@ __global__ __launch_bounds__(kThreads) void k_stats(const Params P) {
     packed = pack_ms(m, s);
   }
   P.slots[g] = packed;
+}
+
+// ----------------------------------------------------------------- k_filter
+// One block per filtered sampling row: the row's k-th largest finite logit tau
+// (radix select over its chunk records, tie classes counted with their
+// multiplicity), then the kept levels above it sorted in descending order, the
+// softmax masses 2^(l*c - R) of those levels, and the top-p cut: a level stays
+// iff the mass of the strictly larger kept levels, over the top-k mass, is
+// below top_p. The row keeps every id with l >= theta (the smallest kept level).
+// Pages: aihero.vn "Speculative decoding", section "Cùng phân bố không có
+// nghĩa cùng chuỗi mỗi lần" (the same temperature, top-k and top-p on both
+// models' rows).
+__global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
+  __shared__ int s_hist[256];
+  __shared__ int s_sel[2];
+  __shared__ int s_n;
+  __shared__ float s_v[kFilterMaxLevels];
+  __shared__ float s_w[kFilterMaxLevels];
+  __shared__ int s_cu[kCuLds];
+  const int tid = threadIdx.x;
+  const int unit = blockIdx.x;
+  const bool is_target = unit >= P.total_draft;
+  const int row = is_target ? unit - P.total_draft : unit;
+  if (P.greedy != nullptr && P.greedy[row_seq(P, row, is_target, s_cu)] != 0) return;
+  const int C = P.chunks;
+  const unsigned* rec0 = P.rec + (size_t)unit * C * P.rec_words;
+  int n_fin = 0, bad = 0;
+  for (int ch = tid; ch < C; ch += kThreads) {
+    const unsigned* h = rec0 + (size_t)ch * P.rec_words;
+    n_fin += min((int)h[0], P.kcap) + ((h[3] & kRecFlagImplicitTies) ? (int)h[2] : 0);
+    bad |= (int)(h[3] & kRecFlagBad);
+  }
+  n_fin = block_sum_i(n_fin);
+  bad = block_sum_i(bad);
+  const int k = P.top_k;
+  float tau = kNegInf;  // more than k finite logits: the k-th largest
+  if (n_fin > k) {
+    unsigned prefix = 0u, mask = 0u;
+    int rem = k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      s_hist[tid] = 0;
+      __syncthreads();
+      for (int ch = 0; ch < C; ++ch) {
+        const unsigned* h = rec0 + (size_t)ch * P.rec_words;
+        const int ne = min((int)h[0], P.kcap);
+        for (int e = tid; e < ne; e += kThreads) {
+          const unsigned key = key_of(__uint_as_float(h[kRecHeader + 2 * e]));
+          if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1);
+        }
+        if (tid == 0 && (h[3] & kRecFlagImplicitTies)) {
+          const unsigned key = key_of(__uint_as_float(h[1]));
+          if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], (int)h[2]);
+        }
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int acc = 0, b = 255;
+        for (; b > 0; --b) {
+          if (acc + s_hist[b] >= rem) break;
+          acc += s_hist[b];
+        }
+        s_sel[0] = b;
+        s_sel[1] = rem - acc;
+      }
+      __syncthreads();
+      prefix |= (unsigned)s_sel[0] << shift;
+      mask |= 255u << shift;
+      rem = s_sel[1];
+      __syncthreads();
+    }
+    tau = float_of_key(prefix);
+  }
+  // levels above tau (fewer than k logits, at most a few tie classes), then tau
+  if (tid == 0) s_n = 0;
+  __syncthreads();
+  int eq = 0;
+  for (int ch = 0; ch < C; ++ch) {
+    const unsigned* h = rec0 + (size_t)ch * P.rec_words;
+    const int ne = min((int)h[0], P.kcap);
+    for (int e = tid; e < ne; e += kThreads) {
+      const float v = __uint_as_float(h[kRecHeader + 2 * e]);
+      if (v > tau) {
+        const int at = atomicAdd(&s_n, 1);
+        if (at < kFilterMaxLevels) {
+          s_v[at] = v;
+          s_w[at] = 1.0f;
+        }
+      } else if (v == tau) {
+        ++eq;
+      }
+    }
+    if (tid == 0 && (h[3] & kRecFlagImplicitTies)) {
+      const float v = __uint_as_float(h[1]);
+      if (v > tau) {
+        const int at = atomicAdd(&s_n, 1);
+        if (at < kFilterMaxLevels) {
+          s_v[at] = v;
+          s_w[at] = (float)h[2];
+        }
+      } else if (v == tau) {
+        eq += (int)h[2];
+      }
+    }
+  }
+  eq = block_sum_i(eq);
+  if (tid == 0 && eq > 0 && s_n < kFilterMaxLevels) {
+    s_v[s_n] = tau;
+    s_w[s_n] = (float)eq;
+    ++s_n;
+  }
+  __syncthreads();
+  const int n = min(s_n, kFilterMaxLevels);
+  int p2 = 2;
+  while (p2 < n) p2 <<= 1;
+  for (int x = n + tid; x < p2; x += kThreads) {
+    s_v[x] = kNegInf;
+    s_w[x] = 0.0f;
+  }
+  __syncthreads();
+  // bitonic sort, descending by value
+  for (int size = 2; size <= p2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int x = tid; x < p2; x += kThreads) {
+        const int y = x ^ stride;
+        if (y > x) {
+          const bool desc = (x & size) == 0;
+          const float a = s_v[x], b = s_v[y];
+          if (desc ? (a < b) : (a > b)) {
+            s_v[x] = b;
+            s_v[y] = a;
+            const float t = s_w[x];
+            s_w[x] = s_w[y];
+            s_w[y] = t;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const float c = P.c;
+  const float m = n > 0 ? s_v[0] : kNegInf;
+  const float R = ref_of(m, c);
+  // masses in sorted order; each thread takes a contiguous run
+  const int per = (p2 + kThreads - 1) / kThreads;
+  const int x0 = min(tid * per, p2), x1 = min(x0 + per, p2);
+  float local = 0.0f;
+  for (int x = x0; x < x1; ++x) {
+    const float w = (x < n) ? s_w[x] * fast_exp2(fmaf(s_v[x], c, -R)) : 0.0f;
+    s_w[x] = w;
+    local += w;
+  }
+  float S_k;
+  const float incl = block_incl_scan(local, S_k);
+  // top-p: the last entry whose strictly-larger mass over S_k is below top_p
+  int last = n - 1;
+  if (P.top_p < 1.0f) {
+    float run = incl - local;
+    int cand = -1;
+    for (int x = x0; x < x1 && x < n; ++x) {
+      if (run / S_k < P.top_p) cand = x;
+      run += s_w[x];
+    }
+    last = block_max_i(cand);
+  }
+  const float theta = (n > 0 && last >= 0) ? s_v[last] : kPosInf;
+  float kept = 0.0f;
+  for (int x = x0; x < x1 && x < n; ++x)
+    if (s_v[x] >= theta) kept += s_w[x];
+  float S_f;
+  block_incl_scan(kept, S_f);
+  if (tid == 0) {
+    RowRes rr;
+    rr.m = m;
+    rr.s = S_f;
+    rr.theta = theta;
+    rr.flags = bad ? 1 : 0;
+    P.rowres[unit] = rr;
+  }
 }
 
 // ------------------------------------------------------------------- k_draw
@@ -614,17 +977,34 @@ __global__ void k_fill_zero(uint4* p, size_t n16) {
     p[k] = make_uint4(0, 0, 0, 0);
 }
 
+// Records stage event i (if the caller passed that many).
+static hipError_t stage_event(hipEvent_t* ev, int nev, int i, hipStream_t s) {
+  return (ev != nullptr && i < nev) ? hipEventRecord(ev[i], s) : hipSuccess;
+}
+
 template <int DT, bool VEC>
 static hipError_t launch_t(const Params& P, const Plan& L, hipStream_t s, hipEvent_t* ev, int nev) {
   hipError_t err;
-  if (nev > 0 && (err = hipEventRecord(ev[0], s)) != hipSuccess) return err;
-  if (L.stats_blocks > 0)
-    hipLaunchKernelGGL((k_stats<DT, VEC>), dim3((unsigned)L.stats_blocks), dim3(kThreads), 0, s, P);
+  int e = 0;
+  if ((err = stage_event(ev, nev, e++, s)) != hipSuccess) return err;
+  if (P.filt)
+    hipLaunchKernelGGL((k_stats<DT, VEC, true>), dim3((unsigned)L.stats_blocks), dim3(kThreads), 0,
+                       s, P);
+  else
+    hipLaunchKernelGGL((k_stats<DT, VEC, false>), dim3((unsigned)L.stats_blocks), dim3(kThreads),
+                       0, s, P);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (nev > 1 && (err = hipEventRecord(ev[1], s)) != hipSuccess) return err;
+  if ((err = stage_event(ev, nev, e++, s)) != hipSuccess) return err;
+  if (P.filt) {
+    hipLaunchKernelGGL(k_filter, dim3((unsigned)L.filter_blocks), dim3(kThreads), 0, s, P);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = stage_event(ev, nev, e++, s)) != hipSuccess) return err;
+  }
   hipLaunchKernelGGL((k_draw<DT, VEC>), dim3((unsigned)L.draw_blocks), dim3(kThreads), 0, s, P);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (nev > 2 && (err = hipEventRecord(ev[2], s)) != hipSuccess) return err;
+  // this and any further events: after the last kernel
+  for (; e < nev; ++e)
+    if ((err = stage_event(ev, nev, e, s)) != hipSuccess) return err;
   return hipSuccess;
 }
 

@@ -78,6 +78,8 @@ def _dense(L, **kw):
     (dict(tokens=None), -1), (dict(draft=None), -1), (dict(uniforms=None), -1),
     (dict(ws=None), -3), (dict(ws=ctypes.c_void_p(0x10010)), -3), (dict(), -3),
     (dict(top_k=2000, V=4096), -5),
+    (dict(top_k=0, top_p=0.9, V=4096), -5),  # top-p without top-k
+    (dict(top_k=4096, top_p=0.9, V=4096), -5),  # top-k off (k >= V), top-p on
 ])
 def test_dense_argument_errors(L, kw, code):
     assert _dense(L, **kw) == code
@@ -123,4 +125,8 @@ def test_workspace_sizes(L):
     # long rows take longer stats chunks, so the partials stay bounded per row
     assert 0 < ws(1, 0, 2048 * 2048, 0, 1.0) < ws(1, 0, 2 ** 30, 0, 1.0) < 64 << 20
     assert ws(512, 3840, 128256, 0, 1.0) >= ws(64, 512, 128256, 0, 1.0)
+    # top-k adds per-chunk candidate records and per-row results
+    assert ws(64, 512, 128256, 50, 0.9) > ws(64, 512, 128256, 0, 1.0)
+    assert ws(64, 512, 128256, 1024, 1.0) > ws(64, 512, 128256, 50, 1.0)
+    assert ws(64, 512, 128256, 128256, 1.0) == ws(64, 512, 128256, 0, 1.0)  # k >= V: off
     assert L.spec_verify_num_stages(0, 1.0) >= 1

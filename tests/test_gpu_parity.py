@@ -43,7 +43,9 @@ SMALL = [
     (W.HEADLINE, dict(B=6, sd_t=1.0)),
     (W.HEADLINE, dict(B=6, sd_t=4.0)),
     ("bf16_B512_Kragged_V128256_halfgreedy", dict(B=20)),
+    ("f16_B256_K4_V151936_topk50_topp0.9", dict(B=6)),
 ]
+FILTERED = "f16_B256_K4_V151936_topk50_topp0.9"
 
 
 @pytest.mark.parametrize("name,ov", SMALL, ids=[f"{n}-{i}" for i, (n, _) in enumerate(SMALL)])
@@ -51,7 +53,10 @@ def test_parity_with_diag(name, ov):
     _check(W.make(name, **ov), api="ragged", diag=True, tag="diag")
 
 
-@pytest.mark.parametrize("name,ov", SMALL[:5], ids=[f"{n}-{i}" for i, (n, _) in enumerate(SMALL[:5])])
+DENSE = SMALL[:5] + SMALL[6:]
+
+
+@pytest.mark.parametrize("name,ov", DENSE, ids=[f"{n}-{i}" for i, (n, _) in enumerate(DENSE)])
 def test_parity_dense_api(name, ov):
     _check(W.make(name, **ov), api="dense", diag=False, tag="dense")
 
@@ -63,6 +68,68 @@ def test_parity_headline_full_size(sd_t):
     gpu, ora, rep = _check(W.make(W.HEADLINE, sd_t=sd_t), api="dense", diag=False, tag="full")
     n = ora["num_accepted"]
     _say(f"      mean accepted={n.mean():.2f} all-accepted={(n == 8).mean():.2f}")
+
+
+def test_parity_filtered_full_size():
+    """B=256, K=4, V=151936 fp16, T=0.8, top-k 50 then top-p 0.9, every
+    sequence checked, through the dense entry point."""
+    gpu, ora, rep = _check(W.make(FILTERED), api="dense", diag=False, tag="full")
+    n = ora["num_accepted"]
+    _say(f"      mean accepted={n.mean():.2f}")
+
+
+# ------------------------------------------------------------- filter edges
+def _filtered(top_k, top_p, **ov):
+    w = W.make(FILTERED, **ov)
+    w["top_k"], w["top_p"] = top_k, top_p
+    return w
+
+
+@pytest.mark.parametrize("top_k,top_p", [(1, 1.0), (5, 1.0), (50, 0.5), (200, 0.95)])
+def test_filters_settings(top_k, top_p):
+    """top-k alone, top-k = 1 (a point mass per row), and tighter or looser
+    top-p after top-k; the candidate bound covers each k here."""
+    _check(_filtered(top_k, top_p, B=6, V=20000), api="ragged", diag=True,
+           tag=f"k={top_k} p={top_p}")
+
+
+@pytest.mark.parametrize("top_k", [257, 1024])
+def test_filters_large_k_exact_select(top_k):
+    """k beyond the per-thread bound: every chunk is cut by the exact select."""
+    _check(_filtered(top_k, 0.9, B=4, V=20000), api="ragged", diag=True, tag=f"k={top_k}")
+
+
+@pytest.mark.parametrize("step", [1.0, 4.0])
+def test_filters_heavy_ties(step):
+    """Logits rounded to a coarse grid: the k-th largest value is shared by
+    hundreds or thousands of ids, so chunks overflow their records and the
+    tie class at the cut is carried as a count."""
+    w = _filtered(50, 0.9, B=6, V=20000)
+    for key in ("draft", "target"):
+        t = w[key].float()
+        w[key] = (torch.round(t / step) * step).to(w[key].dtype)
+    _check(w, api="ragged", diag=True, tag=f"ties step={step}")
+
+
+def test_filters_masked_rows_and_scalar_path():
+    """Rows with most ids at -inf (fewer finite logits than k in some rows), on
+    an odd V (scalar path)."""
+    w = _filtered(50, 0.9, B=6, V=4099)
+    g = torch.Generator().manual_seed(7)
+    for key in ("draft", "target"):
+        t = w[key].float()
+        keep = torch.rand(t.shape, generator=g) < 0.01
+        keep[:, :3] = True  # every row keeps a few finite ids
+        t[~keep] = float("-inf")
+        w[key] = t.to(w[key].dtype)
+    _check(w, api="ragged", diag=True, tag="masked")
+
+
+def test_filters_with_greedy_mask_and_ragged():
+    """Filters on the sampling sequences of a ragged half-greedy batch."""
+    w = W.make("bf16_B512_Kragged_V128256_halfgreedy", B=10, V=30000)
+    w["top_k"], w["top_p"] = 40, 0.8
+    _check(w, api="ragged", diag=True, tag="greedy+filters")
 
 
 def test_parity_ragged_full_size():
