@@ -287,6 +287,42 @@ __device__ __forceinline__ int block_sum_i(int x) {
   return r;
 }
 
+// Radix-select step over a 256-bin histogram (whole block; wave 0 works):
+// the largest bin b with (count of bins above b) < rem <= (count of bins >= b),
+// written as s_sel[0] = b and s_sel[1] = rem - (count of bins above b).
+__device__ __forceinline__ void select_bin(const int* s_hist, int rem, int* s_sel) {
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    int c[4];
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c[j] = s_hist[255 - 4 * lane - j];  // lane 0 holds the top bins
+      sum += c[j];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    const unsigned long long hit = __ballot(incl >= rem);
+    const int first = hit ? (__ffsll(hit) - 1) : (kWave - 1);
+    if (lane == first) {
+      // walk this lane's four bins downward; if rem exceeds every count (not
+      // reachable for a valid rank) the lowest bin is taken
+      int acc = incl - sum;
+      int j = 0;
+      for (; j < 3; ++j) {
+        if (acc + c[j] >= rem) break;
+        acc += c[j];
+      }
+      s_sel[0] = 255 - 4 * lane - j;
+      s_sel[1] = rem - acc;
+    }
+  }
+}
+
 // Order-preserving 32-bit key of a non-NaN float (-0 and +0 share one key).
 __device__ __forceinline__ unsigned key_of(float f) {
   const unsigned u = __float_as_uint(f == 0.0f ? 0.0f : f);

@@ -100,6 +100,37 @@ __device__ __forceinline__ void opaque(uint4& x) {
 }
 __device__ __forceinline__ void opaque(float& x) { asm volatile("" : "+v"(x)); }
 
+// Element k (0 <= k < N, not a compile-time constant) of one raw vector.
+template <int DT>
+__device__ __forceinline__ float elem_of(const uint4& v, int k) {
+  if constexpr (DT == SV_F32) {
+    const unsigned w = (k & 2) ? ((k & 1) ? v.w : v.z) : ((k & 1) ? v.y : v.x);
+    return __uint_as_float(w);
+  } else {
+    const int q = k >> 1;
+    const unsigned w = (q & 2) ? ((q & 1) ? v.w : v.z) : ((q & 1) ? v.y : v.x);
+    const unsigned h = (k & 1) ? (w >> 16) : (w & 0xffffu);
+    if constexpr (DT == SV_BF16) return __uint_as_float(h << 16);
+    else return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+  }
+}
+template <int DT>
+__device__ __forceinline__ float elem_of(const float& v, int) { return v; }
+
+// Writes the elements of one raw vector whose bit is set in `bits` as (value
+// bits, id) pairs at ent[2*off ...], ids id0 + k in ascending order.
+template <int DT, class Raw>
+__device__ __forceinline__ void write_marked(const Raw vec, unsigned bits, int id0, unsigned* ent,
+                                             int& off) {
+  while (bits) {
+    const int k = __builtin_ctz(bits);
+    bits &= bits - 1u;
+    ent[2 * off] = __float_as_uint(elem_of<DT>(vec, k));
+    ent[2 * off + 1] = (unsigned)(id0 + k);
+    ++off;
+  }
+}
+
 // Weight of one id in the final draw: residual max(0, p - q) or bonus p, where
 // an id outside a row's kept set (l < threshold) has probability 0 in that row.
 __device__ __forceinline__ float draw_weight(float lp, float lq, const Job& j, float c) {
@@ -505,11 +536,12 @@ __device__ void topk_block(const Params& P, long long g, const void* base, size_
       }
     }
   };
+  // thread maximum (NaN ignored; a +inf makes the row invalid anyway)
   float tmax = kNegInf;
   int bad = 0;
   each([&](float f, int) {
     bad |= is_nan_or_posinf(f);
-    if (__builtin_isfinite(f)) tmax = fmaxf(tmax, f);
+    tmax = fmaxf(tmax, f);
   });
   // Bound: the largest thread maximum that at least k thread maxima reach; k
   // threads then hold a finite logit >= it, so it is <= the k-th largest.
@@ -528,18 +560,30 @@ __device__ void topk_block(const Params& P, long long g, const void* base, size_
   const int flags = block_sum_i(bad) ? kRecFlagBad : 0;
   unsigned* rec = P.rec + (size_t)g * P.rec_words;
   unsigned* ent = rec + kRecHeader;
-  int cnt = 0;
-  each([&](float f, int) { cnt += (__builtin_isfinite(f) && f >= lb) ? 1 : 0; });
+  // candidates: l >= lb, never -inf (an empty bound admits every finite logit);
+  // bit u*N + k of cmask marks element k of the thread's vector u
+  const float lb2 = (lb == kNegInf) ? -__FLT_MAX__ : lb;
+  static_assert(kFiltVpt * N <= 64, "candidate mask holds one bit per register element");
+  unsigned long long cmask = 0ull;
+#pragma unroll
+  for (int u = 0; u < kFiltVpt; ++u) opaque(r[u]);
+#pragma unroll
+  for (int u = 0; u < kFiltVpt; ++u) {
+    if (vb + u * kThreads + tid < P.nvec) {
+      float f[N];
+      Vc::get(r[u], f);
+#pragma unroll
+      for (int k2 = 0; k2 < N; ++k2)
+        if (f[k2] >= lb2) cmask |= 1ull << (u * N + k2);
+    }
+  }
   int total;
-  int off = block_excl_scan_i(cnt, total);
+  int off = block_excl_scan_i(__popcll(cmask), total);
   if (total <= P.kcap) {
-    each([&](float f, int id) {
-      if (__builtin_isfinite(f) && f >= lb) {
-        ent[2 * off] = __float_as_uint(f);
-        ent[2 * off + 1] = (unsigned)id;
-        ++off;
-      }
-    });
+#pragma unroll
+    for (int u = 0; u < kFiltVpt; ++u)
+      write_marked<DT>(r[u], (unsigned)(cmask >> (u * N)) & ((1u << N) - 1u),
+                       (vb + u * kThreads + tid) * N, ent, off);
     if (tid == 0) {
       rec[0] = (unsigned)total;
       rec[1] = 0u;
@@ -562,15 +606,7 @@ __device__ void topk_block(const Params& P, long long g, const void* base, size_
       }
     });
     __syncthreads();
-    if (tid == 0) {
-      int acc = 0, b = 255;
-      for (; b > 0; --b) {
-        if (acc + s_hist[b] >= rem) break;
-        acc += s_hist[b];
-      }
-      s_sel[0] = b;
-      s_sel[1] = rem - acc;
-    }
+    select_bin(s_hist, rem, s_sel);
     __syncthreads();
     prefix |= (unsigned)s_sel[0] << shift;
     mask |= 255u << shift;
@@ -588,20 +624,22 @@ __device__ void topk_block(const Params& P, long long g, const void* base, size_
   const int gt_tot = block_sum_i(gt);
   const int eq_tot = block_sum_i(eq);
   const bool ties_fit = gt_tot + eq_tot <= P.kcap;  // gt_tot < k <= kcap always
-  cnt = 0;
+  int cnt = 0;
   each([&](float f, int) {
     cnt += (__builtin_isfinite(f) && (f > tau || (ties_fit && f == tau))) ? 1 : 0;
   });
   off = block_excl_scan_i(cnt, total);
+  // (the bound holds for any row with at least k finite logits; the guard keeps
+  // an invalid row, e.g. one full of +inf, inside its record)
   each([&](float f, int id) {
-    if (__builtin_isfinite(f) && (f > tau || (ties_fit && f == tau))) {
+    if (__builtin_isfinite(f) && (f > tau || (ties_fit && f == tau)) && off < P.kcap) {
       ent[2 * off] = __float_as_uint(f);
       ent[2 * off + 1] = (unsigned)id;
       ++off;
     }
   });
   if (tid == 0) {
-    rec[0] = (unsigned)total;
+    rec[0] = (unsigned)min(total, P.kcap);
     rec[1] = __float_as_uint(tau);
     rec[2] = ties_fit ? 0u : (unsigned)eq_tot;
     rec[3] = (unsigned)(flags | (ties_fit ? 0 : kRecFlagImplicitTies));
@@ -732,6 +770,9 @@ __global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
   __shared__ int s_n;
   __shared__ float s_v[kFilterMaxLevels];
   __shared__ float s_w[kFilterMaxLevels];
+  __shared__ unsigned s_key[kFilterLdsKeys];
+  __shared__ unsigned s_hdr[kFilterLdsChunks][4];
+  __shared__ int s_off[kFilterLdsChunks + 1];
   __shared__ int s_cu[kCuLds];
   const int tid = threadIdx.x;
   const int unit = blockIdx.x;
@@ -740,12 +781,79 @@ __global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
   if (P.greedy != nullptr && P.greedy[row_seq(P, row, is_target, s_cu)] != 0) return;
   const int C = P.chunks;
   const unsigned* rec0 = P.rec + (size_t)unit * C * P.rec_words;
-  int n_fin = 0, bad = 0;
-  for (int ch = tid; ch < C; ch += kThreads) {
-    const unsigned* h = rec0 + (size_t)ch * P.rec_words;
-    n_fin += min((int)h[0], P.kcap) + ((h[3] & kRecFlagImplicitTies) ? (int)h[2] : 0);
-    bad |= (int)(h[3] & kRecFlagBad);
+  // Stage the records in LDS when they fit: headers, then every entry's key.
+  bool staged = C <= kFilterLdsChunks;
+  int E = 0;
+  if (staged) {
+    if (tid < C) {
+      const unsigned* h = rec0 + (size_t)tid * P.rec_words;
+      s_hdr[tid][0] = min(h[0], (unsigned)P.kcap);
+      s_hdr[tid][1] = h[1];
+      s_hdr[tid][2] = h[2];
+      s_hdr[tid][3] = h[3];
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      int incl = tid < C ? (int)s_hdr[tid][0] : 0;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (tid >= o) incl += y;
+      }
+      s_off[tid + 1] = incl;
+      if (tid == 0) s_off[0] = 0;
+    }
+    __syncthreads();
+    E = s_off[C];
+    staged = E <= kFilterLdsKeys;
+    if (staged) {
+      for (int i0 = tid; i0 < E; i0 += 4 * kThreads) {
+        unsigned val[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = i0 + j * kThreads;
+          val[j] = 0u;
+          if (i < E) {
+            int lo = 0, hi = C - 1;  // chunk of entry i: the last with s_off <= i
+            while (lo < hi) {
+              const int mid = (lo + hi + 1) >> 1;
+              if (s_off[mid] <= i) lo = mid;
+              else hi = mid - 1;
+            }
+            val[j] = rec0[(size_t)lo * P.rec_words + kRecHeader + 2 * (i - s_off[lo])];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = i0 + j * kThreads;
+          if (i < E) s_key[i] = key_of(__uint_as_float(val[j]));
+        }
+      }
+      __syncthreads();
+    }
   }
+  // fn(key, multiplicity) over every explicit entry and implicit tie class,
+  // spread over the block's threads
+  auto for_entries = [&](auto&& fn) {
+    if (staged) {
+      for (int i = tid; i < E; i += kThreads) fn(s_key[i], 1);
+      if (tid < C && (s_hdr[tid][3] & kRecFlagImplicitTies))
+        fn(key_of(__uint_as_float(s_hdr[tid][1])), (int)s_hdr[tid][2]);
+    } else {
+      for (int ch = 0; ch < C; ++ch) {
+        const unsigned* h = rec0 + (size_t)ch * P.rec_words;
+        const int ne = min((int)h[0], P.kcap);
+        for (int e = tid; e < ne; e += kThreads)
+          fn(key_of(__uint_as_float(h[kRecHeader + 2 * e])), 1);
+        if (tid == 0 && (h[3] & kRecFlagImplicitTies))
+          fn(key_of(__uint_as_float(h[1])), (int)h[2]);
+      }
+    }
+  };
+  int n_fin = 0, bad = 0;
+  for_entries([&](unsigned, int cnt) { n_fin += cnt; });
+  for (int ch = tid; ch < C; ch += kThreads)
+    bad |= (int)(rec0[(size_t)ch * P.rec_words + 3] & kRecFlagBad);
   n_fin = block_sum_i(n_fin);
   bad = block_sum_i(bad);
   const int k = P.top_k;
@@ -756,28 +864,11 @@ __global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
     for (int shift = 24; shift >= 0; shift -= 8) {
       s_hist[tid] = 0;
       __syncthreads();
-      for (int ch = 0; ch < C; ++ch) {
-        const unsigned* h = rec0 + (size_t)ch * P.rec_words;
-        const int ne = min((int)h[0], P.kcap);
-        for (int e = tid; e < ne; e += kThreads) {
-          const unsigned key = key_of(__uint_as_float(h[kRecHeader + 2 * e]));
-          if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1);
-        }
-        if (tid == 0 && (h[3] & kRecFlagImplicitTies)) {
-          const unsigned key = key_of(__uint_as_float(h[1]));
-          if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], (int)h[2]);
-        }
-      }
+      for_entries([&](unsigned key, int cnt) {
+        if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], cnt);
+      });
       __syncthreads();
-      if (tid == 0) {
-        int acc = 0, b = 255;
-        for (; b > 0; --b) {
-          if (acc + s_hist[b] >= rem) break;
-          acc += s_hist[b];
-        }
-        s_sel[0] = b;
-        s_sel[1] = rem - acc;
-      }
+      select_bin(s_hist, rem, s_sel);
       __syncthreads();
       prefix |= (unsigned)s_sel[0] << shift;
       mask |= 255u << shift;
@@ -790,34 +881,18 @@ __global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
   if (tid == 0) s_n = 0;
   __syncthreads();
   int eq = 0;
-  for (int ch = 0; ch < C; ++ch) {
-    const unsigned* h = rec0 + (size_t)ch * P.rec_words;
-    const int ne = min((int)h[0], P.kcap);
-    for (int e = tid; e < ne; e += kThreads) {
-      const float v = __uint_as_float(h[kRecHeader + 2 * e]);
-      if (v > tau) {
-        const int at = atomicAdd(&s_n, 1);
-        if (at < kFilterMaxLevels) {
-          s_v[at] = v;
-          s_w[at] = 1.0f;
-        }
-      } else if (v == tau) {
-        ++eq;
+  for_entries([&](unsigned key, int cnt) {
+    const float v = float_of_key(key);
+    if (v > tau) {
+      const int at = atomicAdd(&s_n, 1);
+      if (at < kFilterMaxLevels) {
+        s_v[at] = v;
+        s_w[at] = (float)cnt;
       }
+    } else if (v == tau) {
+      eq += cnt;
     }
-    if (tid == 0 && (h[3] & kRecFlagImplicitTies)) {
-      const float v = __uint_as_float(h[1]);
-      if (v > tau) {
-        const int at = atomicAdd(&s_n, 1);
-        if (at < kFilterMaxLevels) {
-          s_v[at] = v;
-          s_w[at] = (float)h[2];
-        }
-      } else if (v == tau) {
-        eq += (int)h[2];
-      }
-    }
-  }
+  });
   eq = block_sum_i(eq);
   if (tid == 0 && eq > 0 && s_n < kFilterMaxLevels) {
     s_v[s_n] = tau;
