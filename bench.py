@@ -8,9 +8,9 @@ rows from the previous step.
 
 Prints one JSON line: verified (sequence, position) rows per second, effective
 HBM bandwidth of the compulsory bytes, a roofline entry for the dominant kernel
-(the row-statistics pass: its algorithmic bytes over its HIP-event duration on
-the launch stream) and the CPU oracle timed on a bounded sample of the same
-workload.
+(the fused verification kernel, or the statistics pass of a filtered call: its
+algorithmic bytes over its HIP-event duration on the launch stream) and the CPU
+oracle timed on a bounded sample of the same workload.
 """
 
 import argparse
@@ -31,8 +31,13 @@ import workloads as W  # noqa: E402
 
 PEAK_HBM_GBPS = 8000.0
 METRIC = "verified rows/sec + effective HBM GB/s (% of ~8 TB/s), B=64 K=8 V=128256 bf16"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_stats_bf16_B64_K8_V128256_traffic.json")
-DOMINANT = "k_stats"
+# kernels of a call, in launch order: one fused kernel without filters; the
+# statistics, filter and draw passes with top-k
+STAGES = {1: ["k_verify"], 3: ["k_stats", "k_filter", "k_draw"]}
+
+
+def traffic_file(kernel, workload):
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
 
 
 class HipEvents:
@@ -216,6 +221,8 @@ def main():
     stage_ms = per_stage.mean(axis=0).tolist()
     k1_ms = stage_ms[0]
 
+    names = STAGES.get(nst - 1, [f"stage{i}" for i in range(nst - 1)])
+    dominant = names[0]
     rows = int((w["Ks"] + 1).sum())
     comp = W.compulsory_bytes(w)
     esize = target0.element_size()
@@ -227,8 +234,9 @@ def main():
 
     n_acc = num.cpu().numpy()
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
+    tfile = traffic_file(dominant, args.workload)
+    if os.path.exists(tfile):
+        with open(tfile) as f:
             tr = json.load(f)
         if tr.get("source_sha256") == kernel_source_digest() and tr.get("workload") == args.workload \
                 and args.sd_t in (None, tr.get("sd_t")):
@@ -257,13 +265,12 @@ def main():
         "effective_frac_of_peak": eff / PEAK_HBM_GBPS,
         "compulsory_bytes_per_step": comp,
         "roofline": {
-            "kernel": DOMINANT, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
+            "kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
             "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
             "algorithmic_bytes_per_launch": algo_bytes_k1, "avg_launch_ms": k1_ms,
         },
         "stage_ms": dict(
-            zip(["k_stats", "k_filter", "k_draw"] if len(stage_ms) == 3 else ["k_stats", "k_draw"],
-                stage_ms),
+            zip(names, stage_ms),
             call_mean=float(per_call.mean()), call_median=float(np.median(per_call)),
             ms_per_step_with_stage_events=ms_step_events),
         "acceptance": {

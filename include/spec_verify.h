@@ -76,8 +76,8 @@ typedef enum sv_dtype { SV_F32 = 0, SV_F16 = 1, SV_BF16 = 2 } sv_dtype;
 #define SV_EHIP (-4)         /* a HIP launch or event record failed */
 #define SV_EUNSUPPORTED (-5) /* valid request outside this build's limits:
                                 top_k above SV_MAX_TOP_K, top_p < 1 without
-                                an active top_k (0 < top_k < V), or a grid of
-                                more than 2^24 blocks */
+                                an active top_k (0 < top_k < V), V above
+                                2^30, or a grid of more than 2^24 blocks */
 
 /* Per-sequence codes written to num_accepted[b] instead of a count. */
 #define SV_SEQ_BAD_TOKEN (-1)   /* a draft id outside [0, V) */
@@ -85,6 +85,9 @@ typedef enum sv_dtype { SV_F32 = 0, SV_F16 = 1, SV_BF16 = 2 } sv_dtype;
                                    value (greedy: target rows only) */
 #define SV_SEQ_BAD_OFFSETS (-3) /* ragged offsets: cu[b] > cu[b+1], outside
                                    [0, total_draft_rows], or K_b > 64 */
+#define SV_SEQ_SYNC_TIMEOUT (-4) /* a bounded wait for the sequence's row
+                                    statistics ran out; its outputs are not
+                                    valid */
 
 #define SV_MAX_K 64
 #define SV_MAX_TOP_K 1024
@@ -100,12 +103,13 @@ size_t spec_verify_workspace_bytes(int B, int total_draft_rows, int V, int top_k
                                    float top_p);
 
 /* Zero-fill a workspace on `stream` (kernel fill, no memset node). A workspace
- * must be zero-filled once before its first use: it holds per-sequence
- * counters that must read zero when a call starts. Every call returns them to
- * zero before it ends (also for sequences that report an error), so calls that
- * share one workspace may differ in B, K, V and dtype, as long as it is large
- * enough for each of them. The rest of the workspace holds per-row partial
- * results that each call writes before it reads them. */
+ * must be zero-filled once before its first use: blocks of one call hand
+ * per-row partial results to each other through it, and a zero entry means
+ * "not yet published". Every call returns those entries and its per-sequence
+ * counters to zero before it ends, so calls that share one workspace may differ
+ * in B, K, V and dtype, as long as it is large enough for each of them. After a
+ * call that reports SV_SEQ_SYNC_TIMEOUT or SV_SEQ_BAD_OFFSETS for any sequence,
+ * zero-fill the workspace again. */
 int spec_verify_workspace_init(void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
@@ -153,7 +157,10 @@ int spec_verify_ragged(const void* draft_logits, const void* target_logits,
  *                beyond the kernel count are recorded after the last kernel.
  *                Without filters the kernels are the row statistics pass and
  *                the decision-and-draw pass; with top-k a per-row filter pass
- *                (threshold and kept-set normaliser) runs between them. */
+ *                (threshold and kept-set normaliser) runs between them;
+ *                without filters both run in one kernel.
+ *   spin_limit   bound of a wait for row statistics (0: default); a small
+ *                value forces the SV_SEQ_SYNC_TIMEOUT path in tests. */
 typedef struct sv_diag {
   float* row_max_draft;
   float* row_logsum_draft;
@@ -163,6 +170,7 @@ typedef struct sv_diag {
   float* resid_Z;
   hipEvent_t* stage_events;
   int n_stage_events;
+  int spin_limit;
 } sv_diag;
 
 /* Number of kernels a call launches for these settings (stage events = this+1). */

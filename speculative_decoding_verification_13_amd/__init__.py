@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     SV_SEQ_BAD_OFFSETS,
     SV_SEQ_BAD_ROW,
     SV_SEQ_BAD_TOKEN,
+    SV_SEQ_SYNC_TIMEOUT,
     SpecVerifyError,
     lib,
     make_stage_events,

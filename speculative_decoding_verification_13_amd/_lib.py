@@ -18,6 +18,7 @@ SV_OK = 0
 SV_SEQ_BAD_TOKEN = -1
 SV_SEQ_BAD_ROW = -2
 SV_SEQ_BAD_OFFSETS = -3
+SV_SEQ_SYNC_TIMEOUT = -4
 SV_MAX_K = 64
 
 DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
@@ -34,7 +35,7 @@ class SvDiag(ctypes.Structure):
         ("row_max_draft", _P), ("row_logsum_draft", _P),
         ("row_max_target", _P), ("row_logsum_target", _P),
         ("ratio", _P), ("resid_Z", _P),
-        ("stage_events", _P), ("n_stage_events", _I),
+        ("stage_events", _P), ("n_stage_events", _I), ("spin_limit", _I),
     ]
 
 
@@ -155,8 +156,9 @@ def spec_verify_ragged(draft_logits, target_logits, draft_tokens, uniforms, cu_d
 
     cu_draft int32 [B+1] and greedy uint8 [B] (or None) live on the device;
     ``total_draft_rows`` defaults to draft_tokens.numel(). With ``diag`` (a dict
-    of optional float32 device tensors and a list of events or raw hipEvent_t
-    handles under 'stage_events') the diag entry point is used. Returns (out_tokens, num_accepted)."""
+    of optional float32 device tensors, a list of events or raw hipEvent_t
+    handles under 'stage_events', and an int 'spin_limit') the diag entry point
+    is used. Returns (out_tokens, num_accepted)."""
     dev = target_logits.device
     n_draft = int(draft_tokens.numel()) if total_draft_rows is None else int(total_draft_rows)
     if out_tokens is None:
@@ -178,6 +180,7 @@ def spec_verify_ragged(draft_logits, target_logits, draft_tokens, uniforms, cu_d
             t = diag.get(name)
             setattr(d, name, None if t is None else t.data_ptr())
         events = diag.get("stage_events")
+        d.spin_limit = int(diag.get("spin_limit", 0))
         keep = None
         if events:
             handles = [ev if isinstance(ev, int) else ev.cuda_event for ev in events]

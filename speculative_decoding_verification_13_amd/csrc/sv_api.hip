@@ -13,6 +13,8 @@
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr int kMaxV = 1 << 30;             // a greedy partial holds a 30-bit argmax
+constexpr int kDefaultSpinLimit = 1 << 16;  // iterations of a bounded wait (~1 us each)
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -37,19 +39,21 @@ bool filters_active(int V, int top_k, float top_p) {
 int kcap_for(int top_k) { return (top_k + 256 + 63) / 64 * 64; }
 
 // Workspace layout (per call):
-//   draw_done[B]                           per-sequence counters, zero between calls
+//   draw_done[B], seq_flags[B]             per-sequence counter and status bits
 //   slots[(total_draft + rows) * cmax]     64-bit chunk partials (greedy rows, and
-//                                          every row when no filter is active)
+//                                          every row when no filter is active);
+//                                          zero means "not yet published"
 //   tiles[B * dmax * tiles per draw block] draw-weight tile sums
 // and with top-k active:
 //   rec[(total_draft + rows) * cmax * rec_words]  chunk records of sampling rows
 //   rowres[total_draft + rows]                    kept-set statistics per row
-// Only the counters must be zero when a call starts, and every call leaves
-// them zero, so the layout may differ from call to call. The regions are sized
-// for the scalar path (one element per vector), which has the most chunks:
-// a row of nvec <= V vectors never has more than cmax chunks.
+// Counters, flags, partials and tile sums must be zero when a call starts; the
+// blocks that read them return them to zero, so the layout may differ from call
+// to call. The regions are sized for the scalar path (one element per vector),
+// which has the most chunks: a row of nvec <= V vectors never has more than
+// cmax chunks.
 bool make_plan(int B, int total_draft, int V, int top_k, size_t ws_bytes, sv::Plan& L) {
-  if (B < 0 || total_draft < 0 || V < 1) return false;
+  if (B < 0 || total_draft < 0 || V < 1 || V > kMaxV) return false;
   const long long rows = (long long)total_draft + B;
   if (rows > INT_MAX) return false;
   const size_t units = (size_t)(total_draft + rows);
@@ -65,6 +69,8 @@ bool make_plan(int B, int total_draft, int V, int top_k, size_t ws_bytes, sv::Pl
   const long long dmax = ((long long)V + sv::kDrawVecs - 1) / sv::kDrawVecs;
   size_t off = 0;
   L.off_draw_done = off;
+  off += align_up((size_t)B * 4);
+  L.off_seq_flags = off;
   off += align_up((size_t)B * 4);
   L.off_slots = off;
   off += align_up(units * (size_t)cmax * 8);
@@ -154,14 +160,16 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
   P.slots = reinterpret_cast<unsigned long long*>(ws + L.off_slots);
   P.tiles = reinterpret_cast<float*>(ws + L.off_tiles);
   P.draw_done = reinterpret_cast<int*>(ws + L.off_draw_done);
+  P.seq_flags = reinterpret_cast<int*>(ws + L.off_seq_flags);
+  P.spin_limit = (diag != nullptr && diag->spin_limit > 0) ? diag->spin_limit : kDefaultSpinLimit;
   L.chunks = P.chunks;
   L.chunk_vecs = P.chunk_vecs;
   L.dchunks = P.dchunks;
   L.stats_blocks = ((long long)total_draft + P.rows) * P.chunks - P.stats_block0;
   L.filter_blocks = filt ? (long long)total_draft + P.rows : 0;
   L.draw_blocks = (long long)B * P.dchunks;
-  if (L.stats_blocks > (long long)UINT32_MAX / sv::kThreads ||
-      L.draw_blocks > (long long)UINT32_MAX / sv::kThreads)
+  P.stats_blocks = L.stats_blocks;
+  if (L.stats_blocks + L.draw_blocks > (long long)UINT32_MAX / sv::kThreads)
     return SV_EUNSUPPORTED;
   hipEvent_t* ev = nullptr;
   int nev = 0;
@@ -207,7 +215,7 @@ int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, hipStrea
 }
 
 int spec_verify_num_stages(int top_k, float top_p) {
-  return (top_k > 0 || top_p < 1.0f) ? 3 : 2;
+  return (top_k > 0 || top_p < 1.0f) ? 3 : 1;
 }
 
 int spec_verify(const void* draft_logits, const void* target_logits, const int32_t* draft_tokens,

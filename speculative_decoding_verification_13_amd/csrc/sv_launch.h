@@ -42,6 +42,9 @@ struct RowRes {
   int flags;
 };
 
+// Per-sequence status bits raised by any block (cleared when the sequence ends).
+enum { kSeqFlagTimeout = 1 };
+
 enum { kJobNone = 0, kJobResidual = 1, kJobBonus = 2 };
 
 // Final draw of one sequence (every draw block of the sequence derives it).
@@ -82,6 +85,8 @@ struct Params {
   int nvec;                // vectors (or elements, scalar path) per row
   int ntiles;              // draw tiles per row = dchunks * kTilesPerDraw
   long long stats_block0;  // first stats block (skips draft rows when all greedy)
+  long long stats_blocks;  // stats blocks launched (the fused grid's draw blocks follow)
+  int spin_limit;          // bound of every wait (iterations)
   int filt;                // 1: top-k (and top-p) filters active
   int top_k;
   float top_p;
@@ -91,11 +96,14 @@ struct Params {
   RowRes* rowres;          // [total_draft + rows] (filtered)
   int32_t* out_tokens;
   int32_t* num_accepted;
-  // Chunk partials, 64-bit: sampling (max, sum) floats; greedy (max value,
-  // argmax and bad flag). Draft rows first, then target rows, chunks innermost.
+  // Chunk partials, 64-bit and never zero once written (zero: not yet
+  // published; the readers return them to zero): sampling (max, sum) floats;
+  // greedy (max value, tagged argmax and bad flag). Draft rows first, then
+  // target rows, chunks innermost.
   unsigned long long* slots;  // [(total_draft + rows) * chunks]
   float* tiles;            // [B * ntiles] draw-weight tile sums
   int* draw_done;          // [B] draw blocks finished per sequence (zero between calls)
+  int* seq_flags;          // [B] kSeqFlag* bits (zero between calls)
   DiagPtrs diag;
 };
 
@@ -103,7 +111,7 @@ struct Params {
 struct Plan {
   int chunks, chunk_vecs, dchunks;
   long long stats_blocks, filter_blocks, draw_blocks;
-  size_t off_slots, off_tiles, off_draw_done, off_rec, off_rowres, total_bytes;
+  size_t off_slots, off_tiles, off_draw_done, off_seq_flags, off_rec, off_rowres, total_bytes;
 };
 
 hipError_t launch(int dtype, bool vec, const Params& P, const Plan& L, hipStream_t s,

@@ -33,7 +33,7 @@ namespace sv {
 
 namespace {
 
-constexpr int kCuLds = 2048;  // offsets staged in LDS for the row -> sequence search
+constexpr int kCuLds = 1024;  // offsets staged in LDS for the row -> sequence search
 
 __device__ __forceinline__ bool seq_bounds(const Params& P, int b, int& d0, int& kb) {
   if (P.cu == nullptr) {
@@ -53,7 +53,8 @@ __device__ __forceinline__ bool seq_greedy(const Params& P, int b) {
   return P.all_greedy || (P.greedy != nullptr && P.greedy[b] != 0);
 }
 
-// (max, sum) of a sampling chunk; NaN is stored canonical.
+// (max, sum) of a sampling chunk; NaN is stored canonical. Never all-zero
+// bits: a +0 maximum brings a term 2^0 = 1 into the sum.
 __device__ __forceinline__ unsigned long long pack_ms(float m, float s) {
   if (m != m) m = __builtin_nanf("");
   return ((unsigned long long)__float_as_uint(s) << 32) | __float_as_uint(m);
@@ -62,16 +63,47 @@ __device__ __forceinline__ void unpack_ms(unsigned long long v, float& m, float&
   m = __uint_as_float((unsigned)v);
   s = __uint_as_float((unsigned)(v >> 32));
 }
-// (max value, argmax, bad flag) of a greedy chunk.
+// (max value, argmax, bad flag) of a greedy chunk: the high word has bit 31
+// set (so the slot is never zero), bit 30 the bad flag, bits 0-29 the argmax
+// (an empty chunk's "no index" maps to 2^30 - 1).
 __device__ __forceinline__ unsigned long long pack_am(float v, int idx, int bad) {
-  const unsigned hi = (bad ? 0x80000000u : 0u) | ((unsigned)idx & 0x7fffffffu);
+  const unsigned hi = 0x80000000u | (bad ? 0x40000000u : 0u) | ((unsigned)idx & 0x3fffffffu);
   return ((unsigned long long)hi << 32) | __float_as_uint(v);
 }
 __device__ __forceinline__ void unpack_am(unsigned long long p, float& v, int& idx, int& bad) {
   v = __uint_as_float((unsigned)p);
   const unsigned hi = (unsigned)(p >> 32);
-  idx = (int)(hi & 0x7fffffffu);
-  bad = (hi & 0x80000000u) ? 1 : 0;
+  idx = (int)(hi & 0x3fffffffu);
+  bad = (hi & 0x40000000u) ? 1 : 0;
+}
+
+// A slot read: a plain load after a kernel boundary, an agent-scope load when
+// its writer may still be running in the same grid.
+template <bool POLL>
+__device__ __forceinline__ unsigned long long slot_load(const unsigned long long* p) {
+  if constexpr (POLL) return obs_u64(p);
+  else return *p;
+}
+// Bounded wait for the slots of one batch that read zero (unpublished): every
+// missing slot is read again in each round, so one round trip covers them all.
+// Slots past the batch end hold a nonzero placeholder. Sets `to` on timeout.
+template <int G>
+__device__ __forceinline__ void slots_wait(const unsigned long long* p, unsigned long long* v,
+                                           int limit, int& to) {
+  for (int spins = 0;; ++spins) {
+    bool missing = false;
+#pragma unroll
+    for (int g = 0; g < G; ++g) missing |= v[g] == 0ull;
+    if (!missing) return;
+    if (spins >= limit) {
+      to = 1;
+      return;
+    }
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      if (v[g] == 0ull) v[g] = obs_u64(p + g);
+  }
 }
 
 // One 16-byte vector (or one element on the scalar path) of a row.
@@ -164,15 +196,23 @@ __device__ __forceinline__ void block_sum8(const float* v, float* out) {
 }
 
 // First tile whose inclusive prefix exceeds u*Z (else the last tile with mass).
-// Tile sums are read with agent-scope loads (published by other blocks).
+// Tile sums are read once with agent-scope loads (published by other blocks);
+// a thread's first kTileKeep sums stay in registers for the second walk.
 __device__ __forceinline__ int find_tile(const float* ts, int ntiles, float u, float& Z,
                                          float& target, float& base) {
+  constexpr int kTileKeep = 4;
   __shared__ float s_base;
   const int per = (ntiles + kThreads - 1) / kThreads;
   const int t0 = threadIdx.x * per;
   const int t1 = min(ntiles, t0 + per);
+  float keep[kTileKeep];
   float local = 0.f;
-  for (int t = t0; t < t1; ++t) local += obs_f(ts + t);
+#pragma unroll
+  for (int q = 0; q < kTileKeep; ++q) {
+    keep[q] = (t0 + q < t1) ? obs_f(ts + t0 + q) : 0.f;
+    local += keep[q];
+  }
+  for (int t = t0 + kTileKeep; t < t1; ++t) local += obs_f(ts + t);
   float total;
   const float incl = block_incl_scan(local, total);
   Z = total;
@@ -180,7 +220,10 @@ __device__ __forceinline__ int find_tile(const float* ts, int ntiles, float u, f
   float run = incl - local;
   int cand = INT_MAX, lastpos = -1;
   for (int t = t0; t < t1; ++t) {
-    const float w = obs_f(ts + t);
+    float w = 0.f;
+#pragma unroll
+    for (int q = 0; q < kTileKeep; ++q) w = (t == t0 + q) ? keep[q] : w;
+    if (t >= t0 + kTileKeep) w = obs_f(ts + t);
     const float nxt = run + w;
     if (cand == INT_MAX && nxt > target) cand = t;
     if (w > 0.f) lastpos = t;
@@ -192,7 +235,13 @@ __device__ __forceinline__ int find_tile(const float* ts, int ntiles, float u, f
   __syncthreads();
   if (tile >= t0 && tile < t1) {
     float r = incl - local;
-    for (int t = t0; t < tile; ++t) r += obs_f(ts + t);
+    for (int t = t0; t < tile; ++t) {
+      float w = 0.f;
+#pragma unroll
+      for (int q = 0; q < kTileKeep; ++q) w = (t == t0 + q) ? keep[q] : w;
+      if (t >= t0 + kTileKeep) w = obs_f(ts + t);
+      r += w;
+    }
     s_base = r;
   }
   __syncthreads();
@@ -277,24 +326,30 @@ struct Dec {
   float m[2][SV_MAX_K + 1];  // merged row maxima (draft, target) per position
   float s[2][SV_MAX_K + 1];  // merged sums 2^(l*c - R) (over the kept set)
   float th[2][SV_MAX_K + 1]; // kept-set thresholds (-inf: no filter)
-  int flags;                 // 1 bad token, 2 bad row
+  int flags;                 // 1 bad token, 2 bad row, 4 a wait timed out
   unsigned long long rej;    // ballot of rejected draft positions
 };
 
 // Merge the chunk partials of one position's rows in chunk order (loads issued
-// eight chunks at a time so their round trips overlap).
+// four chunks at a time so their round trips overlap; with POLL, a partial
+// not yet published is waited for).
+template <bool POLL>
 __device__ __forceinline__ void merge_sampling(const unsigned long long* dsl,
                                                const unsigned long long* tsl, bool with_draft,
                                                int C, float c, float& mq, float& sq, float& mp,
-                                               float& sp) {
-  constexpr int G = 8;
+                                               float& sp, int limit, int& to) {
+  constexpr int G = 4;
   for (int k0 = 0; k0 < C; k0 += G) {
     unsigned long long dv[G], tv[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const bool in = k0 + g < C;
-      tv[g] = in ? tsl[k0 + g] : 0ull;
-      dv[g] = (in && with_draft) ? dsl[k0 + g] : 0ull;
+      tv[g] = in ? slot_load<POLL>(tsl + k0 + g) : 1ull;
+      dv[g] = (in && with_draft) ? slot_load<POLL>(dsl + k0 + g) : 1ull;
+    }
+    if constexpr (POLL) {
+      slots_wait<G>(tsl + k0, tv, limit, to);
+      if (with_draft) slots_wait<G>(dsl + k0, dv, limit, to);
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -311,13 +366,15 @@ __device__ __forceinline__ void merge_sampling(const unsigned long long* dsl,
   }
 }
 
+template <bool POLL>
 __device__ __forceinline__ void merge_greedy(const unsigned long long* tsl, int C, float& v,
-                                             int& idx, int& bad) {
-  constexpr int G = 8;
+                                             int& idx, int& bad, int limit, int& to) {
+  constexpr int G = 4;
   for (int k0 = 0; k0 < C; k0 += G) {
     unsigned long long tv[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) tv[g] = (k0 + g < C) ? tsl[k0 + g] : 0ull;
+    for (int g = 0; g < G; ++g) tv[g] = (k0 + g < C) ? slot_load<POLL>(tsl + k0 + g) : 1ull;
+    if constexpr (POLL) slots_wait<G>(tsl + k0, tv, limit, to);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       if (k0 + g < C) {
@@ -336,7 +393,7 @@ __device__ __forceinline__ void merge_greedy(const unsigned long long* tsl, int 
 // result; only the writer block stores the outputs it fixes: the accepted
 // prefix and -1 after it, the side outputs, and num_accepted when nothing is
 // drawn. Returns the job of the final draw (kJobNone when there is none).
-template <int DT>
+template <int DT, bool POLL>
 __device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool writer, Dec& S) {
   const int tid = threadIdx.x;
   const int t0 = d0 + b;
@@ -360,15 +417,27 @@ __device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool 
     lq = load_elem<DT>(P.draft, (size_t)(d0 + tid) * P.V + xs);
     lp = load_elem<DT>(P.target, (size_t)(t0 + tid) * P.V + xs);
   }
+  if constexpr (POLL) {
+    // One thread waits for the sequence's last stats block in grid order (the
+    // last chunk of its bonus row), sleeping between reads so that waiting
+    // blocks add little memory traffic; the partials are read after it.
+    if (tid == 0) {
+      const unsigned long long* last = P.slots + (size_t)(P.total_draft + t0 + kb + 1) * C - 1;
+      for (int spins = 0; obs_u64(last) == 0ull && spins < P.spin_limit; ++spins)
+        __builtin_amdgcn_s_sleep(8);
+    }
+    __syncthreads();
+  }
   float mq = kNegInf, sq = 0.f, mp = kNegInf, sp = 0.f;
   float thq = kNegInf, thp = kNegInf;
   int am = INT_MAX;
   bool bad = false;
+  int timed_out = 0;
   if (active) {
     const unsigned long long* tsl = P.slots + (size_t)(P.total_draft + t0 + tid) * C;
     if (greedy) {
       int gbad = 0;
-      merge_greedy(tsl, C, mp, am, gbad);
+      merge_greedy<POLL>(tsl, C, mp, am, gbad, P.spin_limit, timed_out);
       bad = gbad || mp == kNegInf;
     } else {
       int rbad = 0;
@@ -387,7 +456,8 @@ __device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool 
           rbad |= rd.flags;
         }
       } else {
-        merge_sampling(P.slots + (size_t)(d0 + tid) * C, tsl, is_draft, C, c, mq, sq, mp, sp);
+        merge_sampling<POLL>(P.slots + (size_t)(d0 + tid) * C, tsl, is_draft, C, c, mq, sq, mp,
+                             sp, P.spin_limit, timed_out);
       }
       bool ok = !rbad && __builtin_isfinite(mp) && sp > 0.f && __builtin_isfinite(sp);
       if (is_draft) ok = ok && __builtin_isfinite(mq) && sq > 0.f && __builtin_isfinite(sq);
@@ -401,6 +471,7 @@ __device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool 
     S.th[1][tid] = thp;
     if (bad) atomicOr(&S.flags, 2);
     if (!tok_ok) atomicOr(&S.flags, 1);
+    if (timed_out) atomicOr(&S.flags, 4);
   }
   bool acc = false;
   float ratio = __builtin_nanf("");
@@ -428,7 +499,8 @@ __device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool 
   }
   __syncthreads();
   const int sf = S.flags;
-  const int code = (sf & 1) ? SV_SEQ_BAD_TOKEN : ((sf & 2) ? SV_SEQ_BAD_ROW : 0);
+  const int code = (sf & 4) ? SV_SEQ_SYNC_TIMEOUT
+                            : ((sf & 1) ? SV_SEQ_BAD_TOKEN : ((sf & 2) ? SV_SEQ_BAD_ROW : 0));
   const int n = S.rej ? (__ffsll(S.rej) - 1) : kb;
   const bool draws = code == 0 && !greedy;
 
@@ -648,12 +720,13 @@ __device__ void topk_block(const Params& P, long long g, const void* base, size_
 
 }  // namespace
 
-// ------------------------------------------------------------------ k_stats
-// Block g (after the offset stats_block0) covers chunk g % chunks of unit
-// g / chunks: draft row u for u < total_draft, else target row u - total_draft.
-// Its partial goes to slots[g].
-template <int DT, bool VEC, bool FILT>
-__global__ __launch_bounds__(kThreads) void k_stats(const Params P) {
+// ---------------------------------------------------------------- stats unit
+// Stats block g covers chunk g % chunks of unit g / chunks: draft row u for
+// u < total_draft, else target row u - total_draft. Its partial goes to
+// slots[g]; with PUB it is published with an agent-scope store for readers in
+// the same grid.
+template <int DT, bool VEC, bool FILT, bool PUB>
+__device__ void stats_unit(const Params& P, long long g) {
   using Vc = Vec<DT, VEC>;
   constexpr int N = Vc::N;
   __shared__ float4 s_part[kThreads / kWave];
@@ -661,7 +734,6 @@ __global__ __launch_bounds__(kThreads) void k_stats(const Params P) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const long long g = (long long)blockIdx.x + P.stats_block0;
   const int unit = (int)(g / P.chunks);
   const int ch = (int)(g - (long long)unit * P.chunks);
   const bool is_target = unit >= P.total_draft;
@@ -751,7 +823,14 @@ __global__ __launch_bounds__(kThreads) void k_stats(const Params P) {
     for (int w = 1; w < kThreads / kWave; ++w) merge_ms(m, s, s_part[w].x, s_part[w].y, c);
     packed = pack_ms(m, s);
   }
-  P.slots[g] = packed;
+  if constexpr (PUB) pub_u64(P.slots + g, packed);
+  else P.slots[g] = packed;
+}
+
+// The statistics pass as a kernel of its own (filtered calls).
+template <int DT, bool VEC, bool FILT>
+__global__ __launch_bounds__(kThreads) void k_stats(const Params P) {
+  stats_unit<DT, VEC, FILT, false>(P, (long long)blockIdx.x + P.stats_block0);
 }
 
 // ----------------------------------------------------------------- k_filter
@@ -969,18 +1048,22 @@ __global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
   }
 }
 
-// ------------------------------------------------------------------- k_draw
-// Block (b, ch), ch < dchunks: decision of sequence b, then the tile sums of
-// slice ch of row pair n; the last block of b to finish draws the token.
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_draw(const Params P) {
+// ----------------------------------------------------------------- draw unit
+// Draw block (b, ch), ch < dchunks: decision of sequence b, then the tile sums
+// of slice ch of row pair n. Every block of a sampling sequence counts itself
+// on the sequence's counter; the last one draws the token (or reports a wait
+// that timed out) and returns the sequence's workspace entries to zero. A
+// greedy sequence is decided by block 0 alone. With POLL the row partials may
+// still be in flight (fused grid) and are waited for.
+template <int DT, bool VEC, bool POLL>
+__device__ void draw_unit(const Params& P, int idx) {
   using Vc = Vec<DT, VEC>;
   constexpr int N = Vc::N;
   __shared__ Dec S;
-  __shared__ int s_last;
+  __shared__ int s_last, s_to;
   const int tid = threadIdx.x;
-  const int b = blockIdx.x / P.dchunks;
-  const int ch = blockIdx.x - b * P.dchunks;
+  const int b = idx / P.dchunks;
+  const int ch = idx - b * P.dchunks;
   int d0, kb;
   if (!seq_bounds(P, b, d0, kb)) {
     if (ch == 0 && tid == 0) P.num_accepted[b] = SV_SEQ_BAD_OFFSETS;
@@ -988,62 +1071,115 @@ __global__ __launch_bounds__(kThreads) void k_draw(const Params P) {
   }
   const bool greedy = seq_greedy(P, b);
   if (greedy && ch != 0) return;  // one block decides a greedy sequence
-  const Job j = decide<DT>(P, b, d0, kb, greedy, ch == 0, S);
-  if (j.mode == kJobNone) return;
-  // tile sums of slice ch of row pair n: the thread's vector k*kThreads + tid of
-  // the slice belongs to tile ch*kTilesPerDraw + k
-  const size_t prow = (size_t)j.prow * P.V;
-  const size_t qrow = (size_t)j.qrow * P.V;
-  const int vb = ch * kDrawVecs + tid;
-  typename Vc::Raw rp[kBatch], rq[kBatch];
+  const Job j = decide<DT, POLL>(P, b, d0, kb, greedy, ch == 0, S);
+  const int C = P.chunks;
+  if (greedy) {
+    // the only reader of these partials returns them to zero
+    for (int k = tid; k < (kb + 1) * C; k += kThreads)
+      pub_u64(P.slots + (size_t)(P.total_draft + d0 + b) * C + k, 0ull);
+    return;
+  }
+  if (j.mode != kJobNone) {
+    // tile sums of slice ch of row pair n: the thread's vector k*kThreads + tid
+    // of the slice belongs to tile ch*kTilesPerDraw + k
+    const size_t prow = (size_t)j.prow * P.V;
+    const size_t qrow = (size_t)j.qrow * P.V;
+    const int vb = ch * kDrawVecs + tid;
+    typename Vc::Raw rp[kBatch], rq[kBatch];
 #pragma unroll
-  for (int u = 0; u < kBatch; ++u) {
-    const int v = vb + u * kThreads;
-    if (v < P.nvec) {
-      rp[u] = Vc::load(P.target, prow, v);
-      if (j.mode == kJobResidual) rq[u] = Vc::load(P.draft, qrow, v);
+    for (int u = 0; u < kBatch; ++u) {
+      const int v = vb + u * kThreads;
+      if (v < P.nvec) {
+        rp[u] = Vc::load(P.target, prow, v);
+        if (j.mode == kJobResidual) rq[u] = Vc::load(P.draft, qrow, v);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float ts[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int v = vb + u * kThreads;
+      if (v < P.nvec) {
+        float fp[N], fq[N];
+        Vc::get(rp[u], fp);
+        if (j.mode == kJobResidual) Vc::get(rq[u], fq);
+        float sum = 0.f;
+#pragma unroll
+        for (int k = 0; k < N; ++k) sum += draw_weight(fp[k], fq[k], j, P.c);
+        ts[u] = sum;
+      }
+    }
+    float tot[8];
+    block_sum8(ts, tot);
+    if (tid < kTilesPerDraw) {
+      float val = tot[0];
+#pragma unroll
+      for (int k = 1; k < kTilesPerDraw; ++k) val = (tid == k) ? tot[k] : val;
+      pub_f(P.tiles + (size_t)b * P.ntiles + ch * kTilesPerDraw + tid, val);
     }
   }
-  __builtin_amdgcn_sched_barrier(0);
-  float ts[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int u = 0; u < kBatch; ++u) {
-    const int v = vb + u * kThreads;
-    if (v < P.nvec) {
-      float fp[N], fq[N];
-      Vc::get(rp[u], fp);
-      if (j.mode == kJobResidual) Vc::get(rq[u], fq);
-      float s = 0.f;
-#pragma unroll
-      for (int k = 0; k < N; ++k) s += draw_weight(fp[k], fq[k], j, P.c);
-      ts[u] = s;
-    }
-  }
-  float tot[8];
-  block_sum8(ts, tot);
-  if (tid < kTilesPerDraw) {
-    float val = tot[0];
-#pragma unroll
-    for (int k = 1; k < kTilesPerDraw; ++k) val = (tid == k) ? tot[k] : val;
-    pub_f(P.tiles + (size_t)b * P.ntiles + ch * kTilesPerDraw + tid, val);
-    drain_stores();
-  }
+  // every block of the sequence counts itself, after its stores have landed
+  if (tid == 0 && (S.flags & 4)) raise_flag(P.seq_flags + b, kSeqFlagTimeout);
+  drain_stores();
   __syncthreads();
   if (tid == 0) {
     s_last = (bump(P.draw_done + b) == P.dchunks - 1) ? 1 : 0;
     compiler_fence();
+    s_to = s_last ? (obs_i(P.seq_flags + b) & kSeqFlagTimeout) : 0;
   }
   __syncthreads();
   if (!s_last) return;
-  // Last block of the sequence: every tile sum is published.
-  float Z;
-  const int tok = pick<DT, VEC>(P, b, j, Z);
-  if (tid == 0) {
-    P.out_tokens[j.out_idx] = tok;
-    P.num_accepted[b] = j.n;
-    if (P.diag.resid_Z) P.diag.resid_Z[b] = Z;
-    pub_i(P.draw_done + b, 0);  // the workspace counter returns to zero
+  // Last block of the sequence: every other block has read the partials and
+  // published its tile sums.
+  if (s_to) {
+    for (int k = tid; k <= kb; k += kThreads) P.out_tokens[d0 + b + k] = -1;
+    if (tid == 0) {
+      P.num_accepted[b] = SV_SEQ_SYNC_TIMEOUT;
+      if (P.diag.resid_Z) P.diag.resid_Z[b] = __builtin_nanf("");
+    }
+  } else if (j.mode != kJobNone) {
+    float Z;
+    const int tok = pick<DT, VEC>(P, b, j, Z);
+    if (tid == 0) {
+      P.out_tokens[j.out_idx] = tok;
+      P.num_accepted[b] = j.n;
+      if (P.diag.resid_Z) P.diag.resid_Z[b] = Z;
+    }
   }
+  __syncthreads();
+  // return the sequence's workspace entries to zero
+  if (!P.filt) {
+    for (int k = tid; k < kb * C; k += kThreads) pub_u64(P.slots + (size_t)d0 * C + k, 0ull);
+    for (int k = tid; k < (kb + 1) * C; k += kThreads)
+      pub_u64(P.slots + (size_t)(P.total_draft + d0 + b) * C + k, 0ull);
+  }
+  for (int t = tid; t < P.ntiles; t += kThreads) pub_f(P.tiles + (size_t)b * P.ntiles + t, 0.f);
+  if (tid == 0) {
+    pub_i(P.draw_done + b, 0);
+    pub_i(P.seq_flags + b, 0);
+  }
+}
+
+// The decision-and-draw pass as a kernel of its own (filtered calls).
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_draw(const Params P) {
+  draw_unit<DT, VEC, false>(P, blockIdx.x);
+}
+
+// ------------------------------------------------------------------ k_verify
+// The unfiltered step in one grid: every stats block first, then the draw
+// blocks in sequence order. Blocks start in index order on each of the chip's
+// dies, so every stats block has started before any draw block can wait for
+// it, and stats blocks never wait: the waits always end. Draw blocks take the
+// slots the statistics tail frees, so the draws of the early sequences overlap
+// the last statistics blocks.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void k_verify(const Params P) {
+  if ((long long)blockIdx.x < P.stats_blocks)
+    stats_unit<DT, VEC, false, true>(P, (long long)blockIdx.x + P.stats_block0);
+  else
+    draw_unit<DT, VEC, true>(P, (int)((long long)blockIdx.x - P.stats_blocks));
 }
 
 __global__ void k_fill_zero(uint4* p, size_t n16) {
@@ -1062,20 +1198,19 @@ static hipError_t launch_t(const Params& P, const Plan& L, hipStream_t s, hipEve
   hipError_t err;
   int e = 0;
   if ((err = stage_event(ev, nev, e++, s)) != hipSuccess) return err;
-  if (P.filt)
+  if (P.filt) {
     hipLaunchKernelGGL((k_stats<DT, VEC, true>), dim3((unsigned)L.stats_blocks), dim3(kThreads), 0,
                        s, P);
-  else
-    hipLaunchKernelGGL((k_stats<DT, VEC, false>), dim3((unsigned)L.stats_blocks), dim3(kThreads),
-                       0, s, P);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  if ((err = stage_event(ev, nev, e++, s)) != hipSuccess) return err;
-  if (P.filt) {
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = stage_event(ev, nev, e++, s)) != hipSuccess) return err;
     hipLaunchKernelGGL(k_filter, dim3((unsigned)L.filter_blocks), dim3(kThreads), 0, s, P);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if ((err = stage_event(ev, nev, e++, s)) != hipSuccess) return err;
+    hipLaunchKernelGGL((k_draw<DT, VEC>), dim3((unsigned)L.draw_blocks), dim3(kThreads), 0, s, P);
+  } else {
+    hipLaunchKernelGGL((k_verify<DT, VEC>), dim3((unsigned)(L.stats_blocks + L.draw_blocks)),
+                       dim3(kThreads), 0, s, P);
   }
-  hipLaunchKernelGGL((k_draw<DT, VEC>), dim3((unsigned)L.draw_blocks), dim3(kThreads), 0, s, P);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   // this and any further events: after the last kernel
   for (; e < nev; ++e)

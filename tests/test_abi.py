@@ -44,8 +44,9 @@ def test_codes_match_header(L):
     assert int(codes["SV_SEQ_BAD_ROW"]) == _lib.SV_SEQ_BAD_ROW
     assert int(codes["SV_SEQ_BAD_OFFSETS"]) == _lib.SV_SEQ_BAD_OFFSETS
     assert int(codes["SV_MAX_K"]) == _lib.SV_MAX_K
+    assert int(codes["SV_SEQ_SYNC_TIMEOUT"]) == _lib.SV_SEQ_SYNC_TIMEOUT
     assert set(k for k in codes if k.startswith("SV_SEQ_")) == {
-        "SV_SEQ_BAD_TOKEN", "SV_SEQ_BAD_ROW", "SV_SEQ_BAD_OFFSETS"}
+        "SV_SEQ_BAD_TOKEN", "SV_SEQ_BAD_ROW", "SV_SEQ_BAD_OFFSETS", "SV_SEQ_SYNC_TIMEOUT"}
     for c in (0, -1, -2, -3, -4, -5):
         assert L.spec_verify_strerror(c)
     assert L.spec_verify_strerror(12345) == b"unknown code"
@@ -124,6 +125,7 @@ def test_workspace_sizes(L):
     assert ws(1, 0, 0, 0, 1.0) == 0
     # long rows take longer stats chunks, so the partials stay bounded per row
     assert 0 < ws(1, 0, 2048 * 2048, 0, 1.0) < ws(1, 0, 2 ** 30, 0, 1.0) < 64 << 20
+    assert ws(1, 0, 2 ** 30 + 1, 0, 1.0) == 0  # beyond a 30-bit argmax
     assert ws(512, 3840, 128256, 0, 1.0) >= ws(64, 512, 128256, 0, 1.0)
     # top-k adds per-chunk candidate records and per-row results
     assert ws(64, 512, 128256, 50, 0.9) > ws(64, 512, 128256, 0, 1.0)

@@ -231,10 +231,11 @@ def test_large_magnitude_logits():
     _check(w, api="ragged", diag=True, tag="x300")
 
 
-def test_workspace_counters_return_to_zero():
-    """The per-sequence counters at the head of the workspace read zero after a
-    call whose batch mixes drawing, greedy, bad-token and bad-offset sequences,
-    so the next call on the same workspace starts clean."""
+def test_workspace_returns_to_zero():
+    """An unfiltered call leaves its whole workspace zero (counters, flags, row
+    partials, tile sums), also for a batch that mixes drawing, greedy and
+    bad-token sequences; after a call with bad offsets the workspace is
+    zero-filled again before reuse, as the header asks."""
     import speculative_decoding_verification_13_amd as sv
     w = W.make("bf16_B512_Kragged_V128256_halfgreedy", B=12, V=8192)
     toks = draft_tokens_from_oracle(w)
@@ -243,23 +244,55 @@ def test_workspace_counters_return_to_zero():
     toks[cu[bad]] = w["V"] + 7  # one sampling sequence holds an id outside [0, V)
     ora = run_oracle(w, toks)
     d = to_device(w, toks)
-    n_draft = int(w["cu_draft"][-1])
+    n_draft = int(cu[-1])
     ws = sv.make_workspace(w["B"], n_draft, w["V"])
-    _say("[gpu] counters after a mixed batch")
-    run_gpu(w, toks, api="ragged", dev=d, workspace=ws)
+    _say("[gpu] workspace after a mixed batch")
+    gpu = run_gpu(w, toks, api="ragged", dev=d, workspace=ws)
     torch.cuda.synchronize()
-    assert int(ws[:4 * w["B"]].view(torch.int32).abs().sum()) == 0
+    assert not compare(w, toks, gpu, ora)["mismatches"]
+    assert int((ws != 0).sum()) == 0
     cu_bad = d["cu"].clone()
     cu_bad[5] = cu_bad[6] + 1  # sequence 5 gets cu[5] > cu[6]
-    _say("[gpu] counters after bad offsets")
-    sv.spec_verify_ragged(d["draft"], d["target"], d["tokens"], d["uniforms"], cu_bad,
-                          d["greedy"], w["B"], w["V"], w["temperature"],
-                          total_draft_rows=n_draft, workspace=ws)
-    torch.cuda.synchronize()
-    assert int(ws[:4 * w["B"]].view(torch.int32).abs().sum()) == 0
+    _say("[gpu] bad offsets, then a zero-fill and a clean call")
+    _, num = sv.spec_verify_ragged(d["draft"], d["target"], d["tokens"], d["uniforms"], cu_bad,
+                                   d["greedy"], w["B"], w["V"], w["temperature"],
+                                   total_draft_rows=n_draft, workspace=ws)
+    assert int(num[5]) == sv.SV_SEQ_BAD_OFFSETS
+    sv.lib().spec_verify_workspace_init(ws.data_ptr(), ws.numel(),
+                                        torch.cuda.current_stream().cuda_stream)
     gpu = run_gpu(w, toks, api="ragged", dev=d, workspace=ws)
-    rep = compare(w, toks, gpu, ora)
-    assert not rep["mismatches"]
+    assert not compare(w, toks, gpu, ora)["mismatches"]
+    assert int((ws != 0).sum()) == 0
+
+
+def test_forced_sync_timeout_is_reported():
+    """A wait bound of one iteration, set from the host, makes draw blocks give
+    up on row statistics still in flight; each sequence then either matches
+    the oracle or reports SV_SEQ_SYNC_TIMEOUT with its tokens all -1. A call
+    with the default bound on a fresh workspace is exact again."""
+    import speculative_decoding_verification_13_amd as sv
+    w = W.make(W.HEADLINE, B=16)
+    toks = draft_tokens_from_oracle(w)
+    ora = run_oracle(w, toks)
+    d = to_device(w, toks)
+    n_draft = int(w["cu_draft"][-1])
+    _say("[gpu] forced timeout spin_limit=1")
+    out, num = sv.spec_verify_ragged(d["draft"], d["target"], d["tokens"], d["uniforms"], d["cu"],
+                                     None, w["B"], w["V"], w["temperature"],
+                                     total_draft_rows=n_draft, diag={"spin_limit": 1})
+    num = num.cpu().numpy()
+    out = out.cpu().numpy()
+    cu = w["cu_draft"]
+    for b in range(w["B"]):
+        t0, t1 = cu[b] + b, cu[b + 1] + b + 1
+        if num[b] == sv.SV_SEQ_SYNC_TIMEOUT:
+            assert np.all(out[t0:t1] == -1)
+        elif ora["margin"][b] > 1e-5:
+            assert num[b] == ora["num_accepted"][b]
+            assert np.array_equal(out[t0:t1], ora["out_tokens"][t0:t1])
+    _say(f"      timeouts={(num == sv.SV_SEQ_SYNC_TIMEOUT).sum()} of {w['B']}")
+    gpu = run_gpu(w, toks, api="ragged", dev=d)
+    assert not compare(w, toks, gpu, ora)["mismatches"]
 
 
 def test_workspace_reuse_across_calls_and_shapes():
