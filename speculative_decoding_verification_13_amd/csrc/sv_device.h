@@ -182,6 +182,50 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i, int& bad) {
   }
 }
 
+// ---- wave reductions through DPP (no LDS round trips) ----
+// Steps: swap neighbours, swap pairs, mirror half rows, mirror rows (every lane
+// of a 16-lane row then holds the row's result), then broadcast lane 15 into
+// rows 1 and 3 and lane 31 into rows 2 and 3; lane 63 ends with the wave result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF,
+                                                            0xF, false));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_rows_f(float v, float ident) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, ident),
+                                                        __builtin_bit_cast(int, v), CTRL, ROWS,
+                                                        0xF, false));
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror
+  v = fmaxf(v, dpp_rows_f<0x142, 0xA>(v, kNegInf));  // row_bcast:15
+  v = fmaxf(v, dpp_rows_f<0x143, 0xC>(v, kNegInf));  // row_bcast:31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  v += dpp_rows_f<0x142, 0xA>(v, 0.0f);
+  v += dpp_rows_f<0x143, 0xC>(v, 0.0f);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Wave-wide (max, sum) of per-lane partials: the maximum first, then each
+// lane's sum moved to the maximum's reference (one exponent), then the sum.
+__device__ __forceinline__ void wave_reduce_ms(float& m, float& s, float c) {
+  const float M = wave_max_dpp(m);
+  const float sr = (s == 0.0f) ? 0.0f : s * rescale(ref_of(m, c), ref_of(M, c));
+  s = wave_sum_dpp(sr);
+  m = M;
+}
+
 // Inclusive prefix sum over the wave (lane order).
 __device__ __forceinline__ float wave_incl_scan(float x) {
   const int lane = threadIdx.x & (kWave - 1);

@@ -815,13 +815,22 @@ __device__ void stats_unit(const Params& P, long long g) {
       Vc::get(Vc::load(base, roff, v), f);
       online_update<N>(m, s, f, c);
     }
-    wave_merge_ms(m, s, c);
+    wave_reduce_ms(m, s, c);
     if (lane == 0) s_part[wave] = make_float4(m, s, 0.f, 0.f);
     __syncthreads();
     if (tid != 0) return;
+    // the block's maximum, then every wave's sum at its reference
+    float M = s_part[0].x;
 #pragma unroll
-    for (int w = 1; w < kThreads / kWave; ++w) merge_ms(m, s, s_part[w].x, s_part[w].y, c);
-    packed = pack_ms(m, s);
+    for (int w = 1; w < kThreads / kWave; ++w) M = fmaxf(M, s_part[w].x);
+    const float RM = ref_of(M, c);
+    float S = 0.f;
+#pragma unroll
+    for (int w = 0; w < kThreads / kWave; ++w) {
+      const float sw = s_part[w].y;
+      S += (sw == 0.f) ? 0.f : sw * rescale(ref_of(s_part[w].x, c), RM);
+    }
+    packed = pack_ms(M, S);
   }
   if constexpr (PUB) pub_u64(P.slots + g, packed);
   else P.slots[g] = packed;
