@@ -82,7 +82,11 @@ typedef enum sv_dtype { SV_F32 = 0, SV_F16 = 1, SV_BF16 = 2 } sv_dtype;
 /* Per-sequence codes written to num_accepted[b] instead of a count. */
 #define SV_SEQ_BAD_TOKEN (-1)   /* a draft id outside [0, V) */
 #define SV_SEQ_BAD_ROW (-2)     /* a used row holds NaN or +inf, or no finite
-                                   value (greedy: target rows only) */
+                                   value. The used rows are the draft and target
+                                   rows of positions 0..n (n = the first
+                                   rejection) and the bonus row when every draft
+                                   passes; greedy sequences use no draft rows.
+                                   Rows past the first rejection are never read */
 #define SV_SEQ_BAD_OFFSETS (-3) /* ragged offsets: cu[b] > cu[b+1], outside
                                    [0, total_draft_rows], or K_b > 64 */
 #define SV_SEQ_SYNC_TIMEOUT (-4) /* a bounded wait for the sequence's row

@@ -14,6 +14,7 @@ routines; see the docstrings for the passage each step follows.
 from .verify import (  # noqa: F401
     ACCEPT_MARGIN_INF,
     decode_logits,
+    row_is_valid,
     filtered_distribution,
     accept_ratio,
     residual,

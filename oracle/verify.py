@@ -42,8 +42,12 @@ Readings taken where the pages leave a step open (each is repeated where used):
   R7  greedy: argmax of the raw target logits, lowest id on ties; accept iff it
       equals the draft token; the correction or bonus is that argmax.
   R8  a sequence with a draft id outside [0, V) returns n = -1; otherwise one
-      with a row holding NaN or +inf, or no finite value, returns n = -2
-      (greedy sequences check only their target rows). All tokens are -1 then.
+      whose used rows hold NaN or +inf, or no finite value, returns n = -2. The
+      used rows are those the steps read: draft and target rows of positions
+      0..n (the ratio tests up to the first rejection and the resample at n),
+      and the bonus row when every draft passes; rows past the first rejection
+      are never read. Greedy sequences use no draft rows. All tokens are -1
+      then.
 """
 
 import math
@@ -220,22 +224,30 @@ def verify_sequence(q_rows, p_rows, x, u, temperature, top_k=0, top_p=1.0,
                lse_q=[math.nan] * K, lse_p=[math.nan] * (K + 1),
                ratio=[math.nan] * K, resid_Z=math.nan)
 
-    # R8: token ids, then row validity.
+    # R8: every draft id first; each row when the step that reads it comes.
     if any(not (0 <= int(t) < V) for t in x):
         res["n"] = -1
         return res
-    rows = list(p_rows) + ([] if greedy else list(q_rows))
-    if not all(row_is_valid(r) for r in rows):
+
+    def invalid(*rows):
+        return not all(row_is_valid(r) for r in rows)
+
+    def fail():
         res["n"] = -2
+        res["tokens"] = [-1] * (K + 1)
         return res
 
     if greedy:
         # R7: compare the draft id with the target argmax, position by position.
         n = K
         for i in range(K):
+            if invalid(p_rows[i]):
+                return fail()
             if greedy_token(p_rows[i]) != int(x[i]):
                 n = i
                 break
+        if n == K and invalid(p_rows[K]):
+            return fail()
         for i in range(n):
             tokens[i] = int(x[i])
         tokens[n] = greedy_token(p_rows[n])
@@ -259,6 +271,8 @@ def verify_sequence(q_rows, p_rows, x, u, temperature, top_k=0, top_p=1.0,
     # s.9; [P2] part 4 item 3; [P3] two-models section).
     n = K
     for i in range(K):
+        if invalid(p_rows[i], q_rows[i]):
+            return fail()
         p, _, mp = p_dist(i)
         q, _, mq = q_dist(i)
         r = accept_ratio(p, q, int(x[i]))
@@ -278,6 +292,8 @@ def verify_sequence(q_rows, p_rows, x, u, temperature, top_k=0, top_p=1.0,
             j, Z, m = inverse_cdf(p, float(u[K]))
     else:
         # Bonus token from the (K+1)-th target distribution ([P2] part 4 item 4).
+        if invalid(p_rows[K]):
+            return fail()
         p, _, mp = p_dist(K)
         margin = min(margin, mp)
         j, Z, m = inverse_cdf(p, float(u[K]))
@@ -287,11 +303,15 @@ def verify_sequence(q_rows, p_rows, x, u, temperature, top_k=0, top_p=1.0,
     res["resid_Z"] = Z
 
     if want_diag:
+        # every valid row, used or not (an unused invalid row stays NaN)
         for i in range(K + 1):
-            res["lse_p"][i] = p_dist(i)[1]
+            if row_is_valid(p_rows[i]):
+                res["lse_p"][i] = p_dist(i)[1]
         for i in range(K):
-            res["lse_q"][i] = q_dist(i)[1]
-            res["ratio"][i] = accept_ratio(p_dist(i)[0], q_dist(i)[0], int(x[i]))
+            if row_is_valid(q_rows[i]):
+                res["lse_q"][i] = q_dist(i)[1]
+                if row_is_valid(p_rows[i]):
+                    res["ratio"][i] = accept_ratio(p_dist(i)[0], q_dist(i)[0], int(x[i]))
     return res
 
 

@@ -162,6 +162,11 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
   P.draw_done = reinterpret_cast<int*>(ws + L.off_draw_done);
   P.seq_flags = reinterpret_cast<int*>(ws + L.off_seq_flags);
   P.spin_limit = (diag != nullptr && diag->spin_limit > 0) ? diag->spin_limit : kDefaultSpinLimit;
+  P.full_wait = (diag != nullptr &&
+                 (diag->row_max_draft || diag->row_logsum_draft || diag->row_max_target ||
+                  diag->row_logsum_target || diag->ratio))
+                    ? 1
+                    : 0;
   L.chunks = P.chunks;
   L.chunk_vecs = P.chunk_vecs;
   L.dchunks = P.dchunks;

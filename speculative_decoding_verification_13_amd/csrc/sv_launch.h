@@ -87,6 +87,7 @@ struct Params {
   long long stats_block0;  // first stats block (skips draft rows when all greedy)
   long long stats_blocks;  // stats blocks launched (the fused grid's draw blocks follow)
   int spin_limit;          // bound of every wait (iterations)
+  int full_wait;           // 1: decisions read every row (side outputs requested)
   int filt;                // 1: top-k (and top-p) filters active
   int top_k;
   float top_p;

@@ -53,6 +53,16 @@ __device__ __forceinline__ bool seq_greedy(const Params& P, int b) {
   return P.all_greedy || (P.greedy != nullptr && P.greedy[b] != 0);
 }
 
+// Stats units: draft rows, then target rows (both in row order, so the grid
+// streams each logit array linearly).
+__device__ __forceinline__ long long unit_of(const Params& P, bool is_target, int row) {
+  return is_target ? (long long)P.total_draft + row : (long long)row;
+}
+__device__ __forceinline__ void row_of_unit(const Params& P, int unit, bool& is_target, int& row) {
+  is_target = unit >= P.total_draft;
+  row = is_target ? unit - P.total_draft : unit;
+}
+
 // (max, sum) of a sampling chunk; NaN is stored canonical. Never all-zero
 // bits: a +0 maximum brings a term 2^0 = 1 into the sum.
 __device__ __forceinline__ unsigned long long pack_ms(float m, float s) {
@@ -326,8 +336,12 @@ struct Dec {
   float m[2][SV_MAX_K + 1];  // merged row maxima (draft, target) per position
   float s[2][SV_MAX_K + 1];  // merged sums 2^(l*c - R) (over the kept set)
   float th[2][SV_MAX_K + 1]; // kept-set thresholds (-inf: no filter)
-  int flags;                 // 1 bad token, 2 bad row, 4 a wait timed out
-  unsigned long long rej;    // ballot of rejected draft positions
+  int flags;                 // 1 a draft id outside [0, V)
+  int first;                 // first position that stops the walk (rejection,
+                             // invalid row or id, or the bonus position)
+  int invalid;               // first position with an invalid row
+  int to_pos;                // first position whose wait ran out
+  int timeout;               // the decision is a timed-out wait (read by thread 0)
 };
 
 // Merge the chunk partials of one position's rows in chunk order (loads issued
@@ -388,11 +402,16 @@ __device__ __forceinline__ void merge_greedy(const unsigned long long* tsl, int 
   }
 }
 
-// Decision of sequence b (whole block; thread i owns position i). Every block
-// of the sequence computes it with the same arithmetic and so reaches the same
-// result; only the writer block stores the outputs it fixes: the accepted
-// prefix and -1 after it, the side outputs, and num_accepted when nothing is
-// drawn. Returns the job of the final draw (kJobNone when there is none).
+// Decision of sequence b (whole block; thread i owns position i). Position i
+// stops the walk if a row it reads is invalid, its draft id is out of range or
+// its ratio test rejects; the bonus position always stops. n is the first
+// stopping position. In a fused grid (POLL) a thread waits for its rows until
+// they are published, or until an earlier position has stopped (its rows are
+// then never read), unless every row is wanted for the side outputs. Every
+// block of the sequence computes the same result; only the writer block stores
+// the outputs it fixes: the accepted prefix and -1 after it, the side outputs,
+// and num_accepted when nothing is drawn. Returns the job of the final draw
+// (kJobNone when there is none).
 template <int DT, bool POLL>
 __device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool writer, Dec& S) {
   const int tid = threadIdx.x;
@@ -401,7 +420,28 @@ __device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool 
   const bool is_draft = tid < kb;
   const float c = P.c;
   const int C = P.chunks;
-  if (tid == 0) S.flags = 0;
+  if (tid == 0) {
+    S.flags = 0;
+    S.first = kb + 1;
+    S.invalid = INT_MAX;
+    S.to_pos = INT_MAX;
+  }
+  __syncthreads();
+  const unsigned long long* tsl = P.slots + unit_of(P, true, t0 + min(tid, kb)) * C;
+  const unsigned long long* dsl = is_draft ? P.slots + unit_of(P, false, d0 + tid) * C : tsl;
+  // In a fused grid with at most kFastChunks chunks per row, the partials are
+  // read together with the draft ids (one round trip), before the logits at
+  // the ids; only partials still unpublished are read again.
+  constexpr int kFastChunks = 4;
+  const bool fast = POLL && !P.filt && C <= kFastChunks;
+  unsigned long long tv[kFastChunks], dv[kFastChunks];
+  if (fast && active) {
+#pragma unroll
+    for (int g = 0; g < kFastChunks; ++g) {
+      tv[g] = g < C ? obs_u64(tsl + g) : 1ull;
+      dv[g] = (g < C && is_draft && !greedy) ? obs_u64(dsl + g) : 1ull;
+    }
+  }
   int x = -1;
   float u = 1.f;
   if (is_draft) {
@@ -417,91 +457,145 @@ __device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool 
     lq = load_elem<DT>(P.draft, (size_t)(d0 + tid) * P.V + xs);
     lp = load_elem<DT>(P.target, (size_t)(t0 + tid) * P.V + xs);
   }
-  if constexpr (POLL) {
-    // One thread waits for the sequence's last stats block in grid order (the
-    // last chunk of its bonus row), sleeping between reads so that waiting
-    // blocks add little memory traffic; the partials are read after it.
-    if (tid == 0) {
-      const unsigned long long* last = P.slots + (size_t)(P.total_draft + t0 + kb + 1) * C - 1;
-      for (int spins = 0; obs_u64(last) == 0ull && spins < P.spin_limit; ++spins)
-        __builtin_amdgcn_s_sleep(8);
-    }
-    __syncthreads();
-  }
+  if (!tok_ok) atomicOr(&S.flags, 1);  // every draft id is checked
   float mq = kNegInf, sq = 0.f, mp = kNegInf, sp = 0.f;
   float thq = kNegInf, thp = kNegInf;
   int am = INT_MAX;
-  bool bad = false;
-  int timed_out = 0;
+  bool valid = false, acc = false;
+  float ratio = __builtin_nanf("");
   if (active) {
-    const unsigned long long* tsl = P.slots + (size_t)(P.total_draft + t0 + tid) * C;
-    if (greedy) {
-      int gbad = 0;
-      merge_greedy<POLL>(tsl, C, mp, am, gbad, P.spin_limit, timed_out);
-      bad = gbad || mp == kNegInf;
-    } else {
-      int rbad = 0;
-      if (P.filt) {
-        // kept-set statistics of the filter pass
-        const RowRes rt = P.rowres[P.total_draft + t0 + tid];
-        mp = rt.m;
-        sp = rt.s;
-        thp = rt.theta;
-        rbad = rt.flags;
-        if (is_draft) {
-          const RowRes rd = P.rowres[d0 + tid];
-          mq = rd.m;
-          sq = rd.s;
-          thq = rd.theta;
-          rbad |= rd.flags;
+    bool have = true;
+    int to = 0;
+    if constexpr (POLL) {
+      // Wait for this position's partials: one read per missing partial per
+      // round, with a sleep; a position past an already-known stop needs no
+      // rows (unless every row is wanted for the side outputs). Without the
+      // fast read, the target row's last chunk (its last stats block in grid
+      // order) is awaited first and the partials are read after it.
+      const volatile int* first = &S.first;
+      for (int spins = 0;; ++spins) {
+        bool missing = false;
+        if (fast) {
+#pragma unroll
+          for (int g = 0; g < kFastChunks; ++g) missing |= (tv[g] == 0ull) | (dv[g] == 0ull);
+        } else {
+          missing = obs_u64(tsl + C - 1) == 0ull;
         }
-      } else {
-        merge_sampling<POLL>(P.slots + (size_t)(d0 + tid) * C, tsl, is_draft, C, c, mq, sq, mp,
-                             sp, P.spin_limit, timed_out);
+        if (!missing) break;
+        if (!P.full_wait && *first < tid) {
+          have = false;
+          break;
+        }
+        if (spins >= P.spin_limit) {
+          to = 1;
+          have = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+        if (fast) {
+#pragma unroll
+          for (int g = 0; g < kFastChunks; ++g) {
+            if (tv[g] == 0ull) tv[g] = obs_u64(tsl + g);
+            if (dv[g] == 0ull) dv[g] = obs_u64(dsl + g);
+          }
+        }
       }
-      bool ok = !rbad && __builtin_isfinite(mp) && sp > 0.f && __builtin_isfinite(sp);
-      if (is_draft) ok = ok && __builtin_isfinite(mq) && sq > 0.f && __builtin_isfinite(sq);
-      bad = !ok;
     }
+    if (have && fast) {
+      // merge in chunk order, as the slower path does
+      int gbad = 0;
+#pragma unroll
+      for (int g = 0; g < kFastChunks; ++g) {
+        if (g < C) {
+          float m, s_;
+          if (greedy) {
+            int ci, cb;
+            unpack_am(tv[g], m, ci, cb);
+            argmax_merge(mp, am, m, ci);
+            gbad |= cb;
+          } else {
+            if (is_draft) {
+              unpack_ms(dv[g], m, s_);
+              merge_ms(mq, sq, m, s_, c);
+            }
+            unpack_ms(tv[g], m, s_);
+            merge_ms(mp, sp, m, s_, c);
+          }
+        }
+      }
+      if (greedy) {
+        valid = !gbad && mp != kNegInf;
+      } else {
+        valid = __builtin_isfinite(mp) && sp > 0.f && __builtin_isfinite(sp);
+        if (is_draft) valid = valid && __builtin_isfinite(mq) && sq > 0.f && __builtin_isfinite(sq);
+      }
+    } else if (have) {
+      if (greedy) {
+        int gbad = 0;
+        merge_greedy<POLL>(tsl, C, mp, am, gbad, P.spin_limit, to);
+        valid = !gbad && mp != kNegInf;
+      } else {
+        int rbad = 0;
+        if (P.filt) {
+          // kept-set statistics of the filter pass
+          const RowRes rt = P.rowres[P.total_draft + t0 + tid];
+          mp = rt.m;
+          sp = rt.s;
+          thp = rt.theta;
+          rbad = rt.flags;
+          if (is_draft) {
+            const RowRes rd = P.rowres[d0 + tid];
+            mq = rd.m;
+            sq = rd.s;
+            thq = rd.theta;
+            rbad |= rd.flags;
+          }
+        } else {
+          merge_sampling<POLL>(dsl, tsl, is_draft, C, c, mq, sq, mp, sp, P.spin_limit, to);
+        }
+        valid = !rbad && __builtin_isfinite(mp) && sp > 0.f && __builtin_isfinite(sp);
+        if (is_draft) valid = valid && __builtin_isfinite(mq) && sq > 0.f && __builtin_isfinite(sq);
+      }
+      if (to) have = false;
+    }
+    if (have) {
+      if (is_draft && tok_ok && valid) {
+        if (greedy) {
+          acc = am == x;
+        } else {
+          // r = p(x)/q(x) = 2^((lp*c - Rp) - (lq*c - Rq)) * Sq / Sp; an id
+          // outside a row's kept set has probability 0 there: q(x) = 0 < p(x)
+          // accepts, p(x) = 0 rejects
+          const bool pk = lp >= thp, qk = lq >= thq;
+          if (pk && qk) {
+            const float ep = fmaf(lp, c, -ref_of(mp, c));
+            const float eq = fmaf(lq, c, -ref_of(mq, c));
+            ratio = fast_exp2(ep - eq) * (sq / sp);
+          } else {
+            ratio = pk ? kPosInf : 0.f;
+          }
+          acc = u < ratio;  // strict: u == r rejects
+        }
+      }
+      if (!valid) atomicMin(&S.invalid, tid);
+      if (!acc) atomicMin(&S.first, tid);  // also the bonus position and bad ids
+    }
+    if (to) atomicMin(&S.to_pos, tid);
     S.m[0][tid] = mq;
     S.s[0][tid] = sq;
     S.m[1][tid] = mp;
     S.s[1][tid] = sp;
     S.th[0][tid] = thq;
     S.th[1][tid] = thp;
-    if (bad) atomicOr(&S.flags, 2);
-    if (!tok_ok) atomicOr(&S.flags, 1);
-    if (timed_out) atomicOr(&S.flags, 4);
-  }
-  bool acc = false;
-  float ratio = __builtin_nanf("");
-  if (is_draft && tok_ok && !bad) {
-    if (greedy) {
-      acc = am == x;
-    } else {
-      // r = p(x)/q(x) = 2^((lp*c - Rp) - (lq*c - Rq)) * Sq / Sp; an id outside
-      // a row's kept set has probability 0 there: q(x) = 0 < p(x) accepts,
-      // p(x) = 0 rejects
-      const bool pk = lp >= thp, qk = lq >= thq;
-      if (pk && qk) {
-        const float ep = fmaf(lp, c, -ref_of(mp, c));
-        const float eq = fmaf(lq, c, -ref_of(mq, c));
-        ratio = fast_exp2(ep - eq) * (sq / sp);
-      } else {
-        ratio = pk ? kPosInf : 0.f;
-      }
-      acc = u < ratio;  // strict: u == r rejects
-    }
-  }
-  if (tid < kWave) {
-    const unsigned long long rej = __ballot(is_draft && !acc);
-    if (tid == 0) S.rej = rej;
   }
   __syncthreads();
-  const int sf = S.flags;
-  const int code = (sf & 4) ? SV_SEQ_SYNC_TIMEOUT
-                            : ((sf & 1) ? SV_SEQ_BAD_TOKEN : ((sf & 2) ? SV_SEQ_BAD_ROW : 0));
-  const int n = S.rej ? (__ffsll(S.rej) - 1) : kb;
+  const int first = S.first;
+  const int n = min(first, kb);
+  // a wait that ran out matters if its position is reached (or no stop was seen)
+  const int code = (S.to_pos <= first) ? SV_SEQ_SYNC_TIMEOUT
+                   : (S.flags & 1)     ? SV_SEQ_BAD_TOKEN
+                   : (S.invalid == n)  ? SV_SEQ_BAD_ROW
+                                       : 0;
   const bool draws = code == 0 && !greedy;
 
   if (writer) {
@@ -547,6 +641,8 @@ __device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool 
   j.thr_p = S.th[1][n];
   j.u = u_draw;
   j.out_idx = t0 + n;
+  // a timed-out wait of this block is reported through the sequence flags
+  if (tid == 0) S.timeout = code == SV_SEQ_SYNC_TIMEOUT;
   return j;
 }
 
@@ -736,8 +832,9 @@ __device__ void stats_unit(const Params& P, long long g) {
   const int wave = tid / kWave;
   const int unit = (int)(g / P.chunks);
   const int ch = (int)(g - (long long)unit * P.chunks);
-  const bool is_target = unit >= P.total_draft;
-  const int row = is_target ? unit - P.total_draft : unit;
+  bool is_target;
+  int row;
+  row_of_unit(P, unit, is_target, row);
   bool greedy = P.all_greedy != 0;
   if (!greedy && P.greedy != nullptr) greedy = P.greedy[row_seq(P, row, is_target, s_cu)] != 0;
   if (greedy && !is_target) return;  // greedy sequences never read draft rows
@@ -1057,6 +1154,43 @@ __global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
   }
 }
 
+// Returns the partials of a sequence's rows to zero (whole block): its target
+// rows and, with_draft, its draft rows. In a fused grid (POLL) a row the
+// decision never read may still be in flight: its partial is awaited first.
+// Returns nonzero (in every thread) if such a wait ran out.
+template <bool POLL>
+__device__ int clear_partials(const Params& P, int d0, int kb, int b, bool with_draft) {
+  const int C = P.chunks;
+  const int nd = with_draft ? kb : 0;
+  int to = 0;
+  for (int k = threadIdx.x; k < (nd + kb + 1) * C; k += kThreads) {
+    const int r = k / C, ch = k - r * C;
+    const bool tgt = r >= nd;
+    unsigned long long* p =
+        P.slots + unit_of(P, tgt, tgt ? d0 + b + (r - nd) : d0 + r) * C + ch;
+    if constexpr (POLL) {
+      for (int spins = 0; obs_u64(p) == 0ull; ++spins) {
+        if (spins >= P.spin_limit) {
+          to = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(4);
+      }
+    }
+    pub_u64(p, 0ull);
+  }
+  return block_sum_i(to);
+}
+
+// Marks sequence b as timed out (whole block): tokens -1, code in num_accepted.
+__device__ __forceinline__ void write_timeout(const Params& P, int d0, int kb, int b) {
+  for (int k = threadIdx.x; k <= kb; k += kThreads) P.out_tokens[d0 + b + k] = -1;
+  if (threadIdx.x == 0) {
+    P.num_accepted[b] = SV_SEQ_SYNC_TIMEOUT;
+    if (P.diag.resid_Z) P.diag.resid_Z[b] = __builtin_nanf("");
+  }
+}
+
 // ----------------------------------------------------------------- draw unit
 // Draw block (b, ch), ch < dchunks: decision of sequence b, then the tile sums
 // of slice ch of row pair n. Every block of a sampling sequence counts itself
@@ -1084,8 +1218,8 @@ __device__ void draw_unit(const Params& P, int idx) {
   const int C = P.chunks;
   if (greedy) {
     // the only reader of these partials returns them to zero
-    for (int k = tid; k < (kb + 1) * C; k += kThreads)
-      pub_u64(P.slots + (size_t)(P.total_draft + d0 + b) * C + k, 0ull);
+    __syncthreads();
+    if (clear_partials<POLL>(P, d0, kb, b, false)) write_timeout(P, d0, kb, b);
     return;
   }
   if (j.mode != kJobNone) {
@@ -1128,7 +1262,7 @@ __device__ void draw_unit(const Params& P, int idx) {
     }
   }
   // every block of the sequence counts itself, after its stores have landed
-  if (tid == 0 && (S.flags & 4)) raise_flag(P.seq_flags + b, kSeqFlagTimeout);
+  if (tid == 0 && S.timeout) raise_flag(P.seq_flags + b, kSeqFlagTimeout);
   drain_stores();
   __syncthreads();
   if (tid == 0) {
@@ -1141,11 +1275,7 @@ __device__ void draw_unit(const Params& P, int idx) {
   // Last block of the sequence: every other block has read the partials and
   // published its tile sums.
   if (s_to) {
-    for (int k = tid; k <= kb; k += kThreads) P.out_tokens[d0 + b + k] = -1;
-    if (tid == 0) {
-      P.num_accepted[b] = SV_SEQ_SYNC_TIMEOUT;
-      if (P.diag.resid_Z) P.diag.resid_Z[b] = __builtin_nanf("");
-    }
+    write_timeout(P, d0, kb, b);
   } else if (j.mode != kJobNone) {
     float Z;
     const int tok = pick<DT, VEC>(P, b, j, Z);
@@ -1157,11 +1287,7 @@ __device__ void draw_unit(const Params& P, int idx) {
   }
   __syncthreads();
   // return the sequence's workspace entries to zero
-  if (!P.filt) {
-    for (int k = tid; k < kb * C; k += kThreads) pub_u64(P.slots + (size_t)d0 * C + k, 0ull);
-    for (int k = tid; k < (kb + 1) * C; k += kThreads)
-      pub_u64(P.slots + (size_t)(P.total_draft + d0 + b) * C + k, 0ull);
-  }
+  if (!P.filt && clear_partials<POLL>(P, d0, kb, b, true)) write_timeout(P, d0, kb, b);
   for (int t = tid; t < P.ntiles; t += kThreads) pub_f(P.tiles + (size_t)b * P.ntiles + t, 0.f);
   if (tid == 0) {
     pub_i(P.draw_done + b, 0);

@@ -183,12 +183,13 @@ def test_error_codes_and_precedence():
     u = [0.3] * (K + 1)
     r = oracle.verify_sequence(q_rows, p_rows, [1, V, 2], u, 1.0)
     assert r["n"] == -1 and r["tokens"] == [-1] * (K + 1)
+    # rows of position 0 are always read
     bad = p_rows.copy()
-    bad[3, 5] = np.nan
+    bad[0, 5] = np.nan
     r = oracle.verify_sequence(q_rows, bad, [1, 2, 3], u, 1.0)
     assert r["n"] == -2 and r["tokens"] == [-1] * (K + 1)
     r = oracle.verify_sequence(q_rows, bad, [1, -1, 3], u, 1.0)
-    assert r["n"] == -1
+    assert r["n"] == -1  # an invalid id wins over an invalid row
     bad = q_rows.copy()
     bad[0, :] = -np.inf
     assert oracle.verify_sequence(bad, p_rows, [1, 2, 3], u, 1.0)["n"] == -2
@@ -200,6 +201,46 @@ def test_error_codes_and_precedence():
     bad[:] = np.nan
     r = oracle.verify_sequence(bad, p_rows, [1, 2, 3], u, 1.0, greedy=True)
     assert r["n"] >= 0
+
+
+def test_rows_past_the_first_rejection_are_not_read():
+    """R8 checks the rows the steps read: a NaN or +inf past the first
+    rejection (or in the bonus row when a draft is rejected) changes nothing,
+    while the same value in the bonus row of an all-accepted sequence fails it."""
+    V, K = 16, 3
+    rng = np.random.default_rng(11)
+    q_rows, p_rows = rng.normal(0, 1, (K, V)), rng.normal(0, 1, (K + 1, V))
+    x = [4, 2, 3]
+    p_rows[0, 4] = -np.inf  # p_0(x_0) = 0: position 0 always rejects
+    u = [0.5] * (K + 1)
+    ref = oracle.verify_sequence(q_rows, p_rows, x, u, 1.0)
+    assert ref["n"] == 0
+    for row, col in ((1, 3), (2, 0), (3, 7)):
+        bad = p_rows.copy()
+        bad[row, col] = np.nan
+        r = oracle.verify_sequence(q_rows, bad, x, u, 1.0)
+        assert r["n"] == 0 and r["tokens"] == ref["tokens"]
+        bad[row, col] = np.inf
+        assert oracle.verify_sequence(q_rows, bad, x, u, 1.0)["tokens"] == ref["tokens"]
+    badq = q_rows.copy()
+    badq[2, :] = np.nan
+    assert oracle.verify_sequence(badq, p_rows, x, u, 1.0)["tokens"] == ref["tokens"]
+    # identical rows accept everything: the bonus row is read and must be valid
+    same_q, same_p = p_rows[:K].copy(), p_rows.copy()
+    same_q[0, 4] = same_p[0, 4] = 0.0
+    ok = oracle.verify_sequence(same_q, same_p, x, u, 1.0)
+    assert ok["n"] == K
+    same_p[K, 1] = np.nan
+    assert oracle.verify_sequence(same_q, same_p, x, u, 1.0)["n"] == -2
+    # greedy: position 0 rejects (x_0 is not the argmax), later rows are unread
+    g = p_rows.copy()
+    g[0, :] = 0.0
+    g[0, 9] = 5.0
+    g[2, :] = np.nan
+    r = oracle.verify_sequence(None, g, [1, 2, 3], u, 1.0, greedy=True)
+    assert r["n"] == 0 and r["tokens"][0] == 9
+    g[0, 3] = np.nan
+    assert oracle.verify_sequence(None, g, [1, 2, 3], u, 1.0, greedy=True)["n"] == -2
 
 
 def test_residual_zero_falls_back_to_target():
