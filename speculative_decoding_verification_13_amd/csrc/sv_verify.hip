@@ -129,11 +129,33 @@ struct Vec {
       return load_elem<DT>(base, row_elem + (size_t)v);
     }
   }
+  // The same load marked non-temporal (streamed once: not kept in the caches).
+  __device__ __forceinline__ static Raw load_stream(const void* base, size_t row_elem, int v) {
+    if constexpr (VEC) {
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 t = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) +
+                                         row_elem * Dt<DT>::kBytes) +
+          v);
+      return make_uint4(t.x, t.y, t.z, t.w);
+    } else {
+      return load_elem<DT>(base, row_elem + (size_t)v);
+    }
+  }
   __device__ __forceinline__ static void get(const Raw& r, float* f) {
     if constexpr (VEC) unpack<DT>(r, f);
     else f[0] = r;
   }
 };
+
+#ifndef SV_STATS_NT
+#define SV_STATS_NT 1
+#endif
+#if SV_STATS_NT
+#define SV_STATS_LOAD Vc::load_stream
+#else
+#define SV_STATS_LOAD Vc::load
+#endif
 
 // Makes a register value opaque to the compiler, so values derived from it in
 // one pass are recomputed in the next instead of being kept alive.
@@ -687,7 +709,7 @@ __device__ void topk_block(const Params& P, long long g, const void* base, size_
 #pragma unroll
   for (int u = 0; u < kFiltVpt; ++u) {
     const int v = vb + u * kThreads + tid;
-    if (v < P.nvec) r[u] = Vc::load(base, roff, v);
+    if (v < P.nvec) r[u] = SV_STATS_LOAD(base, roff, v);
   }
   // this thread's logits in registers, in ascending id order: fn(value, id)
   auto each = [&](auto&& fn) {
@@ -856,7 +878,7 @@ __device__ void stats_unit(const Params& P, long long g) {
     for (; v + (kBatch - 1) * kThreads < ve; v += kBatch * kThreads) {
       typename Vc::Raw r[kBatch];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) r[u] = Vc::load(base, roff, v + u * kThreads);
+      for (int u = 0; u < kBatch; ++u) r[u] = SV_STATS_LOAD(base, roff, v + u * kThreads);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
@@ -874,7 +896,7 @@ __device__ void stats_unit(const Params& P, long long g) {
     }
     for (; v < ve; v += kThreads) {
       float f[N];
-      Vc::get(Vc::load(base, roff, v), f);
+      Vc::get(SV_STATS_LOAD(base, roff, v), f);
 #pragma unroll
       for (int k = 0; k < N; ++k) {
         bad |= is_nan_or_posinf(f[k]);
@@ -900,7 +922,7 @@ __device__ void stats_unit(const Params& P, long long g) {
     for (; v + (kBatch - 1) * kThreads < ve; v += kBatch * kThreads) {
       typename Vc::Raw r[kBatch];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) r[u] = Vc::load(base, roff, v + u * kThreads);
+      for (int u = 0; u < kBatch; ++u) r[u] = SV_STATS_LOAD(base, roff, v + u * kThreads);
       __builtin_amdgcn_sched_barrier(0);
       float f[kBatch * N];
 #pragma unroll
@@ -909,7 +931,7 @@ __device__ void stats_unit(const Params& P, long long g) {
     }
     for (; v < ve; v += kThreads) {
       float f[N];
-      Vc::get(Vc::load(base, roff, v), f);
+      Vc::get(SV_STATS_LOAD(base, roff, v), f);
       online_update<N>(m, s, f, c);
     }
     wave_reduce_ms(m, s, c);
