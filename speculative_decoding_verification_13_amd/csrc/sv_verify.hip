@@ -164,6 +164,40 @@ __device__ __forceinline__ void opaque(uint4& x) {
 }
 __device__ __forceinline__ void opaque(float& x) { asm volatile("" : "+v"(x)); }
 
+// Maximum of this thread's register-held logits (vectors v0, v0 + kThreads,
+// ... below nvec) with NaN-propagating maxima: packed over fp16 pairs, over
+// widened values otherwise.
+template <int DT, bool VEC, class Raw>
+__device__ __forceinline__ float thread_max_prop(const Raw (&r)[kFiltVpt], int v0, int nvec) {
+  if constexpr (VEC && DT == SV_F16) {
+    half2_t m2 = {(_Float16)kNegInf, (_Float16)kNegInf};
+#pragma unroll
+    for (int u = 0; u < kFiltVpt; ++u) {
+      if (v0 + u * kThreads < nvec) {
+        const uint4 w = r[u];
+        const half2_t a = __builtin_bit_cast(half2_t, w.x), b = __builtin_bit_cast(half2_t, w.y);
+        const half2_t cc = __builtin_bit_cast(half2_t, w.z), d = __builtin_bit_cast(half2_t, w.w);
+        m2 = __builtin_elementwise_maximum(m2, __builtin_elementwise_maximum(a, b));
+        m2 = __builtin_elementwise_maximum(m2, __builtin_elementwise_maximum(cc, d));
+      }
+    }
+    return __builtin_elementwise_maximum((float)m2.x, (float)m2.y);
+  } else {
+    constexpr int N = VEC ? Dt<DT>::N : 1;
+    float m = kNegInf;
+#pragma unroll
+    for (int u = 0; u < kFiltVpt; ++u) {
+      if (v0 + u * kThreads < nvec) {
+        float f[N];
+        Vec<DT, VEC>::get(r[u], f);
+#pragma unroll
+        for (int k = 0; k < N; ++k) m = __builtin_elementwise_maximum(m, f[k]);
+      }
+    }
+    return m;
+  }
+}
+
 // Element k (0 <= k < N, not a compile-time constant) of one raw vector.
 template <int DT>
 __device__ __forceinline__ float elem_of(const uint4& v, int k) {
@@ -621,14 +655,17 @@ __device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool 
   const bool draws = code == 0 && !greedy;
 
   if (writer) {
-    // slot n of a drawing sequence is written by the block that draws
+    // slot n of a drawing sequence is written by the block that draws. Outputs
+    // another block may overwrite later (a timed-out wait) are written with
+    // agent-scope stores, so they reach the coherence point before this block
+    // counts itself and the later overwrite lands after them.
     if (active && !(draws && tid == n)) {
       int tok = -1;
       if (code == 0) {
         if (tid < n) tok = x;
         else if (tid == n) tok = am;
       }
-      P.out_tokens[t0 + tid] = tok;
+      pub_i(P.out_tokens + t0 + tid, tok);
     }
     const float kLn2 = 0.69314718055994531f;
     const float nan = __builtin_nanf("");
@@ -646,8 +683,8 @@ __device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool 
       }
     }
     if (tid == 0 && !draws) {
-      P.num_accepted[b] = code ? code : n;
-      if (P.diag.resid_Z) P.diag.resid_Z[b] = nan;
+      pub_i(P.num_accepted + b, code ? code : n);
+      if (P.diag.resid_Z) pub_f(P.diag.resid_Z + b, nan);
     }
   }
   Job j;
@@ -726,26 +763,39 @@ __device__ void topk_block(const Params& P, long long g, const void* base, size_
       }
     }
   };
-  // thread maximum (NaN ignored; a +inf makes the row invalid anyway)
-  float tmax = kNegInf;
-  int bad = 0;
-  each([&](float f, int) {
-    bad |= is_nan_or_posinf(f);
-    tmax = fmaxf(tmax, f);
-  });
-  // Bound: the largest thread maximum that at least k thread maxima reach; k
-  // threads then hold a finite logit >= it, so it is <= the k-th largest.
+  // Thread maximum with a NaN-propagating max: a NaN or +inf anywhere in the
+  // thread's logits shows up as the maximum (-inf does not).
+  const float tmax = thread_max_prop<DT, VEC>(r, vb + tid, P.nvec);
+  const int bad = (tmax != tmax || tmax == kPosInf) ? 1 : 0;
+  // Bound: with the threads in groups of g (g = 4, 2 or 1, the largest with
+  // at least k groups), the largest group maximum that at least k group maxima
+  // reach; k groups then hold a finite logit >= it, so it is <= the chunk's
+  // k-th largest. Only the threads that own a group count.
   const int k = P.top_k;
+  __shared__ unsigned s_lbk;  // the bound as an order-preserving key
   float lb = kNegInf;
   if (k <= kBoundMaxK) {
-    s_max[tid] = tmax;
+    const int g = (k <= kThreads / 4) ? 4 : ((k <= kThreads / 2) ? 2 : 1);
+    float gm = tmax;
+    if (g >= 2) gm = fmaxf(gm, dpp_f<0xB1>(gm));  // quad_perm [1,0,3,2]
+    if (g >= 4) gm = fmaxf(gm, dpp_f<0x4E>(gm));  // quad_perm [2,3,0,1]
+    const int ng = kThreads / g;
+    if ((tid & (g - 1)) == 0) s_max[tid / g] = gm;
+    if (tid == 0) s_lbk = key_of(kNegInf);
     __syncthreads();
-    int ge = 0;
-    for (int j = 0; j < kThreads; j += 4) {
-      const float4 t = *reinterpret_cast<const float4*>(&s_max[j]);
-      ge += (t.x >= tmax) + (t.y >= tmax) + (t.z >= tmax) + (t.w >= tmax);
+    if (tid < ng) {
+      const float mine = s_max[tid];
+      int ge = 0;
+      for (int j = 0; j < ng; j += 4) {
+        const float4 t = *reinterpret_cast<const float4*>(&s_max[j]);
+        ge += (t.x >= mine) + (t.y >= mine) + (t.z >= mine) + (t.w >= mine);
+      }
+      const float cand = (ge >= k && mine > kNegInf && mine < kPosInf) ? mine : kNegInf;
+      const float wm = wave_max_dpp(cand);
+      if ((tid & (kWave - 1)) == 0 && wm > kNegInf) atomicMax(&s_lbk, key_of(wm));
     }
-    lb = block_max_f((ge >= k && tmax != kNegInf) ? tmax : kNegInf);
+    __syncthreads();
+    lb = float_of_key(s_lbk);
   }
   const int flags = block_sum_i(bad) ? kRecFlagBad : 0;
   unsigned* rec = P.rec + (size_t)g * P.rec_words;
@@ -1204,12 +1254,13 @@ __device__ int clear_partials(const Params& P, int d0, int kb, int b, bool with_
   return block_sum_i(to);
 }
 
-// Marks sequence b as timed out (whole block): tokens -1, code in num_accepted.
+// Marks sequence b as timed out (whole block): tokens -1, code in num_accepted
+// (agent-scope stores, ordered after the writer block's outputs).
 __device__ __forceinline__ void write_timeout(const Params& P, int d0, int kb, int b) {
-  for (int k = threadIdx.x; k <= kb; k += kThreads) P.out_tokens[d0 + b + k] = -1;
+  for (int k = threadIdx.x; k <= kb; k += kThreads) pub_i(P.out_tokens + d0 + b + k, -1);
   if (threadIdx.x == 0) {
-    P.num_accepted[b] = SV_SEQ_SYNC_TIMEOUT;
-    if (P.diag.resid_Z) P.diag.resid_Z[b] = __builtin_nanf("");
+    pub_i(P.num_accepted + b, SV_SEQ_SYNC_TIMEOUT);
+    if (P.diag.resid_Z) pub_f(P.diag.resid_Z + b, __builtin_nanf(""));
   }
 }
 
@@ -1302,9 +1353,9 @@ __device__ void draw_unit(const Params& P, int idx) {
     float Z;
     const int tok = pick<DT, VEC>(P, b, j, Z);
     if (tid == 0) {
-      P.out_tokens[j.out_idx] = tok;
-      P.num_accepted[b] = j.n;
-      if (P.diag.resid_Z) P.diag.resid_Z[b] = Z;
+      pub_i(P.out_tokens + j.out_idx, tok);
+      pub_i(P.num_accepted + b, j.n);
+      if (P.diag.resid_Z) pub_f(P.diag.resid_Z + b, Z);
     }
   }
   __syncthreads();
