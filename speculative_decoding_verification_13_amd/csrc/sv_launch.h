@@ -29,6 +29,7 @@ constexpr int kBoundMaxK = kThreads;      // largest k bounded by the per-thread
 constexpr int kFilterMaxLevels = 2048;    // LDS entries of the per-row level sort
 constexpr int kFilterLdsKeys = 4096;      // record entries a filter block stages in LDS
 constexpr int kFilterLdsChunks = 64;      // record headers a filter block stages in LDS
+constexpr int kExplicitMax = 2048;        // candidates a filtered draw gathers in LDS
 
 // Chunk record of a filtered row: header then `kcap` (value bits, id) pairs.
 //   [0] entries written   [1] value of an implicit tie class   [2] its count

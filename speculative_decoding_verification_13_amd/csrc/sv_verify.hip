@@ -1264,6 +1264,134 @@ __device__ __forceinline__ void write_timeout(const Params& P, int d0, int kb, i
   }
 }
 
+// Final draw of a filtered sequence from its candidate records (whole block):
+// p_n is zero outside its kept set, whose ids and logits all sit in the chunk
+// records of row p_n when no tie class at the cut was kept as a count, so the
+// residual max(0, p_n - q_n) (or p_n for the bonus) is formed on those ids
+// alone, with q_n's logit loaded at each id. The weights are sorted by id and
+// scanned for the first cumulative weight above u*Z, as the inverse CDF over
+// the whole row would. Returns false (in every thread) when the records do not
+// list the kept set explicitly or it exceeds kExplicitMax; the caller then
+// draws from the rows themselves.
+__device__ bool explicit_usable(const Params& P, const Job& j) {
+  const unsigned* rec0 = P.rec + (size_t)(P.total_draft + j.prow) * P.chunks * P.rec_words;
+  int implicit = 0, ne = 0;
+  for (int ch = threadIdx.x; ch < P.chunks; ch += kThreads) {
+    const unsigned* h = rec0 + (size_t)ch * P.rec_words;
+    ne += min((int)h[0], P.kcap);
+    if ((h[3] & kRecFlagImplicitTies) && __uint_as_float(h[1]) >= j.thr_p) implicit = 1;
+  }
+  return block_sum_i(implicit) == 0 && block_sum_i(ne) <= kExplicitMax;
+}
+
+template <int DT>
+__device__ int explicit_draw(const Params& P, const Job& j, float& Zout) {
+  __shared__ int s_id[kExplicitMax];
+  __shared__ float s_lp[kExplicitMax];
+  __shared__ float s_wt[kExplicitMax];
+  __shared__ int s_cnt;
+  const int tid = threadIdx.x;
+  const float c = P.c;
+  const unsigned* rec0 = P.rec + (size_t)(P.total_draft + j.prow) * P.chunks * P.rec_words;
+  if (tid == 0) s_cnt = 0;
+  __syncthreads();
+  for (int ch = 0; ch < P.chunks; ++ch) {
+    const unsigned* h = rec0 + (size_t)ch * P.rec_words;
+    const int ne = min((int)h[0], P.kcap);
+    for (int e = tid; e < ne; e += kThreads) {
+      const float v = __uint_as_float(h[kRecHeader + 2 * e]);
+      if (v >= j.thr_p) {
+        const int at = atomicAdd(&s_cnt, 1);
+        if (at < kExplicitMax) {
+          s_id[at] = (int)h[kRecHeader + 2 * e + 1];
+          s_lp[at] = v;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int n = min(s_cnt, kExplicitMax);
+  int p2 = 2;
+  while (p2 < n) p2 <<= 1;
+  // weights; pads sort last with zero weight
+  for (int x = tid; x < p2; x += kThreads) {
+    if (x < n) {
+      const float ep = fast_exp2(fmaf(s_lp[x], c, -j.Rp));
+      float w;
+      if (j.mode == kJobBonus) {
+        w = ep * j.invSp;
+      } else {
+        const float lq = load_elem<DT>(P.draft, (size_t)j.qrow * P.V + s_id[x]);
+        const float q = (lq >= j.thr_q) ? fast_exp2(fmaf(lq, c, -j.Rq)) * j.invSq : 0.0f;
+        w = fmaxf(fmaf(ep, j.invSp, -q), 0.0f);
+      }
+      s_wt[x] = w;
+    } else {
+      s_id[x] = INT_MAX;
+      s_lp[x] = kNegInf;
+      s_wt[x] = 0.0f;
+    }
+  }
+  __syncthreads();
+  // bitonic sort by id, ascending
+  for (int size = 2; size <= p2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int x = tid; x < p2; x += kThreads) {
+        const int y = x ^ stride;
+        if (y > x) {
+          const bool up = (x & size) == 0;
+          const int a = s_id[x], bb = s_id[y];
+          if (up ? (a > bb) : (a < bb)) {
+            s_id[x] = bb;
+            s_id[y] = a;
+            const float t = s_wt[x];
+            s_wt[x] = s_wt[y];
+            s_wt[y] = t;
+            const float tl = s_lp[x];
+            s_lp[x] = s_lp[y];
+            s_lp[y] = tl;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // inclusive scan in id order (each thread a contiguous run), then the pick
+  const int per = (p2 + kThreads - 1) / kThreads;
+  const int x0 = min(tid * per, p2), x1 = min(x0 + per, p2);
+  int tok = INT_MAX;
+  float Z = 0.0f;
+  for (int pass = 0; pass < 2; ++pass) {
+    float local = 0.0f;
+    for (int x = x0; x < x1; ++x) local += s_wt[x];
+    float total;
+    const float incl = block_incl_scan(local, total);
+    if (pass == 0 && !(total > 0.0f) && j.mode == kJobResidual) {
+      // the residual mass rounded to zero: draw from p_n instead
+      for (int x = x0; x < x1; ++x)
+        s_wt[x] = (x < n) ? fast_exp2(fmaf(s_lp[x], c, -j.Rp)) * j.invSp : 0.0f;
+      __syncthreads();
+      continue;
+    }
+    Z = total;
+    const float target = j.u * total;
+    float run = incl - local;
+    int cand = INT_MAX, lastpos = -1;
+    for (int x = x0; x < x1; ++x) {
+      const float w = s_wt[x];
+      if (cand == INT_MAX && run + w > target) cand = x;
+      if (w > 0.0f) lastpos = x;
+      run += w;
+    }
+    int at = block_min_i(cand);
+    if (at == INT_MAX) at = block_max_i(lastpos);
+    tok = (at >= 0 && at < n) ? s_id[at] : s_id[0];
+    break;
+  }
+  Zout = Z;
+  return tok;
+}
+
 // ----------------------------------------------------------------- draw unit
 // Draw block (b, ch), ch < dchunks: decision of sequence b, then the tile sums
 // of slice ch of row pair n. Every block of a sampling sequence counts itself
@@ -1294,6 +1422,21 @@ __device__ void draw_unit(const Params& P, int idx) {
     __syncthreads();
     if (clear_partials<POLL>(P, d0, kb, b, false)) write_timeout(P, d0, kb, b);
     return;
+  }
+  if constexpr (!POLL) {
+    // filtered: draw from the candidate records when they list the kept set
+    if (P.filt && j.mode != kJobNone && explicit_usable(P, j)) {
+      if (ch == 0) {
+        float Z;
+        const int tok = explicit_draw<DT>(P, j, Z);
+        if (tid == 0) {
+          pub_i(P.out_tokens + j.out_idx, tok);
+          pub_i(P.num_accepted + b, j.n);
+          if (P.diag.resid_Z) pub_f(P.diag.resid_Z + b, Z);
+        }
+      }
+      return;
+    }
   }
   if (j.mode != kJobNone) {
     // tile sums of slice ch of row pair n: the thread's vector k*kThreads + tid
