@@ -1,5 +1,6 @@
 // C ABI of the verification library: argument checks, workspace layout and the
-// launch of the kernels in sv_verify.hip. Nothing here touches the device
+// launch of the kernels (sv_fused.hip without filters, sv_verify.hip with
+// filters or for rows longer than the one-kernel step takes). Nothing here touches the device
 // before every argument has been checked.
 #include <limits.h>
 #include <math.h>
@@ -43,15 +44,18 @@ int kcap_for(int top_k) { return (top_k + 256 + 63) / 64 * 64; }
 //   slots[(total_draft + rows) * cmax]     64-bit chunk partials (greedy rows, and
 //                                          every row when no filter is active);
 //                                          zero means "not yet published"
-//   tiles[B * dmax * tiles per draw block] draw-weight tile sums
+//   tiles[B * dmax * tiles per draw block] draw-weight tile sums (separate kernels)
+//   draws[B * 2 * dmax]                    slice weight sums of the final draw
+//                                          (one-kernel step)
+//   decs[B * kDecRecordWords]              decision records (one-kernel step)
 // and with top-k active:
 //   rec[(total_draft + rows) * cmax * rec_words]  chunk records of sampling rows
 //   rowres[total_draft + rows]                    kept-set statistics per row
-// Counters, flags, partials and tile sums must be zero when a call starts; the
-// blocks that read them return them to zero, so the layout may differ from call
-// to call. The regions are sized for the scalar path (one element per vector),
-// which has the most chunks: a row of nvec <= V vectors never has more than
-// cmax chunks.
+// Counters, flags, partials, tile and weight sums must be zero when a call
+// starts; the blocks that read them return them to zero, so the layout may
+// differ from call to call. The regions are sized for the scalar path (one
+// element per vector), which has the most chunks: a row of nvec <= V vectors
+// never has more than cmax chunks.
 bool make_plan(int B, int total_draft, int V, int top_k, size_t ws_bytes, sv::Plan& L) {
   if (B < 0 || total_draft < 0 || V < 1 || V > kMaxV) return false;
   const long long rows = (long long)total_draft + B;
@@ -76,6 +80,10 @@ bool make_plan(int B, int total_draft, int V, int top_k, size_t ws_bytes, sv::Pl
   off += align_up(units * (size_t)cmax * 8);
   L.off_tiles = off;
   off += align_up((size_t)B * (size_t)dmax * sv::kTilesPerDraw * 4);
+  L.off_draws = off;
+  off += align_up((size_t)B * 2 * (size_t)dmax * 8);
+  L.off_decs = off;
+  off += align_up((size_t)B * sv::kDecRecordWords * 8);
   L.off_rec = L.off_rowres = off;
   if (filt) {
     const size_t rec_words = sv::kRecHeader + 2 * (size_t)kcap_for(top_k);
@@ -144,6 +152,8 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
   P.chunk_vecs = filt ? sv::kFiltChunkVecs : (int)chunk_vecs_for(P.nvec);
   P.chunks = (P.nvec + P.chunk_vecs - 1) / P.chunk_vecs;
   P.dchunks = (P.nvec + sv::kDrawVecs - 1) / sv::kDrawVecs;
+  // unfiltered rows of at most kMaxDrawSlices slices run as one kernel
+  L.fused = !filt && P.dchunks <= sv::kMaxDrawSlices;
   P.ntiles = P.dchunks * sv::kTilesPerDraw;
   // greedy-only calls skip the draft rows
   P.stats_block0 = all_greedy ? (long long)total_draft * P.chunks : 0;
@@ -159,6 +169,8 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
   P.rowres = filt ? reinterpret_cast<sv::RowRes*>(ws + L.off_rowres) : nullptr;
   P.slots = reinterpret_cast<unsigned long long*>(ws + L.off_slots);
   P.tiles = reinterpret_cast<float*>(ws + L.off_tiles);
+  P.draws = reinterpret_cast<unsigned long long*>(ws + L.off_draws);
+  P.decs = reinterpret_cast<unsigned long long*>(ws + L.off_decs);
   P.draw_done = reinterpret_cast<int*>(ws + L.off_draw_done);
   P.seq_flags = reinterpret_cast<int*>(ws + L.off_seq_flags);
   P.spin_limit = (diag != nullptr && diag->spin_limit > 0) ? diag->spin_limit : kDefaultSpinLimit;
@@ -174,8 +186,20 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
   L.filter_blocks = filt ? (long long)total_draft + P.rows : 0;
   L.draw_blocks = (long long)B * P.dchunks;
   P.stats_blocks = L.stats_blocks;
-  if (L.stats_blocks + L.draw_blocks > (long long)UINT32_MAX / sv::kThreads)
+  if ((long long)B + L.stats_blocks + L.draw_blocks > (long long)UINT32_MAX / sv::kThreads)
     return SV_EUNSUPPORTED;
+  // The one-kernel step places its B decision blocks ahead of the statistics
+  // they wait for when they fill at most a fraction of the chip (two per
+  // compute unit), so the statistics always have room to run; otherwise they
+  // follow the statistics blocks.
+  P.decide_first = 0;
+  if (L.fused) {
+    int dev = 0, cus = 0;
+    if (hipStreamGetDevice(stream, &dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        B <= 2 * cus)
+      P.decide_first = 1;
+  }
   hipEvent_t* ev = nullptr;
   int nev = 0;
   if (diag != nullptr) {
@@ -188,7 +212,17 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
     ev = diag->stage_events;
     nev = diag->n_stage_events;
   }
-  const hipError_t err = sv::launch(dtype, vec, P, L, stream, ev, nev);
+  hipError_t err;
+  if (L.fused) {
+    // stage events: before the kernel, then (every further one) after it
+    if (ev != nullptr && nev > 0 && hipEventRecord(ev[0], stream) != hipSuccess) return SV_EHIP;
+    err = sv::launch_fused(dtype, vec, P, L, stream);
+    if (err != hipSuccess) return SV_EHIP;
+    for (int e = 1; ev != nullptr && e < nev; ++e)
+      if (hipEventRecord(ev[e], stream) != hipSuccess) return SV_EHIP;
+    return SV_OK;
+  }
+  err = sv::launch(dtype, vec, P, L, stream, ev, nev);
   return err == hipSuccess ? SV_OK : SV_EHIP;
 }
 

@@ -10,6 +10,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <stdint.h>
 
 #include <type_traits>
@@ -148,22 +149,70 @@ __device__ __forceinline__ bool is_nan_or_posinf(float x) {
   return __builtin_isfpclass(x, 0x0003 | 0x0200);  // sNaN | qNaN | +inf
 }
 
-// ---- wave / block reductions (wave64) ----
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+// ---- wave reductions through DPP (no LDS round trips; every lane active) ----
+// Reductions: swap neighbours, swap pairs, mirror half rows, mirror rows (every
+// lane of a 16-lane row then holds the row's result), then broadcast lane 15
+// into rows 1 and 3 and lane 31 into rows 2 and 3; lane 63 ends with the wave
+// result. Inclusive scans: shift right by 1, 2, 4, 8 within each row (lanes
+// with no source add the identity), then the same two broadcasts.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
 }
-__device__ __forceinline__ int wave_min_i(int x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = min(x, __shfl_xor(x, o));
-  return x;
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_rows_i(int v, int ident) {
+  return __builtin_amdgcn_update_dpp(ident, v, CTRL, ROWS, 0xF, false);
 }
-__device__ __forceinline__ int wave_max_i(int x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o));
-  return x;
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
 }
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_rows_f(float v, float ident) {
+  return __builtin_bit_cast(float, dpp_rows_i<CTRL, ROWS>(__builtin_bit_cast(int, v),
+                                                          __builtin_bit_cast(int, ident)));
+}
+__device__ __forceinline__ float lane63_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror
+  v = fmaxf(v, dpp_rows_f<0x142, 0xA>(v, kNegInf));  // row_bcast:15
+  v = fmaxf(v, dpp_rows_f<0x143, 0xC>(v, kNegInf));  // row_bcast:31
+  return lane63_f(v);
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  v += dpp_rows_f<0x142, 0xA>(v, 0.0f);
+  v += dpp_rows_f<0x143, 0xC>(v, 0.0f);
+  return lane63_f(v);
+}
+__device__ __forceinline__ int wave_min_i(int v) {
+  v = min(v, dpp_i<0xB1>(v));
+  v = min(v, dpp_i<0x4E>(v));
+  v = min(v, dpp_i<0x141>(v));
+  v = min(v, dpp_i<0x140>(v));
+  v = min(v, dpp_rows_i<0x142, 0xA>(v, INT_MAX));
+  v = min(v, dpp_rows_i<0x143, 0xC>(v, INT_MAX));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+  v = max(v, dpp_i<0xB1>(v));
+  v = max(v, dpp_i<0x4E>(v));
+  v = max(v, dpp_i<0x141>(v));
+  v = max(v, dpp_i<0x140>(v));
+  v = max(v, dpp_rows_i<0x142, 0xA>(v, INT_MIN));
+  v = max(v, dpp_rows_i<0x143, 0xC>(v, INT_MIN));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ float wave_sum(float x) { return wave_sum_dpp(x); }
+
 __device__ __forceinline__ void wave_merge_ms(float& m, float& s, float c) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -182,41 +231,6 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i, int& bad) {
   }
 }
 
-// ---- wave reductions through DPP (no LDS round trips) ----
-// Steps: swap neighbours, swap pairs, mirror half rows, mirror rows (every lane
-// of a 16-lane row then holds the row's result), then broadcast lane 15 into
-// rows 1 and 3 and lane 31 into rows 2 and 3; lane 63 ends with the wave result.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF,
-                                                            0xF, false));
-}
-template <int CTRL, int ROWS>
-__device__ __forceinline__ float dpp_rows_f(float v, float ident) {
-  return __builtin_bit_cast(float,
-                            __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, ident),
-                                                        __builtin_bit_cast(int, v), CTRL, ROWS,
-                                                        0xF, false));
-}
-__device__ __forceinline__ float wave_max_dpp(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
-  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
-  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
-  v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror
-  v = fmaxf(v, dpp_rows_f<0x142, 0xA>(v, kNegInf));  // row_bcast:15
-  v = fmaxf(v, dpp_rows_f<0x143, 0xC>(v, kNegInf));  // row_bcast:31
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
-}
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-  v += dpp_f<0xB1>(v);
-  v += dpp_f<0x4E>(v);
-  v += dpp_f<0x141>(v);
-  v += dpp_f<0x140>(v);
-  v += dpp_rows_f<0x142, 0xA>(v, 0.0f);
-  v += dpp_rows_f<0x143, 0xC>(v, 0.0f);
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
-}
-
 // Wave-wide (max, sum) of per-lane partials: the maximum first, then each
 // lane's sum moved to the maximum's reference (one exponent), then the sum.
 __device__ __forceinline__ void wave_reduce_ms(float& m, float& s, float c) {
@@ -228,12 +242,12 @@ __device__ __forceinline__ void wave_reduce_ms(float& m, float& s, float c) {
 
 // Inclusive prefix sum over the wave (lane order).
 __device__ __forceinline__ float wave_incl_scan(float x) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const float y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  x += dpp_rows_f<0x111, 0xF>(x, 0.0f);  // row_shr:1
+  x += dpp_rows_f<0x112, 0xF>(x, 0.0f);  // row_shr:2
+  x += dpp_rows_f<0x114, 0xF>(x, 0.0f);  // row_shr:4
+  x += dpp_rows_f<0x118, 0xF>(x, 0.0f);  // row_shr:8
+  x += dpp_rows_f<0x142, 0xA>(x, 0.0f);  // row_bcast:15
+  x += dpp_rows_f<0x143, 0xC>(x, 0.0f);  // row_bcast:31
   return x;
 }
 
@@ -273,6 +287,33 @@ __device__ __forceinline__ int block_max_i(int x) {
   x = wave_max_i(x);
   __syncthreads();
   if ((threadIdx.x & (kWave - 1)) == 0) s_w[threadIdx.x / kWave] = x;
+  __syncthreads();
+  int r = s_w[0];
+#pragma unroll
+  for (int k = 1; k < kBlock / kWave; ++k) r = max(r, s_w[k]);
+  return r;
+}
+
+// Smallest thread index of the block whose `pred` holds (INT_MAX if none), and
+// the largest (-1 if none), through one ballot per wave.
+__device__ __forceinline__ int block_first_lane(bool pred) {
+  __shared__ int s_w[kBlock / kWave];
+  const unsigned long long m = __ballot(pred);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0)
+    s_w[threadIdx.x / kWave] = m ? (int)(threadIdx.x + __ffsll((long long)m) - 1) : INT_MAX;
+  __syncthreads();
+  int r = s_w[0];
+#pragma unroll
+  for (int k = 1; k < kBlock / kWave; ++k) r = min(r, s_w[k]);
+  return r;
+}
+__device__ __forceinline__ int block_last_lane(bool pred) {
+  __shared__ int s_w[kBlock / kWave];
+  const unsigned long long m = __ballot(pred);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0)
+    s_w[threadIdx.x / kWave] = m ? (int)(threadIdx.x + 63 - __clzll((long long)m)) : -1;
   __syncthreads();
   int r = s_w[0];
 #pragma unroll

@@ -1,4 +1,5 @@
-// Internal interface between the C ABI (sv_api.hip) and the kernels (sv_verify.hip).
+// Internal interface between the C ABI (sv_api.hip) and the kernels
+// (sv_fused.hip, sv_verify.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -30,6 +31,9 @@ constexpr int kFilterMaxLevels = 2048;    // LDS entries of the per-row level so
 constexpr int kFilterLdsKeys = 4096;      // record entries a filter block stages in LDS
 constexpr int kFilterLdsChunks = 64;      // record headers a filter block stages in LDS
 constexpr int kExplicitMax = 2048;        // candidates a filtered draw gathers in LDS
+constexpr int kMaxDrawSlices = kThreads;  // draw blocks per sequence of the one-kernel
+                                          // step (longer rows take the separate kernels)
+constexpr int kDecRecordWords = 5;        // 64-bit words of a decision record
 
 // Chunk record of a filtered row: header then `kcap` (value bits, id) pairs.
 //   [0] entries written   [1] value of an implicit tie class   [2] its count
@@ -82,11 +86,12 @@ struct Params {
   float c;                 // log2(e) / temperature (0 if all greedy)
   int chunks;              // stats blocks per row
   int chunk_vecs;          // vectors per stats block (a multiple of kStepVecs)
-  int dchunks;             // draw blocks per sequence
+  int dchunks;             // draw blocks (vocabulary slices) per sequence
   int nvec;                // vectors (or elements, scalar path) per row
   int ntiles;              // draw tiles per row = dchunks * kTilesPerDraw
-  long long stats_block0;  // first stats block (skips draft rows when all greedy)
-  long long stats_blocks;  // stats blocks launched (the fused grid's draw blocks follow)
+  long long stats_block0;  // first stats unit block (skips draft rows when all greedy;
+                           // draft-then-target order)
+  long long stats_blocks;  // stats blocks launched
   int spin_limit;          // bound of every wait (iterations)
   int full_wait;           // 1: decisions read every row (side outputs requested)
   int filt;                // 1: top-k (and top-p) filters active
@@ -104,20 +109,33 @@ struct Params {
   // target rows, chunks innermost.
   unsigned long long* slots;  // [(total_draft + rows) * chunks]
   float* tiles;            // [B * ntiles] draw-weight tile sums
-  int* draw_done;          // [B] draw blocks finished per sequence (zero between calls)
+  int* draw_done;          // [B] blocks finished per sequence (zero between calls)
   int* seq_flags;          // [B] kSeqFlag* bits (zero between calls)
+  // One-kernel step: slice weight sums of each sequence's final draw, 64-bit
+  // (tag bit 63, float bits below), two sets of `dchunks` per sequence (the
+  // residual, then the target row if the residual mass rounds to zero).
+  unsigned long long* draws;  // [B * 2 * dchunks]
+  // One-kernel step: decision record of each sampling sequence, published by
+  // its decision block for its draw blocks (zero: not yet published).
+  unsigned long long* decs;   // [B * kDecRecordWords]
+  int decide_first;        // decision blocks ahead of the statistics blocks
   DiagPtrs diag;
 };
 
 // Grid size and workspace offsets of one call.
 struct Plan {
   int chunks, chunk_vecs, dchunks;
+  bool fused;  // one kernel (k_verify) instead of statistics, filter and draw kernels
   long long stats_blocks, filter_blocks, draw_blocks;
-  size_t off_slots, off_tiles, off_draw_done, off_seq_flags, off_rec, off_rowres, total_bytes;
+  size_t off_slots, off_tiles, off_draws, off_decs, off_draw_done, off_seq_flags, off_rec, off_rowres,
+      total_bytes;
 };
 
+// The separate statistics / filter / draw kernels (sv_verify.hip).
 hipError_t launch(int dtype, bool vec, const Params& P, const Plan& L, hipStream_t s,
                   hipEvent_t* ev, int nev);
+// The one-kernel unfiltered step (sv_fused.hip).
+hipError_t launch_fused(int dtype, bool vec, const Params& P, const Plan& L, hipStream_t s);
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t s);
 
 }  // namespace sv

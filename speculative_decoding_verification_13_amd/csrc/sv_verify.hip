@@ -1,4 +1,6 @@
-// The verification step as two HIP kernels for gfx950.
+// The verification step as separate statistics, filter and draw kernels for
+// gfx950: the path of calls with top-k / top-p filters, and of unfiltered calls
+// whose rows are too long for the one-kernel step (sv_fused.hip).
 //
 // k_stats streams every logit row once. Each block takes one chunk of one row
 // and writes one 64-bit partial: for a sampling row the chunk maximum m and the
@@ -26,136 +28,12 @@
 // (greedy check, consistent temperature).
 #include <limits.h>
 
-#include "sv_device.h"
-#include "sv_launch.h"
+#include "sv_rows.h"
 
 namespace sv {
 
 namespace {
 
-constexpr int kCuLds = 1024;  // offsets staged in LDS for the row -> sequence search
-
-__device__ __forceinline__ bool seq_bounds(const Params& P, int b, int& d0, int& kb) {
-  if (P.cu == nullptr) {
-    d0 = b * P.K;
-    kb = P.K;
-    return true;
-  }
-  const int a = P.cu[b];
-  const int e = P.cu[b + 1];
-  if (a < 0 || e < a || e > P.total_draft || e - a > SV_MAX_K) return false;
-  d0 = a;
-  kb = e - a;
-  return true;
-}
-
-__device__ __forceinline__ bool seq_greedy(const Params& P, int b) {
-  return P.all_greedy || (P.greedy != nullptr && P.greedy[b] != 0);
-}
-
-// Stats units: draft rows, then target rows (both in row order, so the grid
-// streams each logit array linearly).
-__device__ __forceinline__ long long unit_of(const Params& P, bool is_target, int row) {
-  return is_target ? (long long)P.total_draft + row : (long long)row;
-}
-__device__ __forceinline__ void row_of_unit(const Params& P, int unit, bool& is_target, int& row) {
-  is_target = unit >= P.total_draft;
-  row = is_target ? unit - P.total_draft : unit;
-}
-
-// (max, sum) of a sampling chunk; NaN is stored canonical. Never all-zero
-// bits: a +0 maximum brings a term 2^0 = 1 into the sum.
-__device__ __forceinline__ unsigned long long pack_ms(float m, float s) {
-  if (m != m) m = __builtin_nanf("");
-  return ((unsigned long long)__float_as_uint(s) << 32) | __float_as_uint(m);
-}
-__device__ __forceinline__ void unpack_ms(unsigned long long v, float& m, float& s) {
-  m = __uint_as_float((unsigned)v);
-  s = __uint_as_float((unsigned)(v >> 32));
-}
-// (max value, argmax, bad flag) of a greedy chunk: the high word has bit 31
-// set (so the slot is never zero), bit 30 the bad flag, bits 0-29 the argmax
-// (an empty chunk's "no index" maps to 2^30 - 1).
-__device__ __forceinline__ unsigned long long pack_am(float v, int idx, int bad) {
-  const unsigned hi = 0x80000000u | (bad ? 0x40000000u : 0u) | ((unsigned)idx & 0x3fffffffu);
-  return ((unsigned long long)hi << 32) | __float_as_uint(v);
-}
-__device__ __forceinline__ void unpack_am(unsigned long long p, float& v, int& idx, int& bad) {
-  v = __uint_as_float((unsigned)p);
-  const unsigned hi = (unsigned)(p >> 32);
-  idx = (int)(hi & 0x3fffffffu);
-  bad = (hi & 0x40000000u) ? 1 : 0;
-}
-
-// A slot read: a plain load after a kernel boundary, an agent-scope load when
-// its writer may still be running in the same grid.
-template <bool POLL>
-__device__ __forceinline__ unsigned long long slot_load(const unsigned long long* p) {
-  if constexpr (POLL) return obs_u64(p);
-  else return *p;
-}
-// Bounded wait for the slots of one batch that read zero (unpublished): every
-// missing slot is read again in each round, so one round trip covers them all.
-// Slots past the batch end hold a nonzero placeholder. Sets `to` on timeout.
-template <int G>
-__device__ __forceinline__ void slots_wait(const unsigned long long* p, unsigned long long* v,
-                                           int limit, int& to) {
-  for (int spins = 0;; ++spins) {
-    bool missing = false;
-#pragma unroll
-    for (int g = 0; g < G; ++g) missing |= v[g] == 0ull;
-    if (!missing) return;
-    if (spins >= limit) {
-      to = 1;
-      return;
-    }
-    __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-      if (v[g] == 0ull) v[g] = obs_u64(p + g);
-  }
-}
-
-// One 16-byte vector (or one element on the scalar path) of a row.
-template <int DT, bool VEC>
-struct Vec {
-  static constexpr int N = VEC ? Dt<DT>::N : 1;
-  using Raw = typename std::conditional<VEC, uint4, float>::type;
-  __device__ __forceinline__ static Raw load(const void* base, size_t row_elem, int v) {
-    if constexpr (VEC) {
-      return reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(base) +
-                                            row_elem * Dt<DT>::kBytes)[v];
-    } else {
-      return load_elem<DT>(base, row_elem + (size_t)v);
-    }
-  }
-  // The same load marked non-temporal (streamed once: not kept in the caches).
-  __device__ __forceinline__ static Raw load_stream(const void* base, size_t row_elem, int v) {
-    if constexpr (VEC) {
-      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-      const u32x4 t = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) +
-                                         row_elem * Dt<DT>::kBytes) +
-          v);
-      return make_uint4(t.x, t.y, t.z, t.w);
-    } else {
-      return load_elem<DT>(base, row_elem + (size_t)v);
-    }
-  }
-  __device__ __forceinline__ static void get(const Raw& r, float* f) {
-    if constexpr (VEC) unpack<DT>(r, f);
-    else f[0] = r;
-  }
-};
-
-#ifndef SV_STATS_NT
-#define SV_STATS_NT 1
-#endif
-#if SV_STATS_NT
-#define SV_STATS_LOAD Vc::load_stream
-#else
-#define SV_STATS_LOAD Vc::load
-#endif
 
 // Makes a register value opaque to the compiler, so values derived from it in
 // one pass are recomputed in the next instead of being kept alive.
@@ -231,35 +109,6 @@ __device__ __forceinline__ void write_marked(const Raw vec, unsigned bits, int i
 
 // Weight of one id in the final draw: residual max(0, p - q) or bonus p, where
 // an id outside a row's kept set (l < threshold) has probability 0 in that row.
-__device__ __forceinline__ float draw_weight(float lp, float lq, const Job& j, float c) {
-  const float ep = (lp >= j.thr_p) ? fast_exp2(fmaf(lp, c, -j.Rp)) : 0.0f;
-  if (j.mode == kJobBonus) return ep * j.invSp;
-  const float q = (lq >= j.thr_q) ? fast_exp2(fmaf(lq, c, -j.Rq)) * j.invSq : 0.0f;
-  return fmaxf(fmaf(ep, j.invSp, -q), 0.0f);
-}
-
-// Block reduction of 8 values per thread; out[u] valid in every thread.
-__device__ __forceinline__ void block_sum8(const float* v, float* out) {
-  __shared__ float s_red[kThreads / kWave][8];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x / kWave;
-  float t[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) t[u] = wave_sum(v[u]);
-  __syncthreads();
-  if (lane == 0) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) s_red[w][u] = t[u];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    float a = 0.f;
-#pragma unroll
-    for (int k = 0; k < kThreads / kWave; ++k) a += s_red[k][u];
-    out[u] = a;
-  }
-}
 
 // First tile whose inclusive prefix exceeds u*Z (else the last tile with mass).
 // Tile sums are read once with agent-scope loads (published by other blocks);
@@ -396,30 +245,23 @@ struct Dec {
   int first;                 // first position that stops the walk (rejection,
                              // invalid row or id, or the bonus position)
   int invalid;               // first position with an invalid row
-  int to_pos;                // first position whose wait ran out
-  int timeout;               // the decision is a timed-out wait (read by thread 0)
 };
 
 // Merge the chunk partials of one position's rows in chunk order (loads issued
-// four chunks at a time so their round trips overlap; with POLL, a partial
-// not yet published is waited for).
-template <bool POLL>
+// four chunks at a time so their round trips overlap). The partials were
+// written by an earlier kernel.
 __device__ __forceinline__ void merge_sampling(const unsigned long long* dsl,
                                                const unsigned long long* tsl, bool with_draft,
                                                int C, float c, float& mq, float& sq, float& mp,
-                                               float& sp, int limit, int& to) {
+                                               float& sp) {
   constexpr int G = 4;
   for (int k0 = 0; k0 < C; k0 += G) {
     unsigned long long dv[G], tv[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const bool in = k0 + g < C;
-      tv[g] = in ? slot_load<POLL>(tsl + k0 + g) : 1ull;
-      dv[g] = (in && with_draft) ? slot_load<POLL>(dsl + k0 + g) : 1ull;
-    }
-    if constexpr (POLL) {
-      slots_wait<G>(tsl + k0, tv, limit, to);
-      if (with_draft) slots_wait<G>(dsl + k0, dv, limit, to);
+      tv[g] = in ? tsl[k0 + g] : 1ull;
+      dv[g] = (in && with_draft) ? dsl[k0 + g] : 1ull;
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -436,15 +278,13 @@ __device__ __forceinline__ void merge_sampling(const unsigned long long* dsl,
   }
 }
 
-template <bool POLL>
 __device__ __forceinline__ void merge_greedy(const unsigned long long* tsl, int C, float& v,
-                                             int& idx, int& bad, int limit, int& to) {
+                                             int& idx, int& bad) {
   constexpr int G = 4;
   for (int k0 = 0; k0 < C; k0 += G) {
     unsigned long long tv[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) tv[g] = (k0 + g < C) ? slot_load<POLL>(tsl + k0 + g) : 1ull;
-    if constexpr (POLL) slots_wait<G>(tsl + k0, tv, limit, to);
+    for (int g = 0; g < G; ++g) tv[g] = (k0 + g < C) ? tsl[k0 + g] : 1ull;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       if (k0 + g < C) {
@@ -461,14 +301,12 @@ __device__ __forceinline__ void merge_greedy(const unsigned long long* tsl, int 
 // Decision of sequence b (whole block; thread i owns position i). Position i
 // stops the walk if a row it reads is invalid, its draft id is out of range or
 // its ratio test rejects; the bonus position always stops. n is the first
-// stopping position. In a fused grid (POLL) a thread waits for its rows until
-// they are published, or until an earlier position has stopped (its rows are
-// then never read), unless every row is wanted for the side outputs. Every
+// stopping position. The row statistics come from an earlier kernel. Every
 // block of the sequence computes the same result; only the writer block stores
 // the outputs it fixes: the accepted prefix and -1 after it, the side outputs,
 // and num_accepted when nothing is drawn. Returns the job of the final draw
 // (kJobNone when there is none).
-template <int DT, bool POLL>
+template <int DT>
 __device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool writer, Dec& S) {
   const int tid = threadIdx.x;
   const int t0 = d0 + b;
@@ -480,24 +318,10 @@ __device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool 
     S.flags = 0;
     S.first = kb + 1;
     S.invalid = INT_MAX;
-    S.to_pos = INT_MAX;
   }
   __syncthreads();
   const unsigned long long* tsl = P.slots + unit_of(P, true, t0 + min(tid, kb)) * C;
   const unsigned long long* dsl = is_draft ? P.slots + unit_of(P, false, d0 + tid) * C : tsl;
-  // In a fused grid with at most kFastChunks chunks per row, the partials are
-  // read together with the draft ids (one round trip), before the logits at
-  // the ids; only partials still unpublished are read again.
-  constexpr int kFastChunks = 4;
-  const bool fast = POLL && !P.filt && C <= kFastChunks;
-  unsigned long long tv[kFastChunks], dv[kFastChunks];
-  if (fast && active) {
-#pragma unroll
-    for (int g = 0; g < kFastChunks; ++g) {
-      tv[g] = g < C ? obs_u64(tsl + g) : 1ull;
-      dv[g] = (g < C && is_draft && !greedy) ? obs_u64(dsl + g) : 1ull;
-    }
-  }
   int x = -1;
   float u = 1.f;
   if (is_draft) {
@@ -520,123 +344,52 @@ __device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool 
   bool valid = false, acc = false;
   float ratio = __builtin_nanf("");
   if (active) {
-    bool have = true;
-    int to = 0;
-    if constexpr (POLL) {
-      // Wait for this position's partials: one read per missing partial per
-      // round, with a sleep; a position past an already-known stop needs no
-      // rows (unless every row is wanted for the side outputs). Without the
-      // fast read, the target row's last chunk (its last stats block in grid
-      // order) is awaited first and the partials are read after it.
-      const volatile int* first = &S.first;
-      for (int spins = 0;; ++spins) {
-        bool missing = false;
-        if (fast) {
-#pragma unroll
-          for (int g = 0; g < kFastChunks; ++g) missing |= (tv[g] == 0ull) | (dv[g] == 0ull);
-        } else {
-          missing = obs_u64(tsl + C - 1) == 0ull;
-        }
-        if (!missing) break;
-        if (!P.full_wait && *first < tid) {
-          have = false;
-          break;
-        }
-        if (spins >= P.spin_limit) {
-          to = 1;
-          have = false;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(8);
-        if (fast) {
-#pragma unroll
-          for (int g = 0; g < kFastChunks; ++g) {
-            if (tv[g] == 0ull) tv[g] = obs_u64(tsl + g);
-            if (dv[g] == 0ull) dv[g] = obs_u64(dsl + g);
-          }
-        }
-      }
-    }
-    if (have && fast) {
-      // merge in chunk order, as the slower path does
+    if (greedy) {
       int gbad = 0;
-#pragma unroll
-      for (int g = 0; g < kFastChunks; ++g) {
-        if (g < C) {
-          float m, s_;
-          if (greedy) {
-            int ci, cb;
-            unpack_am(tv[g], m, ci, cb);
-            argmax_merge(mp, am, m, ci);
-            gbad |= cb;
-          } else {
-            if (is_draft) {
-              unpack_ms(dv[g], m, s_);
-              merge_ms(mq, sq, m, s_, c);
-            }
-            unpack_ms(tv[g], m, s_);
-            merge_ms(mp, sp, m, s_, c);
-          }
+      merge_greedy(tsl, C, mp, am, gbad);
+      valid = !gbad && mp != kNegInf;
+    } else {
+      int rbad = 0;
+      if (P.filt) {
+        // kept-set statistics of the filter pass
+        const RowRes rt = P.rowres[P.total_draft + t0 + tid];
+        mp = rt.m;
+        sp = rt.s;
+        thp = rt.theta;
+        rbad = rt.flags;
+        if (is_draft) {
+          const RowRes rd = P.rowres[d0 + tid];
+          mq = rd.m;
+          sq = rd.s;
+          thq = rd.theta;
+          rbad |= rd.flags;
         }
-      }
-      if (greedy) {
-        valid = !gbad && mp != kNegInf;
       } else {
-        valid = __builtin_isfinite(mp) && sp > 0.f && __builtin_isfinite(sp);
-        if (is_draft) valid = valid && __builtin_isfinite(mq) && sq > 0.f && __builtin_isfinite(sq);
+        merge_sampling(dsl, tsl, is_draft, C, c, mq, sq, mp, sp);
       }
-    } else if (have) {
+      valid = !rbad && __builtin_isfinite(mp) && sp > 0.f && __builtin_isfinite(sp);
+      if (is_draft) valid = valid && __builtin_isfinite(mq) && sq > 0.f && __builtin_isfinite(sq);
+    }
+    if (is_draft && tok_ok && valid) {
       if (greedy) {
-        int gbad = 0;
-        merge_greedy<POLL>(tsl, C, mp, am, gbad, P.spin_limit, to);
-        valid = !gbad && mp != kNegInf;
+        acc = am == x;
       } else {
-        int rbad = 0;
-        if (P.filt) {
-          // kept-set statistics of the filter pass
-          const RowRes rt = P.rowres[P.total_draft + t0 + tid];
-          mp = rt.m;
-          sp = rt.s;
-          thp = rt.theta;
-          rbad = rt.flags;
-          if (is_draft) {
-            const RowRes rd = P.rowres[d0 + tid];
-            mq = rd.m;
-            sq = rd.s;
-            thq = rd.theta;
-            rbad |= rd.flags;
-          }
+        // r = p(x)/q(x) = 2^((lp*c - Rp) - (lq*c - Rq)) * Sq / Sp; an id
+        // outside a row's kept set has probability 0 there: q(x) = 0 < p(x)
+        // accepts, p(x) = 0 rejects
+        const bool pk = lp >= thp, qk = lq >= thq;
+        if (pk && qk) {
+          const float ep = fmaf(lp, c, -ref_of(mp, c));
+          const float eq = fmaf(lq, c, -ref_of(mq, c));
+          ratio = fast_exp2(ep - eq) * (sq / sp);
         } else {
-          merge_sampling<POLL>(dsl, tsl, is_draft, C, c, mq, sq, mp, sp, P.spin_limit, to);
+          ratio = pk ? kPosInf : 0.f;
         }
-        valid = !rbad && __builtin_isfinite(mp) && sp > 0.f && __builtin_isfinite(sp);
-        if (is_draft) valid = valid && __builtin_isfinite(mq) && sq > 0.f && __builtin_isfinite(sq);
+        acc = u < ratio;  // strict: u == r rejects
       }
-      if (to) have = false;
     }
-    if (have) {
-      if (is_draft && tok_ok && valid) {
-        if (greedy) {
-          acc = am == x;
-        } else {
-          // r = p(x)/q(x) = 2^((lp*c - Rp) - (lq*c - Rq)) * Sq / Sp; an id
-          // outside a row's kept set has probability 0 there: q(x) = 0 < p(x)
-          // accepts, p(x) = 0 rejects
-          const bool pk = lp >= thp, qk = lq >= thq;
-          if (pk && qk) {
-            const float ep = fmaf(lp, c, -ref_of(mp, c));
-            const float eq = fmaf(lq, c, -ref_of(mq, c));
-            ratio = fast_exp2(ep - eq) * (sq / sp);
-          } else {
-            ratio = pk ? kPosInf : 0.f;
-          }
-          acc = u < ratio;  // strict: u == r rejects
-        }
-      }
-      if (!valid) atomicMin(&S.invalid, tid);
-      if (!acc) atomicMin(&S.first, tid);  // also the bonus position and bad ids
-    }
-    if (to) atomicMin(&S.to_pos, tid);
+    if (!valid) atomicMin(&S.invalid, tid);
+    if (!acc) atomicMin(&S.first, tid);  // also the bonus position and bad ids
     S.m[0][tid] = mq;
     S.s[0][tid] = sq;
     S.m[1][tid] = mp;
@@ -647,11 +400,7 @@ __device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool 
   __syncthreads();
   const int first = S.first;
   const int n = min(first, kb);
-  // a wait that ran out matters if its position is reached (or no stop was seen)
-  const int code = (S.to_pos <= first) ? SV_SEQ_SYNC_TIMEOUT
-                   : (S.flags & 1)     ? SV_SEQ_BAD_TOKEN
-                   : (S.invalid == n)  ? SV_SEQ_BAD_ROW
-                                       : 0;
+  const int code = (S.flags & 1) ? SV_SEQ_BAD_TOKEN : (S.invalid == n) ? SV_SEQ_BAD_ROW : 0;
   const bool draws = code == 0 && !greedy;
 
   if (writer) {
@@ -700,30 +449,9 @@ __device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool 
   j.thr_p = S.th[1][n];
   j.u = u_draw;
   j.out_idx = t0 + n;
-  // a timed-out wait of this block is reported through the sequence flags
-  if (tid == 0) S.timeout = code == SV_SEQ_SYNC_TIMEOUT;
   return j;
 }
 
-// Sequence of a draft row (is_target false) or target row: the largest b with
-// cu[b] <= row, or cu[b] + b <= row. Whole block (stages cu in LDS).
-__device__ int row_seq(const Params& P, int row, bool is_target, int* s_cu) {
-  if (P.cu == nullptr) return is_target ? row / (P.K + 1) : row / P.K;
-  const bool staged = P.B <= kCuLds;
-  if (staged) {
-    for (int k = threadIdx.x; k < P.B; k += kThreads) s_cu[k] = P.cu[k];
-    __syncthreads();
-  }
-  const int* cu = staged ? s_cu : P.cu;
-  int lo = 0, hi = P.B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    const long long key = (long long)cu[mid] + (is_target ? mid : 0);
-    if (key <= (long long)row) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
-}
 
 // Candidates of one chunk of a filtered sampling row (whole block; the chunk
 // stays in registers). The candidates are the finite logits at or above a
@@ -746,7 +474,7 @@ __device__ void topk_block(const Params& P, long long g, const void* base, size_
 #pragma unroll
   for (int u = 0; u < kFiltVpt; ++u) {
     const int v = vb + u * kThreads + tid;
-    if (v < P.nvec) r[u] = SV_STATS_LOAD(base, roff, v);
+    if (v < P.nvec) r[u] = Vc::load_stream(base, roff, v);
   }
   // this thread's logits in registers, in ascending id order: fn(value, id)
   auto each = [&](auto&& fn) {
@@ -891,17 +619,10 @@ __device__ void topk_block(const Params& P, long long g, const void* base, size_
 // ---------------------------------------------------------------- stats unit
 // Stats block g covers chunk g % chunks of unit g / chunks: draft row u for
 // u < total_draft, else target row u - total_draft. Its partial goes to
-// slots[g]; with PUB it is published with an agent-scope store for readers in
-// the same grid.
-template <int DT, bool VEC, bool FILT, bool PUB>
+// slots[g] (read after the kernel boundary).
+template <int DT, bool VEC, bool FILT>
 __device__ void stats_unit(const Params& P, long long g) {
-  using Vc = Vec<DT, VEC>;
-  constexpr int N = Vc::N;
-  __shared__ float4 s_part[kThreads / kWave];
   __shared__ int s_cu[kCuLds];
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
   const int unit = (int)(g / P.chunks);
   const int ch = (int)(g - (long long)unit * P.chunks);
   bool is_target;
@@ -919,96 +640,15 @@ __device__ void stats_unit(const Params& P, long long g) {
     }
   }
   const int vb = ch * P.chunk_vecs;
-  const int ve = min(P.nvec, vb + P.chunk_vecs);
-  int v = vb + tid;
-  unsigned long long packed;
-  if (greedy) {
-    float bv = kNegInf;
-    int bi = INT_MAX, bad = 0;
-    for (; v + (kBatch - 1) * kThreads < ve; v += kBatch * kThreads) {
-      typename Vc::Raw r[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) r[u] = SV_STATS_LOAD(base, roff, v + u * kThreads);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        float f[N];
-        Vc::get(r[u], f);
-#pragma unroll
-        for (int k = 0; k < N; ++k) {
-          bad |= is_nan_or_posinf(f[k]);
-          if (f[k] > bv) {
-            bv = f[k];
-            bi = (v + u * kThreads) * N + k;
-          }
-        }
-      }
-    }
-    for (; v < ve; v += kThreads) {
-      float f[N];
-      Vc::get(SV_STATS_LOAD(base, roff, v), f);
-#pragma unroll
-      for (int k = 0; k < N; ++k) {
-        bad |= is_nan_or_posinf(f[k]);
-        if (f[k] > bv) {
-          bv = f[k];
-          bi = v * N + k;
-        }
-      }
-    }
-    wave_argmax(bv, bi, bad);
-    if (lane == 0) s_part[wave] = make_float4(bv, __int_as_float(bi), __int_as_float(bad), 0.f);
-    __syncthreads();
-    if (tid != 0) return;
-#pragma unroll
-    for (int w = 1; w < kThreads / kWave; ++w) {
-      argmax_merge(bv, bi, s_part[w].x, __float_as_int(s_part[w].y));
-      bad |= __float_as_int(s_part[w].z);
-    }
-    packed = pack_am(bv, bi, bad);
-  } else {
-    const float c = P.c;
-    float m = kNegInf, s = 0.f;
-    for (; v + (kBatch - 1) * kThreads < ve; v += kBatch * kThreads) {
-      typename Vc::Raw r[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) r[u] = SV_STATS_LOAD(base, roff, v + u * kThreads);
-      __builtin_amdgcn_sched_barrier(0);
-      float f[kBatch * N];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) Vc::get(r[u], f + u * N);
-      online_update<kBatch * N>(m, s, f, c);
-    }
-    for (; v < ve; v += kThreads) {
-      float f[N];
-      Vc::get(SV_STATS_LOAD(base, roff, v), f);
-      online_update<N>(m, s, f, c);
-    }
-    wave_reduce_ms(m, s, c);
-    if (lane == 0) s_part[wave] = make_float4(m, s, 0.f, 0.f);
-    __syncthreads();
-    if (tid != 0) return;
-    // the block's maximum, then every wave's sum at its reference
-    float M = s_part[0].x;
-#pragma unroll
-    for (int w = 1; w < kThreads / kWave; ++w) M = fmaxf(M, s_part[w].x);
-    const float RM = ref_of(M, c);
-    float S = 0.f;
-#pragma unroll
-    for (int w = 0; w < kThreads / kWave; ++w) {
-      const float sw = s_part[w].y;
-      S += (sw == 0.f) ? 0.f : sw * rescale(ref_of(s_part[w].x, c), RM);
-    }
-    packed = pack_ms(M, S);
-  }
-  if constexpr (PUB) pub_u64(P.slots + g, packed);
-  else P.slots[g] = packed;
+  const unsigned long long packed =
+      chunk_stats<DT, VEC>(P, base, roff, vb, min(P.nvec, vb + P.chunk_vecs), greedy);
+  if (threadIdx.x == 0) P.slots[g] = packed;
 }
 
-// The statistics pass as a kernel of its own (filtered calls).
+// The statistics pass (filtered calls, and rows too long for k_verify).
 template <int DT, bool VEC, bool FILT>
 __global__ __launch_bounds__(kThreads) void k_stats(const Params P) {
-  stats_unit<DT, VEC, FILT, false>(P, (long long)blockIdx.x + P.stats_block0);
+  stats_unit<DT, VEC, FILT>(P, (long long)blockIdx.x + P.stats_block0);
 }
 
 // ----------------------------------------------------------------- k_filter
@@ -1227,40 +867,14 @@ __global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
 }
 
 // Returns the partials of a sequence's rows to zero (whole block): its target
-// rows and, with_draft, its draft rows. In a fused grid (POLL) a row the
-// decision never read may still be in flight: its partial is awaited first.
-// Returns nonzero (in every thread) if such a wait ran out.
-template <bool POLL>
-__device__ int clear_partials(const Params& P, int d0, int kb, int b, bool with_draft) {
+// rows and, with_draft, its draft rows.
+__device__ void clear_partials(const Params& P, int d0, int kb, int b, bool with_draft) {
   const int C = P.chunks;
   const int nd = with_draft ? kb : 0;
-  int to = 0;
   for (int k = threadIdx.x; k < (nd + kb + 1) * C; k += kThreads) {
     const int r = k / C, ch = k - r * C;
     const bool tgt = r >= nd;
-    unsigned long long* p =
-        P.slots + unit_of(P, tgt, tgt ? d0 + b + (r - nd) : d0 + r) * C + ch;
-    if constexpr (POLL) {
-      for (int spins = 0; obs_u64(p) == 0ull; ++spins) {
-        if (spins >= P.spin_limit) {
-          to = 1;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(4);
-      }
-    }
-    pub_u64(p, 0ull);
-  }
-  return block_sum_i(to);
-}
-
-// Marks sequence b as timed out (whole block): tokens -1, code in num_accepted
-// (agent-scope stores, ordered after the writer block's outputs).
-__device__ __forceinline__ void write_timeout(const Params& P, int d0, int kb, int b) {
-  for (int k = threadIdx.x; k <= kb; k += kThreads) pub_i(P.out_tokens + d0 + b + k, -1);
-  if (threadIdx.x == 0) {
-    pub_i(P.num_accepted + b, SV_SEQ_SYNC_TIMEOUT);
-    if (P.diag.resid_Z) pub_f(P.diag.resid_Z + b, __builtin_nanf(""));
+    pub_u64(P.slots + unit_of(P, tgt, tgt ? d0 + b + (r - nd) : d0 + r) * C + ch, 0ull);
   }
 }
 
@@ -1393,18 +1007,17 @@ __device__ int explicit_draw(const Params& P, const Job& j, float& Zout) {
 }
 
 // ----------------------------------------------------------------- draw unit
-// Draw block (b, ch), ch < dchunks: decision of sequence b, then the tile sums
-// of slice ch of row pair n. Every block of a sampling sequence counts itself
-// on the sequence's counter; the last one draws the token (or reports a wait
-// that timed out) and returns the sequence's workspace entries to zero. A
-// greedy sequence is decided by block 0 alone. With POLL the row partials may
-// still be in flight (fused grid) and are waited for.
-template <int DT, bool VEC, bool POLL>
+// Draw block (b, ch), ch < dchunks, of the decision-and-draw kernel: decision
+// of sequence b, then the tile sums of slice ch of row pair n. Every block of
+// a sampling sequence counts itself on the sequence's counter; the last one
+// draws the token and returns the sequence's workspace entries to zero. A
+// greedy sequence is decided by block 0 alone.
+template <int DT, bool VEC>
 __device__ void draw_unit(const Params& P, int idx) {
   using Vc = Vec<DT, VEC>;
   constexpr int N = Vc::N;
   __shared__ Dec S;
-  __shared__ int s_last, s_to;
+  __shared__ int s_last;
   const int tid = threadIdx.x;
   const int b = idx / P.dchunks;
   const int ch = idx - b * P.dchunks;
@@ -1415,28 +1028,25 @@ __device__ void draw_unit(const Params& P, int idx) {
   }
   const bool greedy = seq_greedy(P, b);
   if (greedy && ch != 0) return;  // one block decides a greedy sequence
-  const Job j = decide<DT, POLL>(P, b, d0, kb, greedy, ch == 0, S);
-  const int C = P.chunks;
+  const Job j = decide<DT>(P, b, d0, kb, greedy, ch == 0, S);
   if (greedy) {
     // the only reader of these partials returns them to zero
     __syncthreads();
-    if (clear_partials<POLL>(P, d0, kb, b, false)) write_timeout(P, d0, kb, b);
+    clear_partials(P, d0, kb, b, false);
     return;
   }
-  if constexpr (!POLL) {
-    // filtered: draw from the candidate records when they list the kept set
-    if (P.filt && j.mode != kJobNone && explicit_usable(P, j)) {
-      if (ch == 0) {
-        float Z;
-        const int tok = explicit_draw<DT>(P, j, Z);
-        if (tid == 0) {
-          pub_i(P.out_tokens + j.out_idx, tok);
-          pub_i(P.num_accepted + b, j.n);
-          if (P.diag.resid_Z) pub_f(P.diag.resid_Z + b, Z);
-        }
+  // filtered: draw from the candidate records when they list the kept set
+  if (P.filt && j.mode != kJobNone && explicit_usable(P, j)) {
+    if (ch == 0) {
+      float Z;
+      const int tok = explicit_draw<DT>(P, j, Z);
+      if (tid == 0) {
+        pub_i(P.out_tokens + j.out_idx, tok);
+        pub_i(P.num_accepted + b, j.n);
+        if (P.diag.resid_Z) pub_f(P.diag.resid_Z + b, Z);
       }
-      return;
     }
+    return;
   }
   if (j.mode != kJobNone) {
     // tile sums of slice ch of row pair n: the thread's vector k*kThreads + tid
@@ -1478,21 +1088,14 @@ __device__ void draw_unit(const Params& P, int idx) {
     }
   }
   // every block of the sequence counts itself, after its stores have landed
-  if (tid == 0 && S.timeout) raise_flag(P.seq_flags + b, kSeqFlagTimeout);
   drain_stores();
   __syncthreads();
-  if (tid == 0) {
-    s_last = (bump(P.draw_done + b) == P.dchunks - 1) ? 1 : 0;
-    compiler_fence();
-    s_to = s_last ? (obs_i(P.seq_flags + b) & kSeqFlagTimeout) : 0;
-  }
+  if (tid == 0) s_last = (bump(P.draw_done + b) == P.dchunks - 1) ? 1 : 0;
   __syncthreads();
   if (!s_last) return;
   // Last block of the sequence: every other block has read the partials and
   // published its tile sums.
-  if (s_to) {
-    write_timeout(P, d0, kb, b);
-  } else if (j.mode != kJobNone) {
+  if (j.mode != kJobNone) {
     float Z;
     const int tok = pick<DT, VEC>(P, b, j, Z);
     if (tid == 0) {
@@ -1503,34 +1106,15 @@ __device__ void draw_unit(const Params& P, int idx) {
   }
   __syncthreads();
   // return the sequence's workspace entries to zero
-  if (!P.filt && clear_partials<POLL>(P, d0, kb, b, true)) write_timeout(P, d0, kb, b);
+  if (!P.filt) clear_partials(P, d0, kb, b, true);
   for (int t = tid; t < P.ntiles; t += kThreads) pub_f(P.tiles + (size_t)b * P.ntiles + t, 0.f);
-  if (tid == 0) {
-    pub_i(P.draw_done + b, 0);
-    pub_i(P.seq_flags + b, 0);
-  }
+  if (tid == 0) pub_i(P.draw_done + b, 0);
 }
 
-// The decision-and-draw pass as a kernel of its own (filtered calls).
+// The decision-and-draw pass (filtered calls, and rows too long for k_verify).
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_draw(const Params P) {
-  draw_unit<DT, VEC, false>(P, blockIdx.x);
-}
-
-// ------------------------------------------------------------------ k_verify
-// The unfiltered step in one grid: every stats block first, then the draw
-// blocks in sequence order. Blocks start in index order on each of the chip's
-// dies, so every stats block has started before any draw block can wait for
-// it, and stats blocks never wait: the waits always end. Draw blocks take the
-// slots the statistics tail frees, so the draws of the early sequences overlap
-// the last statistics blocks.
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8)))
-void k_verify(const Params P) {
-  if ((long long)blockIdx.x < P.stats_blocks)
-    stats_unit<DT, VEC, false, true>(P, (long long)blockIdx.x + P.stats_block0);
-  else
-    draw_unit<DT, VEC, true>(P, (int)((long long)blockIdx.x - P.stats_blocks));
+  draw_unit<DT, VEC>(P, blockIdx.x);
 }
 
 __global__ void k_fill_zero(uint4* p, size_t n16) {
@@ -1544,6 +1128,9 @@ static hipError_t stage_event(hipEvent_t* ev, int nev, int i, hipStream_t s) {
   return (ev != nullptr && i < nev) ? hipEventRecord(ev[i], s) : hipSuccess;
 }
 
+// Statistics, then (with top-k) the filter pass, then decision and draw. Stage
+// events: before the first kernel, after each kernel of a filtered call (an
+// unfiltered call here is one stage), and every further one after the last.
 template <int DT, bool VEC>
 static hipError_t launch_t(const Params& P, const Plan& L, hipStream_t s, hipEvent_t* ev, int nev) {
   hipError_t err;
@@ -1557,11 +1144,12 @@ static hipError_t launch_t(const Params& P, const Plan& L, hipStream_t s, hipEve
     hipLaunchKernelGGL(k_filter, dim3((unsigned)L.filter_blocks), dim3(kThreads), 0, s, P);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if ((err = stage_event(ev, nev, e++, s)) != hipSuccess) return err;
-    hipLaunchKernelGGL((k_draw<DT, VEC>), dim3((unsigned)L.draw_blocks), dim3(kThreads), 0, s, P);
   } else {
-    hipLaunchKernelGGL((k_verify<DT, VEC>), dim3((unsigned)(L.stats_blocks + L.draw_blocks)),
-                       dim3(kThreads), 0, s, P);
+    hipLaunchKernelGGL((k_stats<DT, VEC, false>), dim3((unsigned)L.stats_blocks), dim3(kThreads),
+                       0, s, P);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
   }
+  hipLaunchKernelGGL((k_draw<DT, VEC>), dim3((unsigned)L.draw_blocks), dim3(kThreads), 0, s, P);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   // this and any further events: after the last kernel
   for (; e < nev; ++e)
