@@ -47,7 +47,6 @@ int kcap_for(int top_k) { return (top_k + 256 + 63) / 64 * 64; }
 //   tiles[B * dmax * tiles per draw block] draw-weight tile sums (separate kernels)
 //   draws[B * 2 * dmax]                    slice weight sums of the final draw
 //                                          (one-kernel step)
-//   decs[B * kDecRecordWords]              decision records (one-kernel step)
 // and with top-k active:
 //   rec[(total_draft + rows) * cmax * rec_words]  chunk records of sampling rows
 //   rowres[total_draft + rows]                    kept-set statistics per row
@@ -82,8 +81,6 @@ bool make_plan(int B, int total_draft, int V, int top_k, size_t ws_bytes, sv::Pl
   off += align_up((size_t)B * (size_t)dmax * sv::kTilesPerDraw * 4);
   L.off_draws = off;
   off += align_up((size_t)B * 2 * (size_t)dmax * 8);
-  L.off_decs = off;
-  off += align_up((size_t)B * sv::kDecRecordWords * 8);
   L.off_rec = L.off_rowres = off;
   if (filt) {
     const size_t rec_words = sv::kRecHeader + 2 * (size_t)kcap_for(top_k);
@@ -170,7 +167,6 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
   P.slots = reinterpret_cast<unsigned long long*>(ws + L.off_slots);
   P.tiles = reinterpret_cast<float*>(ws + L.off_tiles);
   P.draws = reinterpret_cast<unsigned long long*>(ws + L.off_draws);
-  P.decs = reinterpret_cast<unsigned long long*>(ws + L.off_decs);
   P.draw_done = reinterpret_cast<int*>(ws + L.off_draw_done);
   P.seq_flags = reinterpret_cast<int*>(ws + L.off_seq_flags);
   P.spin_limit = (diag != nullptr && diag->spin_limit > 0) ? diag->spin_limit : kDefaultSpinLimit;
@@ -188,17 +184,19 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
   P.stats_blocks = L.stats_blocks;
   if ((long long)B + L.stats_blocks + L.draw_blocks > (long long)UINT32_MAX / sv::kThreads)
     return SV_EUNSUPPORTED;
-  // The one-kernel step places its B decision blocks ahead of the statistics
-  // they wait for when they fill at most a fraction of the chip (two per
-  // compute unit), so the statistics always have room to run; otherwise they
-  // follow the statistics blocks.
-  P.decide_first = 0;
-  if (L.fused) {
+  // Placement of the one-kernel step's draw blocks (see sv_fused.hip): ahead
+  // of the last two positions' statistics of a dense batch when the chip holds
+  // all of them at once with at least one block per compute unit to spare,
+  // after all the statistics otherwise.
+  P.draw_at = L.stats_blocks;
+  if (L.fused && cu == nullptr && K >= 2) {
     int dev = 0, cus = 0;
     if (hipStreamGetDevice(stream, &dev) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        B <= 2 * cus)
-      P.decide_first = 1;
+        cus > 0 && L.draw_blocks <= sv::fused_capacity(dtype, vec, cus) - cus) {
+      const long long per_pos = (all_greedy ? 1LL : 2LL) * B * P.chunks;
+      P.draw_at = (long long)(K - 1) * per_pos;
+    }
   }
   hipEvent_t* ev = nullptr;
   int nev = 0;

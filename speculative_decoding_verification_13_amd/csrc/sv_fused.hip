@@ -1,9 +1,13 @@
 // The unfiltered verification step as one HIP kernel for gfx950.
 //
-// The grid holds every statistics block first, then D draw blocks per sequence
-// in sequence order. A dense batch streams its rows position-major (every
-// sequence's position 0, then position 1, ...), so a sequence that stops early
-// is decided and drawn while the rows of later positions still stream.
+// Grid: the statistics blocks and D draw blocks per sequence. A dense batch
+// streams its rows position-major (every sequence's position 0, then position
+// 1, ...), so a sequence that stops early is decided while the rows of later
+// positions still stream. When the chip can hold every draw block at once with
+// room to spare, the draw blocks sit before the statistics of the last two
+// positions, whose rows only sequences that accept nearly every draft need:
+// the draws then overlap the end of the stream. Otherwise they follow all the
+// statistics.
 //
 // A statistics block streams one chunk of one logit row and publishes one
 // 64-bit partial: for a sampling row the chunk maximum m and the sum of
@@ -14,18 +18,21 @@
 // sequence b. Thread j merges the partials of position j in chunk order as they
 // are published and decides the position: r_j = p_j(x_j)/q_j(x_j), accept iff
 // u_j < r_j. The first stop n (a rejection, an invalid row or id, or the bonus
-// position) ends the walk; every block of the sequence reaches the same n with
-// the same arithmetic, so no decision is broadcast. For the final draw each
-// block loads its slice of row pair n into registers, forms the weights
-// max(0, p_n - q_n) (or p_n for the bonus), and publishes the slice's weight
-// sum. Each block gathers all slice sums: the block whose slice holds u*Z
-// scans its own registers for the token, in ascending id order.
+// position) ends the walk; every draw block of the sequence reaches the same n
+// with the same arithmetic, so no decision is broadcast, and block 0 writes the
+// accepted prefix. For the final draw each block loads its slice of row pair n
+// into registers, forms the weights max(0, p_n - q_n) (or p_n for the bonus),
+// and publishes the slice's weight sum; each block gathers all slice sums, and
+// the block whose slice holds u*Z scans its own registers for the token, in
+// ascending id order.
 //
 // Deadlock freedom: blocks start in index order on each of the chip's dies and
-// statistics blocks never wait, so every statistics block has started before
-// any draw block waits for it; a draw block waits for the other draw blocks of
-// its sequence only after its own slice is published, and they are consecutive
-// in the grid. Every wait is bounded anyway (SV_SEQ_SYNC_TIMEOUT).
+// statistics blocks never wait. Draw blocks placed ahead of statistics they may
+// wait for number fewer than the chip holds at once, less one block per compute
+// unit, so those statistics always find room; a draw block waits for the other
+// draw blocks of its sequence only after its own slice is published, and they
+// are consecutive in the grid. Every wait is bounded anyway
+// (SV_SEQ_SYNC_TIMEOUT).
 //
 // Pages (by title, section): aivaro.ru answer 289 "Как работает speculative
 // decoding на уровне логитов, а не токенов?" s.5 steps 3-4, s.6, s.9 (softmax
@@ -44,11 +51,6 @@ namespace {
 
 constexpr int kPollGroup = 4;   // chunk partials a deciding thread reads per round
 constexpr int kPollSleep = 8;   // s_sleep units (64 clocks each) between rounds
-// Decision record of a sampling sequence: five 64-bit words, each tagged in
-// bit 63 so that a reader sees every word published: (mode << 16 | n, u),
-// then R and 1/S of the draft and the target row at position n.
-constexpr int kDecWords = kDecRecordWords;
-constexpr unsigned kDecTag = 0x80000000u;
 
 // Block-shared state of a draw block.
 struct DrawShared {
@@ -236,11 +238,7 @@ __device__ int slice_draw(const Params& P, Job j, int b, int s, float& Z, int& t
     const int tl = block_last_lane(acc > 0.f);
     if (tid == (tl < 0 ? 0 : tl)) {
       int e = N - 1;
-      float prev = N > 1 ? w[N - 2] : 0.f;
-      while (e > 0 && !(w[e] > prev)) {
-        --e;
-        prev = e > 0 ? w[e - 1] : 0.f;
-      }
+      while (e > 0 && !(w[e] > w[e - 1])) --e;
       s_tok = tl < 0 ? (s * kDrawVecs + ks * kThreads) * N : v * N + e;
     }
   }
@@ -273,14 +271,15 @@ __device__ int clear_partials(const Params& P, int d0, int kb, int b, bool with_
   return __syncthreads_or(to);
 }
 
-// Last block of sequence b to finish (whole block): counts this block on the
-// sequence's counter once its stores have landed (`total` blocks take part).
-// The last one reports a timed-out wait and returns the sequence's decision
-// record, slice sums, counter and flags to zero.
-__device__ void finish_sequence(const Params& P, int b, int t0, int kb, int total, int seq_to,
-                                DrawShared& S) {
+// Counts this block on sequence b's counter once its stores have landed
+// (whole block; `total` blocks take part). The last one returns the sequence's
+// partials (awaiting rows still in flight), slice sums, counter and flags to
+// zero, and reports a timed-out wait.
+__device__ void finish_sequence(const Params& P, int b, int d0, int kb, bool greedy, int total,
+                                int seq_to, DrawShared& S) {
   const int tid = threadIdx.x;
   const int D = P.dchunks;
+  const int t0 = d0 + b;
   if (tid == 0 && seq_to) raise_flag(P.seq_flags + b, kSeqFlagTimeout);
   drain_stores();
   __syncthreads();
@@ -291,14 +290,14 @@ __device__ void finish_sequence(const Params& P, int b, int t0, int kb, int tota
   }
   __syncthreads();
   if (!S.last) return;
-  if (S.flags & kSeqFlagTimeout) {
+  const int cto = clear_partials(P, d0, kb, b, !greedy);
+  if ((S.flags & kSeqFlagTimeout) || cto) {
     for (int k = tid; k <= kb; k += kThreads) pub_i(P.out_tokens + t0 + k, -1);
     if (tid == 0) {
       pub_i(P.num_accepted + b, SV_SEQ_SYNC_TIMEOUT);
       if (P.diag.resid_Z) pub_f(P.diag.resid_Z + b, __builtin_nanf(""));
     }
   }
-  for (int k = tid; k < kDecWords; k += kThreads) pub_u64(P.decs + (size_t)b * kDecWords + k, 0ull);
   for (int k = tid; k < 2 * D; k += kThreads) pub_u64(P.draws + (size_t)b * 2 * D + k, 0ull);
   if (tid == 0) {
     pub_i(P.seq_flags + b, 0);
@@ -306,19 +305,24 @@ __device__ void finish_sequence(const Params& P, int b, int t0, int kb, int tota
   }
 }
 
-// Decision block of sequence b (see the file comment).
+// Draw block s of sequence b (see the file comment). A greedy sequence is
+// decided by its block 0 alone.
 template <int DT, bool VEC>
-__device__ void decide_block(const Params& P, int b) {
+__device__ void draw_block(const Params& P, int idx) {
   __shared__ DrawShared S;
   const int tid = threadIdx.x;
   const int C = P.chunks;
+  const int D = P.dchunks;
   const float c = P.c;
+  const int b = idx / D;
+  const int s = idx - b * D;
   int d0, kb;
   if (!seq_bounds(P, b, d0, kb)) {
-    if (tid == 0) P.num_accepted[b] = SV_SEQ_BAD_OFFSETS;
+    if (s == 0 && tid == 0) P.num_accepted[b] = SV_SEQ_BAD_OFFSETS;
     return;
   }
   const bool greedy = seq_greedy(P, b);
+  if (greedy && s != 0) return;
   const int t0 = d0 + b;
 
   // decision inputs (the logits at the draft ids are loaded before any wait)
@@ -445,101 +449,54 @@ __device__ void decide_block(const Params& P, int b) {
                                                               : 0;
   const bool draws = code == 0 && !greedy;
 
-  // The outputs the decision fixes: the accepted prefix, -1 after n, slot n
-  // when nothing is drawn, and the side outputs. Outputs a later timeout report
-  // may overwrite are written with agent-scope stores, so they land before this
-  // block counts itself.
-  if (tid <= kb && !(draws && tid == n)) {
-    int tok = -1;
-    if (code == 0) {
-      if (tid < n) tok = x;
-      else if (tid == n) tok = S.am[n];
-    }
-    pub_i(P.out_tokens + t0 + tid, tok);
-  }
-  if (tid == 0 && !draws) {
-    pub_i(P.num_accepted + b, code ? code : n);
-    if (P.diag.resid_Z) pub_f(P.diag.resid_Z + b, __builtin_nanf(""));
-  }
-  if (tid <= kb) {
-    const float kLn2 = 0.69314718055994531f;
-    const float nan = __builtin_nanf("");
-    if (P.diag.row_max_target) P.diag.row_max_target[t0 + tid] = mp;
-    if (P.diag.row_logsum_target)
-      P.diag.row_logsum_target[t0 + tid] =
-          greedy ? nan : (__log2f(sp) + fmaf(-mp, c, ref_of(mp, c))) * kLn2;
-    if (tid < kb) {
-      if (P.diag.row_max_draft) P.diag.row_max_draft[d0 + tid] = greedy ? nan : mq;
-      if (P.diag.row_logsum_draft)
-        P.diag.row_logsum_draft[d0 + tid] =
-            greedy ? nan : (__log2f(sq) + fmaf(-mq, c, ref_of(mq, c))) * kLn2;
-      if (P.diag.ratio) P.diag.ratio[d0 + tid] = ratio;
-    }
-  }
-  // the decision record for the draw blocks (sampling sequences)
-  if (!greedy && tid < kDecWords) {
-    const int mode = draws ? (n < kb ? kJobResidual : kJobBonus) : kJobNone;
-    float f = u_draw;
-    if (tid == 1) f = ref_of(S.mq[n], c);
-    if (tid == 2) f = 1.0f / S.sq[n];
-    if (tid == 3) f = ref_of(S.mp[n], c);
-    if (tid == 4) f = 1.0f / S.sp[n];
-    const unsigned hi = kDecTag | (tid == 0 ? ((unsigned)mode << 16) | (unsigned)n : 0u);
-    pub_u64(P.decs + (size_t)b * kDecWords + tid,
-            ((unsigned long long)hi << 32) | (unsigned long long)__float_as_uint(f));
-  }
-  // Every partial of the sequence is read now: return them to zero (rows the
-  // walk never reached may still be in flight and are awaited first).
-  const int cto = clear_partials(P, d0, kb, b, !greedy);
-  finish_sequence(P, b, t0, kb, greedy ? 1 : P.dchunks + 1,
-                  (code == SV_SEQ_SYNC_TIMEOUT || cto) ? 1 : 0, S);
-}
+  int seq_to = code == SV_SEQ_SYNC_TIMEOUT ? 1 : 0;
 
-// Draw block s of sequence b: waits for the decision record, then takes slice s
-// of the final draw (see the file comment).
-template <int DT, bool VEC>
-__device__ void draw_block(const Params& P, int idx) {
-  __shared__ DrawShared S;
-  __shared__ unsigned long long s_rec[kDecWords];
-  const int tid = threadIdx.x;
-  const int D = P.dchunks;
-  const int b = idx / D;
-  const int s = idx - b * D;
-  int d0, kb;
-  if (!seq_bounds(P, b, d0, kb)) return;  // reported by the decision block
-  if (seq_greedy(P, b)) return;           // decided without a draw
-  const int t0 = d0 + b;
-  int to = 0;
-  if (tid < kDecWords) {
-    const unsigned long long* p = P.decs + (size_t)b * kDecWords + tid;
-    unsigned long long v = obs_u64(p);
-    for (int spins = 0; v == 0ull; ++spins) {
-      if (spins >= P.spin_limit) {
-        to = 1;
-        break;
+  if (s == 0) {
+    // The writer block: the accepted prefix, -1 after n, slot n when nothing
+    // is drawn, and the side outputs. Outputs a later timeout report may
+    // overwrite are written with agent-scope stores, so they land before this
+    // block counts itself.
+    if (tid <= kb && !(draws && tid == n)) {
+      int tok = -1;
+      if (code == 0) {
+        if (tid < n) tok = x;
+        else if (tid == n) tok = S.am[n];
       }
-      __builtin_amdgcn_s_sleep(kPollSleep);
-      v = obs_u64(p);
+      pub_i(P.out_tokens + t0 + tid, tok);
     }
-    s_rec[tid] = v;
+    if (tid == 0 && !draws) {
+      pub_i(P.num_accepted + b, code ? code : n);
+      if (P.diag.resid_Z) pub_f(P.diag.resid_Z + b, __builtin_nanf(""));
+    }
+    if (tid <= kb) {
+      const float kLn2 = 0.69314718055994531f;
+      const float nan = __builtin_nanf("");
+      if (P.diag.row_max_target) P.diag.row_max_target[t0 + tid] = mp;
+      if (P.diag.row_logsum_target)
+        P.diag.row_logsum_target[t0 + tid] =
+            greedy ? nan : (__log2f(sp) + fmaf(-mp, c, ref_of(mp, c))) * kLn2;
+      if (tid < kb) {
+        if (P.diag.row_max_draft) P.diag.row_max_draft[d0 + tid] = greedy ? nan : mq;
+        if (P.diag.row_logsum_draft)
+          P.diag.row_logsum_draft[d0 + tid] =
+              greedy ? nan : (__log2f(sq) + fmaf(-mq, c, ref_of(mq, c))) * kLn2;
+        if (P.diag.ratio) P.diag.ratio[d0 + tid] = ratio;
+      }
+    }
   }
-  int seq_to = __syncthreads_or(to);
-  const unsigned hi0 = (unsigned)(s_rec[0] >> 32);
-  const int mode = seq_to ? kJobNone : (int)((hi0 >> 16) & 3u);
-  if (mode != kJobNone) {
-    const int n = (int)(hi0 & 0xffffu);
+  if (draws) {
     Job j;
-    j.mode = mode;
+    j.mode = n < kb ? kJobResidual : kJobBonus;
     j.n = n;
     j.prow = t0 + n;
     j.qrow = d0 + n;
-    j.u = __uint_as_float((unsigned)s_rec[0]);
-    j.Rq = __uint_as_float((unsigned)s_rec[1]);
-    j.invSq = __uint_as_float((unsigned)s_rec[2]);
-    j.Rp = __uint_as_float((unsigned)s_rec[3]);
-    j.invSp = __uint_as_float((unsigned)s_rec[4]);
+    j.Rq = ref_of(S.mq[n], c);
+    j.invSq = 1.0f / S.sq[n];
+    j.Rp = ref_of(S.mp[n], c);
+    j.invSp = 1.0f / S.sp[n];
     j.thr_q = kNegInf;
     j.thr_p = kNegInf;
+    j.u = u_draw;
     j.out_idx = t0 + n;
     float Z = 0.f;
     int dto = 0;
@@ -551,7 +508,7 @@ __device__ void draw_block(const Params& P, int idx) {
       if (P.diag.resid_Z) pub_f(P.diag.resid_Z + b, Z);
     }
   }
-  finish_sequence(P, b, t0, kb, D + 1, seq_to, S);
+  finish_sequence(P, b, d0, kb, greedy, greedy ? 1 : D, seq_to, S);
 }
 
 // Row and chunk of statistics block g. Dense batches stream position-major:
@@ -606,31 +563,48 @@ __device__ void stats_block(const Params& P, long long g) {
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_verify(const Params P) {
+  // Grid order: statistics blocks up to draw_at, the draw blocks, the remaining
+  // statistics blocks (one call site per block kind, so both inline).
   long long g = blockIdx.x;
-  const long long nb = P.B;
-  if (P.decide_first) {
-    if (g < nb) return decide_block<DT, VEC>(P, (int)g);
-    g -= nb;
-    if (g < P.stats_blocks) return stats_block<DT, VEC>(P, g);
-    g -= P.stats_blocks;
-  } else {
-    if (g < P.stats_blocks) return stats_block<DT, VEC>(P, g);
-    g -= P.stats_blocks;
-    if (g < nb) return decide_block<DT, VEC>(P, (int)g);
-    g -= nb;
+  const long long nd = (long long)P.B * P.dchunks;
+  bool stats = true;
+  if (g >= P.draw_at) {
+    if (g < P.draw_at + nd) {
+      stats = false;
+      g -= P.draw_at;
+    } else {
+      g -= nd;
+    }
   }
-  draw_block<DT, VEC>(P, (int)g);
+  if (stats) stats_block<DT, VEC>(P, g);
+  else draw_block<DT, VEC>(P, (int)g);
 }
 
 template <int DT, bool VEC>
 hipError_t launch_t(const Params& P, const Plan& L, hipStream_t s) {
-  hipLaunchKernelGGL((k_verify<DT, VEC>),
-                     dim3((unsigned)(P.B + L.stats_blocks + L.draw_blocks)), dim3(kThreads), 0, s,
-                     P);
+  hipLaunchKernelGGL((k_verify<DT, VEC>), dim3((unsigned)(L.stats_blocks + L.draw_blocks)),
+                     dim3(kThreads), 0, s, P);
   return hipGetLastError();
 }
 
+template <int DT, bool VEC>
+long long capacity_t(int cus) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_verify<DT, VEC>, kThreads, 0) !=
+      hipSuccess)
+    return 0;
+  return (long long)per_cu * cus;
+}
+
 }  // namespace
+
+long long fused_capacity(int dtype, bool vec, int cus) {
+  switch (dtype) {
+    case SV_F32: return vec ? capacity_t<SV_F32, true>(cus) : capacity_t<SV_F32, false>(cus);
+    case SV_F16: return vec ? capacity_t<SV_F16, true>(cus) : capacity_t<SV_F16, false>(cus);
+    default: return vec ? capacity_t<SV_BF16, true>(cus) : capacity_t<SV_BF16, false>(cus);
+  }
+}
 
 hipError_t launch_fused(int dtype, bool vec, const Params& P, const Plan& L, hipStream_t s) {
   switch (dtype) {

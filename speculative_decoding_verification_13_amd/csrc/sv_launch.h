@@ -33,7 +33,6 @@ constexpr int kFilterLdsChunks = 64;      // record headers a filter block stage
 constexpr int kExplicitMax = 2048;        // candidates a filtered draw gathers in LDS
 constexpr int kMaxDrawSlices = kThreads;  // draw blocks per sequence of the one-kernel
                                           // step (longer rows take the separate kernels)
-constexpr int kDecRecordWords = 5;        // 64-bit words of a decision record
 
 // Chunk record of a filtered row: header then `kcap` (value bits, id) pairs.
 //   [0] entries written   [1] value of an implicit tie class   [2] its count
@@ -115,10 +114,7 @@ struct Params {
   // (tag bit 63, float bits below), two sets of `dchunks` per sequence (the
   // residual, then the target row if the residual mass rounds to zero).
   unsigned long long* draws;  // [B * 2 * dchunks]
-  // One-kernel step: decision record of each sampling sequence, published by
-  // its decision block for its draw blocks (zero: not yet published).
-  unsigned long long* decs;   // [B * kDecRecordWords]
-  int decide_first;        // decision blocks ahead of the statistics blocks
+  long long draw_at;       // one-kernel step: statistics blocks ahead of the draw blocks
   DiagPtrs diag;
 };
 
@@ -127,15 +123,17 @@ struct Plan {
   int chunks, chunk_vecs, dchunks;
   bool fused;  // one kernel (k_verify) instead of statistics, filter and draw kernels
   long long stats_blocks, filter_blocks, draw_blocks;
-  size_t off_slots, off_tiles, off_draws, off_decs, off_draw_done, off_seq_flags, off_rec, off_rowres,
+  size_t off_slots, off_tiles, off_draws, off_draw_done, off_seq_flags, off_rec, off_rowres,
       total_bytes;
 };
 
 // The separate statistics / filter / draw kernels (sv_verify.hip).
 hipError_t launch(int dtype, bool vec, const Params& P, const Plan& L, hipStream_t s,
                   hipEvent_t* ev, int nev);
-// The one-kernel unfiltered step (sv_fused.hip).
+// The one-kernel unfiltered step (sv_fused.hip), and the number of its blocks
+// the chip holds at once with `cus` compute units (0 if unknown).
 hipError_t launch_fused(int dtype, bool vec, const Params& P, const Plan& L, hipStream_t s);
+long long fused_capacity(int dtype, bool vec, int cus);
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t s);
 
 }  // namespace sv
