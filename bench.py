@@ -97,6 +97,10 @@ def parse():
                     help="budget of the CPU oracle sample (0 disables)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--traffic-from", metavar="DIR", default=None,
+                    help="only summarise rocprofv3 counter runs: DIR/{fetch,write,cal_fetch,"
+                         "cal_write} hold FETCH_SIZE / WRITE_SIZE runs of this bench command and "
+                         "of --calibrate-copy; writes the traffic file bench.py reads")
     return ap.parse_args()
 
 
@@ -113,8 +117,75 @@ def calibrate_copy():
           flush=True)
 
 
+def _counter_per_dispatch(run_dir, counter):
+    """(kernel name, summed counter value) per dispatch of one rocprofv3 --pmc run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"bench.py: no counter_collection.csv under {run_dir}")
+    per = {}
+    for fn in files:
+        with open(fn, newline="") as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (fn, int(r["Dispatch_Id"]))
+                name, v = per.get(key, (r["Kernel_Name"], 0.0))
+                per[key] = (name, v + float(r["Counter_Value"]))
+    return [per[k] for k in sorted(per)]
+
+
+def traffic_summary(args):
+    """HBM bytes per launch of the dominant kernel from FETCH_SIZE / WRITE_SIZE
+    runs, each scaled by what the counter reads for a plain copy of known size."""
+    import statistics
+    d = args.traffic_from
+    stages = STAGES[1] if W.WORKLOADS[args.workload].get("top_k", 0) <= 0 else STAGES[3]
+    kernel = stages[0] if len(stages) == 1 else "k_stats"
+    cal_bytes_kib = (1 << 30) / 1024.0
+
+    def calib(sub, counter):
+        vals = [v for name, v in _counter_per_dispatch(os.path.join(d, sub), counter)
+                if "copy" in name.lower()]
+        if not vals:
+            raise SystemExit(f"bench.py: no copy dispatch in {sub}")
+        return cal_bytes_kib / statistics.median(vals)
+
+    def kern(sub, counter):
+        vals = [v for name, v in _counter_per_dispatch(os.path.join(d, sub), counter)
+                if f"::{kernel}<" in name or name.startswith(kernel)]
+        # the first dispatch draws the draft tokens (a smaller call); the rest are timed steps
+        return statistics.median(vals[1:] if len(vals) > 1 else vals)
+
+    fs, ws_ = calib("cal_fetch", "FETCH_SIZE"), calib("cal_write", "WRITE_SIZE")
+    fk, wk = kern("fetch", "FETCH_SIZE"), kern("write", "WRITE_SIZE")
+    hbm = (fk * fs + wk * ws_) * 1024.0
+    out = {
+        "kernel": kernel, "workload": args.workload,
+        "sd_t": W.WORKLOADS[args.workload].get("sd_t") if args.sd_t is None else args.sd_t,
+        "source_sha256": kernel_source_digest(),
+        "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
+        "fetch_scale": fs, "write_scale": ws_, "hbm_bytes_per_launch": hbm,
+        "commands": [
+            f"rocprofv3 --pmc {c} --output-format csv -d <out>/{sub} -o run -- python3 bench.py "
+            f"--cpu-seconds 0 --steps 20 --warmup 2 --workload {args.workload}"
+            for c, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write"))] + [
+            f"rocprofv3 --pmc {c} --output-format csv -d <out>/{sub} -o run -- python3 bench.py "
+            "--calibrate-copy" for c, sub in (("FETCH_SIZE", "cal_fetch"), ("WRITE_SIZE", "cal_write"))]
+            + [f"python3 bench.py --traffic-from <out> --workload {args.workload}"],
+    }
+    with open(traffic_file(kernel, args.workload), "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_summary(args)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(sequences shard across GPUs with no exchange; see the design notes)",
