@@ -23,4 +23,6 @@ from .verify import (  # noqa: F401
     verify_sequence,
     verify,
     sample_rows,
+    acceptance_probability,
+    acceptance_stats,
 )

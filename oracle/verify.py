@@ -375,6 +375,69 @@ def verify(draft, target, draft_tokens, uniforms, *, B, V, dtype, K=None,
     return res
 
 
+# --------------------------------------------------------------------------
+# Acceptance statistics ([P1] s.6: a draft token x passes with probability
+# min(1, p(x)/q(x)), and the acceptance rate measures how close the draft is
+# to the target; [P3] section "Khi thời gian tiết kiệm bị chi phí ăn hết":
+# measure the useful tokens per round and the acceptance rate; [P2]
+# "工程里的关键优化点" item 3 adapts K to it). Not printed on the pages: the
+# expectation below is the definition of "the probability that a draft drawn
+# from q_i passes", and the expected count follows from the truncation rule
+# ([P1] s.5 step 4) with the rows held fixed.
+# --------------------------------------------------------------------------
+def acceptance_probability(p, q):
+    """beta = E_{x ~ q}[min(1, r(x))], r = p/q as in accept_ratio.
+
+    Ids with q(x) = 0 are never drafted and carry no weight."""
+    drafted = q > 0.0
+    r = p[drafted] / q[drafted]
+    return float(np.sum(q[drafted] * np.minimum(1.0, r)))
+
+
+def acceptance_stats(draft, target, *, B, V, dtype, temperature, K=None,
+                     cu_draft=None, top_k=0, top_p=1.0):
+    """Acceptance probability of every draft position and the expected number
+    of accepted drafts of every sequence, for sampling verification.
+
+    Same storage layout as ``verify``; the bonus target row of each sequence is
+    not used. For position i of sequence b, beta_i = acceptance_probability(p_i,
+    q_i) on the filtered, tempered rows (R6), NaN if either row is unusable
+    (R8). The walk stops at the first rejection, so draft j is accepted iff
+    drafts 0..j all pass: with the rows fixed, E[n_b] = sum_{j<K_b}
+    prod_{i<=j} beta_i (NaN if any beta of the sequence is NaN; 0 for K_b = 0).
+    Returns dict(beta [sum K_b] float64, expected_accepted [B] float64,
+    margin [sum K_b] float64: the nearer top-p margin of the pair's rows)."""
+    if not (temperature > 0.0) or math.isinf(temperature):
+        raise ValueError("acceptance statistics need a finite temperature > 0")
+    if not (0.0 < top_p <= 1.0):
+        raise ValueError("top_p must lie in (0, 1]")
+    if cu_draft is None:
+        cu = np.arange(B + 1, dtype=np.int64) * int(K)
+    else:
+        cu = np.asarray(cu_draft, dtype=np.int64)
+    draft = np.asarray(draft).reshape(-1, V)
+    target = np.asarray(target).reshape(-1, V)
+    n_draft = int(cu[B])
+    beta = np.full(n_draft, math.nan)
+    margin = np.full(n_draft, ACCEPT_MARGIN_INF)
+    expected = np.zeros(B)
+    for b in range(B):
+        d0, d1 = int(cu[b]), int(cu[b + 1])
+        e, run = 0.0, 1.0
+        for i in range(d1 - d0):
+            lq = decode_logits(draft[d0 + i], dtype)
+            lp = decode_logits(target[d0 + b + i], dtype)
+            if row_is_valid(lq) and row_is_valid(lp):
+                q, _, mq = filtered_distribution(lq, temperature, top_k, top_p)
+                p, _, mp = filtered_distribution(lp, temperature, top_k, top_p)
+                beta[d0 + i] = acceptance_probability(p, q)
+                margin[d0 + i] = min(mq, mp)
+            run *= beta[d0 + i]  # P(drafts 0..i all pass)
+            e += run
+        expected[b] = e
+    return dict(beta=beta, expected_accepted=expected, margin=margin)
+
+
 def sample_rows(rows, uniforms, *, V, dtype, temperature, top_k=0, top_p=1.0,
                 greedy=None):
     """Draw one token per row by the inverse CDF of its filtered distribution.
