@@ -190,6 +190,38 @@ int spec_verify_diag(const void* draft_logits, const void* target_logits,
                      size_t workspace_bytes, hipStream_t stream,
                      const sv_diag* diag);
 
+/* Acceptance statistics of sampling verification (no draft ids, no uniforms):
+ * how often drafts pass, the quantity a caller adapting K per sequence needs
+ * (aivaro.ru answer 289 section 6: a draft token passes with probability
+ * min(1, p/q) and the acceptance rate measures how close the draft is to the
+ * target; aihero.vn "Speculative decoding" section "Khi thời gian tiết kiệm bị
+ * chi phí ăn hết": measure useful tokens per round and the acceptance rate;
+ * lecture-16 notes "工程里的关键优化点" item 3: K adapted to it).
+ *   beta[d] = sum_x q_i(x) * min(1, p_i(x)/q_i(x)) = sum_x min(p_i(x), q_i(x))
+ *       for draft row d = cu[b] + i and the target row of the same position,
+ *       on the tempered, filtered rows: the probability that a draft drawn
+ *       from q_i passes the ratio test. NaN if either row holds NaN or +inf or
+ *       no finite value.
+ *   expected_accepted[b] = sum_{j<K_b} prod_{i<=j} beta_i: the expected number
+ *       of accepted drafts with the rows held fixed (the emitted count is one
+ *       more: the correction or bonus token). 0 when K_b = 0; NaN if a beta of
+ *       the sequence is NaN or the sequence's offsets are invalid (then the
+ *       betas of its rows are unspecified).
+ * Layout as spec_verify_ragged; target row K_b of each sequence (the bonus
+ * row) is not read. cu_draft may be NULL: then every sequence has
+ * K = total_draft_rows / B drafts (total_draft_rows must be a multiple of B,
+ * K <= 64). temperature must be finite and > 0 (greedy verification has no
+ * pass probability); top_k / top_p as spec_verify, and the same limits.
+ * Outputs: beta float [total_draft_rows] (may be NULL when it is 0),
+ * expected_accepted float [B], device memory. The workspace is sized by
+ * spec_verify_workspace_bytes(B, total_draft_rows, V, top_k, top_p) and obeys
+ * the same zero rules. Two passes over the rows: statistics, then the sums. */
+int spec_verify_accept_stats(const void* draft_logits, const void* target_logits,
+                             const int32_t* cu_draft, int B, int total_draft_rows, int V,
+                             float temperature, int top_k, float top_p, sv_dtype dtype,
+                             float* beta, float* expected_accepted, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     make_workspace,
     num_stages,
     spec_verify,
+    spec_verify_accept_stats,
     spec_verify_ragged,
     strerror,
     workspace_bytes,

@@ -49,6 +49,8 @@ SIGNATURES = {
                                 _P, _S, _P]),
     "spec_verify_diag": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _I, _F, _I, _P, _P,
                               _P, _S, _P, ctypes.POINTER(SvDiag)]),
+    "spec_verify_accept_stats": (_I, [_P, _P, _P, _I, _I, _I, _F, _I, _F, _I, _P, _P, _P, _S,
+                                      _P]),
 }
 
 _lib = None
@@ -189,6 +191,30 @@ def spec_verify_ragged(draft_logits, target_logits, draft_tokens, uniforms, cu_d
             d.n_stage_events = len(handles)
         _check(lib().spec_verify_diag(*args, ctypes.byref(d)))
     return out_tokens, num_accepted
+
+
+def spec_verify_accept_stats(draft_logits, target_logits, cu_draft, B, V, temperature, top_k=0,
+                             top_p=1.0, *, total_draft_rows=None, beta=None,
+                             expected_accepted=None, workspace=None):
+    """Pass probability of every draft position and expected accepted drafts of
+    every sequence (see include/spec_verify.h). ``cu_draft`` is an int32 [B+1]
+    device tensor, or None for B sequences of equal length; ``total_draft_rows``
+    defaults to draft_logits.numel() // V. Returns (beta [total_draft_rows],
+    expected_accepted [B]), float32 on the device."""
+    dev = target_logits.device
+    n_draft = (int(draft_logits.numel()) // int(V) if total_draft_rows is None
+               else int(total_draft_rows))
+    if beta is None:
+        beta = torch.empty((n_draft,), dtype=torch.float32, device=dev)
+    if expected_accepted is None:
+        expected_accepted = torch.empty((B,), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = make_workspace(B, n_draft, V, top_k, top_p, dev)
+    _check(lib().spec_verify_accept_stats(
+        _ptr(draft_logits), _ptr(target_logits), _ptr(cu_draft), int(B), n_draft, int(V),
+        float(temperature), int(top_k), float(top_p), _dtype_code(target_logits), _ptr(beta),
+        _ptr(expected_accepted), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return beta, expected_accepted
 
 
 def make_stage_events(n, device=None):

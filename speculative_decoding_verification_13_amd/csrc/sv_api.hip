@@ -47,6 +47,8 @@ int kcap_for(int top_k) { return (top_k + 256 + 63) / 64 * 64; }
 //   tiles[B * dmax * tiles per draw block] draw-weight tile sums (separate kernels)
 //   draws[B * 2 * dmax]                    slice weight sums of the final draw
 //                                          (one-kernel step)
+//   beta_part[total_draft * cmax]          chunk sums of min(p, q) (acceptance
+//   beta_cnt[total_draft]                  statistics) and per-pair counters
 // and with top-k active:
 //   rec[(total_draft + rows) * cmax * rec_words]  chunk records of sampling rows
 //   rowres[total_draft + rows]                    kept-set statistics per row
@@ -81,6 +83,10 @@ bool make_plan(int B, int total_draft, int V, int top_k, size_t ws_bytes, sv::Pl
   off += align_up((size_t)B * (size_t)dmax * sv::kTilesPerDraw * 4);
   L.off_draws = off;
   off += align_up((size_t)B * 2 * (size_t)dmax * 8);
+  L.off_beta_part = off;
+  off += align_up((size_t)total_draft * (size_t)cmax * 4);
+  L.off_beta_cnt = off;
+  off += align_up((size_t)total_draft * 4);
   L.off_rec = L.off_rowres = off;
   if (filt) {
     const size_t rec_words = sv::kRecHeader + 2 * (size_t)kcap_for(top_k);
@@ -224,6 +230,68 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
   return err == hipSuccess ? SV_OK : SV_EHIP;
 }
 
+int run_accept(const void* draft, const void* target, const int32_t* cu, int B, int total_draft,
+               int V, float temperature, int top_k, float top_p, int dtype, float* beta,
+               float* expected, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (dtype != SV_F32 && dtype != SV_F16 && dtype != SV_BF16) return SV_EDTYPE;
+  if (B < 0 || V < 1 || total_draft < 0) return SV_EINVAL;
+  if (!(temperature > 0.0f) || isinf(temperature)) return SV_EINVAL;
+  if (!(top_p > 0.0f && top_p <= 1.0f)) return SV_EINVAL;
+  if (B == 0) return SV_OK;
+  int K = 0;
+  if (cu == nullptr) {
+    if (total_draft % B != 0 || total_draft / B > SV_MAX_K) return SV_EINVAL;
+    K = total_draft / B;
+  }
+  if (target == nullptr || expected == nullptr) return SV_EINVAL;
+  if (total_draft > 0 && (draft == nullptr || beta == nullptr)) return SV_EINVAL;
+  const bool filt = filters_active(V, top_k, top_p);
+  if (filt && (!topk_active(V, top_k) || top_k > SV_MAX_TOP_K)) return SV_EUNSUPPORTED;
+  sv::Plan L;
+  if (!make_plan(B, total_draft, V, filt ? top_k : 0, SIZE_MAX, L)) return SV_EUNSUPPORTED;
+  if (workspace == nullptr || ((uintptr_t)workspace % kAlign) != 0 ||
+      !make_plan(B, total_draft, V, filt ? top_k : 0, workspace_bytes, L))
+    return SV_EWORKSPACE;
+  const int es = esize_of(dtype);
+  const bool vec = ((size_t)V * es) % 16 == 0 && aligned16(target) &&
+                   (draft == nullptr || aligned16(draft));
+  sv::Params P{};
+  P.draft = draft;
+  P.target = target;
+  P.cu = cu;
+  P.B = B;
+  P.K = K;
+  P.V = V;
+  P.total_draft = total_draft;
+  P.rows = total_draft + B;
+  P.c = (float)(1.4426950408889634074 / (double)temperature);
+  P.nvec = vec ? V / (16 / es) : V;
+  P.chunk_vecs = filt ? sv::kFiltChunkVecs : (int)chunk_vecs_for(P.nvec);
+  P.chunks = (P.nvec + P.chunk_vecs - 1) / P.chunk_vecs;
+  P.filt = filt ? 1 : 0;
+  P.top_k = top_k;
+  P.top_p = top_p;
+  P.kcap = filt ? kcap_for(top_k) : 0;
+  P.rec_words = sv::kRecHeader + 2 * P.kcap;
+  char* ws = static_cast<char*>(workspace);
+  P.rec = filt ? reinterpret_cast<unsigned*>(ws + L.off_rec) : nullptr;
+  P.rowres = filt ? reinterpret_cast<sv::RowRes*>(ws + L.off_rowres) : nullptr;
+  P.slots = reinterpret_cast<unsigned long long*>(ws + L.off_slots);
+  P.skip_bonus = 1;
+  P.beta = beta;
+  P.expected = expected;
+  P.beta_part = reinterpret_cast<float*>(ws + L.off_beta_part);
+  P.beta_cnt = reinterpret_cast<int*>(ws + L.off_beta_cnt);
+  L.chunks = P.chunks;
+  L.chunk_vecs = P.chunk_vecs;
+  L.stats_blocks = ((long long)total_draft + P.rows) * P.chunks;
+  L.filter_blocks = filt ? (long long)total_draft + P.rows : 0;
+  P.stats_blocks = L.stats_blocks;
+  if (L.stats_blocks > (long long)UINT32_MAX / sv::kThreads) return SV_EUNSUPPORTED;
+  if (sv::launch_row_stats(dtype, vec, P, L, stream) != hipSuccess) return SV_EHIP;
+  return sv::launch_accept(dtype, vec, P, L, stream) == hipSuccess ? SV_OK : SV_EHIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -289,6 +357,16 @@ int spec_verify_diag(const void* draft_logits, const void* target_logits,
   return run(draft_logits, target_logits, draft_tokens, uniforms, cu_draft, greedy, B, 0,
              total_draft_rows, V, temperature, top_k, top_p, (int)dtype, out_tokens,
              num_accepted, workspace, workspace_bytes, stream, diag);
+}
+
+int spec_verify_accept_stats(const void* draft_logits, const void* target_logits,
+                             const int32_t* cu_draft, int B, int total_draft_rows, int V,
+                             float temperature, int top_k, float top_p, sv_dtype dtype,
+                             float* beta, float* expected_accepted, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  return run_accept(draft_logits, target_logits, cu_draft, B, total_draft_rows, V, temperature,
+                    top_k, top_p, (int)dtype, beta, expected_accepted, workspace,
+                    workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -116,6 +116,12 @@ struct Params {
   unsigned long long* draws;  // [B * 2 * dchunks]
   long long draw_at;       // one-kernel step: statistics blocks ahead of the draw blocks
   DiagPtrs diag;
+  // Acceptance statistics (spec_verify_accept_stats)
+  int skip_bonus;          // 1: the statistics pass skips each sequence's bonus row
+  float* beta;             // [total_draft] output: pass probability per draft position
+  float* expected;         // [B] output: expected accepted drafts per sequence
+  float* beta_part;        // [total_draft * chunks] chunk sums of min(p, q)
+  int* beta_cnt;           // [total_draft] chunks finished per row pair (zero between calls)
 };
 
 // Grid size and workspace offsets of one call.
@@ -124,7 +130,7 @@ struct Plan {
   bool fused;  // one kernel (k_verify) instead of statistics, filter and draw kernels
   long long stats_blocks, filter_blocks, draw_blocks;
   size_t off_slots, off_tiles, off_draws, off_draw_done, off_seq_flags, off_rec, off_rowres,
-      total_bytes;
+      off_beta_part, off_beta_cnt, total_bytes;
 };
 
 // The separate statistics / filter / draw kernels (sv_verify.hip).
@@ -134,6 +140,11 @@ hipError_t launch(int dtype, bool vec, const Params& P, const Plan& L, hipStream
 // the chip holds at once with `cus` compute units (0 if unknown).
 hipError_t launch_fused(int dtype, bool vec, const Params& P, const Plan& L, hipStream_t s);
 long long fused_capacity(int dtype, bool vec, int cus);
+// Row statistics alone (the statistics pass, and the filter pass with top-k):
+// the first stage of the acceptance statistics (sv_verify.hip).
+hipError_t launch_row_stats(int dtype, bool vec, const Params& P, const Plan& L, hipStream_t s);
+// The acceptance statistics after the row statistics (sv_accept.hip).
+hipError_t launch_accept(int dtype, bool vec, const Params& P, const Plan& L, hipStream_t s);
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t s);
 
 }  // namespace sv

@@ -152,6 +152,13 @@ __device__ int row_seq(const Params& P, int row, bool is_target, int* s_cu) {
   return lo;
 }
 
+// Whether target row `row` is its sequence's last (bonus) row (whole block).
+__device__ __forceinline__ bool is_bonus_row(const Params& P, int row, int* s_cu) {
+  if (P.cu == nullptr) return row % (P.K + 1) == P.K;
+  const int b = row_seq(P, row, true, s_cu);
+  return row == P.cu[b + 1] + b;
+}
+
 // Statistics of vectors vb..ve-1 of one row (whole block): for a greedy row
 // the argmax (lowest id on ties) and whether the chunk holds NaN or +inf, for a
 // sampling row the maximum m and the sum of 2^(l*c - R), R = fp32(m*c).

@@ -631,6 +631,7 @@ __device__ void stats_unit(const Params& P, long long g) {
   bool greedy = P.all_greedy != 0;
   if (!greedy && P.greedy != nullptr) greedy = P.greedy[row_seq(P, row, is_target, s_cu)] != 0;
   if (greedy && !is_target) return;  // greedy sequences never read draft rows
+  if (P.skip_bonus && is_target && is_bonus_row(P, row, s_cu)) return;
   const void* base = is_target ? P.target : P.draft;
   const size_t roff = (size_t)row * (size_t)P.V;
   if constexpr (FILT) {
@@ -676,6 +677,7 @@ __global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
   const bool is_target = unit >= P.total_draft;
   const int row = is_target ? unit - P.total_draft : unit;
   if (P.greedy != nullptr && P.greedy[row_seq(P, row, is_target, s_cu)] != 0) return;
+  if (P.skip_bonus && is_target && is_bonus_row(P, row, s_cu)) return;
   const int C = P.chunks;
   const unsigned* rec0 = P.rec + (size_t)unit * C * P.rec_words;
   // Stage the records in LDS when they fit: headers, then every entry's key.
@@ -1166,6 +1168,32 @@ hipError_t launch(int dtype, bool vec, const Params& P, const Plan& L, hipStream
       return vec ? launch_t<SV_F16, true>(P, L, s, ev, nev) : launch_t<SV_F16, false>(P, L, s, ev, nev);
     default:
       return vec ? launch_t<SV_BF16, true>(P, L, s, ev, nev) : launch_t<SV_BF16, false>(P, L, s, ev, nev);
+  }
+}
+
+template <int DT, bool VEC>
+static hipError_t launch_row_stats_t(const Params& P, const Plan& L, hipStream_t s) {
+  if (P.filt) {
+    hipLaunchKernelGGL((k_stats<DT, VEC, true>), dim3((unsigned)L.stats_blocks), dim3(kThreads), 0,
+                       s, P);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(k_filter, dim3((unsigned)L.filter_blocks), dim3(kThreads), 0, s, P);
+  } else {
+    hipLaunchKernelGGL((k_stats<DT, VEC, false>), dim3((unsigned)L.stats_blocks), dim3(kThreads),
+                       0, s, P);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_row_stats(int dtype, bool vec, const Params& P, const Plan& L, hipStream_t s) {
+  switch (dtype) {
+    case SV_F32:
+      return vec ? launch_row_stats_t<SV_F32, true>(P, L, s) : launch_row_stats_t<SV_F32, false>(P, L, s);
+    case SV_F16:
+      return vec ? launch_row_stats_t<SV_F16, true>(P, L, s) : launch_row_stats_t<SV_F16, false>(P, L, s);
+    default:
+      return vec ? launch_row_stats_t<SV_BF16, true>(P, L, s) : launch_row_stats_t<SV_BF16, false>(P, L, s);
   }
 }
 

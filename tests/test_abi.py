@@ -132,3 +132,27 @@ def test_workspace_sizes(L):
     assert ws(64, 512, 128256, 1024, 1.0) > ws(64, 512, 128256, 50, 1.0)
     assert ws(64, 512, 128256, 128256, 1.0) == ws(64, 512, 128256, 0, 1.0)  # k >= V: off
     assert L.spec_verify_num_stages(0, 1.0) >= 1
+
+
+def test_accept_stats_argument_errors(L):
+    def acc(**kw):
+        a = dict(draft=_FAKE, target=_FAKE, cu=_FAKE, B=4, total=12, V=1000, T=1.0, top_k=0,
+                 top_p=1.0, dtype=2, beta=_FAKE, exp=_FAKE, ws=_FAKE_WS, ws_bytes=8)
+        a.update(kw)
+        return L.spec_verify_accept_stats(a["draft"], a["target"], a["cu"], a["B"], a["total"],
+                                          a["V"], a["T"], a["top_k"], a["top_p"], a["dtype"],
+                                          a["beta"], a["exp"], a["ws"], a["ws_bytes"], None)
+    assert acc() == -3
+    assert acc(dtype=5) == -2
+    assert acc(T=0.0) == -1  # greedy verification has no pass probability
+    assert acc(T=float("nan")) == -1
+    assert acc(top_p=0.0) == -1
+    assert acc(B=-1) == -1 and acc(total=-1) == -1 and acc(V=0) == -1
+    assert acc(cu=None, total=13) == -1  # not a multiple of B
+    assert acc(cu=None, total=4 * 65) == -1  # K above 64
+    assert acc(cu=None, total=12) == -3
+    assert acc(target=None) == -1 and acc(exp=None) == -1
+    assert acc(draft=None) == -1 and acc(beta=None) == -1
+    assert acc(draft=None, beta=None, total=0) == -3  # no draft rows: neither is read
+    assert acc(top_k=0, top_p=0.9) == -5
+    assert acc(B=0, draft=None, target=None, cu=None, beta=None, exp=None, ws=None) == 0
