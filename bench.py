@@ -97,6 +97,9 @@ def parse():
                     help="budget of the CPU oracle sample (0 disables)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--path", choices=["verify", "accept"], default="verify",
+                    help="verify: the verification step (default); accept: the "
+                         "acceptance statistics (spec_verify_accept_stats)")
     ap.add_argument("--traffic-from", metavar="DIR", default=None,
                     help="only summarise rocprofv3 counter runs: DIR/{fetch,write,cal_fetch,"
                          "cal_write} hold FETCH_SIZE / WRITE_SIZE runs of this bench command and "
@@ -197,6 +200,9 @@ def main():
     import speculative_decoding_verification_13_amd as sv
 
     w = W.make(args.workload, sd_t=args.sd_t)
+    if args.path == "accept":
+        bench_accept(args, w, sv)
+        return
     # the CPU oracle first: its worker processes fork before this process uses the GPU
     cpu = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
 
@@ -357,6 +363,93 @@ def main():
 
 
 _CPU = {}
+
+
+def bench_accept(args, w, sv):
+    """Acceptance statistics (pass probability per draft position, expected
+    accepted drafts per sequence) on the same workload: two passes over the
+    draft rows and the non-bonus target rows."""
+    cu = w["cu_draft"]
+    B, V = w["B"], w["V"]
+    n_draft = int(cu[-1])
+    T, top_k, top_p = w["temperature"], w["top_k"], w["top_p"]
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        draft, target = W.raw_numpy(w["draft"]), W.raw_numpy(w["target"])
+        t0, done, b = time.perf_counter(), 0, 0
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            d0, d1 = int(cu[b % B]), int(cu[b % B + 1])
+            oracle.acceptance_stats(draft[d0:d1], target[d0 + b % B:d1 + b % B + 1], B=1, V=V,
+                                    dtype=w["dtype"], temperature=T, cu_draft=[0, d1 - d0],
+                                    top_k=top_k, top_p=top_p)
+            done += d1 - d0
+            b += 1
+        el = time.perf_counter() - t0
+        cpu = {"value": done / el, "unit": "draft positions/s", "cores": 1, "kind": "oracle",
+               "sample": f"{b} sequences of the same workload one by one in {el:.1f} s, "
+                         "numpy float64, one process"}
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    draft0, target0 = w["draft"].to(dev), w["target"].to(dev)
+    sets = [(draft0, target0)] + [(draft0.clone(), target0.clone())
+                                  for _ in range(max(1, args.sets) - 1)]
+    cu_d = torch.from_numpy(cu.astype(np.int32)).to(dev) if w["ragged"] else None
+    ws = sv.make_workspace(B, n_draft, V, top_k, top_p, dev)
+    beta = torch.empty(n_draft, dtype=torch.float32, device=dev)
+    exp = torch.empty(B, dtype=torch.float32, device=dev)
+
+    def step(k):
+        d, t = sets[k % len(sets)]
+        sv.spec_verify_accept_stats(d, t, cu_d, B, V, T, top_k, top_p, total_draft_rows=n_draft,
+                                    beta=beta, expected_accepted=exp, workspace=ws)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    hev = HipEvents(2 * args.steps)
+    stream = torch.cuda.current_stream().cuda_stream
+    rec = hev.hip.hipEventRecord
+    rec.argtypes = [hev.ct.c_void_p, hev.ct.c_void_p]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for k in range(args.steps):
+        step(k)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    # per call, on the launch stream (events without the system-scope fence)
+    for k in range(args.steps):
+        rec(hev.handles[2 * k], stream)
+        step(k)
+        rec(hev.handles[2 * k + 1], stream)
+    torch.cuda.synchronize()
+    call_ms = float(np.mean([hev.elapsed_ms(2 * k, 2 * k + 1) for k in range(args.steps)]))
+    hev.close()
+    esize = target0.element_size()
+    pass_bytes = 2 * n_draft * V * esize  # draft rows and their target rows
+    algo = 2 * pass_bytes
+    achieved = algo / (call_ms * 1e-3) / 1e9
+    rec_out = {
+        "metric": "acceptance statistics: draft positions/s (pass probability per position, "
+                  "expected accepted drafts per sequence)",
+        "value": n_draft / (ms_step * 1e-3), "unit": "draft positions/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "V": V, "input_dtype": w["dtype"],
+                   "temperature": T, "top_k": top_k, "top_p": top_p, "sd_t": w["sd_t"],
+                   "draft_positions_per_step": n_draft, "rotating_sets": len(sets),
+                   "entry_point": "spec_verify_accept_stats"},
+        "roofline": {"kernel": "k_stats + k_beta + k_expect (whole call)", "bound": "hbm",
+                     "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
+                     "algorithmic_bytes_per_launch": algo, "avg_launch_ms": call_ms},
+        "mean_beta": float(beta.float().nanmean().item()),
+        "mean_expected_accepted": float(exp.float().nanmean().item()),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec_out), flush=True)
 
 
 def _cpu_one(b):

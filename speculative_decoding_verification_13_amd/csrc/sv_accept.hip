@@ -12,7 +12,7 @@
 // block of the pair gets the same values), sums min(p, q) over its chunk and
 // publishes the sum; the last block of the pair to finish adds the chunk sums
 // in chunk order, writes beta and returns the pair's partials and counter to
-// zero. k_expect forms E[n] per sequence.
+// zero, and the last pair of a sequence to finish forms its E[n].
 //
 // Pages (by title, section): aivaro.ru answer 289 "Как работает speculative
 // decoding на уровне логитов, а не токенов?" s.6 (a draft token passes with
@@ -27,9 +27,10 @@ namespace sv {
 
 namespace {
 
-// Softmax reference R = fp32(m*c), 1/S and kept-set threshold of one row.
+// Softmax reference R = fp32(m*c), sum S of 2^(l*c - R) over the kept set and
+// kept-set threshold of one row: p(x) = 2^(l*c - R) / S for kept ids.
 struct RowStat {
-  float R, invS, thr;
+  float R, S, thr;
   int ok;
 };
 
@@ -56,19 +57,50 @@ __device__ RowStat row_stat(const Params& P, long long unit) {
   RowStat r;
   r.ok = !bad && __builtin_isfinite(m) && s > 0.f && __builtin_isfinite(s);
   r.R = ref_of(m, P.c);
-  r.invS = 1.0f / s;
+  r.S = s;
   r.thr = thr;
   return r;
 }
 
-__device__ __forceinline__ float kept_prob(float l, const RowStat& r, float c) {
-  return (l >= r.thr) ? fast_exp2(fmaf(l, c, -r.R)) * r.invS : 0.0f;
+#ifndef SV_BETA_BATCH
+#define SV_BETA_BATCH 4
+#endif
+#ifndef SV_BETA_WAVES
+#define SV_BETA_WAVES 7
+#endif
+constexpr int kBetaBatch = SV_BETA_BATCH;  // vectors per row per thread in flight
+
+// l*c - R of a logit, -inf outside the kept set.
+template <bool FILT>
+__device__ __forceinline__ float rel_exp(float l, float c, float R, float thr) {
+  const float x = fmaf(l, c, -R);
+  if constexpr (FILT) return (l >= thr) ? x : kNegInf;
+  return x;
+}
+
+// Expected accepted drafts of sequence b from its published pass
+// probabilities: sum_{j<K_b} prod_{i<=j} beta_i (NaN for invalid offsets).
+__device__ void write_expected(const Params& P, int b) {
+  int d0, kb;
+  if (!seq_bounds(P, b, d0, kb)) {
+    P.expected[b] = __builtin_nanf("");
+    return;
+  }
+  float e = 0.f, run = 1.f;
+  for (int i = 0; i < kb; ++i) {
+    run *= obs_f(P.beta + d0 + i);  // P(drafts 0..i all pass)
+    e += run;
+  }
+  P.expected[b] = e;
 }
 
 // Block (pair d, chunk ch): d is a draft row, its pair the target row of the
-// same position.
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_beta(const Params P) {
+// same position. With a = l_p*c - R_p, b = l_q*c - R_q and
+// delta = log2(S_q / S_p): min(p, q) = 2^min(a, b - delta) / S_p, one
+// exponential per pair of logits (the offsets stay small, so each term keeps
+// the precision of its own row's exponent).
+template <int DT, bool VEC, bool FILT>
+__global__ __launch_bounds__(kThreads, SV_BETA_WAVES) void k_beta(const Params P) {
   using Vc = Vec<DT, VEC>;
   constexpr int N = Vc::N;
   __shared__ int s_cu[kCuLds];
@@ -82,32 +114,43 @@ __global__ __launch_bounds__(kThreads) void k_beta(const Params P) {
   const int b = row_seq(P, d, false, s_cu);
   const int t = d + b;  // target row of the same position
   const long long uq = unit_of(P, false, d), up = unit_of(P, true, t);
+  if (g == 0 && P.cu != nullptr) {
+    // sequences without pairs: no draft (expected 0) or invalid offsets (NaN)
+    for (int k = tid; k < P.B; k += kThreads) {
+      int d0, kb;
+      if (!seq_bounds(P, k, d0, kb)) P.expected[k] = __builtin_nanf("");
+      else if (kb == 0) P.expected[k] = 0.f;
+    }
+  }
   if (tid < 2) s_st[tid] = row_stat(P, tid == 0 ? uq : up);
   __syncthreads();
   const RowStat sq = s_st[0], sp = s_st[1];
   const bool ok = sq.ok && sp.ok;
   const float c = P.c;
+  const float delta = __log2f(sq.S / sp.S);
   float acc = 0.f;
   if (ok) {
     const size_t rq = (size_t)d * P.V, rp = (size_t)t * P.V;
     const int vb = ch * P.chunk_vecs;
     const int ve = min(P.nvec, vb + P.chunk_vecs);
     int v = vb + tid;
-    for (; v + (kBatch - 1) * kThreads < ve; v += kBatch * kThreads) {
-      typename Vc::Raw aq[kBatch], ap[kBatch];
+    for (; v + (kBetaBatch - 1) * kThreads < ve; v += kBetaBatch * kThreads) {
+      typename Vc::Raw aq[kBetaBatch], ap[kBetaBatch];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
+      for (int u = 0; u < kBetaBatch; ++u) {
         aq[u] = Vc::load_stream(P.draft, rq, v + u * kThreads);
         ap[u] = Vc::load_stream(P.target, rp, v + u * kThreads);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
+      for (int u = 0; u < kBetaBatch; ++u) {
         float fq[N], fp[N];
         Vc::get(aq[u], fq);
         Vc::get(ap[u], fp);
 #pragma unroll
-        for (int k = 0; k < N; ++k) acc += fminf(kept_prob(fp[k], sp, c), kept_prob(fq[k], sq, c));
+        for (int k = 0; k < N; ++k)
+          acc += fast_exp2(fminf(rel_exp<FILT>(fp[k], c, sp.R, sp.thr),
+                                 rel_exp<FILT>(fq[k], c, sq.R, sq.thr) - delta));
       }
     }
     for (; v < ve; v += kThreads) {
@@ -115,7 +158,9 @@ __global__ __launch_bounds__(kThreads) void k_beta(const Params P) {
       Vc::get(Vc::load_stream(P.draft, rq, v), fq);
       Vc::get(Vc::load_stream(P.target, rp, v), fp);
 #pragma unroll
-      for (int k = 0; k < N; ++k) acc += fminf(kept_prob(fp[k], sp, c), kept_prob(fq[k], sq, c));
+      for (int k = 0; k < N; ++k)
+        acc += fast_exp2(fminf(rel_exp<FILT>(fp[k], c, sp.R, sp.thr),
+                               rel_exp<FILT>(fq[k], c, sq.R, sq.thr) - delta));
     }
   }
   float tot[1];
@@ -128,45 +173,43 @@ __global__ __launch_bounds__(kThreads) void k_beta(const Params P) {
   __syncthreads();
   if (!s_last) return;
   // Last block of the pair: the chunk sums in chunk order, then the pair's
-  // partials and counter back to zero (every block of the pair has read them).
+  // partials and counter back to zero (every block of the pair has read them);
+  // the last pair of the sequence forms the expected count.
   if (tid == 0) {
     float beta = 0.f;
     for (int k = 0; k < C; ++k) beta += obs_f(P.beta_part + (size_t)d * C + k);
-    P.beta[d] = ok ? beta : __builtin_nanf("");
+    pub_f(P.beta + d, ok ? beta / sp.S : __builtin_nanf(""));
     pub_i(P.beta_cnt + d, 0);
+    drain_stores();
+    int d0, kb;
+    const int need = seq_bounds(P, b, d0, kb) ? kb : 1;
+    if (bump(P.draw_done + b) == need - 1) {
+      pub_i(P.draw_done + b, 0);
+      write_expected(P, b);
+    }
   }
   if (!P.filt)
     for (int k = tid; k < 2 * C; k += kThreads)
       P.slots[(k < C ? uq : up) * C + (k < C ? k : k - C)] = 0ull;
 }
 
-// Expected accepted drafts per sequence (one thread each).
+// Expected accepted drafts when the batch has no draft rows (every sequence 0,
+// or NaN for invalid offsets).
 __global__ __launch_bounds__(kThreads) void k_expect(const Params P) {
   const int b = blockIdx.x * kThreads + threadIdx.x;
-  if (b >= P.B) return;
-  int d0, kb;
-  if (!seq_bounds(P, b, d0, kb)) {
-    P.expected[b] = __builtin_nanf("");
-    return;
-  }
-  float e = 0.f, run = 1.f;
-  for (int i = 0; i < kb; ++i) {
-    run *= P.beta[d0 + i];  // P(drafts 0..i all pass)
-    e += run;
-  }
-  P.expected[b] = e;
+  if (b < P.B) write_expected(P, b);
 }
 
 template <int DT, bool VEC>
 hipError_t launch_t(const Params& P, const Plan& L, hipStream_t s) {
-  if (P.total_draft > 0) {
-    hipLaunchKernelGGL((k_beta<DT, VEC>), dim3((unsigned)((long long)P.total_draft * P.chunks)),
-                       dim3(kThreads), 0, s, P);
-    const hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
-  hipLaunchKernelGGL(k_expect, dim3((unsigned)((P.B + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                     s, P);
+  const dim3 grid((unsigned)((long long)P.total_draft * P.chunks));
+  if (P.total_draft == 0)
+    hipLaunchKernelGGL(k_expect, dim3((unsigned)((P.B + kThreads - 1) / kThreads)), dim3(kThreads),
+                       0, s, P);
+  else if (P.filt)
+    hipLaunchKernelGGL((k_beta<DT, VEC, true>), grid, dim3(kThreads), 0, s, P);
+  else
+    hipLaunchKernelGGL((k_beta<DT, VEC, false>), grid, dim3(kThreads), 0, s, P);
   return hipGetLastError();
 }
 

@@ -282,6 +282,7 @@ int run_accept(const void* draft, const void* target, const int32_t* cu, int B, 
   P.expected = expected;
   P.beta_part = reinterpret_cast<float*>(ws + L.off_beta_part);
   P.beta_cnt = reinterpret_cast<int*>(ws + L.off_beta_cnt);
+  P.draw_done = reinterpret_cast<int*>(ws + L.off_draw_done);  // pairs finished per sequence
   L.chunks = P.chunks;
   L.chunk_vecs = P.chunk_vecs;
   L.stats_blocks = ((long long)total_draft + P.rows) * P.chunks;
