@@ -109,8 +109,9 @@ size_t spec_verify_workspace_bytes(int B, int total_draft_rows, int V, int top_k
 /* Zero-fill a workspace on `stream` (kernel fill, no memset node). A workspace
  * must be zero-filled once before its first use: blocks of one call hand
  * per-row partial results to each other through it, and a zero entry means
- * "not yet published". Every call returns those entries and its per-sequence
- * counters to zero before it ends, so calls that share one workspace may differ
+ * "not yet published". Every call returns those entries, its per-sequence
+ * counters and (with filters) its candidate records and per-row results to
+ * zero before it ends, so calls that share one workspace may differ
  * in B, K, V and dtype, as long as it is large enough for each of them. After a
  * call that reports SV_SEQ_SYNC_TIMEOUT or SV_SEQ_BAD_OFFSETS for any sequence,
  * zero-fill the workspace again. */

@@ -173,11 +173,15 @@ __global__ __launch_bounds__(kThreads, SV_BETA_WAVES) void k_beta(const Params P
   __syncthreads();
   if (!s_last) return;
   // Last block of the pair: the chunk sums in chunk order, then the pair's
-  // partials and counter back to zero (every block of the pair has read them);
+  // chunk sums, partials and counter back to zero (every block of the pair
+  // has read the partials);
   // the last pair of the sequence forms the expected count.
   if (tid == 0) {
     float beta = 0.f;
-    for (int k = 0; k < C; ++k) beta += obs_f(P.beta_part + (size_t)d * C + k);
+    for (int k = 0; k < C; ++k) {
+      beta += obs_f(P.beta_part + (size_t)d * C + k);
+      P.beta_part[(size_t)d * C + k] = 0.f;
+    }
     pub_f(P.beta + d, ok ? beta / sp.S : __builtin_nanf(""));
     pub_i(P.beta_cnt + d, 0);
     drain_stores();
@@ -188,9 +192,12 @@ __global__ __launch_bounds__(kThreads, SV_BETA_WAVES) void k_beta(const Params P
       write_expected(P, b);
     }
   }
-  if (!P.filt)
+  if (!P.filt) {
     for (int k = tid; k < 2 * C; k += kThreads)
       P.slots[(k < C ? uq : up) * C + (k < C ? k : k - C)] = 0ull;
+  } else if (tid < 2) {
+    P.rowres[tid == 0 ? uq : up] = RowRes{0.f, 0.f, 0.f, 0};  // every block has read it
+  }
 }
 
 // Expected accepted drafts when the batch has no draft rows (every sequence 0,

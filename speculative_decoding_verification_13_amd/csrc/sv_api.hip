@@ -52,8 +52,10 @@ int kcap_for(int top_k) { return (top_k + 256 + 63) / 64 * 64; }
 // and with top-k active:
 //   rec[(total_draft + rows) * cmax * rec_words]  chunk records of sampling rows
 //   rowres[total_draft + rows]                    kept-set statistics per row
-// Counters, flags, partials, tile and weight sums must be zero when a call
-// starts; the blocks that read them return them to zero, so the layout may
+//   kept[rows * kKeptWords]                       kept set of each target row
+// Every region must be zero when a call starts (counters, flags, partials,
+// tile and weight sums, and with filters the records, row results and kept
+// lists); the blocks that read them return them to zero, so the layout may
 // differ from call to call. The regions are sized for the scalar path (one
 // element per vector), which has the most chunks: a row of nvec <= V vectors
 // never has more than cmax chunks.
@@ -93,6 +95,8 @@ bool make_plan(int B, int total_draft, int V, int top_k, size_t ws_bytes, sv::Pl
     off += align_up(units * (size_t)cmax * rec_words * 4);
     L.off_rowres = off;
     off += align_up(units * sizeof(sv::RowRes));
+    L.off_kept = off;
+    off += align_up((size_t)rows * sv::kKeptWords * 4);
   }
   L.total_bytes = off;
   return off <= ws_bytes;
@@ -170,6 +174,7 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
   char* ws = static_cast<char*>(workspace);
   P.rec = filt ? reinterpret_cast<unsigned*>(ws + L.off_rec) : nullptr;
   P.rowres = filt ? reinterpret_cast<sv::RowRes*>(ws + L.off_rowres) : nullptr;
+  P.kept = filt ? reinterpret_cast<unsigned*>(ws + L.off_kept) : nullptr;
   P.slots = reinterpret_cast<unsigned long long*>(ws + L.off_slots);
   P.tiles = reinterpret_cast<float*>(ws + L.off_tiles);
   P.draws = reinterpret_cast<unsigned long long*>(ws + L.off_draws);

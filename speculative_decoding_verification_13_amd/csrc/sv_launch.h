@@ -31,6 +31,7 @@ constexpr int kFilterMaxLevels = 2048;    // LDS entries of the per-row level so
 constexpr int kFilterLdsKeys = 4096;      // record entries a filter block stages in LDS
 constexpr int kFilterLdsChunks = 64;      // record headers a filter block stages in LDS
 constexpr int kExplicitMax = 2048;        // candidates a filtered draw gathers in LDS
+constexpr int kKeptWords = 2 + 2 * kExplicitMax;  // words of a target row's kept list
 constexpr int kMaxDrawSlices = kThreads;  // draw blocks per sequence of the one-kernel
                                           // step (longer rows take the separate kernels)
 
@@ -99,6 +100,11 @@ struct Params {
   int kcap;                // (value, id) pairs per chunk record
   int rec_words;           // words per chunk record = kRecHeader + 2 * kcap
   unsigned* rec;           // [(total_draft + rows) * chunks * rec_words] (filtered)
+  // Kept set of each filtered target row, written by the filter pass for the
+  // final draw: [0] entries listed, [1] 1 if the set is not listed in full (a
+  // count-only tie class, or more than kExplicitMax ids), then (value bits,
+  // id) pairs. Zero between calls.
+  unsigned* kept;          // [rows * kKeptWords] (filtered)
   RowRes* rowres;          // [total_draft + rows] (filtered)
   int32_t* out_tokens;
   int32_t* num_accepted;
@@ -130,7 +136,7 @@ struct Plan {
   bool fused;  // one kernel (k_verify) instead of statistics, filter and draw kernels
   long long stats_blocks, filter_blocks, draw_blocks;
   size_t off_slots, off_tiles, off_draws, off_draw_done, off_seq_flags, off_rec, off_rowres,
-      off_beta_part, off_beta_cnt, total_bytes;
+      off_kept, off_beta_part, off_beta_cnt, total_bytes;
 };
 
 // The separate statistics / filter / draw kernels (sv_verify.hip).

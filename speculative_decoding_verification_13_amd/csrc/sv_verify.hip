@@ -616,6 +616,21 @@ __device__ void topk_block(const Params& P, long long g, const void* base, size_
 
 }  // namespace
 
+// Returns chunk records to zero (whole block): record r of `nrec`, at
+// rec_of(r), loses its header and the entries the header counts. Groups of 16
+// threads take one record each; a group reads the count before its stores.
+template <class RecOf>
+__device__ void zero_records(const Params& P, int nrec, RecOf rec_of) {
+  constexpr int G = 16;
+  const int grp = threadIdx.x / G, lane = threadIdx.x % G;
+  for (int r = grp; r < nrec; r += kThreads / G) {
+    unsigned* h = rec_of(r);
+    if (h == nullptr) continue;
+    const int words = kRecHeader + 2 * min((int)h[0], P.kcap);
+    for (int w = lane; w < words; w += G) h[w] = 0u;
+  }
+}
+
 // ---------------------------------------------------------------- stats unit
 // Stats block g covers chunk g % chunks of unit g / chunks: draft row u for
 // u < total_draft, else target row u - total_draft. Its partial goes to
@@ -866,6 +881,57 @@ __global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
     rr.flags = bad ? 1 : 0;
     P.rowres[unit] = rr;
   }
+  if (is_target && !P.skip_bonus) {
+    // A target row's kept set, listed for the final draw when every kept id
+    // is an explicit entry (no count-only tie class at or above theta).
+    unsigned* kl = P.kept + (size_t)row * kKeptWords;
+    __syncthreads();
+    if (tid == 0) s_n = 0;
+    __syncthreads();
+    auto add = [&](float v, unsigned id) {
+      const int at = atomicAdd(&s_n, 1);
+      if (at < kExplicitMax) {
+        kl[2 + 2 * at] = __float_as_uint(v);
+        kl[3 + 2 * at] = id;
+      }
+    };
+    int partial = 0;
+    if (staged) {
+      for (int i = tid; i < E; i += kThreads) {
+        const float v = float_of_key(s_key[i]);
+        if (v >= theta) {
+          int lo = 0, hi = C - 1;  // chunk of entry i
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_off[mid] <= i) lo = mid;
+            else hi = mid - 1;
+          }
+          add(v, rec0[(size_t)lo * P.rec_words + kRecHeader + 2 * (i - s_off[lo]) + 1]);
+        }
+      }
+      if (tid < C && (s_hdr[tid][3] & kRecFlagImplicitTies) && __uint_as_float(s_hdr[tid][1]) >= theta)
+        partial = 1;
+    } else {
+      for (int ch = 0; ch < C; ++ch) {
+        const unsigned* h = rec0 + (size_t)ch * P.rec_words;
+        const int ne = min((int)h[0], P.kcap);
+        for (int e = tid; e < ne; e += kThreads) {
+          const float v = __uint_as_float(h[kRecHeader + 2 * e]);
+          if (v >= theta) add(v, h[kRecHeader + 2 * e + 1]);
+        }
+        if (tid == 0 && (h[3] & kRecFlagImplicitTies) && __uint_as_float(h[1]) >= theta) partial = 1;
+      }
+    }
+    partial = block_sum_i(partial);
+    if (tid == 0) {
+      kl[0] = (unsigned)min(s_n, kExplicitMax);
+      kl[1] = (partial || s_n > kExplicitMax) ? 1u : 0u;
+    }
+  }
+  // Every row's records go back to zero (nothing reads them after this pass).
+  __syncthreads();
+  unsigned* recw = P.rec + (size_t)unit * C * P.rec_words;
+  zero_records(P, C, [&](int ch) { return recw + (size_t)ch * P.rec_words; });
 }
 
 // Returns the partials of a sequence's rows to zero (whole block): its target
@@ -880,24 +946,16 @@ __device__ void clear_partials(const Params& P, int d0, int kb, int b, bool with
   }
 }
 
-// Final draw of a filtered sequence from its candidate records (whole block):
-// p_n is zero outside its kept set, whose ids and logits all sit in the chunk
-// records of row p_n when no tie class at the cut was kept as a count, so the
-// residual max(0, p_n - q_n) (or p_n for the bonus) is formed on those ids
-// alone, with q_n's logit loaded at each id. The weights are sorted by id and
-// scanned for the first cumulative weight above u*Z, as the inverse CDF over
-// the whole row would. Returns false (in every thread) when the records do not
-// list the kept set explicitly or it exceeds kExplicitMax; the caller then
-// draws from the rows themselves.
+// Final draw of a filtered sequence from the kept list of row p_n (whole
+// block): p_n is zero outside its kept set, which the filter pass lists in
+// full unless a tie class at the cut was kept as a count or the set exceeds
+// kExplicitMax ids. The residual max(0, p_n - q_n) (or p_n for the bonus) is
+// formed on those ids alone, with q_n's logit loaded at each id; the weights
+// are sorted by id and scanned for the first cumulative weight above u*Z, as
+// the inverse CDF over the whole row would. explicit_usable is false (in every
+// thread) when the list is not complete; the caller then draws from the rows.
 __device__ bool explicit_usable(const Params& P, const Job& j) {
-  const unsigned* rec0 = P.rec + (size_t)(P.total_draft + j.prow) * P.chunks * P.rec_words;
-  int implicit = 0, ne = 0;
-  for (int ch = threadIdx.x; ch < P.chunks; ch += kThreads) {
-    const unsigned* h = rec0 + (size_t)ch * P.rec_words;
-    ne += min((int)h[0], P.kcap);
-    if ((h[3] & kRecFlagImplicitTies) && __uint_as_float(h[1]) >= j.thr_p) implicit = 1;
-  }
-  return block_sum_i(implicit) == 0 && block_sum_i(ne) <= kExplicitMax;
+  return P.kept[(size_t)j.prow * kKeptWords + 1] == 0u;
 }
 
 template <int DT>
@@ -908,22 +966,12 @@ __device__ int explicit_draw(const Params& P, const Job& j, float& Zout) {
   __shared__ int s_cnt;
   const int tid = threadIdx.x;
   const float c = P.c;
-  const unsigned* rec0 = P.rec + (size_t)(P.total_draft + j.prow) * P.chunks * P.rec_words;
-  if (tid == 0) s_cnt = 0;
+  const unsigned* kl = P.kept + (size_t)j.prow * kKeptWords;
+  if (tid == 0) s_cnt = (int)kl[0];
   __syncthreads();
-  for (int ch = 0; ch < P.chunks; ++ch) {
-    const unsigned* h = rec0 + (size_t)ch * P.rec_words;
-    const int ne = min((int)h[0], P.kcap);
-    for (int e = tid; e < ne; e += kThreads) {
-      const float v = __uint_as_float(h[kRecHeader + 2 * e]);
-      if (v >= j.thr_p) {
-        const int at = atomicAdd(&s_cnt, 1);
-        if (at < kExplicitMax) {
-          s_id[at] = (int)h[kRecHeader + 2 * e + 1];
-          s_lp[at] = v;
-        }
-      }
-    }
+  for (int x = tid; x < s_cnt; x += kThreads) {
+    s_lp[x] = __uint_as_float(kl[2 + 2 * x]);
+    s_id[x] = (int)kl[3 + 2 * x];
   }
   __syncthreads();
   const int n = min(s_cnt, kExplicitMax);
@@ -1037,8 +1085,25 @@ __device__ void draw_unit(const Params& P, int idx) {
     clear_partials(P, d0, kb, b, false);
     return;
   }
-  // filtered: draw from the candidate records when they list the kept set
-  if (P.filt && j.mode != kJobNone && explicit_usable(P, j)) {
+  // filtered: the kept lists of the sequence's target rows go back to zero
+  // once this block has counted itself, spread over the blocks of the
+  // sequence, except the list of the row drawn from (the last block clears it)
+  const bool lists = P.filt && P.kept != nullptr;
+  const int keep_row = j.mode != kJobNone ? j.prow : -1;
+  auto zero_list = [&](int row) {
+    unsigned* kl = P.kept + (size_t)row * kKeptWords;
+    const int words = 2 + 2 * (int)kl[0];
+    __syncthreads();  // every thread has read the count
+    for (int w = tid; w < words; w += kThreads) kl[w] = 0u;
+  };
+  auto zero_share = [&]() {
+    if (!lists) return;
+    for (int r = ch; r <= kb; r += P.dchunks)
+      if (d0 + b + r != keep_row) zero_list(d0 + b + r);
+  };
+  // filtered: draw from the kept list when it holds the whole kept set
+  const bool expl = lists && j.mode != kJobNone && explicit_usable(P, j);
+  if (expl) {
     if (ch == 0) {
       float Z;
       const int tok = explicit_draw<DT>(P, j, Z);
@@ -1048,9 +1113,7 @@ __device__ void draw_unit(const Params& P, int idx) {
         if (P.diag.resid_Z) pub_f(P.diag.resid_Z + b, Z);
       }
     }
-    return;
-  }
-  if (j.mode != kJobNone) {
+  } else if (j.mode != kJobNone) {
     // tile sums of slice ch of row pair n: the thread's vector k*kThreads + tid
     // of the slice belongs to tile ch*kTilesPerDraw + k
     const size_t prow = (size_t)j.prow * P.V;
@@ -1094,10 +1157,13 @@ __device__ void draw_unit(const Params& P, int idx) {
   __syncthreads();
   if (tid == 0) s_last = (bump(P.draw_done + b) == P.dchunks - 1) ? 1 : 0;
   __syncthreads();
-  if (!s_last) return;
+  if (!s_last) {
+    zero_share();
+    return;
+  }
   // Last block of the sequence: every other block has read the partials and
   // published its tile sums.
-  if (j.mode != kJobNone) {
+  if (j.mode != kJobNone && !expl) {
     float Z;
     const int tok = pick<DT, VEC>(P, b, j, Z);
     if (tid == 0) {
@@ -1109,6 +1175,15 @@ __device__ void draw_unit(const Params& P, int idx) {
   __syncthreads();
   // return the sequence's workspace entries to zero
   if (!P.filt) clear_partials(P, d0, kb, b, true);
+  if (P.filt) {
+    zero_share();
+    if (lists && keep_row >= 0) zero_list(keep_row);
+    // the per-row filter results every block of the sequence has read
+    for (int r = tid; r < 2 * kb + 1; r += kThreads) {
+      const long long u = r < kb ? unit_of(P, false, d0 + r) : unit_of(P, true, d0 + b + (r - kb));
+      P.rowres[u] = RowRes{0.f, 0.f, 0.f, 0};
+    }
+  }
   for (int t = tid; t < P.ntiles; t += kThreads) pub_f(P.tiles + (size_t)b * P.ntiles + t, 0.f);
   if (tid == 0) pub_i(P.draw_done + b, 0);
 }

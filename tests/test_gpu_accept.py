@@ -177,6 +177,7 @@ def test_accept_stats_edge_cases_and_workspace_reuse():
     assert math.isnan(e1[5]) and math.isnan(b1[int(cu[5]) + 1])
     b2, e2 = _gpu(w, "ragged", workspace=ws)
     assert np.array_equal(b1, b2, equal_nan=True) and np.array_equal(e1, e2, equal_nan=True)
+    assert int((ws != 0).sum()) == 0  # every entry back at zero
     # the workspace is back at zero: verification on it still matches the oracle
     w2 = W.make("bf16_B512_Kragged_V128256_halfgreedy", B=12, V=4096)
     toks = draft_tokens_from_oracle(w2)

@@ -378,3 +378,29 @@ def test_determinism_bitwise():
     b = run_gpu(w, toks, api="ragged", diag=True, dev=d)
     for k in a:
         np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def test_filtered_calls_return_workspace_to_zero():
+    """A call with top-k and top-p leaves every byte of its workspace at zero
+    (partials, counters, candidate records and per-row results), so a larger
+    unfiltered call can follow on the same workspace without a zero-fill; the
+    acceptance statistics with filters do the same."""
+    import speculative_decoding_verification_13_amd as sv
+    small = W.make(FILTERED, B=6, V=20000)
+    big = W.make(W.HEADLINE, B=8)
+    n = max(sv.workspace_bytes(w["B"], int(w["cu_draft"][-1]), w["V"], w["top_k"], w["top_p"])
+            for w in (small, big))
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    for w, api in ((small, "dense"), (small, "ragged"), (big, "dense")):
+        toks = draft_tokens_from_oracle(w)
+        _say(f"[gpu] shared workspace: {w['name']} B={w['B']} V={w['V']} api={api}")
+        rep = compare(w, toks, run_gpu(w, toks, api=api, workspace=ws), run_oracle(w, toks))
+        assert not rep["mismatches"], rep["mismatches"][:3]
+        torch.cuda.synchronize()
+        assert int((ws != 0).sum()) == 0, w["name"]
+    d = small["draft"].cuda()
+    t = small["target"].cuda()
+    sv.spec_verify_accept_stats(d, t, None, small["B"], small["V"], small["temperature"],
+                                small["top_k"], small["top_p"], workspace=ws)
+    torch.cuda.synchronize()
+    assert int((ws != 0).sum()) == 0
