@@ -75,9 +75,8 @@ typedef enum sv_dtype { SV_F32 = 0, SV_F16 = 1, SV_BF16 = 2 } sv_dtype;
                                 than spec_verify_workspace_bytes() */
 #define SV_EHIP (-4)         /* a HIP launch or event record failed */
 #define SV_EUNSUPPORTED (-5) /* valid request outside this build's limits:
-                                top_k above SV_MAX_TOP_K, top_p < 1 without
-                                an active top_k (0 < top_k < V), V above
-                                2^30, or a grid of more than 2^24 blocks */
+                                top_k above SV_MAX_TOP_K, V above 2^30, or
+                                a grid of more than 2^24 blocks */
 
 /* Per-sequence codes written to num_accepted[b] instead of a count. */
 #define SV_SEQ_BAD_TOKEN (-1)   /* a draft id outside [0, V) */
@@ -101,8 +100,10 @@ const char* spec_verify_strerror(int code);
 
 /* Bytes of device workspace a call with these sizes needs (the same value for
  * spec_verify with total_draft_rows = B*K). An active top_k (0 < top_k < V,
- * top_k <= SV_MAX_TOP_K) adds per-chunk candidate records; a workspace sized
- * with it also serves calls without filters. Returns 0 for invalid sizes. */
+ * top_k <= SV_MAX_TOP_K) adds per-chunk candidate records and per-row
+ * results, top_p < 1 alone per-row results; a workspace sized with an active
+ * top_k also serves calls with top-p alone or without filters. Returns 0 for
+ * invalid sizes. */
 size_t spec_verify_workspace_bytes(int B, int total_draft_rows, int V, int top_k,
                                    float top_p);
 
@@ -160,10 +161,10 @@ int spec_verify_ragged(const void* draft_logits, const void* target_logits,
  *   stage_events n_stage_events events recorded on `stream` before the first
  *                kernel and after each kernel of the call (for timing); events
  *                beyond the kernel count are recorded after the last kernel.
- *                Without filters the kernels are the row statistics pass and
- *                the decision-and-draw pass; with top-k a per-row filter pass
- *                (threshold and kept-set normaliser) runs between them;
- *                without filters both run in one kernel.
+ *                With filters the kernels are the row statistics pass, a
+ *                per-row filter pass (threshold and kept-set normaliser) and
+ *                the decision-and-draw pass; without filters all three run
+ *                in one kernel.
  *   spin_limit   bound of a wait for row statistics (0: default); a small
  *                value forces the SV_SEQ_SYNC_TIMEOUT path in tests. */
 typedef struct sv_diag {

@@ -59,12 +59,14 @@ int kcap_for(int top_k) { return (top_k + 256 + 63) / 64 * 64; }
 // differ from call to call. The regions are sized for the scalar path (one
 // element per vector), which has the most chunks: a row of nvec <= V vectors
 // never has more than cmax chunks.
-bool make_plan(int B, int total_draft, int V, int top_k, size_t ws_bytes, sv::Plan& L) {
+bool make_plan(int B, int total_draft, int V, int top_k, float top_p, size_t ws_bytes,
+               sv::Plan& L) {
   if (B < 0 || total_draft < 0 || V < 1 || V > kMaxV) return false;
   const long long rows = (long long)total_draft + B;
   if (rows > INT_MAX) return false;
   const size_t units = (size_t)(total_draft + rows);
   const bool filt = topk_active(V, top_k) && top_k <= SV_MAX_TOP_K;
+  const bool row_results = filt || top_p < 1.0f;
   long long cmax;
   if (filt) {
     cmax = ((long long)V + sv::kFiltChunkVecs - 1) / sv::kFiltChunkVecs;
@@ -89,22 +91,24 @@ bool make_plan(int B, int total_draft, int V, int top_k, size_t ws_bytes, sv::Pl
   off += align_up((size_t)total_draft * (size_t)cmax * 4);
   L.off_beta_cnt = off;
   off += align_up((size_t)total_draft * 4);
-  L.off_rec = L.off_rowres = off;
+  L.off_rec = L.off_rowres = L.off_kept = off;
   if (filt) {
     const size_t rec_words = sv::kRecHeader + 2 * (size_t)kcap_for(top_k);
     off += align_up(units * (size_t)cmax * rec_words * 4);
-    L.off_rowres = off;
-    off += align_up(units * sizeof(sv::RowRes));
     L.off_kept = off;
     off += align_up((size_t)rows * sv::kKeptWords * 4);
+  }
+  if (row_results) {
+    L.off_rowres = off;
+    off += align_up(units * sizeof(sv::RowRes));
   }
   L.total_bytes = off;
   return off <= ws_bytes;
 }
 
-size_t required_bytes(int B, int total_draft, int V, int top_k) {
+size_t required_bytes(int B, int total_draft, int V, int top_k, float top_p) {
   sv::Plan L;
-  if (!make_plan(B, total_draft, V, top_k, SIZE_MAX, L)) return 0;
+  if (!make_plan(B, total_draft, V, top_k, top_p, SIZE_MAX, L)) return 0;
   return L.total_bytes > 0 ? L.total_bytes : kAlign;
 }
 
@@ -127,14 +131,16 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
   if (total_draft > 0 && tokens == nullptr) return SV_EINVAL;
   if (total_draft > 0 && !all_greedy && draft == nullptr) return SV_EINVAL;
   if (!all_greedy && uniforms == nullptr) return SV_EINVAL;
-  // Filters act on sampling rows through top-k; top-p alone (no top-k) is not
-  // in this build.
+  // Filters act on sampling rows: top-k (then top-p) through candidate records,
+  // top-p alone through a radix descent over each whole row.
   const bool filt = !all_greedy && filters_active(V, top_k, top_p);
-  if (filt && (!topk_active(V, top_k) || top_k > SV_MAX_TOP_K)) return SV_EUNSUPPORTED;
+  const bool topk = filt && topk_active(V, top_k);
+  if (topk && top_k > SV_MAX_TOP_K) return SV_EUNSUPPORTED;
   sv::Plan L;
-  if (!make_plan(B, total_draft, V, filt ? top_k : 0, SIZE_MAX, L)) return SV_EUNSUPPORTED;
+  if (!make_plan(B, total_draft, V, topk ? top_k : 0, filt ? top_p : 1.0f, SIZE_MAX, L))
+    return SV_EUNSUPPORTED;
   if (workspace == nullptr || ((uintptr_t)workspace % kAlign) != 0 ||
-      !make_plan(B, total_draft, V, filt ? top_k : 0, workspace_bytes, L))
+      !make_plan(B, total_draft, V, topk ? top_k : 0, filt ? top_p : 1.0f, workspace_bytes, L))
     return SV_EWORKSPACE;
 
   const int es = esize_of(dtype);
@@ -156,7 +162,7 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
   P.all_greedy = all_greedy ? 1 : 0;
   P.c = all_greedy ? 0.0f : (float)(1.4426950408889634074 / (double)temperature);
   P.nvec = vec ? V / n_per_vec : V;
-  P.chunk_vecs = filt ? sv::kFiltChunkVecs : (int)chunk_vecs_for(P.nvec);
+  P.chunk_vecs = topk ? sv::kFiltChunkVecs : (int)chunk_vecs_for(P.nvec);
   P.chunks = (P.nvec + P.chunk_vecs - 1) / P.chunk_vecs;
   P.dchunks = (P.nvec + sv::kDrawVecs - 1) / sv::kDrawVecs;
   // unfiltered rows of at most kMaxDrawSlices slices run as one kernel
@@ -165,16 +171,17 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
   // greedy-only calls skip the draft rows
   P.stats_block0 = all_greedy ? (long long)total_draft * P.chunks : 0;
   P.filt = filt ? 1 : 0;
+  P.nucleus = (filt && !topk) ? 1 : 0;
   P.top_k = top_k;
   P.top_p = top_p;
-  P.kcap = filt ? kcap_for(top_k) : 0;
+  P.kcap = topk ? kcap_for(top_k) : 0;
   P.rec_words = sv::kRecHeader + 2 * P.kcap;
   P.out_tokens = out_tokens;
   P.num_accepted = num_accepted;
   char* ws = static_cast<char*>(workspace);
-  P.rec = filt ? reinterpret_cast<unsigned*>(ws + L.off_rec) : nullptr;
+  P.rec = topk ? reinterpret_cast<unsigned*>(ws + L.off_rec) : nullptr;
   P.rowres = filt ? reinterpret_cast<sv::RowRes*>(ws + L.off_rowres) : nullptr;
-  P.kept = filt ? reinterpret_cast<unsigned*>(ws + L.off_kept) : nullptr;
+  P.kept = topk ? reinterpret_cast<unsigned*>(ws + L.off_kept) : nullptr;
   P.slots = reinterpret_cast<unsigned long long*>(ws + L.off_slots);
   P.tiles = reinterpret_cast<float*>(ws + L.off_tiles);
   P.draws = reinterpret_cast<unsigned long long*>(ws + L.off_draws);
@@ -251,11 +258,13 @@ int run_accept(const void* draft, const void* target, const int32_t* cu, int B, 
   if (target == nullptr || expected == nullptr) return SV_EINVAL;
   if (total_draft > 0 && (draft == nullptr || beta == nullptr)) return SV_EINVAL;
   const bool filt = filters_active(V, top_k, top_p);
-  if (filt && (!topk_active(V, top_k) || top_k > SV_MAX_TOP_K)) return SV_EUNSUPPORTED;
+  const bool topk = filt && topk_active(V, top_k);
+  if (topk && top_k > SV_MAX_TOP_K) return SV_EUNSUPPORTED;
   sv::Plan L;
-  if (!make_plan(B, total_draft, V, filt ? top_k : 0, SIZE_MAX, L)) return SV_EUNSUPPORTED;
+  if (!make_plan(B, total_draft, V, topk ? top_k : 0, top_p, SIZE_MAX, L))
+    return SV_EUNSUPPORTED;
   if (workspace == nullptr || ((uintptr_t)workspace % kAlign) != 0 ||
-      !make_plan(B, total_draft, V, filt ? top_k : 0, workspace_bytes, L))
+      !make_plan(B, total_draft, V, topk ? top_k : 0, top_p, workspace_bytes, L))
     return SV_EWORKSPACE;
   const int es = esize_of(dtype);
   const bool vec = ((size_t)V * es) % 16 == 0 && aligned16(target) &&
@@ -271,15 +280,16 @@ int run_accept(const void* draft, const void* target, const int32_t* cu, int B, 
   P.rows = total_draft + B;
   P.c = (float)(1.4426950408889634074 / (double)temperature);
   P.nvec = vec ? V / (16 / es) : V;
-  P.chunk_vecs = filt ? sv::kFiltChunkVecs : (int)chunk_vecs_for(P.nvec);
+  P.chunk_vecs = topk ? sv::kFiltChunkVecs : (int)chunk_vecs_for(P.nvec);
   P.chunks = (P.nvec + P.chunk_vecs - 1) / P.chunk_vecs;
   P.filt = filt ? 1 : 0;
+  P.nucleus = (filt && !topk) ? 1 : 0;
   P.top_k = top_k;
   P.top_p = top_p;
-  P.kcap = filt ? kcap_for(top_k) : 0;
+  P.kcap = topk ? kcap_for(top_k) : 0;
   P.rec_words = sv::kRecHeader + 2 * P.kcap;
   char* ws = static_cast<char*>(workspace);
-  P.rec = filt ? reinterpret_cast<unsigned*>(ws + L.off_rec) : nullptr;
+  P.rec = topk ? reinterpret_cast<unsigned*>(ws + L.off_rec) : nullptr;
   P.rowres = filt ? reinterpret_cast<sv::RowRes*>(ws + L.off_rowres) : nullptr;
   P.slots = reinterpret_cast<unsigned long long*>(ws + L.off_slots);
   P.skip_bonus = 1;
@@ -316,7 +326,7 @@ const char* spec_verify_strerror(int code) {
 
 size_t spec_verify_workspace_bytes(int B, int total_draft_rows, int V, int top_k, float top_p) {
   (void)top_p;
-  return required_bytes(B, total_draft_rows, V, top_k);
+  return required_bytes(B, total_draft_rows, V, top_k, top_p);
 }
 
 int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {

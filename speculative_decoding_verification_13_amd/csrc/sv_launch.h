@@ -94,7 +94,8 @@ struct Params {
   long long stats_blocks;  // stats blocks launched
   int spin_limit;          // bound of every wait (iterations)
   int full_wait;           // 1: decisions read every row (side outputs requested)
-  int filt;                // 1: top-k (and top-p) filters active
+  int filt;                // 1: filters active (rows carry kept-set results)
+  int nucleus;             // 1: top-p without top-k (no candidate records)
   int top_k;
   float top_p;
   int kcap;                // (value, id) pairs per chunk record

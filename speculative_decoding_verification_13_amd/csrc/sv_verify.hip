@@ -934,6 +934,157 @@ __global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
   zero_records(P, C, [&](int ch) { return recw + (size_t)ch * P.rec_words; });
 }
 
+// ---------------------------------------------------------------- k_nucleus
+// One block per sampling row when top-p acts without top-k: the row's
+// threshold theta (keep l >= theta) and the kept-set sum, found by a radix
+// descent on order-preserving keys. Each pass adds every logit's mass
+// 2^(l*c - R), in 40-bit fixed point (integer sums: exact and independent of
+// the order of addition), to the bin of its next key digit among the logits
+// whose higher digits match the levels fixed so far. Walking the bins from the
+// largest key down, the kept levels are those whose strictly-larger mass is
+// below top_p times the total; the last of them lies in the bin where the
+// running mass, this bin included, first reaches that bound. Digits of 12, 11
+// and 9 bits: two passes resolve a level of a widened bf16 or fp16 logit (the
+// key's low bits are then constant), three a level of an fp32 one. The row's
+// chunk partials (read here only) go back to zero.
+// Pages: aihero.vn "Speculative decoding", section "Cùng phân bố không có
+// nghĩa cùng chuỗi mỗi lần" (the same temperature, top-k and top-p on both
+// models' rows).
+constexpr int kNucBins = 4096;
+constexpr double kNucScale = 1099511627776.0;  // 2^40
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_nucleus(const Params P) {
+  using Vc = Vec<DT, VEC>;
+  constexpr int N = Vc::N;
+  __shared__ unsigned long long s_hist[kNucBins];
+  __shared__ unsigned long long s_wave[kThreads / kWave];
+  __shared__ unsigned long long s_base;
+  __shared__ int s_cu[kCuLds];
+  __shared__ float s_stat[2];
+  __shared__ int s_bin;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int unit = blockIdx.x;
+  const bool is_target = unit >= P.total_draft;
+  const int row = is_target ? unit - P.total_draft : unit;
+  if (P.greedy != nullptr && P.greedy[row_seq(P, row, is_target, s_cu)] != 0) return;
+  if (P.skip_bonus && is_target && is_bonus_row(P, row, s_cu)) return;
+  const int C = P.chunks;
+  const float c = P.c;
+  unsigned long long* sl = P.slots + (size_t)unit * C;
+  if (tid == 0) {
+    float m = kNegInf, sm = 0.f;
+    for (int k = 0; k < C; ++k) {
+      float om, os;
+      unpack_ms(sl[k], om, os);
+      merge_ms(m, sm, om, os, c);
+    }
+    s_stat[0] = m;
+    s_stat[1] = sm;
+  }
+  __syncthreads();
+  for (int k = tid; k < C; k += kThreads) sl[k] = 0ull;
+  const float m = s_stat[0];
+  const bool ok = __builtin_isfinite(m) && s_stat[1] > 0.f && __builtin_isfinite(s_stat[1]);
+  const float R = ref_of(m, c);
+  const size_t roff = (size_t)row * P.V;
+  const void* base = is_target ? P.target : P.draft;
+  constexpr int kLevels = (DT == SV_F32) ? 3 : 2;
+  const int shifts[3] = {20, 9, 0};
+  const int widths[3] = {12, 11, 9};
+  unsigned prefix = 0u, pmask = 0u;
+  unsigned long long above = 0ull, kept = 0ull;
+  double bound = 0.0;
+  for (int lv = 0; ok && lv < kLevels; ++lv) {
+    const int shift = shifts[lv], nb = 1 << widths[lv];
+    for (int x = tid; x < nb; x += kThreads) s_hist[x] = 0ull;
+    __syncthreads();
+    auto add = [&](float l) {
+      const unsigned key = key_of(l);
+      if ((key & pmask) != prefix || !(l > kNegInf)) return;
+      const float w = fast_exp2(fmaf(l, c, -R));
+      atomicAdd(&s_hist[(key >> shift) & (unsigned)(nb - 1)],
+                (unsigned long long)(w * (float)kNucScale));
+    };
+    int v = tid;
+    for (; v + (kBatch - 1) * kThreads < P.nvec; v += kBatch * kThreads) {
+      typename Vc::Raw r[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) r[u] = Vc::load(base, roff, v + u * kThreads);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        float f[N];
+        Vc::get(r[u], f);
+#pragma unroll
+        for (int k = 0; k < N; ++k) add(f[k]);
+      }
+    }
+    for (; v < P.nvec; v += kThreads) {
+      float f[N];
+      Vc::get(Vc::load(base, roff, v), f);
+#pragma unroll
+      for (int k = 0; k < N; ++k) add(f[k]);
+    }
+    __syncthreads();
+    // thread t sums a run of bins in descending key order, then an exclusive
+    // scan over the threads gives the mass above each run
+    const int per = nb / kThreads;
+    const int top = nb - 1 - tid * per;
+    unsigned long long run = 0ull;
+    for (int k = 0; k < per; ++k) run += s_hist[top - k];
+    unsigned long long incl = run;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const unsigned long long y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == kWave - 1) s_wave[tid / kWave] = incl;
+    if (tid == 0) s_bin = -1;
+    __syncthreads();
+    unsigned long long before = 0ull, total = 0ull;
+    for (int w = 0; w < kThreads / kWave; ++w) {
+      if (w < tid / kWave) before += s_wave[w];
+      total += s_wave[w];
+    }
+    if (lv == 0) bound = (double)P.top_p * (double)total;
+    unsigned long long acc = above + before + (incl - run);
+    for (int k = 0; k < per; ++k) {
+      const unsigned long long h = s_hist[top - k];
+      // the strictly-larger mass acc is below the bound and the running mass
+      // reaches it in this bin: the last kept level lies here
+      if ((double)acc < bound && (double)(acc + h) >= bound) {
+        s_bin = top - k;
+        s_base = acc;
+      }
+      acc += h;
+    }
+    __syncthreads();
+    if (s_bin < 0) break;  // the bound lies past every level: all are kept
+    prefix |= (unsigned)s_bin << shift;
+    pmask |= (unsigned)(nb - 1) << shift;
+    above = s_base;
+    kept = s_base + s_hist[s_bin];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    RowRes rr;
+    rr.m = m;
+    rr.flags = ok ? 0 : 1;
+    if (!ok || pmask == 0u) {
+      rr.theta = kNegInf;  // every level kept
+      rr.s = s_stat[1];
+    } else {
+      // the level's low key bits are constant below the resolved digits
+      const unsigned lowmask = ~pmask;
+      const unsigned key = prefix | ((prefix & 0x80000000u) ? 0u : lowmask);
+      rr.theta = float_of_key(key);
+      rr.s = (float)((double)kept / kNucScale);
+    }
+    P.rowres[unit] = rr;
+  }
+}
+
 // Returns the partials of a sequence's rows to zero (whole block): its target
 // rows and, with_draft, its draft rows.
 __device__ void clear_partials(const Params& P, int d0, int kb, int b, bool with_draft) {
@@ -1214,11 +1365,19 @@ static hipError_t launch_t(const Params& P, const Plan& L, hipStream_t s, hipEve
   int e = 0;
   if ((err = stage_event(ev, nev, e++, s)) != hipSuccess) return err;
   if (P.filt) {
-    hipLaunchKernelGGL((k_stats<DT, VEC, true>), dim3((unsigned)L.stats_blocks), dim3(kThreads), 0,
-                       s, P);
+    if (P.nucleus)
+      hipLaunchKernelGGL((k_stats<DT, VEC, false>), dim3((unsigned)L.stats_blocks), dim3(kThreads),
+                         0, s, P);
+    else
+      hipLaunchKernelGGL((k_stats<DT, VEC, true>), dim3((unsigned)L.stats_blocks), dim3(kThreads),
+                         0, s, P);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if ((err = stage_event(ev, nev, e++, s)) != hipSuccess) return err;
-    hipLaunchKernelGGL(k_filter, dim3((unsigned)L.filter_blocks), dim3(kThreads), 0, s, P);
+    if (P.nucleus)
+      hipLaunchKernelGGL((k_nucleus<DT, VEC>), dim3((unsigned)L.filter_blocks), dim3(kThreads), 0,
+                         s, P);
+    else
+      hipLaunchKernelGGL(k_filter, dim3((unsigned)L.filter_blocks), dim3(kThreads), 0, s, P);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if ((err = stage_event(ev, nev, e++, s)) != hipSuccess) return err;
   } else {
@@ -1248,7 +1407,14 @@ hipError_t launch(int dtype, bool vec, const Params& P, const Plan& L, hipStream
 
 template <int DT, bool VEC>
 static hipError_t launch_row_stats_t(const Params& P, const Plan& L, hipStream_t s) {
-  if (P.filt) {
+  if (P.nucleus) {
+    hipLaunchKernelGGL((k_stats<DT, VEC, false>), dim3((unsigned)L.stats_blocks), dim3(kThreads),
+                       0, s, P);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((k_nucleus<DT, VEC>), dim3((unsigned)L.filter_blocks), dim3(kThreads), 0, s,
+                       P);
+  } else if (P.filt) {
     hipLaunchKernelGGL((k_stats<DT, VEC, true>), dim3((unsigned)L.stats_blocks), dim3(kThreads), 0,
                        s, P);
     hipError_t err = hipGetLastError();

@@ -79,8 +79,8 @@ def _dense(L, **kw):
     (dict(tokens=None), -1), (dict(draft=None), -1), (dict(uniforms=None), -1),
     (dict(ws=None), -3), (dict(ws=ctypes.c_void_p(0x10010)), -3), (dict(), -3),
     (dict(top_k=2000, V=4096), -5),
-    (dict(top_k=0, top_p=0.9, V=4096), -5),  # top-p without top-k
-    (dict(top_k=4096, top_p=0.9, V=4096), -5),  # top-k off (k >= V), top-p on
+    (dict(top_k=0, top_p=0.9, V=4096), -3),  # top-p without top-k: reaches the workspace check
+    (dict(top_k=4096, top_p=0.9, V=4096), -3),  # top-k off (k >= V), top-p on
 ])
 def test_dense_argument_errors(L, kw, code):
     assert _dense(L, **kw) == code
@@ -131,6 +131,8 @@ def test_workspace_sizes(L):
     assert ws(64, 512, 128256, 50, 0.9) > ws(64, 512, 128256, 0, 1.0)
     assert ws(64, 512, 128256, 1024, 1.0) > ws(64, 512, 128256, 50, 1.0)
     assert ws(64, 512, 128256, 128256, 1.0) == ws(64, 512, 128256, 0, 1.0)  # k >= V: off
+    # top-p alone adds per-row results only; top-k's layout covers it
+    assert ws(64, 512, 128256, 0, 1.0) < ws(64, 512, 128256, 0, 0.9) < ws(64, 512, 128256, 50, 0.9)
     assert L.spec_verify_num_stages(0, 1.0) >= 1
 
 
@@ -154,5 +156,6 @@ def test_accept_stats_argument_errors(L):
     assert acc(target=None) == -1 and acc(exp=None) == -1
     assert acc(draft=None) == -1 and acc(beta=None) == -1
     assert acc(draft=None, beta=None, total=0) == -3  # no draft rows: neither is read
-    assert acc(top_k=0, top_p=0.9) == -5
+    assert acc(top_k=0, top_p=0.9) == -3  # top-p alone is supported
+    assert acc(top_k=2000, V=4096) == -5  # top_k above SV_MAX_TOP_K
     assert acc(B=0, draft=None, target=None, cu=None, beta=None, exp=None, ws=None) == 0

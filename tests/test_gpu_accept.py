@@ -101,12 +101,17 @@ SMALL = [
     ("bf16_B512_Kragged_V128256_halfgreedy", dict(B=20), "ragged"),
     ("f16_B256_K4_V151936_topk50_topp0.9", dict(B=6), "dense"),
     ("f16_B256_K4_V151936_topk50_topp0.9", dict(B=6, V=1000), "ragged"),  # scalar tail
+    ("f16_B256_K4_V151936_topk50_topp0.9", dict(B=6, V=20000, top_k=0), "dense"),  # top-p alone
 ]
 
 
 @pytest.mark.parametrize("name,ov,api", SMALL, ids=[f"{n}-{i}" for i, (n, _, _) in enumerate(SMALL)])
 def test_accept_stats_parity(name, ov, api):
+    ov = dict(ov)
+    top_k = ov.pop("top_k", None)
     w = W.make(name, **ov)
+    if top_k is not None:
+        w["top_k"] = top_k
     if w["temperature"] == 0.0:
         pytest.skip("greedy workload")
     _say(f"[gpu] accept {w['name']} B={w['B']} V={w['V']} dtype={w['dtype']} api={api}")

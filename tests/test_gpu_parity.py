@@ -93,6 +93,17 @@ def test_filters_settings(top_k, top_p):
            tag=f"k={top_k} p={top_p}")
 
 
+@pytest.mark.parametrize("top_p,dtype,V", [(0.9, "f16", 20000), (0.5, "bf16", 20000),
+                                         (0.99, "f16", 20000), (0.8, "f32", 4099),
+                                         (0.95, "bf16", 151936)])
+def test_top_p_without_top_k(top_p, dtype, V):
+    """top-p alone over the whole row (radix descent on the logit keys), on
+    the vector and scalar paths, through the diag and the dense entry points."""
+    w = _filtered(0, top_p, B=6, V=V, dtype=dtype)
+    _check(w, api="ragged", diag=True, tag=f"p={top_p} {dtype}")
+    _check(w, api="dense", diag=False, tag=f"p={top_p} {dtype}")
+
+
 @pytest.mark.parametrize("top_k", [257, 1024])
 def test_filters_large_k_exact_select(top_k):
     """k beyond the per-thread bound: every chunk is cut by the exact select."""
@@ -400,7 +411,14 @@ def test_filtered_calls_return_workspace_to_zero():
         assert int((ws != 0).sum()) == 0, w["name"]
     d = small["draft"].cuda()
     t = small["target"].cuda()
-    sv.spec_verify_accept_stats(d, t, None, small["B"], small["V"], small["temperature"],
-                                small["top_k"], small["top_p"], workspace=ws)
+    for top_k in (small["top_k"], 0):  # top-k then top-p, and top-p alone
+        sv.spec_verify_accept_stats(d, t, None, small["B"], small["V"], small["temperature"],
+                                    top_k, small["top_p"], workspace=ws)
+        torch.cuda.synchronize()
+        assert int((ws != 0).sum()) == 0
+    tp = _filtered(0, 0.9, B=6, V=20000)
+    toks = draft_tokens_from_oracle(tp)
+    rep = compare(tp, toks, run_gpu(tp, toks, api="ragged", workspace=ws), run_oracle(tp, toks))
+    assert not rep["mismatches"], rep["mismatches"][:3]
     torch.cuda.synchronize()
     assert int((ws != 0).sum()) == 0
