@@ -943,14 +943,14 @@ __global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
 // whose higher digits match the levels fixed so far. Walking the bins from the
 // largest key down, the kept levels are those whose strictly-larger mass is
 // below top_p times the total; the last of them lies in the bin where the
-// running mass, this bin included, first reaches that bound. Digits of 12, 11
-// and 9 bits: two passes resolve a level of a widened bf16 or fp16 logit (the
+// running mass, this bin included, first reaches that bound. Digits of 11, 11
+// and 10 bits: two passes resolve a level of a widened bf16 or fp16 logit (the
 // key's low bits are then constant), three a level of an fp32 one. The row's
 // chunk partials (read here only) go back to zero.
 // Pages: aihero.vn "Speculative decoding", section "Cùng phân bố không có
 // nghĩa cùng chuỗi mỗi lần" (the same temperature, top-k and top-p on both
 // models' rows).
-constexpr int kNucBins = 4096;
+constexpr int kNucBins = 2048;
 constexpr double kNucScale = 1099511627776.0;  // 2^40
 
 template <int DT, bool VEC>
@@ -991,8 +991,8 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(const Params P) {
   const size_t roff = (size_t)row * P.V;
   const void* base = is_target ? P.target : P.draft;
   constexpr int kLevels = (DT == SV_F32) ? 3 : 2;
-  const int shifts[3] = {20, 9, 0};
-  const int widths[3] = {12, 11, 9};
+  const int shifts[3] = {21, 10, 0};
+  const int widths[3] = {11, 11, 10};
   unsigned prefix = 0u, pmask = 0u;
   unsigned long long above = 0ull, kept = 0ull;
   double bound = 0.0;
@@ -1001,17 +1001,21 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(const Params P) {
     for (int x = tid; x < nb; x += kThreads) s_hist[x] = 0ull;
     __syncthreads();
     auto add = [&](float l) {
+      // a mass below 2^-40 is zero in the fixed point: skipped before any
+      // further work (as are -inf and NaN)
+      const float x = fmaf(l, c, -R);
+      if (!(x >= -40.0f)) return;
       const unsigned key = key_of(l);
-      if ((key & pmask) != prefix || !(l > kNegInf)) return;
-      const float w = fast_exp2(fmaf(l, c, -R));
+      if ((key & pmask) != prefix) return;
       atomicAdd(&s_hist[(key >> shift) & (unsigned)(nb - 1)],
-                (unsigned long long)(w * (float)kNucScale));
+                (unsigned long long)(fast_exp2(x) * (float)kNucScale));
     };
     int v = tid;
     for (; v + (kBatch - 1) * kThreads < P.nvec; v += kBatch * kThreads) {
       typename Vc::Raw r[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) r[u] = Vc::load(base, roff, v + u * kThreads);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         float f[N];
