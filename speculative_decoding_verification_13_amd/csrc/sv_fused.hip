@@ -66,6 +66,14 @@ struct DrawShared {
   int flags;    // the sequence's kSeqFlag bits, read by the last block
 };
 
+// Draw weight of one id for rows without a filter: max(0, p - q) for the
+// residual, p for the bonus (every id is in both kept sets).
+__device__ __forceinline__ float weight(float lp, float lq, const Job& j, float c) {
+  const float ep = fast_exp2(fmaf(lp, c, -j.Rp));
+  if (j.mode == kJobBonus) return ep * j.invSp;
+  return fmaxf(fmaf(ep, j.invSp, -fast_exp2(fmaf(lq, c, -j.Rq)) * j.invSq), 0.0f);
+}
+
 __device__ __forceinline__ unsigned long long tag_sum(float z) {
   return (1ull << 63) | (unsigned long long)__float_as_uint(z);
 }
@@ -94,7 +102,7 @@ __device__ __forceinline__ float slice_weights(const Raw (&rp)[kTilesPerDraw],
       }
       float sum = 0.f;
 #pragma unroll
-      for (int e = 0; e < N; ++e) sum += draw_weight(fp[e], fq[e], j, c);
+      for (int e = 0; e < N; ++e) sum += weight(fp[e], fq[e], j, c);
       ts[k] = sum;
     }
   }
@@ -220,7 +228,7 @@ __device__ int slice_draw(const Params& P, Job j, int b, int s, float& Z, int& t
   float acc = 0.f;
 #pragma unroll
   for (int e = 0; e < N; ++e) {
-    acc += (v < P.nvec) ? draw_weight(fp[e], fq[e], j, P.c) : 0.f;
+    acc += (v < P.nvec) ? weight(fp[e], fq[e], j, P.c) : 0.f;
     w[e] = acc;
   }
   float total;
@@ -561,8 +569,14 @@ __device__ void stats_block(const Params& P, long long g) {
   if (threadIdx.x == 0) pub_u64(P.slots + unit_of(P, is_target, row) * P.chunks + ch, packed);
 }
 
+// Waves per SIMD asked of the compiler: bf16 and fp32 rows fit 64 VGPRs
+// without spills (eight blocks per compute unit); fp16 rows, whose unpacking
+// costs more registers, are left to the compiler.
+template <int DT>
+constexpr int kVerifyWaves = DT == SV_BF16 ? 8 : (DT == SV_F32 ? 7 : 1);
+
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_verify(const Params P) {
+__global__ __launch_bounds__(kThreads, kVerifyWaves<DT>) void k_verify(const Params P) {
   // Grid order: statistics blocks up to draw_at, the draw blocks, the remaining
   // statistics blocks (one call site per block kind, so both inline).
   long long g = blockIdx.x;
