@@ -564,8 +564,12 @@ __device__ void stats_block(const Params& P, long long g) {
   if (greedy && !is_target) return;  // greedy sequences never read draft rows
   const void* base = is_target ? P.target : P.draft;
   const int vb = ch * P.chunk_vecs;
+  // Position 0's rows are the ones draws re-read most often (most rejections
+  // come first): ordinary loads leave them in the last-level cache; the rest
+  // stream.
+  const bool first = P.cu == nullptr && (is_target ? row % (P.K + 1) : row % max(P.K, 1)) == 0;
   const unsigned long long packed = chunk_stats<DT, VEC>(
-      P, base, (size_t)row * (size_t)P.V, vb, min(P.nvec, vb + P.chunk_vecs), greedy);
+      P, base, (size_t)row * (size_t)P.V, vb, min(P.nvec, vb + P.chunk_vecs), greedy, !first);
   if (threadIdx.x == 0) pub_u64(P.slots + unit_of(P, is_target, row) * P.chunks + ch, packed);
 }
 

@@ -163,10 +163,11 @@ __device__ __forceinline__ bool is_bonus_row(const Params& P, int row, int* s_cu
 // the argmax (lowest id on ties) and whether the chunk holds NaN or +inf, for a
 // sampling row the maximum m and the sum of 2^(l*c - R), R = fp32(m*c).
 // Returns the packed partial in thread 0 (0 elsewhere). The loads are streamed
-// (each logit is read once).
+// (non-temporal) unless `stream` is false: rows a draw is likely to read again
+// keep the ordinary cache policy.
 template <int DT, bool VEC>
 __device__ unsigned long long chunk_stats(const Params& P, const void* base, size_t roff, int vb,
-                                          int ve, bool greedy) {
+                                          int ve, bool greedy, bool stream = true) {
   using Vc = Vec<DT, VEC>;
   constexpr int N = Vc::N;
   __shared__ float4 s_part[kThreads / kWave];
@@ -180,8 +181,13 @@ __device__ unsigned long long chunk_stats(const Params& P, const void* base, siz
     int bi = INT_MAX, bad = 0;
     for (; v + (kBatch - 1) * kThreads < ve; v += kBatch * kThreads) {
       typename Vc::Raw r[kBatch];
+      if (stream) {
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) r[u] = Vc::load_stream(base, roff, v + u * kThreads);
+        for (int u = 0; u < kBatch; ++u) r[u] = Vc::load_stream(base, roff, v + u * kThreads);
+      } else {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) r[u] = Vc::load(base, roff, v + u * kThreads);
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
@@ -224,8 +230,13 @@ __device__ unsigned long long chunk_stats(const Params& P, const void* base, siz
     float m = kNegInf, s = 0.f;
     for (; v + (kBatch - 1) * kThreads < ve; v += kBatch * kThreads) {
       typename Vc::Raw r[kBatch];
+      if (stream) {
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) r[u] = Vc::load_stream(base, roff, v + u * kThreads);
+        for (int u = 0; u < kBatch; ++u) r[u] = Vc::load_stream(base, roff, v + u * kThreads);
+      } else {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) r[u] = Vc::load(base, roff, v + u * kThreads);
+      }
       __builtin_amdgcn_sched_barrier(0);
       float f[kBatch * N];
 #pragma unroll
