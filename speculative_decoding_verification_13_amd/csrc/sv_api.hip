@@ -21,12 +21,12 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int esize_of(int dtype) { return dtype == SV_F32 ? 4 : 2; }
 
-// Vectors per stats block for rows of nvec vectors: kChunkSteps batches, grown
+// Vectors per stats block for rows of nvec vectors: min_steps batches, grown
 // so that no row has more than kMaxChunks chunks.
-long long chunk_vecs_for(long long nvec) {
+long long chunk_vecs_for(long long nvec, int min_steps) {
   const long long per = (long long)sv::kStepVecs * sv::kMaxChunks;
   long long steps = (nvec + per - 1) / per;
-  if (steps < sv::kChunkSteps) steps = sv::kChunkSteps;
+  if (steps < min_steps) steps = min_steps;
   return steps * sv::kStepVecs;
 }
 
@@ -162,11 +162,13 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
   P.all_greedy = all_greedy ? 1 : 0;
   P.c = all_greedy ? 0.0f : (float)(1.4426950408889634074 / (double)temperature);
   P.nvec = vec ? V / n_per_vec : V;
-  P.chunk_vecs = topk ? sv::kFiltChunkVecs : (int)chunk_vecs_for(P.nvec);
-  P.chunks = (P.nvec + P.chunk_vecs - 1) / P.chunk_vecs;
   P.dchunks = (P.nvec + sv::kDrawVecs - 1) / sv::kDrawVecs;
-  // unfiltered rows of at most kMaxDrawSlices slices run as one kernel
+  // unfiltered rows of at most kMaxDrawSlices slices run as one kernel (with
+  // larger statistics chunks)
   L.fused = !filt && P.dchunks <= sv::kMaxDrawSlices;
+  P.chunk_vecs = topk ? sv::kFiltChunkVecs
+                      : (int)chunk_vecs_for(P.nvec, L.fused ? sv::kFusedChunkSteps : sv::kChunkSteps);
+  P.chunks = (P.nvec + P.chunk_vecs - 1) / P.chunk_vecs;
   P.ntiles = P.dchunks * sv::kTilesPerDraw;
   // greedy-only calls skip the draft rows
   P.stats_block0 = all_greedy ? (long long)total_draft * P.chunks : 0;
@@ -280,7 +282,7 @@ int run_accept(const void* draft, const void* target, const int32_t* cu, int B, 
   P.rows = total_draft + B;
   P.c = (float)(1.4426950408889634074 / (double)temperature);
   P.nvec = vec ? V / (16 / es) : V;
-  P.chunk_vecs = topk ? sv::kFiltChunkVecs : (int)chunk_vecs_for(P.nvec);
+  P.chunk_vecs = topk ? sv::kFiltChunkVecs : (int)chunk_vecs_for(P.nvec, sv::kChunkSteps);
   P.chunks = (P.nvec + P.chunk_vecs - 1) / P.chunk_vecs;
   P.filt = filt ? 1 : 0;
   P.nucleus = (filt && !topk) ? 1 : 0;

@@ -16,10 +16,8 @@ constexpr int kTileVecs = kThreads;       // draw tile = one vector per thread
 constexpr int kStepVecs = kBatch * kThreads;  // vectors of a row one batch covers
 constexpr int kDrawVecs = kStepVecs;      // vectors of each row per draw block
 constexpr int kTilesPerDraw = kDrawVecs / kTileVecs;
-#ifndef SV_CHUNK_STEPS
-#define SV_CHUNK_STEPS 4
-#endif
-constexpr int kChunkSteps = SV_CHUNK_STEPS;  // batches per stats block (64 KB of bf16)
+constexpr int kChunkSteps = 4;            // batches per stats block (64 KB of bf16)
+constexpr int kFusedChunkSteps = 8;       // the same in the one-kernel step (128 KB)
 constexpr int kMaxChunks = 64;            // stats chunks per row (larger rows take
                                           // larger chunks)
 // Filtered rows (top-k): a stats block keeps its whole chunk in registers.
