@@ -6,6 +6,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "spec_verify.h"
@@ -71,10 +72,11 @@ bool make_plan(int B, int total_draft, int V, int top_k, float top_p, size_t ws_
   if (filt) {
     cmax = ((long long)V + sv::kFiltChunkVecs - 1) / sv::kFiltChunkVecs;
   } else {
-    const long long base = (long long)sv::kStepVecs * sv::kChunkSteps;
-    cmax = ((long long)V + base - 1) / base;
+    // the smallest statistics chunk any call takes is one batch
+    cmax = ((long long)V + sv::kStepVecs - 1) / sv::kStepVecs;
     if (cmax > sv::kMaxChunks) cmax = sv::kMaxChunks;
   }
+  L.cmax = cmax;
   const long long dmax = ((long long)V + sv::kDrawVecs - 1) / sv::kDrawVecs;
   size_t off = 0;
   L.off_draw_done = off;
@@ -166,9 +168,17 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
   // unfiltered rows of at most kMaxDrawSlices slices run as one kernel (with
   // larger statistics chunks)
   L.fused = !filt && P.dchunks <= sv::kMaxDrawSlices;
-  P.chunk_vecs = topk ? sv::kFiltChunkVecs
-                      : (int)chunk_vecs_for(P.nvec, L.fused ? sv::kFusedChunkSteps : sv::kChunkSteps);
+  int steps = sv::kChunkSteps;
+  if (L.fused) {
+    // about kFusedBlocks statistics blocks over the call (small batches take
+    // smaller chunks to fill the chip), at most kFusedChunkSteps batches each
+    const long long rows_read = (all_greedy ? 0LL : (long long)total_draft) + P.rows;
+    const long long want = rows_read * P.nvec / ((long long)sv::kFusedBlocks * sv::kStepVecs);
+    steps = (int)std::max(1LL, std::min((long long)sv::kFusedChunkSteps, want));
+  }
+  P.chunk_vecs = topk ? sv::kFiltChunkVecs : (int)chunk_vecs_for(P.nvec, steps);
   P.chunks = (P.nvec + P.chunk_vecs - 1) / P.chunk_vecs;
+  if (P.chunks > L.cmax) return SV_EUNSUPPORTED;  // the workspace holds cmax chunks per row
   P.ntiles = P.dchunks * sv::kTilesPerDraw;
   // greedy-only calls skip the draft rows
   P.stats_block0 = all_greedy ? (long long)total_draft * P.chunks : 0;
@@ -284,6 +294,7 @@ int run_accept(const void* draft, const void* target, const int32_t* cu, int B, 
   P.nvec = vec ? V / (16 / es) : V;
   P.chunk_vecs = topk ? sv::kFiltChunkVecs : (int)chunk_vecs_for(P.nvec, sv::kChunkSteps);
   P.chunks = (P.nvec + P.chunk_vecs - 1) / P.chunk_vecs;
+  if (P.chunks > L.cmax) return SV_EUNSUPPORTED;  // the workspace holds cmax chunks per row
   P.filt = filt ? 1 : 0;
   P.nucleus = (filt && !topk) ? 1 : 0;
   P.top_k = top_k;

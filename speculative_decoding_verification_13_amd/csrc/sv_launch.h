@@ -17,7 +17,8 @@ constexpr int kStepVecs = kBatch * kThreads;  // vectors of a row one batch cove
 constexpr int kDrawVecs = kStepVecs;      // vectors of each row per draw block
 constexpr int kTilesPerDraw = kDrawVecs / kTileVecs;
 constexpr int kChunkSteps = 4;            // batches per stats block (64 KB of bf16)
-constexpr int kFusedChunkSteps = 8;       // the same in the one-kernel step (128 KB)
+constexpr int kFusedChunkSteps = 8;       // at most this many in the one-kernel step (128 KB)
+constexpr int kFusedBlocks = 2048;        // statistics blocks the one-kernel step aims for
 constexpr int kMaxChunks = 64;            // stats chunks per row (larger rows take
                                           // larger chunks)
 // Filtered rows (top-k): a stats block keeps its whole chunk in registers.
@@ -132,6 +133,7 @@ struct Params {
 // Grid size and workspace offsets of one call.
 struct Plan {
   int chunks, chunk_vecs, dchunks;
+  long long cmax;  // chunks per row the workspace holds partials and records for
   bool fused;  // one kernel (k_verify) instead of statistics, filter and draw kernels
   long long stats_blocks, filter_blocks, draw_blocks;
   size_t off_slots, off_tiles, off_draws, off_draw_done, off_seq_flags, off_rec, off_rowres,
