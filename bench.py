@@ -388,7 +388,7 @@ def bench_accept(args, w, sv):
         el = time.perf_counter() - t0
         cpu = {"value": done / el, "unit": "draft positions/s", "cores": 1, "kind": "oracle",
                "sample": f"{b} sequences of the same workload one by one in {el:.1f} s, "
-                         "numpy float64, one process"}
+                         "numpy float64, one process", "cpu_model": _cpu_model()}
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     draft0, target0 = w["draft"].to(dev), w["target"].to(dev)
@@ -452,6 +452,18 @@ def bench_accept(args, w, sv):
     print(json.dumps(rec_out), flush=True)
 
 
+def _cpu_model():
+    """The host CPU's model name (as lscpu prints it), or None."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def _cpu_one(b):
     """Oracle verification of sequence b of the prepared sample (one task)."""
     import oracle
@@ -513,6 +525,7 @@ def cpu_baseline(w, budget_s):
         "single_process": {"value": rows_one / el_one, "unit": "rows/s", "cores": 1,
                            "sample": f"first {n_one} sequences cycled for {el_one:.1f} s"},
         "host_cpus": os.cpu_count(),
+        "cpu_model": _cpu_model(),
     }
 
 
