@@ -62,13 +62,8 @@ __device__ RowStat row_stat(const Params& P, long long unit) {
   return r;
 }
 
-#ifndef SV_BETA_BATCH
-#define SV_BETA_BATCH 4
-#endif
-#ifndef SV_BETA_WAVES
-#define SV_BETA_WAVES 7
-#endif
-constexpr int kBetaBatch = SV_BETA_BATCH;  // vectors per row per thread in flight
+constexpr int kBetaBatch = 4;  // vectors per row per thread in flight (2 to 8 measured alike)
+constexpr int kBetaWaves = 7;  // waves per SIMD asked of the compiler
 
 // l*c - R of a logit, -inf outside the kept set.
 template <bool FILT>
@@ -100,7 +95,7 @@ __device__ void write_expected(const Params& P, int b) {
 // exponential per pair of logits (the offsets stay small, so each term keeps
 // the precision of its own row's exponent).
 template <int DT, bool VEC, bool FILT>
-__global__ __launch_bounds__(kThreads, SV_BETA_WAVES) void k_beta(const Params P) {
+__global__ __launch_bounds__(kThreads, kBetaWaves) void k_beta(const Params P) {
   using Vc = Vec<DT, VEC>;
   constexpr int N = Vc::N;
   __shared__ int s_cu[kCuLds];

@@ -8,6 +8,12 @@
 // (lowest id on ties) and whether the chunk holds NaN or +inf. Blocks never
 // wait on each other; the kernel boundary publishes the partials.
 //
+// With filters a per-row pass sits between them: k_filter (top-k, then top-p)
+// selects the row's k-th largest logit from the chunks' candidate records and
+// applies the top-p cut to the levels above it; k_nucleus (top-p alone) finds
+// the cut by a radix descent over the whole row. Both leave the row's kept-set
+// threshold and normaliser.
+//
 // k_draw runs one group of blocks per sequence, each group covering the vocabulary
 // of one row pair in slices. Every block of the group merges the row partials
 // of its sequence in chunk order, forms r_i = p_i(x_i)/q_i(x_i), tests
