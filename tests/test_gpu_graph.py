@@ -1,0 +1,64 @@
+"""A verification call captured in a HIP graph (torch.cuda.CUDAGraph on ROCm)
+and replayed: the library allocates nothing and records no memset (its
+workspace returns to zero on its own), so every replay must give the eager
+result. Replays alternate with eager calls of the library and eager torch work
+on the same stream, and each replay is checked."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from parity import compare, draft_tokens_from_oracle, run_oracle, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name,ov", [(W.HEADLINE, dict(B=8)),
+                                     ("f16_B256_K4_V151936_topk50_topp0.9", dict(B=4, V=20000))])
+def test_graph_replays_match_eager(name, ov):
+    import speculative_decoding_verification_13_amd as sv
+    w = W.make(name, **ov)
+    toks = draft_tokens_from_oracle(w)
+    ora = run_oracle(w, toks)
+    d = to_device(w, toks)
+    B, V, K = w["B"], w["V"], w["K"]
+    n_draft = B * K
+    print(f"[gpu] graph {w['name']} B={B} V={V} top_k={w['top_k']}", flush=True)
+    ws = sv.make_workspace(B, n_draft, V, w["top_k"], w["top_p"])
+    out = torch.empty((B, K + 1), dtype=torch.int32, device="cuda")
+    num = torch.empty((B,), dtype=torch.int32, device="cuda")
+    args = (d["draft"].view(B, K, V), d["target"].view(B, K + 1, V), d["tokens"].view(B, K),
+            d["uniforms"].view(B, K + 1), B, K, V, w["temperature"], w["top_k"], w["top_p"])
+
+    def call():
+        sv.spec_verify(*args, out_tokens=out, num_accepted=num, workspace=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()  # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager_out, eager_num = out.clone(), num.clone()
+    gpu = dict(out_tokens=eager_out.cpu().numpy().reshape(-1), num_accepted=eager_num.cpu().numpy())
+    assert not compare(w, toks, gpu, ora)["mismatches"]
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    torch.cuda.synchronize()
+    scratch = torch.randn(1 << 20, device="cuda")
+    for r in range(5):
+        out.fill_(-7)
+        num.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_out), f"replay {r}"
+        assert torch.equal(num, eager_num), f"replay {r}"
+        # eager work between replays: torch kernels and an eager library call
+        scratch.mul_(1.0001).add_(0.5)
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_out) and torch.equal(num, eager_num)
+    assert int((ws != 0).sum()) == 0  # the workspace is back at zero after the last call
