@@ -211,6 +211,15 @@ __device__ __forceinline__ int wave_max_i(int v) {
   v = max(v, dpp_rows_i<0x143, 0xC>(v, INT_MIN));
   return __builtin_amdgcn_readlane(v, 63);
 }
+__device__ __forceinline__ int wave_sum_i(int v) {
+  v += dpp_i<0xB1>(v);
+  v += dpp_i<0x4E>(v);
+  v += dpp_i<0x141>(v);
+  v += dpp_i<0x140>(v);
+  v += dpp_rows_i<0x142, 0xA>(v, 0);
+  v += dpp_rows_i<0x143, 0xC>(v, 0);
+  return __builtin_amdgcn_readlane(v, 63);
+}
 __device__ __forceinline__ float wave_sum(float x) { return wave_sum_dpp(x); }
 
 __device__ __forceinline__ void wave_merge_ms(float& m, float& s, float c) {
@@ -248,6 +257,16 @@ __device__ __forceinline__ float wave_incl_scan(float x) {
   x += dpp_rows_f<0x118, 0xF>(x, 0.0f);  // row_shr:8
   x += dpp_rows_f<0x142, 0xA>(x, 0.0f);  // row_bcast:15
   x += dpp_rows_f<0x143, 0xC>(x, 0.0f);  // row_bcast:31
+  return x;
+}
+
+__device__ __forceinline__ int wave_incl_scan_i(int x) {
+  x += dpp_rows_i<0x111, 0xF>(x, 0);  // row_shr:1
+  x += dpp_rows_i<0x112, 0xF>(x, 0);  // row_shr:2
+  x += dpp_rows_i<0x114, 0xF>(x, 0);  // row_shr:4
+  x += dpp_rows_i<0x118, 0xF>(x, 0);  // row_shr:8
+  x += dpp_rows_i<0x142, 0xA>(x, 0);  // row_bcast:15
+  x += dpp_rows_i<0x143, 0xC>(x, 0);  // row_bcast:31
   return x;
 }
 
@@ -326,12 +345,7 @@ __device__ __forceinline__ int block_excl_scan_i(int x, int& total) {
   __shared__ int s_w[kBlock / kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
-  int incl = x;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
+  const int incl = wave_incl_scan_i(x);
   __syncthreads();
   if (lane == kWave - 1) s_w[w] = incl;
   __syncthreads();
@@ -361,8 +375,7 @@ __device__ __forceinline__ float block_max_f(float x) {
 
 __device__ __forceinline__ int block_sum_i(int x) {
   __shared__ int s_w[kBlock / kWave];
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  x = wave_sum_i(x);
   __syncthreads();
   if ((threadIdx.x & (kWave - 1)) == 0) s_w[threadIdx.x / kWave] = x;
   __syncthreads();

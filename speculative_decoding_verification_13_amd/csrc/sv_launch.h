@@ -26,6 +26,7 @@ constexpr int kFiltVpt = 8;               // vectors per thread of a filtered ch
 constexpr int kFiltChunkVecs = kFiltVpt * kThreads;
 constexpr int kRecHeader = 8;             // header words of a chunk record
 constexpr int kBoundMaxK = kThreads;      // largest k bounded by the per-thread maxima
+constexpr int kHitMax = 512;              // candidate vectors a stats block stages in LDS
 constexpr int kFilterMaxLevels = 2048;    // LDS entries of the per-row level sort
 constexpr int kFilterLdsKeys = 4096;      // record entries a filter block stages in LDS
 constexpr int kFilterLdsChunks = 64;      // record headers a filter block stages in LDS

@@ -164,8 +164,9 @@ __device__ __forceinline__ bool is_bonus_row(const Params& P, int row, int* s_cu
 // sampling row the maximum m and the sum of 2^(l*c - R), R = fp32(m*c).
 // Returns the packed partial in thread 0 (0 elsewhere). The loads are streamed
 // (non-temporal) unless `stream` is false: rows a draw is likely to read again
-// keep the ordinary cache policy.
-template <int DT, bool VEC>
+// keep the ordinary cache policy. GREEDY_ONLY compiles the greedy statistics
+// alone (for callers whose other rows never come here).
+template <int DT, bool VEC, bool GREEDY_ONLY = false>
 __device__ unsigned long long chunk_stats(const Params& P, const void* base, size_t roff, int vb,
                                           int ve, bool greedy, bool stream = true) {
   using Vc = Vec<DT, VEC>;
@@ -176,7 +177,7 @@ __device__ unsigned long long chunk_stats(const Params& P, const void* base, siz
   const int wave = tid / kWave;
   int v = vb + tid;
   unsigned long long packed;
-  if (greedy) {
+  if (GREEDY_ONLY || greedy) {
     float bv = kNegInf;
     int bi = INT_MAX, bad = 0;
     for (; v + (kBatch - 1) * kThreads < ve; v += kBatch * kThreads) {

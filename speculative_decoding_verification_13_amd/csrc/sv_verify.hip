@@ -40,81 +40,26 @@ namespace sv {
 
 namespace {
 
-
-// Makes a register value opaque to the compiler, so values derived from it in
-// one pass are recomputed in the next instead of being kept alive.
-__device__ __forceinline__ void opaque(uint4& x) {
-  asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w));
-}
-__device__ __forceinline__ void opaque(float& x) { asm volatile("" : "+v"(x)); }
-
-// Maximum of this thread's register-held logits (vectors v0, v0 + kThreads,
-// ... below nvec) with NaN-propagating maxima: packed over fp16 pairs, over
-// widened values otherwise.
+// NaN-propagating maximum of one register-held vector: packed over fp16
+// pairs, over widened values otherwise.
 template <int DT, bool VEC, class Raw>
-__device__ __forceinline__ float thread_max_prop(const Raw (&r)[kFiltVpt], int v0, int nvec) {
+__device__ __forceinline__ float vec_max_prop(const Raw& w) {
   if constexpr (VEC && DT == SV_F16) {
-    half2_t m2 = {(_Float16)kNegInf, (_Float16)kNegInf};
-#pragma unroll
-    for (int u = 0; u < kFiltVpt; ++u) {
-      if (v0 + u * kThreads < nvec) {
-        const uint4 w = r[u];
-        const half2_t a = __builtin_bit_cast(half2_t, w.x), b = __builtin_bit_cast(half2_t, w.y);
-        const half2_t cc = __builtin_bit_cast(half2_t, w.z), d = __builtin_bit_cast(half2_t, w.w);
-        m2 = __builtin_elementwise_maximum(m2, __builtin_elementwise_maximum(a, b));
-        m2 = __builtin_elementwise_maximum(m2, __builtin_elementwise_maximum(cc, d));
-      }
-    }
+    const half2_t a = __builtin_bit_cast(half2_t, w.x), b = __builtin_bit_cast(half2_t, w.y);
+    const half2_t cc = __builtin_bit_cast(half2_t, w.z), d = __builtin_bit_cast(half2_t, w.w);
+    const half2_t m2 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b),
+                                                     __builtin_elementwise_maximum(cc, d));
     return __builtin_elementwise_maximum((float)m2.x, (float)m2.y);
   } else {
     constexpr int N = VEC ? Dt<DT>::N : 1;
-    float m = kNegInf;
+    float f[N];
+    Vec<DT, VEC>::get(w, f);
+    float m = f[0];
 #pragma unroll
-    for (int u = 0; u < kFiltVpt; ++u) {
-      if (v0 + u * kThreads < nvec) {
-        float f[N];
-        Vec<DT, VEC>::get(r[u], f);
-#pragma unroll
-        for (int k = 0; k < N; ++k) m = __builtin_elementwise_maximum(m, f[k]);
-      }
-    }
+    for (int k = 1; k < N; ++k) m = __builtin_elementwise_maximum(m, f[k]);
     return m;
   }
 }
-
-// Element k (0 <= k < N, not a compile-time constant) of one raw vector.
-template <int DT>
-__device__ __forceinline__ float elem_of(const uint4& v, int k) {
-  if constexpr (DT == SV_F32) {
-    const unsigned w = (k & 2) ? ((k & 1) ? v.w : v.z) : ((k & 1) ? v.y : v.x);
-    return __uint_as_float(w);
-  } else {
-    const int q = k >> 1;
-    const unsigned w = (q & 2) ? ((q & 1) ? v.w : v.z) : ((q & 1) ? v.y : v.x);
-    const unsigned h = (k & 1) ? (w >> 16) : (w & 0xffffu);
-    if constexpr (DT == SV_BF16) return __uint_as_float(h << 16);
-    else return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-  }
-}
-template <int DT>
-__device__ __forceinline__ float elem_of(const float& v, int) { return v; }
-
-// Writes the elements of one raw vector whose bit is set in `bits` as (value
-// bits, id) pairs at ent[2*off ...], ids id0 + k in ascending order.
-template <int DT, class Raw>
-__device__ __forceinline__ void write_marked(const Raw vec, unsigned bits, int id0, unsigned* ent,
-                                             int& off) {
-  while (bits) {
-    const int k = __builtin_ctz(bits);
-    bits &= bits - 1u;
-    ent[2 * off] = __float_as_uint(elem_of<DT>(vec, k));
-    ent[2 * off + 1] = (unsigned)(id0 + k);
-    ++off;
-  }
-}
-
-// Weight of one id in the final draw: residual max(0, p - q) or bonus p, where
-// an id outside a row's kept set (l < threshold) has probability 0 in that row.
 
 // First tile whose inclusive prefix exceeds u*Z (else the last tile with mass).
 // Tile sums are read once with agent-scope loads (published by other blocks);
@@ -463,7 +408,9 @@ __device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool 
 // stays in registers). The candidates are the finite logits at or above a
 // lower bound of the chunk's k-th largest finite logit, so they include every
 // logit the row's top-k set can take from this chunk. They are written to the
-// chunk record as (value bits, id) pairs. A chunk with more candidates than the
+// chunk record as (value bits, id) pairs. Only vectors whose maximum reaches
+// the bound hold candidates: those few are staged in LDS and examined there,
+// so the per-logit work is one maximum. A chunk with more candidates than the
 // record holds (heavy ties, or k beyond what the bound covers) is cut to its
 // exact top k by a radix select on order-preserving keys; a tie class at the
 // cut that still does not fit is recorded as (value, count).
@@ -482,24 +429,31 @@ __device__ void topk_block(const Params& P, long long g, const void* base, size_
     const int v = vb + u * kThreads + tid;
     if (v < P.nvec) r[u] = Vc::load_stream(base, roff, v);
   }
-  // this thread's logits in registers, in ascending id order: fn(value, id)
+  // The rare paths below (invalid chunks, k beyond the bound, more
+  // candidates than the record holds) visit this thread's logits again in
+  // ascending id order, re-reading them one vector at a time so that the
+  // registers above are free by then: fn(value, id).
   auto each = [&](auto&& fn) {
-#pragma unroll
-    for (int u = 0; u < kFiltVpt; ++u) opaque(r[u]);
-#pragma unroll
+#pragma unroll 1
     for (int u = 0; u < kFiltVpt; ++u) {
       const int v = vb + u * kThreads + tid;
       if (v < P.nvec) {
         float f[N];
-        Vc::get(r[u], f);
+        Vc::get(Vc::load(base, roff, v), f);
 #pragma unroll
         for (int k = 0; k < N; ++k) fn(f[k], v * N + k);
       }
     }
   };
-  // Thread maximum with a NaN-propagating max: a NaN or +inf anywhere in the
-  // thread's logits shows up as the maximum (-inf does not).
-  const float tmax = thread_max_prop<DT, VEC>(r, vb + tid, P.nvec);
+  // Vector and thread maxima with a NaN-propagating max: a NaN or +inf
+  // anywhere in the thread's logits shows up as the maximum (-inf does not).
+  float vm[kFiltVpt];
+#pragma unroll
+  for (int u = 0; u < kFiltVpt; ++u)
+    vm[u] = (vb + u * kThreads + tid < P.nvec) ? vec_max_prop<DT, VEC>(r[u]) : kNegInf;
+  float tmax = vm[0];
+#pragma unroll
+  for (int u = 1; u < kFiltVpt; ++u) tmax = __builtin_elementwise_maximum(tmax, vm[u]);
   const int bad = (tmax != tmax || tmax == kPosInf) ? 1 : 0;
   // Bound: with the threads in groups of g (g = 4, 2 or 1, the largest with
   // at least k groups), the largest group maximum that at least k group maxima
@@ -520,6 +474,7 @@ __device__ void topk_block(const Params& P, long long g, const void* base, size_
     if (tid < ng) {
       const float mine = s_max[tid];
       int ge = 0;
+#pragma unroll 2
       for (int j = 0; j < ng; j += 4) {
         const float4 t = *reinterpret_cast<const float4*>(&s_max[j]);
         ge += (t.x >= mine) + (t.y >= mine) + (t.z >= mine) + (t.w >= mine);
@@ -534,30 +489,75 @@ __device__ void topk_block(const Params& P, long long g, const void* base, size_
   const int flags = block_sum_i(bad) ? kRecFlagBad : 0;
   unsigned* rec = P.rec + (size_t)g * P.rec_words;
   unsigned* ent = rec + kRecHeader;
-  // candidates: l >= lb, never -inf (an empty bound admits every finite logit);
-  // bit u*N + k of cmask marks element k of the thread's vector u
+  // candidates: l >= lb, never -inf (an empty bound admits every finite logit)
   const float lb2 = (lb == kNegInf) ? -__FLT_MAX__ : lb;
-  static_assert(kFiltVpt * N <= 64, "candidate mask holds one bit per register element");
-  unsigned long long cmask = 0ull;
+  if (flags == 0 && k <= kBoundMaxK) {
+    // No NaN or +inf here, so a vector holds a candidate iff its maximum
+    // reaches the bound, and there are at most as many such vectors as
+    // candidates. Stage them (thread order, then vector order) and count.
+    __shared__ typename Vc::Raw s_hv[kHitMax];
+    __shared__ int s_hid[kHitMax];
+    unsigned hm = 0u;
 #pragma unroll
-  for (int u = 0; u < kFiltVpt; ++u) opaque(r[u]);
+    for (int u = 0; u < kFiltVpt; ++u) hm |= (vm[u] >= lb2 ? 1u : 0u) << u;
+    int nhit;
+    int hoff = block_excl_scan_i(__builtin_popcount(hm), nhit);
+    if (nhit <= min(P.kcap, kHitMax)) {
 #pragma unroll
-  for (int u = 0; u < kFiltVpt; ++u) {
-    if (vb + u * kThreads + tid < P.nvec) {
-      float f[N];
-      Vc::get(r[u], f);
+      for (int u = 0; u < kFiltVpt; ++u) {
+        if ((hm >> u) & 1u) {
+          s_hv[hoff] = r[u];
+          s_hid[hoff] = vb + u * kThreads + tid;
+          ++hoff;
+        }
+      }
+      __syncthreads();
+      int cnt = 0;
+      for (int j = tid; j < nhit; j += kThreads) {
+        float f[N];
+        Vc::get(s_hv[j], f);
 #pragma unroll
-      for (int k2 = 0; k2 < N; ++k2)
-        if (f[k2] >= lb2) cmask |= 1ull << (u * N + k2);
+        for (int k2 = 0; k2 < N; ++k2) cnt += (f[k2] >= lb2) ? 1 : 0;
+      }
+      int total;
+      int off = block_excl_scan_i(cnt, total);
+      if (total <= P.kcap) {
+        for (int j = tid; j < nhit; j += kThreads) {
+          float f[N];
+          Vc::get(s_hv[j], f);
+          const int id0 = s_hid[j] * N;
+#pragma unroll
+          for (int k2 = 0; k2 < N; ++k2) {
+            if (f[k2] >= lb2) {
+              ent[2 * off] = __float_as_uint(f[k2]);
+              ent[2 * off + 1] = (unsigned)(id0 + k2);
+              ++off;
+            }
+          }
+        }
+        if (tid == 0) {
+          rec[0] = (unsigned)total;
+          rec[1] = 0u;
+          rec[2] = 0u;
+          rec[3] = 0u;
+        }
+        return;
+      }
     }
+    // more candidates than the record holds: the exact cut below
   }
+  int cnt = 0;
+  each([&](float f, int) { cnt += (f >= lb2) ? 1 : 0; });
   int total;
-  int off = block_excl_scan_i(__popcll(cmask), total);
+  int off = block_excl_scan_i(cnt, total);
   if (total <= P.kcap) {
-#pragma unroll
-    for (int u = 0; u < kFiltVpt; ++u)
-      write_marked<DT>(r[u], (unsigned)(cmask >> (u * N)) & ((1u << N) - 1u),
-                       (vb + u * kThreads + tid) * N, ent, off);
+    each([&](float f, int id) {
+      if (f >= lb2) {
+        ent[2 * off] = __float_as_uint(f);
+        ent[2 * off + 1] = (unsigned)id;
+        ++off;
+      }
+    });
     if (tid == 0) {
       rec[0] = (unsigned)total;
       rec[1] = 0u;
@@ -598,7 +598,7 @@ __device__ void topk_block(const Params& P, long long g, const void* base, size_
   const int gt_tot = block_sum_i(gt);
   const int eq_tot = block_sum_i(eq);
   const bool ties_fit = gt_tot + eq_tot <= P.kcap;  // gt_tot < k <= kcap always
-  int cnt = 0;
+  cnt = 0;
   each([&](float f, int) {
     cnt += (__builtin_isfinite(f) && (f > tau || (ties_fit && f == tau))) ? 1 : 0;
   });
@@ -655,15 +655,18 @@ __device__ void stats_unit(const Params& P, long long g) {
   if (P.skip_bonus && is_target && is_bonus_row(P, row, s_cu)) return;
   const void* base = is_target ? P.target : P.draft;
   const size_t roff = (size_t)row * (size_t)P.V;
+  const int vb = ch * P.chunk_vecs;
+  const int ve = min(P.nvec, vb + P.chunk_vecs);
+  unsigned long long packed;
   if constexpr (FILT) {
     if (!greedy) {
       topk_block<DT, VEC>(P, g, base, roff, ch);
       return;
     }
+    packed = chunk_stats<DT, VEC, true>(P, base, roff, vb, ve, true);
+  } else {
+    packed = chunk_stats<DT, VEC>(P, base, roff, vb, ve, greedy);
   }
-  const int vb = ch * P.chunk_vecs;
-  const unsigned long long packed =
-      chunk_stats<DT, VEC>(P, base, roff, vb, min(P.nvec, vb + P.chunk_vecs), greedy);
   if (threadIdx.x == 0) P.slots[g] = packed;
 }
 

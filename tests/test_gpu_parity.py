@@ -196,8 +196,9 @@ def test_greedy_ties_take_lowest_id():
     assert not rep["mismatches"]
 
 
-def _invalid_inputs_workload():
+def _invalid_inputs_workload(top_k=0, top_p=1.0):
     w = W.make("bf16_B32_K4_V32000", B=8, V=2048)
+    w["top_k"], w["top_p"] = top_k, top_p
     toks = draft_tokens_from_oracle(w).copy()
     V, K = w["V"], w["K"]
     cu = w["cu_draft"]
@@ -224,6 +225,20 @@ def test_invalid_inputs_are_flagged_per_sequence():
     assert ora["num_accepted"][7] == 0
     for api, diag in (("ragged", True), ("dense", False)):
         _say(f"[gpu] invalid inputs api={api} diag={diag}")
+        gpu = run_gpu(w, toks, api=api, diag=diag)
+        rep = compare(w, toks, gpu, ora, check_diag=diag)
+        assert not rep["mismatches"], rep["mismatches"]
+
+
+@pytest.mark.parametrize("top_k,top_p", [(20, 0.9), (0, 0.8), (300, 1.0)])
+def test_invalid_inputs_with_filters(top_k, top_p):
+    """The same invalid rows and ids under top-k and top-p: NaN or +inf in a
+    filtered row still flags its sequence, whichever filter path reads it."""
+    w, toks = _invalid_inputs_workload(top_k, top_p)
+    ora = run_oracle(w, toks, want_diag=True)
+    assert list(ora["num_accepted"][3:6]) == [-2, -2, -2]
+    for api, diag in (("ragged", True), ("dense", False)):
+        _say(f"[gpu] invalid inputs k={top_k} p={top_p} api={api} diag={diag}")
         gpu = run_gpu(w, toks, api=api, diag=diag)
         rep = compare(w, toks, gpu, ora, check_diag=diag)
         assert not rep["mismatches"], rep["mismatches"]
