@@ -270,6 +270,28 @@ __device__ __forceinline__ int wave_incl_scan_i(int x) {
   return x;
 }
 
+// Bitonic sort of one (value, weight) pair per lane across the wave, by value
+// in descending order (lane 0 ends with the largest). Each compare-exchange
+// keeps its own pair on equal values, so pairs are permuted, never copied.
+__device__ __forceinline__ void wave_sort_desc(float& v, float& w) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int size = 2; size <= kWave; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const float ov = __shfl_xor(v, stride);
+      const float ow = __shfl_xor(w, stride);
+      // descending runs where (lane & size) == 0, ascending elsewhere; the
+      // lower lane of a pair takes the larger value in a descending run
+      const bool keep_max = ((lane & size) == 0) == ((lane & stride) == 0);
+      if (keep_max ? (ov > v) : (ov < v)) {
+        v = ov;
+        w = ow;
+      }
+    }
+  }
+}
+
 // Block-wide inclusive scan for kBlock threads; `total` receives the block sum.
 __device__ __forceinline__ float block_incl_scan(float x, float& total) {
   __shared__ float s_w[kBlock / kWave];
@@ -385,37 +407,34 @@ __device__ __forceinline__ int block_sum_i(int x) {
   return r;
 }
 
-// Radix-select step over a 256-bin histogram (whole block; wave 0 works):
+// Radix-select step over a histogram of BINS bins (whole block; wave 0 works):
 // the largest bin b with (count of bins above b) < rem <= (count of bins >= b),
-// written as s_sel[0] = b and s_sel[1] = rem - (count of bins above b).
+// written as s_sel[0] = b and s_sel[1] = rem - (count of bins above b). Lane
+// l holds the BINS/64 bins below BINS - 1 - l*BINS/64, so lane 0 holds the top.
+template <int BINS = 256>
 __device__ __forceinline__ void select_bin(const int* s_hist, int rem, int* s_sel) {
+  constexpr int PER = BINS / kWave;
+  static_assert(PER * kWave == BINS, "bins must fill the wave's lanes evenly");
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
-    int c[4];
+    const int top = BINS - 1 - PER * lane;
     int sum = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      c[j] = s_hist[255 - 4 * lane - j];  // lane 0 holds the top bins
-      sum += c[j];
-    }
-    int incl = sum;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
+    for (int j = 0; j < PER; ++j) sum += s_hist[top - j];
+    const int incl = wave_incl_scan_i(sum);
     const unsigned long long hit = __ballot(incl >= rem);
     const int first = hit ? (__ffsll(hit) - 1) : (kWave - 1);
     if (lane == first) {
-      // walk this lane's four bins downward; if rem exceeds every count (not
+      // walk this lane's bins downward; if rem exceeds every count (not
       // reachable for a valid rank) the lowest bin is taken
       int acc = incl - sum;
       int j = 0;
-      for (; j < 3; ++j) {
-        if (acc + c[j] >= rem) break;
-        acc += c[j];
+      for (; j < PER - 1; ++j) {
+        const int c = s_hist[top - j];
+        if (acc + c >= rem) break;
+        acc += c;
       }
-      s_sel[0] = 255 - 4 * lane - j;
+      s_sel[0] = top - j;
       s_sel[1] = rem - acc;
     }
   }

@@ -27,8 +27,9 @@ constexpr int kFiltChunkVecs = kFiltVpt * kThreads;
 constexpr int kRecHeader = 8;             // header words of a chunk record
 constexpr int kBoundMaxK = kThreads;      // largest k bounded by the per-thread maxima
 constexpr int kHitMax = 512;              // candidate vectors a stats block stages in LDS
-constexpr int kFilterMaxLevels = 2048;    // LDS entries of the per-row level sort
-constexpr int kFilterLdsKeys = 4096;      // record entries a filter block stages in LDS
+constexpr int kFilterMaxLevels = 1024;    // LDS entries of the per-row level sort (levels
+                                          // above the k-th largest, plus its tie class)
+constexpr int kFilterLdsKeys = 2048;      // record entries a filter block stages in LDS
 constexpr int kFilterLdsChunks = 64;      // record headers a filter block stages in LDS
 constexpr int kExplicitMax = 2048;        // candidates a filtered draw gathers in LDS
 constexpr int kKeptWords = 2 + 2 * kExplicitMax;  // words of a target row's kept list

@@ -686,16 +686,29 @@ __global__ __launch_bounds__(kThreads) void k_stats(const Params P) {
 // Pages: aihero.vn "Speculative decoding", section "Cùng phân bố không có
 // nghĩa cùng chuỗi mỗi lần" (the same temperature, top-k and top-p on both
 // models' rows).
+constexpr int kFiltBins = 2048;  // 11-bit key digits in the select
+
+template <int DT>
 __global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
-  __shared__ int s_hist[256];
+  // significant high bits of a logit's key: a widened bf16 or fp16 value
+  // leaves the low 16 or 13 key bits constant (all zero for a positive value,
+  // all one for a negative one), so two 11-bit digits fix its level
+  constexpr int kPasses = DT == SV_F32 ? 3 : 2;
+  constexpr int kLastShift = DT == SV_F32 ? 0 : 10;
+  // One LDS pool serves, in turn, the staged offsets of the row -> sequence
+  // search, the select's histogram and the levels (value, weight).
+  constexpr int kPoolWords = kFiltBins > 2 * kFilterMaxLevels ? kFiltBins : 2 * kFilterMaxLevels;
+  static_assert(kPoolWords >= kCuLds, "the pool holds the staged offsets");
+  __shared__ __align__(16) unsigned s_pool[kPoolWords];
+  int* const s_cu = reinterpret_cast<int*>(s_pool);
+  int* const s_hist = reinterpret_cast<int*>(s_pool);
+  float* const s_v = reinterpret_cast<float*>(s_pool);
+  float* const s_w = s_v + kFilterMaxLevels;
   __shared__ int s_sel[2];
   __shared__ int s_n;
-  __shared__ float s_v[kFilterMaxLevels];
-  __shared__ float s_w[kFilterMaxLevels];
   __shared__ unsigned s_key[kFilterLdsKeys];
   __shared__ unsigned s_hdr[kFilterLdsChunks][4];
   __shared__ int s_off[kFilterLdsChunks + 1];
-  __shared__ int s_cu[kCuLds];
   const int tid = threadIdx.x;
   const int unit = blockIdx.x;
   const bool is_target = unit >= P.total_draft;
@@ -784,20 +797,26 @@ __global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
   if (n_fin > k) {
     unsigned prefix = 0u, mask = 0u;
     int rem = k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      s_hist[tid] = 0;
+    for (int pass = 0; pass < kPasses; ++pass) {
+      // digits: bits 31-21, 20-10, 9-0
+      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+      const int width = pass == 2 ? 10 : 11;
+      for (int b = tid; b < kFiltBins; b += kThreads) s_hist[b] = 0;
       __syncthreads();
       for_entries([&](unsigned key, int cnt) {
-        if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], cnt);
+        if ((key & mask) == prefix)
+          atomicAdd(&s_hist[(key >> shift) & ((1u << width) - 1u)], cnt);
       });
       __syncthreads();
-      select_bin(s_hist, rem, s_sel);
+      select_bin<kFiltBins>(s_hist, rem, s_sel);
       __syncthreads();
       prefix |= (unsigned)s_sel[0] << shift;
-      mask |= 255u << shift;
+      mask |= ((1u << width) - 1u) << shift;
       rem = s_sel[1];
       __syncthreads();
     }
+    // the key bits below the last digit, constant for this dtype
+    if (kLastShift > 0) prefix |= (prefix & 0x80000000u) ? 0u : ((1u << kLastShift) - 1u);
     tau = float_of_key(prefix);
   }
   // levels above tau (fewer than k logits, at most a few tie classes), then tau
@@ -824,72 +843,98 @@ __global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
   }
   __syncthreads();
   const int n = min(s_n, kFilterMaxLevels);
-  int p2 = 2;
-  while (p2 < n) p2 <<= 1;
-  for (int x = n + tid; x < p2; x += kThreads) {
-    s_v[x] = kNegInf;
-    s_w[x] = 0.0f;
-  }
-  __syncthreads();
-  // bitonic sort, descending by value
-  for (int size = 2; size <= p2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int x = tid; x < p2; x += kThreads) {
-        const int y = x ^ stride;
-        if (y > x) {
-          const bool desc = (x & size) == 0;
-          const float a = s_v[x], b = s_v[y];
-          if (desc ? (a < b) : (a > b)) {
-            s_v[x] = b;
-            s_v[y] = a;
-            const float t = s_w[x];
-            s_w[x] = s_w[y];
-            s_w[y] = t;
+  const float c = P.c;
+  __shared__ float s_theta;
+  if (n <= kWave) {
+    // Few levels (the usual case): wave 0 sorts them in registers, then scans
+    // their masses and cuts, with no block-wide steps.
+    if (tid < kWave) {
+      float v = tid < n ? s_v[tid] : kNegInf;
+      float w = tid < n ? s_w[tid] : 0.0f;
+      wave_sort_desc(v, w);
+      const float m = n > 0 ? __shfl(v, 0) : kNegInf;
+      const float R = ref_of(m, c);
+      const float e = (tid < n) ? w * fast_exp2(fmaf(v, c, -R)) : 0.0f;
+      const float incl = wave_incl_scan(e);
+      const float S_k = __shfl(incl, kWave - 1);
+      // top-p: the last level whose strictly-larger mass over S_k is below top_p
+      int last = n - 1;
+      if (P.top_p < 1.0f) {
+        const unsigned long long ok = __ballot(tid < n && (incl - e) / S_k < P.top_p);
+        last = ok ? 63 - __clzll(ok) : -1;
+      }
+      const float theta = (n > 0 && last >= 0) ? __shfl(v, last) : kPosInf;
+      const float kincl = wave_incl_scan((tid < n && v >= theta) ? e : 0.0f);
+      if (tid == kWave - 1) {
+        P.rowres[unit] = RowRes{m, kincl, theta, bad ? 1 : 0};
+        s_theta = theta;
+      }
+    }
+  } else {
+    int p2 = 2;
+    while (p2 < n) p2 <<= 1;
+    for (int x = n + tid; x < p2; x += kThreads) {
+      s_v[x] = kNegInf;
+      s_w[x] = 0.0f;
+    }
+    __syncthreads();
+    // bitonic sort, descending by value
+    for (int size = 2; size <= p2; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int x = tid; x < p2; x += kThreads) {
+          const int y = x ^ stride;
+          if (y > x) {
+            const bool desc = (x & size) == 0;
+            const float a = s_v[x], b = s_v[y];
+            if (desc ? (a < b) : (a > b)) {
+              s_v[x] = b;
+              s_v[y] = a;
+              const float t = s_w[x];
+              s_w[x] = s_w[y];
+              s_w[y] = t;
+            }
           }
         }
+        __syncthreads();
       }
-      __syncthreads();
+    }
+    const float m = n > 0 ? s_v[0] : kNegInf;
+    const float R = ref_of(m, c);
+    // masses in sorted order; each thread takes a contiguous run
+    const int per = (p2 + kThreads - 1) / kThreads;
+    const int x0 = min(tid * per, p2), x1 = min(x0 + per, p2);
+    float local = 0.0f;
+    for (int x = x0; x < x1; ++x) {
+      const float w = (x < n) ? s_w[x] * fast_exp2(fmaf(s_v[x], c, -R)) : 0.0f;
+      s_w[x] = w;
+      local += w;
+    }
+    float S_k;
+    const float incl = block_incl_scan(local, S_k);
+    // top-p: the last entry whose strictly-larger mass over S_k is below top_p
+    int last = n - 1;
+    if (P.top_p < 1.0f) {
+      float run = incl - local;
+      int cand = -1;
+      for (int x = x0; x < x1 && x < n; ++x) {
+        if (run / S_k < P.top_p) cand = x;
+        run += s_w[x];
+      }
+      last = block_max_i(cand);
+    }
+    const float theta = (n > 0 && last >= 0) ? s_v[last] : kPosInf;
+    float kept = 0.0f;
+    for (int x = x0; x < x1 && x < n; ++x)
+      if (s_v[x] >= theta) kept += s_w[x];
+    float S_f;
+    block_incl_scan(kept, S_f);
+    if (tid == 0) {
+      P.rowres[unit] = RowRes{m, S_f, theta, bad ? 1 : 0};
+      s_theta = theta;
     }
   }
-  const float c = P.c;
-  const float m = n > 0 ? s_v[0] : kNegInf;
-  const float R = ref_of(m, c);
-  // masses in sorted order; each thread takes a contiguous run
-  const int per = (p2 + kThreads - 1) / kThreads;
-  const int x0 = min(tid * per, p2), x1 = min(x0 + per, p2);
-  float local = 0.0f;
-  for (int x = x0; x < x1; ++x) {
-    const float w = (x < n) ? s_w[x] * fast_exp2(fmaf(s_v[x], c, -R)) : 0.0f;
-    s_w[x] = w;
-    local += w;
-  }
-  float S_k;
-  const float incl = block_incl_scan(local, S_k);
-  // top-p: the last entry whose strictly-larger mass over S_k is below top_p
-  int last = n - 1;
-  if (P.top_p < 1.0f) {
-    float run = incl - local;
-    int cand = -1;
-    for (int x = x0; x < x1 && x < n; ++x) {
-      if (run / S_k < P.top_p) cand = x;
-      run += s_w[x];
-    }
-    last = block_max_i(cand);
-  }
-  const float theta = (n > 0 && last >= 0) ? s_v[last] : kPosInf;
-  float kept = 0.0f;
-  for (int x = x0; x < x1 && x < n; ++x)
-    if (s_v[x] >= theta) kept += s_w[x];
-  float S_f;
-  block_incl_scan(kept, S_f);
-  if (tid == 0) {
-    RowRes rr;
-    rr.m = m;
-    rr.s = S_f;
-    rr.theta = theta;
-    rr.flags = bad ? 1 : 0;
-    P.rowres[unit] = rr;
-  }
+  __syncthreads();
+  const float theta = s_theta;
   if (is_target && !P.skip_bonus) {
     // A target row's kept set, listed for the final draw when every kept id
     // is an explicit entry (no count-only tie class at or above theta).
@@ -1390,7 +1435,7 @@ static hipError_t launch_t(const Params& P, const Plan& L, hipStream_t s, hipEve
       hipLaunchKernelGGL((k_nucleus<DT, VEC>), dim3((unsigned)L.filter_blocks), dim3(kThreads), 0,
                          s, P);
     else
-      hipLaunchKernelGGL(k_filter, dim3((unsigned)L.filter_blocks), dim3(kThreads), 0, s, P);
+      hipLaunchKernelGGL(k_filter<DT>, dim3((unsigned)L.filter_blocks), dim3(kThreads), 0, s, P);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if ((err = stage_event(ev, nev, e++, s)) != hipSuccess) return err;
   } else {
@@ -1432,7 +1477,7 @@ static hipError_t launch_row_stats_t(const Params& P, const Plan& L, hipStream_t
                        s, P);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k_filter, dim3((unsigned)L.filter_blocks), dim3(kThreads), 0, s, P);
+    hipLaunchKernelGGL(k_filter<DT>, dim3((unsigned)L.filter_blocks), dim3(kThreads), 0, s, P);
   } else {
     hipLaunchKernelGGL((k_stats<DT, VEC, false>), dim3((unsigned)L.stats_blocks), dim3(kThreads),
                        0, s, P);

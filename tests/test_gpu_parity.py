@@ -122,6 +122,26 @@ def test_filters_heavy_ties(step):
     _check(w, api="ragged", diag=True, tag=f"ties step={step}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_filters_cut_between_adjacent_values(dtype):
+    """The k-th and (k+1)-th largest logits of every row one and a few units in
+    the last place apart: the select must resolve every bit of the cut."""
+    w = _filtered(50, 1.0, B=4, V=3000, dtype=dtype)
+    for key in ("draft", "target"):
+        t = w[key].float().numpy().copy()
+        for r in range(t.shape[0]):
+            order = np.argsort(-t[r], kind="stable")
+            x = np.float32(t[r, order[49]])
+            bits = np.array([x], dtype=np.float32).view(np.uint32)[0]
+            step = 1 if dtype == "f32" else 1 << 16  # one unit in the last place
+            sign = 1 if x > 0 else -1  # moving the bits down lowers a positive value
+            for rank, ulps in ((50, 1), (51, 3), (52, 700)):
+                nb = np.uint32(int(bits) - sign * ulps * step)
+                t[r, order[rank]] = np.array([nb], dtype=np.uint32).view(np.float32)[0]
+        w[key] = torch.from_numpy(t).to(w[key].dtype)
+    _check(w, api="ragged", diag=True, tag=f"adjacent cut {dtype}")
+
+
 def test_filters_masked_rows_and_scalar_path():
     """Rows with most ids at -inf (fewer finite logits than k in some rows), on
     an odd V (scalar path)."""
