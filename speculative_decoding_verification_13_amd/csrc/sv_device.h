@@ -292,6 +292,29 @@ __device__ __forceinline__ void wave_sort_desc(float& v, float& w) {
   }
 }
 
+// Bitonic sort of one (id, two payloads) triple per lane across the wave, by
+// id in ascending order (ids distinct, or pads of INT_MAX that sort last).
+__device__ __forceinline__ void wave_sort_by_id(int& id, float& a, float& b) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int size = 2; size <= kWave; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const int oid = __shfl_xor(id, stride);
+      const float oa = __shfl_xor(a, stride);
+      const float ob = __shfl_xor(b, stride);
+      // ascending runs where (lane & size) == 0; the lower lane of a pair
+      // takes the smaller id in an ascending run
+      const bool keep_min = ((lane & size) == 0) == ((lane & stride) == 0);
+      if (keep_min ? (oid < id) : (oid > id)) {
+        id = oid;
+        a = oa;
+        b = ob;
+      }
+    }
+  }
+}
+
 // Block-wide inclusive scan for kBlock threads; `total` receives the block sum.
 __device__ __forceinline__ float block_incl_scan(float x, float& total) {
   __shared__ float s_w[kBlock / kWave];

@@ -1176,6 +1176,53 @@ __device__ int explicit_draw(const Params& P, const Job& j, float& Zout) {
   const int tid = threadIdx.x;
   const float c = P.c;
   const unsigned* kl = P.kept + (size_t)j.prow * kKeptWords;
+  if ((int)kl[0] <= kWave) {
+    // Few kept ids (the usual case): wave 0 reads the count and the first 64
+    // entries in one round (words past the count read zero), then sorts,
+    // scans and picks in registers.
+    __shared__ int s_tok;
+    __shared__ float s_Z;
+    if (tid < kWave) {
+      const int n = (int)kl[0];
+      const unsigned lv = kl[2 + 2 * tid], li = kl[3 + 2 * tid];
+      const bool in = tid < n;
+      int id = in ? (int)li : INT_MAX;
+      float lp = in ? __uint_as_float(lv) : kNegInf;
+      float w = 0.0f;
+      if (in) {
+        const float ep = fast_exp2(fmaf(lp, c, -j.Rp));
+        if (j.mode == kJobBonus) {
+          w = ep * j.invSp;
+        } else {
+          const float lq = load_elem<DT>(P.draft, (size_t)j.qrow * P.V + id);
+          const float q = (lq >= j.thr_q) ? fast_exp2(fmaf(lq, c, -j.Rq)) * j.invSq : 0.0f;
+          w = fmaxf(fmaf(ep, j.invSp, -q), 0.0f);
+        }
+      }
+      wave_sort_by_id(id, w, lp);
+      float incl = wave_incl_scan(w);
+      float total = __shfl(incl, kWave - 1);
+      if (!(total > 0.0f) && j.mode == kJobResidual) {
+        // the residual mass rounded to zero: draw from p_n instead
+        w = (id != INT_MAX) ? fast_exp2(fmaf(lp, c, -j.Rp)) * j.invSp : 0.0f;
+        incl = wave_incl_scan(w);
+        total = __shfl(incl, kWave - 1);
+      }
+      const float target = j.u * total;
+      const float excl = incl - w;
+      const unsigned long long hit = __ballot(excl + w > target);
+      const unsigned long long pos = __ballot(w > 0.0f);
+      const int at = hit ? __ffsll(hit) - 1 : (pos ? 63 - __clzll(pos) : -1);
+      const int tok_at = __shfl(id, at >= 0 ? at : 0);
+      if (tid == 0) {
+        s_tok = (at >= 0 && at < n) ? tok_at : id;
+        s_Z = total;
+      }
+    }
+    __syncthreads();
+    Zout = s_Z;
+    return s_tok;
+  }
   if (tid == 0) s_cnt = (int)kl[0];
   __syncthreads();
   for (int x = tid; x < s_cnt; x += kThreads) {
@@ -1270,7 +1317,9 @@ __device__ int explicit_draw(const Params& P, const Job& j, float& Zout) {
 // of sequence b, then the tile sums of slice ch of row pair n. Every block of
 // a sampling sequence counts itself on the sequence's counter; the last one
 // draws the token and returns the sequence's workspace entries to zero. A
-// greedy sequence is decided by block 0 alone.
+// greedy sequence is decided by block 0 alone, and so is a filtered sequence
+// whose target rows all have complete kept lists (block 0 then draws from
+// the list and clears the sequence's entries; the other blocks leave at once).
 template <int DT, bool VEC>
 __device__ void draw_unit(const Params& P, int idx) {
   using Vc = Vec<DT, VEC>;
@@ -1287,6 +1336,17 @@ __device__ void draw_unit(const Params& P, int idx) {
   }
   const bool greedy = seq_greedy(P, b);
   if (greedy && ch != 0) return;  // one block decides a greedy sequence
+  const bool lists = P.filt && P.kept != nullptr;
+  // filtered: whether every target row's kept list is complete, so that the
+  // draw, whichever row it takes, needs no tile sums
+  bool solo = false;
+  if (lists && !greedy) {
+    int inc = 0;
+    for (int r = tid; r <= kb; r += kThreads)
+      inc |= (int)P.kept[(size_t)(d0 + b + r) * kKeptWords + 1];
+    solo = __syncthreads_or(inc) == 0;
+    if (solo && ch != 0) return;
+  }
   const Job j = decide<DT>(P, b, d0, kb, greedy, ch == 0, S);
   if (greedy) {
     // the only reader of these partials returns them to zero
@@ -1297,7 +1357,6 @@ __device__ void draw_unit(const Params& P, int idx) {
   // filtered: the kept lists of the sequence's target rows go back to zero
   // once this block has counted itself, spread over the blocks of the
   // sequence, except the list of the row drawn from (the last block clears it)
-  const bool lists = P.filt && P.kept != nullptr;
   const int keep_row = j.mode != kJobNone ? j.prow : -1;
   auto zero_list = [&](int row) {
     unsigned* kl = P.kept + (size_t)row * kKeptWords;
@@ -1307,7 +1366,7 @@ __device__ void draw_unit(const Params& P, int idx) {
   };
   auto zero_share = [&]() {
     if (!lists) return;
-    for (int r = ch; r <= kb; r += P.dchunks)
+    for (int r = solo ? 0 : ch; r <= kb; r += solo ? 1 : P.dchunks)
       if (d0 + b + r != keep_row) zero_list(d0 + b + r);
   };
   // filtered: draw from the kept list when it holds the whole kept set
@@ -1362,13 +1421,15 @@ __device__ void draw_unit(const Params& P, int idx) {
     }
   }
   // every block of the sequence counts itself, after its stores have landed
-  drain_stores();
-  __syncthreads();
-  if (tid == 0) s_last = (bump(P.draw_done + b) == P.dchunks - 1) ? 1 : 0;
-  __syncthreads();
-  if (!s_last) {
-    zero_share();
-    return;
+  if (!solo) {
+    drain_stores();
+    __syncthreads();
+    if (tid == 0) s_last = (bump(P.draw_done + b) == P.dchunks - 1) ? 1 : 0;
+    __syncthreads();
+    if (!s_last) {
+      zero_share();
+      return;
+    }
   }
   // Last block of the sequence: every other block has read the partials and
   // published its tile sums.
@@ -1393,6 +1454,7 @@ __device__ void draw_unit(const Params& P, int idx) {
       P.rowres[u] = RowRes{0.f, 0.f, 0.f, 0};
     }
   }
+  if (solo) return;  // no tile sums or counter were written
   for (int t = tid; t < P.ntiles; t += kThreads) pub_f(P.tiles + (size_t)b * P.ntiles + t, 0.f);
   if (tid == 0) pub_i(P.draw_done + b, 0);
 }
