@@ -433,11 +433,14 @@ __device__ __forceinline__ int block_sum_i(int x) {
 // Radix-select step over a histogram of BINS bins (whole block; wave 0 works):
 // the largest bin b with (count of bins above b) < rem <= (count of bins >= b),
 // written as s_sel[0] = b and s_sel[1] = rem - (count of bins above b). Lane
-// l holds the BINS/64 bins below BINS - 1 - l*BINS/64, so lane 0 holds the top.
+// l first sums the BINS/64 bins below BINS - 1 - l*BINS/64 (lane 0 holds the
+// top); a scan over the lanes finds the lane whose bins hold the rank, and a
+// second scan over that lane's bins, one per lane, finds the bin. If rem
+// exceeds every count (not reachable for a valid rank) the lowest bin is taken.
 template <int BINS = 256>
 __device__ __forceinline__ void select_bin(const int* s_hist, int rem, int* s_sel) {
   constexpr int PER = BINS / kWave;
-  static_assert(PER * kWave == BINS, "bins must fill the wave's lanes evenly");
+  static_assert(PER * kWave == BINS && PER <= kWave, "bins must fill the wave's lanes evenly");
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
     const int top = BINS - 1 - PER * lane;
@@ -447,18 +450,15 @@ __device__ __forceinline__ void select_bin(const int* s_hist, int rem, int* s_se
     const int incl = wave_incl_scan_i(sum);
     const unsigned long long hit = __ballot(incl >= rem);
     const int first = hit ? (__ffsll(hit) - 1) : (kWave - 1);
-    if (lane == first) {
-      // walk this lane's bins downward; if rem exceeds every count (not
-      // reachable for a valid rank) the lowest bin is taken
-      int acc = incl - sum;
-      int j = 0;
-      for (; j < PER - 1; ++j) {
-        const int c = s_hist[top - j];
-        if (acc + c >= rem) break;
-        acc += c;
-      }
-      s_sel[0] = top - j;
-      s_sel[1] = rem - acc;
+    const int above = __shfl(incl - sum, first);  // count of the bins above lane first's
+    const int ftop = BINS - 1 - PER * first;
+    const int c = lane < PER ? s_hist[ftop - lane] : 0;
+    const int ci = wave_incl_scan_i(c);
+    const unsigned long long hit2 = __ballot(lane < PER && above + ci >= rem);
+    const int j = hit2 ? (__ffsll(hit2) - 1) : (PER - 1);
+    if (lane == j) {
+      s_sel[0] = ftop - j;
+      s_sel[1] = rem - (above + ci - c);
     }
   }
 }

@@ -718,7 +718,8 @@ __global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
   const int C = P.chunks;
   const unsigned* rec0 = P.rec + (size_t)unit * C * P.rec_words;
   // Stage the records in LDS when they fit: headers, then every entry's key.
-  bool staged = C <= kFilterLdsChunks;
+  const bool hdr_staged = C <= kFilterLdsChunks;
+  bool staged = hdr_staged;
   int E = 0;
   if (staged) {
     if (tid < C) {
@@ -730,13 +731,7 @@ __global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
     }
     __syncthreads();
     if (tid < kWave) {
-      int incl = tid < C ? (int)s_hdr[tid][0] : 0;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int y = __shfl_up(incl, o);
-        if (tid >= o) incl += y;
-      }
-      s_off[tid + 1] = incl;
+      s_off[tid + 1] = wave_incl_scan_i(tid < C ? (int)s_hdr[tid][0] : 0);
       if (tid == 0) s_off[0] = 0;
     }
     __syncthreads();
@@ -789,7 +784,7 @@ __global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
   int n_fin = 0, bad = 0;
   for_entries([&](unsigned, int cnt) { n_fin += cnt; });
   for (int ch = tid; ch < C; ch += kThreads)
-    bad |= (int)(rec0[(size_t)ch * P.rec_words + 3] & kRecFlagBad);
+    bad |= (int)((hdr_staged ? s_hdr[ch][3] : rec0[(size_t)ch * P.rec_words + 3]) & kRecFlagBad);
   n_fin = block_sum_i(n_fin);
   bad = block_sum_i(bad);
   const int k = P.top_k;
@@ -982,10 +977,19 @@ __global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
       kl[1] = (partial || s_n > kExplicitMax) ? 1u : 0u;
     }
   }
-  // Every row's records go back to zero (nothing reads them after this pass).
+  // Every row's records go back to zero (nothing reads them after this pass),
+  // their lengths taken from the staged headers when there are some.
   __syncthreads();
   unsigned* recw = P.rec + (size_t)unit * C * P.rec_words;
-  zero_records(P, C, [&](int ch) { return recw + (size_t)ch * P.rec_words; });
+  if (hdr_staged) {
+    constexpr int G = 16;
+    for (int ch = tid / G; ch < C; ch += kThreads / G) {
+      const int words = kRecHeader + 2 * (int)s_hdr[ch][0];
+      for (int w = tid % G; w < words; w += G) recw[(size_t)ch * P.rec_words + w] = 0u;
+    }
+  } else {
+    zero_records(P, C, [&](int ch) { return recw + (size_t)ch * P.rec_words; });
+  }
 }
 
 // ---------------------------------------------------------------- k_nucleus
