@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 import workloads as W  # noqa: E402
 
 PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0  # dense bf16 matrix-core peak of one MI355X
 METRIC = "verified rows/sec + effective HBM GB/s (% of ~8 TB/s), B=64 K=8 V=128256 bf16"
 # kernels of a call, in launch order: one fused kernel without filters; the
 # statistics, filter and draw passes with top-k
@@ -97,9 +98,11 @@ def parse():
                     help="budget of the CPU oracle sample (0 disables)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
-    ap.add_argument("--path", choices=["verify", "accept"], default="verify",
+    ap.add_argument("--path", choices=["verify", "accept", "lmhead"], default="verify",
                     help="verify: the verification step (default); accept: the "
-                         "acceptance statistics (spec_verify_accept_stats)")
+                         "acceptance statistics (spec_verify_accept_stats); lmhead: "
+                         "verification from LM-head hidden states (spec_verify_lmhead, "
+                         f"workload {W.LMHEAD_NAME})")
     ap.add_argument("--traffic-from", metavar="DIR", default=None,
                     help="only summarise rocprofv3 counter runs: DIR/{fetch,write,cal_fetch,"
                          "cal_write} hold FETCH_SIZE / WRITE_SIZE runs of this bench command and "
@@ -199,6 +202,9 @@ def main():
         return
     import speculative_decoding_verification_13_amd as sv
 
+    if args.path == "lmhead":
+        bench_lmhead(args, sv)
+        return
     w = W.make(args.workload, sd_t=args.sd_t)
     if args.path == "accept":
         bench_accept(args, w, sv)
@@ -447,6 +453,113 @@ def bench_accept(args, w, sv):
                      "algorithmic_bytes_per_launch": algo, "avg_launch_ms": call_ms},
         "mean_beta": float(beta.float().nanmean().item()),
         "mean_expected_accepted": float(exp.float().nanmean().item()),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec_out), flush=True)
+
+
+LM_STAGES = ["gemm_draft_stats", "gemm_target_stats", "merge_and_decide", "gemm_draw_rows", "draw"]
+
+
+def bench_lmhead(args, sv):
+    """Verification from LM-head hidden states: the draft and target rows'
+    logits formed on the matrix cores and reduced in the GEMM epilogue, the
+    decision, the draw rows formed again, and the draw."""
+    w = W.make_lmhead()
+    B, K, V, dq, dp, T = w["B"], w["K"], w["V"], w["d_draft"], w["d_target"], w["temperature"]
+    s = W.LM_H_SCALE * W.LM_W_SCALE
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        t_all, done, b = 0.0, 0, 0
+        while t_all < args.cpu_seconds and b < B:
+            hq, hp = w["hq"][b * K:(b + 1) * K], w["hp"][b * (K + 1):(b + 1) * (K + 1)]
+            lq = oracle.lmhead_logits(hq, w["wq"], s)
+            toks, _ = oracle.sample_rows(lq, w["u_draft"][b * K:(b + 1) * K], V=V, dtype="f64",
+                                         temperature=T)
+            t0 = time.perf_counter()
+            oracle.verify_lmhead(hq, w["wq"], hp, w["wp"], toks,
+                                 w["uniforms"][b * (K + 1):(b + 1) * (K + 1)], B=1, K=K, V=V,
+                                 temperature=T, draft_scale=s, target_scale=s)
+            t_all += time.perf_counter() - t0
+            done += K + 1
+            b += 1
+        cpu = {"value": done / t_all, "unit": "rows/s", "cores": os.cpu_count(), "kind": "oracle",
+               "sample": f"{b} sequences of the same workload one by one in {t_all:.1f} s "
+                         "(logits by the BLAS behind numpy on the host's cores, then the float64 "
+                         "verification), draft tokens drawn outside the timed part",
+               "cpu_model": _cpu_model()}
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    hq = W.lmhead_to_device(w["hq"], W.LM_H_SCALE, dev)
+    wq = W.lmhead_to_device(w["wq"], W.LM_W_SCALE, dev)
+    hp = W.lmhead_to_device(w["hp"], W.LM_H_SCALE, dev)
+    wp = W.lmhead_to_device(w["wp"], W.LM_W_SCALE, dev)
+    uni = torch.from_numpy(w["uniforms"]).to(dev)
+    # Draft tokens: the draft model's own draw from its logit rows (formed here
+    # in fp32, exact for these integer-valued inputs, for the input only), made
+    # by the library's K = 0 call.
+    n_draft = B * K
+    lq = hq.float() @ wq.float().T
+    zeros_cu = torch.zeros(n_draft + 1, dtype=torch.int32, device=dev)
+    u_draft = torch.from_numpy(w["u_draft"]).to(dev)
+    tok_out, _ = sv.spec_verify_ragged(None, lq, None, u_draft, zeros_cu, None, n_draft, V, T, 0,
+                                       1.0, total_draft_rows=0)
+    toks = tok_out.clone().view(B, K)
+    del lq, zeros_cu
+    ws = sv.make_lmhead_workspace(B, K, V, dev)
+    out = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
+    num = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def step(ev=None):
+        sv.spec_verify_lmhead(hq, wq, hp, wp, toks, uni, B, K, V, T, out_tokens=out,
+                              num_accepted=num, workspace=ws, stage_events=ev)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    nst = len(LM_STAGES) + 1
+    hev = HipEvents(nst * args.steps)
+    for k in range(args.steps):
+        step(hev.handles[nst * k:nst * (k + 1)])
+    torch.cuda.synchronize()
+    per = np.array([[hev.elapsed_ms(nst * k + i, nst * k + i + 1) for i in range(nst - 1)]
+                    for k in range(args.steps)])
+    hev.close()
+    stage_ms = per.mean(axis=0).tolist()
+    rows = B * (K + 1)
+    flops_t = 2.0 * rows * V * dp
+    flops_d = 2.0 * n_draft * V * dq
+    t_ms = stage_ms[1]
+    achieved = flops_t / (t_ms * 1e-3) / 1e12
+    weight_bytes = 2.0 * V * (dq + dp)
+    n = num.cpu().numpy()
+    rec_out = {
+        "metric": f"LM-head verification ({W.LMHEAD_NAME}): verified rows/s, hidden states and "
+                  "LM-head weights in, logit rows never stored",
+        "value": rows / (ms_step * 1e-3), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": W.LMHEAD_NAME, "B": B, "K": K, "V": V, "d_draft": dq,
+                   "d_target": dp, "temperature": T, "operand_dtype": "bf16",
+                   "accumulate": "f32", "rows_per_step": rows,
+                   "entry_point": "spec_verify_lmhead"},
+        "tflops_per_step": (flops_t + flops_d) / 1e12,
+        "effective_TFLOPs": (flops_t + flops_d) / (ms_step * 1e-3) / 1e12,
+        "roofline": {"kernel": "k_lm_gemm<true> (target rows)", "bound": "mfma",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "algorithmic_flops_per_launch": flops_t, "avg_launch_ms": t_ms},
+        "weight_bytes_per_pass": weight_bytes,
+        "stage_ms": dict(zip(LM_STAGES, stage_ms)),
+        "acceptance": {"mean_accepted": float(n.mean()), "errors": int((n < 0).sum())},
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec_out), flush=True)

@@ -224,6 +224,42 @@ int spec_verify_accept_stats(const void* draft_logits, const void* target_logits
                              float* beta, float* expected_accepted, void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
 
+/* Verification from LM-head hidden states: the same step as spec_verify, with
+ * the logit rows formed inside the library as l = h W^T on the matrix cores
+ * (bf16 operands, fp32 accumulation) and reduced in the GEMM epilogue, so the
+ * [B, K, V] and [B, K+1, V] logit arrays are never stored (aivaro.ru answer
+ * 289 section 8 names the memory the draft and target logits take; the
+ * lecture-16 notes: the target model scores every drafted position in one
+ * pass, its logits being the last layer's output). Only the rows of each
+ * sequence's final draw (p_n, and q_n for a residual) are formed again and
+ * kept, in fp32, inside the workspace.
+ *   hidden_draft   bf16 [B*K, d_draft]     draft model's last hidden states
+ *   weight_draft   bf16 [V, d_draft]       draft LM head (may be NULL with hidden_draft when K == 0)
+ *   hidden_target  bf16 [B*(K+1), d_target]
+ *   weight_target  bf16 [V, d_target]
+ *   draft_tokens   int32 [B, K]; uniforms float [B, K+1]; outputs as spec_verify.
+ * Sampling only: temperature finite and > 0; no top-k / top-p. d_draft and
+ * d_target are multiples of 8 (>= 8); the four matrices are 16-byte aligned.
+ * Row-major throughout. The workspace is sized by
+ * spec_verify_lmhead_workspace_bytes(B, K, V), 256-byte aligned; its first
+ * spec_verify_lmhead_zero_bytes(B, K, V) bytes must be zero before the first
+ * call (spec_verify_workspace_init) and are zero again after every call. The
+ * draw rows (2*B*V floats) sit at the tail of the workspace and hold the last
+ * call's rows. One workspace serves calls of any smaller B, K, V: their zero
+ * regions start at the front and their rows end at the back. stage_events
+ * (may be NULL; n_stage_events of them, caller-created) are recorded on
+ * `stream`: before the draft rows' GEMM, after it, after the target rows'
+ * GEMM, after the merge and decision, after the draw rows' GEMMs, and every
+ * further one after the draw. Errors as spec_verify. */
+size_t spec_verify_lmhead_workspace_bytes(int B, int K, int V);
+size_t spec_verify_lmhead_zero_bytes(int B, int K, int V);
+int spec_verify_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
+                       const void* hidden_target, const void* weight_target, int d_target,
+                       const int32_t* draft_tokens, const float* uniforms, int B, int K, int V,
+                       float temperature, int32_t* out_tokens, int32_t* num_accepted,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream,
+                       hipEvent_t* stage_events, int n_stage_events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,3 +26,4 @@ from .verify import (  # noqa: F401
     acceptance_probability,
     acceptance_stats,
 )
+from .lmhead import lmhead_logits, verify_lmhead  # noqa: F401,E402

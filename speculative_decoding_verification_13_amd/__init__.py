@@ -15,11 +15,13 @@ from ._lib import (  # noqa: F401
     SV_SEQ_SYNC_TIMEOUT,
     SpecVerifyError,
     lib,
+    make_lmhead_workspace,
     make_stage_events,
     make_workspace,
     num_stages,
     spec_verify,
     spec_verify_accept_stats,
+    spec_verify_lmhead,
     spec_verify_ragged,
     strerror,
     workspace_bytes,

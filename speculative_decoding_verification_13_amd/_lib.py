@@ -51,6 +51,10 @@ SIGNATURES = {
                               _P, _S, _P, ctypes.POINTER(SvDiag)]),
     "spec_verify_accept_stats": (_I, [_P, _P, _P, _I, _I, _I, _F, _I, _F, _I, _P, _P, _P, _S,
                                       _P]),
+    "spec_verify_lmhead_workspace_bytes": (_S, [_I, _I, _I]),
+    "spec_verify_lmhead_zero_bytes": (_S, [_I, _I, _I]),
+    "spec_verify_lmhead": (_I, [_P, _P, _I, _P, _P, _I, _P, _P, _I, _I, _I, _F, _P, _P, _P, _S,
+                                _P, _P, _I]),
 }
 
 _lib = None
@@ -215,6 +219,55 @@ def spec_verify_accept_stats(draft_logits, target_logits, cu_draft, B, V, temper
         float(temperature), int(top_k), float(top_p), _dtype_code(target_logits), _ptr(beta),
         _ptr(expected_accepted), _ptr(workspace), workspace.numel(), _stream(dev)))
     return beta, expected_accepted
+
+
+def make_lmhead_workspace(B, K, V, device="cuda"):
+    """Allocate a workspace for spec_verify_lmhead and zero-fill its first
+    spec_verify_lmhead_zero_bytes bytes (the rest holds the draw rows)."""
+    n = int(lib().spec_verify_lmhead_workspace_bytes(int(B), int(K), int(V)))
+    z = int(lib().spec_verify_lmhead_zero_bytes(int(B), int(K), int(V)))
+    if n == 0 and B > 0:
+        raise ValueError("invalid sizes for a workspace")
+    n = max(n, 256)
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    ws = ws[off:off + n]
+    if z > 0:
+        _check(lib().spec_verify_workspace_init(ctypes.c_void_p(ws.data_ptr()), z,
+                                                _stream(ws.device)))
+    return ws
+
+
+def spec_verify_lmhead(hidden_draft, weight_draft, hidden_target, weight_target, draft_tokens,
+                       uniforms, B, K, V, temperature, *, out_tokens=None, num_accepted=None,
+                       workspace=None, stage_events=None):
+    """Verification from bf16 LM-head hidden states (see include/spec_verify.h):
+    hidden_draft [B*K, Dq], weight_draft [V, Dq], hidden_target [B*(K+1), Dp],
+    weight_target [V, Dp]. ``stage_events`` is an optional list of raw
+    hipEvent_t handles (ints) recorded between the stages. Returns
+    (out_tokens [B, K+1], num_accepted [B])."""
+    dev = hidden_target.device
+    for t in (hidden_draft, weight_draft, hidden_target, weight_target):
+        if t is not None and t.dtype != torch.bfloat16:
+            raise ValueError("hidden states and weights must be bfloat16")
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    if num_accepted is None:
+        num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = make_lmhead_workspace(B, K, V, dev)
+    dq = 0 if hidden_draft is None else int(hidden_draft.shape[-1])
+    evs, n_ev = None, 0
+    if stage_events:
+        evs = (ctypes.c_void_p * len(stage_events))(*stage_events)
+        n_ev = len(stage_events)
+    _check(lib().spec_verify_lmhead(
+        _ptr(hidden_draft), _ptr(weight_draft), dq, _ptr(hidden_target), _ptr(weight_target),
+        int(hidden_target.shape[-1]), _ptr(draft_tokens), _ptr(uniforms), int(B), int(K), int(V),
+        float(temperature), _ptr(out_tokens), _ptr(num_accepted), _ptr(workspace),
+        workspace.numel(), _stream(dev), ctypes.cast(evs, ctypes.c_void_p) if evs else None,
+        n_ev))
+    return out_tokens, num_accepted
 
 
 def make_stage_events(n, device=None):

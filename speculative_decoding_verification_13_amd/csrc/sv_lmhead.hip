@@ -1,0 +1,476 @@
+// Verification from LM-head hidden states for gfx950: the logits l = h W^T of
+// every draft and target row are formed on the matrix cores (bf16 operands,
+// fp32 accumulation) and reduced in the GEMM's epilogue to per-row softmax
+// partials, so the [rows, V] logit rows are never stored. Only the two rows
+// the final draw needs per sequence (p_n, and q_n for a residual) are formed
+// again and kept, as fp32.
+//
+//   k_lm_gemm<true>   draft rows, then target rows: per (row, 128-id vocab
+//                     tile) the packed (max, sum of 2^(l*c - R)) partial, and
+//                     the logit at the row's token
+//   k_lm_merge        per row: the vocabulary tiles' partials merged into one
+//                     (and returned to zero)
+//   k_lm_plan         per sequence: the decision, naming the draw's rows
+//   k_lm_gemm<false>  those rows' logits into a [2B, V] fp32 array
+//   k_draw            the decision again, the outputs, and the inverse-CDF draw
+//                     over the stored rows (the same kernel as the logit path)
+//
+// Pages (by title, section): Hung-yi Lee lecture-16 notes (the target model
+// scores every drafted position in one forward pass; the logits are its last
+// layer's output); aivaro.ru answer 289 "Как работает speculative decoding на
+// уровне логитов, а не токенов?" s.8 (the memory the draft and target logits
+// take up), s.6 and s.9 (ratio test, residual).
+#include <utility>
+
+#include "sv_rows.h"
+
+namespace sv {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Block tile: 128 rows x 128 vocabulary ids, 64 hidden elements per step.
+// Four waves in a 2 x 2 arrangement, each a 64 x 64 sub-tile of four 32 x 32
+// MFMA tiles. LDS rows carry 8 bf16 of padding so that the 32 lanes reading
+// one operand column touch distinct banks.
+constexpr int kLmBM = 128;
+constexpr int kLmBN = 128;
+constexpr int kLmBK = 64;
+constexpr int kLmLds = kLmBK + 8;
+constexpr int kXcds = 8;  // blocks are dealt round-robin to the eight XCDs
+
+struct LmGemm {
+  const uint16_t* H;   // hidden rows, bf16 bits, row stride D
+  const uint16_t* W;   // LM-head weight [V, D], bf16 bits
+  const int* gather;   // row m reads hidden row gather[m * gather_step] (< 0: none); null: m
+  int gather_step;
+  int M, D, V, NT, MT;  // rows, hidden size, vocabulary, vocabulary tiles, row tiles
+  // statistics epilogue
+  unsigned long long* part;  // [(unit0 + m) * NT + vt]
+  float* tok_logits;         // [unit0 + m]
+  long long unit0;
+  int K;                     // drafts per sequence (dense)
+  int target;                // 1: rows are target rows, their token is x_i for i < K
+  const int32_t* tokens;
+  float c;
+  // logits epilogue: row m to out[(m * out_step + out_row0) * V + v]
+  float* out;
+  int out_step, out_row0;
+};
+
+__device__ __forceinline__ float shfl_xor32_max(float v) {
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 32));
+  return v;
+}
+__device__ __forceinline__ float shfl_xor32_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) v += __shfl_xor(v, o, 32);
+  return v;
+}
+
+// One block: a 128 x 128 tile of logits. The block order is XCD-aware: block
+// g runs on XCD g % 8, and the row tiles of one vocabulary tile are
+// consecutive blocks of one XCD, so its weight tile is fetched into that XCD's
+// L2 once and read from there by the other row tiles.
+template <bool STATS>
+__global__ __launch_bounds__(kThreads, 2) void k_lm_gemm(const LmGemm G) {
+  __shared__ __align__(16) uint16_t sA[kLmBM * kLmLds];
+  __shared__ __align__(16) uint16_t sB[kLmBN * kLmLds];
+  __shared__ float s_pm[2][kLmBM];
+  __shared__ float s_ps[2][kLmBM];
+  __shared__ int s_tok[kLmBM];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int g = blockIdx.x;
+  const int idx = g / kXcds;
+  const int vt = (idx / G.MT) * kXcds + g % kXcds;
+  const int mt = idx % G.MT;
+  if (vt >= G.NT) return;
+  const int m0 = mt * kLmBM, v0 = vt * kLmBN;
+
+  // Global -> LDS staging: chunk q = tid + 256 * j (j < 4) is tile row q / 8,
+  // hidden elements 8 * (q % 8) .. + 7 of the step.
+  const uint16_t* arow[4];
+  const uint16_t* brow[4];
+  const int kc = (tid & 7) * 8;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = (tid >> 3) + 32 * j;
+    const int m = m0 + r;
+    int h = -1;
+    if (m < G.M) h = G.gather != nullptr ? G.gather[(size_t)m * G.gather_step] : m;
+    arow[j] = h >= 0 ? G.H + (size_t)h * G.D : nullptr;
+    const int v = v0 + r;
+    brow[j] = v < G.V ? G.W + (size_t)v * G.D : nullptr;
+  }
+  uint4 ra[4], rb[4];
+  auto fetch = [&](int k0) {
+    const bool kin = k0 + kc < G.D;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ra[j] = (arow[j] != nullptr && kin)
+                  ? *reinterpret_cast<const uint4*>(arow[j] + k0 + kc) : make_uint4(0, 0, 0, 0);
+      rb[j] = (brow[j] != nullptr && kin)
+                  ? *reinterpret_cast<const uint4*>(brow[j] + k0 + kc) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+
+  fetch(0);
+  for (int k0 = 0; k0 < G.D; k0 += kLmBK) {
+    __syncthreads();  // every wave is done with the previous step's tiles
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = (tid >> 3) + 32 * j;
+      *reinterpret_cast<uint4*>(&sA[r * kLmLds + kc]) = ra[j];
+      *reinterpret_cast<uint4*>(&sB[r * kLmLds + kc]) = rb[j];
+    }
+    __syncthreads();
+    if (k0 + kLmBK < G.D) fetch(k0 + kLmBK);  // next step's operands, in flight during the MFMAs
+#pragma unroll
+    for (int ks = 0; ks < kLmBK / 16; ++ks) {
+      // lane l holds 8 consecutive hidden elements (16 * ks + 8 * (l / 32) ...)
+      // of row (or vocabulary id) l % 32 of each 32 x 32 tile
+      const int kk = ks * 16 + (lane >> 5) * 8;
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+        af[a] = *reinterpret_cast<const bf16x8*>(&sA[(wm * 64 + a * 32 + (lane & 31)) * kLmLds + kk]);
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        bfr[b] = *reinterpret_cast<const bf16x8*>(&sB[(wn * 64 + b * 32 + (lane & 31)) * kLmLds + kk]);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
+    }
+  }
+
+  // Element i of tile (a, b) in lane l: row wm*64 + a*32 + 8*(i/4) + 4*(l/32)
+  // + i%4, vocabulary id v0 + wn*64 + b*32 + l%32.
+  if constexpr (STATS) {
+    if (tid < kLmBM) {
+      const int m = m0 + tid;
+      int tok = -1;
+      if (m < G.M) {
+        if (!G.target) {
+          tok = G.tokens[m];
+        } else {
+          const int i = m % (G.K + 1);
+          if (i < G.K) tok = G.tokens[(m / (G.K + 1)) * G.K + i];
+        }
+      }
+      s_tok[tid] = tok;
+    }
+    __syncthreads();
+    const float c = G.c;
+    const int col0 = v0 + wn * 64 + (lane & 31);
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rl = wm * 64 + a * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        const float x0 = acc[a][0][i], x1 = acc[a][1][i];
+        const int tok = s_tok[rl];
+        if (tok == col0) G.tok_logits[G.unit0 + m0 + rl] = x0;
+        if (tok == col0 + 32) G.tok_logits[G.unit0 + m0 + rl] = x1;
+        const float y0 = col0 < G.V ? x0 : kNegInf;
+        const float y1 = col0 + 32 < G.V ? x1 : kNegInf;
+        const float mx = shfl_xor32_max(fmaxf(y0, y1));
+        const float R = ref_of(mx, c);
+        const float sm = shfl_xor32_sum(fast_exp2(fmaf(y0, c, -R)) + fast_exp2(fmaf(y1, c, -R)));
+        if ((lane & 31) == 0) {
+          s_pm[wn][rl] = mx;
+          s_ps[wn][rl] = sm;
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < kLmBM && m0 + tid < G.M) {
+      float mm = s_pm[0][tid], ss = s_ps[0][tid];
+      merge_ms(mm, ss, s_pm[1][tid], s_ps[1][tid], c);
+      G.part[(size_t)(G.unit0 + m0 + tid) * G.NT + vt] = pack_ms(mm, ss);
+    }
+  } else {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rl = wm * 64 + a * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        const int m = m0 + rl;
+        if (m >= G.M) continue;
+        if (G.gather != nullptr && G.gather[(size_t)m * G.gather_step] < 0) continue;
+        float* orow = G.out + (size_t)(m * G.out_step + G.out_row0) * G.V;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int v = v0 + wn * 64 + b * 32 + (lane & 31);
+          if (v < G.V) orow[v] = acc[a][b][i];
+        }
+      }
+    }
+  }
+}
+
+// Per statistics unit: its vocabulary tiles' partials merged into one (a
+// fixed tree over the block: each thread its run of tiles in order, then the
+// wave and block merges), stored as the unit's only chunk; the tiles' partials
+// go back to zero.
+__global__ __launch_bounds__(kThreads) void k_lm_merge(const unsigned long long* part0,
+                                                        unsigned long long* slots, int NT,
+                                                        float c) {
+  __shared__ float s_m[kThreads / kWave], s_s[kThreads / kWave];
+  const long long u = blockIdx.x;
+  unsigned long long* part = const_cast<unsigned long long*>(part0) + u * NT;
+  const int tid = threadIdx.x;
+  const int per = (NT + kThreads - 1) / kThreads;
+  float m = kNegInf, s = 0.0f;
+  for (int k = tid * per; k < min(NT, (tid + 1) * per); ++k) {
+    float om, os;
+    unpack_ms(part[k], om, os);
+    merge_ms(m, s, om, os, c);
+    part[k] = 0ull;
+  }
+  wave_reduce_ms(m, s, c);
+  if ((tid & (kWave - 1)) == 0) {
+    s_m[tid / kWave] = m;
+    s_s[tid / kWave] = s;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float mm = s_m[0], ss = s_s[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / kWave; ++w) merge_ms(mm, ss, s_m[w], s_s[w], c);
+    slots[u] = pack_ms(mm, ss);
+  }
+}
+
+size_t align_up(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace of the LM-head path:
+//   draw_done[B], seq_flags[B]   counters and status bits of the draw
+//   slots[units]                 merged row partials (one chunk per unit)
+//   tiles[B * ntiles]            draw-weight tile sums
+//   part[units * NT]             vocabulary-tile partials of the GEMM epilogue
+//   tok[units]                   logits at the units' tokens
+//   draw_rows[2B]                hidden rows of each sequence's draw
+// all zero between calls, and at the tail of the caller's workspace
+//   rows[2B * V] fp32            logits of those rows (rewritten every call)
+// Calls of any shape may share a workspace sized for the largest: every
+// shape's zero regions start at the front and its rows end at the back, and
+// neither reaches the other's.
+struct LmPlan {
+  size_t off_draw_done, off_seq_flags, off_slots, off_tiles, off_part, off_tok, off_draw_rows,
+      zero_bytes, rows_bytes, total;
+  int NT, nvec, dchunks, ntiles;
+};
+
+bool lm_plan(int B, int K, int V, LmPlan& L) {
+  if (B < 0 || K < 0 || K > SV_MAX_K || V < 1 || V > (1 << 30)) return false;
+  const long long units = (long long)B * K + (long long)B * (K + 1);
+  if (units > INT_MAX) return false;
+  L.NT = (V + kLmBN - 1) / kLmBN;
+  const bool vec = V % 4 == 0;
+  L.nvec = vec ? V / 4 : V;
+  L.dchunks = (L.nvec + kDrawVecs - 1) / kDrawVecs;
+  L.ntiles = L.dchunks * kTilesPerDraw;
+  size_t off = 0;
+  L.off_draw_done = off;
+  off += align_up((size_t)B * 4);
+  L.off_seq_flags = off;
+  off += align_up((size_t)B * 4);
+  L.off_slots = off;
+  off += align_up((size_t)units * 8);
+  L.off_tiles = off;
+  off += align_up((size_t)B * L.ntiles * 4);
+  L.off_part = off;
+  off += align_up((size_t)units * L.NT * 8);
+  L.off_tok = off;
+  off += align_up((size_t)units * 4);
+  L.off_draw_rows = off;
+  off += align_up((size_t)B * 2 * 4);
+  L.zero_bytes = off;
+  L.rows_bytes = align_up((size_t)B * 2 * V * 4);
+  L.total = off + L.rows_bytes;
+  return true;
+}
+
+}  // namespace
+
+}  // namespace sv
+
+extern "C" size_t spec_verify_lmhead_workspace_bytes(int B, int K, int V) {
+  sv::LmPlan L;
+  if (!sv::lm_plan(B, K, V, L)) return 0;
+  return L.total > 0 ? L.total : 256;
+}
+
+extern "C" size_t spec_verify_lmhead_zero_bytes(int B, int K, int V) {
+  sv::LmPlan L;
+  if (!sv::lm_plan(B, K, V, L)) return 0;
+  return L.zero_bytes;
+}
+
+extern "C" int spec_verify_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
+                                  const void* hidden_target, const void* weight_target,
+                                  int d_target, const int32_t* draft_tokens,
+                                  const float* uniforms, int B, int K, int V, float temperature,
+                                  int32_t* out_tokens, int32_t* num_accepted, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream,
+                                  hipEvent_t* stage_events, int n_stage_events) {
+  using namespace sv;
+  if (B < 0 || K < 0 || K > SV_MAX_K || V < 1) return SV_EINVAL;
+  if (!(temperature > 0.0f) || __builtin_isinf(temperature)) return SV_EINVAL;
+  if (d_target < 8 || d_target % 8 != 0 || (K > 0 && (d_draft < 8 || d_draft % 8 != 0)))
+    return SV_EINVAL;
+  if (B == 0) return SV_OK;
+  if (hidden_target == nullptr || weight_target == nullptr || out_tokens == nullptr ||
+      num_accepted == nullptr || uniforms == nullptr)
+    return SV_EINVAL;
+  if (K > 0 && (hidden_draft == nullptr || weight_draft == nullptr || draft_tokens == nullptr))
+    return SV_EINVAL;
+  const void* ptrs[4] = {hidden_draft, weight_draft, hidden_target, weight_target};
+  for (const void* p : ptrs)
+    if (p != nullptr && ((uintptr_t)p & 15u) != 0) return SV_EINVAL;
+  LmPlan L;
+  if (!lm_plan(B, K, V, L)) return SV_EUNSUPPORTED;
+  if (workspace == nullptr || ((uintptr_t)workspace % 256) != 0 || workspace_bytes < L.total)
+    return SV_EWORKSPACE;
+  const int total_draft = B * K;
+  const int rows = B * (K + 1);
+  const long long gemm_d = (long long)L.NT * ((total_draft + kLmBM - 1) / kLmBM);
+  const long long gemm_t = (long long)L.NT * ((rows + kLmBM - 1) / kLmBM);
+  if (gemm_t + kXcds * 4 > (long long)INT_MAX || gemm_d + kXcds * 4 > (long long)INT_MAX)
+    return SV_EUNSUPPORTED;
+  char* ws = static_cast<char*>(workspace);
+  // the draw rows at the tail of the workspace (256-byte aligned)
+  const size_t off_rows = (workspace_bytes - L.rows_bytes) / 256 * 256;
+  if (off_rows < L.zero_bytes) return SV_EWORKSPACE;
+  float* lrows = reinterpret_cast<float*>(ws + off_rows);
+
+  Params P{};
+  P.draft = lrows;
+  P.target = lrows;
+  P.tokens = draft_tokens;
+  P.uniforms = uniforms;
+  P.cu = nullptr;
+  P.greedy = nullptr;
+  P.B = B;
+  P.K = K;
+  P.V = V;
+  P.total_draft = total_draft;
+  P.rows = rows;
+  P.all_greedy = 0;
+  P.c = (float)(1.4426950408889634074 / (double)temperature);
+  P.chunks = 1;
+  P.nvec = L.nvec;
+  P.dchunks = L.dchunks;
+  P.ntiles = L.ntiles;
+  P.spin_limit = 1 << 16;
+  P.out_tokens = out_tokens;
+  P.num_accepted = num_accepted;
+  P.slots = reinterpret_cast<unsigned long long*>(ws + L.off_slots);
+  P.tiles = reinterpret_cast<float*>(ws + L.off_tiles);
+  P.draw_done = reinterpret_cast<int*>(ws + L.off_draw_done);
+  P.seq_flags = reinterpret_cast<int*>(ws + L.off_seq_flags);
+  P.tok_logits = reinterpret_cast<float*>(ws + L.off_tok);
+  P.draw_remap = 1;
+  P.draw_rows = reinterpret_cast<int*>(ws + L.off_draw_rows);
+  unsigned long long* part = reinterpret_cast<unsigned long long*>(ws + L.off_part);
+
+  auto grid_of = [&](int M) {
+    const int MT = (M + kLmBM - 1) / kLmBM;
+    const long long per_xcd = (L.NT + kXcds - 1) / kXcds;  // vocabulary tiles per XCD
+    return std::make_pair(MT, (unsigned)(per_xcd * MT * kXcds));
+  };
+  // stage events: before the draft statistics, then after the draft and the
+  // target statistics, the merge and plan, the row logits and the draw
+  int e = 0;
+  auto stage = [&]() {
+    if (stage_events != nullptr && e < n_stage_events)
+      return hipEventRecord(stage_events[e++], stream) == hipSuccess;
+    return true;
+  };
+  if (!stage()) return SV_EHIP;
+  LmGemm G{};
+  G.V = V;
+  G.NT = L.NT;
+  G.part = part;
+  G.tok_logits = P.tok_logits;
+  G.K = K;
+  G.tokens = draft_tokens;
+  G.c = P.c;
+  // statistics of the draft rows, then of the target rows
+  if (total_draft > 0) {
+    auto [MT, blocks] = grid_of(total_draft);
+    G.H = static_cast<const uint16_t*>(hidden_draft);
+    G.W = static_cast<const uint16_t*>(weight_draft);
+    G.D = d_draft;
+    G.M = total_draft;
+    G.MT = MT;
+    G.unit0 = 0;
+    G.target = 0;
+    hipLaunchKernelGGL(k_lm_gemm<true>, dim3(blocks), dim3(kThreads), 0, stream, G);
+  }
+  if (!stage()) return SV_EHIP;
+  {
+    auto [MT, blocks] = grid_of(rows);
+    G.H = static_cast<const uint16_t*>(hidden_target);
+    G.W = static_cast<const uint16_t*>(weight_target);
+    G.D = d_target;
+    G.M = rows;
+    G.MT = MT;
+    G.unit0 = total_draft;
+    G.target = 1;
+    hipLaunchKernelGGL(k_lm_gemm<true>, dim3(blocks), dim3(kThreads), 0, stream, G);
+  }
+  if (hipGetLastError() != hipSuccess || !stage()) return SV_EHIP;
+  hipLaunchKernelGGL(k_lm_merge, dim3((unsigned)(total_draft + rows)), dim3(kThreads), 0, stream,
+                     part, P.slots, L.NT, P.c);
+  if (hipGetLastError() != hipSuccess) return SV_EHIP;
+  if (launch_lm_plan(P, stream) != hipSuccess || !stage()) return SV_EHIP;
+  // logits of the draw's rows: target row of position n -> row 2b, draft row -> 2b + 1
+  LmGemm R{};
+  R.V = V;
+  R.NT = L.NT;
+  R.out = lrows;
+  R.out_step = 2;
+  R.gather_step = 2;
+  R.M = B;
+  {
+    auto [MT, blocks] = grid_of(B);
+    R.MT = MT;
+    R.H = static_cast<const uint16_t*>(hidden_target);
+    R.W = static_cast<const uint16_t*>(weight_target);
+    R.D = d_target;
+    R.gather = P.draw_rows;
+    R.out_row0 = 0;
+    hipLaunchKernelGGL(k_lm_gemm<false>, dim3(blocks), dim3(kThreads), 0, stream, R);
+    if (total_draft > 0) {
+      R.H = static_cast<const uint16_t*>(hidden_draft);
+      R.W = static_cast<const uint16_t*>(weight_draft);
+      R.D = d_draft;
+      R.gather = P.draw_rows + 1;
+      R.out_row0 = 1;
+      hipLaunchKernelGGL(k_lm_gemm<false>, dim3(blocks), dim3(kThreads), 0, stream, R);
+    }
+  }
+  if (hipGetLastError() != hipSuccess || !stage()) return SV_EHIP;
+  Plan DL{};
+  DL.draw_blocks = (long long)B * L.dchunks;
+  if (launch_draw_f32(L.nvec != V, P, DL, stream) != hipSuccess) return SV_EHIP;
+  while (e < n_stage_events && stage_events != nullptr)
+    if (!stage()) return SV_EHIP;
+  return SV_OK;
+}

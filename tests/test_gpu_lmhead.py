@@ -1,0 +1,154 @@
+"""GPU parity of verification from LM-head hidden states (spec_verify_lmhead)
+against the float64 oracle on the same seeded inputs.
+
+The workload recipe makes every logit exact in fp32 (integer-valued hidden
+states and weights with small ranges; see workloads.make_lmhead), so the GPU's
+matrix-core accumulation and the oracle's float64 product give the same
+logits, and the bar is the one of the logit path: tokens and num_accepted
+bit-exact for every sequence whose oracle margin exceeds 1e-5 (near-threshold
+sequences are counted and must return a valid outcome).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity import BAND
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _draft_tokens(w):
+    """The draft model's own samples: the oracle's inverse CDF over each draft
+    row's logits (float64), with the workload's u_draft."""
+    if w["K"] == 0:
+        return np.zeros(0, dtype=np.int32)
+    lq = oracle.lmhead_logits(w["hq"], w["wq"], W.LM_H_SCALE * W.LM_W_SCALE)
+    toks, _ = oracle.sample_rows(lq, w["u_draft"], V=w["V"], dtype="f64",
+                                 temperature=w["temperature"])
+    return toks
+
+
+def _oracle(w, toks):
+    s = W.LM_H_SCALE * W.LM_W_SCALE
+    return oracle.verify_lmhead(w["hq"], w["wq"], w["hp"], w["wp"], toks, w["uniforms"],
+                                B=w["B"], K=w["K"], V=w["V"], temperature=w["temperature"],
+                                draft_scale=s, target_scale=s)
+
+
+def _device(w, toks):
+    dev = "cuda"
+    return dict(
+        hq=W.lmhead_to_device(w["hq"], W.LM_H_SCALE, dev) if w["K"] > 0 else None,
+        wq=W.lmhead_to_device(w["wq"], W.LM_W_SCALE, dev) if w["K"] > 0 else None,
+        hp=W.lmhead_to_device(w["hp"], W.LM_H_SCALE, dev),
+        wp=W.lmhead_to_device(w["wp"], W.LM_W_SCALE, dev),
+        toks=torch.from_numpy(np.asarray(toks, dtype=np.int32)).to(dev) if w["K"] > 0 else None,
+        uni=torch.from_numpy(w["uniforms"]).to(dev))
+
+
+def _run(w, d, workspace=None):
+    import speculative_decoding_verification_13_amd as sv
+    out, num = sv.spec_verify_lmhead(d["hq"], d["wq"], d["hp"], d["wp"], d["toks"], d["uni"],
+                                     w["B"], w["K"], w["V"], w["temperature"],
+                                     workspace=workspace)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().reshape(-1), num.cpu().numpy()
+
+
+def _compare(w, toks, out, num, ora):
+    B, K, V = w["B"], w["K"], w["V"]
+    near = 0
+    for b in range(B):
+        sl = slice(b * (K + 1), (b + 1) * (K + 1))
+        if ora["margin"][b] <= BAND:
+            near += 1
+            n = int(num[b])
+            assert 0 <= n <= K, (b, n)
+            assert np.array_equal(out[sl][:n], toks[b * K:b * K + n]), b
+            assert 0 <= out[sl][n] < V, b
+            assert np.all(out[sl][n + 1:] == -1), b
+            continue
+        assert num[b] == ora["num_accepted"][b], (b, num[b], ora["num_accepted"][b])
+        assert np.array_equal(out[sl], ora["out_tokens"][sl]), (b, out[sl], ora["out_tokens"][sl])
+    return near
+
+
+def _check(w, tag, workspace=None):
+    _say(f"[gpu] lmhead {tag}: B={w['B']} K={w['K']} V={w['V']} Dq={w['d_draft']} "
+         f"Dp={w['d_target']} T={w['temperature']}")
+    toks = _draft_tokens(w)
+    ora = _oracle(w, toks)
+    out, num = _run(w, _device(w, toks), workspace)
+    near = _compare(w, toks, out, num, ora)
+    n = ora["num_accepted"]
+    _say(f"      near-threshold={near} mean accepted={n.mean():.2f} "
+         f"all-accepted={(n == w['K']).mean():.2f}")
+    return out, num, ora
+
+
+SMALL = [
+    dict(B=3, K=2, V=1000, d_draft=64, d_target=128),        # one row tile, vocabulary tail
+    dict(B=5, K=4, V=4099, d_draft=200, d_target=264),       # hidden tail, scalar draw rows
+    dict(B=2, K=0, V=3000, d_draft=64, d_target=64),         # no drafts: bonus only
+    dict(B=4, K=8, V=20000, d_draft=512, d_target=1024),     # several row tiles
+    dict(B=20, K=6, V=9000, d_draft=256, d_target=256, temperature=1.3),
+]
+
+
+@pytest.mark.parametrize("ov", SMALL, ids=lambda o: f"B{o['B']}K{o['K']}V{o['V']}")
+def test_lmhead_parity_small(ov):
+    w = W.make_lmhead(**ov, seed=2100 + ov["B"] + ov["K"])
+    _check(w, "small")
+
+
+def test_lmhead_workspace_returns_to_zero_and_serves_other_shapes():
+    import speculative_decoding_verification_13_amd as sv
+    big = dict(B=6, K=5, V=8000, d_draft=128, d_target=256)
+    ws = sv.make_lmhead_workspace(big["B"], big["K"], big["V"])
+    zb = int(sv.lib().spec_verify_lmhead_zero_bytes(big["B"], big["K"], big["V"]))
+    for ov, seed in ((big, 2200), (dict(B=3, K=2, V=5000, d_draft=64, d_target=64), 2201),
+                     (big, 2202)):
+        w = W.make_lmhead(**ov, seed=seed)
+        _check(w, f"reuse seed={seed}", workspace=ws)
+        assert int((ws[:zb] != 0).sum()) == 0
+
+
+def test_lmhead_invalid_token_flagged():
+    w = W.make_lmhead(B=4, K=3, V=2000, d_draft=64, d_target=64, seed=2300)
+    toks = _draft_tokens(w).copy()
+    toks[1 * 3 + 1] = w["V"]      # sequence 1: id out of range
+    toks[2 * 3 + 0] = -7          # sequence 2: negative id
+    ora = _oracle(w, toks)
+    assert list(ora["num_accepted"][1:3]) == [-1, -1]
+    out, num = _run(w, _device(w, toks))
+    _compare(w, toks, out, num, ora)
+
+
+def test_lmhead_argument_errors():
+    import speculative_decoding_verification_13_amd as sv
+    w = W.make_lmhead(B=2, K=2, V=1000, d_draft=64, d_target=64, seed=2400)
+    d = _device(w, _draft_tokens(w))
+    with pytest.raises(sv.SpecVerifyError):
+        sv.spec_verify_lmhead(d["hq"], d["wq"], d["hp"], d["wp"], d["toks"], d["uni"], 2, 2,
+                              1000, 0.0)  # greedy is not supported here
+    bad = d["hp"][:, :60].contiguous()  # hidden size not a multiple of 8
+    with pytest.raises(sv.SpecVerifyError):
+        sv.spec_verify_lmhead(d["hq"], d["wq"], bad, d["wp"][:, :60].contiguous(), d["toks"],
+                              d["uni"], 2, 2, 1000, 0.7)
+
+
+def test_lmhead_parity_full_size():
+    """B=64, K=8, V=128256, hidden sizes 2048 (draft) and 4096 (target), bf16,
+    T=0.7: the benchmark's workload, every sequence checked."""
+    w = W.make_lmhead()
+    _check(w, "full")

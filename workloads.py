@@ -158,3 +158,70 @@ def compulsory_bytes(w):
         rows = int(((Ks + 1) + np.where(g, 0, Ks)).sum())
     small = 4 * int(Ks.sum()) + 4 * int((Ks + 1).sum()) * 2 + 4 * w["B"]
     return rows * w["V"] * esize + small
+
+
+# ---------------------------------------------------------------------------
+# LM-head workloads: hidden states and LM-head weights instead of logit rows.
+# A draft model with hidden size d_draft and a target with d_target share one
+# vocabulary (a 1B-class drafter for an 8B-class target at V = 128256).
+LMHEAD = dict(B=64, K=8, V=128256, d_draft=2048, d_target=4096, temperature=0.7, seed=2001)
+LMHEAD_NAME = "lmhead_bf16_B64_K8_V128256_Dq2048_Dp4096"
+LM_H_SCALE = 1.0 / 8.0    # hidden value = integer in [-8, 8] / 8
+LM_W_SCALE = 1.0 / 512.0  # weight value = integer in [-64, 64] / 512
+
+
+def make_lmhead(B=None, K=None, V=None, d_draft=None, d_target=None, temperature=None,
+                seed=None):
+    """Integer-valued LM-head inputs (numpy int8, times LM_H_SCALE or LM_W_SCALE).
+
+    Hidden entries are uniform integers in [-8, 8], weight entries uniform in
+    [-64, 64]: bf16 holds every value, and every product and partial sum of a
+    logit (|sum| <= d * 8 * 64 < 2^24 for d < 32768) is exact in fp32, so the
+    GPU's fp32 accumulation and the float64 oracle agree exactly. The target
+    shares the draft's directions: for position i < K its first d_draft hidden
+    entries repeat the draft's hidden state of that position and its weight's
+    first d_draft columns are the draft weight; the remaining weight columns
+    are drawn fresh, the remaining hidden entries fresh in [-2, 2], and the
+    bonus position's hidden state fresh in [-8, 8]. Target logits are then the
+    draft logits plus an independent term of about a quarter of their spread.
+    Draw order (PCG64 stream [seed, 0]): draft hidden, draft weight, target
+    weight tail, target hidden (fresh parts, row by row); u_draft from stream
+    [seed, 1] and uniforms from [seed, 2] as in ``make``.
+    """
+    c = dict(LMHEAD)
+    for k, v in dict(B=B, K=K, V=V, d_draft=d_draft, d_target=d_target,
+                     temperature=temperature, seed=seed).items():
+        if v is not None:
+            c[k] = v
+    Bn, Kn, Vn, dq, dp = c["B"], c["K"], c["V"], c["d_draft"], c["d_target"]
+    if dp < dq:
+        raise ValueError("the target's hidden size must be at least the draft's")
+    rng = np.random.default_rng([c["seed"], 0])
+    hq = rng.integers(-8, 9, size=(Bn * Kn, dq), dtype=np.int8)
+    wq = rng.integers(-64, 65, size=(Vn, dq), dtype=np.int8)
+    wp = np.empty((Vn, dp), dtype=np.int8)
+    wp[:, :dq] = wq
+    if dp > dq:
+        wp[:, dq:] = rng.integers(-64, 65, size=(Vn, dp - dq), dtype=np.int8)
+    hp = np.empty((Bn * (Kn + 1), dp), dtype=np.int8)
+    for b in range(Bn):
+        for i in range(Kn + 1):
+            t = b * (Kn + 1) + i
+            if i < Kn:
+                hp[t, :dq] = hq[b * Kn + i]
+                if dp > dq:
+                    hp[t, dq:] = rng.integers(-2, 3, size=dp - dq, dtype=np.int8)
+            else:
+                hp[t] = rng.integers(-8, 9, size=dp, dtype=np.int8)
+    u_draft = np.random.default_rng([c["seed"], 1]).random(Bn * Kn, dtype=np.float32)
+    uniforms = np.random.default_rng([c["seed"], 2]).random(Bn * (Kn + 1), dtype=np.float32)
+    return dict(B=Bn, K=Kn, V=Vn, d_draft=dq, d_target=dp, temperature=float(c["temperature"]),
+                seed=int(c["seed"]), hq=hq, wq=wq, hp=hp, wp=wp, u_draft=u_draft,
+                uniforms=uniforms)
+
+
+def lmhead_to_device(a, scale, device="cuda"):
+    """An int8 array as a bf16 device tensor of a * scale (exact: |a| <= 127,
+    scale a power of two)."""
+    t = torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    return t.to(torch.bfloat16) * scale
