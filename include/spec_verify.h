@@ -248,9 +248,9 @@ int spec_verify_accept_stats(const void* draft_logits, const void* target_logits
  * call's rows. One workspace serves calls of any smaller B, K, V: their zero
  * regions start at the front and their rows end at the back. stage_events
  * (may be NULL; n_stage_events of them, caller-created) are recorded on
- * `stream`: before the draft rows' GEMM, after it, after the target rows'
- * GEMM, after the merge and decision, after the draw rows' GEMMs, and every
- * further one after the draw. Errors as spec_verify. */
+ * `stream`: before the statistics GEMMs (draft and target rows, one launch),
+ * after them, after the merge and decision, after the draw rows' GEMMs, and
+ * every further one after the draw. Errors as spec_verify. */
 size_t spec_verify_lmhead_workspace_bytes(int B, int K, int V);
 size_t spec_verify_lmhead_zero_bytes(int B, int K, int V);
 int spec_verify_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,

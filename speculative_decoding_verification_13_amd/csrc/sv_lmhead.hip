@@ -37,8 +37,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // one operand column touch distinct banks.
 constexpr int kLmBM = 128;
 constexpr int kLmBN = 128;
-constexpr int kLmBK = 64;
+#ifndef SV_LM_BK
+#define SV_LM_BK 64
+#endif
+constexpr int kLmBK = SV_LM_BK;
 constexpr int kLmLds = kLmBK + 8;
+constexpr int kLmCpr = kLmBK / 8;            // 16-byte chunks per tile row and step
+constexpr int kLmRpp = kThreads / kLmCpr;    // tile rows one pass of the block stages
+constexpr int kLmPasses = kLmBM / kLmRpp;    // passes per operand tile
 constexpr int kXcds = 8;  // blocks are dealt round-robin to the eight XCDs
 
 struct LmGemm {
@@ -60,25 +66,26 @@ struct LmGemm {
   int out_step, out_row0;
 };
 
-__device__ __forceinline__ float shfl_xor32_max(float v) {
-#pragma unroll
-  for (int o = 1; o < 32; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 32));
-  return v;
-}
-__device__ __forceinline__ float shfl_xor32_sum(float v) {
-#pragma unroll
-  for (int o = 1; o < 32; o <<= 1) v += __shfl_xor(v, o, 32);
-  return v;
-}
+// Two GEMMs in one launch (the draft's and the target's): blocks below n0
+// run the first, the rest the second. n0 is a multiple of eight, so both keep
+// the XCD-aware block order.
+struct LmPair {
+  LmGemm g[2];
+  int n0;
+};
 
 // One block: a 128 x 128 tile of logits. The block order is XCD-aware: block
 // g runs on XCD g % 8, and the row tiles of one vocabulary tile are
 // consecutive blocks of one XCD, so its weight tile is fetched into that XCD's
 // L2 once and read from there by the other row tiles.
 template <bool STATS>
-__global__ __launch_bounds__(kThreads, 2) void k_lm_gemm(const LmGemm G) {
-  __shared__ __align__(16) uint16_t sA[kLmBM * kLmLds];
-  __shared__ __align__(16) uint16_t sB[kLmBN * kLmLds];
+__global__ __launch_bounds__(kThreads, 2) void k_lm_gemm(const LmPair PR) {
+  const bool second = (int)blockIdx.x >= PR.n0;
+  const LmGemm& G = PR.g[second ? 1 : 0];
+  // operand tiles; after the main loop the statistics epilogue reuses them
+  __shared__ __align__(16) uint16_t sAB[(kLmBM + kLmBN) * kLmLds];
+  uint16_t* const sA = sAB;
+  uint16_t* const sB = sAB + kLmBM * kLmLds;
   __shared__ float s_pm[2][kLmBM];
   __shared__ float s_ps[2][kLmBM];
   __shared__ int s_tok[kLmBM];
@@ -86,39 +93,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_lm_gemm(const LmGemm G) {
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int wm = wave & 1, wn = wave >> 1;
-  const int g = blockIdx.x;
+  const int g = (int)blockIdx.x - (second ? PR.n0 : 0);
   const int idx = g / kXcds;
   const int vt = (idx / G.MT) * kXcds + g % kXcds;
   const int mt = idx % G.MT;
   if (vt >= G.NT) return;
   const int m0 = mt * kLmBM, v0 = vt * kLmBN;
 
-  // Global -> LDS staging: chunk q = tid + 256 * j (j < 4) is tile row q / 8,
-  // hidden elements 8 * (q % 8) .. + 7 of the step.
-  const uint16_t* arow[4];
-  const uint16_t* brow[4];
-  const int kc = (tid & 7) * 8;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = (tid >> 3) + 32 * j;
-    const int m = m0 + r;
-    int h = -1;
-    if (m < G.M) h = G.gather != nullptr ? G.gather[(size_t)m * G.gather_step] : m;
-    arow[j] = h >= 0 ? G.H + (size_t)h * G.D : nullptr;
-    const int v = v0 + r;
-    brow[j] = v < G.V ? G.W + (size_t)v * G.D : nullptr;
-  }
-  uint4 ra[4], rb[4];
-  auto fetch = [&](int k0) {
-    const bool kin = k0 + kc < G.D;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ra[j] = (arow[j] != nullptr && kin)
-                  ? *reinterpret_cast<const uint4*>(arow[j] + k0 + kc) : make_uint4(0, 0, 0, 0);
-      rb[j] = (brow[j] != nullptr && kin)
-                  ? *reinterpret_cast<const uint4*>(brow[j] + k0 + kc) : make_uint4(0, 0, 0, 0);
-    }
-  };
   f32x16 acc[2][2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -126,13 +107,39 @@ __global__ __launch_bounds__(kThreads, 2) void k_lm_gemm(const LmGemm G) {
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+  // Global -> LDS staging: chunk q = tid + 256 * j (j < kLmPasses) is tile
+  // row q / kLmCpr, hidden elements 8 * (q % kLmCpr) .. + 7 of the step.
+  const uint16_t* arow[kLmPasses];
+  const uint16_t* brow[kLmPasses];
+  const int kc = (tid % kLmCpr) * 8;
+#pragma unroll
+  for (int j = 0; j < kLmPasses; ++j) {
+    const int r = tid / kLmCpr + kLmRpp * j;
+    const int m = m0 + r;
+    int h = -1;
+    if (m < G.M) h = G.gather != nullptr ? G.gather[(size_t)m * G.gather_step] : m;
+    arow[j] = h >= 0 ? G.H + (size_t)h * G.D : nullptr;
+    const int v = v0 + r;
+    brow[j] = v < G.V ? G.W + (size_t)v * G.D : nullptr;
+  }
+  uint4 ra[kLmPasses], rb[kLmPasses];
+  auto fetch = [&](int k0) {
+    const bool kin = k0 + kc < G.D;
+#pragma unroll
+    for (int j = 0; j < kLmPasses; ++j) {
+      ra[j] = (arow[j] != nullptr && kin)
+                  ? *reinterpret_cast<const uint4*>(arow[j] + k0 + kc) : make_uint4(0, 0, 0, 0);
+      rb[j] = (brow[j] != nullptr && kin)
+                  ? *reinterpret_cast<const uint4*>(brow[j] + k0 + kc) : make_uint4(0, 0, 0, 0);
+    }
+  };
 
   fetch(0);
   for (int k0 = 0; k0 < G.D; k0 += kLmBK) {
     __syncthreads();  // every wave is done with the previous step's tiles
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = (tid >> 3) + 32 * j;
+    for (int j = 0; j < kLmPasses; ++j) {
+      const int r = tid / kLmCpr + kLmRpp * j;
       *reinterpret_cast<uint4*>(&sA[r * kLmLds + kc]) = ra[j];
       *reinterpret_cast<uint4*>(&sB[r * kLmLds + kc]) = rb[j];
     }
@@ -174,27 +181,51 @@ __global__ __launch_bounds__(kThreads, 2) void k_lm_gemm(const LmGemm G) {
       }
       s_tok[tid] = tok;
     }
-    __syncthreads();
+    // Each wave stages one 32 x 64 half of its sub-tile at a time in LDS
+    // (row-major, 4 floats of padding per row), then lane l reduces half of
+    // row l / 2 (32 ids) and pairs with lane l ^ 1 for the row's 64 ids.
+    constexpr int kEp = 64 + 4;
+    static_assert(4 * 32 * kEp * 4 <= (kLmBM + kLmBN) * kLmLds * 2, "epilogue staging fits");
+    float* const E = reinterpret_cast<float*>(sAB) + wave * 32 * kEp;
     const float c = G.c;
-    const int col0 = v0 + wn * 64 + (lane & 31);
+    const int r = lane >> 1, h = (lane & 1) * 32;
+    const int cb = v0 + wn * 64 + h;  // first vocabulary id of this lane's half row
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
+      __syncthreads();  // the operand tiles (a == 0) or the previous half are read
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int rl = wm * 64 + a * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        const float x0 = acc[a][0][i], x1 = acc[a][1][i];
-        const int tok = s_tok[rl];
-        if (tok == col0) G.tok_logits[G.unit0 + m0 + rl] = x0;
-        if (tok == col0 + 32) G.tok_logits[G.unit0 + m0 + rl] = x1;
-        const float y0 = col0 < G.V ? x0 : kNegInf;
-        const float y1 = col0 + 32 < G.V ? x1 : kNegInf;
-        const float mx = shfl_xor32_max(fmaxf(y0, y1));
-        const float R = ref_of(mx, c);
-        const float sm = shfl_xor32_sum(fast_exp2(fmaf(y0, c, -R)) + fast_exp2(fmaf(y1, c, -R)));
-        if ((lane & 31) == 0) {
-          s_pm[wn][rl] = mx;
-          s_ps[wn][rl] = sm;
-        }
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          E[(8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)) * kEp + b * 32 + (lane & 31)] = acc[a][b][i];
+      __syncthreads();
+      float x[32];
+#pragma unroll
+      for (int j = 0; j < 32; j += 4) {
+        const float4 t = *reinterpret_cast<const float4*>(&E[r * kEp + h + j]);
+        x[j] = t.x;
+        x[j + 1] = t.y;
+        x[j + 2] = t.z;
+        x[j + 3] = t.w;
+      }
+      const int rl = wm * 64 + a * 32 + r;
+      const int tok = s_tok[rl];
+      if (tok >= cb && tok < cb + 32) G.tok_logits[G.unit0 + m0 + rl] = E[r * kEp + h + (tok - cb)];
+      float mx = kNegInf;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        if (cb + j >= G.V) x[j] = kNegInf;
+        mx = fmaxf(mx, x[j]);
+      }
+      mx = fmaxf(mx, dpp_f<0xB1>(mx));  // quad_perm [1,0,3,2]: lane l ^ 1
+      const float R = ref_of(mx, c);
+      float sm = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) sm += fast_exp2(fmaf(x[j], c, -R));
+      sm += dpp_f<0xB1>(sm);
+      if ((lane & 1) == 0) {
+        s_pm[wn][rl] = mx;
+        s_ps[wn][rl] = sm;
       }
     }
     __syncthreads();
@@ -394,8 +425,8 @@ extern "C" int spec_verify_lmhead(const void* hidden_draft, const void* weight_d
     const long long per_xcd = (L.NT + kXcds - 1) / kXcds;  // vocabulary tiles per XCD
     return std::make_pair(MT, (unsigned)(per_xcd * MT * kXcds));
   };
-  // stage events: before the draft statistics, then after the draft and the
-  // target statistics, the merge and plan, the row logits and the draw
+  // stage events: before the statistics GEMMs, then after them, after the
+  // merge and decision, after the draw rows' GEMMs, and after the draw
   int e = 0;
   auto stage = [&]() {
     if (stage_events != nullptr && e < n_stage_events)
@@ -403,28 +434,31 @@ extern "C" int spec_verify_lmhead(const void* hidden_draft, const void* weight_d
     return true;
   };
   if (!stage()) return SV_EHIP;
-  LmGemm G{};
-  G.V = V;
-  G.NT = L.NT;
-  G.part = part;
-  G.tok_logits = P.tok_logits;
-  G.K = K;
-  G.tokens = draft_tokens;
-  G.c = P.c;
-  // statistics of the draft rows, then of the target rows
-  if (total_draft > 0) {
-    auto [MT, blocks] = grid_of(total_draft);
-    G.H = static_cast<const uint16_t*>(hidden_draft);
-    G.W = static_cast<const uint16_t*>(weight_draft);
-    G.D = d_draft;
-    G.M = total_draft;
-    G.MT = MT;
-    G.unit0 = 0;
-    G.target = 0;
-    hipLaunchKernelGGL(k_lm_gemm<true>, dim3(blocks), dim3(kThreads), 0, stream, G);
-  }
-  if (!stage()) return SV_EHIP;
+  // statistics of the draft rows and of the target rows, one launch
+  LmPair S{};
+  unsigned blocks_stats = 0;
   {
+    LmGemm G{};
+    G.V = V;
+    G.NT = L.NT;
+    G.part = part;
+    G.tok_logits = P.tok_logits;
+    G.K = K;
+    G.tokens = draft_tokens;
+    G.c = P.c;
+    if (total_draft > 0) {
+      auto [MT, blocks] = grid_of(total_draft);
+      G.H = static_cast<const uint16_t*>(hidden_draft);
+      G.W = static_cast<const uint16_t*>(weight_draft);
+      G.D = d_draft;
+      G.M = total_draft;
+      G.MT = MT;
+      G.unit0 = 0;
+      G.target = 0;
+      S.g[0] = G;
+      S.n0 = (int)blocks;
+      blocks_stats = blocks;
+    }
     auto [MT, blocks] = grid_of(rows);
     G.H = static_cast<const uint16_t*>(hidden_target);
     G.W = static_cast<const uint16_t*>(weight_target);
@@ -433,22 +467,26 @@ extern "C" int spec_verify_lmhead(const void* hidden_draft, const void* weight_d
     G.MT = MT;
     G.unit0 = total_draft;
     G.target = 1;
-    hipLaunchKernelGGL(k_lm_gemm<true>, dim3(blocks), dim3(kThreads), 0, stream, G);
+    S.g[1] = G;
+    blocks_stats += blocks;
   }
+  hipLaunchKernelGGL(k_lm_gemm<true>, dim3(blocks_stats), dim3(kThreads), 0, stream, S);
   if (hipGetLastError() != hipSuccess || !stage()) return SV_EHIP;
   hipLaunchKernelGGL(k_lm_merge, dim3((unsigned)(total_draft + rows)), dim3(kThreads), 0, stream,
                      part, P.slots, L.NT, P.c);
   if (hipGetLastError() != hipSuccess) return SV_EHIP;
   if (launch_lm_plan(P, stream) != hipSuccess || !stage()) return SV_EHIP;
-  // logits of the draw's rows: target row of position n -> row 2b, draft row -> 2b + 1
-  LmGemm R{};
-  R.V = V;
-  R.NT = L.NT;
-  R.out = lrows;
-  R.out_step = 2;
-  R.gather_step = 2;
-  R.M = B;
+  // logits of the draw's rows, one launch: target row of position n -> row 2b,
+  // draft row -> 2b + 1
   {
+    LmPair R2{};
+    LmGemm R{};
+    R.V = V;
+    R.NT = L.NT;
+    R.out = lrows;
+    R.out_step = 2;
+    R.gather_step = 2;
+    R.M = B;
     auto [MT, blocks] = grid_of(B);
     R.MT = MT;
     R.H = static_cast<const uint16_t*>(hidden_target);
@@ -456,15 +494,19 @@ extern "C" int spec_verify_lmhead(const void* hidden_draft, const void* weight_d
     R.D = d_target;
     R.gather = P.draw_rows;
     R.out_row0 = 0;
-    hipLaunchKernelGGL(k_lm_gemm<false>, dim3(blocks), dim3(kThreads), 0, stream, R);
+    R2.g[0] = R;
+    R2.n0 = (int)blocks;
+    unsigned total = blocks;
     if (total_draft > 0) {
       R.H = static_cast<const uint16_t*>(hidden_draft);
       R.W = static_cast<const uint16_t*>(weight_draft);
       R.D = d_draft;
       R.gather = P.draw_rows + 1;
       R.out_row0 = 1;
-      hipLaunchKernelGGL(k_lm_gemm<false>, dim3(blocks), dim3(kThreads), 0, stream, R);
+      R2.g[1] = R;
+      total += blocks;
     }
+    hipLaunchKernelGGL(k_lm_gemm<false>, dim3(total), dim3(kThreads), 0, stream, R2);
   }
   if (hipGetLastError() != hipSuccess || !stage()) return SV_EHIP;
   Plan DL{};
