@@ -31,12 +31,16 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Block tile: 128 rows x 128 vocabulary ids, 64 hidden elements per step.
-// Four waves in a 2 x 2 arrangement, each a 64 x 64 sub-tile of four 32 x 32
-// MFMA tiles. LDS rows carry 8 bf16 of padding so that the 32 lanes reading
+// Block tile: 128 rows x kLmBN vocabulary ids, 64 hidden elements per step.
+// Four waves in a 2 x 2 arrangement, each a 64 x (32 * kLmNB) sub-tile of
+// 2 x kLmNB 32 x 32 MFMA tiles. LDS rows carry 8 bf16 of padding so that the 32 lanes reading
 // one operand column touch distinct banks.
 constexpr int kLmBM = 128;
-constexpr int kLmBN = 128;
+#ifndef SV_LM_NB
+#define SV_LM_NB 2
+#endif
+constexpr int kLmNB = SV_LM_NB;              // 32-id MFMA tiles per wave along the vocabulary
+constexpr int kLmBN = 2 * 32 * kLmNB;        // two waves along the vocabulary
 #ifndef SV_LM_BK
 #define SV_LM_BK 64
 #endif
@@ -44,7 +48,8 @@ constexpr int kLmBK = SV_LM_BK;
 constexpr int kLmLds = kLmBK + 8;
 constexpr int kLmCpr = kLmBK / 8;            // 16-byte chunks per tile row and step
 constexpr int kLmRpp = kThreads / kLmCpr;    // tile rows one pass of the block stages
-constexpr int kLmPasses = kLmBM / kLmRpp;    // passes per operand tile
+constexpr int kLmPasses = kLmBM / kLmRpp;    // passes per hidden-state tile
+constexpr int kLmPassesB = kLmBN / kLmRpp;   // passes per weight tile
 constexpr int kXcds = 8;  // blocks are dealt round-robin to the eight XCDs
 
 struct LmGemm {
@@ -83,11 +88,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_lm_gemm(const LmPair PR) {
   const bool second = (int)blockIdx.x >= PR.n0;
   const LmGemm& G = PR.g[second ? 1 : 0];
   // operand tiles; after the main loop the statistics epilogue reuses them
-  __shared__ __align__(16) uint16_t sAB[(kLmBM + kLmBN) * kLmLds];
+  // (four waves x 32 rows x 68 floats)
+  constexpr int kOpWords = (kLmBM + kLmBN) * kLmLds;
+  constexpr int kEpWords = 4 * 32 * (64 + 4) * 2;
+  __shared__ __align__(16) uint16_t sAB[kOpWords > kEpWords ? kOpWords : kEpWords];
   uint16_t* const sA = sAB;
   uint16_t* const sB = sAB + kLmBM * kLmLds;
-  __shared__ float s_pm[2][kLmBM];
-  __shared__ float s_ps[2][kLmBM];
+  __shared__ float s_pm[kLmNB][kLmBM];
+  __shared__ float s_ps[kLmNB][kLmBM];
   __shared__ int s_tok[kLmBM];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -100,17 +108,17 @@ __global__ __launch_bounds__(kThreads, 2) void k_lm_gemm(const LmPair PR) {
   if (vt >= G.NT) return;
   const int m0 = mt * kLmBM, v0 = vt * kLmBN;
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][kLmNB];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < kLmNB; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
   // Global -> LDS staging: chunk q = tid + 256 * j (j < kLmPasses) is tile
   // row q / kLmCpr, hidden elements 8 * (q % kLmCpr) .. + 7 of the step.
   const uint16_t* arow[kLmPasses];
-  const uint16_t* brow[kLmPasses];
+  const uint16_t* brow[kLmPassesB];
   const int kc = (tid % kLmCpr) * 8;
 #pragma unroll
   for (int j = 0; j < kLmPasses; ++j) {
@@ -119,30 +127,34 @@ __global__ __launch_bounds__(kThreads, 2) void k_lm_gemm(const LmPair PR) {
     int h = -1;
     if (m < G.M) h = G.gather != nullptr ? G.gather[(size_t)m * G.gather_step] : m;
     arow[j] = h >= 0 ? G.H + (size_t)h * G.D : nullptr;
-    const int v = v0 + r;
+  }
+#pragma unroll
+  for (int j = 0; j < kLmPassesB; ++j) {
+    const int v = v0 + tid / kLmCpr + kLmRpp * j;
     brow[j] = v < G.V ? G.W + (size_t)v * G.D : nullptr;
   }
-  uint4 ra[kLmPasses], rb[kLmPasses];
+  uint4 ra[kLmPasses], rb[kLmPassesB];
   auto fetch = [&](int k0) {
     const bool kin = k0 + kc < G.D;
 #pragma unroll
-    for (int j = 0; j < kLmPasses; ++j) {
+    for (int j = 0; j < kLmPasses; ++j)
       ra[j] = (arow[j] != nullptr && kin)
                   ? *reinterpret_cast<const uint4*>(arow[j] + k0 + kc) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < kLmPassesB; ++j)
       rb[j] = (brow[j] != nullptr && kin)
                   ? *reinterpret_cast<const uint4*>(brow[j] + k0 + kc) : make_uint4(0, 0, 0, 0);
-    }
   };
 
   fetch(0);
   for (int k0 = 0; k0 < G.D; k0 += kLmBK) {
     __syncthreads();  // every wave is done with the previous step's tiles
 #pragma unroll
-    for (int j = 0; j < kLmPasses; ++j) {
-      const int r = tid / kLmCpr + kLmRpp * j;
-      *reinterpret_cast<uint4*>(&sA[r * kLmLds + kc]) = ra[j];
-      *reinterpret_cast<uint4*>(&sB[r * kLmLds + kc]) = rb[j];
-    }
+    for (int j = 0; j < kLmPasses; ++j)
+      *reinterpret_cast<uint4*>(&sA[(tid / kLmCpr + kLmRpp * j) * kLmLds + kc]) = ra[j];
+#pragma unroll
+    for (int j = 0; j < kLmPassesB; ++j)
+      *reinterpret_cast<uint4*>(&sB[(tid / kLmCpr + kLmRpp * j) * kLmLds + kc]) = rb[j];
     __syncthreads();
     if (k0 + kLmBK < G.D) fetch(k0 + kLmBK);  // next step's operands, in flight during the MFMAs
 #pragma unroll
@@ -150,23 +162,24 @@ __global__ __launch_bounds__(kThreads, 2) void k_lm_gemm(const LmPair PR) {
       // lane l holds 8 consecutive hidden elements (16 * ks + 8 * (l / 32) ...)
       // of row (or vocabulary id) l % 32 of each 32 x 32 tile
       const int kk = ks * 16 + (lane >> 5) * 8;
-      bf16x8 af[2], bfr[2];
+      bf16x8 af[2], bfr[kLmNB];
 #pragma unroll
       for (int a = 0; a < 2; ++a)
         af[a] = *reinterpret_cast<const bf16x8*>(&sA[(wm * 64 + a * 32 + (lane & 31)) * kLmLds + kk]);
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-        bfr[b] = *reinterpret_cast<const bf16x8*>(&sB[(wn * 64 + b * 32 + (lane & 31)) * kLmLds + kk]);
+      for (int b = 0; b < kLmNB; ++b)
+        bfr[b] = *reinterpret_cast<const bf16x8*>(
+            &sB[(wn * 32 * kLmNB + b * 32 + (lane & 31)) * kLmLds + kk]);
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < kLmNB; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
     }
   }
 
   // Element i of tile (a, b) in lane l: row wm*64 + a*32 + 8*(i/4) + 4*(l/32)
-  // + i%4, vocabulary id v0 + wn*64 + b*32 + l%32.
+  // + i%4, vocabulary id v0 + wn*32*kLmNB + b*32 + l%32.
   if constexpr (STATS) {
     if (tid < kLmBM) {
       const int m = m0 + tid;
@@ -181,57 +194,62 @@ __global__ __launch_bounds__(kThreads, 2) void k_lm_gemm(const LmPair PR) {
       }
       s_tok[tid] = tok;
     }
-    // Each wave stages one 32 x 64 half of its sub-tile at a time in LDS
+    // Each wave stages one 32 x 64 slice of its sub-tile at a time in LDS
     // (row-major, 4 floats of padding per row), then lane l reduces half of
-    // row l / 2 (32 ids) and pairs with lane l ^ 1 for the row's 64 ids.
+    // row l / 2 (32 ids) and pairs with lane l ^ 1 for the slice's 64 ids.
+    // Slot wn * kLmNB / 2 + slice of s_pm / s_ps holds each row's partial.
     constexpr int kEp = 64 + 4;
-    static_assert(4 * 32 * kEp * 4 <= (kLmBM + kLmBN) * kLmLds * 2, "epilogue staging fits");
     float* const E = reinterpret_cast<float*>(sAB) + wave * 32 * kEp;
     const float c = G.c;
     const int r = lane >> 1, h = (lane & 1) * 32;
-    const int cb = v0 + wn * 64 + h;  // first vocabulary id of this lane's half row
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
-      __syncthreads();  // the operand tiles (a == 0) or the previous half are read
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int sl = 0; sl < kLmNB / 2; ++sl) {
+        __syncthreads();  // the operand tiles, or the previous slice, are read
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          E[(8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)) * kEp + b * 32 + (lane & 31)] = acc[a][b][i];
-      __syncthreads();
-      float x[32];
+        for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-      for (int j = 0; j < 32; j += 4) {
-        const float4 t = *reinterpret_cast<const float4*>(&E[r * kEp + h + j]);
-        x[j] = t.x;
-        x[j + 1] = t.y;
-        x[j + 2] = t.z;
-        x[j + 3] = t.w;
-      }
-      const int rl = wm * 64 + a * 32 + r;
-      const int tok = s_tok[rl];
-      if (tok >= cb && tok < cb + 32) G.tok_logits[G.unit0 + m0 + rl] = E[r * kEp + h + (tok - cb)];
-      float mx = kNegInf;
+          for (int i = 0; i < 16; ++i)
+            E[(8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)) * kEp + bb * 32 + (lane & 31)] =
+                acc[a][2 * sl + bb][i];
+        __syncthreads();
+        float x[32];
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        if (cb + j >= G.V) x[j] = kNegInf;
-        mx = fmaxf(mx, x[j]);
-      }
-      mx = fmaxf(mx, dpp_f<0xB1>(mx));  // quad_perm [1,0,3,2]: lane l ^ 1
-      const float R = ref_of(mx, c);
-      float sm = 0.0f;
+        for (int j = 0; j < 32; j += 4) {
+          const float4 t = *reinterpret_cast<const float4*>(&E[r * kEp + h + j]);
+          x[j] = t.x;
+          x[j + 1] = t.y;
+          x[j + 2] = t.z;
+          x[j + 3] = t.w;
+        }
+        const int cb = v0 + wn * 32 * kLmNB + sl * 64 + h;  // first id of this lane's half row
+        const int rl = wm * 64 + a * 32 + r;
+        const int tok = s_tok[rl];
+        if (tok >= cb && tok < cb + 32) G.tok_logits[G.unit0 + m0 + rl] = E[r * kEp + h + (tok - cb)];
+        float mx = kNegInf;
 #pragma unroll
-      for (int j = 0; j < 32; ++j) sm += fast_exp2(fmaf(x[j], c, -R));
-      sm += dpp_f<0xB1>(sm);
-      if ((lane & 1) == 0) {
-        s_pm[wn][rl] = mx;
-        s_ps[wn][rl] = sm;
+        for (int j = 0; j < 32; ++j) {
+          if (cb + j >= G.V) x[j] = kNegInf;
+          mx = fmaxf(mx, x[j]);
+        }
+        mx = fmaxf(mx, dpp_f<0xB1>(mx));  // quad_perm [1,0,3,2]: lane l ^ 1
+        const float R = ref_of(mx, c);
+        float sm = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) sm += fast_exp2(fmaf(x[j], c, -R));
+        sm += dpp_f<0xB1>(sm);
+        if ((lane & 1) == 0) {
+          s_pm[wn * (kLmNB / 2) + sl][rl] = mx;
+          s_ps[wn * (kLmNB / 2) + sl][rl] = sm;
+        }
       }
     }
     __syncthreads();
     if (tid < kLmBM && m0 + tid < G.M) {
       float mm = s_pm[0][tid], ss = s_ps[0][tid];
-      merge_ms(mm, ss, s_pm[1][tid], s_ps[1][tid], c);
+#pragma unroll
+      for (int q = 1; q < kLmNB; ++q) merge_ms(mm, ss, s_pm[q][tid], s_ps[q][tid], c);
       G.part[(size_t)(G.unit0 + m0 + tid) * G.NT + vt] = pack_ms(mm, ss);
     }
   } else {
@@ -245,8 +263,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_lm_gemm(const LmPair PR) {
         if (G.gather != nullptr && G.gather[(size_t)m * G.gather_step] < 0) continue;
         float* orow = G.out + (size_t)(m * G.out_step + G.out_row0) * G.V;
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const int v = v0 + wn * 64 + b * 32 + (lane & 31);
+        for (int b = 0; b < kLmNB; ++b) {
+          const int v = v0 + wn * 32 * kLmNB + b * 32 + (lane & 31);
           if (v < G.V) orow[v] = acc[a][b][i];
         }
       }
