@@ -111,6 +111,23 @@ def test_lmhead_parity_small(ov):
     _check(w, "small")
 
 
+def _random_config(i):
+    """Seeded random small shape: rows, vocabulary and hidden sizes that end
+    mid-tile, K from 0 to 12, temperatures from 0.3 to 1.7."""
+    rng = np.random.default_rng([4242, i])
+    dq = 8 * int(rng.integers(1, 65))
+    dp = dq + 8 * int(rng.integers(0, 65))
+    return dict(B=int(rng.integers(1, 9)), K=int(rng.integers(0, 13)),
+                V=int(rng.integers(2, 6000)), d_draft=dq, d_target=dp,
+                temperature=float(np.round(rng.uniform(0.3, 1.7), 2)))
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_lmhead_parity_random(i):
+    w = W.make_lmhead(**_random_config(i), seed=2500 + i)
+    _check(w, f"random {i}")
+
+
 def test_lmhead_workspace_returns_to_zero_and_serves_other_shapes():
     import speculative_decoding_verification_13_amd as sv
     big = dict(B=6, K=5, V=8000, d_draft=128, d_target=256)
