@@ -5,7 +5,7 @@
 // the final draw needs per sequence (p_n, and q_n for a residual) are formed
 // again and kept, as fp32.
 //
-//   k_lm_gemm<true>   draft rows, then target rows: per (row, 128-id vocab
+//   k_lm_gemm<true>   draft rows, then target rows: per (row, 256-id vocab
 //                     tile) the packed (max, sum of 2^(l*c - R)) partial, and
 //                     the logit at the row's token
 //   k_lm_merge        per row: the vocabulary tiles' partials merged into one
@@ -31,26 +31,44 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Block tile: 128 rows x kLmBN vocabulary ids, 64 hidden elements per step.
-// Four waves in a 2 x 2 arrangement, each a 64 x (32 * kLmNB) sub-tile of
-// 2 x kLmNB 32 x 32 MFMA tiles. LDS rows carry 8 bf16 of padding so that the 32 lanes reading
+// Block tile: 128 rows x (WN * 32 * kLmNB) vocabulary ids, 64 hidden elements
+// per step. Waves in a 2 x WN arrangement, each a 64 x (32 * kLmNB) sub-tile
+// of 2 x kLmNB 32 x 32 MFMA tiles. LDS rows carry 8 bf16 of padding so that the 32 lanes reading
 // one operand column touch distinct banks.
 constexpr int kLmBM = 128;
 #ifndef SV_LM_NB
 #define SV_LM_NB 2
 #endif
 constexpr int kLmNB = SV_LM_NB;              // 32-id MFMA tiles per wave along the vocabulary
-constexpr int kLmBN = 2 * 32 * kLmNB;        // two waves along the vocabulary
+// Waves along the vocabulary: four for the statistics GEMM (a 256-id tile, so
+// each row tile of hidden states is re-read by half as many blocks), two for
+// the draw rows' GEMM (HBM-bound; its 128-id tile keeps three blocks per
+// compute unit).
+#ifndef SV_LM_WN
+#define SV_LM_WN 4
+#endif
+constexpr int kLmStatsWN = SV_LM_WN;
+constexpr int kLmRowsWN = 2;
 #ifndef SV_LM_BK
 #define SV_LM_BK 64
 #endif
 constexpr int kLmBK = SV_LM_BK;
 constexpr int kLmLds = kLmBK + 8;
 constexpr int kLmCpr = kLmBK / 8;            // 16-byte chunks per tile row and step
-constexpr int kLmRpp = kThreads / kLmCpr;    // tile rows one pass of the block stages
-constexpr int kLmPasses = kLmBM / kLmRpp;    // passes per hidden-state tile
-constexpr int kLmPassesB = kLmBN / kLmRpp;   // passes per weight tile
 constexpr int kXcds = 8;  // blocks are dealt round-robin to the eight XCDs
+
+// Shape of a block with WN waves along the vocabulary.
+template <int WN>
+struct LmTile {
+  static constexpr int kThreads = 2 * WN * kWave;        // two waves along the rows
+  static constexpr int kBN = WN * 32 * kLmNB;            // vocabulary ids per block
+  static constexpr int kSlots = WN * kLmNB / 2;          // 64-id slices of a tile row
+  static constexpr int kRpp = kThreads / kLmCpr;         // tile rows one staging pass covers
+  static constexpr int kPassesA = kLmBM / kRpp;          // passes per hidden-state tile
+  static constexpr int kPassesB = kBN / kRpp;            // passes per weight tile
+  static_assert(kLmNB % 2 == 0 && kLmBM % kRpp == 0 && kBN % kRpp == 0,
+                "the staging passes and the epilogue's 64-id slices must tile the block");
+};
 
 struct LmGemm {
   const uint16_t* H;   // hidden rows, bf16 bits, row stride D
@@ -79,23 +97,26 @@ struct LmPair {
   int n0;
 };
 
-// One block: a 128 x 128 tile of logits. The block order is XCD-aware: block
+// One block: a 128 x LmTile<WN>::kBN tile of logits. The block order is XCD-aware: block
 // g runs on XCD g % 8, and the row tiles of one vocabulary tile are
 // consecutive blocks of one XCD, so its weight tile is fetched into that XCD's
 // L2 once and read from there by the other row tiles.
-template <bool STATS>
-__global__ __launch_bounds__(kThreads, 2) void k_lm_gemm(const LmPair PR) {
+template <bool STATS, int WN>
+__global__ __launch_bounds__(LmTile<WN>::kThreads, 2) void k_lm_gemm(const LmPair PR) {
+  using T = LmTile<WN>;
+  constexpr int kLmBN = T::kBN, kLmRpp = T::kRpp;
+  constexpr int kLmPasses = T::kPassesA, kLmPassesB = T::kPassesB, kLmSlots = T::kSlots;
   const bool second = (int)blockIdx.x >= PR.n0;
   const LmGemm& G = PR.g[second ? 1 : 0];
   // operand tiles; after the main loop the statistics epilogue reuses them
-  // (four waves x 32 rows x 68 floats)
+  // (each wave 32 rows x 68 floats)
   constexpr int kOpWords = (kLmBM + kLmBN) * kLmLds;
-  constexpr int kEpWords = 4 * 32 * (64 + 4) * 2;
+  constexpr int kEpWords = 2 * WN * 32 * (64 + 4) * 2;
   __shared__ __align__(16) uint16_t sAB[kOpWords > kEpWords ? kOpWords : kEpWords];
   uint16_t* const sA = sAB;
   uint16_t* const sB = sAB + kLmBM * kLmLds;
-  __shared__ float s_pm[kLmNB][kLmBM];
-  __shared__ float s_ps[kLmNB][kLmBM];
+  __shared__ float s_pm[kLmSlots][kLmBM];
+  __shared__ float s_ps[kLmSlots][kLmBM];
   __shared__ int s_tok[kLmBM];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -115,7 +136,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_lm_gemm(const LmPair PR) {
     for (int b = 0; b < kLmNB; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
-  // Global -> LDS staging: chunk q = tid + 256 * j (j < kLmPasses) is tile
+  // Global -> LDS staging: chunk q = tid + T::kThreads * j (j < kLmPasses) is tile
   // row q / kLmCpr, hidden elements 8 * (q % kLmCpr) .. + 7 of the step.
   const uint16_t* arow[kLmPasses];
   const uint16_t* brow[kLmPassesB];
@@ -249,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_lm_gemm(const LmPair PR) {
     if (tid < kLmBM && m0 + tid < G.M) {
       float mm = s_pm[0][tid], ss = s_ps[0][tid];
 #pragma unroll
-      for (int q = 1; q < kLmNB; ++q) merge_ms(mm, ss, s_pm[q][tid], s_ps[q][tid], c);
+      for (int q = 1; q < kLmSlots; ++q) merge_ms(mm, ss, s_pm[q][tid], s_ps[q][tid], c);
       G.part[(size_t)(G.unit0 + m0 + tid) * G.NT + vt] = pack_ms(mm, ss);
     }
   } else {
@@ -329,7 +350,7 @@ bool lm_plan(int B, int K, int V, LmPlan& L) {
   if (B < 0 || K < 0 || K > SV_MAX_K || V < 1 || V > (1 << 30)) return false;
   const long long units = (long long)B * K + (long long)B * (K + 1);
   if (units > INT_MAX) return false;
-  L.NT = (V + kLmBN - 1) / kLmBN;
+  L.NT = (V + LmTile<kLmStatsWN>::kBN - 1) / LmTile<kLmStatsWN>::kBN;
   const bool vec = V % 4 == 0;
   L.nvec = vec ? V / 4 : V;
   L.dchunks = (L.nvec + kDrawVecs - 1) / kDrawVecs;
@@ -438,9 +459,9 @@ extern "C" int spec_verify_lmhead(const void* hidden_draft, const void* weight_d
   P.draw_rows = reinterpret_cast<int*>(ws + L.off_draw_rows);
   unsigned long long* part = reinterpret_cast<unsigned long long*>(ws + L.off_part);
 
-  auto grid_of = [&](int M) {
+  auto grid_of = [&](int M, int NT) {
     const int MT = (M + kLmBM - 1) / kLmBM;
-    const long long per_xcd = (L.NT + kXcds - 1) / kXcds;  // vocabulary tiles per XCD
+    const long long per_xcd = (NT + kXcds - 1) / kXcds;  // vocabulary tiles per XCD
     return std::make_pair(MT, (unsigned)(per_xcd * MT * kXcds));
   };
   // stage events: before the statistics GEMMs, then after them, after the
@@ -465,7 +486,7 @@ extern "C" int spec_verify_lmhead(const void* hidden_draft, const void* weight_d
     G.tokens = draft_tokens;
     G.c = P.c;
     if (total_draft > 0) {
-      auto [MT, blocks] = grid_of(total_draft);
+      auto [MT, blocks] = grid_of(total_draft, L.NT);
       G.H = static_cast<const uint16_t*>(hidden_draft);
       G.W = static_cast<const uint16_t*>(weight_draft);
       G.D = d_draft;
@@ -477,7 +498,7 @@ extern "C" int spec_verify_lmhead(const void* hidden_draft, const void* weight_d
       S.n0 = (int)blocks;
       blocks_stats = blocks;
     }
-    auto [MT, blocks] = grid_of(rows);
+    auto [MT, blocks] = grid_of(rows, L.NT);
     G.H = static_cast<const uint16_t*>(hidden_target);
     G.W = static_cast<const uint16_t*>(weight_target);
     G.D = d_target;
@@ -488,7 +509,8 @@ extern "C" int spec_verify_lmhead(const void* hidden_draft, const void* weight_d
     S.g[1] = G;
     blocks_stats += blocks;
   }
-  hipLaunchKernelGGL(k_lm_gemm<true>, dim3(blocks_stats), dim3(kThreads), 0, stream, S);
+  hipLaunchKernelGGL((k_lm_gemm<true, kLmStatsWN>), dim3(blocks_stats),
+                     dim3(LmTile<kLmStatsWN>::kThreads), 0, stream, S);
   if (hipGetLastError() != hipSuccess || !stage()) return SV_EHIP;
   hipLaunchKernelGGL(k_lm_merge, dim3((unsigned)(total_draft + rows)), dim3(kThreads), 0, stream,
                      part, P.slots, L.NT, P.c);
@@ -500,12 +522,12 @@ extern "C" int spec_verify_lmhead(const void* hidden_draft, const void* weight_d
     LmPair R2{};
     LmGemm R{};
     R.V = V;
-    R.NT = L.NT;
+    R.NT = (V + LmTile<kLmRowsWN>::kBN - 1) / LmTile<kLmRowsWN>::kBN;
     R.out = lrows;
     R.out_step = 2;
     R.gather_step = 2;
     R.M = B;
-    auto [MT, blocks] = grid_of(B);
+    auto [MT, blocks] = grid_of(B, R.NT);
     R.MT = MT;
     R.H = static_cast<const uint16_t*>(hidden_target);
     R.W = static_cast<const uint16_t*>(weight_target);
@@ -524,7 +546,8 @@ extern "C" int spec_verify_lmhead(const void* hidden_draft, const void* weight_d
       R2.g[1] = R;
       total += blocks;
     }
-    hipLaunchKernelGGL(k_lm_gemm<false>, dim3(total), dim3(kThreads), 0, stream, R2);
+    hipLaunchKernelGGL((k_lm_gemm<false, kLmRowsWN>), dim3(total),
+                       dim3(LmTile<kLmRowsWN>::kThreads), 0, stream, R2);
   }
   if (hipGetLastError() != hipSuccess || !stage()) return SV_EHIP;
   Plan DL{};
