@@ -31,24 +31,20 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Block tile: 128 rows x (WN * 32 * kLmNB) vocabulary ids, 64 hidden elements
-// per step. Waves in a 2 x WN arrangement, each a 64 x (32 * kLmNB) sub-tile
-// of 2 x kLmNB 32 x 32 MFMA tiles. LDS rows carry 8 bf16 of padding so that the 32 lanes reading
+// Block tile: 128 rows x (WN * 32 * NB) vocabulary ids, 64 hidden elements
+// per step. Waves in a 2 x WN arrangement, each a 64 x (32 * NB) sub-tile of
+// 2 x NB 32 x 32 MFMA tiles. LDS rows carry 8 bf16 of padding so that the 32 lanes reading
 // one operand column touch distinct banks.
 constexpr int kLmBM = 128;
-#ifndef SV_LM_NB
-#define SV_LM_NB 2
-#endif
-constexpr int kLmNB = SV_LM_NB;              // 32-id MFMA tiles per wave along the vocabulary
-// Waves along the vocabulary: four for the statistics GEMM (a 256-id tile, so
-// each row tile of hidden states is re-read by half as many blocks), two for
-// the draw rows' GEMM (HBM-bound; its 128-id tile keeps three blocks per
-// compute unit).
-#ifndef SV_LM_WN
-#define SV_LM_WN 4
-#endif
-constexpr int kLmStatsWN = SV_LM_WN;
-constexpr int kLmRowsWN = 2;
+// Shapes of the two GEMMs (waves along the vocabulary, 32-id MFMA tiles per
+// wave along it). The statistics GEMM takes eight waves of 64 x 64: a 256-id
+// tile, so each row tile of hidden states is re-read by half as many blocks
+// as with 128 ids, at four waves per SIMD. The draw rows' GEMM is HBM-bound
+// (one live row per sequence and model): eight waves of 64 x 128, a 512-id
+// tile, keep the most weight bytes in flight per block (measured 303-306 us
+// against 318-320 with four such waves and 357 with four waves of 64 x 64).
+constexpr int kLmStatsWN = 4, kLmStatsNB = 2;
+constexpr int kLmRowsWN = 4, kLmRowsNB = 4;
 #ifndef SV_LM_BK
 #define SV_LM_BK 64
 #endif
@@ -57,16 +53,16 @@ constexpr int kLmLds = kLmBK + 8;
 constexpr int kLmCpr = kLmBK / 8;            // 16-byte chunks per tile row and step
 constexpr int kXcds = 8;  // blocks are dealt round-robin to the eight XCDs
 
-// Shape of a block with WN waves along the vocabulary.
-template <int WN>
+// Shape of a block with WN waves along the vocabulary, each NB MFMA tiles wide.
+template <int WN, int NB>
 struct LmTile {
   static constexpr int kThreads = 2 * WN * kWave;        // two waves along the rows
-  static constexpr int kBN = WN * 32 * kLmNB;            // vocabulary ids per block
-  static constexpr int kSlots = WN * kLmNB / 2;          // 64-id slices of a tile row
+  static constexpr int kBN = WN * 32 * NB;               // vocabulary ids per block
+  static constexpr int kSlots = WN * NB / 2;             // 64-id slices of a tile row
   static constexpr int kRpp = kThreads / kLmCpr;         // tile rows one staging pass covers
   static constexpr int kPassesA = kLmBM / kRpp;          // passes per hidden-state tile
   static constexpr int kPassesB = kBN / kRpp;            // passes per weight tile
-  static_assert(kLmNB % 2 == 0 && kLmBM % kRpp == 0 && kBN % kRpp == 0,
+  static_assert(NB % 2 == 0 && kLmBM % kRpp == 0 && kBN % kRpp == 0,
                 "the staging passes and the epilogue's 64-id slices must tile the block");
 };
 
@@ -97,13 +93,14 @@ struct LmPair {
   int n0;
 };
 
-// One block: a 128 x LmTile<WN>::kBN tile of logits. The block order is XCD-aware: block
+// One block: a 128 x LmTile<WN, NB>::kBN tile of logits. The block order is XCD-aware: block
 // g runs on XCD g % 8, and the row tiles of one vocabulary tile are
 // consecutive blocks of one XCD, so its weight tile is fetched into that XCD's
 // L2 once and read from there by the other row tiles.
-template <bool STATS, int WN>
-__global__ __launch_bounds__(LmTile<WN>::kThreads, 2) void k_lm_gemm(const LmPair PR) {
-  using T = LmTile<WN>;
+template <bool STATS, int WN, int NB>
+__global__ __launch_bounds__(2 * WN * kWave, 2) void k_lm_gemm(const LmPair PR) {
+  using T = LmTile<WN, NB>;
+  constexpr int kLmNB = NB;
   constexpr int kLmBN = T::kBN, kLmRpp = T::kRpp;
   constexpr int kLmPasses = T::kPassesA, kLmPassesB = T::kPassesB, kLmSlots = T::kSlots;
   const bool second = (int)blockIdx.x >= PR.n0;
@@ -350,7 +347,7 @@ bool lm_plan(int B, int K, int V, LmPlan& L) {
   if (B < 0 || K < 0 || K > SV_MAX_K || V < 1 || V > (1 << 30)) return false;
   const long long units = (long long)B * K + (long long)B * (K + 1);
   if (units > INT_MAX) return false;
-  L.NT = (V + LmTile<kLmStatsWN>::kBN - 1) / LmTile<kLmStatsWN>::kBN;
+  L.NT = (V + LmTile<kLmStatsWN, kLmStatsNB>::kBN - 1) / LmTile<kLmStatsWN, kLmStatsNB>::kBN;
   const bool vec = V % 4 == 0;
   L.nvec = vec ? V / 4 : V;
   L.dchunks = (L.nvec + kDrawVecs - 1) / kDrawVecs;
@@ -509,8 +506,8 @@ extern "C" int spec_verify_lmhead(const void* hidden_draft, const void* weight_d
     S.g[1] = G;
     blocks_stats += blocks;
   }
-  hipLaunchKernelGGL((k_lm_gemm<true, kLmStatsWN>), dim3(blocks_stats),
-                     dim3(LmTile<kLmStatsWN>::kThreads), 0, stream, S);
+  hipLaunchKernelGGL((k_lm_gemm<true, kLmStatsWN, kLmStatsNB>), dim3(blocks_stats),
+                     dim3(LmTile<kLmStatsWN, kLmStatsNB>::kThreads), 0, stream, S);
   if (hipGetLastError() != hipSuccess || !stage()) return SV_EHIP;
   hipLaunchKernelGGL(k_lm_merge, dim3((unsigned)(total_draft + rows)), dim3(kThreads), 0, stream,
                      part, P.slots, L.NT, P.c);
@@ -522,7 +519,7 @@ extern "C" int spec_verify_lmhead(const void* hidden_draft, const void* weight_d
     LmPair R2{};
     LmGemm R{};
     R.V = V;
-    R.NT = (V + LmTile<kLmRowsWN>::kBN - 1) / LmTile<kLmRowsWN>::kBN;
+    R.NT = (V + LmTile<kLmRowsWN, kLmRowsNB>::kBN - 1) / LmTile<kLmRowsWN, kLmRowsNB>::kBN;
     R.out = lrows;
     R.out_step = 2;
     R.gather_step = 2;
@@ -546,8 +543,8 @@ extern "C" int spec_verify_lmhead(const void* hidden_draft, const void* weight_d
       R2.g[1] = R;
       total += blocks;
     }
-    hipLaunchKernelGGL((k_lm_gemm<false, kLmRowsWN>), dim3(total),
-                       dim3(LmTile<kLmRowsWN>::kThreads), 0, stream, R2);
+    hipLaunchKernelGGL((k_lm_gemm<false, kLmRowsWN, kLmRowsNB>), dim3(total),
+                       dim3(LmTile<kLmRowsWN, kLmRowsNB>::kThreads), 0, stream, R2);
   }
   if (hipGetLastError() != hipSuccess || !stage()) return SV_EHIP;
   Plan DL{};
