@@ -1002,19 +1002,30 @@ __global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
 // threshold theta (keep l >= theta) and the kept-set sum, found by a radix
 // descent on order-preserving keys. Each pass adds every logit's mass
 // 2^(l*c - R), in 40-bit fixed point (integer sums: exact and independent of
-// the order of addition), to the bin of its next key digit among the logits
-// whose higher digits match the levels fixed so far. Walking the bins from the
-// largest key down, the kept levels are those whose strictly-larger mass is
-// below top_p times the total; the last of them lies in the bin where the
-// running mass, this bin included, first reaches that bound. Digits of 11, 11
-// and 10 bits: two passes resolve a level of a widened bf16 or fp16 logit (the
-// key's low bits are then constant), three a level of an fp32 one. The row's
+// the order of addition), to the bin of its key among the logits whose keys
+// lie in the range fixed so far. Walking the bins from the largest key down,
+// the kept levels are those whose strictly-larger mass is below top_p times
+// the total; the last of them lies in the bin where the running mass, this bin
+// included, first reaches that bound, and the next pass splits that bin. The
+// first pass bins only the keys of the top window (masses from 2^-16 of the
+// maximum's up), in at most 2048 equal bins no narrower than one level (a
+// widened bf16 or fp16 logit's low 16 or 13 key bits are constant), and sums
+// the whole row's mass in registers: when the level lies in the window (the
+// usual case) and the window holds at most 2048 levels (a bf16 row at the
+// temperatures of sampling), one pass resolves it. Otherwise a pass bins the
+// keys below the window down to the 2^-40 cutoff, and each further pass
+// divides the bin by 2^11, so an fp32 level takes at most four. The row's
 // chunk partials (read here only) go back to zero.
 // Pages: aihero.vn "Speculative decoding", section "Cùng phân bố không có
 // nghĩa cùng chuỗi mỗi lần" (the same temperature, top-k and top-p on both
 // models' rows).
 constexpr int kNucBins = 2048;
+// The first pass bins only the logits within 2^-16 of the row maximum's mass
+// (the top window): at the sampling workloads it holds about 2% of a row's
+// logits and over 98% of its mass, so the top-p level nearly always lies in
+// it, and the rest of the row only adds to the total.
 constexpr double kNucScale = 1099511627776.0;  // 2^40
+constexpr float kNucTop = 16.0f;
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_nucleus(const Params P) {
@@ -1025,6 +1036,8 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(const Params P) {
   __shared__ unsigned long long s_base;
   __shared__ int s_cu[kCuLds];
   __shared__ float s_stat[2];
+  __shared__ unsigned s_kmin[2];
+  __shared__ unsigned long long s_tot[kThreads / kWave];
   __shared__ int s_bin;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -1045,6 +1058,24 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(const Params P) {
     }
     s_stat[0] = m;
     s_stat[1] = sm;
+    // The smallest keys whose logits pass the mass tests below (2^-40 and
+    // the top window's 2^-kNucTop): each test is monotone in the key, fails at
+    // -inf and holds at the maximum, so a bisection over the keys between
+    // finds the key exactly.
+    for (int t = 0; t < 2; ++t) {
+      const float cut = t == 0 ? -40.0f : -kNucTop;
+      unsigned lo = key_of(kNegInf), hi = lo;
+      if (__builtin_isfinite(m)) {
+        const float R0 = ref_of(m, c);
+        hi = key_of(m);
+        while (hi - lo > 1u) {
+          const unsigned mid = lo + (hi - lo) / 2u;
+          if (fmaf(float_of_key(mid), c, -R0) >= cut) hi = mid;
+          else lo = mid;
+        }
+      }
+      s_kmin[t] = hi;
+    }
   }
   __syncthreads();
   for (int k = tid; k < C; k += kThreads) sl[k] = 0ull;
@@ -1053,25 +1084,42 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(const Params P) {
   const float R = ref_of(m, c);
   const size_t roff = (size_t)row * P.V;
   const void* base = is_target ? P.target : P.draft;
-  constexpr int kLevels = (DT == SV_F32) ? 3 : 2;
-  const int shifts[3] = {21, 10, 0};
-  const int widths[3] = {11, 11, 10};
-  unsigned prefix = 0u, pmask = 0u;
+  // low key bits every level of the input type shares
+  constexpr int kLowBits = DT == SV_BF16 ? 16 : (DT == SV_F16 ? 13 : 0);
+  constexpr unsigned kLowMask = (1u << kLowBits) - 1u;
+  // The first pass bins the keys [kbase, kbase + span] of the top window
+  // (from the smallest key passing its test, widened to a level boundary, to
+  // the maximum's) and sums every logit's mass, the row total, in registers.
+  // When the crossing lies below the window, the next pass bins the keys
+  // below it that can carry mass.
+  const unsigned kb_all = s_kmin[0] & ~kLowMask, kb_top = s_kmin[1] & ~kLowMask;
+  unsigned kbase = 0u, span = 0u;
+  int s = kLowBits;
+  if (ok) {
+    kbase = kb_top;
+    span = key_of(m) - kbase;
+  }
+  bool found = false;  // a level has been resolved (else every level is kept)
   unsigned long long above = 0ull, kept = 0ull;
   double bound = 0.0;
-  for (int lv = 0; ok && lv < kLevels; ++lv) {
-    const int shift = shifts[lv], nb = 1 << widths[lv];
+  const int nb = kNucBins;
+  for (int lv = 0; ok; ++lv) {
+    // bins of 2^s keys: the fewest that leave at most nb of them
+    s = kLowBits;
+    while ((span >> s) >= (unsigned)nb) ++s;
     for (int x = tid; x < nb; x += kThreads) s_hist[x] = 0ull;
     __syncthreads();
+    unsigned long long tot = 0ull;
     auto add = [&](float l) {
       // a mass below 2^-40 is zero in the fixed point: skipped before any
       // further work (as are -inf and NaN)
       const float x = fmaf(l, c, -R);
       if (!(x >= -40.0f)) return;
-      const unsigned key = key_of(l);
-      if ((key & pmask) != prefix) return;
-      atomicAdd(&s_hist[(key >> shift) & (unsigned)(nb - 1)],
-                (unsigned long long)(fast_exp2(x) * (float)kNucScale));
+      const unsigned long long q = (unsigned long long)(fast_exp2(x) * (float)kNucScale);
+      if (lv == 0) tot += q;
+      const unsigned d = key_of(l) - kbase;  // wraps past span below the range
+      if (d > span) return;
+      atomicAdd(&s_hist[d >> s], q);
     };
     int v = tid;
     for (; v + (kBatch - 1) * kThreads < P.nvec; v += kBatch * kThreads) {
@@ -1093,7 +1141,17 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(const Params P) {
 #pragma unroll
       for (int k = 0; k < N; ++k) add(f[k]);
     }
+    if (lv == 0) {
+#pragma unroll
+      for (int o = kWave / 2; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
+      if (lane == 0) s_tot[tid / kWave] = tot;
+    }
     __syncthreads();
+    if (lv == 0) {
+      unsigned long long row_total = 0ull;
+      for (int w = 0; w < kThreads / kWave; ++w) row_total += s_tot[w];
+      bound = (double)P.top_p * (double)row_total;
+    }
     // thread t sums a run of bins in descending key order, then an exclusive
     // scan over the threads gives the mass above each run
     const int per = nb / kThreads;
@@ -1114,7 +1172,6 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(const Params P) {
       if (w < tid / kWave) before += s_wave[w];
       total += s_wave[w];
     }
-    if (lv == 0) bound = (double)P.top_p * (double)total;
     unsigned long long acc = above + before + (incl - run);
     for (int k = 0; k < per; ++k) {
       const unsigned long long h = s_hist[top - k];
@@ -1127,24 +1184,35 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(const Params P) {
       acc += h;
     }
     __syncthreads();
-    if (s_bin < 0) break;  // the bound lies past every level: all are kept
-    prefix |= (unsigned)s_bin << shift;
-    pmask |= (unsigned)(nb - 1) << shift;
+    if (s_bin < 0) {
+      if (lv == 0 && kb_top > kb_all) {
+        // below the top window: its mass is strictly larger than every level left
+        above += total;
+        kbase = kb_all;
+        span = kb_top - 1u - kb_all;
+        continue;
+      }
+      break;  // the bound lies past every level: all are kept
+    }
+    found = true;
+    kbase += (unsigned)s_bin << s;
     above = s_base;
     kept = s_base + s_hist[s_bin];
     __syncthreads();
+    if (s == kLowBits) break;  // the bin is one level
+    span = (1u << s) - 1u;
   }
   if (tid == 0) {
     RowRes rr;
     rr.m = m;
     rr.flags = ok ? 0 : 1;
-    if (!ok || pmask == 0u) {
+    if (!ok || !found) {
       rr.theta = kNegInf;  // every level kept
       rr.s = s_stat[1];
     } else {
-      // the level's low key bits are constant below the resolved digits
-      const unsigned lowmask = ~pmask;
-      const unsigned key = prefix | ((prefix & 0x80000000u) ? 0u : lowmask);
+      // the level's constant low key bits: zero for a positive value, ones
+      // for a negative one (its key is the complement of its bits)
+      const unsigned key = kbase | ((kbase & 0x80000000u) ? 0u : kLowMask);
       rr.theta = float_of_key(key);
       rr.s = (float)((double)kept / kNucScale);
     }

@@ -104,6 +104,25 @@ def test_top_p_without_top_k(top_p, dtype, V):
     _check(w, api="dense", diag=False, tag=f"p={top_p} {dtype}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_top_p_level_below_top_window(dtype):
+    """top-p alone where the kept set reaches below the first pass's top window
+    (masses from 2^-16 of the maximum's): at temperature 0.3 the window holds
+    all but 2e-6 to 2e-4 of a row's mass, so top_p = 1 - 2^-20 (exact in
+    float32) puts the last kept level of every target row under it and the descent
+    continues over the keys below the window."""
+    top_p = 1.0 - 2.0 ** -20
+    w = _filtered(0, top_p, B=6, V=20000, dtype=dtype, temperature=0.3)
+    V, c = w["V"], 1.4426950408889634 / 0.3
+    rows = w["target"].float().numpy().astype(np.float64).reshape(-1, V)
+    for r in rows:
+        x = (r - r.max()) * c
+        mass = np.exp2(x[x >= -40])
+        assert mass[mass >= 2.0 ** -16].sum() < top_p * mass.sum()
+    _check(w, api="ragged", diag=True, tag=f"p=1-2^-20 T=0.3 {dtype}")
+    _check(w, api="dense", diag=False, tag=f"p=1-2^-20 T=0.3 {dtype}")
+
+
 @pytest.mark.parametrize("top_k", [257, 1024])
 def test_filters_large_k_exact_select(top_k):
     """k beyond the per-thread bound: every chunk is cut by the exact select."""
