@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     SV_SEQ_BAD_ROW,
     SV_SEQ_BAD_TOKEN,
     SV_SEQ_SYNC_TIMEOUT,
+    SequenceError,
     SpecVerifyError,
     lib,
     make_lmhead_workspace,

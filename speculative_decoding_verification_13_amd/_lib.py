@@ -83,6 +83,18 @@ class SpecVerifyError(RuntimeError):
         super().__init__(f"spec_verify error {code}: {strerror(code)}")
 
 
+class SequenceError(RuntimeError):
+    """A per-sequence code after which the workspace must be zero-filled again
+    (SV_SEQ_SYNC_TIMEOUT or SV_SEQ_BAD_OFFSETS), raised on request."""
+
+    def __init__(self, code):
+        self.code = code
+        text = {SV_SEQ_SYNC_TIMEOUT: "a wait for row statistics ran out",
+                SV_SEQ_BAD_OFFSETS: "invalid ragged offsets"}.get(code, "sequence error")
+        super().__init__(f"sequence code {code}: {text}; zero-fill the workspace "
+                         "(spec_verify_workspace_init) before reusing it")
+
+
 def strerror(code):
     return lib().spec_verify_strerror(int(code)).decode()
 
@@ -100,6 +112,36 @@ def _ptr(t):
     if not t.is_contiguous():
         raise ValueError("spec_verify needs contiguous tensors")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _expect(t, name, dtype, numel, allow_none=False):
+    """Raise ValueError unless tensor ``t`` has ``dtype`` (a torch dtype, or a
+    tuple of them) and exactly ``numel`` elements. The C ABI trusts the sizes it
+    is given, so a short tensor would be read past its end."""
+    if t is None:
+        if allow_none:
+            return
+        raise ValueError(f"{name} is required here")
+    dts = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in dts:
+        raise ValueError(f"{name} must be {' or '.join(map(str, dts))}, got {t.dtype}")
+    if int(t.numel()) != int(numel):
+        raise ValueError(f"{name} holds {t.numel()} elements, expected {numel}")
+
+
+def _check_logits(draft, target, n_draft, n_target, V, draft_needed):
+    """Both logit arrays in one storage type, with n_draft and n_target rows of V."""
+    _expect(target, "target_logits", tuple(DTYPE_CODES), n_target * V)
+    _expect(draft, "draft_logits", target.dtype, n_draft * V, allow_none=not draft_needed)
+
+
+def _check_sequences(num_accepted):
+    """Synchronise and raise if a sequence reports a timed-out wait or invalid
+    offsets: the workspace must then be zero-filled again before reuse."""
+    torch.cuda.synchronize(num_accepted.device)
+    bad = num_accepted[(num_accepted == SV_SEQ_SYNC_TIMEOUT) | (num_accepted == SV_SEQ_BAD_OFFSETS)]
+    if bad.numel() > 0:
+        raise SequenceError(int(bad[0]))
 
 
 def _stream(device):
@@ -129,6 +171,10 @@ def num_stages(top_k=0, top_p=1.0):
     return int(lib().spec_verify_num_stages(int(top_k), float(top_p)))
 
 
+def _nbytes(t):
+    return int(t.numel()) * int(t.element_size())
+
+
 def _dtype_code(t):
     if t.dtype not in DTYPE_CODES:
         raise ValueError(f"unsupported logit dtype {t.dtype}")
@@ -136,55 +182,90 @@ def _dtype_code(t):
 
 
 def spec_verify(draft_logits, target_logits, draft_tokens, uniforms, B, K, V, temperature,
-                top_k=0, top_p=1.0, *, out_tokens=None, num_accepted=None, workspace=None):
+                top_k=0, top_p=1.0, *, out_tokens=None, num_accepted=None, workspace=None,
+                check_sequences=False):
     """Dense verification. Shapes: draft [B,K,V], target [B,K+1,V], draft_tokens
     int32 [B,K], uniforms float32 [B,K+1]. Returns (out_tokens [B,K+1],
-    num_accepted [B]), both int32 on the device."""
+    num_accepted [B]), both int32 on the device. Dtypes and element counts are
+    checked (ValueError). With ``check_sequences`` the call synchronises and
+    raises SequenceError if a sequence reports SV_SEQ_SYNC_TIMEOUT."""
+    B, K, V = int(B), int(K), int(V)
     dev = target_logits.device
+    sampling = float(temperature) != 0.0
+    _check_logits(draft_logits, target_logits, B * K, B * (K + 1), V, K > 0 and sampling)
+    _expect(draft_tokens, "draft_tokens", torch.int32, B * K, allow_none=K == 0)
+    _expect(uniforms, "uniforms", torch.float32, B * (K + 1), allow_none=not sampling)
     if out_tokens is None:
         out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
     if num_accepted is None:
         num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    _expect(out_tokens, "out_tokens", torch.int32, B * (K + 1))
+    _expect(num_accepted, "num_accepted", torch.int32, B)
     if workspace is None:
         workspace = make_workspace(B, B * K, V, top_k, top_p, dev)
     _check(lib().spec_verify(
         _ptr(draft_logits), _ptr(target_logits), _ptr(draft_tokens), _ptr(uniforms),
-        int(B), int(K), int(V), float(temperature), int(top_k), float(top_p),
+        B, K, V, float(temperature), int(top_k), float(top_p),
         _dtype_code(target_logits), _ptr(out_tokens), _ptr(num_accepted), _ptr(workspace),
-        workspace.numel(), _stream(dev)))
+        _nbytes(workspace), _stream(dev)))
+    if check_sequences:
+        _check_sequences(num_accepted)
     return out_tokens, num_accepted
+
+
+# Element counts of the diag side outputs for (total draft rows, B).
+_DIAG_SIZES = dict(row_max_draft=lambda d, b: d, row_logsum_draft=lambda d, b: d,
+                   row_max_target=lambda d, b: d + b, row_logsum_target=lambda d, b: d + b,
+                   ratio=lambda d, b: d, resid_Z=lambda d, b: b)
 
 
 def spec_verify_ragged(draft_logits, target_logits, draft_tokens, uniforms, cu_draft, greedy,
                        B, V, temperature, top_k=0, top_p=1.0, *, total_draft_rows=None,
-                       out_tokens=None, num_accepted=None, workspace=None, diag=None):
+                       out_tokens=None, num_accepted=None, workspace=None, diag=None,
+                       check_sequences=False):
     """Ragged verification over packed rows (see include/spec_verify.h).
 
     cu_draft int32 [B+1] and greedy uint8 [B] (or None) live on the device;
     ``total_draft_rows`` defaults to draft_tokens.numel(). With ``diag`` (a dict
     of optional float32 device tensors, a list of events or raw hipEvent_t
     handles under 'stage_events', and an int 'spin_limit') the diag entry point
-    is used. Returns (out_tokens, num_accepted)."""
+    is used. Dtypes and element counts are checked (ValueError). With
+    ``check_sequences`` the call synchronises and raises SequenceError if a
+    sequence reports SV_SEQ_SYNC_TIMEOUT or SV_SEQ_BAD_OFFSETS. Returns
+    (out_tokens, num_accepted)."""
+    B, V = int(B), int(V)
     dev = target_logits.device
     n_draft = int(draft_tokens.numel()) if total_draft_rows is None else int(total_draft_rows)
+    sampling = float(temperature) != 0.0
+    # a draft array may be absent only when no sampling sequence reads it
+    _check_logits(draft_logits, target_logits, n_draft, n_draft + B, V,
+                  n_draft > 0 and sampling and greedy is None)
+    _expect(draft_tokens, "draft_tokens", torch.int32, n_draft, allow_none=n_draft == 0)
+    _expect(uniforms, "uniforms", torch.float32, n_draft + B, allow_none=not sampling)
+    _expect(cu_draft, "cu_draft", torch.int32, B + 1)
+    _expect(greedy, "greedy", torch.uint8, B, allow_none=True)
+    for name, n in _DIAG_SIZES.items():
+        if diag is not None:
+            _expect(diag.get(name), name, torch.float32, n(n_draft, B), allow_none=True)
     if out_tokens is None:
         out_tokens = torch.empty((n_draft + B,), dtype=torch.int32, device=dev)
     if num_accepted is None:
         num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    _expect(out_tokens, "out_tokens", torch.int32, n_draft + B)
+    _expect(num_accepted, "num_accepted", torch.int32, B)
     if workspace is None:
         workspace = make_workspace(B, n_draft, V, top_k, top_p, dev)
     args = [_ptr(draft_logits), _ptr(target_logits), _ptr(draft_tokens), _ptr(uniforms),
-            _ptr(cu_draft), _ptr(greedy), int(B), n_draft, int(V), float(temperature),
+            _ptr(cu_draft), _ptr(greedy), B, n_draft, V, float(temperature),
             int(top_k), float(top_p), _dtype_code(target_logits), _ptr(out_tokens),
-            _ptr(num_accepted), _ptr(workspace), workspace.numel(), _stream(dev)]
+            _ptr(num_accepted), _ptr(workspace), _nbytes(workspace), _stream(dev)]
     if diag is None:
         _check(lib().spec_verify_ragged(*args))
     else:
         d = SvDiag()
-        for name in ("row_max_draft", "row_logsum_draft", "row_max_target",
-                     "row_logsum_target", "ratio", "resid_Z"):
+        for name in _DIAG_SIZES:
             t = diag.get(name)
-            setattr(d, name, None if t is None else t.data_ptr())
+            setattr(d, name, None if t is None else _ptr(t).value)
         events = diag.get("stage_events")
         d.spin_limit = int(diag.get("spin_limit", 0))
         keep = None
@@ -194,6 +275,8 @@ def spec_verify_ragged(draft_logits, target_logits, draft_tokens, uniforms, cu_d
             d.stage_events = ctypes.cast(keep, ctypes.c_void_p)
             d.n_stage_events = len(handles)
         _check(lib().spec_verify_diag(*args, ctypes.byref(d)))
+    if check_sequences:
+        _check_sequences(num_accepted)
     return out_tokens, num_accepted
 
 
@@ -205,19 +288,24 @@ def spec_verify_accept_stats(draft_logits, target_logits, cu_draft, B, V, temper
     device tensor, or None for B sequences of equal length; ``total_draft_rows``
     defaults to draft_logits.numel() // V. Returns (beta [total_draft_rows],
     expected_accepted [B]), float32 on the device."""
+    B, V = int(B), int(V)
     dev = target_logits.device
-    n_draft = (int(draft_logits.numel()) // int(V) if total_draft_rows is None
+    n_draft = (int(draft_logits.numel()) // V if total_draft_rows is None
                else int(total_draft_rows))
+    _check_logits(draft_logits, target_logits, n_draft, n_draft + B, V, n_draft > 0)
+    _expect(cu_draft, "cu_draft", torch.int32, B + 1, allow_none=True)
     if beta is None:
         beta = torch.empty((n_draft,), dtype=torch.float32, device=dev)
     if expected_accepted is None:
         expected_accepted = torch.empty((B,), dtype=torch.float32, device=dev)
+    _expect(beta, "beta", torch.float32, n_draft)
+    _expect(expected_accepted, "expected_accepted", torch.float32, B)
     if workspace is None:
         workspace = make_workspace(B, n_draft, V, top_k, top_p, dev)
     _check(lib().spec_verify_accept_stats(
-        _ptr(draft_logits), _ptr(target_logits), _ptr(cu_draft), int(B), n_draft, int(V),
+        _ptr(draft_logits), _ptr(target_logits), _ptr(cu_draft), B, n_draft, V,
         float(temperature), int(top_k), float(top_p), _dtype_code(target_logits), _ptr(beta),
-        _ptr(expected_accepted), _ptr(workspace), workspace.numel(), _stream(dev)))
+        _ptr(expected_accepted), _ptr(workspace), _nbytes(workspace), _stream(dev)))
     return beta, expected_accepted
 
 
@@ -246,26 +334,34 @@ def spec_verify_lmhead(hidden_draft, weight_draft, hidden_target, weight_target,
     weight_target [V, Dp]. ``stage_events`` is an optional list of raw
     hipEvent_t handles (ints) recorded between the stages. Returns
     (out_tokens [B, K+1], num_accepted [B])."""
+    B, K, V = int(B), int(K), int(V)
     dev = hidden_target.device
-    for t in (hidden_draft, weight_draft, hidden_target, weight_target):
-        if t is not None and t.dtype != torch.bfloat16:
-            raise ValueError("hidden states and weights must be bfloat16")
+    dq = 0 if hidden_draft is None else int(hidden_draft.shape[-1])
+    dp = int(hidden_target.shape[-1])
+    bf = torch.bfloat16
+    _expect(hidden_target, "hidden_target", bf, B * (K + 1) * dp)
+    _expect(weight_target, "weight_target", bf, V * dp)
+    _expect(hidden_draft, "hidden_draft", bf, B * K * dq, allow_none=K == 0)
+    _expect(weight_draft, "weight_draft", bf, V * dq, allow_none=K == 0)
+    _expect(draft_tokens, "draft_tokens", torch.int32, B * K, allow_none=K == 0)
+    _expect(uniforms, "uniforms", torch.float32, B * (K + 1))
     if out_tokens is None:
         out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
     if num_accepted is None:
         num_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    _expect(out_tokens, "out_tokens", torch.int32, B * (K + 1))
+    _expect(num_accepted, "num_accepted", torch.int32, B)
     if workspace is None:
         workspace = make_lmhead_workspace(B, K, V, dev)
-    dq = 0 if hidden_draft is None else int(hidden_draft.shape[-1])
     evs, n_ev = None, 0
     if stage_events:
         evs = (ctypes.c_void_p * len(stage_events))(*stage_events)
         n_ev = len(stage_events)
     _check(lib().spec_verify_lmhead(
         _ptr(hidden_draft), _ptr(weight_draft), dq, _ptr(hidden_target), _ptr(weight_target),
-        int(hidden_target.shape[-1]), _ptr(draft_tokens), _ptr(uniforms), int(B), int(K), int(V),
+        dp, _ptr(draft_tokens), _ptr(uniforms), B, K, V,
         float(temperature), _ptr(out_tokens), _ptr(num_accepted), _ptr(workspace),
-        workspace.numel(), _stream(dev), ctypes.cast(evs, ctypes.c_void_p) if evs else None,
+        _nbytes(workspace), _stream(dev), ctypes.cast(evs, ctypes.c_void_p) if evs else None,
         n_ev))
     return out_tokens, num_accepted
 

@@ -1092,12 +1092,17 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(const Params P) {
   // the maximum's) and sums every logit's mass, the row total, in registers.
   // When the crossing lies below the window, the next pass bins the keys
   // below it that can carry mass.
+  // Each pass covers the keys [kbase, kbase + span], never above kmax: the
+  // maximum's key in the window, kb_top - 1 below it (the window's mass is
+  // already counted as the mass above), so a split bin never reaches back
+  // into a range another pass has summed.
   const unsigned kb_all = s_kmin[0] & ~kLowMask, kb_top = s_kmin[1] & ~kLowMask;
-  unsigned kbase = 0u, span = 0u;
+  unsigned kbase = 0u, span = 0u, kmax = 0u;
   int s = kLowBits;
   if (ok) {
     kbase = kb_top;
-    span = key_of(m) - kbase;
+    kmax = key_of(m);
+    span = kmax - kbase;
   }
   bool found = false;  // a level has been resolved (else every level is kept)
   unsigned long long above = 0ull, kept = 0ull;
@@ -1189,7 +1194,8 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(const Params P) {
         // below the top window: its mass is strictly larger than every level left
         above += total;
         kbase = kb_all;
-        span = kb_top - 1u - kb_all;
+        kmax = kb_top - 1u;
+        span = kmax - kbase;
         continue;
       }
       break;  // the bound lies past every level: all are kept
@@ -1200,7 +1206,7 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(const Params P) {
     kept = s_base + s_hist[s_bin];
     __syncthreads();
     if (s == kLowBits) break;  // the bin is one level
-    span = (1u << s) - 1u;
+    span = min((1u << s) - 1u, kmax - kbase);
   }
   if (tid == 0) {
     RowRes rr;

@@ -120,6 +120,17 @@ def test_accept_stats_parity(name, ov, api):
     _compare(w, beta, exp, ora)
 
 
+@pytest.mark.parametrize("dtype,top_p", [("bf16", 0.99), ("f16", 0.995)])
+def test_accept_stats_top_p_split_below_top_window(dtype, top_p):
+    """top-p alone where the cut of most rows lies below the top window and a
+    bin under the window is split (V = 128256, T = 1)."""
+    w = W.make("bf16_B32_K4_V32000", B=8, V=128256, dtype=dtype)
+    w["top_p"] = top_p
+    _say(f"[gpu] accept top-p split {dtype} p={top_p}")
+    beta, exp = _gpu(w, "dense")
+    _compare(w, beta, exp, _oracle(w))
+
+
 def test_accept_stats_headline_full_size():
     """B=64, K=8, V=128256 bf16: every pair and every sequence."""
     w = W.make(W.HEADLINE, sd_t=1.0)

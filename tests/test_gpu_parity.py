@@ -123,6 +123,20 @@ def test_top_p_level_below_top_window(dtype):
     _check(w, api="dense", diag=False, tag=f"p=1-2^-20 T=0.3 {dtype}")
 
 
+@pytest.mark.parametrize("dtype,temperature,top_p", [("bf16", 1.0, 0.99), ("bf16", 0.7, 0.995),
+                                                     ("f16", 1.0, 0.99)])
+def test_top_p_split_below_top_window(dtype, temperature, top_p):
+    """top-p alone on full-vocabulary rows (V = 128256, N(0, 3^2) with 20 peaks)
+    where most rows' last kept level lies below the top window and the keys
+    below it need bins wider than one level, so the search splits a bin whose
+    range ends just under the window (the window's mass must not be counted
+    twice). Through the diag and dense entry points."""
+    w = W.make("bf16_B32_K4_V32000", B=8, V=128256, dtype=dtype, temperature=temperature)
+    w["top_p"] = top_p
+    _check(w, api="ragged", diag=True, tag=f"p={top_p} T={temperature} {dtype} split")
+    _check(w, api="dense", diag=False, tag=f"p={top_p} T={temperature} {dtype} split")
+
+
 @pytest.mark.parametrize("top_k", [257, 1024])
 def test_filters_large_k_exact_select(top_k):
     """k beyond the per-thread bound: every chunk is cut by the exact select."""
