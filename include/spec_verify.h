@@ -44,7 +44,9 @@
  * Ownership: the caller owns every buffer (inputs, outputs and the workspace);
  * the library allocates nothing, keeps no state between calls and enqueues all
  * work on `stream` without synchronising it. Calls that share a workspace must
- * be ordered (same stream, or synchronised).
+ * be ordered (same stream, or synchronised). The one exception is
+ * spec_verify_noalloc, whose workspace is a fixed array inside the library
+ * (one per device, shared by every such call on that device).
  *
  * Errors: argument errors return a negative SV_E* code before any device work.
  * Data errors found on the device are reported per sequence in num_accepted
@@ -77,6 +79,9 @@ typedef enum sv_dtype { SV_F32 = 0, SV_F16 = 1, SV_BF16 = 2 } sv_dtype;
 #define SV_EUNSUPPORTED (-5) /* valid request outside this build's limits:
                                 top_k above SV_MAX_TOP_K, V above 2^30, or
                                 a grid of more than 2^24 blocks */
+#define SV_ESCRATCH (-6)     /* spec_verify_noalloc: the call needs more than
+                                the library's fixed scratch array holds
+                                (SV_NOALLOC_SCRATCH_BYTES) */
 
 /* Per-sequence codes written to num_accepted[b] instead of a count. */
 #define SV_SEQ_BAD_TOKEN (-1)   /* a draft id outside [0, V) */
@@ -94,6 +99,8 @@ typedef enum sv_dtype { SV_F32 = 0, SV_F16 = 1, SV_BF16 = 2 } sv_dtype;
 
 #define SV_MAX_K 64
 #define SV_MAX_TOP_K 1024
+/* Bytes of the fixed scratch array spec_verify_noalloc uses on each device. */
+#define SV_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
 
 /* Human-readable text for a return code or per-sequence code. Never NULL. */
 const char* spec_verify_strerror(int code);
@@ -133,6 +140,27 @@ int spec_verify(const void* draft_logits, const void* target_logits,
                 int V, float temperature, int top_k, float top_p, sv_dtype dtype,
                 int32_t* out_tokens, int32_t* num_accepted, void* workspace,
                 size_t workspace_bytes, hipStream_t stream);
+
+/* spec_verify for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation. Arguments, outputs, return codes and per-sequence codes
+ * are those of spec_verify; the workspace is a fixed array inside the library,
+ * SV_NOALLOC_SCRATCH_BYTES on each device that calls it, held from the first
+ * call on that device until the process ends. The call allocates nothing (no
+ * hipMalloc, no allocating library routine); its first call on a device looks
+ * up that device's copy of the array. Each call first clears the part of the
+ * array it uses with a fill kernel on `stream` (no memset node), so nothing of
+ * an earlier call carries over, not even after SV_SEQ_SYNC_TIMEOUT. Every call
+ * on one device shares that device's array: calls that overlap on one GPU
+ * (other streams or threads) race, and the caller must order them. Returns
+ * SV_ESCRATCH, before any device work, when the call needs more than
+ * SV_NOALLOC_SCRATCH_BYTES (its spec_verify_workspace_bytes): unfiltered and
+ * top-p-alone calls fit up to B = 512, K = 16 at V = 128256; active top-k
+ * does not fit at these vocabularies. */
+int spec_verify_noalloc(const void* draft_logits, const void* target_logits,
+                        const int32_t* draft_tokens, const float* uniforms, int B, int K,
+                        int V, float temperature, int top_k, float top_p, sv_dtype dtype,
+                        int32_t* out_tokens, int32_t* num_accepted, hipStream_t stream);
 
 /* Ragged batch (per-sequence K_b, the dynamic-K setting of the lecture-16 notes,
  * "工程里的关键优化点" item 3): packed rows as described above.

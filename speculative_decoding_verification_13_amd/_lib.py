@@ -20,6 +20,7 @@ SV_SEQ_BAD_ROW = -2
 SV_SEQ_BAD_OFFSETS = -3
 SV_SEQ_SYNC_TIMEOUT = -4
 SV_MAX_K = 64
+SV_ESCRATCH = -6
 
 DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
@@ -45,6 +46,7 @@ SIGNATURES = {
     "spec_verify_workspace_init": (_I, [_P, _S, _P]),
     "spec_verify_num_stages": (_I, [_I, _F]),
     "spec_verify": (_I, [_P, _P, _P, _P, _I, _I, _I, _F, _I, _F, _I, _P, _P, _P, _S, _P]),
+    "spec_verify_noalloc": (_I, [_P, _P, _P, _P, _I, _I, _I, _F, _I, _F, _I, _P, _P, _P]),
     "spec_verify_ragged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _I, _F, _I, _P, _P,
                                 _P, _S, _P]),
     "spec_verify_diag": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _I, _F, _I, _P, _P,
@@ -217,6 +219,27 @@ def spec_verify(draft_logits, target_logits, draft_tokens, uniforms, B, K, V, te
 _DIAG_SIZES = dict(row_max_draft=lambda d, b: d, row_logsum_draft=lambda d, b: d,
                    row_max_target=lambda d, b: d + b, row_logsum_target=lambda d, b: d + b,
                    ratio=lambda d, b: d, resid_Z=lambda d, b: b)
+
+
+def spec_verify_noalloc(draft_logits, target_logits, draft_tokens, uniforms, B, K, V,
+                        temperature, top_k=0, top_p=1.0, *, out_tokens, num_accepted):
+    """spec_verify with no workspace: the library uses its fixed per-device
+    scratch array and allocates nothing (for graph capture and loops that must
+    not allocate); the caller passes the outputs. Calls that overlap on one
+    GPU race. Raises SpecVerifyError(SV_ESCRATCH) when the shape needs more
+    than the array holds."""
+    B, K, V = int(B), int(K), int(V)
+    sampling = float(temperature) != 0.0
+    _check_logits(draft_logits, target_logits, B * K, B * (K + 1), V, K > 0 and sampling)
+    _expect(draft_tokens, "draft_tokens", torch.int32, B * K, allow_none=K == 0)
+    _expect(uniforms, "uniforms", torch.float32, B * (K + 1), allow_none=not sampling)
+    _expect(out_tokens, "out_tokens", torch.int32, B * (K + 1))
+    _expect(num_accepted, "num_accepted", torch.int32, B)
+    _check(lib().spec_verify_noalloc(
+        _ptr(draft_logits), _ptr(target_logits), _ptr(draft_tokens), _ptr(uniforms),
+        B, K, V, float(temperature), int(top_k), float(top_p), _dtype_code(target_logits),
+        _ptr(out_tokens), _ptr(num_accepted), _stream(target_logits.device)))
+    return out_tokens, num_accepted
 
 
 def spec_verify_ragged(draft_logits, target_logits, draft_tokens, uniforms, cu_draft, greedy,

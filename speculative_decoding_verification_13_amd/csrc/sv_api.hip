@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 
 #include "spec_verify.h"
 #include "sv_launch.h"
@@ -117,11 +118,41 @@ size_t required_bytes(int B, int total_draft, int V, int top_k, float top_p) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Workspace of spec_verify_noalloc: one fixed array per device. In host code
+// `scratch` names a host-side stand-in, never the device memory; the device
+// address of each device's copy is looked up once, with that device current,
+// and kept in scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the stream's device (SV_OK, or SV_EHIP /
+// SV_EUNSUPPORTED if it cannot be found).
+int scratch_of(hipStream_t stream, void** out) {
+  int dev = 0;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess) return SV_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return SV_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return SV_EHIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return SV_EHIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return SV_EHIP;
+    if (e != hipSuccess || p == nullptr) return SV_EHIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return SV_OK;
+}
+
 int run(const void* draft, const void* target, const int32_t* tokens, const float* uniforms,
         const int32_t* cu, const uint8_t* greedy, int B, int K, int total_draft, int V,
         float temperature, int top_k, float top_p, int dtype, int32_t* out_tokens,
         int32_t* num_accepted, void* workspace, size_t workspace_bytes, hipStream_t stream,
-        const sv_diag* diag) {
+        const sv_diag* diag, bool noalloc = false) {
   if (dtype != SV_F32 && dtype != SV_F16 && dtype != SV_BF16) return SV_EDTYPE;
   if (B < 0 || V < 1 || total_draft < 0) return SV_EINVAL;
   if (cu == nullptr && (K < 0 || K > SV_MAX_K)) return SV_EINVAL;
@@ -141,6 +172,15 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
   sv::Plan L;
   if (!make_plan(B, total_draft, V, topk ? top_k : 0, filt ? top_p : 1.0f, SIZE_MAX, L))
     return SV_EUNSUPPORTED;
+  if (noalloc) {
+    // the library's fixed array, cleared where this call uses it (every
+    // region of the layout must read zero when the kernels start)
+    if (L.total_bytes > SV_NOALLOC_SCRATCH_BYTES) return SV_ESCRATCH;
+    const int rc = scratch_of(stream, &workspace);
+    if (rc != SV_OK) return rc;
+    workspace_bytes = SV_NOALLOC_SCRATCH_BYTES;
+    if (sv::fill_zero(workspace, L.total_bytes, stream) != hipSuccess) return SV_EHIP;
+  }
   if (workspace == nullptr || ((uintptr_t)workspace % kAlign) != 0 ||
       !make_plan(B, total_draft, V, topk ? top_k : 0, filt ? top_p : 1.0f, workspace_bytes, L))
     return SV_EWORKSPACE;
@@ -333,6 +373,7 @@ const char* spec_verify_strerror(int code) {
     case SV_EWORKSPACE: return "workspace null, not 256-byte aligned, or too small";
     case SV_EHIP: return "HIP launch or event record failed";
     case SV_EUNSUPPORTED: return "request outside this build's limits";
+    case SV_ESCRATCH: return "call needs more than the fixed scratch array holds";
     default: return "unknown code";
   }
 }
@@ -362,6 +403,18 @@ int spec_verify(const void* draft_logits, const void* target_logits, const int32
   return run(draft_logits, target_logits, draft_tokens, uniforms, nullptr, nullptr, B, K,
              (int)total, V, temperature, top_k, top_p, (int)dtype, out_tokens, num_accepted,
              workspace, workspace_bytes, stream, nullptr);
+}
+
+int spec_verify_noalloc(const void* draft_logits, const void* target_logits,
+                        const int32_t* draft_tokens, const float* uniforms, int B, int K, int V,
+                        float temperature, int top_k, float top_p, sv_dtype dtype,
+                        int32_t* out_tokens, int32_t* num_accepted, hipStream_t stream) {
+  if (K < 0 || K > SV_MAX_K || B < 0) return SV_EINVAL;
+  const long long total = (long long)B * K;
+  if (total > INT_MAX) return SV_EINVAL;
+  return run(draft_logits, target_logits, draft_tokens, uniforms, nullptr, nullptr, B, K,
+             (int)total, V, temperature, top_k, top_p, (int)dtype, out_tokens, num_accepted,
+             nullptr, 0, stream, nullptr, true);
 }
 
 int spec_verify_ragged(const void* draft_logits, const void* target_logits,

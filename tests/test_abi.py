@@ -47,7 +47,8 @@ def test_codes_match_header(L):
     assert int(codes["SV_SEQ_SYNC_TIMEOUT"]) == _lib.SV_SEQ_SYNC_TIMEOUT
     assert set(k for k in codes if k.startswith("SV_SEQ_")) == {
         "SV_SEQ_BAD_TOKEN", "SV_SEQ_BAD_ROW", "SV_SEQ_BAD_OFFSETS", "SV_SEQ_SYNC_TIMEOUT"}
-    for c in (0, -1, -2, -3, -4, -5):
+    assert int(codes["SV_ESCRATCH"]) == _lib.SV_ESCRATCH
+    for c in (0, -1, -2, -3, -4, -5, -6):
         assert L.spec_verify_strerror(c)
     assert L.spec_verify_strerror(12345) == b"unknown code"
 
@@ -159,3 +160,25 @@ def test_accept_stats_argument_errors(L):
     assert acc(top_k=0, top_p=0.9) == -3  # top-p alone is supported
     assert acc(top_k=2000, V=4096) == -5  # top_k above SV_MAX_TOP_K
     assert acc(B=0, draft=None, target=None, cu=None, beta=None, exp=None, ws=None) == 0
+
+
+def test_noalloc_host_checks(L):
+    """The allocation-free entry point checks its arguments like spec_verify,
+    and refuses a shape whose workspace exceeds its fixed array (16 MiB), both
+    before any device call."""
+    def na(**kw):
+        a = dict(draft=_FAKE, target=_FAKE, tokens=_FAKE, uniforms=_FAKE, B=4, K=4, V=1024,
+                 T=1.0, top_k=0, top_p=1.0, dtype=2, out=_FAKE, num=_FAKE)
+        a.update(kw)
+        return L.spec_verify_noalloc(a["draft"], a["target"], a["tokens"], a["uniforms"], a["B"],
+                                     a["K"], a["V"], a["T"], a["top_k"], a["top_p"], a["dtype"],
+                                     a["out"], a["num"], None)
+    assert na(dtype=3) == -2
+    assert na(K=65) == -1 and na(B=-1) == -1 and na(T=float("nan")) == -1
+    assert na(target=None) == -1 and na(uniforms=None) == -1
+    assert na(B=0, draft=None, target=None, tokens=None, uniforms=None, out=None, num=None) == 0
+    # top-k records at LLM vocabularies, and a batch too large for 16 MiB
+    assert na(B=64, K=8, V=128256, top_k=50, top_p=0.9) == -6
+    assert na(B=1024, K=16, V=128256) == -6
+    assert L.spec_verify_workspace_bytes(1024, 1024 * 16, 128256, 0, 1.0) > 16 << 20
+    assert L.spec_verify_workspace_bytes(512, 512 * 16, 128256, 0, 0.9) <= 16 << 20
