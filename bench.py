@@ -322,6 +322,78 @@ def main():
     eff = comp / (ms_step * 1e-3) / 1e9
 
     n_acc = num.cpu().numpy()
+
+    # The same call with the acceptance statistics as side outputs (beta per
+    # draft position and the expected accepted count): the verification's row
+    # statistics are reused by one more pass over the row pairs.
+    beta_d = torch.empty(max(n_draft, 1), dtype=torch.float32, device=dev)[:n_draft]
+    exp_d = torch.empty(B, dtype=torch.float32, device=dev)
+    with_stats = None
+    if T > 0 and n_draft > 0:
+        def step_stats(k):
+            d, t = sets[k % len(sets)]
+            sv.spec_verify_ragged(d, t, tokens_d, uni_d, cu_d, greedy_d, B, V, T, top_k, top_p,
+                                  total_draft_rows=n_draft, out_tokens=out, num_accepted=num,
+                                  workspace=ws, diag={"beta": beta_d, "expected_accepted": exp_d})
+        for k in range(args.warmup):
+            step_stats(k)
+        torch.cuda.synchronize()
+        start.record()
+        for k in range(args.steps):
+            step_stats(k)
+        stop.record()
+        torch.cuda.synchronize()
+        ms_stats = start.elapsed_time(stop) / args.steps
+        with_stats = {
+            "ms_per_step": ms_stats, "entry_point": "spec_verify_diag (beta, expected_accepted)",
+            "passes_over_rows": 2 if top_k <= 0 and top_p >= 1.0 else 4,
+            "mean_beta": float(beta_d.float().mean().cpu()),
+            "mean_expected_accepted": float(exp_d.float().mean().cpu()),
+        }
+
+    # The other target-perturbation settings of a swept workload (the same
+    # draft rows and draft tokens, targets drawn with the other spread), each
+    # timed like the headline steps.
+    sweep = {}
+    spec = W.WORKLOADS[args.workload]
+    if args.sd_t is None and spec.get("sd_t_sweep"):
+        for sd in spec["sd_t_sweep"]:
+            if sd == w["sd_t"]:
+                continue
+            wt = W.make(args.workload, sd_t=sd)
+            t_sets = [wt["target"].to(dev) for _ in range(len(sets))]
+            t_dense = [t.view(B, K + 1, V) for t in t_sets] if dense else None
+
+            def step_sd(k):
+                if dense:
+                    sv.spec_verify(dense_sets[k % len(sets)][0], t_dense[k % len(sets)],
+                                   tokens_d.view(B, K), uni_d.view(B, K + 1), B, K, V, T, top_k,
+                                   top_p, out_tokens=out.view(B, K + 1), num_accepted=num,
+                                   workspace=ws)
+                else:
+                    sv.spec_verify_ragged(sets[k % len(sets)][0], t_sets[k % len(sets)], tokens_d,
+                                          uni_d, cu_d, greedy_d, B, V, T, top_k, top_p,
+                                          total_draft_rows=n_draft, out_tokens=out,
+                                          num_accepted=num, workspace=ws)
+            for k in range(args.warmup):
+                step_sd(k)
+            torch.cuda.synchronize()
+            start.record()
+            for k in range(args.steps):
+                step_sd(k)
+            stop.record()
+            torch.cuda.synchronize()
+            ms_sd = start.elapsed_time(stop) / args.steps
+            na = num.cpu().numpy()
+            sweep[str(sd)] = {
+                "ms_per_step": ms_sd, "rows_per_s": rows / (ms_sd * 1e-3),
+                "effective_frac_of_peak": comp / (ms_sd * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                "mean_accepted": float(na.mean()),
+                "all_accepted_frac": float((na == w["Ks"]).mean()),
+                "errors": int((na < 0).sum()),
+            }
+            del t_sets, t_dense
+
     traffic = None
     tfile = traffic_file(dominant, args.workload)
     if os.path.exists(tfile):
@@ -369,6 +441,8 @@ def main():
             "all_accepted_frac": float((n_acc == w["Ks"]).mean()),
             "errors": int((n_acc < 0).sum()),
         },
+        "with_accept_stats": with_stats,
+        "sd_t_sweep": sweep or None,
         "wall_s": wall,
         "host_enqueue_us_per_step": host_enqueue / args.steps * 1e6,
         "cpu_baseline": cpu,

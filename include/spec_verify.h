@@ -134,7 +134,17 @@ int spec_verify_workspace_init(void* workspace, size_t workspace_bytes,
  *   temperature   > 0 sampling, == 0 greedy for every sequence
  *   top_k         <= 0 or >= V: off;  top_p in (0, 1], 1: off
  *   out_tokens    int32 [B, K+1];  num_accepted int32 [B]
- * B == 0 returns SV_OK and launches nothing. */
+ * B == 0 returns SV_OK and launches nothing.
+ * Device occupancy: without filters the call is one kernel whose draw blocks
+ * wait (bounded) for row statistics that later blocks of the same grid
+ * compute. For a dense batch with K >= 2 the draw blocks are placed ahead of
+ * the last two positions' statistics when the device holds all of them at
+ * once with a block per compute unit to spare; this assumes the call has the
+ * device to itself. A kernel running beside it on another stream that keeps
+ * compute units busy can make those waits run out: the sequences concerned
+ * report SV_SEQ_SYNC_TIMEOUT (then zero-fill the workspace before reuse). The
+ * compute-unit count and the kernel's occupancy are looked up once per device
+ * and kept (facts about the device, no data of any call). */
 int spec_verify(const void* draft_logits, const void* target_logits,
                 const int32_t* draft_tokens, const float* uniforms, int B, int K,
                 int V, float temperature, int top_k, float top_p, sv_dtype dtype,
@@ -194,7 +204,22 @@ int spec_verify_ragged(const void* draft_logits, const void* target_logits,
  *                the decision-and-draw pass; without filters all three run
  *                in one kernel.
  *   spin_limit   bound of a wait for row statistics (0: default); a small
- *                value forces the SV_SEQ_SYNC_TIMEOUT path in tests. */
+ *                value forces the SV_SEQ_SYNC_TIMEOUT path in tests.
+ *   beta, expected_accepted
+ *                the acceptance statistics of the same rows, as
+ *                spec_verify_accept_stats defines them: beta float
+ *                [total_draft_rows], expected_accepted float [B]. Both or
+ *                neither (else SV_EINVAL). Greedy sequences get NaN (a draft
+ *                of theirs has no pass probability); K_b = 0 gives 0. When
+ *                the call runs as one kernel (no top-k / top-p) a second
+ *                kernel sums min(p, q) over every (draft, target) row pair
+ *                from the first one's row statistics: two passes over the
+ *                rows in all. With filters (or rows of more than 256 * 1024
+ *                vectors) the acceptance statistics run as their own two
+ *                passes after the verification, and a call that also has
+ *                greedy sequences returns SV_EUNSUPPORTED. Stage events then
+ *                mark the verification kernels as above, and every event past
+ *                them is recorded after the acceptance statistics. */
 typedef struct sv_diag {
   float* row_max_draft;
   float* row_logsum_draft;
@@ -205,6 +230,8 @@ typedef struct sv_diag {
   hipEvent_t* stage_events;
   int n_stage_events;
   int spin_limit;
+  float* beta;
+  float* expected_accepted;
 } sv_diag;
 
 /* Number of kernels a call launches for these settings (stage events = this+1). */

@@ -37,6 +37,7 @@ class SvDiag(ctypes.Structure):
         ("row_max_target", _P), ("row_logsum_target", _P),
         ("ratio", _P), ("resid_Z", _P),
         ("stage_events", _P), ("n_stage_events", _I), ("spin_limit", _I),
+        ("beta", _P), ("expected_accepted", _P),
     ]
 
 
@@ -218,7 +219,8 @@ def spec_verify(draft_logits, target_logits, draft_tokens, uniforms, B, K, V, te
 # Element counts of the diag side outputs for (total draft rows, B).
 _DIAG_SIZES = dict(row_max_draft=lambda d, b: d, row_logsum_draft=lambda d, b: d,
                    row_max_target=lambda d, b: d + b, row_logsum_target=lambda d, b: d + b,
-                   ratio=lambda d, b: d, resid_Z=lambda d, b: b)
+                   ratio=lambda d, b: d, resid_Z=lambda d, b: b,
+                   beta=lambda d, b: d, expected_accepted=lambda d, b: b)
 
 
 def spec_verify_noalloc(draft_logits, target_logits, draft_tokens, uniforms, B, K, V,

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <mutex>
 
@@ -118,6 +119,31 @@ size_t required_bytes(int B, int total_draft, int V, int top_k, float top_p) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Blocks of the one-kernel step one device holds at once (compute units times
+// the kernel's occupancy), per device and kernel instance (3 dtypes x vector
+// or scalar path). Facts about the device, looked up on first use and kept:
+// no call's data is stored. 0 means not known yet; a racing first lookup
+// stores the same value twice.
+constexpr int kCapDevices = 64;
+std::atomic<long long> fused_cap_cache[kCapDevices][6];
+
+long long fused_capacity_of(hipStream_t stream, int dtype, bool vec) {
+  int dev = 0;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess) return 0;
+  const int slot = dtype * 2 + (vec ? 1 : 0);
+  if (dev < 0 || dev >= kCapDevices || slot < 0 || slot >= 6) return 0;
+  long long cap = fused_cap_cache[dev][slot].load(std::memory_order_relaxed);
+  if (cap > 0) return cap;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 0;
+  cap = sv::fused_capacity(dtype, vec, cus);
+  // keep the compute-unit count with it (capacity - cus is what the placement uses)
+  if (cap > 0) fused_cap_cache[dev][slot].store(cap * 1024 + cus, std::memory_order_relaxed);
+  return cap * 1024 + cus;
+}
+
 // Workspace of spec_verify_noalloc: one fixed array per device. In host code
 // `scratch` names a host-side stand-in, never the device memory; the device
 // address of each device's copy is looked up once, with that device current,
@@ -147,6 +173,10 @@ int scratch_of(hipStream_t stream, void** out) {
   *out = scratch_ptr[dev];
   return SV_OK;
 }
+
+int run_accept(const void* draft, const void* target, const int32_t* cu, int B, int total_draft,
+               int V, float temperature, int top_k, float top_p, int dtype, float* beta,
+               float* expected, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 int run(const void* draft, const void* target, const int32_t* tokens, const float* uniforms,
         const int32_t* cu, const uint8_t* greedy, int B, int K, int total_draft, int V,
@@ -208,6 +238,13 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
   // unfiltered rows of at most kMaxDrawSlices slices run as one kernel (with
   // larger statistics chunks)
   L.fused = !filt && P.dchunks <= sv::kMaxDrawSlices;
+  // acceptance statistics as side outputs (both pointers, or neither)
+  const bool want_beta =
+      diag != nullptr && (diag->beta != nullptr || diag->expected_accepted != nullptr);
+  if (want_beta && (diag->expected_accepted == nullptr ||
+                    (total_draft > 0 && diag->beta == nullptr)))
+    return SV_EINVAL;
+  if (want_beta && !L.fused && (all_greedy || greedy != nullptr)) return SV_EUNSUPPORTED;
   int steps = sv::kChunkSteps;
   if (L.fused) {
     // about kFusedBlocks statistics blocks over the call (small batches take
@@ -260,10 +297,9 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
   // after all the statistics otherwise.
   P.draw_at = L.stats_blocks;
   if (L.fused && cu == nullptr && K >= 2) {
-    int dev = 0, cus = 0;
-    if (hipStreamGetDevice(stream, &dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        cus > 0 && L.draw_blocks <= sv::fused_capacity(dtype, vec, cus) - cus) {
+    const long long packed = fused_capacity_of(stream, dtype, vec);
+    const long long cap = packed / 1024, cus = packed % 1024;
+    if (cap > 0 && L.draw_blocks <= cap - cus) {
       const long long per_pos = (all_greedy ? 1LL : 2LL) * B * P.chunks;
       P.draw_at = (long long)(K - 1) * per_pos;
     }
@@ -282,16 +318,41 @@ int run(const void* draft, const void* target, const int32_t* tokens, const floa
   }
   hipError_t err;
   if (L.fused) {
-    // stage events: before the kernel, then (every further one) after it
+    P.keep_pair_partials = want_beta ? 1 : 0;
+    // stage events: before the kernel, then (every further one) after it, or
+    // with the acceptance statistics the second after the verification and
+    // every further one after the statistics
     if (ev != nullptr && nev > 0 && hipEventRecord(ev[0], stream) != hipSuccess) return SV_EHIP;
     err = sv::launch_fused(dtype, vec, P, L, stream);
     if (err != hipSuccess) return SV_EHIP;
-    for (int e = 1; ev != nullptr && e < nev; ++e)
+    if (want_beta) {
+      if (ev != nullptr && nev > 1 && hipEventRecord(ev[1], stream) != hipSuccess) return SV_EHIP;
+      // the second pass: min(p, q) over every pair, from the partials the
+      // verification left (same chunking), then beta and E[n]
+      P.beta = diag->beta;
+      P.expected = diag->expected_accepted;
+      P.beta_part = reinterpret_cast<float*>(ws + L.off_beta_part);
+      P.beta_cnt = reinterpret_cast<int*>(ws + L.off_beta_cnt);
+      P.filt = 0;
+      if (sv::launch_accept(dtype, vec, P, L, stream) != hipSuccess) return SV_EHIP;
+    }
+    for (int e = want_beta ? 2 : 1; ev != nullptr && e < nev; ++e)
       if (hipEventRecord(ev[e], stream) != hipSuccess) return SV_EHIP;
     return SV_OK;
   }
-  err = sv::launch(dtype, vec, P, L, stream, ev, nev);
-  return err == hipSuccess ? SV_OK : SV_EHIP;
+  err = sv::launch(dtype, vec, P, L, stream, ev, want_beta ? std::min(nev, 4) : nev);
+  if (err != hipSuccess) return SV_EHIP;
+  if (want_beta) {
+    // the acceptance statistics as their own passes (the verification has
+    // returned the workspace to zero)
+    const int rc = run_accept(draft, target, cu, B, total_draft, V, temperature, top_k, top_p,
+                              dtype, diag->beta, diag->expected_accepted, workspace,
+                              workspace_bytes, stream);
+    if (rc != SV_OK) return rc;
+    for (int e = 4; ev != nullptr && e < nev; ++e)
+      if (hipEventRecord(ev[e], stream) != hipSuccess) return SV_EHIP;
+  }
+  return SV_OK;
 }
 
 int run_accept(const void* draft, const void* target, const int32_t* cu, int B, int total_draft,

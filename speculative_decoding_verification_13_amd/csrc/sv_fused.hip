@@ -257,12 +257,16 @@ __device__ int slice_draw(const Params& P, Job j, int b, int s, float& Z, int& t
 // Returns the partials of a sequence's rows to zero (whole block): its target
 // rows and, with_draft, its draft rows. A row the decision never read may still
 // be in flight: its partial is awaited first. Returns nonzero (in every
-// thread) if such a wait ran out.
-__device__ int clear_partials(const Params& P, int d0, int kb, int b, bool with_draft) {
+// thread) if such a wait ran out. With keep_pairs only the bonus row's
+// partials are cleared: the acceptance statistics pass reads the others next
+// (it clears them, and the kernel boundary orders it after every publish).
+__device__ int clear_partials(const Params& P, int d0, int kb, int b, bool with_draft,
+                              bool keep_pairs = false) {
   const int C = P.chunks;
   const int nd = with_draft ? kb : 0;
+  const int first = keep_pairs ? nd + kb : 0;  // the bonus row is row nd + kb
   int to = 0;
-  for (int k = threadIdx.x; k < (nd + kb + 1) * C; k += kThreads) {
+  for (int k = threadIdx.x + first * C; k < (nd + kb + 1) * C; k += kThreads) {
     const int r = k / C, ch = k - r * C;
     const bool tgt = r >= nd;
     unsigned long long* p =
@@ -298,7 +302,7 @@ __device__ void finish_sequence(const Params& P, int b, int d0, int kb, bool gre
   }
   __syncthreads();
   if (!S.last) return;
-  const int cto = clear_partials(P, d0, kb, b, !greedy);
+  const int cto = clear_partials(P, d0, kb, b, !greedy, P.keep_pair_partials && !greedy);
   if ((S.flags & kSeqFlagTimeout) || cto) {
     for (int k = tid; k <= kb; k += kThreads) pub_i(P.out_tokens + t0 + k, -1);
     if (tid == 0) {

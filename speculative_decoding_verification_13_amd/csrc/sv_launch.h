@@ -95,6 +95,9 @@ struct Params {
   long long stats_blocks;  // stats blocks launched
   int spin_limit;          // bound of every wait (iterations)
   int full_wait;           // 1: decisions read every row (side outputs requested)
+  int keep_pair_partials;  // 1: the one-kernel step leaves the partials of every
+                           // sampling sequence's draft rows and non-bonus target
+                           // rows for the acceptance statistics pass that follows
   int filt;                // 1: filters active (rows carry kept-set results)
   int nucleus;             // 1: top-p without top-k (no candidate records)
   int top_k;

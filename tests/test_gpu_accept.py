@@ -199,3 +199,79 @@ def test_accept_stats_edge_cases_and_workspace_reuse():
     toks = draft_tokens_from_oracle(w2)
     rep = compare(w2, toks, run_gpu(w2, toks, api="ragged", workspace=ws), run_oracle(w2, toks))
     assert not rep["mismatches"], rep["mismatches"][:3]
+
+
+# ------------------------------------------------ beta as side outputs of a call
+def _verify_with_beta(w, toks, workspace=None, extra=None):
+    """One diag call with beta and expected_accepted requested; returns the
+    verification outputs and the statistics (numpy)."""
+    import speculative_decoding_verification_13_amd as sv
+    from parity import to_device
+    d = to_device(w, toks)
+    n_draft, B = int(w["cu_draft"][-1]), w["B"]
+    beta = torch.full((n_draft,), -1.0, dtype=torch.float32, device="cuda")
+    exp = torch.full((B,), -1.0, dtype=torch.float32, device="cuda")
+    diag = dict(beta=beta, expected_accepted=exp, **(extra or {}))
+    g = d["greedy"] if w["greedy"].any() else None
+    out, num = sv.spec_verify_ragged(d["draft"], d["target"], d["tokens"], d["uniforms"], d["cu"],
+                                     g, B, w["V"], w["temperature"], w["top_k"], w["top_p"],
+                                     total_draft_rows=n_draft, diag=diag, workspace=workspace)
+    torch.cuda.synchronize()
+    return (dict(out_tokens=out.cpu().numpy(), num_accepted=num.cpu().numpy()),
+            beta.cpu().numpy().astype(np.float64), exp.cpu().numpy().astype(np.float64))
+
+
+@pytest.mark.parametrize("sd_t", [1.0, 0.25])
+def test_verify_with_beta_headline_full_size(sd_t):
+    """B=64, K=8, V=128256 bf16: verification with the acceptance statistics
+    as side outputs (the verification's row statistics reused, one more pass)
+    matches the oracle on both: tokens and n, every beta and E[n]."""
+    import speculative_decoding_verification_13_amd as sv
+    from parity import compare, draft_tokens_from_oracle, run_oracle
+    w = W.make(W.HEADLINE, sd_t=sd_t)
+    toks = draft_tokens_from_oracle(w)
+    ws = sv.make_workspace(w["B"], int(w["cu_draft"][-1]), w["V"])
+    _say(f"[gpu] verify+beta full {w['name']} sd_t={sd_t}")
+    gpu, beta, exp = _verify_with_beta(w, toks, workspace=ws)
+    rep = compare(w, toks, gpu, run_oracle(w, toks))
+    assert not rep["mismatches"], rep["mismatches"][:3]
+    _compare(w, beta, exp, _oracle(w))
+    assert int((ws != 0).sum()) == 0  # every entry back at zero
+
+
+def test_verify_with_beta_ragged_half_greedy():
+    """Ragged K with half the sequences greedy: sampling sequences match the
+    oracle's statistics, greedy ones get NaN; K_b = 0 gives 0."""
+    from parity import compare, draft_tokens_from_oracle, run_oracle
+    w = W.make("bf16_B512_Kragged_V128256_halfgreedy", B=12, V=30000)
+    cu = np.asarray(w["cu_draft"], dtype=np.int64)
+    kb = np.diff(cu)
+    kb[4] += kb[6]
+    kb[6] = 0  # sequence 6 (sampling) has no drafts
+    w["cu_draft"] = np.concatenate([[0], np.cumsum(kb)]).astype(np.int32)
+    w["Ks"] = kb
+    toks = draft_tokens_from_oracle(w)
+    _say("[gpu] verify+beta ragged half greedy")
+    gpu, beta, exp = _verify_with_beta(w, toks)
+    rep = compare(w, toks, gpu, run_oracle(w, toks))
+    assert not rep["mismatches"], rep["mismatches"][:3]
+    samp = [b for b in range(w["B"]) if not w["greedy"][b]]
+    _compare(w, beta, exp, _oracle(w, samp))
+    cu = np.asarray(w["cu_draft"], dtype=np.int64)
+    for b in range(w["B"]):
+        if w["greedy"][b]:
+            assert np.all(np.isnan(beta[cu[b]:cu[b + 1]])) and math.isnan(exp[b]), b
+    assert exp[6] == 0.0
+
+
+def test_verify_with_beta_filtered_fallback():
+    """With top-k and top-p the statistics run as their own passes after the
+    verification: same results as the oracle."""
+    from parity import compare, draft_tokens_from_oracle, run_oracle
+    w = W.make("f16_B256_K4_V151936_topk50_topp0.9", B=6, V=20000)
+    toks = draft_tokens_from_oracle(w)
+    _say("[gpu] verify+beta filtered")
+    gpu, beta, exp = _verify_with_beta(w, toks)
+    rep = compare(w, toks, gpu, run_oracle(w, toks))
+    assert not rep["mismatches"], rep["mismatches"][:3]
+    _compare(w, beta, exp, _oracle(w))

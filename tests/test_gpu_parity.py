@@ -352,6 +352,12 @@ def test_bad_offsets_flagged():
         num = num.cpu().numpy()
         assert num[bad_seq] == sv.SV_SEQ_BAD_OFFSETS
         assert list(num[:2]) == list(ora["num_accepted"][:2])
+        # the binding's opt-in check synchronises and raises on such a code
+        # (the workspace must be zero-filled again before reuse)
+        with pytest.raises(sv.SequenceError):
+            sv.spec_verify_ragged(d["draft"], d["target"], d["tokens"], d["uniforms"], cu, None, 3,
+                                  w["V"], w["temperature"], total_draft_rows=int(toks.size),
+                                  check_sequences=True)
 
 
 def test_large_magnitude_logits():
