@@ -14,6 +14,7 @@ oracle timed on a bounded sample of the same workload.
 """
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -283,6 +284,24 @@ def main():
     wall = time.perf_counter() - t_wall
     ms_step = start.elapsed_time(stop) / args.steps
 
+    # Host cost of the C entry point alone: the same call with its arguments
+    # marshalled once (the binding's Python checks and conversions excluded).
+    c_enqueue_us = None
+    if dense:
+        L = sv.lib()
+        d, t = dense_sets[0]
+        cargs = [ctypes.c_void_p(d.data_ptr()), ctypes.c_void_p(t.data_ptr()),
+                 ctypes.c_void_p(tokens_d.data_ptr()), ctypes.c_void_p(uni_d.data_ptr()), B, K, V,
+                 T, top_k, top_p, sv._lib.DTYPE_CODES[t.dtype], ctypes.c_void_p(out.data_ptr()),
+                 ctypes.c_void_p(num.data_ptr()), ctypes.c_void_p(ws.data_ptr()),
+                 ws.numel(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)]
+        torch.cuda.synchronize()
+        t_c = time.perf_counter()
+        for k in range(args.steps):
+            L.spec_verify(*cargs)
+        c_enqueue_us = (time.perf_counter() - t_c) / args.steps * 1e6
+        torch.cuda.synchronize()
+
     # The same K steps again with stage events on the launch stream: before the
     # first kernel, between the kernels and after the last (HIP events without
     # the system-scope fence). They give each kernel's duration; recording them
@@ -445,6 +464,7 @@ def main():
         "sd_t_sweep": sweep or None,
         "wall_s": wall,
         "host_enqueue_us_per_step": host_enqueue / args.steps * 1e6,
+        "host_enqueue_us_per_step_c_abi": c_enqueue_us,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

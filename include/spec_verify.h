@@ -315,6 +315,26 @@ int spec_verify_lmhead(const void* hidden_draft, const void* weight_draft, int d
                        void* workspace, size_t workspace_bytes, hipStream_t stream,
                        hipEvent_t* stage_events, int n_stage_events);
 
+/* spec_verify_lmhead with side outputs, for checking the logits the
+ * decisions were made on (every pointer of diag may be NULL; diag may be NULL):
+ *   logits_draft   float [B*K, V]      the draft rows' logits as the statistics
+ *   logits_target  float [B*(K+1), V]  GEMM formed them (fp32 accumulation),
+ *                                      before any reduction
+ * Device memory owned by the caller. Writing them costs 4 bytes per logit of
+ * HBM traffic; the default call writes none. */
+typedef struct sv_lmhead_diag {
+  float* logits_draft;
+  float* logits_target;
+} sv_lmhead_diag;
+
+int spec_verify_lmhead_diag(const void* hidden_draft, const void* weight_draft, int d_draft,
+                            const void* hidden_target, const void* weight_target, int d_target,
+                            const int32_t* draft_tokens, const float* uniforms, int B, int K,
+                            int V, float temperature, int32_t* out_tokens, int32_t* num_accepted,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream,
+                            hipEvent_t* stage_events, int n_stage_events,
+                            const sv_lmhead_diag* diag);
+
 #ifdef __cplusplus
 }
 #endif

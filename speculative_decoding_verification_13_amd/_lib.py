@@ -58,7 +58,13 @@ SIGNATURES = {
     "spec_verify_lmhead_zero_bytes": (_S, [_I, _I, _I]),
     "spec_verify_lmhead": (_I, [_P, _P, _I, _P, _P, _I, _P, _P, _I, _I, _I, _F, _P, _P, _P, _S,
                                 _P, _P, _I]),
+    "spec_verify_lmhead_diag": (_I, [_P, _P, _I, _P, _P, _I, _P, _P, _I, _I, _I, _F, _P, _P, _P,
+                                     _S, _P, _P, _I, _P]),
 }
+
+
+class SvLmheadDiag(ctypes.Structure):
+    _fields_ = [("logits_draft", _P), ("logits_target", _P)]
 
 _lib = None
 
@@ -148,7 +154,11 @@ def _check_sequences(num_accepted):
 
 
 def _stream(device):
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    """The current HIP stream of ``device`` as a raw handle."""
+    idx = device.index if isinstance(device, torch.device) else None
+    if idx is None:
+        idx = torch.cuda.current_device()
+    return ctypes.c_void_p(torch._C._cuda_getCurrentRawStream(idx))
 
 
 def workspace_bytes(B, total_draft_rows, V, top_k=0, top_p=1.0):
@@ -353,12 +363,14 @@ def make_lmhead_workspace(B, K, V, device="cuda"):
 
 def spec_verify_lmhead(hidden_draft, weight_draft, hidden_target, weight_target, draft_tokens,
                        uniforms, B, K, V, temperature, *, out_tokens=None, num_accepted=None,
-                       workspace=None, stage_events=None):
+                       workspace=None, stage_events=None, logits_draft=None, logits_target=None):
     """Verification from bf16 LM-head hidden states (see include/spec_verify.h):
     hidden_draft [B*K, Dq], weight_draft [V, Dq], hidden_target [B*(K+1), Dp],
     weight_target [V, Dp]. ``stage_events`` is an optional list of raw
-    hipEvent_t handles (ints) recorded between the stages. Returns
-    (out_tokens [B, K+1], num_accepted [B])."""
+    hipEvent_t handles (ints) recorded between the stages. ``logits_draft``
+    [B*K, V] and ``logits_target`` [B*(K+1), V] (float32 device tensors, or
+    None) receive the logits the statistics GEMM formed (the diag entry point).
+    Returns (out_tokens [B, K+1], num_accepted [B])."""
     B, K, V = int(B), int(K), int(V)
     dev = hidden_target.device
     dq = 0 if hidden_draft is None else int(hidden_draft.shape[-1])
@@ -382,12 +394,19 @@ def spec_verify_lmhead(hidden_draft, weight_draft, hidden_target, weight_target,
     if stage_events:
         evs = (ctypes.c_void_p * len(stage_events))(*stage_events)
         n_ev = len(stage_events)
-    _check(lib().spec_verify_lmhead(
-        _ptr(hidden_draft), _ptr(weight_draft), dq, _ptr(hidden_target), _ptr(weight_target),
-        dp, _ptr(draft_tokens), _ptr(uniforms), B, K, V,
-        float(temperature), _ptr(out_tokens), _ptr(num_accepted), _ptr(workspace),
-        _nbytes(workspace), _stream(dev), ctypes.cast(evs, ctypes.c_void_p) if evs else None,
-        n_ev))
+    _expect(logits_draft, "logits_draft", torch.float32, B * K * V, allow_none=True)
+    _expect(logits_target, "logits_target", torch.float32, B * (K + 1) * V, allow_none=True)
+    args = [_ptr(hidden_draft), _ptr(weight_draft), dq, _ptr(hidden_target), _ptr(weight_target),
+            dp, _ptr(draft_tokens), _ptr(uniforms), B, K, V,
+            float(temperature), _ptr(out_tokens), _ptr(num_accepted), _ptr(workspace),
+            _nbytes(workspace), _stream(dev), ctypes.cast(evs, ctypes.c_void_p) if evs else None,
+            n_ev]
+    if logits_draft is None and logits_target is None:
+        _check(lib().spec_verify_lmhead(*args))
+    else:
+        d = SvLmheadDiag(None if logits_draft is None else _ptr(logits_draft).value,
+                         None if logits_target is None else _ptr(logits_target).value)
+        _check(lib().spec_verify_lmhead_diag(*args, ctypes.byref(d)))
     return out_tokens, num_accepted
 
 

@@ -80,7 +80,8 @@ struct LmGemm {
   int target;                // 1: rows are target rows, their token is x_i for i < K
   const int32_t* tokens;
   float c;
-  // logits epilogue: row m to out[(m * out_step + out_row0) * V + v]
+  // logits: row m to out[(m * out_step + out_row0) * V + v] (the draw rows'
+  // GEMM; the statistics GEMM when not null)
   float* out;
   int out_step, out_row0;
 };
@@ -198,6 +199,26 @@ __global__ __launch_bounds__(2 * WN * kWave, 2) void k_lm_gemm(const LmPair PR) 
 
   // Element i of tile (a, b) in lane l: row wm*64 + a*32 + 8*(i/4) + 4*(l/32)
   // + i%4, vocabulary id v0 + wn*32*kLmNB + b*32 + l%32.
+  // The logits themselves: the draw rows' GEMM always, the statistics GEMM
+  // only when the caller asked for its logits (spec_verify_lmhead_diag).
+  if (!STATS || G.out != nullptr) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rl = wm * 64 + a * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        const int m = m0 + rl;
+        if (m >= G.M) continue;
+        if (G.gather != nullptr && G.gather[(size_t)m * G.gather_step] < 0) continue;
+        float* orow = G.out + (size_t)(m * G.out_step + G.out_row0) * G.V;
+#pragma unroll
+        for (int b = 0; b < kLmNB; ++b) {
+          const int v = v0 + wn * 32 * kLmNB + b * 32 + (lane & 31);
+          if (v < G.V) orow[v] = acc[a][b][i];
+        }
+      }
+    }
+  }
   if constexpr (STATS) {
     if (tid < kLmBM) {
       const int m = m0 + tid;
@@ -269,23 +290,6 @@ __global__ __launch_bounds__(2 * WN * kWave, 2) void k_lm_gemm(const LmPair PR) 
 #pragma unroll
       for (int q = 1; q < kLmSlots; ++q) merge_ms(mm, ss, s_pm[q][tid], s_ps[q][tid], c);
       G.part[(size_t)(G.unit0 + m0 + tid) * G.NT + vt] = pack_ms(mm, ss);
-    }
-  } else {
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int rl = wm * 64 + a * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        const int m = m0 + rl;
-        if (m >= G.M) continue;
-        if (G.gather != nullptr && G.gather[(size_t)m * G.gather_step] < 0) continue;
-        float* orow = G.out + (size_t)(m * G.out_step + G.out_row0) * G.V;
-#pragma unroll
-        for (int b = 0; b < kLmNB; ++b) {
-          const int v = v0 + wn * 32 * kLmNB + b * 32 + (lane & 31);
-          if (v < G.V) orow[v] = acc[a][b][i];
-        }
-      }
     }
   }
 }
@@ -389,13 +393,14 @@ extern "C" size_t spec_verify_lmhead_zero_bytes(int B, int K, int V) {
   return L.zero_bytes;
 }
 
-extern "C" int spec_verify_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
-                                  const void* hidden_target, const void* weight_target,
-                                  int d_target, const int32_t* draft_tokens,
-                                  const float* uniforms, int B, int K, int V, float temperature,
-                                  int32_t* out_tokens, int32_t* num_accepted, void* workspace,
-                                  size_t workspace_bytes, hipStream_t stream,
-                                  hipEvent_t* stage_events, int n_stage_events) {
+namespace {
+
+int run_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
+               const void* hidden_target, const void* weight_target, int d_target,
+               const int32_t* draft_tokens, const float* uniforms, int B, int K, int V,
+               float temperature, int32_t* out_tokens, int32_t* num_accepted, void* workspace,
+               size_t workspace_bytes, hipStream_t stream, hipEvent_t* stage_events,
+               int n_stage_events, float* logits_draft, float* logits_target) {
   using namespace sv;
   if (B < 0 || K < 0 || K > SV_MAX_K || V < 1) return SV_EINVAL;
   if (!(temperature > 0.0f) || __builtin_isinf(temperature)) return SV_EINVAL;
@@ -482,6 +487,8 @@ extern "C" int spec_verify_lmhead(const void* hidden_draft, const void* weight_d
     G.K = K;
     G.tokens = draft_tokens;
     G.c = P.c;
+    G.out_step = 1;
+    G.out_row0 = 0;
     if (total_draft > 0) {
       auto [MT, blocks] = grid_of(total_draft, L.NT);
       G.H = static_cast<const uint16_t*>(hidden_draft);
@@ -491,6 +498,7 @@ extern "C" int spec_verify_lmhead(const void* hidden_draft, const void* weight_d
       G.MT = MT;
       G.unit0 = 0;
       G.target = 0;
+      G.out = logits_draft;
       S.g[0] = G;
       S.n0 = (int)blocks;
       blocks_stats = blocks;
@@ -503,6 +511,7 @@ extern "C" int spec_verify_lmhead(const void* hidden_draft, const void* weight_d
     G.MT = MT;
     G.unit0 = total_draft;
     G.target = 1;
+    G.out = logits_target;
     S.g[1] = G;
     blocks_stats += blocks;
   }
@@ -553,4 +562,35 @@ extern "C" int spec_verify_lmhead(const void* hidden_draft, const void* weight_d
   while (e < n_stage_events && stage_events != nullptr)
     if (!stage()) return SV_EHIP;
   return SV_OK;
+}
+
+}  // namespace
+
+extern "C" int spec_verify_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
+                                  const void* hidden_target, const void* weight_target,
+                                  int d_target, const int32_t* draft_tokens,
+                                  const float* uniforms, int B, int K, int V, float temperature,
+                                  int32_t* out_tokens, int32_t* num_accepted, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream,
+                                  hipEvent_t* stage_events, int n_stage_events) {
+  return run_lmhead(hidden_draft, weight_draft, d_draft, hidden_target, weight_target, d_target,
+                    draft_tokens, uniforms, B, K, V, temperature, out_tokens, num_accepted,
+                    workspace, workspace_bytes, stream, stage_events, n_stage_events, nullptr,
+                    nullptr);
+}
+
+extern "C" int spec_verify_lmhead_diag(const void* hidden_draft, const void* weight_draft,
+                                       int d_draft, const void* hidden_target,
+                                       const void* weight_target, int d_target,
+                                       const int32_t* draft_tokens, const float* uniforms, int B,
+                                       int K, int V, float temperature, int32_t* out_tokens,
+                                       int32_t* num_accepted, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream,
+                                       hipEvent_t* stage_events, int n_stage_events,
+                                       const sv_lmhead_diag* diag) {
+  return run_lmhead(hidden_draft, weight_draft, d_draft, hidden_target, weight_target, d_target,
+                    draft_tokens, uniforms, B, K, V, temperature, out_tokens, num_accepted,
+                    workspace, workspace_bytes, stream, stage_events, n_stage_events,
+                    diag != nullptr ? diag->logits_draft : nullptr,
+                    diag != nullptr ? diag->logits_target : nullptr);
 }

@@ -169,3 +169,89 @@ def test_lmhead_parity_full_size():
     T=0.7: the benchmark's workload, every sequence checked."""
     w = W.make_lmhead()
     _check(w, "full")
+
+
+# ------------------------------------------- general bf16 operands (no integer grid)
+def _check_real(w, tag):
+    """General bf16 hidden states and weights (workloads.make_lmhead_real): the
+    GPU's logits round in fp32. The call also returns the logits its statistics
+    GEMM formed (spec_verify_lmhead_diag). Three checks follow:
+    - each row's largest error against the float64 oracle must lie within the
+      rigorous blocked-summation bound of tests/lmhead_band.py;
+    - that row's measured error, carried through the ratio tests and the
+      inverse CDF (tests/lmhead_band.py), widens each sequence's band;
+    - tokens and n are bit-exact for every sequence whose oracle margin lies
+      outside its band; the sequences inside are counted and must return a
+      valid outcome."""
+    import speculative_decoding_verification_13_amd as sv
+    from lmhead_band import row_error_bounds, sequence_bands
+    B, K, V, T = w["B"], w["K"], w["V"], w["temperature"]
+    _say(f"[gpu] lmhead real {tag}: B={B} K={K} V={V} Dq={w['d_draft']} Dp={w['d_target']} T={T}")
+    lq = (w["hq"].astype(np.float64) @ w["wq"].astype(np.float64).T if K > 0
+          else np.zeros((0, V)))
+    lp = w["hp"].astype(np.float64) @ w["wp"].astype(np.float64).T
+    toks = (oracle.sample_rows(lq, w["u_draft"], V=V, dtype="f64", temperature=T)[0] if K > 0
+            else np.zeros(0, dtype=np.int32))
+    ora = oracle.verify(lq, lp, toks, w["uniforms"], B=B, V=V, K=K, dtype="f64", temperature=T,
+                        want_diag=True)
+    dev = "cuda"
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(torch.bfloat16)
+    ld = torch.empty(B * K * V, dtype=torch.float32, device=dev) if K > 0 else None
+    lt = torch.empty(B * (K + 1) * V, dtype=torch.float32, device=dev)
+    out, num = sv.spec_verify_lmhead(
+        bf(w["hq"]) if K > 0 else None, bf(w["wq"]) if K > 0 else None, bf(w["hp"]), bf(w["wp"]),
+        torch.from_numpy(np.asarray(toks, np.int32)).to(dev) if K > 0 else None,
+        torch.from_numpy(w["uniforms"]).to(dev), B, K, V, T, logits_draft=ld, logits_target=lt)
+    torch.cuda.synchronize()
+    out, num = out.cpu().numpy().reshape(-1), num.cpu().numpy()
+    et = np.abs(lt.cpu().numpy().reshape(-1, V).astype(np.float64) - lp).max(axis=1)
+    bt = row_error_bounds(w["hp"], w["wp"])
+    assert np.all(et <= bt), (et.max(), bt.min())
+    ed = np.zeros(0)
+    if K > 0:
+        ed = np.abs(ld.cpu().numpy().reshape(-1, V).astype(np.float64) - lq).max(axis=1)
+        bd = row_error_bounds(w["hq"], w["wq"])
+        assert np.all(ed <= bd), (ed.max(), bd.min())
+    bands = sequence_bands(ora, ed, et, B, K, T)
+    near = 0
+    for b in range(B):
+        sl = slice(b * (K + 1), (b + 1) * (K + 1))
+        if ora["margin"][b] <= bands[b]:
+            near += 1
+            n = int(num[b])
+            assert 0 <= n <= K, (b, n)
+            assert np.array_equal(out[sl][:n], toks[b * K:b * K + n]), b
+            assert 0 <= out[sl][n] < V, b
+            assert np.all(out[sl][n + 1:] == -1), b
+            continue
+        assert num[b] == ora["num_accepted"][b], (b, num[b], ora["num_accepted"][b], bands[b])
+        assert np.array_equal(out[sl], ora["out_tokens"][sl]), (b, out[sl], ora["out_tokens"][sl])
+    worst = max(float(np.max(et / bt)), float(np.max(ed / bd)) if K > 0 else 0.0)
+    _say(f"      inside their band={near} of {B}; largest logit error draft "
+         f"{ed.max() if K > 0 else 0:.2e} target {et.max():.2e} (at most {worst:.3f} of the "
+         f"bound); median band {np.median(bands):.2e}; mean accepted "
+         f"{ora['num_accepted'].mean():.2f}")
+    return near
+
+
+def test_lmhead_real_parity_full_size():
+    """B=64, K=8, V=128256, hidden sizes 2048 and 4096, T=0.7, general bf16
+    operands (logit spread 3, 20 peaks at +8, target = draft + N(0, 1))."""
+    w = W.make_lmhead_real()
+    near = _check_real(w, "full")
+    assert near <= w["B"] // 4
+
+
+def _real_config(i):
+    rng = np.random.default_rng([4343, i])
+    dq = 8 * int(rng.integers(1, 129))
+    dp = dq + 8 * int(rng.integers(1, 129))
+    return dict(B=int(rng.integers(1, 17)), K=int(rng.integers(0, 11)),
+                V=int(rng.integers(100, 9000)), d_draft=dq, d_target=dp,
+                temperature=float(np.round(rng.uniform(0.4, 1.5), 2)))
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_lmhead_real_parity_random(i):
+    w = W.make_lmhead_real(**_real_config(i), seed=2700 + i)
+    _check_real(w, f"random {i}")

@@ -225,3 +225,75 @@ def lmhead_to_device(a, scale, device="cuda"):
     scale a power of two)."""
     t = torch.from_numpy(np.ascontiguousarray(a)).to(device)
     return t.to(torch.bfloat16) * scale
+
+
+LMHEAD_REAL_NAME = "lmhead_real_bf16_B64_K8_V128256_Dq2048_Dp4096"
+
+
+def make_lmhead_real(B=None, K=None, V=None, d_draft=None, d_target=None, temperature=None,
+                     seed=None, sd=3.0, peaks=20, boost=8.0, sd_t=1.0):
+    """General bf16 LM-head inputs (no integer grid): every value is a bf16
+    number, returned as float32 arrays holding exactly those values.
+
+    The logits follow the logit workloads' shape. The draft weight is W_q ~
+    N(0, sd^2 / d_draft) per entry, and each draft hidden row is N(0, 1) plus,
+    for `peaks` distinct ids k of that row, (boost / |W_q[k]|^2) W_q[k]. So
+    logits have spread about sd, and those ids sit about `boost` higher. The
+    target shares the draft's directions: its weight is [W_q | W_e] with
+    W_e ~ N(0, sd_t^2 / (d_target - d_draft)), and its hidden row at position
+    i < K is [the draft's row i | e] with e ~ N(0, 1), so its logits are the
+    draft's plus about N(0, sd_t^2). Its bonus row is a fresh draft-like row
+    followed by e. Hidden rows and weights are then cast to bf16
+    (round-to-nearest-even, torch CPU).
+    Draw order (PCG64 stream [seed, 0]): W_q, W_e, then per sequence and
+    position the hidden row, its peak ids and e; u_draft from [seed, 1] and
+    uniforms from [seed, 2] as in ``make``.
+    """
+    c = dict(LMHEAD)
+    for k, v in dict(B=B, K=K, V=V, d_draft=d_draft, d_target=d_target,
+                     temperature=temperature, seed=seed).items():
+        if v is not None:
+            c[k] = v
+    Bn, Kn, Vn, dq, dp = c["B"], c["K"], c["V"], c["d_draft"], c["d_target"]
+    if dp < dq:
+        raise ValueError("the target's hidden size must be at least the draft's")
+    rng = np.random.default_rng([c["seed"], 1000])
+    wq = (rng.standard_normal((Vn, dq), dtype=np.float32) * np.float32(sd / np.sqrt(dq)))
+    de = dp - dq
+    we = (rng.standard_normal((Vn, de), dtype=np.float32) * np.float32(sd_t / np.sqrt(de))
+          if de > 0 else np.zeros((Vn, 0), np.float32))
+    wq = _bf16(wq)
+    we = _bf16(we)
+    norm2 = np.einsum("vd,vd->v", wq.astype(np.float64), wq.astype(np.float64))
+
+    def draft_like():
+        h = rng.standard_normal(dq, dtype=np.float32).astype(np.float64)
+        if peaks > 0:
+            ids = rng.choice(Vn, int(peaks), replace=False)
+            h += (boost / norm2[ids]) @ wq[ids].astype(np.float64)
+        return h.astype(np.float32)
+
+    hq = np.empty((Bn * Kn, dq), dtype=np.float32)
+    hp = np.empty((Bn * (Kn + 1), dp), dtype=np.float32)
+    for b in range(Bn):
+        for i in range(Kn + 1):
+            h = draft_like()
+            e = rng.standard_normal(de, dtype=np.float32)
+            if i < Kn:
+                hq[b * Kn + i] = h
+            hp[b * (Kn + 1) + i, :dq] = h
+            hp[b * (Kn + 1) + i, dq:] = e
+    # rounding is elementwise, so the target's copy of each draft row rounds alike
+    hq, hp = _bf16(hq), _bf16(hp)
+    wp = np.concatenate([wq, we], axis=1)
+    u_draft = np.random.default_rng([c["seed"], 1]).random(Bn * Kn, dtype=np.float32)
+    uniforms = np.random.default_rng([c["seed"], 2]).random(Bn * (Kn + 1), dtype=np.float32)
+    return dict(B=Bn, K=Kn, V=Vn, d_draft=dq, d_target=dp, temperature=float(c["temperature"]),
+                seed=int(c["seed"]), hq=hq, wq=wq, hp=hp, wp=wp, u_draft=u_draft,
+                uniforms=uniforms)
+
+
+def _bf16(a):
+    """float32 array rounded to bf16 (round-to-nearest-even), as float32."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(
+        torch.bfloat16).to(torch.float32).numpy()
