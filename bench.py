@@ -99,11 +99,12 @@ def parse():
                     help="budget of the CPU oracle sample (0 disables)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
-    ap.add_argument("--path", choices=["verify", "accept", "lmhead"], default="verify",
+    ap.add_argument("--path", choices=["verify", "accept", "lmhead", "multi"], default="verify",
                     help="verify: the verification step (default); accept: the "
                          "acceptance statistics (spec_verify_accept_stats); lmhead: "
                          "verification from LM-head hidden states (spec_verify_lmhead, "
-                         f"workload {W.LMHEAD_NAME})")
+                         f"workload {W.LMHEAD_NAME}); multi: several draft chains per "
+                         f"sequence (spec_verify_multi, workload {MULTI_NAME})")
     ap.add_argument("--traffic-from", metavar="DIR", default=None,
                     help="only summarise rocprofv3 counter runs: DIR/{fetch,write,cal_fetch,"
                          "cal_write} hold FETCH_SIZE / WRITE_SIZE runs of this bench command and "
@@ -205,6 +206,9 @@ def main():
 
     if args.path == "lmhead":
         bench_lmhead(args, sv)
+        return
+    if args.path == "multi":
+        bench_multi(args, sv)
         return
     w = W.make(args.workload, sd_t=args.sd_t)
     if args.path == "accept":
@@ -561,6 +565,88 @@ def bench_accept(args, w, sv):
 
 
 LM_STAGES = ["gemm_stats", "merge_and_decide", "gemm_draw_rows", "draw"]
+
+
+MULTI_NAME = "multi_bf16_B64_M4_K4_V128256"
+MULTI = dict(B=64, M=4, K=4, V=128256, dtype="bf16", temperature=0.7, seed=3100)
+
+
+def bench_multi(args, sv):
+    """Several draft chains per sequence: B=64 sequences with M=4 chains of K=4
+    drafts each, V=128256 bf16, T=0.7 (the logit workloads' recipe per chain).
+    A step is one spec_verify_multi call: the row statistics of every draft and
+    target row, then the walk over the chains."""
+    import oracle
+    c = MULTI
+    B, M, K, V, T = c["B"], c["M"], c["K"], c["V"], c["temperature"]
+    w = W.make_multi(**c)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    draft0 = w["draft"].to(dev)
+    # draft tokens: each chain's own draw from its rows (the library, K = 0)
+    n_rows = B * M * K
+    zeros_cu = torch.zeros(n_rows + 1, dtype=torch.int32, device=dev)
+    tok, _ = sv.spec_verify_ragged(None, draft0.view(n_rows, V), None,
+                                   torch.from_numpy(w["u_draft"].reshape(-1)).to(dev), zeros_cu,
+                                   None, n_rows, V, T, total_draft_rows=0)
+    toks = tok.cpu().numpy().reshape(B, M, K)
+    W.share_target_prefixes(w["target"], toks)
+    target0 = w["target"].to(dev)
+    tokens_d = torch.from_numpy(np.ascontiguousarray(toks, np.int32)).to(dev)
+    uni_d = torch.from_numpy(w["uniforms"]).to(dev)
+    sets = [(draft0, target0)] + [(draft0.clone(), target0.clone())
+                                  for _ in range(max(1, args.sets) - 1)]
+    n = int(sv.lib().spec_verify_multi_workspace_bytes(B, M, K, V))
+    ws = sv._lib._zeroed_workspace(max(n, 256), dev)
+    out = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    num = torch.empty(B, dtype=torch.int32, device=dev)
+    chain = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def step(k):
+        d, t = sets[k % len(sets)]
+        sv.spec_verify_multi(d, t, tokens_d, uni_d, B, M, K, V, T, out_tokens=out,
+                             num_accepted=num, out_chain=chain, workspace=ws)
+    for k in range(args.warmup):
+        step(k)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(args.steps):
+        step(k)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    n_acc = num.cpu().numpy()
+    comp = (B * M * K + B * M * (K + 1)) * V * target0.element_size()
+    cpu = None
+    if args.cpu_seconds > 0:
+        draft, target = W.raw_numpy(w["draft"].reshape(-1, V)), W.raw_numpy(w["target"].reshape(-1, V))
+        t0, done = time.perf_counter(), 0
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            b = done % B
+            oracle.verify_multi(draft[b * M * K:(b + 1) * M * K],
+                                target[b * M * (K + 1):(b + 1) * M * (K + 1)], toks[b],
+                                w["uniforms"][b], B=1, M=M, K=K, V=V, dtype=c["dtype"],
+                                temperature=T)
+            done += 1
+        el = time.perf_counter() - t0
+        cpu = {"value": done / el, "unit": "sequences/s", "cores": 1, "kind": "oracle",
+               "sample": f"{done} sequences of the same workload one by one in {el:.1f} s, "
+                         "numpy float64, one process", "cpu_model": _cpu_model()}
+    print(json.dumps({
+        "metric": "verified sequences/sec, several draft chains per sequence",
+        "value": B / (ms * 1e-3), "unit": "sequences/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": MULTI_NAME, "B": B, "M": M, "K": K, "V": V,
+                   "input_dtype": c["dtype"], "temperature": T, "rotating_sets": len(sets),
+                   "entry_point": "spec_verify_multi"},
+        "effective_GBps": comp / (ms * 1e-3) / 1e9,
+        "effective_frac_of_peak": comp / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "compulsory_bytes_per_step": comp,
+        "acceptance": {"mean_accepted": float(n_acc.mean()), "errors": int((n_acc < 0).sum())},
+        "cpu_baseline": cpu,
+    }), flush=True)
 
 
 def bench_lmhead(args, sv):

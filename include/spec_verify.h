@@ -99,6 +99,7 @@ typedef enum sv_dtype { SV_F32 = 0, SV_F16 = 1, SV_BF16 = 2 } sv_dtype;
 
 #define SV_MAX_K 64
 #define SV_MAX_TOP_K 1024
+#define SV_MAX_CHAINS 4
 /* Bytes of the fixed scratch array spec_verify_noalloc uses on each device. */
 #define SV_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
 
@@ -278,6 +279,47 @@ int spec_verify_accept_stats(const void* draft_logits, const void* target_logits
                              float temperature, int top_k, float top_p, sv_dtype dtype,
                              float* beta, float* expected_accepted, void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
+
+/* Several draft chains per sequence (the lecture-16 notes, part "1、第16講":
+ * there can be several drafters; the pages give no rule, so the one used is
+ * their own single step applied again, from aivaro.ru answer 289 section 6:
+ * accepting x ~ q with probability min(1, p(x)/q(x)), else drawing from
+ * max(0, p - q)/Z, is rejection sampling whose result follows p; after a
+ * rejection the remainder max(0, p - q)/Z is the law the next candidate,
+ * drawn independently, is tested against).
+ * M chains of K drafts share each sequence's prefix; chain m's rows at
+ * position j are conditioned on its own tokens 0..j-1, and the caller's target
+ * rows of chains with equal prefixes must agree. Position j is checked against
+ * the chains still alive (their tokens so far equal the emitted ones), in
+ * chain order, starting from the lowest live chain's target row p_j: a
+ * candidate is accepted iff u < r(x)/q_m(x), where r is the current law (p_j,
+ * then each remainder). An accepted token keeps alive the chains that
+ * proposed it. When every candidate is rejected the token is drawn from the
+ * last remainder, by inverse CDF over ascending ids (the bonus position K
+ * draws from p_K). Sampling only, no top-k / top-p.
+ *   draft_logits  [B, M, K, V]     target_logits [B, M, K+1, V]
+ *   draft_tokens  int32 [B, M, K]
+ *   uniforms      float [B, K+1, M+1]: [b, j, m] tests chain m's candidate at
+ *                 position j, [b, j, M] is the draw at j (used where the walk
+ *                 stops)
+ *   out_tokens    int32 [B, K+1] (-1 padded); num_accepted int32 [B] (n, or
+ *                 SV_SEQ_BAD_TOKEN for any id outside [0, V), SV_SEQ_BAD_ROW
+ *                 for a used row with NaN, +inf or no finite value)
+ *   out_chain     int32 [B] or NULL: the lowest chain holding the emitted
+ *                 prefix (the cache to keep), -1 with an error code
+ * 1 <= M <= SV_MAX_CHAINS, 0 <= K <= SV_MAX_K, temperature finite and > 0,
+ * rows of at most 1024 * 256 vectors (16-byte vectors when V * element size is
+ * a multiple of 16 and both arrays are 16-byte aligned, else elements). The
+ * workspace (spec_verify_multi_workspace_bytes) obeys the zero rules of
+ * spec_verify. Two kernels: the row statistics of every row, then one block
+ * per sequence for the walk (one pass over the vocabulary per rejection and
+ * per draw). */
+size_t spec_verify_multi_workspace_bytes(int B, int M, int K, int V);
+int spec_verify_multi(const void* draft_logits, const void* target_logits,
+                      const int32_t* draft_tokens, const float* uniforms, int B, int M, int K,
+                      int V, float temperature, sv_dtype dtype, int32_t* out_tokens,
+                      int32_t* num_accepted, int32_t* out_chain, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
 
 /* Verification from LM-head hidden states: the same step as spec_verify, with
  * the logit rows formed inside the library as l = h W^T on the matrix cores

@@ -27,3 +27,4 @@ from .verify import (  # noqa: F401
     acceptance_stats,
 )
 from .lmhead import lmhead_logits, verify_lmhead  # noqa: F401,E402
+from .multi import verify_multi, verify_multi_sequence  # noqa: F401,E402

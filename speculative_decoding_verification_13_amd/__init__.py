@@ -23,6 +23,7 @@ from ._lib import (  # noqa: F401
     spec_verify,
     spec_verify_accept_stats,
     spec_verify_lmhead,
+    spec_verify_multi,
     spec_verify_noalloc,
     spec_verify_ragged,
     strerror,

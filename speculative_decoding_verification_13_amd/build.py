@@ -15,7 +15,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libspecverify.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["sv_api.hip", "sv_fused.hip", "sv_verify.hip", "sv_accept.hip", "sv_lmhead.hip"]
+SOURCES = ["sv_api.hip", "sv_fused.hip", "sv_verify.hip", "sv_accept.hip", "sv_lmhead.hip",
+           "sv_multi.hip"]
 ARCH = "gfx950"
 
 

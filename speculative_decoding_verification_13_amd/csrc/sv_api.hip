@@ -422,9 +422,85 @@ int run_accept(const void* draft, const void* target, const int32_t* cu, int B, 
   return sv::launch_accept(dtype, vec, P, L, stream) == hipSuccess ? SV_OK : SV_EHIP;
 }
 
+bool multi_sizes(int B, int M, int K, int V, long long& seqs, long long& drafts) {
+  if (B < 0 || M < 1 || M > SV_MAX_CHAINS || K < 0 || K > SV_MAX_K || V < 1) return false;
+  seqs = (long long)B * M;
+  drafts = seqs * K;
+  return seqs * (K + 1) <= INT_MAX;
+}
+
+int run_multi(const void* draft, const void* target, const int32_t* tokens, const float* uniforms,
+              int B, int M, int K, int V, float temperature, int dtype, int32_t* out_tokens,
+              int32_t* num_accepted, int32_t* out_chain, void* workspace, size_t workspace_bytes,
+              hipStream_t stream) {
+  if (dtype != SV_F32 && dtype != SV_F16 && dtype != SV_BF16) return SV_EDTYPE;
+  long long seqs, drafts;
+  if (!multi_sizes(B, M, K, V, seqs, drafts)) return SV_EINVAL;
+  if (!(temperature > 0.0f) || isinf(temperature)) return SV_EINVAL;
+  if (B == 0) return SV_OK;
+  if (target == nullptr || uniforms == nullptr || out_tokens == nullptr ||
+      num_accepted == nullptr)
+    return SV_EINVAL;
+  if (K > 0 && (draft == nullptr || tokens == nullptr)) return SV_EINVAL;
+  sv::Plan L;
+  if (!make_plan((int)seqs, (int)drafts, V, 0, 1.0f, SIZE_MAX, L)) return SV_EUNSUPPORTED;
+  if (workspace == nullptr || ((uintptr_t)workspace % kAlign) != 0 ||
+      !make_plan((int)seqs, (int)drafts, V, 0, 1.0f, workspace_bytes, L))
+    return SV_EWORKSPACE;
+  const int es = esize_of(dtype);
+  const bool vec = ((size_t)V * es) % 16 == 0 && aligned16(target) &&
+                   (draft == nullptr || aligned16(draft));
+  sv::Params P{};
+  P.draft = draft;
+  P.target = target;
+  P.tokens = tokens;
+  P.uniforms = uniforms;
+  P.B = (int)seqs;
+  P.K = K;
+  P.V = V;
+  P.total_draft = (int)drafts;
+  P.rows = (int)(seqs * (K + 1));
+  P.c = (float)(1.4426950408889634074 / (double)temperature);
+  P.nvec = vec ? V / (16 / es) : V;
+  if ((P.nvec + sv::kTileVecs - 1) / sv::kTileVecs > 1024) return SV_EUNSUPPORTED;
+  P.chunk_vecs = (int)chunk_vecs_for(P.nvec, sv::kChunkSteps);
+  P.chunks = (P.nvec + P.chunk_vecs - 1) / P.chunk_vecs;
+  if (P.chunks > L.cmax) return SV_EUNSUPPORTED;
+  P.out_tokens = out_tokens;
+  P.num_accepted = num_accepted;
+  P.slots = reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(workspace) + L.off_slots);
+  P.spin_limit = kDefaultSpinLimit;
+  P.M = M;
+  P.out_chain = out_chain;
+  L.chunks = P.chunks;
+  L.chunk_vecs = P.chunk_vecs;
+  L.stats_blocks = ((long long)P.total_draft + P.rows) * P.chunks;
+  L.filter_blocks = 0;
+  P.stats_blocks = L.stats_blocks;
+  if (L.stats_blocks > (long long)INT_MAX / sv::kThreads) return SV_EUNSUPPORTED;
+  if (sv::launch_row_stats(dtype, vec, P, L, stream) != hipSuccess) return SV_EHIP;
+  return sv::launch_multi(dtype, vec, P, stream) == hipSuccess ? SV_OK : SV_EHIP;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t spec_verify_multi_workspace_bytes(int B, int M, int K, int V) {
+  long long seqs, drafts;
+  if (!multi_sizes(B, M, K, V, seqs, drafts)) return 0;
+  return required_bytes((int)seqs, (int)drafts, V, 0, 1.0f);
+}
+
+int spec_verify_multi(const void* draft_logits, const void* target_logits,
+                      const int32_t* draft_tokens, const float* uniforms, int B, int M, int K,
+                      int V, float temperature, sv_dtype dtype, int32_t* out_tokens,
+                      int32_t* num_accepted, int32_t* out_chain, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  return run_multi(draft_logits, target_logits, draft_tokens, uniforms, B, M, K, V, temperature,
+                   (int)dtype, out_tokens, num_accepted, out_chain, workspace, workspace_bytes,
+                   stream);
+}
 
 const char* spec_verify_strerror(int code) {
   switch (code) {

@@ -142,6 +142,10 @@ struct Params {
   float* tok_logits;       // [total_draft + rows] or null
   int draw_remap;          // 1: the draw's rows are 2b and 2b + 1
   int* draw_rows;          // [2B] hidden rows of the draw (target, draft; -1: none)
+  // Several draft chains per sequence (sv_multi.hip): B above counts the
+  // chains as sequences of the statistics pass (B = sequences * M).
+  int M;                   // chains per sequence
+  int32_t* out_chain;      // [B / M] the lowest chain holding the emitted prefix, or null
 };
 
 // Grid size and workspace offsets of one call.
@@ -167,6 +171,8 @@ hipError_t launch_row_stats(int dtype, bool vec, const Params& P, const Plan& L,
 // The acceptance statistics after the row statistics (sv_accept.hip).
 hipError_t launch_accept(int dtype, bool vec, const Params& P, const Plan& L, hipStream_t s);
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t s);
+// Several draft chains: the walk after the statistics pass (sv_multi.hip).
+hipError_t launch_multi(int dtype, bool vec, const Params& P, hipStream_t s);
 // LM-head path (sv_lmhead.hip drives these from sv_verify.hip): the decision
 // that picks the draw's hidden rows, and the draw over fp32 logit rows.
 hipError_t launch_lm_plan(const Params& P, hipStream_t s);

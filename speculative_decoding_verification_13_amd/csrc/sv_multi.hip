@@ -1,0 +1,390 @@
+// Verification of several draft chains per sequence for gfx950
+// (spec_verify_multi).
+//
+// M chains of K drafts share one prefix; chain m's rows at position j are
+// conditioned on that chain's own tokens. The row statistics of every draft
+// and target row come from the statistics pass of the single-chain path
+// (k_stats, the chains laid out as B*M sequences). Then k_multi runs one block
+// per sequence. It walks the positions: the chains still alive are those whose
+// tokens so far equal the emitted ones. Their candidates at position j are
+// tested in chain order against the current law r, starting from the lowest
+// live chain's target row p_j: accept iff u < r(x)/q_m(x). After a rejection
+// the law becomes max(0, r - q_m)/Z, one pass over the vocabulary for Z. The
+// next candidate is tested against it. An accepted token keeps the chains
+// that proposed it and moves to the next position. When every candidate is
+// rejected (or at the bonus position), the token is drawn from the current
+// law by inverse CDF in ascending id order: one pass for per-tile sums, then
+// a scan of the crossing tile. The law of an id is p(x) with each rejected
+// candidate's q peeled off in turn, so no law is ever stored.
+//
+// Pages (by title, section): aivaro.ru answer 289 "Как работает speculative
+// decoding на уровне логитов, а не токенов?" s.6 (accept min(1, p/q), else
+// draw from max(0, p - q)/Z: rejection sampling whose result follows p),
+// s.5 steps 3-4 (truncation); Hung-yi Lee lecture-16 notes part "1、第16講"
+// (there can be several drafters) and part "4、推测解码验证流程图" item 4
+// (bonus token); aihero.vn "Speculative decoding" section "Chấp nhận bằng tỉ
+// lệ, không chỉ bằng argmax" (q draft, p target at the same prefix).
+#include "sv_rows.h"
+
+namespace sv {
+
+namespace {
+
+constexpr int kMultiBatch = 4;         // tiles a thread has in flight per round of a pass
+constexpr int kMultiMaxTiles = 1024;   // tiles (kTileVecs vectors) a row may have
+
+struct RowS {
+  float R, iS;  // reference R = fp32(max*c) and 1/S of the row's sum of 2^(l*c - R)
+  int ok;       // the row holds no NaN or +inf and some finite value
+};
+
+// Merged statistics of one row from its chunk partials, in chunk order.
+__device__ RowS merged_row(const Params& P, long long unit) {
+  float m = kNegInf, s = 0.f;
+  const unsigned long long* sl = P.slots + unit * P.chunks;
+  for (int k = 0; k < P.chunks; ++k) {
+    float om, os;
+    unpack_ms(sl[k], om, os);
+    merge_ms(m, s, om, os, P.c);
+  }
+  RowS r;
+  r.ok = __builtin_isfinite(m) && s > 0.f && __builtin_isfinite(s);
+  r.R = ref_of(m, P.c);
+  r.iS = 1.0f / s;
+  return r;
+}
+
+struct MultiShared {
+  float tsum[kMultiMaxTiles][kThreads / kWave];  // per-tile, per-wave sums of a draw pass
+  RowS p;                      // the node's target row
+  RowS q[SV_MAX_CHAINS];       // the rejected candidates' draft rows, in order
+  int qrow[SV_MAX_CHAINS];     // their draft rows
+  float iZ[SV_MAX_CHAINS];     // 1/Z of each remainder
+  int nrej;
+  int prow;                    // the node's target row
+  int pok;                     // the node's target row is usable
+  // thread 0's decisions, read by the whole block
+  int act;                     // 1 accepted, 2 rejected, 4 an unusable draft row
+  int xrow;                    // draft row of the candidate under test
+  RowS xq;                     // its statistics
+  float base;                  // mass before the crossing tile
+  float target;                // u * Z of the draw
+  int ct;                      // the crossing tile
+  int tok;                     // the drawn token
+};
+
+// Law of the N ids of vector v at the current node: r = p, with each rejected
+// candidate's q peeled off in turn, r <- max(0, r - q_k)/Z_k. With `extra`,
+// also d = max(0, r - q_extra) (the mass a rejection of that candidate leaves).
+template <int DT, bool VEC>
+__device__ __forceinline__ void law_of(const Params& P, const MultiShared& S,
+                                       const typename Vec<DT, VEC>::Raw& rp,
+                                       const typename Vec<DT, VEC>::Raw (&rq)[SV_MAX_CHAINS],
+                                       const typename Vec<DT, VEC>::Raw& rx, bool extra,
+                                       float* r, float* d) {
+  using Vc = Vec<DT, VEC>;
+  constexpr int N = Vc::N;
+  const float c = P.c;
+  float f[N];
+  Vc::get(rp, f);
+#pragma unroll
+  for (int e = 0; e < N; ++e) r[e] = fast_exp2(fmaf(f[e], c, -S.p.R)) * S.p.iS;
+#pragma unroll
+  for (int k = 0; k < SV_MAX_CHAINS; ++k) {
+    if (k < S.nrej) {
+      Vc::get(rq[k], f);
+      const RowS q = S.q[k];
+      const float iz = S.iZ[k];
+#pragma unroll
+      for (int e = 0; e < N; ++e)
+        r[e] = fmaxf(r[e] - fast_exp2(fmaf(f[e], c, -q.R)) * q.iS, 0.f) * iz;
+    }
+  }
+  if (extra) {
+    Vc::get(rx, f);
+#pragma unroll
+    for (int e = 0; e < N; ++e)
+      d[e] = fmaxf(r[e] - fast_exp2(fmaf(f[e], c, -S.xq.R)) * S.xq.iS, 0.f);
+  }
+}
+
+// One pass over the vocabulary (whole block). With `extra` it returns the sum
+// of max(0, r - q_extra) over every id (the next remainder's mass). Otherwise
+// it leaves per-tile sums of r in S.tsum (one wave sum per tile and wave) and
+// returns 0.
+template <int DT, bool VEC>
+__device__ float vocab_pass(const Params& P, MultiShared& S, bool extra) {
+  using Vc = Vec<DT, VEC>;
+  constexpr int N = Vc::N;
+  using Raw = typename Vc::Raw;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int T = (P.nvec + kTileVecs - 1) / kTileVecs;
+  const size_t prow = (size_t)S.prow * P.V;
+  float total = 0.f;
+  for (int t0 = 0; t0 < T; t0 += kMultiBatch) {
+    Raw rp[kMultiBatch], rq[kMultiBatch][SV_MAX_CHAINS], rx[kMultiBatch];
+#pragma unroll
+    for (int i = 0; i < kMultiBatch; ++i) {
+      const int v = (t0 + i) * kTileVecs + tid;
+      const bool in = v < P.nvec;
+      rp[i] = in ? Vc::load(P.target, prow, v) : Raw{};
+#pragma unroll
+      for (int k = 0; k < SV_MAX_CHAINS; ++k)
+        rq[i][k] = (in && k < S.nrej) ? Vc::load(P.draft, (size_t)S.qrow[k] * P.V, v) : Raw{};
+      rx[i] = (in && extra) ? Vc::load(P.draft, (size_t)S.xrow * P.V, v) : Raw{};
+    }
+#pragma unroll
+    for (int i = 0; i < kMultiBatch; ++i) {
+      const int v = (t0 + i) * kTileVecs + tid;
+      float r[N], d[N];
+      law_of<DT, VEC>(P, S, rp[i], rq[i], rx[i], extra, r, d);
+      float w = 0.f;
+      if (v < P.nvec) {
+#pragma unroll
+        for (int e = 0; e < N; ++e) w += extra ? d[e] : r[e];
+      }
+      if (extra) {
+        total += w;
+      } else if (t0 + i < T) {
+        const float ws = wave_sum(w);
+        if (lane == 0) S.tsum[t0 + i][wave] = ws;
+      }
+    }
+  }
+  if (!extra) {
+    __syncthreads();
+    return 0.f;
+  }
+  float out[1];
+  block_sum<1>(&total, out);
+  return out[0];
+}
+
+// Inverse CDF of the current law with uniform u (whole block): the smallest
+// id whose cumulative weight in ascending id order exceeds u * Z; if rounding
+// leaves none, the last id with positive weight.
+template <int DT, bool VEC>
+__device__ int draw_law(const Params& P, MultiShared& S, float u) {
+  using Vc = Vec<DT, VEC>;
+  constexpr int N = Vc::N;
+  using Raw = typename Vc::Raw;
+  const int tid = threadIdx.x;
+  const int T = (P.nvec + kTileVecs - 1) / kTileVecs;
+  vocab_pass<DT, VEC>(P, S, false);
+  if (tid == 0) {
+    float z = 0.f;
+    for (int t = 0; t < T; ++t) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < kThreads / kWave; ++w) s += S.tsum[t][w];
+      S.tsum[t][0] = s;
+      z += s;
+    }
+    const float target = u * z;
+    int ct = -1, last = -1;
+    float run = 0.f, base = 0.f, lbase = 0.f;
+    for (int t = 0; t < T; ++t) {
+      const float s = S.tsum[t][0];
+      if (ct < 0 && run + s > target) {
+        ct = t;
+        base = run;
+      }
+      if (s > 0.f) {
+        last = t;
+        lbase = run;
+      }
+      run += s;
+    }
+    if (ct < 0) {
+      ct = last < 0 ? 0 : last;
+      base = last < 0 ? 0.f : lbase;
+    }
+    S.ct = ct;
+    S.base = base;
+    S.target = target;
+  }
+  __syncthreads();
+  const int ct = S.ct;
+  const float base = S.base, target = S.target;
+  const int v = ct * kTileVecs + tid;
+  Raw rp{}, rq[SV_MAX_CHAINS], rx{};
+#pragma unroll
+  for (int k = 0; k < SV_MAX_CHAINS; ++k) rq[k] = Raw{};
+  if (v < P.nvec) {
+    rp = Vc::load(P.target, (size_t)S.prow * P.V, v);
+#pragma unroll
+    for (int k = 0; k < SV_MAX_CHAINS; ++k)
+      if (k < S.nrej) rq[k] = Vc::load(P.draft, (size_t)S.qrow[k] * P.V, v);
+  }
+  float r[N], d[N], w[N];
+  law_of<DT, VEC>(P, S, rp, rq, rx, false, r, d);
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    acc += (v < P.nvec) ? r[e] : 0.f;
+    w[e] = acc;
+  }
+  float tot;
+  const float excl = base + (block_incl_scan(acc, tot) - acc);
+  int cand = INT_MAX, lastpos = -1;
+  float prev = 0.f;
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    if (cand == INT_MAX && excl + w[e] > target) cand = v * N + e;
+    if (w[e] > prev) lastpos = v * N + e;
+    prev = w[e];
+  }
+  int tok = block_min_i(cand);
+  if (tok == INT_MAX) tok = block_max_i(lastpos);
+  if (tok < 0) tok = ct * kTileVecs * N;
+  return tok;
+}
+
+// One sequence (one block): see the file comment.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads, 1) void k_multi(const Params P) {
+  __shared__ MultiShared S;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int M = P.M, K = P.K;
+  const float c = P.c;
+  const int t_out = b * (K + 1);
+  // draft ids of every chain: any outside [0, V) makes the sequence invalid
+  int bad = 0;
+  for (int k = tid; k < M * K; k += kThreads) {
+    const int x = P.tokens[(size_t)b * M * K + k];
+    bad |= !(x >= 0 && x < P.V);
+  }
+  const int badtok = __syncthreads_or(bad);
+  int live = (1 << M) - 1;
+  int n = -1, code = badtok ? SV_SEQ_BAD_TOKEN : 0, tok = -1, lead = 0;
+  for (int j = 0; j <= K && code == 0 && n < 0; ++j) {
+    lead = __builtin_ctz((unsigned)live);
+    const int s_lead = b * M + lead;  // chain lead as a sequence of the statistics pass
+    if (tid == 0) {
+      S.prow = s_lead * (K + 1) + j;
+      S.p = merged_row(P, unit_of(P, true, S.prow));
+      S.nrej = 0;
+      S.pok = S.p.ok;
+    }
+    __syncthreads();
+    if (!S.pok) {
+      code = SV_SEQ_BAD_ROW;
+      break;
+    }
+    const float* ub = P.uniforms + ((size_t)b * (K + 1) + j) * (M + 1);
+    if (j == K) {  // bonus: draw from p_K of the lowest live chain
+      tok = draw_law<DT, VEC>(P, S, ub[M]);
+      n = K;
+      break;
+    }
+    int accepted = -1;
+    for (int m = 0; m < M; ++m) {
+      if (!(live & (1 << m))) continue;
+      // thread 0 tests chain m's candidate against the current law
+      if (tid == 0) {
+        const int s = b * M + m;
+        const int drow = s * K + j;
+        const RowS q = merged_row(P, unit_of(P, false, drow));
+        S.xrow = drow;
+        S.xq = q;
+        if (!q.ok) {
+          S.act = 4;
+        } else {
+          const int x = P.tokens[(size_t)s * K + j];
+          float r = fast_exp2(fmaf(load_elem<DT>(P.target, (size_t)S.prow * P.V + x), c, -S.p.R)) *
+                    S.p.iS;
+          for (int k = 0; k < S.nrej; ++k)
+            r = fmaxf(r - fast_exp2(fmaf(load_elem<DT>(P.draft, (size_t)S.qrow[k] * P.V + x), c,
+                                         -S.q[k].R)) * S.q[k].iS, 0.f) * S.iZ[k];
+          const float qx =
+              fast_exp2(fmaf(load_elem<DT>(P.draft, (size_t)drow * P.V + x), c, -q.R)) * q.iS;
+          // r/q with q(x) = 0 < r(x) accepting and r(x) = q(x) = 0 rejecting
+          const float ratio = r / qx;
+          S.act = ub[m] < ratio ? 1 : 2;
+        }
+      }
+      __syncthreads();
+      const int act = S.act;
+      if (act == 4) {
+        code = SV_SEQ_BAD_ROW;
+        break;
+      }
+      if (act == 1) {
+        accepted = m;
+        break;
+      }
+      // rejected: the mass the remainder keeps, then the remainder is the law
+      const float z = vocab_pass<DT, VEC>(P, S, true);
+      if (tid == 0 && z > 0.f) {
+        // a mass that rounds to zero keeps the current law
+        S.q[S.nrej] = S.xq;
+        S.qrow[S.nrej] = S.xrow;
+        S.iZ[S.nrej] = 1.0f / z;
+        S.nrej += 1;
+      }
+      __syncthreads();
+    }
+    if (code != 0) break;
+    if (accepted < 0) {
+      tok = draw_law<DT, VEC>(P, S, ub[M]);
+      n = j;
+      break;
+    }
+    // the accepted token; the chains that proposed it stay alive
+    const int t = P.tokens[((size_t)b * M + accepted) * K + j];
+    if (tid == 0) pub_i(P.out_tokens + t_out + j, t);
+    int keep = 0;
+    for (int m = 0; m < M; ++m)
+      if ((live & (1 << m)) && P.tokens[((size_t)b * M + m) * K + j] == t) keep |= 1 << m;
+    live = keep;
+    __syncthreads();
+  }
+  // outputs: the prefix was written as it was accepted; the drawn token, the
+  // padding, n and the chain holding the prefix
+  if (code != 0) {
+    for (int k = tid; k <= K; k += kThreads) P.out_tokens[t_out + k] = -1;
+    if (tid == 0) {
+      P.num_accepted[b] = code;
+      if (P.out_chain) P.out_chain[b] = -1;
+    }
+  } else {
+    for (int k = tid + n; k <= K; k += kThreads) P.out_tokens[t_out + k] = k == n ? tok : -1;
+    if (tid == 0) {
+      P.num_accepted[b] = n;
+      if (P.out_chain) P.out_chain[b] = lead;
+    }
+  }
+  // the statistics pass's partials of this sequence's rows back to zero
+  const int C = P.chunks;
+  const long long d_units = (long long)M * K * C, t_units = (long long)M * (K + 1) * C;
+  for (long long k = tid; k < d_units + t_units; k += kThreads) {
+    const bool tgt = k >= d_units;
+    const long long kk = tgt ? k - d_units : k;
+    const long long row = (tgt ? (long long)b * M * (K + 1) : (long long)b * M * K) + kk / C;
+    P.slots[unit_of(P, tgt, (int)row) * C + kk % C] = 0ull;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_multi(int dtype, bool vec, const Params& P, hipStream_t s) {
+  const dim3 grid((unsigned)(P.B / P.M)), block(kThreads);
+  switch (dtype) {
+    case SV_F32:
+      if (vec) hipLaunchKernelGGL((k_multi<SV_F32, true>), grid, block, 0, s, P);
+      else hipLaunchKernelGGL((k_multi<SV_F32, false>), grid, block, 0, s, P);
+      break;
+    case SV_F16:
+      if (vec) hipLaunchKernelGGL((k_multi<SV_F16, true>), grid, block, 0, s, P);
+      else hipLaunchKernelGGL((k_multi<SV_F16, false>), grid, block, 0, s, P);
+      break;
+    default:
+      if (vec) hipLaunchKernelGGL((k_multi<SV_BF16, true>), grid, block, 0, s, P);
+      else hipLaunchKernelGGL((k_multi<SV_BF16, false>), grid, block, 0, s, P);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sv

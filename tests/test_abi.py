@@ -182,3 +182,23 @@ def test_noalloc_host_checks(L):
     assert na(B=1024, K=16, V=128256) == -6
     assert L.spec_verify_workspace_bytes(1024, 1024 * 16, 128256, 0, 1.0) > 16 << 20
     assert L.spec_verify_workspace_bytes(512, 512 * 16, 128256, 0, 0.9) <= 16 << 20
+
+
+def test_multi_host_checks(L):
+    def mc(**kw):
+        a = dict(draft=_FAKE, target=_FAKE, tokens=_FAKE, uniforms=_FAKE, B=4, M=3, K=4, V=1024,
+                 T=1.0, dtype=2, out=_FAKE, num=_FAKE, chain=None, ws=_FAKE_WS, ws_bytes=16)
+        a.update(kw)
+        return L.spec_verify_multi(a["draft"], a["target"], a["tokens"], a["uniforms"], a["B"],
+                                   a["M"], a["K"], a["V"], a["T"], a["dtype"], a["out"], a["num"],
+                                   a["chain"], a["ws"], a["ws_bytes"], None)
+    assert mc() == -3
+    assert mc(M=0) == -1 and mc(M=5) == -1 and mc(K=65) == -1 and mc(V=0) == -1
+    assert mc(T=0.0) == -1 and mc(T=float("nan")) == -1
+    assert mc(dtype=9) == -2
+    assert mc(target=None) == -1 and mc(uniforms=None) == -1 and mc(tokens=None) == -1
+    assert mc(K=0, tokens=None, draft=None) == -3
+    assert mc(B=0, draft=None, target=None, tokens=None, uniforms=None, out=None, num=None) == 0
+    assert L.spec_verify_multi_workspace_bytes(4, 3, 4, 1024) == \
+        L.spec_verify_workspace_bytes(12, 48, 1024, 0, 1.0)
+    assert L.spec_verify_multi_workspace_bytes(4, 5, 4, 1024) == 0

@@ -297,3 +297,59 @@ def _bf16(a):
     """float32 array rounded to bf16 (round-to-nearest-even), as float32."""
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(
         torch.bfloat16).to(torch.float32).numpy()
+
+
+# ---------------------------------------------------------------------------
+# Several draft chains per sequence (M drafters, each proposing K tokens).
+def make_multi(B=16, M=3, K=4, V=32000, dtype="bf16", temperature=1.0, seed=3001, sd=3.0,
+               peaks=20, boost=8.0, sd_t=1.0):
+    """Rows of M draft chains per sequence, without draft tokens.
+
+    Target rows follow the logit workloads' recipe, N(0, sd^2) with `peaks`
+    ids raised by `boost`, one fresh row per (sequence, chain, position); the
+    rows of position 0 are the chain-0 row for every chain (one shared
+    prefix). A chain's draft row is its target row plus N(0, sd_t^2) noise of
+    its own (a different drafter per chain). Draft tokens come from a sampler
+    the caller passes in, position by position. share_target_prefixes then
+    makes the target rows of chains with equal prefixes agree. Draw order
+    (PCG64 stream [seed, 0]) per sequence, chain, position: the target row,
+    its peak ids, the draft noise. u_draft [B, M, K] comes from [seed, 1],
+    uniforms [B, K+1, M+1] from [seed, 2]. Rows are cast to `dtype`
+    (round-to-nearest-even, torch CPU)."""
+    rng = np.random.default_rng([seed, 0])
+    tgt = np.empty((B, M, K + 1, V), np.float32)
+    dft = np.empty((B, M, K, V), np.float32)
+    for b in range(B):
+        for m in range(M):
+            for j in range(K + 1):
+                g = rng.standard_normal(V, dtype=np.float32) * np.float32(sd)
+                if peaks > 0:
+                    g[rng.choice(V, int(peaks), replace=False)] += np.float32(boost)
+                tgt[b, m, j] = g if (j > 0 or m == 0) else tgt[b, 0, 0]
+                if j < K:
+                    dft[b, m, j] = tgt[b, m, j] + (rng.standard_normal(V, dtype=np.float32)
+                                                   * np.float32(sd_t))
+    u_draft = np.random.default_rng([seed, 1]).random((B, M, K), dtype=np.float32)
+    uniforms = np.random.default_rng([seed, 2]).random((B, K + 1, M + 1), dtype=np.float32)
+    return dict(B=B, M=M, K=K, V=V, dtype=dtype, temperature=float(temperature),
+                draft=_cast(dft.reshape(B * M * K, V), dtype).reshape(B, M, K, V),
+                target=_cast(tgt.reshape(B * M * (K + 1), V), dtype).reshape(B, M, K + 1, V),
+                u_draft=u_draft, uniforms=uniforms)
+
+
+def share_target_prefixes(target, tokens):
+    """Copy, for every position j >= 1, the target row of the lowest chain
+    with a given prefix (tokens 0..j-1) to the other chains with that prefix
+    (target [B, M, K+1, V] torch tensor, tokens [B, M, K] ints; in place)."""
+    B, M, K1 = target.shape[:3]
+    tok = np.asarray(tokens).reshape(B, M, K1 - 1)
+    for b in range(B):
+        for j in range(1, K1):
+            first = {}
+            for m in range(M):
+                key = tuple(int(t) for t in tok[b, m, :j])
+                if key in first:
+                    target[b, m, j] = target[b, first[key], j]
+                else:
+                    first[key] = m
+    return target
