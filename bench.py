@@ -78,10 +78,19 @@ class HipEvents:
         self.handles = []
 
 
-def kernel_source_digest():
+# The sources each counted kernel is compiled from (its own file and the
+# headers it includes); a change to any of them voids its counter record.
+KERNEL_SOURCES = {
+    "k_verify": ["sv_fused.hip", "sv_rows.h", "sv_device.h", "sv_launch.h"],
+    "k_stats": ["sv_verify.hip", "sv_rows.h", "sv_device.h", "sv_launch.h"],
+}
+
+
+def kernel_source_digest(kernel):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "speculative_decoding_verification_13_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    names = KERNEL_SOURCES.get(kernel) or sorted(os.listdir(csrc))
+    for f in names:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()
@@ -172,7 +181,7 @@ def traffic_summary(args):
     out = {
         "kernel": kernel, "workload": args.workload,
         "sd_t": W.WORKLOADS[args.workload].get("sd_t") if args.sd_t is None else args.sd_t,
-        "source_sha256": kernel_source_digest(),
+        "source_sha256": kernel_source_digest(kernel),
         "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
         "fetch_scale": fs, "write_scale": ws_, "hbm_bytes_per_launch": hbm,
         "commands": [
@@ -422,7 +431,7 @@ def main():
     if os.path.exists(tfile):
         with open(tfile) as f:
             tr = json.load(f)
-        if tr.get("source_sha256") == kernel_source_digest() and tr.get("workload") == args.workload \
+        if tr.get("source_sha256") == kernel_source_digest(tr.get("kernel")) and tr.get("workload") == args.workload \
                 and args.sd_t in (None, tr.get("sd_t")):
             traffic = tr.get("hbm_bytes_per_launch")
 
