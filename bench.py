@@ -104,6 +104,10 @@ def parse():
     ap.add_argument("--workload", default=W.HEADLINE, choices=sorted(W.WORKLOADS))
     ap.add_argument("--sd-t", type=float, default=None, help="target perturbation sd")
     ap.add_argument("--sets", type=int, default=4, help="rotating input copies")
+    ap.add_argument("--top-k", type=int, default=None,
+                    help="override the workload's top-k (0: none)")
+    ap.add_argument("--top-p", type=float, default=None,
+                    help="override the workload's top-p (1: none)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU oracle sample (0 disables)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -220,6 +224,10 @@ def main():
         bench_multi(args, sv)
         return
     w = W.make(args.workload, sd_t=args.sd_t)
+    if args.top_k is not None:
+        w["top_k"] = args.top_k
+    if args.top_p is not None:
+        w["top_p"] = args.top_p
     if args.path == "accept":
         bench_accept(args, w, sv)
         return
@@ -343,6 +351,8 @@ def main():
     k1_ms = ms_step if single else stage_ms[0]
 
     names = STAGES.get(nst - 1, [f"stage{i}" for i in range(nst - 1)])
+    if nst - 1 == 3 and top_k <= 0:
+        names = ["k_stats", "k_nucleus", "k_draw"]  # top-p alone
     dominant = names[0]
     rows = int((w["Ks"] + 1).sum())
     comp = W.compulsory_bytes(w)

@@ -1000,22 +1000,25 @@ __global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
 // ---------------------------------------------------------------- k_nucleus
 // One block per sampling row when top-p acts without top-k: the row's
 // threshold theta (keep l >= theta) and the kept-set sum, found by a radix
-// descent on order-preserving keys. Each pass adds every logit's mass
-// 2^(l*c - R), in 40-bit fixed point (integer sums: exact and independent of
-// the order of addition), to the bin of its key among the logits whose keys
-// lie in the range fixed so far. Walking the bins from the largest key down,
-// the kept levels are those whose strictly-larger mass is below top_p times
-// the total; the last of them lies in the bin where the running mass, this bin
-// included, first reaches that bound, and the next pass splits that bin. The
-// first pass bins only the keys of the top window (masses from 2^-16 of the
-// maximum's up), in at most 2048 equal bins no narrower than one level (a
-// widened bf16 or fp16 logit's low 16 or 13 key bits are constant), and sums
-// the whole row's mass in registers: when the level lies in the window (the
-// usual case) and the window holds at most 2048 levels (a bf16 row at the
-// temperatures of sampling), one pass resolves it. Otherwise a pass bins the
-// keys below the window down to the 2^-40 cutoff, and each further pass
-// divides the bin by 2^11, so an fp32 level takes at most four. The row's
-// chunk partials (read here only) go back to zero.
+// descent on order-preserving keys. Each pass adds the mass 2^(l*c - R) of
+// every logit whose key lies in the range fixed so far, in 40-bit fixed point
+// (integer sums: exact and independent of the order of addition), to the bin
+// of its key. Walking the bins from the largest key down, the kept levels are
+// those whose strictly-larger mass is below top_p times the row total S (the
+// sum the statistics pass formed, merged here in chunk order); the last of
+// them lies in the bin where the running mass, this bin included, first
+// reaches that bound, and the next pass splits that bin. The first pass bins
+// only the keys of the top window (masses from 2^-16 of the maximum's up), in
+// at most 2048 equal bins no narrower than one level (a widened bf16 or fp16
+// logit's low 16 or 13 key bits are constant). A logit below the window costs
+// one compare with the window's lowest value; the mass, its fixed point and
+// the LDS add are spent on the window's logits alone (about 2% of a row at
+// the sampling workloads). When the level lies in the window (the usual case)
+// and the window holds at most 2048 levels (a bf16 row at the temperatures of
+// sampling), one pass resolves it. Otherwise a pass bins the keys below the
+// window down to the 2^-40 cutoff, and each further pass divides the bin by
+// 2^11, so an fp32 level takes at most four. The row's chunk partials (read
+// here only) go back to zero.
 // Pages: aihero.vn "Speculative decoding", section "Cùng phân bố không có
 // nghĩa cùng chuỗi mỗi lần" (the same temperature, top-k and top-p on both
 // models' rows).
@@ -1026,6 +1029,7 @@ constexpr int kNucBins = 2048;
 // it, and the rest of the row only adds to the total.
 constexpr double kNucScale = 1099511627776.0;  // 2^40
 constexpr float kNucTop = 16.0f;
+constexpr int kNucRing = 128;  // candidates a wave holds in LDS: twice a wave
 
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_nucleus(const Params P) {
@@ -1037,8 +1041,8 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(const Params P) {
   __shared__ int s_cu[kCuLds];
   __shared__ float s_stat[2];
   __shared__ unsigned s_kmin[2];
-  __shared__ unsigned long long s_tot[kThreads / kWave];
   __shared__ int s_bin;
+  __shared__ float s_ring[kThreads / kWave][kNucRing];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int unit = blockIdx.x;
@@ -1058,24 +1062,34 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(const Params P) {
     }
     s_stat[0] = m;
     s_stat[1] = sm;
-    // The smallest keys whose logits pass the mass tests below (2^-40 and
-    // the top window's 2^-kNucTop): each test is monotone in the key, fails at
-    // -inf and holds at the maximum, so a bisection over the keys between
-    // finds the key exactly.
-    for (int t = 0; t < 2; ++t) {
-      const float cut = t == 0 ? -40.0f : -kNucTop;
-      unsigned lo = key_of(kNegInf), hi = lo;
-      if (__builtin_isfinite(m)) {
-        const float R0 = ref_of(m, c);
-        hi = key_of(m);
-        while (hi - lo > 1u) {
-          const unsigned mid = lo + (hi - lo) / 2u;
-          if (fmaf(float_of_key(mid), c, -R0) >= cut) hi = mid;
-          else lo = mid;
-        }
+  }
+  __syncthreads();
+  if (tid < 2 * kWave) {
+    // The smallest keys whose logits pass the mass tests below (2^-40 by wave
+    // 0, the top window's 2^-kNucTop by wave 1): each test is monotone in the
+    // key, fails at -inf and holds at the maximum. Each round the wave probes
+    // 64 keys spread over (lo, hi]; the passing probes are a suffix of the
+    // lanes, and the first of them and the one before it bound the key anew,
+    // so the interval shrinks 64-fold a round and the key is found exactly.
+    const float m0 = s_stat[0];
+    const float cut = tid < kWave ? -40.0f : -kNucTop;
+    unsigned lo = key_of(kNegInf), hi = lo;
+    if (__builtin_isfinite(m0)) {
+      const float R0 = ref_of(m0, c);
+      hi = key_of(m0);
+      while (hi - lo > 1u) {
+        const unsigned long long span = hi - lo;
+        const unsigned probe =
+            lo + (unsigned)((span * (unsigned long long)(lane + 1) + kWave - 1) / kWave);
+        const bool pass = fmaf(float_of_key(probe), c, -R0) >= cut;
+        // lane 63 probes hi, which passes
+        const int first = __ffsll((unsigned long long)__builtin_amdgcn_ballot_w64(pass)) - 1;
+        const unsigned below = __shfl(probe, first > 0 ? first - 1 : 0);
+        hi = __shfl(probe, first);
+        lo = first > 0 ? below : lo;
       }
-      s_kmin[t] = hi;
     }
+    if (lane == 0) s_kmin[tid / kWave] = hi;
   }
   __syncthreads();
   for (int k = tid; k < C; k += kThreads) sl[k] = 0ull;
@@ -1089,9 +1103,8 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(const Params P) {
   constexpr unsigned kLowMask = (1u << kLowBits) - 1u;
   // The first pass bins the keys [kbase, kbase + span] of the top window
   // (from the smallest key passing its test, widened to a level boundary, to
-  // the maximum's) and sums every logit's mass, the row total, in registers.
-  // When the crossing lies below the window, the next pass bins the keys
-  // below it that can carry mass.
+  // the maximum's). When the crossing lies below the window, the next pass
+  // bins the keys below it that can carry mass.
   // Each pass covers the keys [kbase, kbase + span], never above kmax: the
   // maximum's key in the window, kb_top - 1 below it (the window's mass is
   // already counted as the mass above), so a split bin never reaches back
@@ -1106,57 +1119,90 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(const Params P) {
   }
   bool found = false;  // a level has been resolved (else every level is kept)
   unsigned long long above = 0ull, kept = 0ull;
-  double bound = 0.0;
+  const double bound = (double)P.top_p * (double)s_stat[1] * kNucScale;
   const int nb = kNucBins;
+  // the wave's index, known to the compiler as wave-uniform (scalar loop bounds)
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+  float* ring = s_ring[wv];
   for (int lv = 0; ok; ++lv) {
     // bins of 2^s keys: the fewest that leave at most nb of them
     s = kLowBits;
     while ((span >> s) >= (unsigned)nb) ++s;
     for (int x = tid; x < nb; x += kThreads) s_hist[x] = 0ull;
     __syncthreads();
-    unsigned long long tot = 0ull;
+    // A logit of the pass's key range: its mass in fixed point, into the bin
+    // of its key. Keys below the range wrap past span. A mass below 2^-40
+    // (possible only at the level-widened low end of the range) adds zero.
     auto add = [&](float l) {
-      // a mass below 2^-40 is zero in the fixed point: skipped before any
-      // further work (as are -inf and NaN)
-      const float x = fmaf(l, c, -R);
-      if (!(x >= -40.0f)) return;
-      const unsigned long long q = (unsigned long long)(fast_exp2(x) * (float)kNucScale);
-      if (lv == 0) tot += q;
-      const unsigned d = key_of(l) - kbase;  // wraps past span below the range
+      const unsigned d = key_of(l) - kbase;
       if (d > span) return;
+      const unsigned long long q =
+          (unsigned long long)(fast_exp2(fmaf(l, c, -R)) * (float)kNucScale);
       atomicAdd(&s_hist[d >> s], q);
     };
-    int v = tid;
-    for (; v + (kBatch - 1) * kThreads < P.nvec; v += kBatch * kThreads) {
-      typename Vc::Raw r[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) r[u] = Vc::load(base, roff, v + u * kThreads);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        float f[N];
-        Vc::get(r[u], f);
-#pragma unroll
-        for (int k = 0; k < N; ++k) add(f[k]);
+    // The candidates of each wave (a superset of the range: lo_f <= l <= hi_f,
+    // which NaN fails) are appended to the wave's ring in LDS in ballot order,
+    // and the wave adds them 64 at a time with every lane busy: about 2% of
+    // the logits pass in the window pass, so adding them where they were
+    // loaded would run the add for one or two lanes at a time. n and head
+    // count appended and added candidates; both are wave-uniform, so every
+    // loop below runs on wave-uniform bounds.
+    const float lo_f = float_of_key(kbase), hi_f = float_of_key(kbase + span);
+    unsigned n = 0u, head = 0u;
+    auto drain64 = [&]() {
+      __builtin_amdgcn_wave_barrier();
+      add(ring[(head + lane) & (kNucRing - 1)]);
+      head += kWave;
+      __builtin_amdgcn_wave_barrier();
+    };
+    // The window pass skips the upper test: no logit lies above the maximum.
+    auto stage = [&](float l, auto upper) {
+      const bool in = decltype(upper)::value ? (l >= lo_f && l <= hi_f) : (l >= lo_f);
+      const unsigned long long msk = __builtin_amdgcn_ballot_w64(in);
+      if (msk == 0ull) return;
+      if (in) {
+        const unsigned pos = __builtin_amdgcn_mbcnt_hi(
+            (unsigned)(msk >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)msk, n));
+        ring[pos & (kNucRing - 1)] = l;
       }
-    }
-    for (; v < P.nvec; v += kThreads) {
-      float f[N];
-      Vc::get(Vc::load(base, roff, v), f);
+      n += (unsigned)__popcll(msk);
+      // fewer than 64 were pending before this append, so the ring of 128
+      // never overwrites one not yet added
+      if (n - head >= (unsigned)kWave) drain64();
+    };
+    auto stream = [&](auto upper) {
+      int vb = wv * kWave;  // the wave's first vector
+      for (; vb + kWave - 1 + (kBatch - 1) * kThreads < P.nvec; vb += kBatch * kThreads) {
+        typename Vc::Raw r[kBatch];
 #pragma unroll
-      for (int k = 0; k < N; ++k) add(f[k]);
-    }
-    if (lv == 0) {
+        for (int u = 0; u < kBatch; ++u) r[u] = Vc::load(base, roff, vb + lane + u * kThreads);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int o = kWave / 2; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
-      if (lane == 0) s_tot[tid / kWave] = tot;
-    }
+        for (int u = 0; u < kBatch; ++u) {
+          float f[N];
+          Vc::get(r[u], f);
+#pragma unroll
+          for (int k = 0; k < N; ++k) stage(f[k], upper);
+        }
+      }
+      for (; vb < P.nvec; vb += kThreads) {
+        const int v = vb + lane;
+        float f[N];
+        if (v < P.nvec) {
+          Vc::get(Vc::load(base, roff, v), f);
+        } else {
+#pragma unroll
+          for (int k = 0; k < N; ++k) f[k] = __builtin_nanf("");
+        }
+#pragma unroll
+        for (int k = 0; k < N; ++k) stage(f[k], upper);
+      }
+    };
+    if (lv == 0) stream(std::false_type{});
+    else stream(std::true_type{});
+    __builtin_amdgcn_wave_barrier();
+    if (lane < (int)(n - head)) add(ring[(head + lane) & (kNucRing - 1)]);
     __syncthreads();
-    if (lv == 0) {
-      unsigned long long row_total = 0ull;
-      for (int w = 0; w < kThreads / kWave; ++w) row_total += s_tot[w];
-      bound = (double)P.top_p * (double)row_total;
-    }
     // thread t sums a run of bins in descending key order, then an exclusive
     // scan over the threads gives the mass above each run
     const int per = nb / kThreads;

@@ -72,7 +72,10 @@ def nucleus_threshold(l, temperature, top_p, dtype, clamp_top=True, info=None):
     live = x >= np.float32(CUTOFF)
     q = (np.exp2(x[live]).astype(np.float32) * SCALE).astype(np.uint64)
     keys = key_of(l[live]).astype(np.int64)
-    bound = float(np.float32(top_p)) * float(int(q.sum()))
+    # the row total is the statistics pass's fp32 sum of the masses, not the
+    # fixed-point one (a logit below the window only adds to that total)
+    total = float(np.exp2(x).astype(np.float32).sum(dtype=np.float32))
+    bound = float(np.float32(top_p)) * total * float(SCALE)
     kbase, kmax = kb_top, int(key_of(m))
     span = kmax - kbase
     above, kept, found = 0, 0, False
