@@ -308,12 +308,13 @@ int spec_verify_accept_stats(const void* draft_logits, const void* target_logits
  *   out_chain     int32 [B] or NULL: the lowest chain holding the emitted
  *                 prefix (the cache to keep), -1 with an error code
  * 1 <= M <= SV_MAX_CHAINS, 0 <= K <= SV_MAX_K, temperature finite and > 0,
- * rows of at most 1024 * 256 vectors (16-byte vectors when V * element size is
- * a multiple of 16 and both arrays are 16-byte aligned, else elements). The
+ * rows of at most 2^18 vectors (16-byte vectors when V * element size is a
+ * multiple of 16 and both arrays are 16-byte aligned, else elements; longer
+ * rows return SV_EUNSUPPORTED). The
  * workspace (spec_verify_multi_workspace_bytes) obeys the zero rules of
  * spec_verify. Two kernels: the row statistics of every row, then one block
- * per sequence for the walk (one pass over the vocabulary per rejection and
- * per draw). */
+ * of 1024 threads per sequence for the walk (one pass over the vocabulary per
+ * rejection and per draw). */
 size_t spec_verify_multi_workspace_bytes(int B, int M, int K, int V);
 int spec_verify_multi(const void* draft_logits, const void* target_logits,
                       const int32_t* draft_tokens, const float* uniforms, int B, int M, int K,

@@ -462,7 +462,7 @@ int run_multi(const void* draft, const void* target, const int32_t* tokens, cons
   P.rows = (int)(seqs * (K + 1));
   P.c = (float)(1.4426950408889634074 / (double)temperature);
   P.nvec = vec ? V / (16 / es) : V;
-  if ((P.nvec + sv::kTileVecs - 1) / sv::kTileVecs > 1024) return SV_EUNSUPPORTED;
+  if (P.nvec > sv::kMultiMaxVecs) return SV_EUNSUPPORTED;  // the walk's tile sums
   P.chunk_vecs = (int)chunk_vecs_for(P.nvec, sv::kChunkSteps);
   P.chunks = (P.nvec + P.chunk_vecs - 1) / P.chunk_vecs;
   if (P.chunks > L.cmax) return SV_EUNSUPPORTED;

@@ -13,6 +13,7 @@ namespace sv {
 constexpr int kThreads = 256;             // threads per block (4 waves)
 constexpr int kBatch = 4;                 // 16-byte vectors per thread in flight per batch
 constexpr int kTileVecs = kThreads;       // draw tile = one vector per thread
+constexpr int kMultiMaxVecs = 1 << 18;    // vectors a row of spec_verify_multi may have
 constexpr int kStepVecs = kBatch * kThreads;  // vectors of a row one batch covers
 constexpr int kDrawVecs = kStepVecs;      // vectors of each row per draw block
 constexpr int kTilesPerDraw = kDrawVecs / kTileVecs;

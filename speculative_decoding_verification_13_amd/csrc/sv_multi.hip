@@ -5,8 +5,8 @@
 // conditioned on that chain's own tokens. The row statistics of every draft
 // and target row come from the statistics pass of the single-chain path
 // (k_stats, the chains laid out as B*M sequences). Then k_multi runs one block
-// per sequence. It walks the positions: the chains still alive are those whose
-// tokens so far equal the emitted ones. Their candidates at position j are
+// of 1024 threads per sequence. It walks the positions: the chains still
+// alive are those whose tokens so far equal the emitted ones. Their candidates at position j are
 // tested in chain order against the current law r, starting from the lowest
 // live chain's target row p_j: accept iff u < r(x)/q_m(x). After a rejection
 // the law becomes max(0, r - q_m)/Z, one pass over the vocabulary for Z. The
@@ -30,8 +30,17 @@ namespace sv {
 
 namespace {
 
-constexpr int kMultiBatch = 4;         // tiles a thread has in flight per round of a pass
-constexpr int kMultiMaxTiles = 1024;   // tiles (kTileVecs vectors) a row may have
+// A block of 1024 threads walks one sequence: each pass over the vocabulary
+// streams its rows with every thread of a whole compute unit, which the walk
+// (one block per sequence, B blocks) needs to keep enough loads in flight.
+constexpr int kMT = 1024;               // threads of a k_multi block
+constexpr int kMW = kMT / kWave;        // its waves
+constexpr int kMTile = kMT;             // vectors of a draw tile: one per thread
+constexpr int kMultiMaxTiles = kMultiMaxVecs / kMTile;  // tiles a row may have
+
+// Tiles a thread has in flight per round of a pass that loads R rows at each
+// vector: about eight vector loads per thread whatever the number of rows.
+__host__ __device__ constexpr int multi_batch(int R) { return R <= 1 ? 8 : (R == 2 ? 4 : 2); }
 
 struct RowS {
   float R, iS;  // reference R = fp32(max*c) and 1/S of the row's sum of 2^(l*c - R)
@@ -55,7 +64,9 @@ __device__ RowS merged_row(const Params& P, long long unit) {
 }
 
 struct MultiShared {
-  float tsum[kMultiMaxTiles][kThreads / kWave];  // per-tile, per-wave sums of a draw pass
+  float tsum[kMultiMaxTiles][kMW];  // per-tile, per-wave sums of a draw pass
+  float red[kMW];              // block reductions
+  int redi[kMW];
   RowS p;                      // the node's target row
   RowS q[SV_MAX_CHAINS];       // the rejected candidates' draft rows, in order
   int qrow[SV_MAX_CHAINS];     // their draft rows
@@ -73,78 +84,122 @@ struct MultiShared {
   int tok;                     // the drawn token
 };
 
-// Law of the N ids of vector v at the current node: r = p, with each rejected
-// candidate's q peeled off in turn, r <- max(0, r - q_k)/Z_k. With `extra`,
-// also d = max(0, r - q_extra) (the mass a rejection of that candidate leaves).
-template <int DT, bool VEC>
+// Block reductions and scan over the kMT threads (every thread gets the result).
+__device__ __forceinline__ float mt_sum(MultiShared& S, float x) {
+  x = wave_sum(x);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) S.red[threadIdx.x / kWave] = x;
+  __syncthreads();
+  float a = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMW; ++k) a += S.red[k];
+  return a;
+}
+__device__ __forceinline__ float mt_incl_scan(MultiShared& S, float x, float& total) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const float incl = wave_incl_scan(x);
+  __syncthreads();
+  if (lane == kWave - 1) S.red[w] = incl;
+  __syncthreads();
+  float base = 0.f;
+  total = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMW; ++k) {
+    const float t = S.red[k];
+    if (k < w) base += t;
+    total += t;
+  }
+  return base + incl;
+}
+template <bool MIN>
+__device__ __forceinline__ int mt_ext_i(MultiShared& S, int x) {
+  x = MIN ? wave_min_i(x) : wave_max_i(x);
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) S.redi[threadIdx.x / kWave] = x;
+  __syncthreads();
+  int r = S.redi[0];
+#pragma unroll
+  for (int k = 1; k < kMW; ++k) r = MIN ? min(r, S.redi[k]) : max(r, S.redi[k]);
+  return r;
+}
+
+// Law of the N ids of one vector at the current node: r = p, with each of the
+// NR rejected candidates' q peeled off in turn, r <- max(0, r - q_k)/Z_k. With
+// EXTRA, also d = max(0, r - q_extra) (the mass a rejection of that candidate
+// leaves).
+template <int DT, bool VEC, int NR, bool EXTRA>
 __device__ __forceinline__ void law_of(const Params& P, const MultiShared& S,
-                                       const typename Vec<DT, VEC>::Raw& rp,
-                                       const typename Vec<DT, VEC>::Raw (&rq)[SV_MAX_CHAINS],
-                                       const typename Vec<DT, VEC>::Raw& rx, bool extra,
-                                       float* r, float* d) {
+                                       const typename Vec<DT, VEC>::Raw* rv, float* r, float* d) {
   using Vc = Vec<DT, VEC>;
   constexpr int N = Vc::N;
   const float c = P.c;
   float f[N];
-  Vc::get(rp, f);
+  Vc::get(rv[0], f);
 #pragma unroll
   for (int e = 0; e < N; ++e) r[e] = fast_exp2(fmaf(f[e], c, -S.p.R)) * S.p.iS;
 #pragma unroll
-  for (int k = 0; k < SV_MAX_CHAINS; ++k) {
-    if (k < S.nrej) {
-      Vc::get(rq[k], f);
-      const RowS q = S.q[k];
-      const float iz = S.iZ[k];
+  for (int k = 0; k < NR; ++k) {
+    Vc::get(rv[1 + k], f);
+    const RowS q = S.q[k];
+    const float iz = S.iZ[k];
 #pragma unroll
-      for (int e = 0; e < N; ++e)
-        r[e] = fmaxf(r[e] - fast_exp2(fmaf(f[e], c, -q.R)) * q.iS, 0.f) * iz;
-    }
+    for (int e = 0; e < N; ++e)
+      r[e] = fmaxf(r[e] - fast_exp2(fmaf(f[e], c, -q.R)) * q.iS, 0.f) * iz;
   }
-  if (extra) {
-    Vc::get(rx, f);
+  if constexpr (EXTRA) {
+    Vc::get(rv[1 + NR], f);
 #pragma unroll
     for (int e = 0; e < N; ++e)
       d[e] = fmaxf(r[e] - fast_exp2(fmaf(f[e], c, -S.xq.R)) * S.xq.iS, 0.f);
   }
 }
 
-// One pass over the vocabulary (whole block). With `extra` it returns the sum
-// of max(0, r - q_extra) over every id (the next remainder's mass). Otherwise
-// it leaves per-tile sums of r in S.tsum (one wave sum per tile and wave) and
+// The rows of vector v at the current node: p, the NR rejected q's and (EXTRA)
+// the candidate's q; zero vectors past the row's end.
+template <int DT, bool VEC, int NR, bool EXTRA>
+__device__ __forceinline__ void load_rows(const Params& P, const MultiShared& S, int v,
+                                          typename Vec<DT, VEC>::Raw* rv) {
+  using Vc = Vec<DT, VEC>;
+  constexpr int R = 1 + NR + (EXTRA ? 1 : 0);
+  const bool in = v < P.nvec;
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const void* base = k == 0 ? P.target : P.draft;
+    const int row = k == 0 ? S.prow : (k <= NR ? S.qrow[k - 1] : S.xrow);
+    rv[k] = in ? Vc::load(base, (size_t)row * P.V, v) : typename Vc::Raw{};
+  }
+}
+
+// One pass over the vocabulary (whole block). With EXTRA it returns the sum of
+// max(0, r - q_extra) over every id (the next remainder's mass). Otherwise it
+// leaves per-tile sums of r in S.tsum (one wave sum per tile and wave) and
 // returns 0.
-template <int DT, bool VEC>
-__device__ float vocab_pass(const Params& P, MultiShared& S, bool extra) {
+template <int DT, bool VEC, int NR, bool EXTRA>
+__device__ float vocab_pass(const Params& P, MultiShared& S) {
   using Vc = Vec<DT, VEC>;
   constexpr int N = Vc::N;
   using Raw = typename Vc::Raw;
+  constexpr int R = 1 + NR + (EXTRA ? 1 : 0);
+  constexpr int NBT = multi_batch(R);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
-  const int T = (P.nvec + kTileVecs - 1) / kTileVecs;
-  const size_t prow = (size_t)S.prow * P.V;
+  const int T = (P.nvec + kMTile - 1) / kMTile;
   float total = 0.f;
-  for (int t0 = 0; t0 < T; t0 += kMultiBatch) {
-    Raw rp[kMultiBatch], rq[kMultiBatch][SV_MAX_CHAINS], rx[kMultiBatch];
+  for (int t0 = 0; t0 < T; t0 += NBT) {
+    Raw rv[NBT][R];
 #pragma unroll
-    for (int i = 0; i < kMultiBatch; ++i) {
-      const int v = (t0 + i) * kTileVecs + tid;
-      const bool in = v < P.nvec;
-      rp[i] = in ? Vc::load(P.target, prow, v) : Raw{};
+    for (int i = 0; i < NBT; ++i) load_rows<DT, VEC, NR, EXTRA>(P, S, (t0 + i) * kMTile + tid, rv[i]);
 #pragma unroll
-      for (int k = 0; k < SV_MAX_CHAINS; ++k)
-        rq[i][k] = (in && k < S.nrej) ? Vc::load(P.draft, (size_t)S.qrow[k] * P.V, v) : Raw{};
-      rx[i] = (in && extra) ? Vc::load(P.draft, (size_t)S.xrow * P.V, v) : Raw{};
-    }
-#pragma unroll
-    for (int i = 0; i < kMultiBatch; ++i) {
-      const int v = (t0 + i) * kTileVecs + tid;
+    for (int i = 0; i < NBT; ++i) {
+      const int v = (t0 + i) * kMTile + tid;
       float r[N], d[N];
-      law_of<DT, VEC>(P, S, rp[i], rq[i], rx[i], extra, r, d);
+      law_of<DT, VEC, NR, EXTRA>(P, S, rv[i], r, d);
       float w = 0.f;
       if (v < P.nvec) {
 #pragma unroll
-        for (int e = 0; e < N; ++e) w += extra ? d[e] : r[e];
+        for (int e = 0; e < N; ++e) w += EXTRA ? d[e] : r[e];
       }
-      if (extra) {
+      if constexpr (EXTRA) {
         total += w;
       } else if (t0 + i < T) {
         const float ws = wave_sum(w);
@@ -152,32 +207,42 @@ __device__ float vocab_pass(const Params& P, MultiShared& S, bool extra) {
       }
     }
   }
-  if (!extra) {
+  if constexpr (!EXTRA) {
     __syncthreads();
     return 0.f;
+  } else {
+    return mt_sum(S, total);
   }
-  float out[1];
-  block_sum<1>(&total, out);
-  return out[0];
+}
+
+// The mass max(0, r - q_candidate) summed over the vocabulary.
+template <int DT, bool VEC>
+__device__ float remainder_mass(const Params& P, MultiShared& S) {
+  switch (S.nrej) {
+    case 0: return vocab_pass<DT, VEC, 0, true>(P, S);
+    case 1: return vocab_pass<DT, VEC, 1, true>(P, S);
+    case 2: return vocab_pass<DT, VEC, 2, true>(P, S);
+    default: return vocab_pass<DT, VEC, SV_MAX_CHAINS - 1, true>(P, S);
+  }
 }
 
 // Inverse CDF of the current law with uniform u (whole block): the smallest
 // id whose cumulative weight in ascending id order exceeds u * Z; if rounding
 // leaves none, the last id with positive weight.
-template <int DT, bool VEC>
-__device__ int draw_law(const Params& P, MultiShared& S, float u) {
+template <int DT, bool VEC, int NR>
+__device__ int draw_law_n(const Params& P, MultiShared& S, float u) {
   using Vc = Vec<DT, VEC>;
   constexpr int N = Vc::N;
   using Raw = typename Vc::Raw;
   const int tid = threadIdx.x;
-  const int T = (P.nvec + kTileVecs - 1) / kTileVecs;
-  vocab_pass<DT, VEC>(P, S, false);
+  const int T = (P.nvec + kMTile - 1) / kMTile;
+  vocab_pass<DT, VEC, NR, false>(P, S);
   if (tid == 0) {
     float z = 0.f;
     for (int t = 0; t < T; ++t) {
       float s = 0.f;
 #pragma unroll
-      for (int w = 0; w < kThreads / kWave; ++w) s += S.tsum[t][w];
+      for (int w = 0; w < kMW; ++w) s += S.tsum[t][w];
       S.tsum[t][0] = s;
       z += s;
     }
@@ -207,18 +272,11 @@ __device__ int draw_law(const Params& P, MultiShared& S, float u) {
   __syncthreads();
   const int ct = S.ct;
   const float base = S.base, target = S.target;
-  const int v = ct * kTileVecs + tid;
-  Raw rp{}, rq[SV_MAX_CHAINS], rx{};
-#pragma unroll
-  for (int k = 0; k < SV_MAX_CHAINS; ++k) rq[k] = Raw{};
-  if (v < P.nvec) {
-    rp = Vc::load(P.target, (size_t)S.prow * P.V, v);
-#pragma unroll
-    for (int k = 0; k < SV_MAX_CHAINS; ++k)
-      if (k < S.nrej) rq[k] = Vc::load(P.draft, (size_t)S.qrow[k] * P.V, v);
-  }
+  const int v = ct * kMTile + tid;
+  Raw rv[1 + NR];
+  load_rows<DT, VEC, NR, false>(P, S, v, rv);
   float r[N], d[N], w[N];
-  law_of<DT, VEC>(P, S, rp, rq, rx, false, r, d);
+  law_of<DT, VEC, NR, false>(P, S, rv, r, d);
   float acc = 0.f;
 #pragma unroll
   for (int e = 0; e < N; ++e) {
@@ -226,7 +284,7 @@ __device__ int draw_law(const Params& P, MultiShared& S, float u) {
     w[e] = acc;
   }
   float tot;
-  const float excl = base + (block_incl_scan(acc, tot) - acc);
+  const float excl = base + (mt_incl_scan(S, acc, tot) - acc);
   int cand = INT_MAX, lastpos = -1;
   float prev = 0.f;
 #pragma unroll
@@ -235,15 +293,26 @@ __device__ int draw_law(const Params& P, MultiShared& S, float u) {
     if (w[e] > prev) lastpos = v * N + e;
     prev = w[e];
   }
-  int tok = block_min_i(cand);
-  if (tok == INT_MAX) tok = block_max_i(lastpos);
-  if (tok < 0) tok = ct * kTileVecs * N;
+  int tok = mt_ext_i<true>(S, cand);
+  if (tok == INT_MAX) tok = mt_ext_i<false>(S, lastpos);
+  if (tok < 0) tok = ct * kMTile * N;
   return tok;
+}
+
+template <int DT, bool VEC>
+__device__ int draw_law(const Params& P, MultiShared& S, float u) {
+  switch (S.nrej) {
+    case 0: return draw_law_n<DT, VEC, 0>(P, S, u);
+    case 1: return draw_law_n<DT, VEC, 1>(P, S, u);
+    case 2: return draw_law_n<DT, VEC, 2>(P, S, u);
+    case 3: return draw_law_n<DT, VEC, 3>(P, S, u);
+    default: return draw_law_n<DT, VEC, SV_MAX_CHAINS>(P, S, u);
+  }
 }
 
 // One sequence (one block): see the file comment.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads, 1) void k_multi(const Params P) {
+__global__ __launch_bounds__(kMT, 1) void k_multi(const Params P) {
   __shared__ MultiShared S;
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
@@ -252,7 +321,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_multi(const Params P) {
   const int t_out = b * (K + 1);
   // draft ids of every chain: any outside [0, V) makes the sequence invalid
   int bad = 0;
-  for (int k = tid; k < M * K; k += kThreads) {
+  for (int k = tid; k < M * K; k += kMT) {
     const int x = P.tokens[(size_t)b * M * K + k];
     bad |= !(x >= 0 && x < P.V);
   }
@@ -316,7 +385,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_multi(const Params P) {
         break;
       }
       // rejected: the mass the remainder keeps, then the remainder is the law
-      const float z = vocab_pass<DT, VEC>(P, S, true);
+      const float z = remainder_mass<DT, VEC>(P, S);
       if (tid == 0 && z > 0.f) {
         // a mass that rounds to zero keeps the current law
         S.q[S.nrej] = S.xq;
@@ -344,13 +413,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_multi(const Params P) {
   // outputs: the prefix was written as it was accepted; the drawn token, the
   // padding, n and the chain holding the prefix
   if (code != 0) {
-    for (int k = tid; k <= K; k += kThreads) P.out_tokens[t_out + k] = -1;
+    for (int k = tid; k <= K; k += kMT) P.out_tokens[t_out + k] = -1;
     if (tid == 0) {
       P.num_accepted[b] = code;
       if (P.out_chain) P.out_chain[b] = -1;
     }
   } else {
-    for (int k = tid + n; k <= K; k += kThreads) P.out_tokens[t_out + k] = k == n ? tok : -1;
+    for (int k = tid + n; k <= K; k += kMT) P.out_tokens[t_out + k] = k == n ? tok : -1;
     if (tid == 0) {
       P.num_accepted[b] = n;
       if (P.out_chain) P.out_chain[b] = lead;
@@ -359,7 +428,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_multi(const Params P) {
   // the statistics pass's partials of this sequence's rows back to zero
   const int C = P.chunks;
   const long long d_units = (long long)M * K * C, t_units = (long long)M * (K + 1) * C;
-  for (long long k = tid; k < d_units + t_units; k += kThreads) {
+  for (long long k = tid; k < d_units + t_units; k += kMT) {
     const bool tgt = k >= d_units;
     const long long kk = tgt ? k - d_units : k;
     const long long row = (tgt ? (long long)b * M * (K + 1) : (long long)b * M * K) + kk / C;
@@ -370,7 +439,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_multi(const Params P) {
 }  // namespace
 
 hipError_t launch_multi(int dtype, bool vec, const Params& P, hipStream_t s) {
-  const dim3 grid((unsigned)(P.B / P.M)), block(kThreads);
+  const dim3 grid((unsigned)(P.B / P.M)), block(kMT);
   switch (dtype) {
     case SV_F32:
       if (vec) hipLaunchKernelGGL((k_multi<SV_F32, true>), grid, block, 0, s, P);
