@@ -104,6 +104,8 @@ def parse():
     ap.add_argument("--workload", default=W.HEADLINE, choices=sorted(W.WORKLOADS))
     ap.add_argument("--sd-t", type=float, default=None, help="target perturbation sd")
     ap.add_argument("--sets", type=int, default=4, help="rotating input copies")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip timing the other workloads in the headline run")
     ap.add_argument("--top-k", type=int, default=None,
                     help="override the workload's top-k (0: none)")
     ap.add_argument("--top-p", type=float, default=None,
@@ -173,11 +175,14 @@ def traffic_summary(args):
             raise SystemExit(f"bench.py: no copy dispatch in {sub}")
         return cal_bytes_kib / statistics.median(vals)
 
+    # The counter runs are `--steps 20 --warmup 2`: the first dispatch of the
+    # kernel draws the draft tokens (a smaller call), the next 22 are the warmup
+    # and timed steps; the calls after them (stage events, acceptance
+    # statistics, the sd_t sweep) are left out.
     def kern(sub, counter):
         vals = [v for name, v in _counter_per_dispatch(os.path.join(d, sub), counter)
                 if f"::{kernel}<" in name or name.startswith(kernel)]
-        # the first dispatch draws the draft tokens (a smaller call); the rest are timed steps
-        return statistics.median(vals[1:] if len(vals) > 1 else vals)
+        return statistics.median(vals[1:23] if len(vals) > 1 else vals)
 
     fs, ws_ = calib("cal_fetch", "FETCH_SIZE"), calib("cal_write", "WRITE_SIZE")
     fk, wk = kern("fetch", "FETCH_SIZE"), kern("write", "WRITE_SIZE")
@@ -190,7 +195,7 @@ def traffic_summary(args):
         "fetch_scale": fs, "write_scale": ws_, "hbm_bytes_per_launch": hbm,
         "commands": [
             f"rocprofv3 --pmc {c} --output-format csv -d <out>/{sub} -o run -- python3 bench.py "
-            f"--cpu-seconds 0 --steps 20 --warmup 2 --workload {args.workload}"
+            f"--cpu-seconds 0 --steps 20 --warmup 2 --no-other-configs --workload {args.workload}"
             for c, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write"))] + [
             f"rocprofv3 --pmc {c} --output-format csv -d <out>/{sub} -o run -- python3 bench.py "
             "--calibrate-copy" for c, sub in (("FETCH_SIZE", "cal_fetch"), ("WRITE_SIZE", "cal_write"))]
@@ -393,6 +398,13 @@ def main():
             "mean_expected_accepted": float(exp_d.float().mean().cpu()),
         }
 
+    # The other workloads, in the headline run only (the default command).
+    others = {}
+    if (args.workload == W.HEADLINE and args.sd_t is None and args.top_k is None
+            and args.top_p is None and not args.no_other_configs):
+        for name in OTHER_CONFIGS:
+            others[name] = time_config(name, sv, dev, max(10, args.steps // 4), args.warmup)
+
     # The other target-perturbation settings of a swept workload (the same
     # draft rows and draft tokens, targets drawn with the other spread), each
     # timed like the headline steps.
@@ -485,6 +497,7 @@ def main():
         },
         "with_accept_stats": with_stats,
         "sd_t_sweep": sweep or None,
+        "other_configs": others or None,
         "wall_s": wall,
         "host_enqueue_us_per_step": host_enqueue / args.steps * 1e6,
         "host_enqueue_us_per_step_c_abi": c_enqueue_us,
@@ -494,6 +507,71 @@ def main():
 
 
 _CPU = {}
+
+
+# Every other logit workload, timed in the headline run so that its line
+# carries them all: the small cases (C0, C1: latency-bound, report-only), the
+# filtered batch and the ragged half-greedy batch.
+OTHER_CONFIGS = ["tiny_f32_B4_K4_V1024", "bf16_B32_K4_V32000",
+                 "f16_B256_K4_V151936_topk50_topp0.9", "bf16_B512_Kragged_V128256_halfgreedy"]
+
+
+def time_config(name, sv, dev, steps, warmup):
+    """One workload's verification step, timed as the headline's: inputs in HBM
+    (four rotating copies when a copy fits in the 256 MB Infinity Cache), the
+    draft tokens drawn by the library, K calls back to back between two events."""
+    w = W.make(name)
+    B, V = w["B"], w["V"]
+    cu = w["cu_draft"]
+    n_draft = int(cu[-1])
+    n_target = n_draft + B
+    T, top_k, top_p = w["temperature"], w["top_k"], w["top_p"]
+    d0, t0 = w["draft"].to(dev), w["target"].to(dev)
+    cu_d = torch.from_numpy(cu.astype(np.int32)).to(dev)
+    greedy_d = torch.from_numpy(w["greedy"].astype(np.uint8)).to(dev) if w["greedy"].any() else None
+    uni_d = torch.from_numpy(w["uniforms"]).to(dev)
+    zeros_cu = torch.zeros(n_draft + 1, dtype=torch.int32, device=dev)
+    g_rows = (torch.from_numpy(W.draft_row_greedy_mask(w).astype(np.uint8)).to(dev)
+              if w["greedy"].any() else None)
+    tokens_d, _ = sv.spec_verify_ragged(None, d0, None, torch.from_numpy(w["u_draft"]).to(dev),
+                                        zeros_cu, g_rows, n_draft, V, T, top_k, top_p,
+                                        total_draft_rows=0)
+    comp = W.compulsory_bytes(w)
+    nsets = 1 if comp > (256 << 20) else 4
+    sets = [(d0, t0)] + [(d0.clone(), t0.clone()) for _ in range(nsets - 1)]
+    ws = sv.make_workspace(B, n_draft, V, top_k, top_p, dev)
+    out = torch.empty(n_target, dtype=torch.int32, device=dev)
+    num = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def step(k):
+        d, t = sets[k % nsets]
+        sv.spec_verify_ragged(d, t, tokens_d, uni_d, cu_d, greedy_d, B, V, T, top_k, top_p,
+                              total_draft_rows=n_draft, out_tokens=out, num_accepted=num,
+                              workspace=ws)
+
+    for k in range(warmup):
+        step(k)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(steps):
+        step(k)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    n_acc = num.cpu().numpy()
+    res = {
+        "ms_per_step": ms, "rows_per_s": n_target / (ms * 1e-3),
+        "effective_GBps": comp / (ms * 1e-3) / 1e9,
+        "effective_frac_of_peak": comp / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "compulsory_bytes_per_step": comp, "steps": steps, "rotating_sets": nsets,
+        "entry_point": "spec_verify_ragged",
+        "mean_accepted": float(n_acc[n_acc >= 0].mean()) if (n_acc >= 0).any() else None,
+        "errors": int((n_acc < 0).sum()),
+    }
+    del sets, d0, t0, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_accept(args, w, sv):
