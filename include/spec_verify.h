@@ -304,7 +304,9 @@ int spec_verify_accept_stats(const void* draft_logits, const void* target_logits
  *                 stops)
  *   out_tokens    int32 [B, K+1] (-1 padded); num_accepted int32 [B] (n, or
  *                 SV_SEQ_BAD_TOKEN for any id outside [0, V), SV_SEQ_BAD_ROW
- *                 for a used row with NaN, +inf or no finite value)
+ *                 for a used row with NaN, +inf or no finite value,
+ *                 SV_SEQ_SYNC_TIMEOUT if a bounded wait between the blocks of
+ *                 the sequence ran out; then fill the workspace with zeros again)
  *   out_chain     int32 [B] or NULL: the lowest chain holding the emitted
  *                 prefix (the cache to keep), -1 with an error code
  * 1 <= M <= SV_MAX_CHAINS, 0 <= K <= SV_MAX_K, temperature finite and > 0,
@@ -312,9 +314,13 @@ int spec_verify_accept_stats(const void* draft_logits, const void* target_logits
  * multiple of 16 and both arrays are 16-byte aligned, else elements; longer
  * rows return SV_EUNSUPPORTED). The
  * workspace (spec_verify_multi_workspace_bytes) obeys the zero rules of
- * spec_verify. Two kernels: the row statistics of every row, then one block
- * of 1024 threads per sequence for the walk (one pass over the vocabulary per
- * rejection and per draw). */
+ * spec_verify. Two kernels: the row statistics of every row, then the walk,
+ * four blocks of 1024 threads per sequence, each on a quarter of the
+ * vocabulary (one pass per rejection and per draw, the blocks exchanging
+ * their sums through the workspace after each pass). The blocks of a sequence
+ * wait for each other, so, as for spec_verify, the call assumes no other
+ * kernel holds the device's compute units meanwhile; a wait that runs out
+ * gives SV_SEQ_SYNC_TIMEOUT instead of a hang. */
 size_t spec_verify_multi_workspace_bytes(int B, int M, int K, int V);
 int spec_verify_multi(const void* draft_logits, const void* target_logits,
                       const int32_t* draft_tokens, const float* uniforms, int B, int M, int K,

@@ -422,6 +422,18 @@ int run_accept(const void* draft, const void* target, const int32_t* cu, int B, 
   return sv::launch_accept(dtype, vec, P, L, stream) == hipSuccess ? SV_OK : SV_EHIP;
 }
 
+// Tile totals a sequence's draw may publish (tiles of 1024 vectors, the
+// walk's block width; a row has at most min(V, kMultiMaxVecs) vectors), and
+// the bytes of the walk's cross-block state after the statistics layout: a
+// sync record and the tile totals per sequence.
+int multi_tiles(int V) {
+  const int vecs = V < sv::kMultiMaxVecs ? V : sv::kMultiMaxVecs;
+  return (vecs + 1023) / 1024;
+}
+size_t multi_state_bytes(int B, int V) {
+  return align_up((size_t)B * sv::kMultiSyncWords * 4) + align_up((size_t)B * multi_tiles(V) * 4);
+}
+
 bool multi_sizes(int B, int M, int K, int V, long long& seqs, long long& drafts) {
   if (B < 0 || M < 1 || M > SV_MAX_CHAINS || K < 0 || K > SV_MAX_K || V < 1) return false;
   seqs = (long long)B * M;
@@ -445,7 +457,7 @@ int run_multi(const void* draft, const void* target, const int32_t* tokens, cons
   sv::Plan L;
   if (!make_plan((int)seqs, (int)drafts, V, 0, 1.0f, SIZE_MAX, L)) return SV_EUNSUPPORTED;
   if (workspace == nullptr || ((uintptr_t)workspace % kAlign) != 0 ||
-      !make_plan((int)seqs, (int)drafts, V, 0, 1.0f, workspace_bytes, L))
+      L.total_bytes + multi_state_bytes(B, V) > workspace_bytes)
     return SV_EWORKSPACE;
   const int es = esize_of(dtype);
   const bool vec = ((size_t)V * es) % 16 == 0 && aligned16(target) &&
@@ -472,6 +484,10 @@ int run_multi(const void* draft, const void* target, const int32_t* tokens, cons
   P.spin_limit = kDefaultSpinLimit;
   P.M = M;
   P.out_chain = out_chain;
+  char* ms = reinterpret_cast<char*>(workspace) + L.total_bytes;
+  P.msync = reinterpret_cast<int*>(ms);
+  P.mtiles = reinterpret_cast<float*>(ms + align_up((size_t)B * sv::kMultiSyncWords * 4));
+  P.mtiles_stride = multi_tiles(V);
   L.chunks = P.chunks;
   L.chunk_vecs = P.chunk_vecs;
   L.stats_blocks = ((long long)P.total_draft + P.rows) * P.chunks;
@@ -489,7 +505,9 @@ extern "C" {
 size_t spec_verify_multi_workspace_bytes(int B, int M, int K, int V) {
   long long seqs, drafts;
   if (!multi_sizes(B, M, K, V, seqs, drafts)) return 0;
-  return required_bytes((int)seqs, (int)drafts, V, 0, 1.0f);
+  sv::Plan L;
+  if (!make_plan((int)seqs, (int)drafts, V, 0, 1.0f, SIZE_MAX, L)) return 0;
+  return L.total_bytes + multi_state_bytes(B, V);
 }
 
 int spec_verify_multi(const void* draft_logits, const void* target_logits,

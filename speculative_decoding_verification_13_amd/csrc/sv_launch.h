@@ -14,6 +14,8 @@ constexpr int kThreads = 256;             // threads per block (4 waves)
 constexpr int kBatch = 4;                 // 16-byte vectors per thread in flight per batch
 constexpr int kTileVecs = kThreads;       // draw tile = one vector per thread
 constexpr int kMultiMaxVecs = 1 << 18;    // vectors a row of spec_verify_multi may have
+constexpr int kMultiSplit = 4;            // blocks that share one sequence's walk
+constexpr int kMultiSyncWords = 16;       // per-sequence words of the walk's cross-block state
 constexpr int kStepVecs = kBatch * kThreads;  // vectors of a row one batch covers
 constexpr int kDrawVecs = kStepVecs;      // vectors of each row per draw block
 constexpr int kTilesPerDraw = kDrawVecs / kTileVecs;
@@ -147,6 +149,9 @@ struct Params {
   // chains as sequences of the statistics pass (B = sequences * M).
   int M;                   // chains per sequence
   int32_t* out_chain;      // [B / M] the lowest chain holding the emitted prefix, or null
+  int* msync;              // [B / M * kMultiSyncWords] the walk's cross-block state
+  float* mtiles;           // [B / M * mtiles_stride] tile totals of a sequence's draw
+  int mtiles_stride;
 };
 
 // Grid size and workspace offsets of one call.

@@ -4,9 +4,12 @@
 // M chains of K drafts share one prefix; chain m's rows at position j are
 // conditioned on that chain's own tokens. The row statistics of every draft
 // and target row come from the statistics pass of the single-chain path
-// (k_stats, the chains laid out as B*M sequences). Then k_multi runs one block
-// of 1024 threads per sequence. It walks the positions: the chains still
-// alive are those whose tokens so far equal the emitted ones. Their candidates at position j are
+// (k_stats, the chains laid out as B*M sequences). Then k_multi runs
+// kMultiSplit blocks of 1024 threads per sequence, each on a contiguous range
+// of the vocabulary's tiles; every block walks the sequence the same way and
+// the blocks exchange their pass sums through the workspace. It walks the
+// positions: the chains still alive are those whose tokens so far equal the
+// emitted ones. Their candidates at position j are
 // tested in chain order against the current law r, starting from the lowest
 // live chain's target row p_j: accept iff u < r(x)/q_m(x). After a rejection
 // the law becomes max(0, r - q_m)/Z, one pass over the vocabulary for Z. The
@@ -82,7 +85,41 @@ struct MultiShared {
   float target;                // u * Z of the draw
   int ct;                      // the crossing tile
   int tok;                     // the drawn token
+  int tb, te;                  // this block's tiles of every pass
+  int pass;                    // passes this block has joined
+  int to;                      // a wait of this block ran out
 };
+
+// Cross-block state of sequence b in the workspace (zero between calls):
+// word 0 counts the passes the sequence's blocks have published (each block
+// bumps it once a pass), word 1 the blocks that are done, word 2 is set when a
+// wait ran out, and words 4 + kMultiSplit * (pass & 1) + g hold block g's
+// remainder mass of a pass (two sets: a block publishes pass p + 1 only after
+// every block published pass p, which each did after reading pass p - 1).
+__device__ __forceinline__ int* msync_of(const Params& P, int b) {
+  return P.msync + (size_t)b * kMultiSyncWords;
+}
+
+// Every block of sequence b publishes, then waits (bounded) until all have
+// published this pass.
+__device__ void seq_sync(const Params& P, MultiShared& S, int b) {
+  drain_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int* ctr = msync_of(P, b);
+    bump(ctr);
+    const int want = kMultiSplit * (S.pass + 1);
+    for (int spins = 0; obs_i(ctr) < want; ++spins) {
+      if (spins >= P.spin_limit) {
+        S.to = 1;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    S.pass += 1;
+  }
+  __syncthreads();
+}
 
 // Block reductions and scan over the kMT threads (every thread gets the result).
 __device__ __forceinline__ float mt_sum(MultiShared& S, float x) {
@@ -170,10 +207,10 @@ __device__ __forceinline__ void load_rows(const Params& P, const MultiShared& S,
   }
 }
 
-// One pass over the vocabulary (whole block). With EXTRA it returns the sum of
-// max(0, r - q_extra) over every id (the next remainder's mass). Otherwise it
-// leaves per-tile sums of r in S.tsum (one wave sum per tile and wave) and
-// returns 0.
+// One pass over this block's tiles of the vocabulary (whole block). With
+// EXTRA it returns the block's sum of max(0, r - q_extra) (its part of the
+// next remainder's mass). Otherwise it leaves per-tile sums of r in S.tsum
+// (one wave sum per tile and wave) and returns 0.
 template <int DT, bool VEC, int NR, bool EXTRA>
 __device__ float vocab_pass(const Params& P, MultiShared& S) {
   using Vc = Vec<DT, VEC>;
@@ -183,25 +220,26 @@ __device__ float vocab_pass(const Params& P, MultiShared& S) {
   constexpr int NBT = multi_batch(R);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
-  const int T = (P.nvec + kMTile - 1) / kMTile;
+  const int tb = S.tb, te = S.te;
   float total = 0.f;
-  for (int t0 = 0; t0 < T; t0 += NBT) {
+  for (int t0 = tb; t0 < te; t0 += NBT) {
     Raw rv[NBT][R];
 #pragma unroll
-    for (int i = 0; i < NBT; ++i) load_rows<DT, VEC, NR, EXTRA>(P, S, (t0 + i) * kMTile + tid, rv[i]);
+    for (int i = 0; i < NBT; ++i)
+      load_rows<DT, VEC, NR, EXTRA>(P, S, t0 + i < te ? (t0 + i) * kMTile + tid : P.nvec, rv[i]);
 #pragma unroll
     for (int i = 0; i < NBT; ++i) {
       const int v = (t0 + i) * kMTile + tid;
       float r[N], d[N];
       law_of<DT, VEC, NR, EXTRA>(P, S, rv[i], r, d);
       float w = 0.f;
-      if (v < P.nvec) {
+      if (t0 + i < te && v < P.nvec) {
 #pragma unroll
         for (int e = 0; e < N; ++e) w += EXTRA ? d[e] : r[e];
       }
       if constexpr (EXTRA) {
         total += w;
-      } else if (t0 + i < T) {
+      } else if (t0 + i < te) {
         const float ws = wave_sum(w);
         if (lane == 0) S.tsum[t0 + i][wave] = ws;
       }
@@ -215,37 +253,53 @@ __device__ float vocab_pass(const Params& P, MultiShared& S) {
   }
 }
 
-// The mass max(0, r - q_candidate) summed over the vocabulary.
+// The mass max(0, r - q_candidate) summed over the vocabulary: each block's
+// part, published, then the parts added in block order (the same sum in every
+// block of the sequence).
 template <int DT, bool VEC>
-__device__ float remainder_mass(const Params& P, MultiShared& S) {
+__device__ float remainder_mass(const Params& P, MultiShared& S, int b, int g) {
+  float part;
   switch (S.nrej) {
-    case 0: return vocab_pass<DT, VEC, 0, true>(P, S);
-    case 1: return vocab_pass<DT, VEC, 1, true>(P, S);
-    case 2: return vocab_pass<DT, VEC, 2, true>(P, S);
-    default: return vocab_pass<DT, VEC, SV_MAX_CHAINS - 1, true>(P, S);
+    case 0: part = vocab_pass<DT, VEC, 0, true>(P, S); break;
+    case 1: part = vocab_pass<DT, VEC, 1, true>(P, S); break;
+    case 2: part = vocab_pass<DT, VEC, 2, true>(P, S); break;
+    default: part = vocab_pass<DT, VEC, SV_MAX_CHAINS - 1, true>(P, S);
   }
+  float* parts = reinterpret_cast<float*>(msync_of(P, b) + 4 + kMultiSplit * (S.pass & 1));
+  if (threadIdx.x == 0) pub_f(parts + g, part);
+  seq_sync(P, S, b);
+  float z = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMultiSplit; ++k) z += obs_f(parts + k);
+  return z;
 }
 
 // Inverse CDF of the current law with uniform u (whole block): the smallest
 // id whose cumulative weight in ascending id order exceeds u * Z; if rounding
 // leaves none, the last id with positive weight.
 template <int DT, bool VEC, int NR>
-__device__ int draw_law_n(const Params& P, MultiShared& S, float u) {
+__device__ int draw_law_n(const Params& P, MultiShared& S, float u, int b) {
   using Vc = Vec<DT, VEC>;
   constexpr int N = Vc::N;
   using Raw = typename Vc::Raw;
   const int tid = threadIdx.x;
   const int T = (P.nvec + kMTile - 1) / kMTile;
   vocab_pass<DT, VEC, NR, false>(P, S);
+  // this block's tile totals to the sequence's list, then every tile's
+  float* tiles = P.mtiles + (size_t)b * P.mtiles_stride;
+  for (int t = S.tb + tid; t < S.te; t += kMT) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMW; ++w) s += S.tsum[t][w];
+    pub_f(tiles + t, s);
+  }
+  seq_sync(P, S, b);
+  if (S.to) return -1;
+  for (int t = tid; t < T; t += kMT) S.tsum[t][0] = obs_f(tiles + t);
+  __syncthreads();
   if (tid == 0) {
     float z = 0.f;
-    for (int t = 0; t < T; ++t) {
-      float s = 0.f;
-#pragma unroll
-      for (int w = 0; w < kMW; ++w) s += S.tsum[t][w];
-      S.tsum[t][0] = s;
-      z += s;
-    }
+    for (int t = 0; t < T; ++t) z += S.tsum[t][0];
     const float target = u * z;
     int ct = -1, last = -1;
     float run = 0.f, base = 0.f, lbase = 0.f;
@@ -271,6 +325,7 @@ __device__ int draw_law_n(const Params& P, MultiShared& S, float u) {
   }
   __syncthreads();
   const int ct = S.ct;
+  if (ct < S.tb || ct >= S.te) return -1;  // another block of the sequence picks
   const float base = S.base, target = S.target;
   const int v = ct * kMTile + tid;
   Raw rv[1 + NR];
@@ -299,14 +354,15 @@ __device__ int draw_law_n(const Params& P, MultiShared& S, float u) {
   return tok;
 }
 
+// The drawn token in the block whose tiles hold the crossing, -1 in the others.
 template <int DT, bool VEC>
-__device__ int draw_law(const Params& P, MultiShared& S, float u) {
+__device__ int draw_law(const Params& P, MultiShared& S, float u, int b) {
   switch (S.nrej) {
-    case 0: return draw_law_n<DT, VEC, 0>(P, S, u);
-    case 1: return draw_law_n<DT, VEC, 1>(P, S, u);
-    case 2: return draw_law_n<DT, VEC, 2>(P, S, u);
-    case 3: return draw_law_n<DT, VEC, 3>(P, S, u);
-    default: return draw_law_n<DT, VEC, SV_MAX_CHAINS>(P, S, u);
+    case 0: return draw_law_n<DT, VEC, 0>(P, S, u, b);
+    case 1: return draw_law_n<DT, VEC, 1>(P, S, u, b);
+    case 2: return draw_law_n<DT, VEC, 2>(P, S, u, b);
+    case 3: return draw_law_n<DT, VEC, 3>(P, S, u, b);
+    default: return draw_law_n<DT, VEC, SV_MAX_CHAINS>(P, S, u, b);
   }
 }
 
@@ -314,11 +370,21 @@ __device__ int draw_law(const Params& P, MultiShared& S, float u) {
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kMT, 1) void k_multi(const Params P) {
   __shared__ MultiShared S;
+  __shared__ int s_last;
   const int tid = threadIdx.x;
-  const int b = blockIdx.x;
+  // kMultiSplit consecutive blocks walk sequence b, block g on the g-th
+  // contiguous range of the vocabulary's tiles
+  const int b = blockIdx.x / kMultiSplit, g = blockIdx.x % kMultiSplit;
   const int M = P.M, K = P.K;
   const float c = P.c;
   const int t_out = b * (K + 1);
+  if (tid == 0) {
+    const int T = (P.nvec + kMTile - 1) / kMTile;
+    S.tb = g * T / kMultiSplit;
+    S.te = (g + 1) * T / kMultiSplit;
+    S.pass = 0;
+    S.to = 0;
+  }
   // draft ids of every chain: any outside [0, V) makes the sequence invalid
   int bad = 0;
   for (int k = tid; k < M * K; k += kMT) {
@@ -344,7 +410,7 @@ __global__ __launch_bounds__(kMT, 1) void k_multi(const Params P) {
     }
     const float* ub = P.uniforms + ((size_t)b * (K + 1) + j) * (M + 1);
     if (j == K) {  // bonus: draw from p_K of the lowest live chain
-      tok = draw_law<DT, VEC>(P, S, ub[M]);
+      tok = draw_law<DT, VEC>(P, S, ub[M], b);
       n = K;
       break;
     }
@@ -385,7 +451,8 @@ __global__ __launch_bounds__(kMT, 1) void k_multi(const Params P) {
         break;
       }
       // rejected: the mass the remainder keeps, then the remainder is the law
-      const float z = remainder_mass<DT, VEC>(P, S);
+      const float z = remainder_mass<DT, VEC>(P, S, b, g);
+      if (S.to) break;
       if (tid == 0 && z > 0.f) {
         // a mass that rounds to zero keeps the current law
         S.q[S.nrej] = S.xq;
@@ -395,36 +462,64 @@ __global__ __launch_bounds__(kMT, 1) void k_multi(const Params P) {
       }
       __syncthreads();
     }
-    if (code != 0) break;
+    if (code != 0 || S.to) break;
     if (accepted < 0) {
-      tok = draw_law<DT, VEC>(P, S, ub[M]);
+      tok = draw_law<DT, VEC>(P, S, ub[M], b);
       n = j;
       break;
     }
     // the accepted token; the chains that proposed it stay alive
     const int t = P.tokens[((size_t)b * M + accepted) * K + j];
-    if (tid == 0) pub_i(P.out_tokens + t_out + j, t);
+    if (tid == 0 && g == 0) pub_i(P.out_tokens + t_out + j, t);
     int keep = 0;
     for (int m = 0; m < M; ++m)
       if ((live & (1 << m)) && P.tokens[((size_t)b * M + m) * K + j] == t) keep |= 1 << m;
     live = keep;
     __syncthreads();
   }
-  // outputs: the prefix was written as it was accepted; the drawn token, the
-  // padding, n and the chain holding the prefix
-  if (code != 0) {
-    for (int k = tid; k <= K; k += kMT) P.out_tokens[t_out + k] = -1;
-    if (tid == 0) {
-      P.num_accepted[b] = code;
-      if (P.out_chain) P.out_chain[b] = -1;
-    }
-  } else {
-    for (int k = tid + n; k <= K; k += kMT) P.out_tokens[t_out + k] = k == n ? tok : -1;
-    if (tid == 0) {
-      P.num_accepted[b] = n;
-      if (P.out_chain) P.out_chain[b] = lead;
+  // outputs: block 0 wrote the prefix as it was accepted and writes the
+  // padding, n and the chain holding the prefix; the block whose tiles held
+  // the draw's crossing writes the drawn token
+  const bool timed = S.to != 0;
+  if (!timed) {
+    if (code != 0) {
+      if (g == 0) {
+        for (int k = tid; k <= K; k += kMT) P.out_tokens[t_out + k] = -1;
+        if (tid == 0) {
+          P.num_accepted[b] = code;
+          if (P.out_chain) P.out_chain[b] = -1;
+        }
+      }
+    } else {
+      if (g == 0) {
+        for (int k = tid + n + 1; k <= K; k += kMT) P.out_tokens[t_out + k] = -1;
+        if (tid == 0) {
+          P.num_accepted[b] = n;
+          if (P.out_chain) P.out_chain[b] = lead;
+        }
+      }
+      if (tok >= 0 && tid == 0) P.out_tokens[t_out + n] = tok;
     }
   }
+  // Every block counts itself done; the last one reports a timed-out wait of
+  // any of them and returns the sequence's workspace entries to zero.
+  int* sy = msync_of(P, b);
+  if (timed && tid == 0) raise_flag(sy + 2, 1);
+  drain_stores();
+  __syncthreads();
+  if (tid == 0) s_last = bump(sy + 1) == kMultiSplit - 1;
+  __syncthreads();
+  if (!s_last) return;
+  if (obs_i(sy + 2) != 0) {
+    for (int k = tid; k <= K; k += kMT) P.out_tokens[t_out + k] = -1;
+    if (tid == 0) {
+      P.num_accepted[b] = SV_SEQ_SYNC_TIMEOUT;
+      if (P.out_chain) P.out_chain[b] = -1;
+    }
+  }
+  for (int k = tid; k < kMultiSyncWords; k += kMT) pub_i(sy + k, 0);
+  const int T = (P.nvec + kMTile - 1) / kMTile;
+  for (int t = tid; t < T; t += kMT) pub_f(P.mtiles + (size_t)b * P.mtiles_stride + t, 0.f);
   // the statistics pass's partials of this sequence's rows back to zero
   const int C = P.chunks;
   const long long d_units = (long long)M * K * C, t_units = (long long)M * (K + 1) * C;
@@ -439,7 +534,7 @@ __global__ __launch_bounds__(kMT, 1) void k_multi(const Params P) {
 }  // namespace
 
 hipError_t launch_multi(int dtype, bool vec, const Params& P, hipStream_t s) {
-  const dim3 grid((unsigned)(P.B / P.M)), block(kMT);
+  const dim3 grid((unsigned)(P.B / P.M * kMultiSplit)), block(kMT);
   switch (dtype) {
     case SV_F32:
       if (vec) hipLaunchKernelGGL((k_multi<SV_F32, true>), grid, block, 0, s, P);

@@ -199,6 +199,12 @@ def test_multi_host_checks(L):
     assert mc(target=None) == -1 and mc(uniforms=None) == -1 and mc(tokens=None) == -1
     assert mc(K=0, tokens=None, draft=None) == -3
     assert mc(B=0, draft=None, target=None, tokens=None, uniforms=None, out=None, num=None) == 0
-    assert L.spec_verify_multi_workspace_bytes(4, 3, 4, 1024) == \
-        L.spec_verify_workspace_bytes(12, 48, 1024, 0, 1.0)
+    # the logit path's workspace for the B*M chains, then the walk's state: a
+    # 16-word sync record and the tile totals (tiles of 1024 vectors) per sequence
+    up = lambda x: (x + 255) // 256 * 256
+    for B, V in ((4, 1024), (3, 128256), (2, 5)):
+        tiles = (min(V, 1 << 18) + 1023) // 1024
+        assert L.spec_verify_multi_workspace_bytes(B, 3, 4, V) == \
+            L.spec_verify_workspace_bytes(3 * B, 12 * B, V, 0, 1.0) + up(B * 16 * 4) + \
+            up(B * tiles * 4)
     assert L.spec_verify_multi_workspace_bytes(4, 5, 4, 1024) == 0

@@ -103,3 +103,43 @@ def test_multi_invalid_inputs():
     w["target"], w["draft"] = t, d
     ora, out, num = _check(w, toks, "invalid")
     assert list(ora["num_accepted"][1:4]) == [-1, -2, -2]
+
+
+def test_multi_workspace_returns_to_zero_and_many_sequences():
+    """The walk runs four blocks per sequence that exchange their pass sums and
+    tile totals through the workspace; the last block of each sequence returns
+    those entries (and the statistics partials) to zero. 300 sequences give
+    1200 walk blocks, more than the chip holds at once (one per compute unit),
+    so later sequences start as earlier ones finish. Two calls on one
+    workspace, then every byte of it must read zero."""
+    import speculative_decoding_verification_13_amd as sv
+    w = W.make_multi(B=300, M=2, K=2, V=2048, dtype="bf16", temperature=1.0, seed=3030)
+    toks = _tokens(w)
+    B, M, K, V = w["B"], w["M"], w["K"], w["V"]
+    dev = "cuda"
+    nbytes = int(sv.lib().spec_verify_multi_workspace_bytes(B, M, K, V))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    args = (w["draft"].to(dev), w["target"].to(dev),
+            torch.from_numpy(np.ascontiguousarray(toks, np.int32)).to(dev),
+            torch.from_numpy(w["uniforms"]).to(dev), B, M, K, V, w["temperature"])
+    out1, num1, ch1 = sv.spec_verify_multi(*args, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(ws)) == 0
+    out2, num2, ch2 = sv.spec_verify_multi(*args, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(ws)) == 0
+    assert torch.equal(out1, out2) and torch.equal(num1, num2) and torch.equal(ch1, ch2)
+    ora = oracle.verify_multi(W.raw_numpy(w["draft"].reshape(-1, V)),
+                              W.raw_numpy(w["target"].reshape(-1, V)), toks, w["uniforms"], B=B,
+                              M=M, K=K, V=V, dtype=w["dtype"], temperature=w["temperature"])
+    out, num = out1.cpu().numpy().reshape(-1), num1.cpu().numpy()
+    near = 0
+    for b in range(B):
+        if ora["margin"][b] <= BAND:
+            near += 1
+            continue
+        sl = slice(b * (K + 1), (b + 1) * (K + 1))
+        assert num[b] == ora["num_accepted"][b], b
+        assert np.array_equal(out[sl], ora["out_tokens"][sl]), b
+    _say(f"[gpu] multi B={B}: workspace back to zero after two calls, near-threshold={near}")
+
