@@ -1030,19 +1030,28 @@ constexpr int kNucBins = 2048;
 constexpr double kNucScale = 1099511627776.0;  // 2^40
 constexpr float kNucTop = 16.0f;
 constexpr int kNucRing = 128;  // candidates a wave holds in LDS: twice a wave
+#ifndef SV_NUC_THREADS
+#define SV_NUC_THREADS 256
+#endif
+// Threads of a k_nucleus block (one block per row). The bin scan runs on the
+// first kNucScan of them.
+constexpr int kNucThreads = SV_NUC_THREADS;
+constexpr int kNucScan = 256;
+static_assert(kNucThreads % kWave == 0 && kNucThreads >= kNucScan && kNucBins % kNucScan == 0,
+              "whole waves, and the scan's threads take equal runs of bins");
 
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_nucleus(const Params P) {
+__global__ __launch_bounds__(kNucThreads) void k_nucleus(const Params P) {
   using Vc = Vec<DT, VEC>;
   constexpr int N = Vc::N;
   __shared__ unsigned long long s_hist[kNucBins];
-  __shared__ unsigned long long s_wave[kThreads / kWave];
+  __shared__ unsigned long long s_wave[kNucScan / kWave];
   __shared__ unsigned long long s_base;
   __shared__ int s_cu[kCuLds];
   __shared__ float s_stat[2];
   __shared__ unsigned s_kmin[2];
   __shared__ int s_bin;
-  __shared__ float s_ring[kThreads / kWave][kNucRing];
+  __shared__ float s_ring[kNucThreads / kWave][kNucRing];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int unit = blockIdx.x;
@@ -1092,7 +1101,7 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(const Params P) {
     if (lane == 0) s_kmin[tid / kWave] = hi;
   }
   __syncthreads();
-  for (int k = tid; k < C; k += kThreads) sl[k] = 0ull;
+  for (int k = tid; k < C; k += kNucThreads) sl[k] = 0ull;
   const float m = s_stat[0];
   const bool ok = __builtin_isfinite(m) && s_stat[1] > 0.f && __builtin_isfinite(s_stat[1]);
   const float R = ref_of(m, c);
@@ -1128,7 +1137,7 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(const Params P) {
     // bins of 2^s keys: the fewest that leave at most nb of them
     s = kLowBits;
     while ((span >> s) >= (unsigned)nb) ++s;
-    for (int x = tid; x < nb; x += kThreads) s_hist[x] = 0ull;
+    for (int x = tid; x < nb; x += kNucThreads) s_hist[x] = 0ull;
     __syncthreads();
     // A logit of the pass's key range: its mass in fixed point, into the bin
     // of its key. Keys below the range wrap past span. A mass below 2^-40
@@ -1170,12 +1179,15 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(const Params P) {
       // never overwrites one not yet added
       if (n - head >= (unsigned)kWave) drain64();
     };
+    // The row is streamed with non-temporal loads, as in the statistics pass
+    // (measured 60 against 64 us with ordinary loads at the headline shape).
     auto stream = [&](auto upper) {
       int vb = wv * kWave;  // the wave's first vector
-      for (; vb + kWave - 1 + (kBatch - 1) * kThreads < P.nvec; vb += kBatch * kThreads) {
+      for (; vb + kWave - 1 + (kBatch - 1) * kNucThreads < P.nvec; vb += kBatch * kNucThreads) {
         typename Vc::Raw r[kBatch];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) r[u] = Vc::load(base, roff, vb + lane + u * kThreads);
+        for (int u = 0; u < kBatch; ++u)
+          r[u] = Vc::load_stream(base, roff, vb + lane + u * kNucThreads);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
@@ -1185,11 +1197,11 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(const Params P) {
           for (int k = 0; k < N; ++k) stage(f[k], upper);
         }
       }
-      for (; vb < P.nvec; vb += kThreads) {
+      for (; vb < P.nvec; vb += kNucThreads) {
         const int v = vb + lane;
         float f[N];
         if (v < P.nvec) {
-          Vc::get(Vc::load(base, roff, v), f);
+          Vc::get(Vc::load_stream(base, roff, v), f);
         } else {
 #pragma unroll
           for (int k = 0; k < N; ++k) f[k] = __builtin_nanf("");
@@ -1203,36 +1215,41 @@ __global__ __launch_bounds__(kThreads) void k_nucleus(const Params P) {
     __builtin_amdgcn_wave_barrier();
     if (lane < (int)(n - head)) add(ring[(head + lane) & (kNucRing - 1)]);
     __syncthreads();
-    // thread t sums a run of bins in descending key order, then an exclusive
-    // scan over the threads gives the mass above each run
-    const int per = nb / kThreads;
+    // scan thread t sums a run of bins in descending key order, then an
+    // exclusive scan over those threads gives the mass above each run
+    const bool scanner = tid < kNucScan;
+    const int per = nb / kNucScan;
     const int top = nb - 1 - tid * per;
-    unsigned long long run = 0ull;
-    for (int k = 0; k < per; ++k) run += s_hist[top - k];
-    unsigned long long incl = run;
+    unsigned long long run = 0ull, incl = 0ull;
+    if (scanner) {
+      for (int k = 0; k < per; ++k) run += s_hist[top - k];
+      incl = run;
 #pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const unsigned long long y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
+      for (int o = 1; o < kWave; o <<= 1) {
+        const unsigned long long y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      if (lane == kWave - 1) s_wave[tid / kWave] = incl;
     }
-    if (lane == kWave - 1) s_wave[tid / kWave] = incl;
     if (tid == 0) s_bin = -1;
     __syncthreads();
     unsigned long long before = 0ull, total = 0ull;
-    for (int w = 0; w < kThreads / kWave; ++w) {
+    for (int w = 0; w < kNucScan / kWave; ++w) {
       if (w < tid / kWave) before += s_wave[w];
       total += s_wave[w];
     }
-    unsigned long long acc = above + before + (incl - run);
-    for (int k = 0; k < per; ++k) {
-      const unsigned long long h = s_hist[top - k];
-      // the strictly-larger mass acc is below the bound and the running mass
-      // reaches it in this bin: the last kept level lies here
-      if ((double)acc < bound && (double)(acc + h) >= bound) {
-        s_bin = top - k;
-        s_base = acc;
+    if (scanner) {
+      unsigned long long acc = above + before + (incl - run);
+      for (int k = 0; k < per; ++k) {
+        const unsigned long long h = s_hist[top - k];
+        // the strictly-larger mass acc is below the bound and the running mass
+        // reaches it in this bin: the last kept level lies here
+        if ((double)acc < bound && (double)(acc + h) >= bound) {
+          s_bin = top - k;
+          s_base = acc;
+        }
+        acc += h;
       }
-      acc += h;
     }
     __syncthreads();
     if (s_bin < 0) {
@@ -1650,8 +1667,8 @@ static hipError_t launch_t(const Params& P, const Plan& L, hipStream_t s, hipEve
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if ((err = stage_event(ev, nev, e++, s)) != hipSuccess) return err;
     if (P.nucleus)
-      hipLaunchKernelGGL((k_nucleus<DT, VEC>), dim3((unsigned)L.filter_blocks), dim3(kThreads), 0,
-                         s, P);
+      hipLaunchKernelGGL((k_nucleus<DT, VEC>), dim3((unsigned)L.filter_blocks), dim3(kNucThreads),
+                         0, s, P);
     else
       hipLaunchKernelGGL(k_filter<DT>, dim3((unsigned)L.filter_blocks), dim3(kThreads), 0, s, P);
     if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -1688,8 +1705,8 @@ static hipError_t launch_row_stats_t(const Params& P, const Plan& L, hipStream_t
                        0, s, P);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((k_nucleus<DT, VEC>), dim3((unsigned)L.filter_blocks), dim3(kThreads), 0, s,
-                       P);
+    hipLaunchKernelGGL((k_nucleus<DT, VEC>), dim3((unsigned)L.filter_blocks), dim3(kNucThreads), 0,
+                       s, P);
   } else if (P.filt) {
     hipLaunchKernelGGL((k_stats<DT, VEC, true>), dim3((unsigned)L.stats_blocks), dim3(kThreads), 0,
                        s, P);
