@@ -25,6 +25,17 @@ stay alive. Their next tokens are independent draws given that prefix, so
 the next position is checked the same way. The bonus position K draws from
 the lowest live chain's target row.
 
+Filters and greedy verification as for one chain (aihero.vn "Speculative
+decoding", section "Cùng phân bố không có nghĩa cùng chuỗi mỗi lần": the same
+temperature, top-k and top-p on both models' rows, and a greedy check):
+every row's law is its filtered distribution (R6), and the top-p margins of
+the rows a walk uses join its margin. With temperature 0 the target law is a
+point mass at the argmax (lowest id on ties), so the step above accepts a
+candidate exactly when it equals that argmax, and a rejection leaves the law
+unchanged: the first live chain whose token is the argmax is accepted, and
+when none is, the argmax is emitted (the bonus position emits it too). Only
+target rows are read then.
+
 Layout (per sequence): q_rows [M, K, V], p_rows [M, K+1, V], x [M, K]; the
 uniforms u [K+1, M+1]: u[j, m] tests chain m's candidate at position j,
 u[j, M] is the draw at j (taken only at the position where the walk stops).
@@ -38,11 +49,12 @@ import math
 import numpy as np
 
 from .verify import (ACCEPT_MARGIN_INF, accept_ratio, decode_logits, filtered_distribution,
-                     inverse_cdf, residual, row_is_valid)
+                     greedy_token, inverse_cdf, residual, row_is_valid)
 
 
-def verify_multi_sequence(q_rows, p_rows, x, u, temperature):
-    """One sequence with M candidate chains (see the module docstring).
+def verify_multi_sequence(q_rows, p_rows, x, u, temperature, top_k=0, top_p=1.0):
+    """One sequence with M candidate chains (see the module docstring);
+    temperature 0 verifies greedily.
 
     Returns dict(tokens (K+1, -1 padded), n, chosen [K+1] (the chain whose
     candidate was accepted at each position, -1 where the token was drawn or
@@ -61,11 +73,23 @@ def verify_multi_sequence(q_rows, p_rows, x, u, temperature):
         return res
     margin = ACCEPT_MARGIN_INF
     live = list(range(M))
+    greedy = temperature == 0.0
     for j in range(K + 1):
         lead = live[0]
         if not row_is_valid(p_rows[lead, j]):
             return dict(res, n=-2, tokens=[-1] * (K + 1), chosen=[-1] * (K + 1))
-        r = filtered_distribution(p_rows[lead, j], temperature)[0]
+        if greedy:
+            a = greedy_token(p_rows[lead, j])
+            tokens[j] = a
+            accepted = None if j == K else next((m for m in live if int(x[m, j]) == a), None)
+            if accepted is None:
+                res.update(n=j, chain=lead)
+                return res
+            chosen[j] = accepted
+            live = [m for m in live if int(x[m, j]) == a]
+            continue
+        r, _, mp = filtered_distribution(p_rows[lead, j], temperature, top_k, top_p)
+        margin = min(margin, mp)
         if j == K:
             t, _, m_ = inverse_cdf(r, float(u[K][M]))
             tokens[K] = t
@@ -75,9 +99,9 @@ def verify_multi_sequence(q_rows, p_rows, x, u, temperature):
         for m in live:
             if not row_is_valid(q_rows[m, j]):
                 return dict(res, n=-2, tokens=[-1] * (K + 1), chosen=[-1] * (K + 1))
-            q = filtered_distribution(q_rows[m, j], temperature)[0]
+            q, _, mq = filtered_distribution(q_rows[m, j], temperature, top_k, top_p)
             ratio = accept_ratio(r, q, int(x[m, j]))
-            margin = min(margin, abs(float(u[j][m]) - ratio))
+            margin = min(margin, mq, abs(float(u[j][m]) - ratio))
             if float(u[j][m]) < ratio:
                 accepted = m
                 break
@@ -97,14 +121,19 @@ def verify_multi_sequence(q_rows, p_rows, x, u, temperature):
     raise AssertionError("the bonus position always ends the walk")
 
 
-def verify_multi(draft, target, draft_tokens, uniforms, *, B, M, K, V, dtype, temperature):
+def verify_multi(draft, target, draft_tokens, uniforms, *, B, M, K, V, dtype, temperature,
+                 top_k=0, top_p=1.0):
     """Batch driver: draft [B, M, K, V], target [B, M, K+1, V] storage arrays,
-    draft_tokens [B, M, K], uniforms [B, K+1, M+1] (float32 values).
-    Returns dict(out_tokens [B*(K+1)] int32, num_accepted [B] int32, chain [B]
-    int32, chosen [B*(K+1)] int32, margin [B] float64)."""
-    if not (temperature > 0.0) or math.isinf(temperature):
-        raise ValueError("several chains are verified by sampling: temperature > 0")
-    d = decode_logits(np.asarray(draft), dtype).reshape(B, M, K, V)
+    draft_tokens [B, M, K], uniforms [B, K+1, M+1] (float32 values);
+    temperature 0 verifies greedily (the draft rows are not read, draft may be
+    None). Returns dict(out_tokens [B*(K+1)] int32, num_accepted [B] int32,
+    chain [B] int32, chosen [B*(K+1)] int32, margin [B] float64)."""
+    if not (temperature >= 0.0) or math.isinf(temperature):
+        raise ValueError("temperature must be finite and >= 0")
+    if temperature == 0.0 and draft is None:
+        d = np.zeros((B, M, K, V))
+    else:
+        d = decode_logits(np.asarray(draft), dtype).reshape(B, M, K, V)
     t = decode_logits(np.asarray(target), dtype).reshape(B, M, K + 1, V)
     x = np.asarray(draft_tokens).reshape(B, M, K)
     u = np.asarray(uniforms, np.float32).astype(np.float64).reshape(B, K + 1, M + 1)
@@ -114,7 +143,7 @@ def verify_multi(draft, target, draft_tokens, uniforms, *, B, M, K, V, dtype, te
     chain = np.zeros(B, np.int32)
     margin = np.full(B, ACCEPT_MARGIN_INF)
     for b in range(B):
-        r = verify_multi_sequence(d[b], t[b], x[b], u[b], temperature)
+        r = verify_multi_sequence(d[b], t[b], x[b], u[b], temperature, top_k, top_p)
         out[b * (K + 1):(b + 1) * (K + 1)] = r["tokens"]
         chosen[b * (K + 1):(b + 1) * (K + 1)] = r["chosen"]
         num[b] = r["n"]

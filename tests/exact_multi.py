@@ -11,7 +11,7 @@ import oracle
 from exact_paths import step_measure, threshold
 
 
-def enumerate_multi(q_rows, p_rows, x, T):
+def enumerate_multi(q_rows, p_rows, x, T, top_k=0, top_p=1.0):
     """Outcomes for fixed candidate tokens x [M, K]: a list of
     (probability, n, accepted prefix (list), law of the token at position n)."""
     M, K = x.shape
@@ -19,7 +19,7 @@ def enumerate_multi(q_rows, p_rows, x, T):
     out = []
 
     def run(u):
-        return oracle.verify_multi_sequence(q_rows, p_rows, x, u, T)
+        return oracle.verify_multi_sequence(q_rows, p_rows, x, u, T, top_k, top_p)
 
     def rec(u, j, live, weight, prefix):
         if j == K:

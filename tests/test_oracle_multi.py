@@ -11,7 +11,11 @@
 - Exact enumeration on random small trees: the token emitted at position 0
   follows p_0, and the token at position 1, given that position 0 emitted t,
   follows the target row after the prefix t ([P1] s.6: the result follows
-  the target).
+  the target). With top-k / top-p the same holds for the filtered target
+  rows, candidates drawn from the filtered draft rows.
+- With filters, and greedily (temperature 0), one chain is again the
+  single-draft verification; a greedy hand example with several chains and a
+  tied argmax (lowest id).
 """
 
 import itertools
@@ -111,3 +115,101 @@ def test_tree_outputs_follow_target_rows(M, K, V, seed):
     for t in range(V):
         if reach1[t] > 1e-6:
             assert law1[t] / reach1[t] == pytest.approx(softmax(prow((t,)) / T), abs=1e-8), t
+
+
+@pytest.mark.parametrize("top_k,top_p,T", [(5, 1.0, 0.9), (0, 0.7, 0.9), (8, 0.8, 1.3),
+                                           (0, 1.0, 0.0), (5, 0.7, 0.0)])
+def test_one_chain_is_single_draft_verification_filtered_and_greedy(top_k, top_p, T):
+    rng = np.random.default_rng([12, top_k, int(top_p * 10), int(T * 10)])
+    K, V = 4, 40
+    for trial in range(40):
+        q = rng.normal(0, 2, (K, V))
+        p = np.concatenate([q, rng.normal(0, 2, (1, V))]) + rng.normal(0, 1.0, (K + 1, V))
+        if T == 0.0:
+            # greedy drafts: often the target's argmax too, so some prefixes pass
+            x = np.array([int(np.argmax(p[i] if rng.random() < 0.6 else q[i])) for i in range(K)])
+        else:
+            x = rng.integers(0, V, K)
+        u1 = rng.random(K + 1)
+        single = oracle.verify_sequence(q, p, x, u1, T, top_k, top_p, greedy=T == 0.0)
+        um = np.stack([u1[:K + 1], np.full(K + 1, u1[K])], axis=1)  # [K+1, 2]
+        multi = oracle.verify_multi_sequence(q[None], p[None], x[None], um, T, top_k, top_p)
+        assert multi["n"] == single["n"] and multi["tokens"] == single["tokens"], trial
+        if T > 0.0:
+            assert multi["margin"] == pytest.approx(single["margin"], abs=1e-12), trial
+
+
+def test_greedy_several_chains_hand_example():
+    V, K = 6, 2
+    p = np.full((3, K + 1, V), -5.0)
+    p[:, 0, 4] = 2.0           # position 0: argmax 4
+    p[:, 1, 1] = 3.0           # position 1 after the prefix [4]: ids 1 and 3 tie, lowest id 1
+    p[:, 1, 3] = 3.0
+    p[:, 2, 5] = 1.0           # bonus: argmax 5
+    q = np.zeros((3, K, V))
+    u = np.full((K + 1, 4), 0.5)
+    # chains 0 and 2 propose 4 then 1, chain 1 proposes 2: chain 0 accepted twice, then bonus 5
+    res = oracle.verify_multi_sequence(q, p, np.array([[4, 1], [2, 2], [4, 1]]), u, 0.0)
+    assert res["n"] == 2 and res["tokens"] == [4, 1, 5] and res["chosen"] == [0, 0, -1]
+    assert res["chain"] == 0
+    # only chain 1 proposes the argmax at position 0, then 3 (tied, not the lowest id)
+    res = oracle.verify_multi_sequence(q, p, np.array([[0, 1], [4, 3], [2, 1]]), u, 0.0)
+    assert res["n"] == 1 and res["tokens"] == [4, 1, -1] and res["chosen"] == [1, -1, -1]
+    assert res["chain"] == 1
+    # no chain proposes the argmax: the argmax is emitted at position 0
+    res = oracle.verify_multi_sequence(q, p, np.array([[0, 1], [2, 3], [3, 1]]), u, 0.0)
+    assert res["n"] == 0 and res["tokens"] == [4, -1, -1] and res["chain"] == 0
+    # a NaN target row on the path is an invalid row; draft rows are not read
+    p2 = p.copy()
+    p2[0, 1, 2] = np.nan
+    qn = np.full((3, K, V), np.nan)
+    res = oracle.verify_multi_sequence(qn, p2, np.array([[4, 1], [2, 2], [4, 1]]), u, 0.0)
+    assert res["n"] == -2
+
+
+@pytest.mark.parametrize("M,K,V,top_k,top_p,seed", [(2, 1, 5, 3, 1.0, 0), (2, 1, 5, 0, 0.75, 1),
+                                                   (2, 2, 4, 3, 0.8, 2)])
+def test_tree_outputs_follow_filtered_target_rows(M, K, V, top_k, top_p, seed):
+    rng = np.random.default_rng([32, seed])
+    T = 0.9
+    qfun, pfun = {}, {}
+
+    def qrow(m, prefix):
+        return qfun.setdefault((m, prefix), rng.normal(0, 1.5, V))
+
+    def prow(prefix):
+        return pfun.setdefault(prefix, rng.normal(0, 1.5, V))
+
+    def filt(row):
+        return oracle.filtered_distribution(row, T, top_k, top_p)[0]
+
+    law0 = np.zeros(V)
+    law1 = {t: np.zeros(V) for t in range(V)}
+    reach1 = np.zeros(V)
+    total = 0.0
+    for flat in itertools.product(range(V), repeat=M * K):
+        x = np.array(flat).reshape(M, K)
+        qrows = np.stack([[qrow(m, tuple(x[m, :j])) for j in range(K)] for m in range(M)])
+        prows = np.stack([[prow(tuple(x[m, :j])) for j in range(K + 1)] for m in range(M)])
+        w = 1.0
+        for m in range(M):
+            for j in range(K):
+                w *= filt(qrows[m, j])[x[m, j]]
+        if w == 0.0:
+            continue  # a draft outside its drafter's kept set is never proposed
+        total += w
+        for prob, n, prefix, dist in enumerate_multi(qrows, prows, x, T, top_k, top_p):
+            pw = w * prob
+            if n == 0:
+                law0 += pw * dist
+                continue
+            t = prefix[0]
+            law0[t] += pw
+            reach1[t] += pw
+            law1[t] += pw * (dist if n == 1 else np.eye(V)[prefix[1]])
+    assert total == pytest.approx(1.0, abs=1e-12)
+    assert law0 == pytest.approx(filt(prow(())), abs=1e-9)
+    for t in range(V):
+        if reach1[t] > 1e-6:
+            assert law1[t] / reach1[t] == pytest.approx(filt(prow((t,))), abs=1e-8), t
+
