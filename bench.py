@@ -693,7 +693,7 @@ def bench_multi(args, sv):
     uni_d = torch.from_numpy(w["uniforms"]).to(dev)
     sets = [(draft0, target0)] + [(draft0.clone(), target0.clone())
                                   for _ in range(max(1, args.sets) - 1)]
-    n = int(sv.lib().spec_verify_multi_workspace_bytes(B, M, K, V))
+    n = int(sv.lib().spec_verify_multi_workspace_bytes(B, M, K, V, 0, 1.0))
     ws = sv._lib._zeroed_workspace(max(n, 256), dev)
     out = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
     num = torch.empty(B, dtype=torch.int32, device=dev)

@@ -296,7 +296,13 @@ int spec_verify_accept_stats(const void* draft_logits, const void* target_logits
  * then each remainder). An accepted token keeps alive the chains that
  * proposed it. When every candidate is rejected the token is drawn from the
  * last remainder, by inverse CDF over ascending ids (the bonus position K
- * draws from p_K). Sampling only, no top-k / top-p.
+ * draws from p_K). top_k / top_p filter every row as in spec_verify (each
+ * law is the row's kept-set distribution; aihero.vn "Speculative decoding",
+ * section "Cùng phân bố không có nghĩa cùng chuỗi mỗi lần"). temperature 0
+ * verifies greedily: the first live chain whose token is the argmax of p_j
+ * (lowest id on ties) is accepted, and when none is the argmax is emitted
+ * (the limit of the rule above when p_j is a point mass); draft rows and
+ * uniforms are not read then (draft_logits and uniforms may be NULL).
  *   draft_logits  [B, M, K, V]     target_logits [B, M, K+1, V]
  *   draft_tokens  int32 [B, M, K]
  *   uniforms      float [B, K+1, M+1]: [b, j, m] tests chain m's candidate at
@@ -309,7 +315,8 @@ int spec_verify_accept_stats(const void* draft_logits, const void* target_logits
  *                 the sequence ran out; then fill the workspace with zeros again)
  *   out_chain     int32 [B] or NULL: the lowest chain holding the emitted
  *                 prefix (the cache to keep), -1 with an error code
- * 1 <= M <= SV_MAX_CHAINS, 0 <= K <= SV_MAX_K, temperature finite and > 0,
+ * 1 <= M <= SV_MAX_CHAINS, 0 <= K <= SV_MAX_K, temperature finite and >= 0,
+ * top_k and top_p with the meaning and limits of spec_verify,
  * rows of at most 2^18 vectors (16-byte vectors when V * element size is a
  * multiple of 16 and both arrays are 16-byte aligned, else elements; longer
  * rows return SV_EUNSUPPORTED). The
@@ -321,12 +328,12 @@ int spec_verify_accept_stats(const void* draft_logits, const void* target_logits
  * wait for each other, so, as for spec_verify, the call assumes no other
  * kernel holds the device's compute units meanwhile; a wait that runs out
  * gives SV_SEQ_SYNC_TIMEOUT instead of a hang. */
-size_t spec_verify_multi_workspace_bytes(int B, int M, int K, int V);
+size_t spec_verify_multi_workspace_bytes(int B, int M, int K, int V, int top_k, float top_p);
 int spec_verify_multi(const void* draft_logits, const void* target_logits,
                       const int32_t* draft_tokens, const float* uniforms, int B, int M, int K,
-                      int V, float temperature, sv_dtype dtype, int32_t* out_tokens,
-                      int32_t* num_accepted, int32_t* out_chain, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream);
+                      int V, float temperature, int top_k, float top_p, sv_dtype dtype,
+                      int32_t* out_tokens, int32_t* num_accepted, int32_t* out_chain,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Verification from LM-head hidden states: the same step as spec_verify, with
  * the logit rows formed inside the library as l = h W^T on the matrix cores

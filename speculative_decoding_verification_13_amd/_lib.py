@@ -54,8 +54,9 @@ SIGNATURES = {
                               _P, _S, _P, ctypes.POINTER(SvDiag)]),
     "spec_verify_accept_stats": (_I, [_P, _P, _P, _I, _I, _I, _F, _I, _F, _I, _P, _P, _P, _S,
                                       _P]),
-    "spec_verify_multi_workspace_bytes": (_S, [_I, _I, _I, _I]),
-    "spec_verify_multi": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _S, _P]),
+    "spec_verify_multi_workspace_bytes": (_S, [_I, _I, _I, _I, _I, _F]),
+    "spec_verify_multi": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _F, _I, _P, _P, _P, _P, _S,
+                               _P]),
     "spec_verify_lmhead_workspace_bytes": (_S, [_I, _I, _I]),
     "spec_verify_lmhead_zero_bytes": (_S, [_I, _I, _I]),
     "spec_verify_lmhead": (_I, [_P, _P, _I, _P, _P, _I, _P, _P, _I, _I, _I, _F, _P, _P, _P, _S,
@@ -347,17 +348,19 @@ def spec_verify_accept_stats(draft_logits, target_logits, cu_draft, B, V, temper
 
 
 def spec_verify_multi(draft_logits, target_logits, draft_tokens, uniforms, B, M, K, V,
-                      temperature, *, out_tokens=None, num_accepted=None, out_chain=None,
-                      workspace=None):
+                      temperature, top_k=0, top_p=1.0, *, out_tokens=None, num_accepted=None,
+                      out_chain=None, workspace=None):
     """Several draft chains per sequence (see include/spec_verify.h): draft
     [B, M, K, V], target [B, M, K+1, V], draft_tokens int32 [B, M, K], uniforms
-    float32 [B, K+1, M+1]. Returns (out_tokens [B, K+1], num_accepted [B],
+    float32 [B, K+1, M+1]; temperature 0 verifies greedily (draft_logits and
+    uniforms may be None). Returns (out_tokens [B, K+1], num_accepted [B],
     out_chain [B]), int32 on the device."""
     B, M, K, V = int(B), int(M), int(K), int(V)
+    greedy = float(temperature) == 0.0
     dev = target_logits.device
-    _check_logits(draft_logits, target_logits, B * M * K, B * M * (K + 1), V, K > 0)
+    _check_logits(draft_logits, target_logits, B * M * K, B * M * (K + 1), V, K > 0 and not greedy)
     _expect(draft_tokens, "draft_tokens", torch.int32, B * M * K, allow_none=K == 0)
-    _expect(uniforms, "uniforms", torch.float32, B * (K + 1) * (M + 1))
+    _expect(uniforms, "uniforms", torch.float32, B * (K + 1) * (M + 1), allow_none=greedy)
     if out_tokens is None:
         out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
     if num_accepted is None:
@@ -368,14 +371,15 @@ def spec_verify_multi(draft_logits, target_logits, draft_tokens, uniforms, B, M,
     _expect(num_accepted, "num_accepted", torch.int32, B)
     _expect(out_chain, "out_chain", torch.int32, B)
     if workspace is None:
-        n = int(lib().spec_verify_multi_workspace_bytes(B, M, K, V))
+        n = int(lib().spec_verify_multi_workspace_bytes(B, M, K, V, int(top_k), float(top_p)))
         if n == 0 and B > 0:
             raise ValueError("invalid sizes for a workspace")
         workspace = _zeroed_workspace(max(n, 256), dev)
     _check(lib().spec_verify_multi(
         _ptr(draft_logits), _ptr(target_logits), _ptr(draft_tokens), _ptr(uniforms), B, M, K, V,
-        float(temperature), _dtype_code(target_logits), _ptr(out_tokens), _ptr(num_accepted),
-        _ptr(out_chain), _ptr(workspace), _nbytes(workspace), _stream(dev)))
+        float(temperature), int(top_k), float(top_p), _dtype_code(target_logits),
+        _ptr(out_tokens), _ptr(num_accepted), _ptr(out_chain), _ptr(workspace),
+        _nbytes(workspace), _stream(dev)))
     return out_tokens, num_accepted, out_chain
 
 

@@ -442,20 +442,28 @@ bool multi_sizes(int B, int M, int K, int V, long long& seqs, long long& drafts)
 }
 
 int run_multi(const void* draft, const void* target, const int32_t* tokens, const float* uniforms,
-              int B, int M, int K, int V, float temperature, int dtype, int32_t* out_tokens,
-              int32_t* num_accepted, int32_t* out_chain, void* workspace, size_t workspace_bytes,
-              hipStream_t stream) {
+              int B, int M, int K, int V, float temperature, int top_k, float top_p, int dtype,
+              int32_t* out_tokens, int32_t* num_accepted, int32_t* out_chain, void* workspace,
+              size_t workspace_bytes, hipStream_t stream) {
   if (dtype != SV_F32 && dtype != SV_F16 && dtype != SV_BF16) return SV_EDTYPE;
   long long seqs, drafts;
   if (!multi_sizes(B, M, K, V, seqs, drafts)) return SV_EINVAL;
-  if (!(temperature > 0.0f) || isinf(temperature)) return SV_EINVAL;
+  if (!(temperature >= 0.0f) || isinf(temperature)) return SV_EINVAL;
+  if (!(top_p > 0.0f && top_p <= 1.0f)) return SV_EINVAL;
   if (B == 0) return SV_OK;
-  if (target == nullptr || uniforms == nullptr || out_tokens == nullptr ||
-      num_accepted == nullptr)
-    return SV_EINVAL;
-  if (K > 0 && (draft == nullptr || tokens == nullptr)) return SV_EINVAL;
+  const bool all_greedy = temperature == 0.0f;
+  if (target == nullptr || out_tokens == nullptr || num_accepted == nullptr) return SV_EINVAL;
+  if (!all_greedy && uniforms == nullptr) return SV_EINVAL;
+  if (K > 0 && (tokens == nullptr || (!all_greedy && draft == nullptr))) return SV_EINVAL;
+  // filters as for one chain: top-k (then top-p) through candidate records and
+  // the per-row cut, top-p alone through the nucleus pass
+  const bool filt = !all_greedy && filters_active(V, top_k, top_p);
+  const bool topk = filt && topk_active(V, top_k);
+  if (topk && top_k > SV_MAX_TOP_K) return SV_EUNSUPPORTED;
+  const int pk = topk ? top_k : 0;
+  const float pp = filt ? top_p : 1.0f;
   sv::Plan L;
-  if (!make_plan((int)seqs, (int)drafts, V, 0, 1.0f, SIZE_MAX, L)) return SV_EUNSUPPORTED;
+  if (!make_plan((int)seqs, (int)drafts, V, pk, pp, SIZE_MAX, L)) return SV_EUNSUPPORTED;
   if (workspace == nullptr || ((uintptr_t)workspace % kAlign) != 0 ||
       L.total_bytes + multi_state_bytes(B, V) > workspace_bytes)
     return SV_EWORKSPACE;
@@ -472,12 +480,26 @@ int run_multi(const void* draft, const void* target, const int32_t* tokens, cons
   P.V = V;
   P.total_draft = (int)drafts;
   P.rows = (int)(seqs * (K + 1));
-  P.c = (float)(1.4426950408889634074 / (double)temperature);
+  P.all_greedy = all_greedy ? 1 : 0;
+  P.c = all_greedy ? 0.0f : (float)(1.4426950408889634074 / (double)temperature);
   P.nvec = vec ? V / (16 / es) : V;
   if (P.nvec > sv::kMultiMaxVecs) return SV_EUNSUPPORTED;  // the walk's tile sums
-  P.chunk_vecs = (int)chunk_vecs_for(P.nvec, sv::kChunkSteps);
+  P.chunk_vecs = topk ? sv::kFiltChunkVecs : (int)chunk_vecs_for(P.nvec, sv::kChunkSteps);
   P.chunks = (P.nvec + P.chunk_vecs - 1) / P.chunk_vecs;
   if (P.chunks > L.cmax) return SV_EUNSUPPORTED;
+  P.stats_block0 = all_greedy ? (long long)P.total_draft * P.chunks : 0;  // no draft rows read
+  P.filt = filt ? 1 : 0;
+  P.nucleus = (filt && !topk) ? 1 : 0;
+  P.top_k = top_k;
+  P.top_p = top_p;
+  P.kcap = topk ? kcap_for(top_k) : 0;
+  P.rec_words = sv::kRecHeader + 2 * P.kcap;
+  P.rec = topk ? reinterpret_cast<unsigned*>(reinterpret_cast<char*>(workspace) + L.off_rec)
+               : nullptr;
+  P.rowres = filt ? reinterpret_cast<sv::RowRes*>(reinterpret_cast<char*>(workspace) +
+                                                  L.off_rowres)
+                  : nullptr;
+  P.kept = nullptr;  // the walk lists no kept sets
   P.out_tokens = out_tokens;
   P.num_accepted = num_accepted;
   P.slots = reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(workspace) + L.off_slots);
@@ -490,8 +512,8 @@ int run_multi(const void* draft, const void* target, const int32_t* tokens, cons
   P.mtiles_stride = multi_tiles(V);
   L.chunks = P.chunks;
   L.chunk_vecs = P.chunk_vecs;
-  L.stats_blocks = ((long long)P.total_draft + P.rows) * P.chunks;
-  L.filter_blocks = 0;
+  L.stats_blocks = ((long long)P.total_draft + P.rows) * P.chunks - P.stats_block0;
+  L.filter_blocks = filt ? (long long)P.total_draft + P.rows : 0;
   P.stats_blocks = L.stats_blocks;
   if (L.stats_blocks > (long long)INT_MAX / sv::kThreads) return SV_EUNSUPPORTED;
   if (sv::launch_row_stats(dtype, vec, P, L, stream) != hipSuccess) return SV_EHIP;
@@ -502,22 +524,24 @@ int run_multi(const void* draft, const void* target, const int32_t* tokens, cons
 
 extern "C" {
 
-size_t spec_verify_multi_workspace_bytes(int B, int M, int K, int V) {
+size_t spec_verify_multi_workspace_bytes(int B, int M, int K, int V, int top_k, float top_p) {
   long long seqs, drafts;
   if (!multi_sizes(B, M, K, V, seqs, drafts)) return 0;
+  if (!(top_p > 0.0f && top_p <= 1.0f)) return 0;
+  const bool topk = topk_active(V, top_k) && top_k <= SV_MAX_TOP_K;
   sv::Plan L;
-  if (!make_plan((int)seqs, (int)drafts, V, 0, 1.0f, SIZE_MAX, L)) return 0;
+  if (!make_plan((int)seqs, (int)drafts, V, topk ? top_k : 0, top_p, SIZE_MAX, L)) return 0;
   return L.total_bytes + multi_state_bytes(B, V);
 }
 
 int spec_verify_multi(const void* draft_logits, const void* target_logits,
                       const int32_t* draft_tokens, const float* uniforms, int B, int M, int K,
-                      int V, float temperature, sv_dtype dtype, int32_t* out_tokens,
-                      int32_t* num_accepted, int32_t* out_chain, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
+                      int V, float temperature, int top_k, float top_p, sv_dtype dtype,
+                      int32_t* out_tokens, int32_t* num_accepted, int32_t* out_chain,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return run_multi(draft_logits, target_logits, draft_tokens, uniforms, B, M, K, V, temperature,
-                   (int)dtype, out_tokens, num_accepted, out_chain, workspace, workspace_bytes,
-                   stream);
+                   top_k, top_p, (int)dtype, out_tokens, num_accepted, out_chain, workspace,
+                   workspace_bytes, stream);
 }
 
 const char* spec_verify_strerror(int code) {

@@ -46,12 +46,28 @@ constexpr int kMultiMaxTiles = kMultiMaxVecs / kMTile;  // tiles a row may have
 __host__ __device__ constexpr int multi_batch(int R) { return R <= 1 ? 8 : (R == 2 ? 4 : 2); }
 
 struct RowS {
-  float R, iS;  // reference R = fp32(max*c) and 1/S of the row's sum of 2^(l*c - R)
+  float R, iS;  // reference R = fp32(max*c) and 1/S of the row's (kept) sum of 2^(l*c - R)
+  float thr;    // kept set: l >= thr (-inf without filters)
   int ok;       // the row holds no NaN or +inf and some finite value
 };
 
-// Merged statistics of one row from its chunk partials, in chunk order.
+// Probability of logit l in a row: 2^(l*c - R) / S inside its kept set, 0 outside.
+__device__ __forceinline__ float prob_of(float l, const RowS& r, float c) {
+  return l >= r.thr ? fast_exp2(fmaf(l, c, -r.R)) * r.iS : 0.f;
+}
+
+// Statistics of one row: with filters the kept-set maximum, sum and threshold
+// of the cut pass; otherwise its chunk partials merged in chunk order.
 __device__ RowS merged_row(const Params& P, long long unit) {
+  RowS r;
+  if (P.filt) {
+    const RowRes rr = P.rowres[unit];
+    r.ok = rr.flags == 0 && __builtin_isfinite(rr.m) && rr.s > 0.f && __builtin_isfinite(rr.s);
+    r.R = ref_of(rr.m, P.c);
+    r.iS = 1.0f / rr.s;
+    r.thr = rr.theta;
+    return r;
+  }
   float m = kNegInf, s = 0.f;
   const unsigned long long* sl = P.slots + unit * P.chunks;
   for (int k = 0; k < P.chunks; ++k) {
@@ -59,10 +75,10 @@ __device__ RowS merged_row(const Params& P, long long unit) {
     unpack_ms(sl[k], om, os);
     merge_ms(m, s, om, os, P.c);
   }
-  RowS r;
   r.ok = __builtin_isfinite(m) && s > 0.f && __builtin_isfinite(s);
   r.R = ref_of(m, P.c);
   r.iS = 1.0f / s;
+  r.thr = kNegInf;
   return r;
 }
 
@@ -172,22 +188,22 @@ __device__ __forceinline__ void law_of(const Params& P, const MultiShared& S,
   const float c = P.c;
   float f[N];
   Vc::get(rv[0], f);
+  const RowS p = S.p;
 #pragma unroll
-  for (int e = 0; e < N; ++e) r[e] = fast_exp2(fmaf(f[e], c, -S.p.R)) * S.p.iS;
+  for (int e = 0; e < N; ++e) r[e] = prob_of(f[e], p, c);
 #pragma unroll
   for (int k = 0; k < NR; ++k) {
     Vc::get(rv[1 + k], f);
     const RowS q = S.q[k];
     const float iz = S.iZ[k];
 #pragma unroll
-    for (int e = 0; e < N; ++e)
-      r[e] = fmaxf(r[e] - fast_exp2(fmaf(f[e], c, -q.R)) * q.iS, 0.f) * iz;
+    for (int e = 0; e < N; ++e) r[e] = fmaxf(r[e] - prob_of(f[e], q, c), 0.f) * iz;
   }
   if constexpr (EXTRA) {
     Vc::get(rv[1 + NR], f);
+    const RowS xq = S.xq;
 #pragma unroll
-    for (int e = 0; e < N; ++e)
-      d[e] = fmaxf(r[e] - fast_exp2(fmaf(f[e], c, -S.xq.R)) * S.xq.iS, 0.f);
+    for (int e = 0; e < N; ++e) d[e] = fmaxf(r[e] - prob_of(f[e], xq, c), 0.f);
   }
 }
 
@@ -394,7 +410,41 @@ __global__ __launch_bounds__(kMT, 1) void k_multi(const Params P) {
   const int badtok = __syncthreads_or(bad);
   int live = (1 << M) - 1;
   int n = -1, code = badtok ? SV_SEQ_BAD_TOKEN : 0, tok = -1, lead = 0;
-  for (int j = 0; j <= K && code == 0 && n < 0; ++j) {
+  // Greedy (temperature 0): the target law is a point mass at the argmax of
+  // the lowest live chain's row (lowest id on ties); the first live chain
+  // proposing it is accepted, and when none does it is emitted. No pass over
+  // the vocabulary, so every block of the sequence takes the same steps
+  // without exchanging anything; block 0 writes the outputs.
+  for (int j = 0; P.all_greedy && j <= K && code == 0 && n < 0; ++j) {
+    lead = __builtin_ctz((unsigned)live);
+    if (tid == 0) {
+      const int prow = (b * M + lead) * (K + 1) + j;
+      float v = kNegInf;
+      int am = INT_MAX, bad = 0;
+      merge_greedy(P.slots + unit_of(P, true, prow) * P.chunks, P.chunks, v, am, bad);
+      S.pok = !bad && v != kNegInf;
+      S.tok = am;
+    }
+    __syncthreads();
+    if (!S.pok) {
+      code = SV_SEQ_BAD_ROW;
+      break;
+    }
+    const int a = S.tok;
+    __syncthreads();  // every thread has read S before thread 0 writes it again
+    int keep = 0;
+    if (j < K)
+      for (int m = 0; m < M; ++m)
+        if ((live & (1 << m)) && P.tokens[((size_t)b * M + m) * K + j] == a) keep |= 1 << m;
+    if (keep == 0) {
+      tok = g == 0 ? a : -1;
+      n = j;
+      break;
+    }
+    if (tid == 0 && g == 0) pub_i(P.out_tokens + t_out + j, a);
+    live = keep;
+  }
+  for (int j = 0; !P.all_greedy && j <= K && code == 0 && n < 0; ++j) {
     lead = __builtin_ctz((unsigned)live);
     const int s_lead = b * M + lead;  // chain lead as a sequence of the statistics pass
     if (tid == 0) {
@@ -428,13 +478,11 @@ __global__ __launch_bounds__(kMT, 1) void k_multi(const Params P) {
           S.act = 4;
         } else {
           const int x = P.tokens[(size_t)s * K + j];
-          float r = fast_exp2(fmaf(load_elem<DT>(P.target, (size_t)S.prow * P.V + x), c, -S.p.R)) *
-                    S.p.iS;
+          float r = prob_of(load_elem<DT>(P.target, (size_t)S.prow * P.V + x), S.p, c);
           for (int k = 0; k < S.nrej; ++k)
-            r = fmaxf(r - fast_exp2(fmaf(load_elem<DT>(P.draft, (size_t)S.qrow[k] * P.V + x), c,
-                                         -S.q[k].R)) * S.q[k].iS, 0.f) * S.iZ[k];
-          const float qx =
-              fast_exp2(fmaf(load_elem<DT>(P.draft, (size_t)drow * P.V + x), c, -q.R)) * q.iS;
+            r = fmaxf(r - prob_of(load_elem<DT>(P.draft, (size_t)S.qrow[k] * P.V + x), S.q[k], c),
+                      0.f) * S.iZ[k];
+          const float qx = prob_of(load_elem<DT>(P.draft, (size_t)drow * P.V + x), q, c);
           // r/q with q(x) = 0 < r(x) accepting and r(x) = q(x) = 0 rejecting
           const float ratio = r / qx;
           S.act = ub[m] < ratio ? 1 : 2;
@@ -520,7 +568,8 @@ __global__ __launch_bounds__(kMT, 1) void k_multi(const Params P) {
   for (int k = tid; k < kMultiSyncWords; k += kMT) pub_i(sy + k, 0);
   const int T = (P.nvec + kMTile - 1) / kMTile;
   for (int t = tid; t < T; t += kMT) pub_f(P.mtiles + (size_t)b * P.mtiles_stride + t, 0.f);
-  // the statistics pass's partials of this sequence's rows back to zero
+  // the statistics pass's partials (and with filters the cut pass's row
+  // results) of this sequence's rows back to zero
   const int C = P.chunks;
   const long long d_units = (long long)M * K * C, t_units = (long long)M * (K + 1) * C;
   for (long long k = tid; k < d_units + t_units; k += kMT) {
@@ -528,6 +577,14 @@ __global__ __launch_bounds__(kMT, 1) void k_multi(const Params P) {
     const long long kk = tgt ? k - d_units : k;
     const long long row = (tgt ? (long long)b * M * (K + 1) : (long long)b * M * K) + kk / C;
     P.slots[unit_of(P, tgt, (int)row) * C + kk % C] = 0ull;
+  }
+  if (P.filt) {
+    const int nd = M * K, nt = M * (K + 1);
+    for (int k = tid; k < nd + nt; k += kMT) {
+      const bool tgt = k >= nd;
+      const int row = tgt ? b * nt + (k - nd) : b * nd + k;
+      P.rowres[unit_of(P, tgt, row)] = RowRes{0.f, 0.f, 0.f, 0};
+    }
   }
 }
 

@@ -67,6 +67,27 @@ __device__ __forceinline__ void unpack_am(unsigned long long p, float& v, int& i
   idx = (int)(hi & 0x3fffffffu);
   bad = (hi & 0x40000000u) ? 1 : 0;
 }
+// Merge of a greedy row's C chunk partials, in chunk order (loads issued four
+// chunks at a time so their round trips overlap).
+__device__ __forceinline__ void merge_greedy(const unsigned long long* tsl, int C, float& v,
+                                             int& idx, int& bad) {
+  constexpr int G = 4;
+  for (int k0 = 0; k0 < C; k0 += G) {
+    unsigned long long tv[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) tv[g] = (k0 + g < C) ? tsl[k0 + g] : 1ull;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (k0 + g < C) {
+        float cv;
+        int ci, cb;
+        unpack_am(tv[g], cv, ci, cb);
+        argmax_merge(v, idx, cv, ci);
+        bad |= cb;
+      }
+    }
+  }
+}
 
 // One 16-byte vector (or one element on the scalar path) of a row.
 template <int DT, bool VEC>

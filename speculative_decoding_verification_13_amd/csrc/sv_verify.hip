@@ -229,25 +229,6 @@ __device__ __forceinline__ void merge_sampling(const unsigned long long* dsl,
   }
 }
 
-__device__ __forceinline__ void merge_greedy(const unsigned long long* tsl, int C, float& v,
-                                             int& idx, int& bad) {
-  constexpr int G = 4;
-  for (int k0 = 0; k0 < C; k0 += G) {
-    unsigned long long tv[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) tv[g] = (k0 + g < C) ? tsl[k0 + g] : 1ull;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      if (k0 + g < C) {
-        float cv;
-        int ci, cb;
-        unpack_am(tv[g], cv, ci, cb);
-        argmax_merge(v, idx, cv, ci);
-        bad |= cb;
-      }
-    }
-  }
-}
 
 // Decision of sequence b (whole block; thread i owns position i). Position i
 // stops the walk if a row it reads is invalid, its draft id is out of range or
@@ -935,9 +916,10 @@ __global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
   }
   __syncthreads();
   const float theta = s_theta;
-  if (is_target && !P.skip_bonus) {
+  if (is_target && !P.skip_bonus && P.kept != nullptr) {
     // A target row's kept set, listed for the final draw when every kept id
-    // is an explicit entry (no count-only tie class at or above theta).
+    // is an explicit entry (no count-only tie class at or above theta; none
+    // when the caller keeps no lists).
     unsigned* kl = P.kept + (size_t)row * kKeptWords;
     __syncthreads();
     if (tid == 0) s_n = 0;

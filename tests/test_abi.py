@@ -187,24 +187,34 @@ def test_noalloc_host_checks(L):
 def test_multi_host_checks(L):
     def mc(**kw):
         a = dict(draft=_FAKE, target=_FAKE, tokens=_FAKE, uniforms=_FAKE, B=4, M=3, K=4, V=1024,
-                 T=1.0, dtype=2, out=_FAKE, num=_FAKE, chain=None, ws=_FAKE_WS, ws_bytes=16)
+                 T=1.0, top_k=0, top_p=1.0, dtype=2, out=_FAKE, num=_FAKE, chain=None, ws=_FAKE_WS,
+                 ws_bytes=16)
         a.update(kw)
         return L.spec_verify_multi(a["draft"], a["target"], a["tokens"], a["uniforms"], a["B"],
-                                   a["M"], a["K"], a["V"], a["T"], a["dtype"], a["out"], a["num"],
-                                   a["chain"], a["ws"], a["ws_bytes"], None)
+                                   a["M"], a["K"], a["V"], a["T"], a["top_k"], a["top_p"],
+                                   a["dtype"], a["out"], a["num"], a["chain"], a["ws"],
+                                   a["ws_bytes"], None)
     assert mc() == -3
     assert mc(M=0) == -1 and mc(M=5) == -1 and mc(K=65) == -1 and mc(V=0) == -1
-    assert mc(T=0.0) == -1 and mc(T=float("nan")) == -1
+    assert mc(T=-1.0) == -1 and mc(T=float("nan")) == -1 and mc(T=float("inf")) == -1
+    assert mc(top_p=0.0) == -1 and mc(top_p=1.5) == -1 and mc(top_p=float("nan")) == -1
+    assert mc(top_k=2000, V=4096) == -5  # an active top-k above SV_MAX_TOP_K (1024)
     assert mc(dtype=9) == -2
     assert mc(target=None) == -1 and mc(uniforms=None) == -1 and mc(tokens=None) == -1
+    assert mc(draft=None) == -1
     assert mc(K=0, tokens=None, draft=None) == -3
+    # greedy: draft rows and uniforms are not read
+    assert mc(T=0.0, draft=None, uniforms=None) == -3
+    assert mc(T=0.0, tokens=None) == -1
     assert mc(B=0, draft=None, target=None, tokens=None, uniforms=None, out=None, num=None) == 0
     # the logit path's workspace for the B*M chains, then the walk's state: a
     # 16-word sync record and the tile totals (tiles of 1024 vectors) per sequence
     up = lambda x: (x + 255) // 256 * 256
-    for B, V in ((4, 1024), (3, 128256), (2, 5)):
+    for B, V, k, p in ((4, 1024, 0, 1.0), (3, 128256, 0, 1.0), (2, 5, 0, 1.0),
+                       (3, 128256, 50, 0.9), (3, 32000, 0, 0.9)):
         tiles = (min(V, 1 << 18) + 1023) // 1024
-        assert L.spec_verify_multi_workspace_bytes(B, 3, 4, V) == \
-            L.spec_verify_workspace_bytes(3 * B, 12 * B, V, 0, 1.0) + up(B * 16 * 4) + \
+        assert L.spec_verify_multi_workspace_bytes(B, 3, 4, V, k, p) == \
+            L.spec_verify_workspace_bytes(3 * B, 12 * B, V, k, p) + up(B * 16 * 4) + \
             up(B * tiles * 4)
-    assert L.spec_verify_multi_workspace_bytes(4, 5, 4, 1024) == 0
+    assert L.spec_verify_multi_workspace_bytes(4, 5, 4, 1024, 0, 1.0) == 0
+    assert L.spec_verify_multi_workspace_bytes(4, 3, 4, 1024, 0, 0.0) == 0

@@ -83,7 +83,7 @@ def test_graph_replays_several_chains():
     toks = toks.reshape(B, M, K)
     W.share_target_prefixes(w["target"], toks)
     dev = "cuda"
-    ws = torch.zeros(int(sv.lib().spec_verify_multi_workspace_bytes(B, M, K, V)),
+    ws = torch.zeros(int(sv.lib().spec_verify_multi_workspace_bytes(B, M, K, V, 0, 1.0)),
                      dtype=torch.uint8, device=dev)
     out = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
     num = torch.empty((B,), dtype=torch.int32, device=dev)
