@@ -687,6 +687,7 @@ def bench_multi(args, sv):
                                    torch.from_numpy(w["u_draft"].reshape(-1)).to(dev), zeros_cu,
                                    None, n_rows, V, T, total_draft_rows=0)
     toks = tok.cpu().numpy().reshape(B, M, K)
+    target_raw = w["target"].clone()
     W.share_target_prefixes(w["target"], toks)
     target0 = w["target"].to(dev)
     tokens_d = torch.from_numpy(np.ascontiguousarray(toks, np.int32)).to(dev)
@@ -715,6 +716,44 @@ def bench_multi(args, sv):
     ms = start.elapsed_time(stop) / args.steps
     n_acc = num.cpu().numpy()
     comp = (B * M * K + B * M * (K + 1)) * V * target0.element_size()
+
+    # The same chains verified with filters and greedily: draft tokens drawn
+    # by the library from the filtered rows (the argmax at temperature 0), the
+    # target rows of equal prefixes made equal again, each timed as above on
+    # one copy of the inputs (591 MB, beyond the Infinity Cache).
+    u_draft_d = torch.from_numpy(w["u_draft"].reshape(-1)).to(dev)
+
+    def variant(temp, top_k, top_p):
+        vt, _ = sv.spec_verify_ragged(None, draft0.view(n_rows, V), None, u_draft_d, zeros_cu,
+                                      None, n_rows, V, temp, top_k, top_p, total_draft_rows=0)
+        vtoks = vt.cpu().numpy().reshape(B, M, K)
+        tgt = target_raw.clone()
+        W.share_target_prefixes(tgt, vtoks)
+        tgt_d = tgt.to(dev)
+        vtok_d = torch.from_numpy(np.ascontiguousarray(vtoks, np.int32)).to(dev)
+        vws = sv._lib._zeroed_workspace(
+            max(int(sv.lib().spec_verify_multi_workspace_bytes(B, M, K, V, top_k, top_p)), 256),
+            dev)
+
+        def vstep():
+            sv.spec_verify_multi(draft0, tgt_d, vtok_d, uni_d, B, M, K, V, temp, top_k, top_p,
+                                 out_tokens=out, num_accepted=num, out_chain=chain, workspace=vws)
+        for _ in range(args.warmup):
+            vstep()
+        nsteps = max(10, args.steps // 4)
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(nsteps):
+            vstep()
+        stop.record()
+        torch.cuda.synchronize()
+        va = num.cpu().numpy()
+        return {"ms_per_step": start.elapsed_time(stop) / nsteps, "steps": nsteps,
+                "temperature": temp, "top_k": top_k, "top_p": top_p,
+                "mean_accepted": float(va[va >= 0].mean()) if (va >= 0).any() else None,
+                "errors": int((va < 0).sum())}
+    variants = {"top_k50_top_p0.9": variant(T, 50, 0.9), "top_p0.9": variant(T, 0, 0.9),
+                "greedy": variant(0.0, 0, 1.0)}
     cpu = None
     if args.cpu_seconds > 0:
         draft, target = W.raw_numpy(w["draft"].reshape(-1, V)), W.raw_numpy(w["target"].reshape(-1, V))
@@ -742,6 +781,7 @@ def bench_multi(args, sv):
         "effective_frac_of_peak": comp / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "compulsory_bytes_per_step": comp,
         "acceptance": {"mean_accepted": float(n_acc.mean()), "errors": int((n_acc < 0).sum())},
+        "variants": variants,
         "cpu_baseline": cpu,
     }), flush=True)
 

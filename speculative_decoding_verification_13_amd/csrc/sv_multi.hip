@@ -51,14 +51,18 @@ struct RowS {
   int ok;       // the row holds no NaN or +inf and some finite value
 };
 
-// Probability of logit l in a row: 2^(l*c - R) / S inside its kept set, 0 outside.
+// Probability of logit l in a row: 2^(l*c - R) / S inside its kept set, 0
+// outside (FILT: the row has a cut; without one every id is kept).
+template <bool FILT>
 __device__ __forceinline__ float prob_of(float l, const RowS& r, float c) {
-  return l >= r.thr ? fast_exp2(fmaf(l, c, -r.R)) * r.iS : 0.f;
+  const float v = fast_exp2(fmaf(l, c, -r.R)) * r.iS;
+  if constexpr (FILT) return l >= r.thr ? v : 0.f;
+  return v;
 }
 
 // Statistics of one row: with filters the kept-set maximum, sum and threshold
 // of the cut pass; otherwise its chunk partials merged in chunk order.
-__device__ RowS merged_row(const Params& P, long long unit) {
+__device__ __forceinline__ RowS merged_row(const Params& P, long long unit) {
   RowS r;
   if (P.filt) {
     const RowRes rr = P.rowres[unit];
@@ -180,7 +184,7 @@ __device__ __forceinline__ int mt_ext_i(MultiShared& S, int x) {
 // NR rejected candidates' q peeled off in turn, r <- max(0, r - q_k)/Z_k. With
 // EXTRA, also d = max(0, r - q_extra) (the mass a rejection of that candidate
 // leaves).
-template <int DT, bool VEC, int NR, bool EXTRA>
+template <int DT, bool VEC, bool FILT, int NR, bool EXTRA>
 __device__ __forceinline__ void law_of(const Params& P, const MultiShared& S,
                                        const typename Vec<DT, VEC>::Raw* rv, float* r, float* d) {
   using Vc = Vec<DT, VEC>;
@@ -190,20 +194,20 @@ __device__ __forceinline__ void law_of(const Params& P, const MultiShared& S,
   Vc::get(rv[0], f);
   const RowS p = S.p;
 #pragma unroll
-  for (int e = 0; e < N; ++e) r[e] = prob_of(f[e], p, c);
+  for (int e = 0; e < N; ++e) r[e] = prob_of<FILT>(f[e], p, c);
 #pragma unroll
   for (int k = 0; k < NR; ++k) {
     Vc::get(rv[1 + k], f);
     const RowS q = S.q[k];
     const float iz = S.iZ[k];
 #pragma unroll
-    for (int e = 0; e < N; ++e) r[e] = fmaxf(r[e] - prob_of(f[e], q, c), 0.f) * iz;
+    for (int e = 0; e < N; ++e) r[e] = fmaxf(r[e] - prob_of<FILT>(f[e], q, c), 0.f) * iz;
   }
   if constexpr (EXTRA) {
     Vc::get(rv[1 + NR], f);
     const RowS xq = S.xq;
 #pragma unroll
-    for (int e = 0; e < N; ++e) d[e] = fmaxf(r[e] - prob_of(f[e], xq, c), 0.f);
+    for (int e = 0; e < N; ++e) d[e] = fmaxf(r[e] - prob_of<FILT>(f[e], xq, c), 0.f);
   }
 }
 
@@ -227,7 +231,7 @@ __device__ __forceinline__ void load_rows(const Params& P, const MultiShared& S,
 // EXTRA it returns the block's sum of max(0, r - q_extra) (its part of the
 // next remainder's mass). Otherwise it leaves per-tile sums of r in S.tsum
 // (one wave sum per tile and wave) and returns 0.
-template <int DT, bool VEC, int NR, bool EXTRA>
+template <int DT, bool VEC, bool FILT, int NR, bool EXTRA>
 __device__ float vocab_pass(const Params& P, MultiShared& S) {
   using Vc = Vec<DT, VEC>;
   constexpr int N = Vc::N;
@@ -247,7 +251,7 @@ __device__ float vocab_pass(const Params& P, MultiShared& S) {
     for (int i = 0; i < NBT; ++i) {
       const int v = (t0 + i) * kMTile + tid;
       float r[N], d[N];
-      law_of<DT, VEC, NR, EXTRA>(P, S, rv[i], r, d);
+      law_of<DT, VEC, FILT, NR, EXTRA>(P, S, rv[i], r, d);
       float w = 0.f;
       if (t0 + i < te && v < P.nvec) {
 #pragma unroll
@@ -272,15 +276,18 @@ __device__ float vocab_pass(const Params& P, MultiShared& S) {
 // The mass max(0, r - q_candidate) summed over the vocabulary: each block's
 // part, published, then the parts added in block order (the same sum in every
 // block of the sequence).
-template <int DT, bool VEC>
-__device__ float remainder_mass(const Params& P, MultiShared& S, int b, int g) {
-  float part;
+template <int DT, bool VEC, bool FILT>
+__device__ float remainder_part(const Params& P, MultiShared& S) {
   switch (S.nrej) {
-    case 0: part = vocab_pass<DT, VEC, 0, true>(P, S); break;
-    case 1: part = vocab_pass<DT, VEC, 1, true>(P, S); break;
-    case 2: part = vocab_pass<DT, VEC, 2, true>(P, S); break;
-    default: part = vocab_pass<DT, VEC, SV_MAX_CHAINS - 1, true>(P, S);
+    case 0: return vocab_pass<DT, VEC, FILT, 0, true>(P, S);
+    case 1: return vocab_pass<DT, VEC, FILT, 1, true>(P, S);
+    case 2: return vocab_pass<DT, VEC, FILT, 2, true>(P, S);
+    default: return vocab_pass<DT, VEC, FILT, SV_MAX_CHAINS - 1, true>(P, S);
   }
+}
+template <int DT, bool VEC, bool FILT>
+__device__ __forceinline__ float remainder_mass(const Params& P, MultiShared& S, int b, int g) {
+  const float part = remainder_part<DT, VEC, FILT>(P, S);
   float* parts = reinterpret_cast<float*>(msync_of(P, b) + 4 + kMultiSplit * (S.pass & 1));
   if (threadIdx.x == 0) pub_f(parts + g, part);
   seq_sync(P, S, b);
@@ -293,14 +300,14 @@ __device__ float remainder_mass(const Params& P, MultiShared& S, int b, int g) {
 // Inverse CDF of the current law with uniform u (whole block): the smallest
 // id whose cumulative weight in ascending id order exceeds u * Z; if rounding
 // leaves none, the last id with positive weight.
-template <int DT, bool VEC, int NR>
+template <int DT, bool VEC, bool FILT, int NR>
 __device__ int draw_law_n(const Params& P, MultiShared& S, float u, int b) {
   using Vc = Vec<DT, VEC>;
   constexpr int N = Vc::N;
   using Raw = typename Vc::Raw;
   const int tid = threadIdx.x;
   const int T = (P.nvec + kMTile - 1) / kMTile;
-  vocab_pass<DT, VEC, NR, false>(P, S);
+  vocab_pass<DT, VEC, FILT, NR, false>(P, S);
   // this block's tile totals to the sequence's list, then every tile's
   float* tiles = P.mtiles + (size_t)b * P.mtiles_stride;
   for (int t = S.tb + tid; t < S.te; t += kMT) {
@@ -347,7 +354,7 @@ __device__ int draw_law_n(const Params& P, MultiShared& S, float u, int b) {
   Raw rv[1 + NR];
   load_rows<DT, VEC, NR, false>(P, S, v, rv);
   float r[N], d[N], w[N];
-  law_of<DT, VEC, NR, false>(P, S, rv, r, d);
+  law_of<DT, VEC, FILT, NR, false>(P, S, rv, r, d);
   float acc = 0.f;
 #pragma unroll
   for (int e = 0; e < N; ++e) {
@@ -371,19 +378,19 @@ __device__ int draw_law_n(const Params& P, MultiShared& S, float u, int b) {
 }
 
 // The drawn token in the block whose tiles hold the crossing, -1 in the others.
-template <int DT, bool VEC>
-__device__ int draw_law(const Params& P, MultiShared& S, float u, int b) {
+template <int DT, bool VEC, bool FILT>
+__device__ __forceinline__ int draw_law(const Params& P, MultiShared& S, float u, int b) {
   switch (S.nrej) {
-    case 0: return draw_law_n<DT, VEC, 0>(P, S, u, b);
-    case 1: return draw_law_n<DT, VEC, 1>(P, S, u, b);
-    case 2: return draw_law_n<DT, VEC, 2>(P, S, u, b);
-    case 3: return draw_law_n<DT, VEC, 3>(P, S, u, b);
-    default: return draw_law_n<DT, VEC, SV_MAX_CHAINS>(P, S, u, b);
+    case 0: return draw_law_n<DT, VEC, FILT, 0>(P, S, u, b);
+    case 1: return draw_law_n<DT, VEC, FILT, 1>(P, S, u, b);
+    case 2: return draw_law_n<DT, VEC, FILT, 2>(P, S, u, b);
+    case 3: return draw_law_n<DT, VEC, FILT, 3>(P, S, u, b);
+    default: return draw_law_n<DT, VEC, FILT, SV_MAX_CHAINS>(P, S, u, b);
   }
 }
 
 // One sequence (one block): see the file comment.
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool FILT>
 __global__ __launch_bounds__(kMT, 1) void k_multi(const Params P) {
   __shared__ MultiShared S;
   __shared__ int s_last;
@@ -460,7 +467,7 @@ __global__ __launch_bounds__(kMT, 1) void k_multi(const Params P) {
     }
     const float* ub = P.uniforms + ((size_t)b * (K + 1) + j) * (M + 1);
     if (j == K) {  // bonus: draw from p_K of the lowest live chain
-      tok = draw_law<DT, VEC>(P, S, ub[M], b);
+      tok = draw_law<DT, VEC, FILT>(P, S, ub[M], b);
       n = K;
       break;
     }
@@ -478,11 +485,11 @@ __global__ __launch_bounds__(kMT, 1) void k_multi(const Params P) {
           S.act = 4;
         } else {
           const int x = P.tokens[(size_t)s * K + j];
-          float r = prob_of(load_elem<DT>(P.target, (size_t)S.prow * P.V + x), S.p, c);
+          float r = prob_of<true>(load_elem<DT>(P.target, (size_t)S.prow * P.V + x), S.p, c);
           for (int k = 0; k < S.nrej; ++k)
-            r = fmaxf(r - prob_of(load_elem<DT>(P.draft, (size_t)S.qrow[k] * P.V + x), S.q[k], c),
-                      0.f) * S.iZ[k];
-          const float qx = prob_of(load_elem<DT>(P.draft, (size_t)drow * P.V + x), q, c);
+            r = fmaxf(r - prob_of<true>(load_elem<DT>(P.draft, (size_t)S.qrow[k] * P.V + x),
+                                        S.q[k], c), 0.f) * S.iZ[k];
+          const float qx = prob_of<true>(load_elem<DT>(P.draft, (size_t)drow * P.V + x), q, c);
           // r/q with q(x) = 0 < r(x) accepting and r(x) = q(x) = 0 rejecting
           const float ratio = r / qx;
           S.act = ub[m] < ratio ? 1 : 2;
@@ -499,7 +506,7 @@ __global__ __launch_bounds__(kMT, 1) void k_multi(const Params P) {
         break;
       }
       // rejected: the mass the remainder keeps, then the remainder is the law
-      const float z = remainder_mass<DT, VEC>(P, S, b, g);
+      const float z = remainder_mass<DT, VEC, FILT>(P, S, b, g);
       if (S.to) break;
       if (tid == 0 && z > 0.f) {
         // a mass that rounds to zero keeps the current law
@@ -512,7 +519,7 @@ __global__ __launch_bounds__(kMT, 1) void k_multi(const Params P) {
     }
     if (code != 0 || S.to) break;
     if (accepted < 0) {
-      tok = draw_law<DT, VEC>(P, S, ub[M], b);
+      tok = draw_law<DT, VEC, FILT>(P, S, ub[M], b);
       n = j;
       break;
     }
@@ -588,22 +595,25 @@ __global__ __launch_bounds__(kMT, 1) void k_multi(const Params P) {
   }
 }
 
+template <int DT>
+void launch_multi_dt(bool vec, const Params& P, dim3 grid, dim3 block, hipStream_t s) {
+  if (P.filt) {
+    if (vec) hipLaunchKernelGGL((k_multi<DT, true, true>), grid, block, 0, s, P);
+    else hipLaunchKernelGGL((k_multi<DT, false, true>), grid, block, 0, s, P);
+  } else {
+    if (vec) hipLaunchKernelGGL((k_multi<DT, true, false>), grid, block, 0, s, P);
+    else hipLaunchKernelGGL((k_multi<DT, false, false>), grid, block, 0, s, P);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_multi(int dtype, bool vec, const Params& P, hipStream_t s) {
   const dim3 grid((unsigned)(P.B / P.M * kMultiSplit)), block(kMT);
   switch (dtype) {
-    case SV_F32:
-      if (vec) hipLaunchKernelGGL((k_multi<SV_F32, true>), grid, block, 0, s, P);
-      else hipLaunchKernelGGL((k_multi<SV_F32, false>), grid, block, 0, s, P);
-      break;
-    case SV_F16:
-      if (vec) hipLaunchKernelGGL((k_multi<SV_F16, true>), grid, block, 0, s, P);
-      else hipLaunchKernelGGL((k_multi<SV_F16, false>), grid, block, 0, s, P);
-      break;
-    default:
-      if (vec) hipLaunchKernelGGL((k_multi<SV_BF16, true>), grid, block, 0, s, P);
-      else hipLaunchKernelGGL((k_multi<SV_BF16, false>), grid, block, 0, s, P);
+    case SV_F32: launch_multi_dt<SV_F32>(vec, P, grid, block, s); break;
+    case SV_F16: launch_multi_dt<SV_F16>(vec, P, grid, block, s); break;
+    default: launch_multi_dt<SV_BF16>(vec, P, grid, block, s);
   }
   return hipGetLastError();
 }
