@@ -526,6 +526,7 @@ __device__ void topk_block(const Params& P, long long g, const void* base, size_
           rec[1] = 0u;
           rec[2] = 0u;
           rec[3] = 0u;
+          rec[4] = __float_as_uint(lb2);
         }
         return;
       }
@@ -549,6 +550,7 @@ __device__ void topk_block(const Params& P, long long g, const void* base, size_
       rec[1] = 0u;
       rec[2] = 0u;
       rec[3] = (unsigned)flags;
+      rec[4] = __float_as_uint(lb2);
     }
     return;
   }
@@ -603,6 +605,7 @@ __device__ void topk_block(const Params& P, long long g, const void* base, size_
     rec[1] = __float_as_uint(tau);
     rec[2] = ties_fit ? 0u : (unsigned)eq_tot;
     rec[3] = (unsigned)(flags | (ties_fit ? 0 : kRecFlagImplicitTies));
+    rec[4] = __float_as_uint(tau);
   }
 }
 
@@ -663,44 +666,44 @@ __global__ __launch_bounds__(kThreads) void k_stats(const Params P) {
 }
 
 // ----------------------------------------------------------------- k_filter
-// One block per filtered sampling row: the row's k-th largest finite logit tau
-// (radix select over its chunk records, tie classes counted with their
-// multiplicity), then the kept levels above it sorted in descending order, the
-// softmax masses 2^(l*c - R) of those levels, and the top-p cut: a level stays
-// iff the mass of the strictly larger kept levels, over the top-k mass, is
-// below top_p. The row keeps every id with l >= theta (the smallest kept level).
+// Per filtered sampling row: the row's k-th largest finite logit tau (tie
+// classes counted with their multiplicity), the softmax masses 2^(l*c - R) of
+// the levels at or above it, and the top-p cut: a level stays iff the mass of
+// the strictly larger kept levels, over the top-k mass, is below top_p. The
+// row keeps every id with l >= theta (the smallest kept level).
 // Pages: aihero.vn "Speculative decoding", section "Cùng phân bố không có
 // nghĩa cùng chuỗi mỗi lần" (the same temperature, top-k and top-p on both
 // models' rows).
 constexpr int kFiltBins = 2048;  // 11-bit key digits in the select
 
+// The general path, one whole block per row: radix select over the chunk
+// records, then the levels above tau sorted in descending order and cut. Its
+// staging arrays live in `lds` (kFilterBlockWords words).
+constexpr int kFilterPoolWords = kFiltBins > 2 * kFilterMaxLevels ? kFiltBins : 2 * kFilterMaxLevels;
+constexpr int kFilterBlockWords = kFilterPoolWords + kFilterLdsKeys + 4 * kFilterLdsChunks +
+                                  kFilterLdsChunks + 1;
+
 template <int DT>
-__global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
+__device__ void filter_row_block(const Params& P, int unit, unsigned* lds) {
   // significant high bits of a logit's key: a widened bf16 or fp16 value
   // leaves the low 16 or 13 key bits constant (all zero for a positive value,
   // all one for a negative one), so two 11-bit digits fix its level
   constexpr int kPasses = DT == SV_F32 ? 3 : 2;
   constexpr int kLastShift = DT == SV_F32 ? 0 : 10;
-  // One LDS pool serves, in turn, the staged offsets of the row -> sequence
-  // search, the select's histogram and the levels (value, weight).
-  constexpr int kPoolWords = kFiltBins > 2 * kFilterMaxLevels ? kFiltBins : 2 * kFilterMaxLevels;
-  static_assert(kPoolWords >= kCuLds, "the pool holds the staged offsets");
-  __shared__ __align__(16) unsigned s_pool[kPoolWords];
-  int* const s_cu = reinterpret_cast<int*>(s_pool);
+  // One LDS pool serves, in turn, the select's histogram and the levels
+  // (value, weight).
+  unsigned* const s_pool = lds;
   int* const s_hist = reinterpret_cast<int*>(s_pool);
   float* const s_v = reinterpret_cast<float*>(s_pool);
   float* const s_w = s_v + kFilterMaxLevels;
   __shared__ int s_sel[2];
   __shared__ int s_n;
-  __shared__ unsigned s_key[kFilterLdsKeys];
-  __shared__ unsigned s_hdr[kFilterLdsChunks][4];
-  __shared__ int s_off[kFilterLdsChunks + 1];
+  unsigned* const s_key = lds + kFilterPoolWords;
+  unsigned(*const s_hdr)[4] = reinterpret_cast<unsigned(*)[4]>(s_key + kFilterLdsKeys);
+  int* const s_off = reinterpret_cast<int*>(s_key + kFilterLdsKeys + 4 * kFilterLdsChunks);
   const int tid = threadIdx.x;
-  const int unit = blockIdx.x;
   const bool is_target = unit >= P.total_draft;
   const int row = is_target ? unit - P.total_draft : unit;
-  if (P.greedy != nullptr && P.greedy[row_seq(P, row, is_target, s_cu)] != 0) return;
-  if (P.skip_bonus && is_target && is_bonus_row(P, row, s_cu)) return;
   const int C = P.chunks;
   const unsigned* rec0 = P.rec + (size_t)unit * C * P.rec_words;
   // Stage the records in LDS when they fit: headers, then every entry's key.
@@ -976,6 +979,248 @@ __global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
     }
   } else {
     zero_records(P, C, [&](int ch) { return recw + (size_t)ch * P.rec_words; });
+  }
+}
+
+// The usual path, one wave per row, for bf16 and fp16 rows whose candidates
+// fit the wave: every chunk record's entries are loaded at once (slot s of a
+// lane holds entry 64*q + lane of one chunk), and the candidates at or above
+// the row's bound (the largest chunk bound; the row's k-th largest is never
+// below it) are counted in a histogram of 2048 bins of one level each, from
+// the bound's level up. A widened bf16 or fp16 logit's low 16 or 13 key bits
+// are constant, so a bin is one logit value and its count that value's
+// multiplicity. tau's bin is the one where the count from the top reaches k,
+// and the cut walks the bins from the top with their masses count * 2^(l*c - R).
+// Returns false, having written nothing, when the row needs the general path:
+// fp32, more than 64 chunks or 32 slots, a chunk with NaN or +inf, at most k
+// finite logits, or candidates beyond 2048 levels above the bound.
+constexpr int kFiltRowsPerBlock = kThreads / kWave;
+constexpr int kFastSlots = 32;  // 64-entry slots a lane holds
+// Histogram words: bins in groups of 32 (one lane's), each group followed by
+// four pad words, so a lane's group starts on 16 bytes and the groups of
+// neighbouring lanes fall on different banks.
+constexpr int kFastHistWords = kFiltBins + kFiltBins / 8;
+__device__ __forceinline__ int fast_idx(int b) { return b + 4 * (b >> 5); }
+
+template <int DT>
+__device__ __forceinline__ bool filter_row_fast(const Params& P, int unit, bool is_target, int row,
+                                                unsigned* hist) {
+  if constexpr (DT == SV_F32) {
+    return false;
+  } else {
+    constexpr int kLow = DT == SV_BF16 ? 16 : 13;
+    constexpr unsigned kLowMask = (1u << kLow) - 1u;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int C = P.chunks;
+    if (C > kWave) return false;
+    const unsigned* rec0 = P.rec + (size_t)unit * C * P.rec_words;
+    // chunk c's header in lane c: entries, tie value, tie count, flags; bound
+    uint4 hd = make_uint4(0u, 0u, 0u, 0u);
+    unsigned hb = 0u;
+    if (lane < C) {
+      const unsigned* hp = rec0 + (size_t)lane * P.rec_words;
+      hd = *reinterpret_cast<const uint4*>(hp);
+      hb = hp[4];
+    }
+    const int cnt = lane < C ? min((int)hd.x, P.kcap) : 0;
+    const bool imp = lane < C && (hd.w & kRecFlagImplicitTies) != 0u;
+    if (__builtin_amdgcn_ballot_w64(lane < C && (hd.w & kRecFlagBad) != 0u) != 0ull) return false;
+    const int nq = (cnt + kWave - 1) / kWave;  // slots of chunk `lane`
+    const int qexcl = wave_incl_scan_i(nq) - nq;
+    const int nslots = __builtin_amdgcn_readlane(qexcl + nq, kWave - 1);
+    if (nslots > kFastSlots) return false;
+    if (wave_sum_i(cnt + (imp ? (int)hd.z : 0)) <= P.top_k) return false;
+    const float bnd = wave_max_dpp(lane < C ? __uint_as_float(hb) : kNegInf);
+    if (!(bnd > -__FLT_MAX__)) return false;
+    const unsigned kb = key_of(bnd) & ~kLowMask;  // bin 0: the bound's level
+    // Slot table in lanes 0..31: slot s holds entries 64*(s - first slot of
+    // its chunk) + lane of chunk c(s), the last chunk whose first slot is at or
+    // before s. soff: the word offset of the slot's first entry; slim: its
+    // number of entries.
+    int cs = 0;
+    for (int cc = 1; cc < C; ++cc) cs += (__builtin_amdgcn_readlane(qexcl, cc) <= lane) ? 1 : 0;
+    const int e0 = (lane - __shfl(qexcl, cs)) * kWave;
+    const int soff = cs * P.rec_words + kRecHeader + 2 * e0;
+    const int slim = lane < nslots ? min(kWave, __shfl(cnt, cs) - e0) : 0;
+    uint2 ev[kFastSlots];
+    unsigned vmask = 0u;
+#pragma unroll
+    for (int s = 0; s < kFastSlots; ++s) {
+      ev[s] = make_uint2(0u, 0u);
+      if (s < nslots && lane < __builtin_amdgcn_readlane(slim, s)) {
+        ev[s] = *reinterpret_cast<const uint2*>(rec0 + __builtin_amdgcn_readlane(soff, s) + 2 * lane);
+        vmask |= 1u << s;
+      }
+    }
+    for (int i = lane; i < kFastHistWords / 4; i += kWave)
+      reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
+    __builtin_amdgcn_wave_barrier();
+    // count the candidates at or above the bound by level
+    bool over = false;
+    auto add = [&](float v, unsigned n) {
+      const unsigned bin = (key_of(v) - kb) >> kLow;
+      if (bin < (unsigned)kFiltBins) atomicAdd(&hist[fast_idx((int)bin)], n);
+      else over = true;
+    };
+#pragma unroll
+    for (int s = 0; s < kFastSlots; ++s) {
+      if (s < nslots) {
+        const float v = __uint_as_float(ev[s].x);
+        const bool in = ((vmask >> s) & 1u) && v >= bnd;
+        if (__builtin_amdgcn_ballot_w64(in) != 0ull && in) add(v, 1u);
+      }
+    }
+    if (imp && __uint_as_float(hd.y) >= bnd) add(__uint_as_float(hd.y), hd.z);
+    if (__builtin_amdgcn_ballot_w64(over) != 0ull) return false;
+    __builtin_amdgcn_wave_barrier();
+    // lane l holds the 32 bins of group 63 - l (lane 0 the top ones); bit j of
+    // nzm: bin top - j is not empty
+    const int g = kWave - 1 - lane;
+    const int top = 32 * g + 31;
+    const uint4* hg = reinterpret_cast<const uint4*>(hist + 36 * g);
+    int lsum = 0;
+    unsigned nzm = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint4 q = hg[i];  // bins 32g + 4i .. 32g + 4i + 3, that is j = 31 - 4i - t
+      lsum += (int)(q.x + q.y + q.z + q.w);
+      nzm |= ((q.x != 0u) ? 1u : 0u) << (31 - 4 * i) | ((q.y != 0u) ? 1u : 0u) << (30 - 4 * i) |
+             ((q.z != 0u) ? 1u : 0u) << (29 - 4 * i) | ((q.w != 0u) ? 1u : 0u) << (28 - 4 * i);
+    }
+    // tau: the bin where the count from the top reaches k (lane ft's group,
+    // then its bins, one per lane)
+    const int k = P.top_k;
+    const int incl = wave_incl_scan_i(lsum);
+    const unsigned long long hit = __builtin_amdgcn_ballot_w64(incl >= k);
+    if (hit == 0ull) return false;
+    const int ft = __ffsll((unsigned long long)hit) - 1;
+    const int above_ft = __builtin_amdgcn_readlane(incl - lsum, ft);
+    const int top_ft = 32 * (kWave - 1 - ft) + 31;
+    const int cj = lane < 32 ? (int)hist[fast_idx(top_ft - lane)] : 0;
+    const unsigned long long hit2 =
+        __builtin_amdgcn_ballot_w64(lane < 32 && above_ft + wave_incl_scan_i(cj) >= k);
+    const int btau = top_ft - (__ffsll((unsigned long long)hit2) - 1);
+    // the row maximum: the top non-empty bin
+    const int fm = __ffsll((unsigned long long)__builtin_amdgcn_ballot_w64(nzm != 0u)) - 1;
+    const int bmax = 32 * (kWave - 1 - fm) + 31 - (__ffs((int)__builtin_amdgcn_readlane((int)nzm, fm)) - 1);
+    auto level = [&](int b) {
+      unsigned key = kb + ((unsigned)b << kLow);
+      if (!(key & 0x80000000u)) key |= kLowMask;
+      return float_of_key(key);
+    };
+    const float c = P.c;
+    const float m = level(bmax);
+    const float R = ref_of(m, c);
+    // the levels from tau up: this lane's non-empty bins at or above btau, in
+    // descending order; their masses replace their counts in the histogram
+    const unsigned ftmask = 0xFFFFFFFFu >> (31 - (top_ft - btau));  // bins of lane ft down to btau
+    const unsigned live = lane < ft ? nzm : (lane == ft ? nzm & ftmask : 0u);
+    float esum = 0.0f;
+    for (unsigned mm = live; mm != 0u; mm &= mm - 1u) {
+      const int b = top - (__ffs((int)mm) - 1);
+      unsigned* hw = &hist[fast_idx(b)];
+      const float e = (float)*hw * fast_exp2(fmaf(level(b), c, -R));
+      *hw = __float_as_uint(e);
+      esum += e;
+    }
+    const float eincl = wave_incl_scan(esum);
+    const float S_k = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                    __builtin_bit_cast(int, eincl), kWave - 1));
+    // kept: the mass of the strictly larger levels over S_k below top_p (every
+    // level from tau up when top_p is 1)
+    const bool all = !(P.top_p < 1.0f);
+    float above = eincl - esum, kincl = 0.0f;
+    int bk = -1;
+    for (unsigned mm = live; mm != 0u; mm &= mm - 1u) {
+      const int b = top - (__ffs((int)mm) - 1);
+      const float e = __uint_as_float(hist[fast_idx(b)]);
+      if (all || above / S_k < P.top_p) {
+        bk = b;
+        kincl = above + e;
+      }
+      above += e;
+    }
+    const int lk = 63 - __clzll((long long)__builtin_amdgcn_ballot_w64(bk >= 0));
+    const float theta = level(__builtin_amdgcn_readlane(bk, lk));
+    const float S_f = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                    __builtin_bit_cast(int, kincl), lk));
+    if (lane == 0) P.rowres[unit] = RowRes{m, S_f, theta, 0};
+    if (is_target && !P.skip_bonus && P.kept != nullptr) {
+      // the kept set (no count-only tie class at or above theta), in slot order
+      unsigned* kl = P.kept + (size_t)row * kKeptWords;
+      int n = 0;
+#pragma unroll
+      for (int s = 0; s < kFastSlots; ++s) {
+        if (s < nslots) {
+          const bool in = ((vmask >> s) & 1u) && __uint_as_float(ev[s].x) >= theta;
+          const unsigned long long msk = __builtin_amdgcn_ballot_w64(in);
+          if (msk != 0ull) {
+            const int at = n + (int)__builtin_amdgcn_mbcnt_hi(
+                                   (unsigned)(msk >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)msk, 0u));
+            if (in && at < kExplicitMax) *reinterpret_cast<uint2*>(kl + 2 + 2 * at) = ev[s];
+            n += __builtin_popcountll(msk);
+          }
+        }
+      }
+      const bool partial =
+          __builtin_amdgcn_ballot_w64(imp && __uint_as_float(hd.y) >= theta) != 0ull;
+      if (lane == 0) {
+        kl[0] = (unsigned)min(n, kExplicitMax);
+        kl[1] = (partial || n > kExplicitMax) ? 1u : 0u;
+      }
+    }
+    // the records go back to zero: every entry read, then the headers
+    unsigned* recw = P.rec + (size_t)unit * C * P.rec_words;
+#pragma unroll
+    for (int s = 0; s < kFastSlots; ++s)
+      if ((vmask >> s) & 1u)
+        *reinterpret_cast<uint2*>(recw + __builtin_amdgcn_readlane(soff, s) + 2 * lane) =
+            make_uint2(0u, 0u);
+    if (lane < C) {
+      uint4* hp = reinterpret_cast<uint4*>(recw + (size_t)lane * P.rec_words);
+      hp[0] = make_uint4(0u, 0u, 0u, 0u);
+      hp[1] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    return true;
+  }
+}
+
+// Four rows per block: each wave tries its row on the fast path, then the
+// whole block takes the rows that need the general path, one at a time, in
+// the LDS the histograms held.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
+  __shared__ __align__(16) unsigned s_fh[kFiltRowsPerBlock][kFastHistWords];
+  __shared__ int s_fail[kFiltRowsPerBlock];
+  static_assert(kFastHistWords >= kCuLds, "the first histogram holds the staged offsets");
+  static_assert(kFiltRowsPerBlock * kFastHistWords >= kFilterBlockWords,
+                "the histograms hold the general path's staging");
+  int* const s_cu = reinterpret_cast<int*>(s_fh[0]);
+  const int wave = threadIdx.x / kWave;
+  const long long units = (long long)P.total_draft + P.rows;
+  const long long u = (long long)blockIdx.x * kFiltRowsPerBlock + wave;
+  const bool valid = u < units;
+  const int unit = valid ? (int)u : 0;
+  bool is_target;
+  int row;
+  row_of_unit(P, unit, is_target, row);
+  // greedy rows and skipped bonus rows have no records (whole block: the
+  // offsets are staged once per call)
+  bool skip = !valid;
+  if (P.greedy != nullptr) skip |= P.greedy[row_seq(P, row, is_target, s_cu)] != 0;
+  if (P.skip_bonus) {
+    const bool bonus = is_bonus_row(P, is_target ? row : 0, s_cu);
+    skip |= is_target && bonus;
+  }
+  __syncthreads();  // the staged offsets are read before the histograms reuse them
+  const bool done = skip || filter_row_fast<DT>(P, unit, is_target, row, s_fh[wave]);
+  if ((threadIdx.x & (kWave - 1)) == 0) s_fail[wave] = done ? 0 : 1;
+  __syncthreads();
+  for (int w = 0; w < kFiltRowsPerBlock; ++w) {
+    if (s_fail[w]) {
+      __syncthreads();  // the LDS of the histograms, or of the previous row, is free
+      filter_row_block<DT>(P, blockIdx.x * kFiltRowsPerBlock + w, &s_fh[0][0]);
+    }
   }
 }
 
@@ -1455,8 +1700,11 @@ __device__ void draw_unit(const Params& P, int idx) {
   __shared__ Dec S;
   __shared__ int s_last;
   const int tid = threadIdx.x;
-  const int b = idx / P.dchunks;
-  const int ch = idx - b * P.dchunks;
+  // block order: every sequence's first block, then every sequence's second,
+  // and so on, so that the first blocks (which draw alone when the kept lists
+  // are complete) start together; no block of this kernel waits for another
+  const int ch = idx / P.B;
+  const int b = idx - ch * P.B;
   int d0, kb;
   if (!seq_bounds(P, b, d0, kb)) {
     if (ch == 0 && tid == 0) P.num_accepted[b] = SV_SEQ_BAD_OFFSETS;
@@ -1634,6 +1882,11 @@ static hipError_t stage_event(hipEvent_t* ev, int nev, int i, hipStream_t s) {
 // Statistics, then (with top-k) the filter pass, then decision and draw. Stage
 // events: before the first kernel, after each kernel of a filtered call (an
 // unfiltered call here is one stage), and every further one after the last.
+// Blocks of the filter launch: one row per wave.
+static unsigned filter_grid(const Plan& L) {
+  return (unsigned)((L.filter_blocks + kFiltRowsPerBlock - 1) / kFiltRowsPerBlock);
+}
+
 template <int DT, bool VEC>
 static hipError_t launch_t(const Params& P, const Plan& L, hipStream_t s, hipEvent_t* ev, int nev) {
   hipError_t err;
@@ -1652,7 +1905,7 @@ static hipError_t launch_t(const Params& P, const Plan& L, hipStream_t s, hipEve
       hipLaunchKernelGGL((k_nucleus<DT, VEC>), dim3((unsigned)L.filter_blocks), dim3(kNucThreads),
                          0, s, P);
     else
-      hipLaunchKernelGGL(k_filter<DT>, dim3((unsigned)L.filter_blocks), dim3(kThreads), 0, s, P);
+      hipLaunchKernelGGL(k_filter<DT>, dim3(filter_grid(L)), dim3(kThreads), 0, s, P);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if ((err = stage_event(ev, nev, e++, s)) != hipSuccess) return err;
   } else {
@@ -1694,7 +1947,7 @@ static hipError_t launch_row_stats_t(const Params& P, const Plan& L, hipStream_t
                        s, P);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k_filter<DT>, dim3((unsigned)L.filter_blocks), dim3(kThreads), 0, s, P);
+    hipLaunchKernelGGL(k_filter<DT>, dim3(filter_grid(L)), dim3(kThreads), 0, s, P);
   } else {
     hipLaunchKernelGGL((k_stats<DT, VEC, false>), dim3((unsigned)L.stats_blocks), dim3(kThreads),
                        0, s, P);
