@@ -42,8 +42,6 @@ constexpr int kMaxDrawSlices = kThreads;  // draw blocks per sequence of the one
 // Chunk record of a filtered row: header then `kcap` (value bits, id) pairs.
 //   [0] entries written   [1] value of an implicit tie class   [2] its count
 //   [3] flags: 1 NaN or +inf seen, 2 the tie class is implicit (count only)
-//   [4] a lower bound of the chunk's k-th largest finite logit (-FLT_MAX when
-//       the chunk gives none); every entry at or above it is in the record
 enum { kRecFlagBad = 1, kRecFlagImplicitTies = 2 };
 
 // Per-row result of the filter pass: kept-set maximum, kept-set sum of

@@ -399,7 +399,9 @@ __device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool 
 // so the per-logit work is one maximum. A chunk with more candidates than the
 // record holds (heavy ties, or k beyond what the bound covers) is cut to its
 // exact top k by a radix select on order-preserving keys; a tie class at the
-// cut that still does not fit is recorded as (value, count).
+// cut that still does not fit is recorded as (value, count). Header word 4
+// holds a lower bound of the chunk's k-th largest finite logit (-FLT_MAX when
+// the chunk gives none): every logit at or above it is in the record.
 template <int DT, bool VEC>
 __device__ void topk_block(const Params& P, long long g, const void* base, size_t roff, int ch) {
   using Vc = Vec<DT, VEC>;
