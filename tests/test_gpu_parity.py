@@ -175,6 +175,23 @@ def test_filters_cut_between_adjacent_values(dtype):
     _check(w, api="ragged", diag=True, tag=f"adjacent cut {dtype}")
 
 
+@pytest.mark.parametrize("dtype,peak", [("f16", 40.0), ("bf16", 1.0e6)])
+def test_filters_wide_candidate_range(dtype, peak):
+    """Every third row holds a few ids far above the rest, so its top-k
+    candidates span more than 2048 levels of the dtype: those rows leave the
+    one-wave level histogram for the block-wide select, while the rows beside
+    them in the same launch block stay on it."""
+    w = _filtered(50, 0.9, B=6, V=20000, dtype=dtype)
+    g = torch.Generator().manual_seed(11)
+    for key in ("draft", "target"):
+        t = w[key].float()
+        for r in range(0, t.shape[0], 3):
+            ids = torch.randperm(t.shape[1], generator=g)[:3]
+            t[r, ids] = peak * torch.tensor([1.0, 0.75, 0.5])
+        w[key] = t.to(w[key].dtype)
+    _check(w, api="ragged", diag=True, tag=f"wide range {dtype}")
+
+
 def test_filters_masked_rows_and_scalar_path():
     """Rows with most ids at -inf (fewer finite logits than k in some rows), on
     an odd V (scalar path)."""
