@@ -984,223 +984,49 @@ __device__ void filter_row_block(const Params& P, int unit, unsigned* lds) {
   }
 }
 
-// The usual path, one wave per row, for bf16 and fp16 rows whose candidates
-// fit the wave: every chunk record's entries are loaded at once (slot s of a
-// lane holds entry 64*q + lane of one chunk), and the candidates at or above
-// the row's bound (the largest chunk bound; the row's k-th largest is never
-// below it) are counted in a histogram of 2048 bins of one level each, from
-// the bound's level up. A widened bf16 or fp16 logit's low 16 or 13 key bits
-// are constant, so a bin is one logit value and its count that value's
-// multiplicity. tau's bin is the one where the count from the top reaches k,
-// and the cut walks the bins from the top with their masses count * 2^(l*c - R).
-// Returns false, having written nothing, when the row needs the general path:
-// fp32, more than 64 chunks or 32 slots, a chunk with NaN or +inf, at most k
-// finite logits, or candidates beyond 2048 levels above the bound.
-constexpr int kFiltRowsPerBlock = kThreads / kWave;
-constexpr int kFastSlots = 32;  // 64-entry slots a lane holds
+// The usual path, two waves per row, for bf16 and fp16 rows whose candidates
+// fit: every chunk record's entries are loaded at once (the row's slots of 64
+// entries of one chunk, split between the two waves), and the candidates at or
+// above the row's bound (the largest chunk bound; the row's k-th largest is
+// never below it) are counted in a histogram of 2048 bins of one level each,
+// from the bound's level up. A widened bf16 or fp16 logit's low 16 or 13 key
+// bits are constant, so a bin is one logit value and its count that value's
+// multiplicity. The first wave then finds tau's bin (where the count from the
+// top reaches k) and walks the bins from the top with their masses
+// count * 2^(l*c - R) for the top-p cut; both waves list the kept set and
+// return the records to zero. A row takes the general path instead (having
+// written nothing) for fp32, more than 64 chunks or 32 slots, a chunk with NaN
+// or +inf, at most k finite logits, or candidates beyond 2048 levels above the
+// bound.
+constexpr int kFiltRowsPerBlock = kThreads / (2 * kWave);
+constexpr int kFastSlots = 32;                   // 64-entry slots of a row
+constexpr int kHalfSlots = kFastSlots / 2;       // slots a wave holds
 // Histogram words: bins in groups of 32 (one lane's), each group followed by
 // four pad words, so a lane's group starts on 16 bytes and the groups of
 // neighbouring lanes fall on different banks.
 constexpr int kFastHistWords = kFiltBins + kFiltBins / 8;
 __device__ __forceinline__ int fast_idx(int b) { return b + 4 * (b >> 5); }
+enum { kFiltFast = 0, kFiltGeneral = 1, kFiltNone = 2 };
 
-template <int DT>
-__device__ __forceinline__ bool filter_row_fast(const Params& P, int unit, bool is_target, int row,
-                                                unsigned* hist) {
-  if constexpr (DT == SV_F32) {
-    return false;
-  } else {
-    constexpr int kLow = DT == SV_BF16 ? 16 : 13;
-    constexpr unsigned kLowMask = (1u << kLow) - 1u;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int C = P.chunks;
-    if (C > kWave) return false;
-    const unsigned* rec0 = P.rec + (size_t)unit * C * P.rec_words;
-    // chunk c's header in lane c: entries, tie value, tie count, flags; bound
-    uint4 hd = make_uint4(0u, 0u, 0u, 0u);
-    unsigned hb = 0u;
-    if (lane < C) {
-      const unsigned* hp = rec0 + (size_t)lane * P.rec_words;
-      hd = *reinterpret_cast<const uint4*>(hp);
-      hb = hp[4];
-    }
-    const int cnt = lane < C ? min((int)hd.x, P.kcap) : 0;
-    const bool imp = lane < C && (hd.w & kRecFlagImplicitTies) != 0u;
-    if (__builtin_amdgcn_ballot_w64(lane < C && (hd.w & kRecFlagBad) != 0u) != 0ull) return false;
-    const int nq = (cnt + kWave - 1) / kWave;  // slots of chunk `lane`
-    const int qexcl = wave_incl_scan_i(nq) - nq;
-    const int nslots = __builtin_amdgcn_readlane(qexcl + nq, kWave - 1);
-    if (nslots > kFastSlots) return false;
-    if (wave_sum_i(cnt + (imp ? (int)hd.z : 0)) <= P.top_k) return false;
-    const float bnd = wave_max_dpp(lane < C ? __uint_as_float(hb) : kNegInf);
-    if (!(bnd > -__FLT_MAX__)) return false;
-    const unsigned kb = key_of(bnd) & ~kLowMask;  // bin 0: the bound's level
-    // Slot table in lanes 0..31: slot s holds entries 64*(s - first slot of
-    // its chunk) + lane of chunk c(s), the last chunk whose first slot is at or
-    // before s. soff: the word offset of the slot's first entry; slim: its
-    // number of entries.
-    int cs = 0;
-    for (int cc = 1; cc < C; ++cc) cs += (__builtin_amdgcn_readlane(qexcl, cc) <= lane) ? 1 : 0;
-    const int e0 = (lane - __shfl(qexcl, cs)) * kWave;
-    const int soff = cs * P.rec_words + kRecHeader + 2 * e0;
-    const int slim = lane < nslots ? min(kWave, __shfl(cnt, cs) - e0) : 0;
-    uint2 ev[kFastSlots];
-    unsigned vmask = 0u;
-#pragma unroll
-    for (int s = 0; s < kFastSlots; ++s) {
-      ev[s] = make_uint2(0u, 0u);
-      if (s < nslots && lane < __builtin_amdgcn_readlane(slim, s)) {
-        ev[s] = *reinterpret_cast<const uint2*>(rec0 + __builtin_amdgcn_readlane(soff, s) + 2 * lane);
-        vmask |= 1u << s;
-      }
-    }
-    for (int i = lane; i < kFastHistWords / 4; i += kWave)
-      reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
-    __builtin_amdgcn_wave_barrier();
-    // count the candidates at or above the bound by level
-    bool over = false;
-    auto add = [&](float v, unsigned n) {
-      const unsigned bin = (key_of(v) - kb) >> kLow;
-      if (bin < (unsigned)kFiltBins) atomicAdd(&hist[fast_idx((int)bin)], n);
-      else over = true;
-    };
-#pragma unroll
-    for (int s = 0; s < kFastSlots; ++s) {
-      if (s < nslots) {
-        const float v = __uint_as_float(ev[s].x);
-        const bool in = ((vmask >> s) & 1u) && v >= bnd;
-        if (__builtin_amdgcn_ballot_w64(in) != 0ull && in) add(v, 1u);
-      }
-    }
-    if (imp && __uint_as_float(hd.y) >= bnd) add(__uint_as_float(hd.y), hd.z);
-    if (__builtin_amdgcn_ballot_w64(over) != 0ull) return false;
-    __builtin_amdgcn_wave_barrier();
-    // lane l holds the 32 bins of group 63 - l (lane 0 the top ones); bit j of
-    // nzm: bin top - j is not empty
-    const int g = kWave - 1 - lane;
-    const int top = 32 * g + 31;
-    const uint4* hg = reinterpret_cast<const uint4*>(hist + 36 * g);
-    int lsum = 0;
-    unsigned nzm = 0u;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint4 q = hg[i];  // bins 32g + 4i .. 32g + 4i + 3, that is j = 31 - 4i - t
-      lsum += (int)(q.x + q.y + q.z + q.w);
-      nzm |= ((q.x != 0u) ? 1u : 0u) << (31 - 4 * i) | ((q.y != 0u) ? 1u : 0u) << (30 - 4 * i) |
-             ((q.z != 0u) ? 1u : 0u) << (29 - 4 * i) | ((q.w != 0u) ? 1u : 0u) << (28 - 4 * i);
-    }
-    // tau: the bin where the count from the top reaches k (lane ft's group,
-    // then its bins, one per lane)
-    const int k = P.top_k;
-    const int incl = wave_incl_scan_i(lsum);
-    const unsigned long long hit = __builtin_amdgcn_ballot_w64(incl >= k);
-    if (hit == 0ull) return false;
-    const int ft = __ffsll((unsigned long long)hit) - 1;
-    const int above_ft = __builtin_amdgcn_readlane(incl - lsum, ft);
-    const int top_ft = 32 * (kWave - 1 - ft) + 31;
-    const int cj = lane < 32 ? (int)hist[fast_idx(top_ft - lane)] : 0;
-    const unsigned long long hit2 =
-        __builtin_amdgcn_ballot_w64(lane < 32 && above_ft + wave_incl_scan_i(cj) >= k);
-    const int btau = top_ft - (__ffsll((unsigned long long)hit2) - 1);
-    // the row maximum: the top non-empty bin
-    const int fm = __ffsll((unsigned long long)__builtin_amdgcn_ballot_w64(nzm != 0u)) - 1;
-    const int bmax = 32 * (kWave - 1 - fm) + 31 - (__ffs((int)__builtin_amdgcn_readlane((int)nzm, fm)) - 1);
-    auto level = [&](int b) {
-      unsigned key = kb + ((unsigned)b << kLow);
-      if (!(key & 0x80000000u)) key |= kLowMask;
-      return float_of_key(key);
-    };
-    const float c = P.c;
-    const float m = level(bmax);
-    const float R = ref_of(m, c);
-    // the levels from tau up: this lane's non-empty bins at or above btau, in
-    // descending order; their masses replace their counts in the histogram
-    const unsigned ftmask = 0xFFFFFFFFu >> (31 - (top_ft - btau));  // bins of lane ft down to btau
-    const unsigned live = lane < ft ? nzm : (lane == ft ? nzm & ftmask : 0u);
-    float esum = 0.0f;
-    for (unsigned mm = live; mm != 0u; mm &= mm - 1u) {
-      const int b = top - (__ffs((int)mm) - 1);
-      unsigned* hw = &hist[fast_idx(b)];
-      const float e = (float)*hw * fast_exp2(fmaf(level(b), c, -R));
-      *hw = __float_as_uint(e);
-      esum += e;
-    }
-    const float eincl = wave_incl_scan(esum);
-    const float S_k = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                    __builtin_bit_cast(int, eincl), kWave - 1));
-    // kept: the mass of the strictly larger levels over S_k below top_p (every
-    // level from tau up when top_p is 1)
-    const bool all = !(P.top_p < 1.0f);
-    float above = eincl - esum, kincl = 0.0f;
-    int bk = -1;
-    for (unsigned mm = live; mm != 0u; mm &= mm - 1u) {
-      const int b = top - (__ffs((int)mm) - 1);
-      const float e = __uint_as_float(hist[fast_idx(b)]);
-      if (all || above / S_k < P.top_p) {
-        bk = b;
-        kincl = above + e;
-      }
-      above += e;
-    }
-    const int lk = 63 - __clzll((long long)__builtin_amdgcn_ballot_w64(bk >= 0));
-    const float theta = level(__builtin_amdgcn_readlane(bk, lk));
-    const float S_f = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                    __builtin_bit_cast(int, kincl), lk));
-    if (lane == 0) P.rowres[unit] = RowRes{m, S_f, theta, 0};
-    if (is_target && !P.skip_bonus && P.kept != nullptr) {
-      // the kept set (no count-only tie class at or above theta), in slot order
-      unsigned* kl = P.kept + (size_t)row * kKeptWords;
-      int n = 0;
-#pragma unroll
-      for (int s = 0; s < kFastSlots; ++s) {
-        if (s < nslots) {
-          const bool in = ((vmask >> s) & 1u) && __uint_as_float(ev[s].x) >= theta;
-          const unsigned long long msk = __builtin_amdgcn_ballot_w64(in);
-          if (msk != 0ull) {
-            const int at = n + (int)__builtin_amdgcn_mbcnt_hi(
-                                   (unsigned)(msk >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)msk, 0u));
-            if (in && at < kExplicitMax) *reinterpret_cast<uint2*>(kl + 2 + 2 * at) = ev[s];
-            n += __builtin_popcountll(msk);
-          }
-        }
-      }
-      const bool partial =
-          __builtin_amdgcn_ballot_w64(imp && __uint_as_float(hd.y) >= theta) != 0ull;
-      if (lane == 0) {
-        kl[0] = (unsigned)min(n, kExplicitMax);
-        kl[1] = (partial || n > kExplicitMax) ? 1u : 0u;
-      }
-    }
-    // the records go back to zero: every entry read, then the headers
-    unsigned* recw = P.rec + (size_t)unit * C * P.rec_words;
-#pragma unroll
-    for (int s = 0; s < kFastSlots; ++s)
-      if ((vmask >> s) & 1u)
-        *reinterpret_cast<uint2*>(recw + __builtin_amdgcn_readlane(soff, s) + 2 * lane) =
-            make_uint2(0u, 0u);
-    if (lane < C) {
-      uint4* hp = reinterpret_cast<uint4*>(recw + (size_t)lane * P.rec_words);
-      hp[0] = make_uint4(0u, 0u, 0u, 0u);
-      hp[1] = make_uint4(0u, 0u, 0u, 0u);
-    }
-    return true;
-  }
-}
-
-// Four rows per block: each wave tries its row on the fast path, then the
-// whole block takes the rows that need the general path, one at a time, in
-// the LDS the histograms held.
+// Two rows per block: each row's two waves take the usual path together, then
+// the whole block takes the rows that need the general path, one at a time, in
+// the LDS the histograms held. Every wave passes every barrier.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
+  constexpr bool kFast = DT != SV_F32;
+  constexpr int kLow = DT == SV_BF16 ? 16 : 13;
+  constexpr unsigned kLowMask = (1u << kLow) - 1u;
   __shared__ __align__(16) unsigned s_fh[kFiltRowsPerBlock][kFastHistWords];
-  __shared__ int s_fail[kFiltRowsPerBlock];
+  __shared__ int s_state[kFiltRowsPerBlock], s_over[kFiltRowsPerBlock], s_kn[kFiltRowsPerBlock];
+  __shared__ float s_theta[kFiltRowsPerBlock];
   static_assert(kFastHistWords >= kCuLds, "the first histogram holds the staged offsets");
   static_assert(kFiltRowsPerBlock * kFastHistWords >= kFilterBlockWords,
                 "the histograms hold the general path's staging");
   int* const s_cu = reinterpret_cast<int*>(s_fh[0]);
-  const int wave = threadIdx.x / kWave;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int ri = wave >> 1, h = wave & 1;  // the row of this wave, and its half
   const long long units = (long long)P.total_draft + P.rows;
-  const long long u = (long long)blockIdx.x * kFiltRowsPerBlock + wave;
+  const long long u = (long long)blockIdx.x * kFiltRowsPerBlock + ri;
   const bool valid = u < units;
   const int unit = valid ? (int)u : 0;
   bool is_target;
@@ -1214,12 +1040,223 @@ __global__ __launch_bounds__(kThreads) void k_filter(const Params P) {
     const bool bonus = is_bonus_row(P, is_target ? row : 0, s_cu);
     skip |= is_target && bonus;
   }
+  if (threadIdx.x < kFiltRowsPerBlock) {
+    s_over[threadIdx.x] = 0;
+    s_kn[threadIdx.x] = 0;
+  }
   __syncthreads();  // the staged offsets are read before the histograms reuse them
-  const bool done = skip || filter_row_fast<DT>(P, unit, is_target, row, s_fh[wave]);
-  if ((threadIdx.x & (kWave - 1)) == 0) s_fail[wave] = done ? 0 : 1;
-  __syncthreads();
+  unsigned* const hist = s_fh[ri];
+  const int C = P.chunks;
+  const unsigned* rec0 = P.rec + (size_t)unit * C * P.rec_words;
+  // chunk c's header in lane c: entries, tie value, tie count, flags; bound
+  bool ok = kFast && !skip && C <= kWave;
+  uint4 hd = make_uint4(0u, 0u, 0u, 0u);
+  unsigned hb = 0u;
+  if (ok && lane < C) {
+    const unsigned* hp = rec0 + (size_t)lane * P.rec_words;
+    hd = *reinterpret_cast<const uint4*>(hp);
+    hb = hp[4];
+  }
+  const int cnt = lane < C ? min((int)hd.x, P.kcap) : 0;
+  const bool imp = lane < C && (hd.w & kRecFlagImplicitTies) != 0u;
+  int nq = 0, qexcl = 0, nslots = 0, soff = 0, slim = 0;
+  float bnd = kNegInf;
+  unsigned kb = 0u;
+  if (ok) {  // wave-uniform; both waves of a row reach the same decisions
+    ok = __builtin_amdgcn_ballot_w64(lane < C && (hd.w & kRecFlagBad) != 0u) == 0ull;
+    nq = (cnt + kWave - 1) / kWave;  // slots of chunk `lane`
+    qexcl = wave_incl_scan_i(nq) - nq;
+    nslots = __builtin_amdgcn_readlane(qexcl + nq, kWave - 1);
+    ok = ok && nslots <= kFastSlots;
+    ok = ok && wave_sum_i(cnt + (imp ? (int)hd.z : 0)) > P.top_k;
+    bnd = wave_max_dpp(lane < C ? __uint_as_float(hb) : kNegInf);
+    ok = ok && bnd > -__FLT_MAX__;
+    kb = key_of(bnd) & ~kLowMask;  // bin 0: the bound's level
+    // Slot table in lanes 0..31: slot s holds entries 64*(s - first slot of
+    // its chunk) + lane of chunk c(s), the last chunk whose first slot is at or
+    // before s. soff: the word offset of the slot's first entry; slim: its
+    // number of entries.
+    int cs = 0;
+    for (int cc = 1; cc < C; ++cc) cs += (__builtin_amdgcn_readlane(qexcl, cc) <= lane) ? 1 : 0;
+    const int e0 = (lane - __shfl(qexcl, cs)) * kWave;
+    soff = cs * P.rec_words + kRecHeader + 2 * e0;
+    slim = lane < nslots ? min(kWave, __shfl(cnt, cs) - e0) : 0;
+  }
+  // This wave's slots h, h + 2, ...: every one is loaded, with no branch, so
+  // that all the loads are in flight together. A slot past the last reads the
+  // first slot's entries, and a lane past its slot's count reads a zero entry
+  // of the same record (a slot never runs past its chunk's kcap entries).
+  // vmask marks the entries.
+  uint2 ev[kHalfSlots];
+  unsigned vmask = 0u;
+  if (ok) {
+#pragma unroll
+    for (int j = 0; j < kHalfSlots; ++j) {
+      const int s = 2 * j + h;
+      const int so = s < nslots ? __builtin_amdgcn_readlane(soff, s) : __builtin_amdgcn_readlane(soff, 0);
+      ev[j] = *reinterpret_cast<const uint2*>(rec0 + so + 2 * lane);
+      if (s < nslots && lane < __builtin_amdgcn_readlane(slim, s)) vmask |= 1u << j;
+    }
+    for (int i = h * kWave + lane; i < kFastHistWords / 4; i += 2 * kWave)
+      reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  __syncthreads();  // the histograms are clear
+  if (ok) {
+    // count the candidates at or above the bound by level; a candidate beyond
+    // the last bin goes to the last pad word and makes the row take the
+    // general path
+    bool over = false;
+    auto add = [&](float v, unsigned n) {
+      const unsigned bin = (key_of(v) - kb) >> kLow;
+      over |= bin >= (unsigned)kFiltBins;
+      atomicAdd(&hist[bin < (unsigned)kFiltBins ? fast_idx((int)bin) : kFastHistWords - 1], n);
+    };
+#pragma unroll
+    for (int j = 0; j < kHalfSlots; ++j) {
+      const float v = __uint_as_float(ev[j].x);
+      if (((vmask >> j) & 1u) && v >= bnd) add(v, 1u);
+    }
+    if (h == 0 && imp && __uint_as_float(hd.y) >= bnd) add(__uint_as_float(hd.y), hd.z);
+    if (__builtin_amdgcn_ballot_w64(over) != 0ull && lane == 0) s_over[ri] = 1;
+  }
+  __syncthreads();  // the counts and the overflow marks are in
+  ok = ok && s_over[ri] == 0;
+  if (h == 0) {
+    int state = skip ? kFiltNone : kFiltGeneral;
+    if (ok) {
+      // lane l holds the 32 bins of group 63 - l (lane 0 the top ones); bit j
+      // of nzm: bin top - j is not empty
+      const int g = kWave - 1 - lane;
+      const int top = 32 * g + 31;
+      const uint4* hg = reinterpret_cast<const uint4*>(hist + 36 * g);
+      int lsum = 0;
+      unsigned nzm = 0u;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint4 q = hg[i];  // bins 32g + 4i .. 32g + 4i + 3, that is j = 31 - 4i - t
+        lsum += (int)(q.x + q.y + q.z + q.w);
+        nzm |= ((q.x != 0u) ? 1u : 0u) << (31 - 4 * i) | ((q.y != 0u) ? 1u : 0u) << (30 - 4 * i) |
+               ((q.z != 0u) ? 1u : 0u) << (29 - 4 * i) | ((q.w != 0u) ? 1u : 0u) << (28 - 4 * i);
+      }
+      // tau: the bin where the count from the top reaches k (lane ft's group,
+      // then its bins, one per lane)
+      const int k = P.top_k;
+      const int incl = wave_incl_scan_i(lsum);
+      const unsigned long long hit = __builtin_amdgcn_ballot_w64(incl >= k);
+      const int ft = hit ? __ffsll((unsigned long long)hit) - 1 : 0;
+      const int above_ft = __builtin_amdgcn_readlane(incl - lsum, ft);
+      const int top_ft = 32 * (kWave - 1 - ft) + 31;
+      const int cj = lane < 32 ? (int)hist[fast_idx(top_ft - lane)] : 0;
+      const unsigned long long hit2 =
+          __builtin_amdgcn_ballot_w64(lane < 32 && above_ft + wave_incl_scan_i(cj) >= k);
+      const int btau = top_ft - (hit2 ? __ffsll((unsigned long long)hit2) - 1 : 0);
+      // the row maximum: the top non-empty bin
+      const int fm = __ffsll((unsigned long long)__builtin_amdgcn_ballot_w64(nzm != 0u)) - 1;
+      const int bmax =
+          32 * (kWave - 1 - fm) + 31 - (__ffs((int)__builtin_amdgcn_readlane((int)nzm, fm)) - 1);
+      auto level = [&](int b) {
+        unsigned key = kb + ((unsigned)b << kLow);
+        if (!(key & 0x80000000u)) key |= kLowMask;
+        return float_of_key(key);
+      };
+      const float c = P.c;
+      const float m = level(bmax);
+      const float R = ref_of(m, c);
+      // the levels from tau up: this lane's non-empty bins at or above btau,
+      // in descending order; their masses replace their counts
+      const unsigned ftmask = 0xFFFFFFFFu >> (31 - (top_ft - btau));  // lane ft's bins down to btau
+      const unsigned live = lane < ft ? nzm : (lane == ft ? nzm & ftmask : 0u);
+      float esum = 0.0f;
+      for (unsigned mm = live; mm != 0u; mm &= mm - 1u) {
+        const int b = top - (__ffs((int)mm) - 1);
+        unsigned* hw = &hist[fast_idx(b)];
+        const float e = (float)*hw * fast_exp2(fmaf(level(b), c, -R));
+        *hw = __float_as_uint(e);
+        esum += e;
+      }
+      const float eincl = wave_incl_scan(esum);
+      const float S_k = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                      __builtin_bit_cast(int, eincl), kWave - 1));
+      // kept: the mass of the strictly larger levels over S_k below top_p
+      // (every level from tau up when top_p is 1)
+      const bool all = !(P.top_p < 1.0f);
+      float above = eincl - esum, kincl = 0.0f;
+      int bk = -1;
+      for (unsigned mm = live; mm != 0u; mm &= mm - 1u) {
+        const int b = top - (__ffs((int)mm) - 1);
+        const float e = __uint_as_float(hist[fast_idx(b)]);
+        if (all || above / S_k < P.top_p) {
+          bk = b;
+          kincl = above + e;
+        }
+        above += e;
+      }
+      const unsigned long long kept_lanes = __builtin_amdgcn_ballot_w64(bk >= 0);
+      if (hit != 0ull && hit2 != 0ull && kept_lanes != 0ull) {
+        const int lk = 63 - __clzll((long long)kept_lanes);
+        const float theta = level(__builtin_amdgcn_readlane(bk, lk));
+        const float S_f = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                        __builtin_bit_cast(int, kincl), lk));
+        if (lane == 0) {
+          P.rowres[unit] = RowRes{m, S_f, theta, 0};
+          s_theta[ri] = theta;
+        }
+        state = kFiltFast;
+      }
+    }
+    if (lane == 0) s_state[ri] = state;
+  }
+  __syncthreads();  // every row's state and theta are in
+  const int state = s_state[ri];
+  const bool lists = is_target && !P.skip_bonus && P.kept != nullptr;
+  bool partial = false;
+  if (state == kFiltFast) {
+    const float theta = s_theta[ri];
+    if (lists) {
+      // the kept set (no count-only tie class at or above theta): each slot's
+      // kept entries take consecutive places of the list
+      unsigned* kl = P.kept + (size_t)row * kKeptWords;
+#pragma unroll
+      for (int j = 0; j < kHalfSlots; ++j) {
+        const bool in = ((vmask >> j) & 1u) && __uint_as_float(ev[j].x) >= theta;
+        const unsigned long long msk = __builtin_amdgcn_ballot_w64(in);
+        if (msk != 0ull) {
+          int base = 0;
+          if (lane == 0) base = atomicAdd(&s_kn[ri], __builtin_popcountll(msk));
+          base = __builtin_amdgcn_readfirstlane(base);
+          const int at = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                    (unsigned)(msk >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)msk, 0u));
+          if (in && at < kExplicitMax) *reinterpret_cast<uint2*>(kl + 2 + 2 * at) = ev[j];
+        }
+      }
+      partial = h == 0 &&
+                __builtin_amdgcn_ballot_w64(imp && __uint_as_float(hd.y) >= theta) != 0ull;
+    }
+    // the records go back to zero: every slot's span (entries past a chunk's
+    // count are zero already), then the headers
+    unsigned* recw = P.rec + (size_t)unit * C * P.rec_words;
+#pragma unroll
+    for (int j = 0; j < kHalfSlots; ++j) {
+      const int s = 2 * j + h;
+      if (s < nslots)
+        *reinterpret_cast<uint2*>(recw + __builtin_amdgcn_readlane(soff, s) + 2 * lane) =
+            make_uint2(0u, 0u);
+    }
+    if (h == 0 && lane < C) {
+      uint4* hp = reinterpret_cast<uint4*>(recw + (size_t)lane * P.rec_words);
+      hp[0] = make_uint4(0u, 0u, 0u, 0u);
+      hp[1] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  __syncthreads();  // the kept counts are in
+  if (state == kFiltFast && lists && h == 0 && lane == 0) {
+    unsigned* kl = P.kept + (size_t)row * kKeptWords;
+    const int n = s_kn[ri];
+    kl[0] = (unsigned)min(n, kExplicitMax);
+    kl[1] = (partial || n > kExplicitMax) ? 1u : 0u;
+  }
   for (int w = 0; w < kFiltRowsPerBlock; ++w) {
-    if (s_fail[w]) {
+    if (s_state[w] == kFiltGeneral) {
       __syncthreads();  // the LDS of the histograms, or of the previous row, is free
       filter_row_block<DT>(P, blockIdx.x * kFiltRowsPerBlock + w, &s_fh[0][0]);
     }
