@@ -1753,16 +1753,21 @@ __device__ void draw_unit(const Params& P, int idx) {
   if (greedy && ch != 0) return;  // one block decides a greedy sequence
   const bool lists = P.filt && P.kept != nullptr;
   // filtered: whether every target row's kept list is complete, so that the
-  // draw, whichever row it takes, needs no tile sums
+  // draw, whichever row it takes, needs no tile sums. The first block resolves
+  // it after its decision, so that the two sets of loads overlap; the others
+  // leave at once when it holds.
   bool solo = false;
+  int inc = 0;
   if (lists && !greedy) {
-    int inc = 0;
     for (int r = tid; r <= kb; r += kThreads)
       inc |= (int)P.kept[(size_t)(d0 + b + r) * kKeptWords + 1];
-    solo = __syncthreads_or(inc) == 0;
-    if (solo && ch != 0) return;
+    if (ch != 0) {
+      solo = __syncthreads_or(inc) == 0;
+      if (solo) return;
+    }
   }
   const Job j = decide<DT>(P, b, d0, kb, greedy, ch == 0, S);
+  if (lists && !greedy && ch == 0) solo = __syncthreads_or(inc) == 0;
   if (greedy) {
     // the only reader of these partials returns them to zero
     __syncthreads();
