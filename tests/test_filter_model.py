@@ -17,29 +17,39 @@ rows).
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 import workloads as W
 from filter_model import filter_row
 
 
-def _rows(name, dtype):
+def _rows(name, dtype, shift=0.0):
+    """Full-size rows of a workload; ``shift`` moves every logit (rounded back
+    to the storage type), so that the candidates can be negative values."""
     w = W.make(name, B=2)
     rows = np.concatenate([oracle.decode_logits(W.raw_numpy(w["draft"]), dtype),
                            oracle.decode_logits(W.raw_numpy(w["target"]), dtype)])
+    if shift:
+        t = torch.from_numpy(rows.astype(np.float32) + np.float32(shift))
+        rows = t.to(torch.bfloat16 if dtype == "bf16" else torch.float16).to(torch.float64).numpy()
     return rows, w["temperature"]
 
 
-CASES = [("f16_B256_K4_V151936_topk50_topp0.9", "f16", 50, 0.9),
-         ("f16_B256_K4_V151936_topk50_topp0.9", "f16", 5, 1.0),
-         ("f16_B256_K4_V151936_topk50_topp0.9", "f16", 200, 0.95),
-         (W.HEADLINE, "bf16", 50, 0.9),
-         (W.HEADLINE, "bf16", 1, 1.0)]
+CASES = [("f16_B256_K4_V151936_topk50_topp0.9", "f16", 50, 0.9, 0.0),
+         ("f16_B256_K4_V151936_topk50_topp0.9", "f16", 5, 1.0, 0.0),
+         ("f16_B256_K4_V151936_topk50_topp0.9", "f16", 200, 0.95, 0.0),
+         ("f16_B256_K4_V151936_topk50_topp0.9", "f16", 50, 0.9, -60.0),
+         (W.HEADLINE, "bf16", 50, 0.9, 0.0),
+         (W.HEADLINE, "bf16", 1, 1.0, 0.0),
+         (W.HEADLINE, "bf16", 50, 0.9, -60.0)]
 
 
-@pytest.mark.parametrize("name,dtype,top_k,top_p", CASES)
-def test_usual_path_matches_oracle(name, dtype, top_k, top_p):
-    rows, T = _rows(name, dtype)
+@pytest.mark.parametrize("name,dtype,top_k,top_p,shift", CASES)
+def test_usual_path_matches_oracle(name, dtype, top_k, top_p, shift):
+    """shift -60 makes every candidate negative: a negative level's key has its
+    low bits set, which the bins and the level values must respect."""
+    rows, T = _rows(name, dtype, shift)
     checked = near = 0
     for r in rows:
         prob, lse, margin = oracle.filtered_distribution(r, T, top_k, top_p)
@@ -55,7 +65,7 @@ def test_usual_path_matches_oracle(name, dtype, top_k, top_p):
         R = np.float32(np.float32(r.max()) * c)
         np.testing.assert_allclose(kept * 2.0 ** float(R), np.exp(lse), rtol=1e-5)
         checked += 1
-    print(f"{dtype} k={top_k} p={top_p}: checked={checked} near={near}")
+    print(f"{dtype} k={top_k} p={top_p} shift={shift}: checked={checked} near={near}")
     assert checked >= len(rows) - 2
 
 

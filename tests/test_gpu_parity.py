@@ -192,6 +192,16 @@ def test_filters_wide_candidate_range(dtype, peak):
     _check(w, api="ragged", diag=True, tag=f"wide range {dtype}")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_filters_negative_candidates(dtype):
+    """Every logit moved down by 60, so the top-k candidates are negative
+    values, whose keys carry set low bits on the level histogram."""
+    w = _filtered(50, 0.9, B=6, V=20000, dtype=dtype)
+    for key in ("draft", "target"):
+        w[key] = (w[key].float() - 60.0).to(w[key].dtype)
+    _check(w, api="ragged", diag=True, tag=f"negative {dtype}")
+
+
 def test_filters_masked_rows_and_scalar_path():
     """Rows with most ids at -inf (fewer finite logits than k in some rows), on
     an odd V (scalar path)."""
