@@ -831,6 +831,11 @@ def bench_lmhead(args, sv):
     tok_out, _ = sv.spec_verify_ragged(None, lq, None, u_draft, zeros_cu, None, n_draft, V, T, 0,
                                        1.0, total_draft_rows=0)
     toks = tok_out.clone().view(B, K)
+    # greedy drafting for the greedy call: each draft row's argmax (the
+    # library's K = 0 call at temperature 0)
+    g_out, _ = sv.spec_verify_ragged(None, lq, None, None, zeros_cu, None, n_draft, V, 0.0, 0,
+                                     1.0, total_draft_rows=0)
+    toks_greedy = g_out.clone().view(B, K)
     del lq, zeros_cu
     ws = sv.make_lmhead_workspace(B, K, V, dev)
     out = torch.empty(B, K + 1, dtype=torch.int32, device=dev)
@@ -859,13 +864,44 @@ def bench_lmhead(args, sv):
                     for k in range(args.steps)])
     hev.close()
     stage_ms = per.mean(axis=0).tolist()
+    n_sampling = num.cpu().numpy()
+    # the same shape verified greedily: the target rows alone, no draw rows
+    def greedy_step(ev=None):
+        sv.spec_verify_lmhead(None, None, hp, wp, toks_greedy, None, B, K, V, 0.0,
+                              out_tokens=out, num_accepted=num, workspace=ws, stage_events=ev)
+
+    for _ in range(args.warmup):
+        greedy_step()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        greedy_step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_greedy = start.elapsed_time(stop) / args.steps
+    hev = HipEvents(nst * args.steps)
+    for k in range(args.steps):
+        greedy_step(hev.handles[nst * k:nst * (k + 1)])
+    torch.cuda.synchronize()
+    gper = np.array([[hev.elapsed_ms(nst * k + i, nst * k + i + 1) for i in range(nst - 1)]
+                     for k in range(args.steps)])
+    hev.close()
+    g_stage = gper.mean(axis=0).tolist()
+    ng = num.cpu().numpy()
     rows = B * (K + 1)
     flops_t = 2.0 * rows * V * dp
     flops_d = 2.0 * n_draft * V * dq
+    greedy = {"ms_per_step": ms_greedy, "rows_per_s": rows / (ms_greedy * 1e-3),
+              "statistics_gemm_ms": g_stage[0],
+              "statistics_gemm_frac_of_peak": flops_t / (g_stage[0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+              "stage_ms": dict(zip(LM_STAGES, g_stage)),
+              "mean_accepted": float(ng[ng >= 0].mean()) if (ng >= 0).any() else None,
+              "errors": int((ng < 0).sum()),
+              "note": "temperature 0: target rows only (argmax partials), greedy draft tokens"}
     t_ms = stage_ms[0]
     achieved = (flops_t + flops_d) / (t_ms * 1e-3) / 1e12
     weight_bytes = 2.0 * V * (dq + dp)
-    n = num.cpu().numpy()
+    n = n_sampling
     rec_out = {
         "metric": f"LM-head verification ({W.LMHEAD_NAME}): verified rows/s, hidden states and "
                   "LM-head weights in, logit rows never stored",
@@ -885,6 +921,7 @@ def bench_lmhead(args, sv):
         "weight_bytes_per_pass": weight_bytes,
         "stage_ms": dict(zip(LM_STAGES, stage_ms)),
         "acceptance": {"mean_accepted": float(n.mean()), "errors": int((n < 0).sum())},
+        "greedy": greedy,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec_out), flush=True)

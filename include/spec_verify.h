@@ -349,8 +349,12 @@ int spec_verify_multi(const void* draft_logits, const void* target_logits,
  *   hidden_target  bf16 [B*(K+1), d_target]
  *   weight_target  bf16 [V, d_target]
  *   draft_tokens   int32 [B, K]; uniforms float [B, K+1]; outputs as spec_verify.
- * Sampling only: temperature finite and > 0; no top-k / top-p. d_draft and
- * d_target are multiples of 8 (>= 8); the four matrices are 16-byte aligned.
+ * temperature finite and >= 0; no top-k / top-p. Temperature 0 verifies
+ * greedily (accept iff the draft id is the target row's argmax, the lowest id
+ * on ties; the correction or bonus token is that argmax): no draft row is
+ * formed and no uniform read, so hidden_draft, weight_draft and uniforms may
+ * be NULL and d_draft is not checked. d_draft (sampling) and d_target are
+ * multiples of 8 (>= 8); the matrices given are 16-byte aligned.
  * Row-major throughout. The workspace is sized by
  * spec_verify_lmhead_workspace_bytes(B, K, V), 256-byte aligned; its first
  * spec_verify_lmhead_zero_bytes(B, K, V) bytes must be zero before the first
@@ -361,7 +365,9 @@ int spec_verify_multi(const void* draft_logits, const void* target_logits,
  * (may be NULL; n_stage_events of them, caller-created) are recorded on
  * `stream`: before the statistics GEMMs (draft and target rows, one launch),
  * after them, after the merge and decision, after the draw rows' GEMMs, and
- * every further one after the draw. Errors as spec_verify. */
+ * every further one after the draw (greedy calls record the same events; the
+ * decision kernel and the draw rows' GEMMs are not launched). Errors as
+ * spec_verify. */
 size_t spec_verify_lmhead_workspace_bytes(int B, int K, int V);
 size_t spec_verify_lmhead_zero_bytes(int B, int K, int V);
 int spec_verify_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
@@ -375,7 +381,8 @@ int spec_verify_lmhead(const void* hidden_draft, const void* weight_draft, int d
  * decisions were made on (every pointer of diag may be NULL; diag may be NULL):
  *   logits_draft   float [B*K, V]      the draft rows' logits as the statistics
  *   logits_target  float [B*(K+1), V]  GEMM formed them (fp32 accumulation),
- *                                      before any reduction
+ *                                      before any reduction (a greedy call
+ *                                      forms no draft logits)
  * Device memory owned by the caller. Writing them costs 4 bytes per logit of
  * HBM traffic; the default call writes none. */
 typedef struct sv_lmhead_diag {

@@ -50,10 +50,14 @@ def verify_lmhead(hidden_draft, weight_draft, hidden_target, weight_target, draf
     hidden_draft [B*K, Dq], weight_draft [V, Dq], hidden_target [B*(K+1), Dp],
     weight_target [V, Dp]; the logits are ``lmhead_logits`` of each pair (times
     its scale), then ``verify`` runs on them as float64 rows (dense layout,
-    sampling at ``temperature``).
+    sampling at ``temperature``; temperature 0 verifies greedily, reading no
+    draft rows (R7), so the draft pair may be None).
     """
-    lq = (lmhead_logits(hidden_draft, weight_draft, draft_scale) if K > 0
-          else np.zeros((0, V), dtype=np.float64))
+    if temperature == 0.0:
+        lq = None
+    else:
+        lq = (lmhead_logits(hidden_draft, weight_draft, draft_scale) if K > 0
+              else np.zeros((0, V), dtype=np.float64))
     lp = lmhead_logits(hidden_target, weight_target, target_scale)
     return verify(lq, lp, draft_tokens, uniforms, B=B, V=V, K=K, dtype="f64",
                   temperature=temperature, want_diag=want_diag)

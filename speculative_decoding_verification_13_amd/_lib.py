@@ -418,18 +418,21 @@ def spec_verify_lmhead(hidden_draft, weight_draft, hidden_target, weight_target,
     hipEvent_t handles (ints) recorded between the stages. ``logits_draft``
     [B*K, V] and ``logits_target`` [B*(K+1), V] (float32 device tensors, or
     None) receive the logits the statistics GEMM formed (the diag entry point).
-    Returns (out_tokens [B, K+1], num_accepted [B])."""
+    Temperature 0 verifies greedily: the draft pair and the uniforms may be
+    None, and no draft logits are formed. Returns (out_tokens [B, K+1],
+    num_accepted [B])."""
     B, K, V = int(B), int(K), int(V)
+    greedy = float(temperature) == 0.0  # reads no draft rows and no uniforms
     dev = hidden_target.device
     dq = 0 if hidden_draft is None else int(hidden_draft.shape[-1])
     dp = int(hidden_target.shape[-1])
     bf = torch.bfloat16
     _expect(hidden_target, "hidden_target", bf, B * (K + 1) * dp)
     _expect(weight_target, "weight_target", bf, V * dp)
-    _expect(hidden_draft, "hidden_draft", bf, B * K * dq, allow_none=K == 0)
-    _expect(weight_draft, "weight_draft", bf, V * dq, allow_none=K == 0)
+    _expect(hidden_draft, "hidden_draft", bf, B * K * dq, allow_none=K == 0 or greedy)
+    _expect(weight_draft, "weight_draft", bf, V * dq, allow_none=K == 0 or greedy)
     _expect(draft_tokens, "draft_tokens", torch.int32, B * K, allow_none=K == 0)
-    _expect(uniforms, "uniforms", torch.float32, B * (K + 1))
+    _expect(uniforms, "uniforms", torch.float32, B * (K + 1), allow_none=greedy)
     if out_tokens is None:
         out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
     if num_accepted is None:

@@ -15,6 +15,12 @@
 //   k_draw            the decision again, the outputs, and the inverse-CDF draw
 //                     over the stored rows (the same kernel as the logit path)
 //
+// Greedy verification (temperature 0) reads no draft rows: k_lm_gemm<true>
+// runs on the target rows alone, with per tile the packed (max, argmax with
+// the lowest id on ties, NaN / +inf seen) partial of the logit path's greedy
+// rows; k_lm_merge_am merges them, and k_draw decides and writes the outputs
+// (the correction or bonus token is the argmax, so no row is formed again).
+//
 // Pages (by title, section): Hung-yi Lee lecture-16 notes (the target model
 // scores every drafted position in one forward pass; the logits are its last
 // layer's output); aivaro.ru answer 289 "Как работает speculative decoding на
@@ -98,7 +104,8 @@ struct LmPair {
 // g runs on XCD g % 8, and the row tiles of one vocabulary tile are
 // consecutive blocks of one XCD, so its weight tile is fetched into that XCD's
 // L2 once and read from there by the other row tiles.
-template <bool STATS, int WN, int NB>
+// GREEDY (statistics only): (max, argmax, NaN/+inf) partials instead of (max, sum).
+template <bool STATS, int WN, int NB, bool GREEDY = false>
 __global__ __launch_bounds__(2 * WN * kWave, 2) void k_lm_gemm(const LmPair PR) {
   using T = LmTile<WN, NB>;
   constexpr int kLmNB = NB;
@@ -114,7 +121,7 @@ __global__ __launch_bounds__(2 * WN * kWave, 2) void k_lm_gemm(const LmPair PR) 
   uint16_t* const sA = sAB;
   uint16_t* const sB = sAB + kLmBM * kLmLds;
   __shared__ float s_pm[kLmSlots][kLmBM];
-  __shared__ float s_ps[kLmSlots][kLmBM];
+  __shared__ float s_ps[kLmSlots][kLmBM];  // greedy: the argmax, bit 31 NaN or +inf seen
   __shared__ int s_tok[kLmBM];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -264,6 +271,32 @@ __global__ __launch_bounds__(2 * WN * kWave, 2) void k_lm_gemm(const LmPair PR) 
         }
         const int cb = v0 + wn * 32 * kLmNB + sl * 64 + h;  // first id of this lane's half row
         const int rl = wm * 64 + a * 32 + r;
+        if constexpr (GREEDY) {
+          // the largest logit of the 32 ids (NaN never wins), its lowest id
+          // (none while every value is -inf) and whether any is NaN or +inf,
+          // then with lane l ^ 1, the other half of the slice's 64 ids
+          float mx = kNegInf;
+          int bd = 0;
+#pragma unroll
+          for (int j = 0; j < 32; ++j) {
+            if (cb + j >= G.V) x[j] = kNegInf;
+            bd |= is_nan_or_posinf(x[j]) ? 1 : 0;
+            mx = fmaxf(mx, x[j]);
+          }
+          int jm = 32;
+#pragma unroll
+          for (int j = 31; j >= 0; --j) jm = (x[j] == mx) ? j : jm;
+          int ai = (mx > kNegInf) ? cb + jm : INT_MAX;
+          const float omx = dpp_f<0xB1>(mx);  // quad_perm [1,0,3,2]: lane l ^ 1
+          const int oai = dpp_i<0xB1>(ai);
+          bd |= dpp_i<0xB1>(bd);
+          argmax_merge(mx, ai, omx, oai);
+          if ((lane & 1) == 0) {
+            s_pm[wn * (kLmNB / 2) + sl][rl] = mx;
+            s_ps[wn * (kLmNB / 2) + sl][rl] = __uint_as_float((unsigned)ai | ((unsigned)bd << 31));
+          }
+          continue;
+        }
         const int tok = s_tok[rl];
         if (tok >= cb && tok < cb + 32) G.tok_logits[G.unit0 + m0 + rl] = E[r * kEp + h + (tok - cb)];
         float mx = kNegInf;
@@ -286,10 +319,24 @@ __global__ __launch_bounds__(2 * WN * kWave, 2) void k_lm_gemm(const LmPair PR) 
     }
     __syncthreads();
     if (tid < kLmBM && m0 + tid < G.M) {
-      float mm = s_pm[0][tid], ss = s_ps[0][tid];
+      if constexpr (GREEDY) {
+        // the slices in increasing id order: the strict compare keeps the first maximum
+        float mm = s_pm[0][tid];
+        const unsigned p0 = __float_as_uint(s_ps[0][tid]);
+        int ai = (int)(p0 & 0x7fffffffu), bd = (int)(p0 >> 31);
 #pragma unroll
-      for (int q = 1; q < kLmSlots; ++q) merge_ms(mm, ss, s_pm[q][tid], s_ps[q][tid], c);
-      G.part[(size_t)(G.unit0 + m0 + tid) * G.NT + vt] = pack_ms(mm, ss);
+        for (int q = 1; q < kLmSlots; ++q) {
+          const unsigned pq = __float_as_uint(s_ps[q][tid]);
+          argmax_merge(mm, ai, s_pm[q][tid], (int)(pq & 0x7fffffffu));
+          bd |= (int)(pq >> 31);
+        }
+        G.part[(size_t)(G.unit0 + m0 + tid) * G.NT + vt] = pack_am(mm, ai, bd);
+      } else {
+        float mm = s_pm[0][tid], ss = s_ps[0][tid];
+#pragma unroll
+        for (int q = 1; q < kLmSlots; ++q) merge_ms(mm, ss, s_pm[q][tid], s_ps[q][tid], c);
+        G.part[(size_t)(G.unit0 + m0 + tid) * G.NT + vt] = pack_ms(mm, ss);
+      }
     }
   }
 }
@@ -324,6 +371,47 @@ __global__ __launch_bounds__(kThreads) void k_lm_merge(const unsigned long long*
 #pragma unroll
     for (int w = 1; w < kThreads / kWave; ++w) merge_ms(mm, ss, s_m[w], s_s[w], c);
     slots[u] = pack_ms(mm, ss);
+  }
+}
+
+// Per greedy statistics unit (from unit0): its vocabulary tiles' (max,
+// argmax, NaN/+inf) partials merged into one, the lowest id on ties, stored
+// as the unit's only chunk; the tiles' partials go back to zero.
+__global__ __launch_bounds__(kThreads) void k_lm_merge_am(const unsigned long long* part0,
+                                                           unsigned long long* slots, int NT,
+                                                           long long unit0) {
+  __shared__ float s_v[kThreads / kWave];
+  __shared__ int s_i[kThreads / kWave], s_b[kThreads / kWave];
+  const long long u = unit0 + blockIdx.x;
+  unsigned long long* part = const_cast<unsigned long long*>(part0) + u * NT;
+  const int tid = threadIdx.x;
+  const int per = (NT + kThreads - 1) / kThreads;
+  float v = kNegInf;
+  int i = INT_MAX, bad = 0;
+  for (int k = tid * per; k < min(NT, (tid + 1) * per); ++k) {
+    float ov;
+    int oi, ob;
+    unpack_am(part[k], ov, oi, ob);
+    argmax_merge(v, i, ov, oi);
+    bad |= ob;
+    part[k] = 0ull;
+  }
+  wave_argmax(v, i, bad);
+  if ((tid & (kWave - 1)) == 0) {
+    s_v[tid / kWave] = v;
+    s_i[tid / kWave] = i;
+    s_b[tid / kWave] = bad;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float vv = s_v[0];
+    int ii = s_i[0], bb = s_b[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / kWave; ++w) {
+      argmax_merge(vv, ii, s_v[w], s_i[w]);
+      bb |= s_b[w];
+    }
+    slots[u] = pack_am(vv, ii, bb);
   }
 }
 
@@ -403,14 +491,18 @@ int run_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
                int n_stage_events, float* logits_draft, float* logits_target) {
   using namespace sv;
   if (B < 0 || K < 0 || K > SV_MAX_K || V < 1) return SV_EINVAL;
-  if (!(temperature > 0.0f) || __builtin_isinf(temperature)) return SV_EINVAL;
-  if (d_target < 8 || d_target % 8 != 0 || (K > 0 && (d_draft < 8 || d_draft % 8 != 0)))
+  if (!(temperature >= 0.0f) || __builtin_isinf(temperature)) return SV_EINVAL;
+  // temperature 0: greedy verification, which reads no draft rows and no uniforms
+  const bool greedy = temperature == 0.0f;
+  if (d_target < 8 || d_target % 8 != 0 ||
+      (!greedy && K > 0 && (d_draft < 8 || d_draft % 8 != 0)))
     return SV_EINVAL;
   if (B == 0) return SV_OK;
   if (hidden_target == nullptr || weight_target == nullptr || out_tokens == nullptr ||
-      num_accepted == nullptr || uniforms == nullptr)
+      num_accepted == nullptr || (!greedy && uniforms == nullptr))
     return SV_EINVAL;
-  if (K > 0 && (hidden_draft == nullptr || weight_draft == nullptr || draft_tokens == nullptr))
+  if (K > 0 && (draft_tokens == nullptr ||
+                (!greedy && (hidden_draft == nullptr || weight_draft == nullptr))))
     return SV_EINVAL;
   const void* ptrs[4] = {hidden_draft, weight_draft, hidden_target, weight_target};
   for (const void* p : ptrs)
@@ -443,8 +535,8 @@ int run_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
   P.V = V;
   P.total_draft = total_draft;
   P.rows = rows;
-  P.all_greedy = 0;
-  P.c = (float)(1.4426950408889634074 / (double)temperature);
+  P.all_greedy = greedy ? 1 : 0;
+  P.c = greedy ? 0.0f : (float)(1.4426950408889634074 / (double)temperature);
   P.chunks = 1;
   P.nvec = L.nvec;
   P.dchunks = L.dchunks;
@@ -489,7 +581,7 @@ int run_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
     G.c = P.c;
     G.out_step = 1;
     G.out_row0 = 0;
-    if (total_draft > 0) {
+    if (total_draft > 0 && !greedy) {
       auto [MT, blocks] = grid_of(total_draft, L.NT);
       G.H = static_cast<const uint16_t*>(hidden_draft);
       G.W = static_cast<const uint16_t*>(weight_draft);
@@ -512,12 +604,34 @@ int run_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
     G.unit0 = total_draft;
     G.target = 1;
     G.out = logits_target;
-    S.g[1] = G;
+    if (blocks_stats == 0) {  // the target rows alone
+      S.g[0] = G;
+      S.n0 = (int)blocks;
+    } else {
+      S.g[1] = G;
+    }
     blocks_stats += blocks;
   }
-  hipLaunchKernelGGL((k_lm_gemm<true, kLmStatsWN, kLmStatsNB>), dim3(blocks_stats),
-                     dim3(LmTile<kLmStatsWN, kLmStatsNB>::kThreads), 0, stream, S);
+  if (greedy)
+    hipLaunchKernelGGL((k_lm_gemm<true, kLmStatsWN, kLmStatsNB, true>), dim3(blocks_stats),
+                       dim3(LmTile<kLmStatsWN, kLmStatsNB>::kThreads), 0, stream, S);
+  else
+    hipLaunchKernelGGL((k_lm_gemm<true, kLmStatsWN, kLmStatsNB>), dim3(blocks_stats),
+                       dim3(LmTile<kLmStatsWN, kLmStatsNB>::kThreads), 0, stream, S);
   if (hipGetLastError() != hipSuccess || !stage()) return SV_EHIP;
+  if (greedy) {
+    // the target rows' argmax partials; the decision and the outputs are the
+    // draw kernel's (the stage events keep their places)
+    hipLaunchKernelGGL(k_lm_merge_am, dim3((unsigned)rows), dim3(kThreads), 0, stream, part,
+                       P.slots, L.NT, (long long)total_draft);
+    if (hipGetLastError() != hipSuccess || !stage() || !stage()) return SV_EHIP;
+    Plan DL{};
+    DL.draw_blocks = (long long)B * L.dchunks;
+    if (launch_draw_f32(L.nvec != V, P, DL, stream) != hipSuccess) return SV_EHIP;
+    while (e < n_stage_events && stage_events != nullptr)
+      if (!stage()) return SV_EHIP;
+    return SV_OK;
+  }
   hipLaunchKernelGGL(k_lm_merge, dim3((unsigned)(total_draft + rows)), dim3(kThreads), 0, stream,
                      part, P.slots, L.NT, P.c);
   if (hipGetLastError() != hipSuccess) return SV_EHIP;

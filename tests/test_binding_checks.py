@@ -98,3 +98,8 @@ def test_lmhead_checks():
         sv.spec_verify_lmhead(hq.float(), wq, hp, wp, toks, u, B, K, Vl, 1.0)
     with pytest.raises(ValueError, match="uniforms"):
         sv.spec_verify_lmhead(hq, wq, hp, wp, toks, u[:-1], B, K, Vl, 1.0)
+    # sampling needs the draft pair and the uniforms; only greedy (T = 0) may omit them
+    with pytest.raises(ValueError, match="uniforms"):
+        sv.spec_verify_lmhead(hq, wq, hp, wp, toks, None, B, K, Vl, 1.0)
+    with pytest.raises(ValueError, match="hidden_draft"):
+        sv.spec_verify_lmhead(None, wq, hp, wp, toks, u, B, K, Vl, 1.0)

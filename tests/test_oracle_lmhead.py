@@ -69,6 +69,31 @@ def test_verify_lmhead_with_identity_head_is_verify_on_the_hidden_rows():
     assert np.array_equal(a["num_accepted"], b["num_accepted"])
 
 
+def test_greedy_verify_lmhead_by_hand():
+    """Temperature 0 on an identity head: the target logits are the hidden
+    rows, each position's check is draft token == the row's argmax (the lowest
+    id on ties), and the emitted token at the first mismatch, or the bonus,
+    is that argmax ([P3] section "Cùng phân bố không có nghĩa cùng chuỗi mỗi
+    lần": greedy decoding checks the argmax). No draft hidden states are read."""
+    rng = np.random.default_rng(11)
+    B, K, V = 3, 4, 16
+    hp = rng.integers(-8, 9, size=(B * (K + 1), V)).astype(np.int8)
+    eye = np.eye(V, dtype=np.int8)
+    am = np.argmax(hp.astype(np.int64), axis=1).reshape(B, K + 1)  # first maximum
+    toks = am[:, :K].copy()
+    toks[1, 1] = (toks[1, 1] + 1) % V  # sequence 1 stops at position 1
+    toks[2, 0] = (toks[2, 0] + 3) % V  # sequence 2 stops at position 0
+    res = oracle.verify_lmhead(None, None, hp, eye, toks.reshape(-1), np.zeros(B * (K + 1)),
+                               B=B, K=K, V=V, temperature=0.0)
+    want_n = [K, 1, 0]
+    want = np.full((B, K + 1), -1)
+    for b, n in enumerate(want_n):
+        want[b, :n] = toks[b, :n]
+        want[b, n] = am[b, n]
+    assert res["num_accepted"].tolist() == want_n
+    assert np.array_equal(res["out_tokens"].reshape(B, K + 1), want)
+
+
 def test_workload_recipe_shares_the_draft_directions():
     """The generator's target logits at position i < K are the draft logits
     plus the term of the target's extra hidden entries (checked through the
