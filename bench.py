@@ -914,7 +914,7 @@ def bench_lmhead(args, sv):
                    "entry_point": "spec_verify_lmhead"},
         "tflops_per_step": (flops_t + flops_d) / 1e12,
         "effective_TFLOPs": (flops_t + flops_d) / (ms_step * 1e-3) / 1e12,
-        "roofline": {"kernel": "k_lm_gemm<true> (draft and target rows, one launch)",
+        "roofline": {"kernel": "k_lm_stats (draft and target rows, one launch)",
                      "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
                      "algorithmic_flops_per_launch": flops_t + flops_d, "avg_launch_ms": t_ms},

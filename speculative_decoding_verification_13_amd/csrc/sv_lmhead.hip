@@ -5,17 +5,17 @@
 // the final draw needs per sequence (p_n, and q_n for a residual) are formed
 // again and kept, as fp32.
 //
-//   k_lm_gemm<true>   draft rows, then target rows: per (row, 256-id vocab
+//   k_lm_stats        draft rows, then target rows: per (row, 384-id vocab
 //                     tile) the packed (max, sum of 2^(l*c - R)) partial, and
 //                     the logit at the row's token
 //   k_lm_merge        per row: the vocabulary tiles' partials merged into one
 //                     (and returned to zero)
 //   k_lm_plan         per sequence: the decision, naming the draw's rows
-//   k_lm_gemm<false>  those rows' logits into a [2B, V] fp32 array
+//   k_lm_rows         those rows' logits into a [2B, V] fp32 array
 //   k_draw            the decision again, the outputs, and the inverse-CDF draw
 //                     over the stored rows (the same kernel as the logit path)
 //
-// Greedy verification (temperature 0) reads no draft rows: k_lm_gemm<true>
+// Greedy verification (temperature 0) reads no draft rows: k_lm_stats<true>
 // runs on the target rows alone, with per tile the packed (max, argmax with
 // the lowest id on ties, NaN / +inf seen) partial of the logit path's greedy
 // rows; k_lm_merge_am merges them, and k_draw decides and writes the outputs
@@ -37,19 +37,15 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Block tile: 128 rows x (WN * 32 * NB) vocabulary ids, 64 hidden elements
-// per step. Waves in a 2 x WN arrangement, each a 64 x (32 * NB) sub-tile of
-// 2 x NB 32 x 32 MFMA tiles. LDS rows carry 8 bf16 of padding so that the 32 lanes reading
-// one operand column touch distinct banks.
+// Draw rows' GEMM (k_lm_rows). Block tile: 128 rows x (WN * 32 * NB)
+// vocabulary ids, 64 hidden elements per step. Waves in a 2 x WN arrangement,
+// each a 64 x (32 * NB) sub-tile of 2 x NB 32 x 32 MFMA tiles. LDS rows carry
+// 8 bf16 of padding so that the 32 lanes reading one operand column touch
+// distinct banks. The GEMM is HBM-bound (one live row per sequence and
+// model): eight waves of 64 x 128, a 512-id tile, keep the most weight bytes
+// in flight per block (measured 303-306 us against 318-320 with four such
+// waves and 357 with four waves of 64 x 64).
 constexpr int kLmBM = 128;
-// Shapes of the two GEMMs (waves along the vocabulary, 32-id MFMA tiles per
-// wave along it). The statistics GEMM takes eight waves of 64 x 64: a 256-id
-// tile, so each row tile of hidden states is re-read by half as many blocks
-// as with 128 ids, at four waves per SIMD. The draw rows' GEMM is HBM-bound
-// (one live row per sequence and model): eight waves of 64 x 128, a 512-id
-// tile, keep the most weight bytes in flight per block (measured 303-306 us
-// against 318-320 with four such waves and 357 with four waves of 64 x 64).
-constexpr int kLmStatsWN = 4, kLmStatsNB = 2;
 constexpr int kLmRowsWN = 4, kLmRowsNB = 4;
 #ifndef SV_LM_BK
 #define SV_LM_BK 64
@@ -64,12 +60,10 @@ template <int WN, int NB>
 struct LmTile {
   static constexpr int kThreads = 2 * WN * kWave;        // two waves along the rows
   static constexpr int kBN = WN * 32 * NB;               // vocabulary ids per block
-  static constexpr int kSlots = WN * NB / 2;             // 64-id slices of a tile row
   static constexpr int kRpp = kThreads / kLmCpr;         // tile rows one staging pass covers
   static constexpr int kPassesA = kLmBM / kRpp;          // passes per hidden-state tile
   static constexpr int kPassesB = kBN / kRpp;            // passes per weight tile
-  static_assert(NB % 2 == 0 && kLmBM % kRpp == 0 && kBN % kRpp == 0,
-                "the staging passes and the epilogue's 64-id slices must tile the block");
+  static_assert(kLmBM % kRpp == 0 && kBN % kRpp == 0, "the staging passes must tile the block");
 };
 
 struct LmGemm {
@@ -100,29 +94,21 @@ struct LmPair {
   int n0;
 };
 
-// One block: a 128 x LmTile<WN, NB>::kBN tile of logits. The block order is XCD-aware: block
-// g runs on XCD g % 8, and the row tiles of one vocabulary tile are
-// consecutive blocks of one XCD, so its weight tile is fetched into that XCD's
-// L2 once and read from there by the other row tiles.
-// GREEDY (statistics only): (max, argmax, NaN/+inf) partials instead of (max, sum).
-template <bool STATS, int WN, int NB, bool GREEDY = false>
-__global__ __launch_bounds__(2 * WN * kWave, 2) void k_lm_gemm(const LmPair PR) {
+// One block: a 128 x LmTile<WN, NB>::kBN tile of logits, stored to out. The
+// block order is XCD-aware: block g runs on XCD g % 8, and the row tiles of
+// one vocabulary tile are consecutive blocks of one XCD, so its weight tile is
+// fetched into that XCD's L2 once and read from there by the other row tiles.
+template <int WN, int NB>
+__global__ __launch_bounds__(2 * WN * kWave, 2) void k_lm_rows(const LmPair PR) {
   using T = LmTile<WN, NB>;
   constexpr int kLmNB = NB;
   constexpr int kLmBN = T::kBN, kLmRpp = T::kRpp;
-  constexpr int kLmPasses = T::kPassesA, kLmPassesB = T::kPassesB, kLmSlots = T::kSlots;
+  constexpr int kLmPasses = T::kPassesA, kLmPassesB = T::kPassesB;
   const bool second = (int)blockIdx.x >= PR.n0;
   const LmGemm& G = PR.g[second ? 1 : 0];
-  // operand tiles; after the main loop the statistics epilogue reuses them
-  // (each wave 32 rows x 68 floats)
-  constexpr int kOpWords = (kLmBM + kLmBN) * kLmLds;
-  constexpr int kEpWords = 2 * WN * 32 * (64 + 4) * 2;
-  __shared__ __align__(16) uint16_t sAB[kOpWords > kEpWords ? kOpWords : kEpWords];
+  __shared__ __align__(16) uint16_t sAB[(kLmBM + kLmBN) * kLmLds];
   uint16_t* const sA = sAB;
   uint16_t* const sB = sAB + kLmBM * kLmLds;
-  __shared__ float s_pm[kLmSlots][kLmBM];
-  __shared__ float s_ps[kLmSlots][kLmBM];  // greedy: the argmax, bit 31 NaN or +inf seen
-  __shared__ int s_tok[kLmBM];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -206,137 +192,323 @@ __global__ __launch_bounds__(2 * WN * kWave, 2) void k_lm_gemm(const LmPair PR) 
 
   // Element i of tile (a, b) in lane l: row wm*64 + a*32 + 8*(i/4) + 4*(l/32)
   // + i%4, vocabulary id v0 + wn*32*kLmNB + b*32 + l%32.
-  // The logits themselves: the draw rows' GEMM always, the statistics GEMM
-  // only when the caller asked for its logits (spec_verify_lmhead_diag).
-  if (!STATS || G.out != nullptr) {
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+  for (int a = 0; a < 2; ++a) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rl = wm * 64 + a * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      const int m = m0 + rl;
+      if (m >= G.M) continue;
+      if (G.gather != nullptr && G.gather[(size_t)m * G.gather_step] < 0) continue;
+      float* orow = G.out + (size_t)(m * G.out_step + G.out_row0) * G.V;
+#pragma unroll
+      for (int b = 0; b < kLmNB; ++b) {
+        const int v = v0 + wn * 32 * kLmNB + b * 32 + (lane & 31);
+        if (v < G.V) orow[v] = acc[a][b][i];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Statistics GEMM (k_lm_stats). Block tile: 192 rows x 384 vocabulary ids, 12
+// waves in a 2 x 6 arrangement, each a 96 x 64 sub-tile of 3 x 2 32 x 32 MFMA
+// tiles; 64 hidden elements per step. Both operand tiles of a step ([hidden
+// rows; weight rows], 128 bytes a row) are filled by direct global -> LDS
+// loads into one of two stages while the MFMAs read the other, so no operand
+// passes through registers before the MFMA reads it.
+//
+// Why this shape: every 16-byte operand chunk the compute units fetch comes
+// from L2 (or further), and that stream, not the matrix cores, set the pace of
+// the earlier 128 x 256 tile (7.6 GB fetched a call at the target workload,
+// about 450 us at the rate the fetch path sustains). Per call the fetch is
+// (hidden bytes) x (vocabulary tiles) + (weight bytes) x (row tiles): 192 rows
+// divide 576 target rows into three tiles and 384 ids divide V = 128256 into
+// 334, which brings it to 4.7 GB. Twelve waves (three per SIMD) hide the LDS
+// reads of one wave behind the MFMAs of the others.
+constexpr int kStBM = 192, kStBN = 384, kStBK = 64;
+constexpr int kStWM = 2, kStWN = 6;                          // waves along rows, ids
+constexpr int kStTM = 3, kStTN = 2;                          // MFMA tiles per wave
+constexpr int kStWaves = kStWM * kStWN;
+constexpr int kStThreads = kStWaves * kWave;
+constexpr int kStRowBytes = kStBK * 2;                       // one operand row of a step
+constexpr int kStStageBytes = (kStBM + kStBN) * kStRowBytes;  // 72 KB
+constexpr int kStDma = kStStageBytes / 1024 / kStWaves;      // 1 KB loads per wave and stage
+constexpr int kStSlots = kStBN / 64;                          // 64-id slices of a tile row
+constexpr int kStEp = 64 + 4;                                 // epilogue staging row (floats)
+static_assert(kStBM == kStWM * kStTM * 32 && kStBN == kStWN * kStTN * 32 && kStTN == 2,
+              "each wave covers one 64-id slice of the tile");
+static_assert(kStStageBytes % (1024 * kStWaves) == 0, "the loads split evenly over the waves");
+static_assert(kStWaves * 32 * kStEp * 4 <= 2 * kStStageBytes, "epilogue staging fits the stages");
+
+// Read by the loads of hidden elements past D (a step that D ends inside).
+__device__ __align__(16) const uint16_t kLmZeros[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(1))) void* global_void_ptr;
+
+// s_waitcnt immediate: vector memory count 0, the other counters unconstrained
+constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
+
+// One block: a 192 x 384 tile of logits, reduced per row and 64-id slice in
+// the epilogue and merged into one partial per (row, tile). Block order as in
+// k_lm_rows (XCD-aware: the row tiles of one vocabulary tile are consecutive
+// blocks of one XCD). GREEDY: (max, argmax, NaN/+inf) partials instead of
+// (max, sum).
+template <bool GREEDY>
+__global__ __launch_bounds__(kStThreads, 3) void k_lm_stats(const LmPair PR) {
+  const bool second = (int)blockIdx.x >= PR.n0;
+  const LmGemm& G = PR.g[second ? 1 : 0];
+  // Two operand stages (after the main loop the epilogue stages its slices
+  // there), then the per-slot partials and the rows' tokens. One LDS array:
+  // with several, the compiler waits for the loads into one stage before
+  // every read of the other.
+  __shared__ __align__(16) unsigned char s_lds[2 * kStStageBytes + (2 * kStSlots + 1) * kStBM * 4];
+  unsigned char* const s_op = s_lds;
+  float (*const s_pm)[kStBM] = reinterpret_cast<float (*)[kStBM]>(s_lds + 2 * kStStageBytes);
+  // greedy: the argmax, bit 31 NaN or +inf seen
+  float (*const s_ps)[kStBM] = s_pm + kStSlots;
+  int* const s_tok = reinterpret_cast<int*>(s_ps + kStSlots);
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int wm = wave % kStWM, wn = wave / kStWM;
+  const int g = (int)blockIdx.x - (second ? PR.n0 : 0);
+  const int idx = g / kXcds;
+  const int vt = (idx / G.MT) * kXcds + g % kXcds;
+  const int mt = idx % G.MT;
+  if (vt >= G.NT) return;
+  const int m0 = mt * kStBM, v0 = vt * kStBN;
+
+  // Load i of this wave fills 1 KB q = wave + kStWaves * i of a stage: tile
+  // rows 8q .. 8q + 7 (hidden rows first, then weight rows); lane l the row
+  // 8q + l / 8 and 16-byte slot l % 8, which holds chunk (l % 8) ^ (row % 8)
+  // of the step (the swizzle spreads the MFMA reads of one chunk column over
+  // all banks). Rows past M or V repeat the last row; their results are
+  // never used.
+  const uint16_t* src[kStDma];
+  int kch[kStDma];  // first hidden element of this lane's chunk within a step
+#pragma unroll
+  for (int i = 0; i < kStDma; ++i) {
+    const int q = wave + kStWaves * i;
+    const int r = q * 8 + (lane >> 3);
+    const int cg = (lane & 7) ^ (r & 7);
+    const uint16_t* row;
+    if (r < kStBM) {
+      const int m = min(m0 + r, G.M - 1);
+      row = G.H + (size_t)m * G.D;
+    } else {
+      const int v = min(v0 + r - kStBM, G.V - 1);
+      row = G.W + (size_t)v * G.D;
+    }
+    kch[i] = cg * 8;
+    src[i] = row + kch[i];
+  }
+  const int nsteps = (G.D + kStBK - 1) / kStBK;
+  // the loads of step st into a stage; chunks past D read zeros. Kept
+  // free of branches: the compiler then tracks these loads precisely and does
+  // not wait for them before the MFMAs' LDS reads of the other stage.
+  auto issue = [&](int st, int stage) {
+    unsigned char* base = s_op + stage * kStStageBytes + wave * 1024;
+    const int k0 = st * kStBK;
+#pragma unroll
+    for (int i = 0; i < kStDma; ++i) {
+      const uint16_t* p = (k0 + kch[i] < G.D) ? src[i] + k0 : kLmZeros;
+      __builtin_amdgcn_global_load_lds((global_void_ptr)p,
+                                       (lds_void_ptr)(base + i * kStWaves * 1024), 16, 0, 0);
+    }
+  };
+
+  f32x16 acc[kStTM][kStTN];
+#pragma unroll
+  for (int a = 0; a < kStTM; ++a)
+#pragma unroll
+    for (int b = 0; b < kStTN; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+
+  issue(0, 0);
+  for (int t = 0; t < nsteps; ++t) {
+    // this wave's loads of step t have landed; the barrier makes every wave's
+    // visible and ends every wave's reads of step t - 1, whose stage the
+    // loads of step t + 1 then fill (the last step repeats its own loads into
+    // the other stage, which nothing reads)
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(min(t + 1, nsteps - 1), (t + 1) & 1);
+    const unsigned char* base = s_op + (t & 1) * kStStageBytes;
+    // lane l reads row l % 32 of each 32 x 32 tile, chunk 2 ks + l / 32 of
+    // the step (8 consecutive hidden elements)
+    bf16x8 af[2][kStTM], bfr[2][kStTN];
+    auto rd = [&](int ks, int sl) {
+      const int cg = ks * 2 + (lane >> 5);
+#pragma unroll
+      for (int a = 0; a < kStTM; ++a) {
+        const int r = wm * kStTM * 32 + a * 32 + (lane & 31);
+        af[sl][a] = *reinterpret_cast<const bf16x8*>(base + r * kStRowBytes + ((cg ^ (r & 7)) * 16));
+      }
+#pragma unroll
+      for (int b = 0; b < kStTN; ++b) {
+        const int r = kStBM + wn * kStTN * 32 + b * 32 + (lane & 31);
+        bfr[sl][b] = *reinterpret_cast<const bf16x8*>(base + r * kStRowBytes + ((cg ^ (r & 7)) * 16));
+      }
+    };
+    rd(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < kStBK / 16; ++ks) {
+      if (ks + 1 < kStBK / 16) rd(ks + 1, (ks + 1) & 1);
+#pragma unroll
+      for (int a = 0; a < kStTM; ++a)
+#pragma unroll
+        for (int b = 0; b < kStTN; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][a], bfr[ks & 1][b],
+                                                               acc[a][b], 0, 0, 0);
+    }
+    // the first substep's reads, then one read of the next substep after each MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, kStTM + kStTN, 0);
+#pragma unroll
+    for (int ks = 0; ks < kStBK / 16; ++ks) {
+      if (ks + 1 < kStBK / 16) {
+#pragma unroll
+        for (int i = 0; i < kStTM + kStTN; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kStTM * kStTN - (kStTM + kStTN), 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, kStTM * kStTN, 0);
+      }
+    }
+  }
+
+  // Element i of tile (a, b) in lane l: row wm*96 + a*32 + 8*(i/4) + 4*(l/32)
+  // + i%4, vocabulary id v0 + wn*64 + b*32 + l%32.
+  // The logits themselves only when the caller asked for them
+  // (spec_verify_lmhead_diag).
+  if (G.out != nullptr) {
+#pragma unroll
+    for (int a = 0; a < kStTM; ++a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int rl = wm * 64 + a * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        const int m = m0 + rl;
+        const int m = m0 + wm * kStTM * 32 + a * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
         if (m >= G.M) continue;
-        if (G.gather != nullptr && G.gather[(size_t)m * G.gather_step] < 0) continue;
-        float* orow = G.out + (size_t)(m * G.out_step + G.out_row0) * G.V;
+        float* orow = G.out + (size_t)m * G.V;
 #pragma unroll
-        for (int b = 0; b < kLmNB; ++b) {
-          const int v = v0 + wn * 32 * kLmNB + b * 32 + (lane & 31);
+        for (int b = 0; b < kStTN; ++b) {
+          const int v = v0 + wn * kStTN * 32 + b * 32 + (lane & 31);
           if (v < G.V) orow[v] = acc[a][b][i];
         }
       }
     }
   }
-  if constexpr (STATS) {
-    if (tid < kLmBM) {
-      const int m = m0 + tid;
-      int tok = -1;
-      if (m < G.M) {
-        if (!G.target) {
-          tok = G.tokens[m];
-        } else {
-          const int i = m % (G.K + 1);
-          if (i < G.K) tok = G.tokens[(m / (G.K + 1)) * G.K + i];
-        }
-      }
-      s_tok[tid] = tok;
-    }
-    // Each wave stages one 32 x 64 slice of its sub-tile at a time in LDS
-    // (row-major, 4 floats of padding per row), then lane l reduces half of
-    // row l / 2 (32 ids) and pairs with lane l ^ 1 for the slice's 64 ids.
-    // Slot wn * kLmNB / 2 + slice of s_pm / s_ps holds each row's partial.
-    constexpr int kEp = 64 + 4;
-    float* const E = reinterpret_cast<float*>(sAB) + wave * 32 * kEp;
-    const float c = G.c;
-    const int r = lane >> 1, h = (lane & 1) * 32;
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-#pragma unroll
-      for (int sl = 0; sl < kLmNB / 2; ++sl) {
-        __syncthreads();  // the operand tiles, or the previous slice, are read
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            E[(8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)) * kEp + bb * 32 + (lane & 31)] =
-                acc[a][2 * sl + bb][i];
-        __syncthreads();
-        float x[32];
-#pragma unroll
-        for (int j = 0; j < 32; j += 4) {
-          const float4 t = *reinterpret_cast<const float4*>(&E[r * kEp + h + j]);
-          x[j] = t.x;
-          x[j + 1] = t.y;
-          x[j + 2] = t.z;
-          x[j + 3] = t.w;
-        }
-        const int cb = v0 + wn * 32 * kLmNB + sl * 64 + h;  // first id of this lane's half row
-        const int rl = wm * 64 + a * 32 + r;
-        if constexpr (GREEDY) {
-          // the largest logit of the 32 ids (NaN never wins), its lowest id
-          // (none while every value is -inf) and whether any is NaN or +inf,
-          // then with lane l ^ 1, the other half of the slice's 64 ids
-          float mx = kNegInf;
-          int bd = 0;
-#pragma unroll
-          for (int j = 0; j < 32; ++j) {
-            if (cb + j >= G.V) x[j] = kNegInf;
-            bd |= is_nan_or_posinf(x[j]) ? 1 : 0;
-            mx = fmaxf(mx, x[j]);
-          }
-          int jm = 32;
-#pragma unroll
-          for (int j = 31; j >= 0; --j) jm = (x[j] == mx) ? j : jm;
-          int ai = (mx > kNegInf) ? cb + jm : INT_MAX;
-          const float omx = dpp_f<0xB1>(mx);  // quad_perm [1,0,3,2]: lane l ^ 1
-          const int oai = dpp_i<0xB1>(ai);
-          bd |= dpp_i<0xB1>(bd);
-          argmax_merge(mx, ai, omx, oai);
-          if ((lane & 1) == 0) {
-            s_pm[wn * (kLmNB / 2) + sl][rl] = mx;
-            s_ps[wn * (kLmNB / 2) + sl][rl] = __uint_as_float((unsigned)ai | ((unsigned)bd << 31));
-          }
-          continue;
-        }
-        const int tok = s_tok[rl];
-        if (tok >= cb && tok < cb + 32) G.tok_logits[G.unit0 + m0 + rl] = E[r * kEp + h + (tok - cb)];
-        float mx = kNegInf;
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-          if (cb + j >= G.V) x[j] = kNegInf;
-          mx = fmaxf(mx, x[j]);
-        }
-        mx = fmaxf(mx, dpp_f<0xB1>(mx));  // quad_perm [1,0,3,2]: lane l ^ 1
-        const float R = ref_of(mx, c);
-        float sm = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 32; ++j) sm += fast_exp2(fmaf(x[j], c, -R));
-        sm += dpp_f<0xB1>(sm);
-        if ((lane & 1) == 0) {
-          s_pm[wn * (kLmNB / 2) + sl][rl] = mx;
-          s_ps[wn * (kLmNB / 2) + sl][rl] = sm;
-        }
-      }
-    }
-    __syncthreads();
-    if (tid < kLmBM && m0 + tid < G.M) {
-      if constexpr (GREEDY) {
-        // the slices in increasing id order: the strict compare keeps the first maximum
-        float mm = s_pm[0][tid];
-        const unsigned p0 = __float_as_uint(s_ps[0][tid]);
-        int ai = (int)(p0 & 0x7fffffffu), bd = (int)(p0 >> 31);
-#pragma unroll
-        for (int q = 1; q < kLmSlots; ++q) {
-          const unsigned pq = __float_as_uint(s_ps[q][tid]);
-          argmax_merge(mm, ai, s_pm[q][tid], (int)(pq & 0x7fffffffu));
-          bd |= (int)(pq >> 31);
-        }
-        G.part[(size_t)(G.unit0 + m0 + tid) * G.NT + vt] = pack_am(mm, ai, bd);
+  if (tid < kStBM) {
+    const int m = m0 + tid;
+    int tok = -1;
+    if (m < G.M) {
+      if (!G.target) {
+        tok = G.tokens[m];
       } else {
-        float mm = s_pm[0][tid], ss = s_ps[0][tid];
-#pragma unroll
-        for (int q = 1; q < kLmSlots; ++q) merge_ms(mm, ss, s_pm[q][tid], s_ps[q][tid], c);
-        G.part[(size_t)(G.unit0 + m0 + tid) * G.NT + vt] = pack_ms(mm, ss);
+        const int i = m % (G.K + 1);
+        if (i < G.K) tok = G.tokens[(m / (G.K + 1)) * G.K + i];
       }
+    }
+    s_tok[tid] = tok;
+  }
+  // Each wave stages one 32 x 64 slice of its sub-tile at a time in LDS
+  // (row-major, 4 floats of padding per row), then lane l reduces half of
+  // row l / 2 (32 ids) and pairs with lane l ^ 1 for the slice's 64 ids.
+  // Slot wn of s_pm / s_ps holds each row's partial of the wave's slice.
+  // The last step's repeated loads land before any wave stages a slice.
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  float* const E = reinterpret_cast<float*>(s_op) + wave * 32 * kStEp;
+  const float c = G.c;
+  const int r = lane >> 1, h = (lane & 1) * 32;
+  const int cb = v0 + wn * 64 + h;  // first id of this lane's half row
+#pragma unroll
+  for (int a = 0; a < kStTM; ++a) {
+    __syncthreads();  // the operand stages, or the previous slice, are read
+#pragma unroll
+    for (int b = 0; b < kStTN; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        E[(8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)) * kStEp + b * 32 + (lane & 31)] = acc[a][b][i];
+    __syncthreads();
+    float x[32];
+#pragma unroll
+    for (int j = 0; j < 32; j += 4) {
+      const float4 t4 = *reinterpret_cast<const float4*>(&E[r * kStEp + h + j]);
+      x[j] = t4.x;
+      x[j + 1] = t4.y;
+      x[j + 2] = t4.z;
+      x[j + 3] = t4.w;
+    }
+    const int rl = wm * kStTM * 32 + a * 32 + r;
+    if constexpr (GREEDY) {
+      // the largest logit of the 32 ids (NaN never wins), its lowest id
+      // (none while every value is -inf) and whether any is NaN or +inf,
+      // then with lane l ^ 1, the other half of the slice's 64 ids
+      float mx = kNegInf;
+      int bd = 0;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        if (cb + j >= G.V) x[j] = kNegInf;
+        bd |= is_nan_or_posinf(x[j]) ? 1 : 0;
+        mx = fmaxf(mx, x[j]);
+      }
+      int jm = 32;
+#pragma unroll
+      for (int j = 31; j >= 0; --j) jm = (x[j] == mx) ? j : jm;
+      int ai = (mx > kNegInf) ? cb + jm : INT_MAX;
+      const float omx = dpp_f<0xB1>(mx);  // quad_perm [1,0,3,2]: lane l ^ 1
+      const int oai = dpp_i<0xB1>(ai);
+      bd |= dpp_i<0xB1>(bd);
+      argmax_merge(mx, ai, omx, oai);
+      if ((lane & 1) == 0) {
+        s_pm[wn][rl] = mx;
+        s_ps[wn][rl] = __uint_as_float((unsigned)ai | ((unsigned)bd << 31));
+      }
+    } else {
+      const int tok = s_tok[rl];
+      if (tok >= cb && tok < cb + 32) G.tok_logits[G.unit0 + m0 + rl] = E[r * kStEp + h + (tok - cb)];
+      float mx = kNegInf;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        if (cb + j >= G.V) x[j] = kNegInf;
+        mx = fmaxf(mx, x[j]);
+      }
+      mx = fmaxf(mx, dpp_f<0xB1>(mx));  // quad_perm [1,0,3,2]: lane l ^ 1
+      const float R = ref_of(mx, c);
+      float sm = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) sm += fast_exp2(fmaf(x[j], c, -R));
+      sm += dpp_f<0xB1>(sm);
+      if ((lane & 1) == 0) {
+        s_pm[wn][rl] = mx;
+        s_ps[wn][rl] = sm;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < kStBM && m0 + tid < G.M) {
+    if constexpr (GREEDY) {
+      // the slices in increasing id order: the strict compare keeps the first maximum
+      float mm = s_pm[0][tid];
+      const unsigned p0 = __float_as_uint(s_ps[0][tid]);
+      int ai = (int)(p0 & 0x7fffffffu), bd = (int)(p0 >> 31);
+#pragma unroll
+      for (int q = 1; q < kStSlots; ++q) {
+        const unsigned pq = __float_as_uint(s_ps[q][tid]);
+        argmax_merge(mm, ai, s_pm[q][tid], (int)(pq & 0x7fffffffu));
+        bd |= (int)(pq >> 31);
+      }
+      G.part[(size_t)(G.unit0 + m0 + tid) * G.NT + vt] = pack_am(mm, ai, bd);
+    } else {
+      float mm = s_pm[0][tid], ss = s_ps[0][tid];
+#pragma unroll
+      for (int q = 1; q < kStSlots; ++q) merge_ms(mm, ss, s_pm[q][tid], s_ps[q][tid], c);
+      G.part[(size_t)(G.unit0 + m0 + tid) * G.NT + vt] = pack_ms(mm, ss);
     }
   }
 }
@@ -439,7 +611,7 @@ bool lm_plan(int B, int K, int V, LmPlan& L) {
   if (B < 0 || K < 0 || K > SV_MAX_K || V < 1 || V > (1 << 30)) return false;
   const long long units = (long long)B * K + (long long)B * (K + 1);
   if (units > INT_MAX) return false;
-  L.NT = (V + LmTile<kLmStatsWN, kLmStatsNB>::kBN - 1) / LmTile<kLmStatsWN, kLmStatsNB>::kBN;
+  L.NT = (V + kStBN - 1) / kStBN;
   const bool vec = V % 4 == 0;
   L.nvec = vec ? V / 4 : V;
   L.dchunks = (L.nvec + kDrawVecs - 1) / kDrawVecs;
@@ -513,8 +685,8 @@ int run_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
     return SV_EWORKSPACE;
   const int total_draft = B * K;
   const int rows = B * (K + 1);
-  const long long gemm_d = (long long)L.NT * ((total_draft + kLmBM - 1) / kLmBM);
-  const long long gemm_t = (long long)L.NT * ((rows + kLmBM - 1) / kLmBM);
+  const long long gemm_d = (long long)L.NT * ((total_draft + kStBM - 1) / kStBM);
+  const long long gemm_t = (long long)L.NT * ((rows + kStBM - 1) / kStBM);
   if (gemm_t + kXcds * 4 > (long long)INT_MAX || gemm_d + kXcds * 4 > (long long)INT_MAX)
     return SV_EUNSUPPORTED;
   char* ws = static_cast<char*>(workspace);
@@ -553,8 +725,8 @@ int run_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
   P.draw_rows = reinterpret_cast<int*>(ws + L.off_draw_rows);
   unsigned long long* part = reinterpret_cast<unsigned long long*>(ws + L.off_part);
 
-  auto grid_of = [&](int M, int NT) {
-    const int MT = (M + kLmBM - 1) / kLmBM;
+  auto grid_of = [&](int M, int NT, int BM) {
+    const int MT = (M + BM - 1) / BM;
     const long long per_xcd = (NT + kXcds - 1) / kXcds;  // vocabulary tiles per XCD
     return std::make_pair(MT, (unsigned)(per_xcd * MT * kXcds));
   };
@@ -582,7 +754,7 @@ int run_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
     G.out_step = 1;
     G.out_row0 = 0;
     if (total_draft > 0 && !greedy) {
-      auto [MT, blocks] = grid_of(total_draft, L.NT);
+      auto [MT, blocks] = grid_of(total_draft, L.NT, kStBM);
       G.H = static_cast<const uint16_t*>(hidden_draft);
       G.W = static_cast<const uint16_t*>(weight_draft);
       G.D = d_draft;
@@ -595,7 +767,7 @@ int run_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
       S.n0 = (int)blocks;
       blocks_stats = blocks;
     }
-    auto [MT, blocks] = grid_of(rows, L.NT);
+    auto [MT, blocks] = grid_of(rows, L.NT, kStBM);
     G.H = static_cast<const uint16_t*>(hidden_target);
     G.W = static_cast<const uint16_t*>(weight_target);
     G.D = d_target;
@@ -613,11 +785,9 @@ int run_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
     blocks_stats += blocks;
   }
   if (greedy)
-    hipLaunchKernelGGL((k_lm_gemm<true, kLmStatsWN, kLmStatsNB, true>), dim3(blocks_stats),
-                       dim3(LmTile<kLmStatsWN, kLmStatsNB>::kThreads), 0, stream, S);
+    hipLaunchKernelGGL(k_lm_stats<true>, dim3(blocks_stats), dim3(kStThreads), 0, stream, S);
   else
-    hipLaunchKernelGGL((k_lm_gemm<true, kLmStatsWN, kLmStatsNB>), dim3(blocks_stats),
-                       dim3(LmTile<kLmStatsWN, kLmStatsNB>::kThreads), 0, stream, S);
+    hipLaunchKernelGGL(k_lm_stats<false>, dim3(blocks_stats), dim3(kStThreads), 0, stream, S);
   if (hipGetLastError() != hipSuccess || !stage()) return SV_EHIP;
   if (greedy) {
     // the target rows' argmax partials; the decision and the outputs are the
@@ -647,7 +817,7 @@ int run_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
     R.out_step = 2;
     R.gather_step = 2;
     R.M = B;
-    auto [MT, blocks] = grid_of(B, R.NT);
+    auto [MT, blocks] = grid_of(B, R.NT, kLmBM);
     R.MT = MT;
     R.H = static_cast<const uint16_t*>(hidden_target);
     R.W = static_cast<const uint16_t*>(weight_target);
@@ -666,7 +836,7 @@ int run_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
       R2.g[1] = R;
       total += blocks;
     }
-    hipLaunchKernelGGL((k_lm_gemm<false, kLmRowsWN, kLmRowsNB>), dim3(total),
+    hipLaunchKernelGGL((k_lm_rows<kLmRowsWN, kLmRowsNB>), dim3(total),
                        dim3(LmTile<kLmRowsWN, kLmRowsNB>::kThreads), 0, stream, R2);
   }
   if (hipGetLastError() != hipSuccess || !stage()) return SV_EHIP;
