@@ -282,17 +282,20 @@ __global__ __launch_bounds__(kStThreads, 3) void k_lm_stats(const LmPair PR) {
 
   // Load i of this wave fills 1 KB q = wave + kStWaves * i of a stage: tile
   // rows 8q .. 8q + 7 (hidden rows first, then weight rows); lane l the row
-  // 8q + l / 8 and 16-byte slot l % 8, which holds chunk (l % 8) ^ (row % 8)
-  // of the step (the swizzle spreads the MFMA reads of one chunk column over
-  // all banks). Rows past M or V repeat the last row; their results are
-  // never used.
+  // 8q + l / 8 and 16-byte slot l % 8, which holds chunk (l % 8) ^ swz(row)
+  // of the step. gfx950's LDS serves a 16-byte read of 16 lanes at once from
+  // 64 banks; with 128-byte rows, rows r and r + 1 sit on the two halves of
+  // the banks, so swz(r) = (r / 2) % 8 gives the 16 rows that 16 lanes read
+  // at one chunk column 16 distinct bank groups (r % 8 would put rows r and
+  // r + 8 on the same ones: measured 10% slower). Rows past M or V repeat
+  // the last row; their results are never used.
   const uint16_t* src[kStDma];
   int kch[kStDma];  // first hidden element of this lane's chunk within a step
 #pragma unroll
   for (int i = 0; i < kStDma; ++i) {
     const int q = wave + kStWaves * i;
     const int r = q * 8 + (lane >> 3);
-    const int cg = (lane & 7) ^ (r & 7);
+    const int cg = (lane & 7) ^ ((r >> 1) & 7);
     const uint16_t* row;
     if (r < kStBM) {
       const int m = min(m0 + r, G.M - 1);
@@ -347,12 +350,12 @@ __global__ __launch_bounds__(kStThreads, 3) void k_lm_stats(const LmPair PR) {
 #pragma unroll
       for (int a = 0; a < kStTM; ++a) {
         const int r = wm * kStTM * 32 + a * 32 + (lane & 31);
-        af[sl][a] = *reinterpret_cast<const bf16x8*>(base + r * kStRowBytes + ((cg ^ (r & 7)) * 16));
+        af[sl][a] = *reinterpret_cast<const bf16x8*>(base + r * kStRowBytes + ((cg ^ ((r >> 1) & 7)) * 16));
       }
 #pragma unroll
       for (int b = 0; b < kStTN; ++b) {
         const int r = kStBM + wn * kStTN * 32 + b * 32 + (lane & 31);
-        bfr[sl][b] = *reinterpret_cast<const bf16x8*>(base + r * kStRowBytes + ((cg ^ (r & 7)) * 16));
+        bfr[sl][b] = *reinterpret_cast<const bf16x8*>(base + r * kStRowBytes + ((cg ^ ((r >> 1) & 7)) * 16));
       }
     };
     rd(0, 0);
