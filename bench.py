@@ -661,7 +661,7 @@ def bench_accept(args, w, sv):
     print(json.dumps(rec_out), flush=True)
 
 
-LM_STAGES = ["gemm_stats", "merge_and_decide", "gemm_draw_rows", "draw"]
+LM_STAGES = ["gemm_stats", "merge", "decide_and_draw"]
 
 
 MULTI_NAME = "multi_bf16_B64_M4_K4_V128256"
@@ -788,8 +788,8 @@ def bench_multi(args, sv):
 
 def bench_lmhead(args, sv):
     """Verification from LM-head hidden states: the draft and target rows'
-    logits formed on the matrix cores and reduced in the GEMM epilogue, the
-    decision, the draw rows formed again, and the draw."""
+    logits formed on the matrix cores, reduced in the GEMM epilogue and
+    stored, the merge of the tile partials, and the decision and draw."""
     w = W.make_lmhead()
     B, K, V, dq, dp, T = w["B"], w["K"], w["V"], w["d_draft"], w["d_target"], w["temperature"]
     s = W.LM_H_SCALE * W.LM_W_SCALE
@@ -865,7 +865,7 @@ def bench_lmhead(args, sv):
     hev.close()
     stage_ms = per.mean(axis=0).tolist()
     n_sampling = num.cpu().numpy()
-    # the same shape verified greedily: the target rows alone, no draw rows
+    # the same shape verified greedily: the target rows alone, no rows stored
     def greedy_step(ev=None):
         sv.spec_verify_lmhead(None, None, hp, wp, toks_greedy, None, B, K, V, 0.0,
                               out_tokens=out, num_accepted=num, workspace=ws, stage_events=ev)

@@ -338,12 +338,12 @@ int spec_verify_multi(const void* draft_logits, const void* target_logits,
 /* Verification from LM-head hidden states: the same step as spec_verify, with
  * the logit rows formed inside the library as l = h W^T on the matrix cores
  * (bf16 operands, fp32 accumulation) and reduced in the GEMM epilogue, so the
- * [B, K, V] and [B, K+1, V] logit arrays are never stored (aivaro.ru answer
- * 289 section 8 names the memory the draft and target logits take; the
- * lecture-16 notes: the target model scores every drafted position in one
- * pass, its logits being the last layer's output). Only the rows of each
- * sequence's final draw (p_n, and q_n for a residual) are formed again and
- * kept, in fp32, inside the workspace.
+ * bf16 [B, K, V] and [B, K+1, V] logit arrays are never written by a model
+ * and read back (aivaro.ru answer 289 section 8 names the memory the draft and
+ * target logits take; the lecture-16 notes: the target model scores every
+ * drafted position in one pass, its logits being the last layer's output).
+ * A sampling call stores the fp32 rows inside the workspace as the GEMM forms
+ * them, and the final draw reads its rows (p_n, and q_n for a residual) there.
  *   hidden_draft   bf16 [B*K, d_draft]     draft model's last hidden states
  *   weight_draft   bf16 [V, d_draft]       draft LM head (may be NULL with hidden_draft when K == 0)
  *   hidden_target  bf16 [B*(K+1), d_target]
@@ -352,22 +352,20 @@ int spec_verify_multi(const void* draft_logits, const void* target_logits,
  * temperature finite and >= 0; no top-k / top-p. Temperature 0 verifies
  * greedily (accept iff the draft id is the target row's argmax, the lowest id
  * on ties; the correction or bonus token is that argmax): no draft row is
- * formed and no uniform read, so hidden_draft, weight_draft and uniforms may
- * be NULL and d_draft is not checked. d_draft (sampling) and d_target are
- * multiples of 8 (>= 8); the matrices given are 16-byte aligned.
+ * formed, no row stored and no uniform read, so hidden_draft, weight_draft and
+ * uniforms may be NULL and d_draft is not checked. d_draft (sampling) and
+ * d_target are multiples of 8 (>= 8); the matrices given are 16-byte aligned.
  * Row-major throughout. The workspace is sized by
  * spec_verify_lmhead_workspace_bytes(B, K, V), 256-byte aligned; its first
  * spec_verify_lmhead_zero_bytes(B, K, V) bytes must be zero before the first
  * call (spec_verify_workspace_init) and are zero again after every call. The
- * draw rows (2*B*V floats) sit at the tail of the workspace and hold the last
- * call's rows. One workspace serves calls of any smaller B, K, V: their zero
- * regions start at the front and their rows end at the back. stage_events
- * (may be NULL; n_stage_events of them, caller-created) are recorded on
- * `stream`: before the statistics GEMMs (draft and target rows, one launch),
- * after them, after the merge and decision, after the draw rows' GEMMs, and
- * every further one after the draw (greedy calls record the same events; the
- * decision kernel and the draw rows' GEMMs are not launched). Errors as
- * spec_verify. */
+ * logits ((B*K + B*(K+1)) * V floats, draft rows first) sit at the tail of the
+ * workspace and hold the last sampling call's rows. One workspace serves calls
+ * of any smaller B, K, V: their zero regions start at the front and their
+ * logits end at the back. stage_events (may be NULL; n_stage_events of them,
+ * caller-created) are recorded on `stream`: before the statistics GEMM (draft
+ * and target rows, one launch), after it, after the merge of its partials,
+ * and every further one after the decision and draw. Errors as spec_verify. */
 size_t spec_verify_lmhead_workspace_bytes(int B, int K, int V);
 size_t spec_verify_lmhead_zero_bytes(int B, int K, int V);
 int spec_verify_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
@@ -383,8 +381,10 @@ int spec_verify_lmhead(const void* hidden_draft, const void* weight_draft, int d
  *   logits_target  float [B*(K+1), V]  GEMM formed them (fp32 accumulation),
  *                                      before any reduction (a greedy call
  *                                      forms no draft logits)
- * Device memory owned by the caller. Writing them costs 4 bytes per logit of
- * HBM traffic; the default call writes none. */
+ * Device memory owned by the caller. A sampling call stores these rows in
+ * place of the workspace's and its draw reads them there, so they must not
+ * overlap the workspace or each other; a greedy call writes logits_target
+ * only for this output. */
 typedef struct sv_lmhead_diag {
   float* logits_draft;
   float* logits_target;

@@ -139,12 +139,9 @@ struct Params {
   // Verification from LM-head hidden states (sv_lmhead.hip): the logit of
   // each statistics unit at its token (draft units: their own token; target
   // units at position i < K_b: token x_i), written by the GEMM epilogue, read
-  // by the decision instead of the logit rows; and the final draw reads row
-  // pair n from a [2B, V] fp32 array (target row 2b, draft row 2b + 1) given
-  // as both logit arrays.
+  // by the decision instead of the logit rows (the final draw reads the fp32
+  // rows the GEMM stored, given as the two logit arrays).
   float* tok_logits;       // [total_draft + rows] or null
-  int draw_remap;          // 1: the draw's rows are 2b and 2b + 1
-  int* draw_rows;          // [2B] hidden rows of the draw (target, draft; -1: none)
   // Several draft chains per sequence (sv_multi.hip): B above counts the
   // chains as sequences of the statistics pass (B = sequences * M).
   int M;                   // chains per sequence
@@ -181,7 +178,6 @@ hipError_t fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_multi(int dtype, bool vec, const Params& P, hipStream_t s);
 // LM-head path (sv_lmhead.hip drives these from sv_verify.hip): the decision
 // that picks the draw's hidden rows, and the draw over fp32 logit rows.
-hipError_t launch_lm_plan(const Params& P, hipStream_t s);
 hipError_t launch_draw_f32(bool vec, const Params& P, const Plan& L, hipStream_t s);
 
 }  // namespace sv

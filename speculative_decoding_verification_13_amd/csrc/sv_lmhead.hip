@@ -1,19 +1,21 @@
 // Verification from LM-head hidden states for gfx950: the logits l = h W^T of
 // every draft and target row are formed on the matrix cores (bf16 operands,
-// fp32 accumulation) and reduced in the GEMM's epilogue to per-row softmax
-// partials, so the [rows, V] logit rows are never stored. Only the two rows
-// the final draw needs per sequence (p_n, and q_n for a residual) are formed
-// again and kept, as fp32.
+// fp32 accumulation), reduced in the GEMM's epilogue to per-row softmax
+// partials, and stored as fp32 for the final draw, which reads two rows per
+// sequence (p_n, and q_n for a residual).
 //
 //   k_lm_stats        draft rows, then target rows: per (row, 384-id vocab
-//                     tile) the packed (max, sum of 2^(l*c - R)) partial, and
-//                     the logit at the row's token
+//                     tile) the packed (max, sum of 2^(l*c - R)) partial, the
+//                     logit at the row's token, and the logits themselves
 //   k_lm_merge        per row: the vocabulary tiles' partials merged into one
 //                     (and returned to zero)
-//   k_lm_plan         per sequence: the decision, naming the draw's rows
-//   k_lm_rows         those rows' logits into a [2B, V] fp32 array
-//   k_draw            the decision again, the outputs, and the inverse-CDF draw
-//                     over the stored rows (the same kernel as the logit path)
+//   k_draw            the decision, the outputs, and the inverse-CDF draw over
+//                     the stored rows (the same kernel as the logit path)
+//
+// Storing every row costs the statistics GEMM about 95 us at B = 64, K = 8,
+// V = 128256 (558 MB of writes beside its loads); forming the two draw rows of
+// each sequence again instead streamed both weights a second time (1.58 GB,
+// 303-336 us).
 //
 // Greedy verification (temperature 0) reads no draft rows: k_lm_stats<true>
 // runs on the target rows alone, with per tile the packed (max, argmax with
@@ -37,40 +39,11 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Draw rows' GEMM (k_lm_rows). Block tile: 128 rows x (WN * 32 * NB)
-// vocabulary ids, 64 hidden elements per step. Waves in a 2 x WN arrangement,
-// each a 64 x (32 * NB) sub-tile of 2 x NB 32 x 32 MFMA tiles. LDS rows carry
-// 8 bf16 of padding so that the 32 lanes reading one operand column touch
-// distinct banks. The GEMM is HBM-bound (one live row per sequence and
-// model): eight waves of 64 x 128, a 512-id tile, keep the most weight bytes
-// in flight per block (measured 303-306 us against 318-320 with four such
-// waves and 357 with four waves of 64 x 64).
-constexpr int kLmBM = 128;
-constexpr int kLmRowsWN = 4, kLmRowsNB = 4;
-#ifndef SV_LM_BK
-#define SV_LM_BK 64
-#endif
-constexpr int kLmBK = SV_LM_BK;
-constexpr int kLmLds = kLmBK + 8;
-constexpr int kLmCpr = kLmBK / 8;            // 16-byte chunks per tile row and step
 constexpr int kXcds = 8;  // blocks are dealt round-robin to the eight XCDs
-
-// Shape of a block with WN waves along the vocabulary, each NB MFMA tiles wide.
-template <int WN, int NB>
-struct LmTile {
-  static constexpr int kThreads = 2 * WN * kWave;        // two waves along the rows
-  static constexpr int kBN = WN * 32 * NB;               // vocabulary ids per block
-  static constexpr int kRpp = kThreads / kLmCpr;         // tile rows one staging pass covers
-  static constexpr int kPassesA = kLmBM / kRpp;          // passes per hidden-state tile
-  static constexpr int kPassesB = kBN / kRpp;            // passes per weight tile
-  static_assert(kLmBM % kRpp == 0 && kBN % kRpp == 0, "the staging passes must tile the block");
-};
 
 struct LmGemm {
   const uint16_t* H;   // hidden rows, bf16 bits, row stride D
   const uint16_t* W;   // LM-head weight [V, D], bf16 bits
-  const int* gather;   // row m reads hidden row gather[m * gather_step] (< 0: none); null: m
-  int gather_step;
   int M, D, V, NT, MT;  // rows, hidden size, vocabulary, vocabulary tiles, row tiles
   // statistics epilogue
   unsigned long long* part;  // [(unit0 + m) * NT + vt]
@@ -80,10 +53,7 @@ struct LmGemm {
   int target;                // 1: rows are target rows, their token is x_i for i < K
   const int32_t* tokens;
   float c;
-  // logits: row m to out[(m * out_step + out_row0) * V + v] (the draw rows'
-  // GEMM; the statistics GEMM when not null)
-  float* out;
-  int out_step, out_row0;
+  float* out;                // logits: row m to out[m * V + v] (null: not stored)
 };
 
 // Two GEMMs in one launch (the draft's and the target's): blocks below n0
@@ -93,122 +63,6 @@ struct LmPair {
   LmGemm g[2];
   int n0;
 };
-
-// One block: a 128 x LmTile<WN, NB>::kBN tile of logits, stored to out. The
-// block order is XCD-aware: block g runs on XCD g % 8, and the row tiles of
-// one vocabulary tile are consecutive blocks of one XCD, so its weight tile is
-// fetched into that XCD's L2 once and read from there by the other row tiles.
-template <int WN, int NB>
-__global__ __launch_bounds__(2 * WN * kWave, 2) void k_lm_rows(const LmPair PR) {
-  using T = LmTile<WN, NB>;
-  constexpr int kLmNB = NB;
-  constexpr int kLmBN = T::kBN, kLmRpp = T::kRpp;
-  constexpr int kLmPasses = T::kPassesA, kLmPassesB = T::kPassesB;
-  const bool second = (int)blockIdx.x >= PR.n0;
-  const LmGemm& G = PR.g[second ? 1 : 0];
-  __shared__ __align__(16) uint16_t sAB[(kLmBM + kLmBN) * kLmLds];
-  uint16_t* const sA = sAB;
-  uint16_t* const sB = sAB + kLmBM * kLmLds;
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int wm = wave & 1, wn = wave >> 1;
-  const int g = (int)blockIdx.x - (second ? PR.n0 : 0);
-  const int idx = g / kXcds;
-  const int vt = (idx / G.MT) * kXcds + g % kXcds;
-  const int mt = idx % G.MT;
-  if (vt >= G.NT) return;
-  const int m0 = mt * kLmBM, v0 = vt * kLmBN;
-
-  f32x16 acc[2][kLmNB];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < kLmNB; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
-  // Global -> LDS staging: chunk q = tid + T::kThreads * j (j < kLmPasses) is tile
-  // row q / kLmCpr, hidden elements 8 * (q % kLmCpr) .. + 7 of the step.
-  const uint16_t* arow[kLmPasses];
-  const uint16_t* brow[kLmPassesB];
-  const int kc = (tid % kLmCpr) * 8;
-#pragma unroll
-  for (int j = 0; j < kLmPasses; ++j) {
-    const int r = tid / kLmCpr + kLmRpp * j;
-    const int m = m0 + r;
-    int h = -1;
-    if (m < G.M) h = G.gather != nullptr ? G.gather[(size_t)m * G.gather_step] : m;
-    arow[j] = h >= 0 ? G.H + (size_t)h * G.D : nullptr;
-  }
-#pragma unroll
-  for (int j = 0; j < kLmPassesB; ++j) {
-    const int v = v0 + tid / kLmCpr + kLmRpp * j;
-    brow[j] = v < G.V ? G.W + (size_t)v * G.D : nullptr;
-  }
-  uint4 ra[kLmPasses], rb[kLmPassesB];
-  auto fetch = [&](int k0) {
-    const bool kin = k0 + kc < G.D;
-#pragma unroll
-    for (int j = 0; j < kLmPasses; ++j)
-      ra[j] = (arow[j] != nullptr && kin)
-                  ? *reinterpret_cast<const uint4*>(arow[j] + k0 + kc) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < kLmPassesB; ++j)
-      rb[j] = (brow[j] != nullptr && kin)
-                  ? *reinterpret_cast<const uint4*>(brow[j] + k0 + kc) : make_uint4(0, 0, 0, 0);
-  };
-
-  fetch(0);
-  for (int k0 = 0; k0 < G.D; k0 += kLmBK) {
-    __syncthreads();  // every wave is done with the previous step's tiles
-#pragma unroll
-    for (int j = 0; j < kLmPasses; ++j)
-      *reinterpret_cast<uint4*>(&sA[(tid / kLmCpr + kLmRpp * j) * kLmLds + kc]) = ra[j];
-#pragma unroll
-    for (int j = 0; j < kLmPassesB; ++j)
-      *reinterpret_cast<uint4*>(&sB[(tid / kLmCpr + kLmRpp * j) * kLmLds + kc]) = rb[j];
-    __syncthreads();
-    if (k0 + kLmBK < G.D) fetch(k0 + kLmBK);  // next step's operands, in flight during the MFMAs
-#pragma unroll
-    for (int ks = 0; ks < kLmBK / 16; ++ks) {
-      // lane l holds 8 consecutive hidden elements (16 * ks + 8 * (l / 32) ...)
-      // of row (or vocabulary id) l % 32 of each 32 x 32 tile
-      const int kk = ks * 16 + (lane >> 5) * 8;
-      bf16x8 af[2], bfr[kLmNB];
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-        af[a] = *reinterpret_cast<const bf16x8*>(&sA[(wm * 64 + a * 32 + (lane & 31)) * kLmLds + kk]);
-#pragma unroll
-      for (int b = 0; b < kLmNB; ++b)
-        bfr[b] = *reinterpret_cast<const bf16x8*>(
-            &sB[(wn * 32 * kLmNB + b * 32 + (lane & 31)) * kLmLds + kk]);
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < kLmNB; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
-    }
-  }
-
-  // Element i of tile (a, b) in lane l: row wm*64 + a*32 + 8*(i/4) + 4*(l/32)
-  // + i%4, vocabulary id v0 + wn*32*kLmNB + b*32 + l%32.
-#pragma unroll
-  for (int a = 0; a < 2; ++a) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int rl = wm * 64 + a * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      const int m = m0 + rl;
-      if (m >= G.M) continue;
-      if (G.gather != nullptr && G.gather[(size_t)m * G.gather_step] < 0) continue;
-      float* orow = G.out + (size_t)(m * G.out_step + G.out_row0) * G.V;
-#pragma unroll
-      for (int b = 0; b < kLmNB; ++b) {
-        const int v = v0 + wn * 32 * kLmNB + b * 32 + (lane & 31);
-        if (v < G.V) orow[v] = acc[a][b][i];
-      }
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Statistics GEMM (k_lm_stats). Block tile: 192 rows x 384 vocabulary ids, 12
@@ -251,10 +105,11 @@ typedef __attribute__((address_space(1))) void* global_void_ptr;
 constexpr int kWaitVm0 = (7 << 4) | (15 << 8);
 
 // One block: a 192 x 384 tile of logits, reduced per row and 64-id slice in
-// the epilogue and merged into one partial per (row, tile). Block order as in
-// k_lm_rows (XCD-aware: the row tiles of one vocabulary tile are consecutive
-// blocks of one XCD). GREEDY: (max, argmax, NaN/+inf) partials instead of
-// (max, sum).
+// the epilogue and merged into one partial per (row, tile). The block order is
+// XCD-aware: block g runs on XCD g % 8, and the row tiles of one vocabulary
+// tile are consecutive blocks of one XCD, so its weight tile is fetched into
+// that XCD's L2 once and read from there by the other row tiles. GREEDY:
+// (max, argmax, NaN/+inf) partials instead of (max, sum).
 template <bool GREEDY>
 __global__ __launch_bounds__(kStThreads, 3) void k_lm_stats(const LmPair PR) {
   const bool second = (int)blockIdx.x >= PR.n0;
@@ -388,8 +243,10 @@ __global__ __launch_bounds__(kStThreads, 3) void k_lm_stats(const LmPair PR) {
 
   // Element i of tile (a, b) in lane l: row wm*96 + a*32 + 8*(i/4) + 4*(l/32)
   // + i%4, vocabulary id v0 + wn*64 + b*32 + l%32.
-  // The logits themselves only when the caller asked for them
-  // (spec_verify_lmhead_diag).
+  // The logits themselves: the sampling call's draw reads two rows per
+  // sequence, and spec_verify_lmhead_diag returns them. Non-temporal stores:
+  // nothing reads them again before the draw, so they need not displace the
+  // operands in L2.
   if (G.out != nullptr) {
 #pragma unroll
     for (int a = 0; a < kStTM; ++a) {
@@ -401,7 +258,7 @@ __global__ __launch_bounds__(kStThreads, 3) void k_lm_stats(const LmPair PR) {
 #pragma unroll
         for (int b = 0; b < kStTN; ++b) {
           const int v = v0 + wn * kStTN * 32 + b * 32 + (lane & 31);
-          if (v < G.V) orow[v] = acc[a][b][i];
+          if (v < G.V) __builtin_nontemporal_store(acc[a][b][i], orow + v);
         }
       }
     }
@@ -598,15 +455,15 @@ size_t align_up(size_t x) { return (x + 255) / 256 * 256; }
 //   tiles[B * ntiles]            draw-weight tile sums
 //   part[units * NT]             vocabulary-tile partials of the GEMM epilogue
 //   tok[units]                   logits at the units' tokens
-//   draw_rows[2B]                hidden rows of each sequence's draw
 // all zero between calls, and at the tail of the caller's workspace
-//   rows[2B * V] fp32            logits of those rows (rewritten every call)
+//   logits[units * V] fp32       every row's logits, draft rows first (rewritten
+//                                by every sampling call; greedy calls leave it)
 // Calls of any shape may share a workspace sized for the largest: every
-// shape's zero regions start at the front and its rows end at the back, and
+// shape's zero regions start at the front and its logits end at the back, and
 // neither reaches the other's.
 struct LmPlan {
-  size_t off_draw_done, off_seq_flags, off_slots, off_tiles, off_part, off_tok, off_draw_rows,
-      zero_bytes, rows_bytes, total;
+  size_t off_draw_done, off_seq_flags, off_slots, off_tiles, off_part, off_tok, zero_bytes,
+      logits_bytes, total;
   int NT, nvec, dchunks, ntiles;
 };
 
@@ -632,11 +489,9 @@ bool lm_plan(int B, int K, int V, LmPlan& L) {
   off += align_up((size_t)units * L.NT * 8);
   L.off_tok = off;
   off += align_up((size_t)units * 4);
-  L.off_draw_rows = off;
-  off += align_up((size_t)B * 2 * 4);
   L.zero_bytes = off;
-  L.rows_bytes = align_up((size_t)B * 2 * V * 4);
-  L.total = off + L.rows_bytes;
+  L.logits_bytes = align_up((size_t)units * (size_t)V * 4);
+  L.total = off + L.logits_bytes;
   return true;
 }
 
@@ -693,14 +548,19 @@ int run_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
   if (gemm_t + kXcds * 4 > (long long)INT_MAX || gemm_d + kXcds * 4 > (long long)INT_MAX)
     return SV_EUNSUPPORTED;
   char* ws = static_cast<char*>(workspace);
-  // the draw rows at the tail of the workspace (256-byte aligned)
-  const size_t off_rows = (workspace_bytes - L.rows_bytes) / 256 * 256;
-  if (off_rows < L.zero_bytes) return SV_EWORKSPACE;
-  float* lrows = reinterpret_cast<float*>(ws + off_rows);
+  // every row's logits at the tail of the workspace (256-byte aligned), draft
+  // rows first; rows the caller asked for (the diag entry point) go to the
+  // caller's arrays instead, and the draw reads them there
+  const size_t off_logits = (workspace_bytes - L.logits_bytes) / 256 * 256;
+  if (off_logits < L.zero_bytes) return SV_EWORKSPACE;
+  float* const ws_logits = reinterpret_cast<float*>(ws + off_logits);
+  float* const ldraft = logits_draft != nullptr ? logits_draft : ws_logits;
+  float* const ltarget =
+      logits_target != nullptr ? logits_target : ws_logits + (size_t)total_draft * V;
 
   Params P{};
-  P.draft = lrows;
-  P.target = lrows;
+  P.draft = ldraft;
+  P.target = ltarget;
   P.tokens = draft_tokens;
   P.uniforms = uniforms;
   P.cu = nullptr;
@@ -724,17 +584,15 @@ int run_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
   P.draw_done = reinterpret_cast<int*>(ws + L.off_draw_done);
   P.seq_flags = reinterpret_cast<int*>(ws + L.off_seq_flags);
   P.tok_logits = reinterpret_cast<float*>(ws + L.off_tok);
-  P.draw_remap = 1;
-  P.draw_rows = reinterpret_cast<int*>(ws + L.off_draw_rows);
   unsigned long long* part = reinterpret_cast<unsigned long long*>(ws + L.off_part);
 
-  auto grid_of = [&](int M, int NT, int BM) {
-    const int MT = (M + BM - 1) / BM;
+  auto grid_of = [&](int M, int NT) {
+    const int MT = (M + kStBM - 1) / kStBM;
     const long long per_xcd = (NT + kXcds - 1) / kXcds;  // vocabulary tiles per XCD
     return std::make_pair(MT, (unsigned)(per_xcd * MT * kXcds));
   };
   // stage events: before the statistics GEMMs, then after them, after the
-  // merge and decision, after the draw rows' GEMMs, and after the draw
+  // merge, and after the draw
   int e = 0;
   auto stage = [&]() {
     if (stage_events != nullptr && e < n_stage_events)
@@ -754,10 +612,8 @@ int run_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
     G.K = K;
     G.tokens = draft_tokens;
     G.c = P.c;
-    G.out_step = 1;
-    G.out_row0 = 0;
     if (total_draft > 0 && !greedy) {
-      auto [MT, blocks] = grid_of(total_draft, L.NT, kStBM);
+      auto [MT, blocks] = grid_of(total_draft, L.NT);
       G.H = static_cast<const uint16_t*>(hidden_draft);
       G.W = static_cast<const uint16_t*>(weight_draft);
       G.D = d_draft;
@@ -765,12 +621,12 @@ int run_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
       G.MT = MT;
       G.unit0 = 0;
       G.target = 0;
-      G.out = logits_draft;
+      G.out = ldraft;
       S.g[0] = G;
       S.n0 = (int)blocks;
       blocks_stats = blocks;
     }
-    auto [MT, blocks] = grid_of(rows, L.NT, kStBM);
+    auto [MT, blocks] = grid_of(rows, L.NT);
     G.H = static_cast<const uint16_t*>(hidden_target);
     G.W = static_cast<const uint16_t*>(weight_target);
     G.D = d_target;
@@ -778,7 +634,8 @@ int run_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
     G.MT = MT;
     G.unit0 = total_draft;
     G.target = 1;
-    G.out = logits_target;
+    // greedy: the draw reads no rows, so only the diag caller's are stored
+    G.out = greedy ? logits_target : ltarget;
     if (blocks_stats == 0) {  // the target rows alone
       S.g[0] = G;
       S.n0 = (int)blocks;
@@ -794,53 +651,12 @@ int run_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
   if (hipGetLastError() != hipSuccess || !stage()) return SV_EHIP;
   if (greedy) {
     // the target rows' argmax partials; the decision and the outputs are the
-    // draw kernel's (the stage events keep their places)
+    // draw kernel's
     hipLaunchKernelGGL(k_lm_merge_am, dim3((unsigned)rows), dim3(kThreads), 0, stream, part,
                        P.slots, L.NT, (long long)total_draft);
-    if (hipGetLastError() != hipSuccess || !stage() || !stage()) return SV_EHIP;
-    Plan DL{};
-    DL.draw_blocks = (long long)B * L.dchunks;
-    if (launch_draw_f32(L.nvec != V, P, DL, stream) != hipSuccess) return SV_EHIP;
-    while (e < n_stage_events && stage_events != nullptr)
-      if (!stage()) return SV_EHIP;
-    return SV_OK;
-  }
-  hipLaunchKernelGGL(k_lm_merge, dim3((unsigned)(total_draft + rows)), dim3(kThreads), 0, stream,
-                     part, P.slots, L.NT, P.c);
-  if (hipGetLastError() != hipSuccess) return SV_EHIP;
-  if (launch_lm_plan(P, stream) != hipSuccess || !stage()) return SV_EHIP;
-  // logits of the draw's rows, one launch: target row of position n -> row 2b,
-  // draft row -> 2b + 1
-  {
-    LmPair R2{};
-    LmGemm R{};
-    R.V = V;
-    R.NT = (V + LmTile<kLmRowsWN, kLmRowsNB>::kBN - 1) / LmTile<kLmRowsWN, kLmRowsNB>::kBN;
-    R.out = lrows;
-    R.out_step = 2;
-    R.gather_step = 2;
-    R.M = B;
-    auto [MT, blocks] = grid_of(B, R.NT, kLmBM);
-    R.MT = MT;
-    R.H = static_cast<const uint16_t*>(hidden_target);
-    R.W = static_cast<const uint16_t*>(weight_target);
-    R.D = d_target;
-    R.gather = P.draw_rows;
-    R.out_row0 = 0;
-    R2.g[0] = R;
-    R2.n0 = (int)blocks;
-    unsigned total = blocks;
-    if (total_draft > 0) {
-      R.H = static_cast<const uint16_t*>(hidden_draft);
-      R.W = static_cast<const uint16_t*>(weight_draft);
-      R.D = d_draft;
-      R.gather = P.draw_rows + 1;
-      R.out_row0 = 1;
-      R2.g[1] = R;
-      total += blocks;
-    }
-    hipLaunchKernelGGL((k_lm_rows<kLmRowsWN, kLmRowsNB>), dim3(total),
-                       dim3(LmTile<kLmRowsWN, kLmRowsNB>::kThreads), 0, stream, R2);
+  } else {
+    hipLaunchKernelGGL(k_lm_merge, dim3((unsigned)(total_draft + rows)), dim3(kThreads), 0,
+                       stream, part, P.slots, L.NT, P.c);
   }
   if (hipGetLastError() != hipSuccess || !stage()) return SV_EHIP;
   Plan DL{};

@@ -376,8 +376,8 @@ __device__ Job decide(const Params& P, int b, int d0, int kb, bool greedy, bool 
   Job j;
   j.mode = draws ? (n < kb ? kJobResidual : kJobBonus) : kJobNone;
   j.n = n;
-  j.prow = P.draw_remap ? 2 * b : t0 + n;
-  j.qrow = P.draw_remap ? 2 * b + 1 : d0 + n;
+  j.prow = t0 + n;
+  j.qrow = d0 + n;
   j.Rq = ref_of(S.m[0][n], c);
   j.invSq = 1.0f / S.s[0][n];
   j.Rp = ref_of(S.m[1][n], c);
@@ -1875,12 +1875,11 @@ __device__ void draw_unit(const Params& P, int idx) {
     }
   }
   if (P.tok_logits != nullptr) {
-    // LM-head path: the token logits and draw rows of the sequence
+    // LM-head path: the token logits of the sequence
     for (int r = tid; r < 2 * kb + 1; r += kThreads) {
       const long long u = r < kb ? unit_of(P, false, d0 + r) : unit_of(P, true, d0 + b + (r - kb));
       P.tok_logits[u] = 0.f;
     }
-    if (tid < 2) P.draw_rows[2 * b + tid] = 0;
   }
   if (solo) return;  // no tile sums or counter were written
   for (int t = tid; t < P.ntiles; t += kThreads) pub_f(P.tiles + (size_t)b * P.ntiles + t, 0.f);
@@ -1891,25 +1890,6 @@ __device__ void draw_unit(const Params& P, int idx) {
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_draw(const Params P) {
   draw_unit<DT, VEC>(P, blockIdx.x);
-}
-
-// Decision of each sequence ahead of the LM-head path's final draw (one block
-// per sequence, nothing written but the plan): the hidden rows whose logits the
-// draw needs, the target row of position n and, for a residual draw, the
-// draft row of position n; -1 where there is none.
-__global__ __launch_bounds__(kThreads) void k_lm_plan(const Params P) {
-  __shared__ Dec S;
-  const int b = blockIdx.x;
-  int d0, kb;
-  if (!seq_bounds(P, b, d0, kb)) {
-    if (threadIdx.x < 2) P.draw_rows[2 * b + threadIdx.x] = -1;
-    return;
-  }
-  const Job j = decide<SV_F32>(P, b, d0, kb, false, false, S);
-  if (threadIdx.x == 0) {
-    P.draw_rows[2 * b] = j.mode != kJobNone ? d0 + b + j.n : -1;
-    P.draw_rows[2 * b + 1] = j.mode == kJobResidual ? d0 + j.n : -1;
-  }
 }
 
 __global__ void k_fill_zero(uint4* p, size_t n16) {
@@ -2008,11 +1988,6 @@ hipError_t launch_row_stats(int dtype, bool vec, const Params& P, const Plan& L,
     default:
       return vec ? launch_row_stats_t<SV_BF16, true>(P, L, s) : launch_row_stats_t<SV_BF16, false>(P, L, s);
   }
-}
-
-hipError_t launch_lm_plan(const Params& P, hipStream_t s) {
-  hipLaunchKernelGGL(k_lm_plan, dim3((unsigned)P.B), dim3(kThreads), 0, s, P);
-  return hipGetLastError();
 }
 
 hipError_t launch_draw_f32(bool vec, const Params& P, const Plan& L, hipStream_t s) {
