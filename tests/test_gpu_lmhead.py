@@ -140,6 +140,37 @@ def test_lmhead_workspace_returns_to_zero_and_serves_other_shapes():
         assert int((ws[:zb] != 0).sum()) == 0
 
 
+@pytest.mark.parametrize("which", ["both", "target", "draft"])
+def test_lmhead_diag_rows_serve_the_draw(which):
+    """A sampling call stores every row's logits and draws from them; the diag
+    entry point stores the rows the caller asks for in the caller's arrays
+    instead, and the draw reads them there. Outputs must equal the plain
+    call's bit for bit, and the returned rows the exact logits (the workload's
+    products are exact in fp32). Hidden sizes with a partial last step and
+    rows past one 192-row tile."""
+    import speculative_decoding_verification_13_amd as sv
+    w = W.make_lmhead(B=9, K=3, V=4100, d_draft=200, d_target=264, seed=2350)
+    toks = _draft_tokens(w)
+    d = _device(w, toks)
+    B, K, V, T = w["B"], w["K"], w["V"], w["temperature"]
+    out0, num0 = _run(w, d)
+    ld = torch.full((B * K, V), float("nan"), device="cuda") if which in ("both", "draft") else None
+    lt = torch.full((B * (K + 1), V), float("nan"), device="cuda") if which in ("both", "target") \
+        else None
+    out1, num1 = sv.spec_verify_lmhead(d["hq"], d["wq"], d["hp"], d["wp"], d["toks"], d["uni"],
+                                       B, K, V, T, logits_draft=ld, logits_target=lt)
+    torch.cuda.synchronize()
+    assert np.array_equal(out1.cpu().numpy().reshape(-1), out0)
+    assert np.array_equal(num1.cpu().numpy(), num0)
+    s = W.LM_H_SCALE * W.LM_W_SCALE
+    if ld is not None:
+        ref = oracle.lmhead_logits(w["hq"], w["wq"], s)
+        assert np.array_equal(ld.cpu().numpy().astype(np.float64), ref)
+    if lt is not None:
+        ref = oracle.lmhead_logits(w["hp"], w["wp"], s)
+        assert np.array_equal(lt.cpu().numpy().astype(np.float64), ref)
+
+
 def test_lmhead_invalid_token_flagged():
     w = W.make_lmhead(B=4, K=3, V=2000, d_draft=64, d_target=64, seed=2300)
     toks = _draft_tokens(w).copy()
