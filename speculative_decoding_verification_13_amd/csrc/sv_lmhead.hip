@@ -142,8 +142,8 @@ __global__ __launch_bounds__(kStThreads, 3) void k_lm_stats(const LmPair PR) {
   // 64 banks; with 128-byte rows, rows r and r + 1 sit on the two halves of
   // the banks, so swz(r) = (r / 2) % 8 gives the 16 rows that 16 lanes read
   // at one chunk column 16 distinct bank groups (r % 8 would put rows r and
-  // r + 8 on the same ones: measured 10% slower). Rows past M or V repeat
-  // the last row; their results are never used.
+  // r + 8 on the same ones: 2-way conflicts on every read). Rows past M or V
+  // repeat the last row; their results are never used.
   const uint16_t* src[kStDma];
   int kch[kStDma];  // first hidden element of this lane's chunk within a step
 #pragma unroll
