@@ -417,10 +417,11 @@ def spec_verify_lmhead(hidden_draft, weight_draft, hidden_target, weight_target,
     weight_target [V, Dp]. ``stage_events`` is an optional list of raw
     hipEvent_t handles (ints) recorded between the stages. ``logits_draft``
     [B*K, V] and ``logits_target`` [B*(K+1), V] (float32 device tensors, or
-    None) receive the logits the statistics GEMM formed (the diag entry point).
-    Temperature 0 verifies greedily: the draft pair and the uniforms may be
-    None, and no draft logits are formed. Returns (out_tokens [B, K+1],
-    num_accepted [B])."""
+    None) receive the logits the statistics GEMM formed (the diag entry point);
+    a sampling call's draw then reads its rows there, so they must not overlap
+    the workspace or each other. Temperature 0 verifies greedily: the draft
+    pair and the uniforms may be None, and no draft logits are formed. Returns
+    (out_tokens [B, K+1], num_accepted [B])."""
     B, K, V = int(B), int(K), int(V)
     greedy = float(temperature) == 0.0  # reads no draft rows and no uniforms
     dev = hidden_target.device
