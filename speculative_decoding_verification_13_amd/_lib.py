@@ -448,6 +448,15 @@ def spec_verify_lmhead(hidden_draft, weight_draft, hidden_target, weight_target,
         n_ev = len(stage_events)
     _expect(logits_draft, "logits_draft", torch.float32, B * K * V, allow_none=True)
     _expect(logits_target, "logits_target", torch.float32, B * (K + 1) * V, allow_none=True)
+    # the call writes the logits arrays and its draw reads them back, so they
+    # may share no byte with the workspace or with each other
+    spans = [(t.data_ptr(), t.data_ptr() + _nbytes(t), name) for t, name in
+             ((workspace, "workspace"), (logits_draft, "logits_draft"),
+              (logits_target, "logits_target")) if t is not None and t.numel() > 0]
+    for i, (a0, a1, na) in enumerate(spans):
+        for b0, b1, nb in spans[i + 1:]:
+            if a0 < b1 and b0 < a1:
+                raise ValueError(f"{na} and {nb} overlap")
     args = [_ptr(hidden_draft), _ptr(weight_draft), dq, _ptr(hidden_target), _ptr(weight_target),
             dp, _ptr(draft_tokens), _ptr(uniforms), B, K, V,
             float(temperature), _ptr(out_tokens), _ptr(num_accepted), _ptr(workspace),

@@ -103,3 +103,28 @@ def test_lmhead_checks():
         sv.spec_verify_lmhead(hq, wq, hp, wp, toks, None, B, K, Vl, 1.0)
     with pytest.raises(ValueError, match="hidden_draft"):
         sv.spec_verify_lmhead(None, wq, hp, wp, toks, u, B, K, Vl, 1.0)
+
+
+def test_lmhead_logits_arrays_must_not_overlap():
+    """A sampling call writes the diag logits arrays and its draw reads them
+    back, so the binding refuses arrays that share bytes with each other or
+    with the workspace."""
+    dq, dp, Vl = 16, 32, 40
+    hq = torch.zeros(B * K, dq, dtype=torch.bfloat16)
+    wq = torch.zeros(Vl, dq, dtype=torch.bfloat16)
+    hp = torch.zeros(B * (K + 1), dp, dtype=torch.bfloat16)
+    wp = torch.zeros(Vl, dp, dtype=torch.bfloat16)
+    toks = torch.zeros(B * K, dtype=torch.int32)
+    u = torch.zeros(B * (K + 1), dtype=torch.float32)
+    both = torch.zeros(B * (K + 1) * Vl + B * K * Vl, dtype=torch.float32)
+    lt = both[:B * (K + 1) * Vl]
+    ld = both[B * (K + 1) * Vl - 1:B * (K + 1) * Vl - 1 + B * K * Vl]  # one float shared
+    ws = torch.zeros(int(sv.lib().spec_verify_lmhead_workspace_bytes(B, K, Vl)) + 4 * B * K * Vl,
+                     dtype=torch.uint8)
+    with pytest.raises(ValueError, match="overlap"):
+        sv.spec_verify_lmhead(hq, wq, hp, wp, toks, u, B, K, Vl, 1.0, workspace=ws,
+                              logits_draft=ld, logits_target=lt)
+    inside = ws[-4 * B * K * Vl:].view(torch.float32)
+    with pytest.raises(ValueError, match="overlap"):
+        sv.spec_verify_lmhead(hq, wq, hp, wp, toks, u, B, K, Vl, 1.0, workspace=ws,
+                              logits_draft=inside)
