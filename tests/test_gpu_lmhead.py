@@ -102,6 +102,7 @@ SMALL = [
     dict(B=2, K=0, V=3000, d_draft=64, d_target=64),         # no drafts: bonus only
     dict(B=4, K=8, V=20000, d_draft=512, d_target=1024),     # several row tiles
     dict(B=20, K=6, V=9000, d_draft=256, d_target=256, temperature=1.3),
+    dict(B=25, K=8, V=1000, d_draft=72, d_target=136),       # two 192-row tiles and a tail
 ]
 
 
