@@ -124,3 +124,59 @@ def test_graph_replays_several_chains():
         assert all(torch.equal(a, e) for a, e in zip((out, num, chain), eager))
     assert int((ws != 0).sum()) == 0
 
+
+
+@pytest.mark.parametrize("temperature", [0.9, 0.0], ids=["sampling", "greedy"])
+def test_graph_replays_lmhead(temperature):
+    """spec_verify_lmhead captured and replayed: the statistics GEMM, the merge
+    of its partials and the draw (which reads the rows the GEMM stored in the
+    workspace); its zero regions return to zero, so replays must match the
+    eager call."""
+    import speculative_decoding_verification_13_amd as sv
+    w = W.make_lmhead(B=6, K=4, V=3000, d_draft=136, d_target=200, temperature=temperature,
+                      seed=3060)
+    B, K, V = w["B"], w["K"], w["V"]
+    dev = "cuda"
+    s_h, s_w = W.LM_H_SCALE, W.LM_W_SCALE
+    hp = W.lmhead_to_device(w["hp"], s_h, dev)
+    wp = W.lmhead_to_device(w["wp"], s_w, dev)
+    greedy = temperature == 0.0
+    hq = None if greedy else W.lmhead_to_device(w["hq"], s_h, dev)
+    wq = None if greedy else W.lmhead_to_device(w["wq"], s_w, dev)
+    toks = torch.from_numpy((np.arange(B * K) * 7919 % V).astype(np.int32)).to(dev)
+    uni = None if greedy else torch.from_numpy(w["uniforms"]).to(dev)
+    print(f"[gpu] graph lmhead B={B} K={K} V={V} T={temperature}", flush=True)
+    ws = sv.make_lmhead_workspace(B, K, V, dev)
+    zb = int(sv.lib().spec_verify_lmhead_zero_bytes(B, K, V))
+    out = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    num = torch.empty((B,), dtype=torch.int32, device=dev)
+
+    def call():
+        sv.spec_verify_lmhead(hq, wq, hp, wp, toks, uni, B, K, V, temperature, out_tokens=out,
+                              num_accepted=num, workspace=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager_out, eager_num = out.clone(), num.clone()
+    assert int((eager_num >= 0).sum()) == B
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    torch.cuda.synchronize()
+    scratch = torch.randn(1 << 20, device=dev)
+    for r in range(5):
+        out.fill_(-7)
+        num.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_out), f"replay {r}"
+        assert torch.equal(num, eager_num), f"replay {r}"
+        scratch.mul_(1.0001).add_(0.5)
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_out) and torch.equal(num, eager_num)
+    assert int((ws[:zb] != 0).sum()) == 0
