@@ -381,10 +381,10 @@ int spec_verify_lmhead(const void* hidden_draft, const void* weight_draft, int d
  *   logits_target  float [B*(K+1), V]  GEMM formed them (fp32 accumulation),
  *                                      before any reduction (a greedy call
  *                                      forms no draft logits)
- * Device memory owned by the caller. A sampling call stores these rows in
- * place of the workspace's and its draw reads them there, so they must not
- * overlap the workspace or each other; a greedy call writes logits_target
- * only for this output. */
+ * Device memory owned by the caller, 16-byte aligned (else SV_EINVAL). A
+ * sampling call stores these rows in place of the workspace's and its draw
+ * reads them there, so they must not overlap the workspace or each other; a
+ * greedy call writes logits_target only for this output. */
 typedef struct sv_lmhead_diag {
   float* logits_draft;
   float* logits_target;

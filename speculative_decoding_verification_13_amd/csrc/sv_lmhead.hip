@@ -534,7 +534,10 @@ int run_lmhead(const void* hidden_draft, const void* weight_draft, int d_draft,
   if (K > 0 && (draft_tokens == nullptr ||
                 (!greedy && (hidden_draft == nullptr || weight_draft == nullptr))))
     return SV_EINVAL;
-  const void* ptrs[4] = {hidden_draft, weight_draft, hidden_target, weight_target};
+  // the draw reads the stored rows, the caller's logits arrays among them, in
+  // 16-byte vectors
+  const void* ptrs[6] = {hidden_draft, weight_draft, hidden_target, weight_target, logits_draft,
+                         logits_target};
   for (const void* p : ptrs)
     if (p != nullptr && ((uintptr_t)p & 15u) != 0) return SV_EINVAL;
   LmPlan L;

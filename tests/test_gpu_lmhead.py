@@ -194,6 +194,11 @@ def test_lmhead_argument_errors():
     with pytest.raises(sv.SpecVerifyError):
         sv.spec_verify_lmhead(d["hq"], d["wq"], bad, d["wp"][:, :60].contiguous(), d["toks"],
                               d["uni"], 2, 2, 1000, 0.7)
+    # a diag logits array the draw would read with misaligned 16-byte loads
+    buf = torch.zeros(2 * 3 * 1000 + 1, dtype=torch.float32, device="cuda")
+    with pytest.raises(sv.SpecVerifyError):
+        sv.spec_verify_lmhead(d["hq"], d["wq"], d["hp"], d["wp"], d["toks"], d["uni"], 2, 2,
+                              1000, 0.7, logits_target=buf[1:])
 
 
 # ------------------------------------------------------------ greedy (T = 0)
