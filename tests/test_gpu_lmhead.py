@@ -103,6 +103,8 @@ SMALL = [
     dict(B=4, K=8, V=20000, d_draft=512, d_target=1024),     # several row tiles
     dict(B=20, K=6, V=9000, d_draft=256, d_target=256, temperature=1.3),
     dict(B=25, K=8, V=1000, d_draft=72, d_target=136),       # two 192-row tiles and a tail
+    dict(B=3, K=2, V=1, d_draft=8, d_target=8),              # one id, one 16-byte chunk a row
+    dict(B=50, K=3, V=383, d_draft=8, d_target=16),          # > 192 rows, V under one tile
 ]
 
 
