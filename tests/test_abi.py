@@ -218,3 +218,22 @@ def test_multi_host_checks(L):
             up(B * tiles * 4)
     assert L.spec_verify_multi_workspace_bytes(4, 5, 4, 1024, 0, 1.0) == 0
     assert L.spec_verify_multi_workspace_bytes(4, 3, 4, 1024, 0, 0.0) == 0
+
+
+def test_lmhead_workspace_sizes(L):
+    """The LM-head workspace: a zero region at the front (counters, merged
+    partials, draw tile sums, the (row, 384-id tile) partials of the GEMM
+    epilogue and the token logits), then every row's fp32 logits, draft rows
+    first. A shape's zero region fits inside a larger shape's, and invalid
+    shapes give 0."""
+    ws, zb = L.spec_verify_lmhead_workspace_bytes, L.spec_verify_lmhead_zero_bytes
+    for B, K, V in ((64, 8, 128256), (3, 0, 1), (25, 8, 1000), (50, 3, 383)):
+        units = B * K + B * (K + 1)
+        total, zero = ws(B, K, V), zb(B, K, V)
+        assert zero % 256 == 0 and total % 256 == 0
+        logits = -(-units * V * 4 // 256) * 256
+        assert total == zero + logits, (B, K, V)
+        tiles = -(-V // 384)
+        assert zero >= units * (8 + tiles * 8 + 4), (B, K, V)  # slots, partials, token logits
+    assert zb(3, 2, 1000) <= zb(6, 5, 8000) and ws(3, 2, 1000) <= ws(6, 5, 8000)
+    assert ws(-1, 2, 100) == 0 and ws(2, -1, 100) == 0 and ws(2, 2, 0) == 0
