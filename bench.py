@@ -83,6 +83,7 @@ class HipEvents:
 KERNEL_SOURCES = {
     "k_verify": ["sv_fused.hip", "sv_rows.h", "sv_device.h", "sv_launch.h"],
     "k_stats": ["sv_verify.hip", "sv_rows.h", "sv_device.h", "sv_launch.h"],
+    "k_lm_stats": ["sv_lmhead.hip", "sv_rows.h", "sv_device.h", "sv_launch.h"],
 }
 
 
@@ -164,8 +165,15 @@ def traffic_summary(args):
     runs, each scaled by what the counter reads for a plain copy of known size."""
     import statistics
     d = args.traffic_from
-    stages = STAGES[1] if W.WORKLOADS[args.workload].get("top_k", 0) <= 0 else STAGES[3]
-    kernel = stages[0] if len(stages) == 1 else "k_stats"
+    lm = args.path == "lmhead"
+    if lm:
+        # the sampling call's statistics GEMM (the greedy call's is k_lm_stats<true>)
+        kernel, workload, match, extra = "k_lm_stats", W.LMHEAD_NAME, "k_lm_stats<false>", \
+            "--path lmhead"
+    else:
+        stages = STAGES[1] if W.WORKLOADS[args.workload].get("top_k", 0) <= 0 else STAGES[3]
+        kernel = stages[0] if len(stages) == 1 else "k_stats"
+        workload, match, extra = args.workload, None, f"--no-other-configs --workload {args.workload}"
     cal_bytes_kib = (1 << 30) / 1024.0
 
     def calib(sub, counter):
@@ -180,28 +188,34 @@ def traffic_summary(args):
     # and timed steps; the calls after them (stage events, acceptance
     # statistics, the sd_t sweep) are left out.
     def kern(sub, counter):
+        def wanted(name):
+            if match:
+                return match in name
+            return f"::{kernel}<" in name or name.startswith(kernel)
         vals = [v for name, v in _counter_per_dispatch(os.path.join(d, sub), counter)
-                if f"::{kernel}<" in name or name.startswith(kernel)]
+                if wanted(name)]
         return statistics.median(vals[1:23] if len(vals) > 1 else vals)
 
     fs, ws_ = calib("cal_fetch", "FETCH_SIZE"), calib("cal_write", "WRITE_SIZE")
     fk, wk = kern("fetch", "FETCH_SIZE"), kern("write", "WRITE_SIZE")
     hbm = (fk * fs + wk * ws_) * 1024.0
     out = {
-        "kernel": kernel, "workload": args.workload,
-        "sd_t": W.WORKLOADS[args.workload].get("sd_t") if args.sd_t is None else args.sd_t,
+        "kernel": kernel, "workload": workload,
+        "sd_t": None if lm else
+                (W.WORKLOADS[args.workload].get("sd_t") if args.sd_t is None else args.sd_t),
         "source_sha256": kernel_source_digest(kernel),
         "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
         "fetch_scale": fs, "write_scale": ws_, "hbm_bytes_per_launch": hbm,
         "commands": [
             f"rocprofv3 --pmc {c} --output-format csv -d <out>/{sub} -o run -- python3 bench.py "
-            f"--cpu-seconds 0 --steps 20 --warmup 2 --no-other-configs --workload {args.workload}"
+            f"--cpu-seconds 0 --steps 20 --warmup 2 {extra}"
             for c, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write"))] + [
             f"rocprofv3 --pmc {c} --output-format csv -d <out>/{sub} -o run -- python3 bench.py "
             "--calibrate-copy" for c, sub in (("FETCH_SIZE", "cal_fetch"), ("WRITE_SIZE", "cal_write"))]
-            + [f"python3 bench.py --traffic-from <out> --workload {args.workload}"],
+            + [f"python3 bench.py --traffic-from <out> "
+               + ("--path lmhead" if lm else f"--workload {args.workload}")],
     }
-    with open(traffic_file(kernel, args.workload), "w") as fh:
+    with open(traffic_file(kernel, workload), "w") as fh:
         json.dump(out, fh, indent=1)
         fh.write("\n")
     print(json.dumps(out), flush=True)
@@ -902,9 +916,18 @@ def bench_lmhead(args, sv):
     achieved = (flops_t + flops_d) / (t_ms * 1e-3) / 1e12
     weight_bytes = 2.0 * V * (dq + dp)
     n = n_sampling
+    # HBM bytes per launch of the statistics GEMM from the counter record,
+    # while the kernel's sources are the ones it was taken on
+    lm_traffic = None
+    tfile = traffic_file("k_lm_stats", W.LMHEAD_NAME)
+    if os.path.exists(tfile):
+        with open(tfile) as fh:
+            tr = json.load(fh)
+        if tr.get("source_sha256") == kernel_source_digest("k_lm_stats"):
+            lm_traffic = tr.get("hbm_bytes_per_launch")
     rec_out = {
         "metric": f"LM-head verification ({W.LMHEAD_NAME}): verified rows/s, hidden states and "
-                  "LM-head weights in, logit rows never stored",
+                  "LM-head weights in",
         "value": rows / (ms_step * 1e-3), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
@@ -916,7 +939,8 @@ def bench_lmhead(args, sv):
         "effective_TFLOPs": (flops_t + flops_d) / (ms_step * 1e-3) / 1e12,
         "roofline": {"kernel": "k_lm_stats (draft and target rows, one launch)",
                      "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": lm_traffic,
                      "algorithmic_flops_per_launch": flops_t + flops_d, "avg_launch_ms": t_ms},
         "weight_bytes_per_pass": weight_bytes,
         "stage_ms": dict(zip(LM_STAGES, stage_ms)),
